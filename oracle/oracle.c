@@ -1,0 +1,367 @@
+/*
+ * Cluster attention: plain, slow, fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call this code:
+ * only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * load it. It shares no code, header or table with the HIP library.
+ *
+ * Every step follows the pages literally, one loop nest per formula, in
+ * float64 from the stored input values (float32 and bf16 values are exact in
+ * float64). Sources:
+ *   [MC]  model card "Hooshaai/distilbert-sst2-cluster-attention":
+ *         "Architecture Overview" (pipeline figure), "Mathematical
+ *         Formulation & Derivation" section 1 (Lloyd) and section 2 (Theorem 1).
+ *   [CF]  "ClusterFormer" specification on the "Hooshaai/svd-sst2-roberta-
+ *         cluster" page: section 2.1 (Lloyd), 2.3 (K = L), 3 (tensor trace),
+ *         4 (FLOP model).
+ * Readings where the pages are silent or disagree (also listed in the design
+ * notes): the window holds key j for query i iff |i - j| <= floor(W/2),
+ * clipped to [0, L); ties in the argmin go to the lowest cluster index; an
+ * empty cluster's centroid is the zero vector (the max(1, n) denominator);
+ * the returned pair is (c^(I), mu^(I)); softmax is max-subtracted, with no
+ * mask and no dropout; the scale is 1/sqrt(d) in both branches.
+ *
+ * Layout: each (b, h) pair is one "slice"; a slice of Q, K or V is a
+ * contiguous [L, d] row-major block and slices follow in b-major, h-minor
+ * order, i.e. the whole tensor is contiguous [B, H, L, d].
+ *
+ * Parity status: every function is pinned by the CPU tests (exact rational
+ * and 50-digit decimal brute force, closed forms and invariants); the end-to-
+ * end values have no worked example on the pages to pin them further.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int ora_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void ora_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* K = min(num_clusters, L)  ([CF] 2.1). */
+int ora_num_clusters(int nclust, int L) { return nclust < L ? nclust : L; }
+
+/* Window radius: floor(W / 2) (reading of W as the full window width). */
+int ora_radius(int W) { return W / 2; }
+
+/* Strided initialisation mu_k^(0) = Q[floor(k L / K)]  ([MC] 1, [CF] 2.1). */
+void ora_init_centroids(const double *Q, long S, int L, int d, int K, double *mu) {
+    for (long s = 0; s < S; ++s) {
+        for (int k = 0; k < K; ++k) {
+            long row = ((long)k * (long)L) / (long)K;
+            const double *src = Q + (s * L + row) * (long)d;
+            double *dst = mu + (s * K + k) * (long)d;
+            for (int j = 0; j < d; ++j) dst[j] = src[j];
+        }
+    }
+}
+
+/*
+ * Assignment step ([MC] 1, [CF] 2.1): D_ik = ||q_i - mu_k||_2^2 by direct
+ * difference, c_i = the smallest k attaining the minimum. Also records
+ * dbest_i = D_{i,c_i}, gap_i = (second smallest D) - dbest_i (+inf when K = 1;
+ * 0 on an exact tie) and qn2_i = ||q_i||^2. Any of the three may be NULL.
+ */
+void ora_assign(const double *Q, const double *mu, long S, int L, int d, int K,
+                int32_t *c, double *dbest, double *gap, double *qn2) {
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        for (int i = 0; i < L; ++i) {
+            const double *q = Q + (s * L + i) * (long)d;
+            double best = INFINITY, second = INFINITY;
+            int arg = 0;
+            for (int k = 0; k < K; ++k) {
+                const double *m = mu + (s * K + k) * (long)d;
+                double D = 0.0;
+                for (int j = 0; j < d; ++j) {
+                    double diff = q[j] - m[j];
+                    D += diff * diff;
+                }
+                if (D < best) {
+                    second = best;
+                    best = D;
+                    arg = k;
+                } else if (D < second) {
+                    second = D;
+                }
+            }
+            long t = s * L + i;
+            c[t] = arg;
+            if (dbest) dbest[t] = best;
+            if (gap) gap[t] = second - best;
+            if (qn2) {
+                double n2 = 0.0;
+                for (int j = 0; j < d; ++j) n2 += q[j] * q[j];
+                qn2[t] = n2;
+            }
+        }
+    }
+}
+
+/*
+ * Update step ([MC] 1, [CF] 2.1): n_k = #{i : c_i = k};
+ * mu_k = (sum over c_i = k of q_i) / max(1, n_k), so an empty cluster gets the
+ * zero vector. counts may be NULL.
+ */
+void ora_update(const double *Q, const int32_t *c, long S, int L, int d, int K,
+                double *mu, int32_t *counts) {
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double *sum = mu + s * K * (long)d;
+        int32_t *n = (int32_t *)calloc((size_t)K, sizeof(int32_t));
+        for (long e = 0; e < (long)K * d; ++e) sum[e] = 0.0;
+        for (int i = 0; i < L; ++i) {
+            int k = c[s * L + i];
+            const double *q = Q + (s * L + i) * (long)d;
+            n[k] += 1;
+            for (int j = 0; j < d; ++j) sum[(long)k * d + j] += q[j];
+        }
+        for (int k = 0; k < K; ++k) {
+            double den = n[k] > 1 ? (double)n[k] : 1.0;
+            for (int j = 0; j < d; ++j) sum[(long)k * d + j] /= den;
+            if (counts) counts[s * K + k] = n[k];
+        }
+        free(n);
+    }
+}
+
+/* Within-cluster objective J = sum_i ||q_i - mu_{c_i}||^2 per slice. */
+void ora_objective(const double *Q, const double *mu, const int32_t *c, long S,
+                   int L, int d, int K, double *J) {
+    for (long s = 0; s < S; ++s) {
+        double acc = 0.0;
+        for (int i = 0; i < L; ++i) {
+            const double *q = Q + (s * L + i) * (long)d;
+            const double *m = mu + (s * K + c[s * L + i]) * (long)d;
+            for (int j = 0; j < d; ++j) {
+                double diff = q[j] - m[j];
+                acc += diff * diff;
+            }
+        }
+        J[s] = acc;
+    }
+}
+
+/*
+ * Centroid cross-attention ([MC] pipeline figure, [CF] 3):
+ * V^cent_k = sum_j softmax_j(mu_k . k_j / sqrt(d)) v_j over all L keys.
+ * psum (nullable) receives each probability row's sum, for the pins.
+ */
+void ora_centroid_xattn(const double *mu, const double *Kt, const double *V,
+                        long S, int L, int d, int K, double *vcent, double *psum) {
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double *e = (double *)malloc(sizeof(double) * (size_t)L);
+        for (int k = 0; k < K; ++k) {
+            const double *m = mu + (s * K + k) * (long)d;
+            double mx = -INFINITY;
+            for (int j = 0; j < L; ++j) {
+                const double *kr = Kt + (s * L + j) * (long)d;
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += m[t] * kr[t];
+                e[j] = dot * scale;
+                if (e[j] > mx) mx = e[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < L; ++j) {
+                e[j] = exp(e[j] - mx);
+                z += e[j];
+            }
+            double *o = vcent + (s * K + k) * (long)d;
+            for (int t = 0; t < d; ++t) o[t] = 0.0;
+            double ps = 0.0;
+            for (int j = 0; j < L; ++j) {
+                double p = e[j] / z;
+                ps += p;
+                const double *vr = V + (s * L + j) * (long)d;
+                for (int t = 0; t < d; ++t) o[t] += p * vr[t];
+            }
+            if (psum) psum[s * K + k] = ps;
+        }
+        free(e);
+    }
+}
+
+/*
+ * Local sliding-window branch ([MC] pipeline figure, [CF] 3): for query i the
+ * keys are j in [max(0, i - r), min(L - 1, i + r)], r = floor(W / 2);
+ * O^loc_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over that window.
+ */
+void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
+                    int L, int d, int W, double *oloc, double *psum) {
+    const double scale = 1.0 / sqrt((double)d);
+    const int r = ora_radius(W);
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double *e = (double *)malloc(sizeof(double) * (size_t)L);
+        for (int i = 0; i < L; ++i) {
+            const double *q = Q + (s * L + i) * (long)d;
+            int lo = i - r < 0 ? 0 : i - r;
+            int hi = i + r > L - 1 ? L - 1 : i + r;
+            double mx = -INFINITY;
+            for (int j = lo; j <= hi; ++j) {
+                const double *kr = Kt + (s * L + j) * (long)d;
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += q[t] * kr[t];
+                e[j] = dot * scale;
+                if (e[j] > mx) mx = e[j];
+            }
+            double z = 0.0;
+            for (int j = lo; j <= hi; ++j) {
+                e[j] = exp(e[j] - mx);
+                z += e[j];
+            }
+            double *o = oloc + (s * L + i) * (long)d;
+            for (int t = 0; t < d; ++t) o[t] = 0.0;
+            double ps = 0.0;
+            for (int j = lo; j <= hi; ++j) {
+                double p = e[j] / z;
+                ps += p;
+                const double *vr = V + (s * L + j) * (long)d;
+                for (int t = 0; t < d; ++t) o[t] += p * vr[t];
+            }
+            if (psum) psum[s * L + i] = ps;
+        }
+        free(e);
+    }
+}
+
+/*
+ * Gather and convex fusion ([MC] Architecture Overview item 2, [CF] 3):
+ * O_i = (1 - alpha) V^cent_{c_i} + alpha O^loc_i.
+ */
+void ora_fuse(const double *vcent, const int32_t *c, const double *oloc, long S,
+              int L, int d, int K, double alpha, double *out) {
+    for (long s = 0; s < S; ++s) {
+        for (int i = 0; i < L; ++i) {
+            const double *g = vcent + (s * K + c[s * L + i]) * (long)d;
+            const double *l = oloc + (s * L + i) * (long)d;
+            double *o = out + (s * L + i) * (long)d;
+            for (int t = 0; t < d; ++t) o[t] = (1.0 - alpha) * g[t] + alpha * l[t];
+        }
+    }
+}
+
+/*
+ * Whole forward pass for one batch. K = min(nclust, L). Traces (all
+ * nullable): mu_hist [(iters+1), S, K, d] (mu^(0..I)), c_hist [iters, S, L],
+ * gap_hist [iters, S, L], J [iters, S] (objective after assignment t, i.e.
+ * against mu^(t-1)), Jp [iters, S] (objective after update t), qn2 [S, L],
+ * vcent [S, K, d], oloc [S, L, d]. Returns K, or -1 on invalid arguments.
+ */
+int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H,
+                int L, int d, int nclust, int iters, int W, double alpha,
+                double *out, int32_t *assign, double *mu_hist, int32_t *c_hist,
+                double *gap_hist, double *J, double *Jp, double *qn2,
+                double *vcent_out, double *oloc_out) {
+    if (B < 1 || H < 1 || L < 1 || d < 1 || nclust < 1 || iters < 1 || W < 0)
+        return -1;
+    const long S = (long)B * H;
+    const int K = ora_num_clusters(nclust, L);
+    double *mu = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
+    double *mu_next = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
+    double *gap = (double *)malloc(sizeof(double) * (size_t)(S * L));
+    double *vcent = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
+    double *oloc = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
+    double *Js = (double *)malloc(sizeof(double) * (size_t)S);
+
+    ora_init_centroids(Q, S, L, d, K, mu);
+    if (mu_hist) memcpy(mu_hist, mu, sizeof(double) * (size_t)(S * K * d));
+    for (int t = 1; t <= iters; ++t) {
+        ora_assign(Q, mu, S, L, d, K, assign, NULL, gap, t == 1 ? qn2 : NULL);
+        if (c_hist) memcpy(c_hist + (long)(t - 1) * S * L, assign, sizeof(int32_t) * (size_t)(S * L));
+        if (gap_hist) memcpy(gap_hist + (long)(t - 1) * S * L, gap, sizeof(double) * (size_t)(S * L));
+        if (J) {
+            ora_objective(Q, mu, assign, S, L, d, K, Js);
+            memcpy(J + (long)(t - 1) * S, Js, sizeof(double) * (size_t)S);
+        }
+        ora_update(Q, assign, S, L, d, K, mu_next, NULL);
+        double *tmp = mu;
+        mu = mu_next;
+        mu_next = tmp;
+        if (mu_hist) memcpy(mu_hist + (long)t * S * K * d, mu, sizeof(double) * (size_t)(S * K * d));
+        if (Jp) {
+            ora_objective(Q, mu, assign, S, L, d, K, Js);
+            memcpy(Jp + (long)(t - 1) * S, Js, sizeof(double) * (size_t)S);
+        }
+    }
+    ora_centroid_xattn(mu, Kt, V, S, L, d, K, vcent, NULL);
+    ora_local_attn(Q, Kt, V, S, L, d, W, oloc, NULL);
+    ora_fuse(vcent, assign, oloc, S, L, d, K, alpha, out);
+    if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
+    if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));
+    free(mu); free(mu_next); free(gap); free(vcent); free(oloc); free(Js);
+    return K;
+}
+
+/*
+ * The steps after clustering, from a given final assignment c (length S*L,
+ * values in [0, K)): mu = update(c), V^cent from mu, local branch, fusion.
+ * Used to check a GPU output against the GPU's own assignment.
+ */
+void ora_forward_from_assign(const double *Q, const double *Kt, const double *V,
+                             long S, int L, int d, int K, const int32_t *c, int W,
+                             double alpha, double *out, double *mu_out,
+                             double *vcent_out, double *oloc_out) {
+    double *mu = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
+    double *vcent = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
+    double *oloc = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
+    ora_update(Q, c, S, L, d, K, mu, NULL);
+    ora_centroid_xattn(mu, Kt, V, S, L, d, K, vcent, NULL);
+    ora_local_attn(Q, Kt, V, S, L, d, W, oloc, NULL);
+    ora_fuse(vcent, c, oloc, S, L, d, K, alpha, out);
+    if (mu_out) memcpy(mu_out, mu, sizeof(double) * (size_t)(S * K * d));
+    if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
+    if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));
+    free(mu); free(vcent); free(oloc);
+}
+
+/* C = A B with A [M, P] and B [P, N], row-major, plain sums over p in order. */
+void ora_matmul(const double *A, const double *Bm, long M, long P, long N, double *C) {
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < M; ++i) {
+        double *crow = C + i * N;
+        for (long j = 0; j < N; ++j) crow[j] = 0.0;
+        for (long p = 0; p < P; ++p) {
+            double a = A[i * P + p];
+            const double *brow = Bm + p * N;
+            for (long j = 0; j < N; ++j) crow[j] += a * brow[j];
+        }
+    }
+}
+
+/*
+ * Round to the nearest bf16 value (8 significant bits), ties to even, from
+ * float64 directly. Models bf16 storage of an intermediate in the full-layer
+ * workload. Range: normal and subnormal bf16; no overflow handling (not
+ * reached by the workloads).
+ */
+double ora_round_bf16(double x) {
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    frexp(x, &e);               /* x = m 2^e, 0.5 <= |m| < 1 */
+    int qexp = e - 8;           /* quantum of an 8-bit significand */
+    if (qexp < -133) qexp = -133; /* bf16 subnormal quantum 2^-133 */
+    double scaled = ldexp(x, -qexp);
+    return ldexp(rint(scaled), qexp);
+}
+
+void ora_round_bf16_array(double *x, long n) {
+    for (long i = 0; i < n; ++i) x[i] = ora_round_bf16(x[i]);
+}
