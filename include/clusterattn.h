@@ -1,0 +1,214 @@
+/*
+ * clusterattn.h - C ABI of the MI355X (gfx950) cluster attention library.
+ *
+ * The operation (forward pass of Cluster Attention, inference):
+ *   model card "Hooshaai/distilbert-sst2-cluster-attention", Architecture
+ *   Overview (pipeline figure) and Mathematical Formulation 1; "ClusterFormer"
+ *   specification on the "Hooshaai/svd-sst2-roberta-cluster" page, sections
+ *   2.1 and 3. Per (batch b, head h) slice, with tokens i = 0..L-1:
+ *     K       = min(nclust, L) clusters
+ *     mu^(0)  = Q[floor(k L / K)]                       (strided init)
+ *     for t = 1..iters:
+ *       c_i   = argmin_k ||q_i - mu_k||^2               (lowest k on ties)
+ *       mu_k  = sum_{c_i = k} q_i / max(1, n_k)         (empty -> zero vector)
+ *     Vc_k    = softmax_j(mu_k . k_j / sqrt(d)) v_j     (all L keys)
+ *     Ol_i    = softmax_j(q_i . k_j / sqrt(d)) v_j      (|i - j| <= floor(W/2))
+ *     O_i     = (1 - alpha) Vc_{c_i} + alpha Ol_i
+ *   The clustering returns (c^(iters), mu^(iters)); no mask, no dropout.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are device pointers to contiguous row-major arrays. "[B,H,L,d]"
+ *     means slice s = b*H + h holds rows s*L .. s*L+L-1 of d elements each.
+ *   - Storage dtype CA_F32 (float) or CA_BF16 (uint16 bf16 bits). All
+ *     arithmetic is fp32; a bf16 output is rounded to nearest-even once, at
+ *     the store. Centroids, centroid context and partials are always fp32.
+ *   - d must be 64 (CA_ERR_UNSUPPORTED otherwise); K = min(nclust, L) must
+ *     be <= 256 (CA_ERR_UNSUPPORTED otherwise).
+ *   - Ownership: the caller owns every buffer, including the workspace; the
+ *     library never allocates, frees or synchronises. Work is enqueued on
+ *     `stream` (0 = the null stream) and runs asynchronously.
+ *   - Errors: argument errors are detected on the host before any launch and
+ *     leave all outputs untouched (CA_ERR_INVALID_ARG / CA_ERR_UNSUPPORTED).
+ *     A failed launch returns CA_ERR_HIP.
+ *   - Alignment: tensor pointers must be 16-byte aligned, int32 pointers
+ *     4-byte aligned, the workspace 256-byte aligned.
+ *   - Determinism: no floating-point atomics; every reduction has a fixed
+ *     order, so identical inputs give bitwise identical outputs, and a run
+ *     with iters = t reproduces the first t iterations of a longer run.
+ *   - Reentrancy: no global mutable state; concurrent calls on different
+ *     streams must use different workspaces and outputs.
+ */
+#ifndef CLUSTERATTN_H
+#define CLUSTERATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CA_OK = 0,
+    CA_ERR_INVALID_ARG = 1,
+    CA_ERR_UNSUPPORTED = 2,
+    CA_ERR_HIP = 3
+} ca_status_t;
+
+typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype_t;
+
+/* Execution strategy of cluster_attn_forward_ex. AUTO picks FUSED when the
+ * shape allows it (L <= 128), else STAGED. FUSED: one launch, one workgroup
+ * per slice, the whole slice staged in LDS. STAGED: one kernel per step. */
+typedef enum { CA_PATH_AUTO = 0, CA_PATH_FUSED = 1, CA_PATH_STAGED = 2 } ca_path_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *ca_status_string(ca_status_t s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int ca_version(void);
+
+/*
+ * Bytes of workspace cluster_attn_forward needs for this shape (0 when the
+ * fused path applies). Returns 0 for invalid arguments as well; the forward
+ * call reports those.
+ */
+size_t cluster_attn_workspace_size(int B, int H, int L, int d, int nclust,
+                                   ca_dtype_t dt);
+
+/*
+ * Cluster attention forward (the whole operation above).
+ *   Q, K, V     in   device, [B,H,L,d], dtype dt.
+ *   B, H, L, d       all >= 1; d == 64.
+ *   nclust           >= 1; clamped to L.
+ *   iters            >= 1 Lloyd iterations.
+ *   W                >= 0 window width; radius floor(W/2).
+ *   alpha            fusion weight, 0 <= alpha <= 1 (NaN rejected).
+ *   out         out  device, [B,H,L,d], dtype dt; must not overlap Q, K, V.
+ *   assign_out  out  device, [B,H,L] int32 in [0, min(nclust,L)); may be NULL.
+ *   workspace        device, >= cluster_attn_workspace_size(...) bytes; may
+ *                    be NULL when that size is 0.
+ */
+ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V,
+                                 int B, int H, int L, int d, int nclust,
+                                 int iters, int W, float alpha, void *out,
+                                 int32_t *assign_out, ca_dtype_t dt,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/* Same as cluster_attn_forward with an explicit strategy. CA_PATH_FUSED on a
+ * shape it cannot take returns CA_ERR_UNSUPPORTED. STAGED needs
+ * cluster_attn_workspace_size_ex(..., CA_PATH_STAGED) bytes. */
+ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
+                                    int B, int H, int L, int d, int nclust,
+                                    int iters, int W, float alpha, void *out,
+                                    int32_t *assign_out, ca_dtype_t dt,
+                                    void *workspace, size_t workspace_bytes,
+                                    ca_path_t path, hipStream_t stream);
+
+size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust,
+                                      ca_dtype_t dt, ca_path_t path);
+
+/* ---------------------------------------------------------------------
+ * Single steps (one kernel each), for callers composing their own loop and
+ * for step-by-step checking. S = B*H slices; Kc = number of centroids.
+ * --------------------------------------------------------------------- */
+
+/*
+ * One assignment step (model card, Mathematical Formulation 1; ClusterFormer
+ * 2.1): assign[s,i] = argmin_k ||q_i - mu_k||^2, lowest k on ties, computed
+ * as ||mu_k||^2 - 2 q_i . mu_k in fp32.
+ *   Q in [S,L,d] dtype dt; mu in fp32 [S,Kc,d] (NULL: use the strided init
+ *   rows Q[floor(k L / Kc)], Kc <= L); assign out int32 [S,L].
+ */
+ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L,
+                             int d, int Kc, ca_dtype_t dt, int32_t *assign,
+                             hipStream_t stream);
+
+/*
+ * One update step (same passages): mu[s,k] = sum_{assign = k} q_i /
+ * max(1, n_k), an empty cluster gives the zero vector; counts[s,k] = n_k
+ * (counts may be NULL). Deterministic: per-tile partial sums in token order,
+ * then a fixed-order sum over tiles.
+ *   Q in [S,L,d] dtype dt; assign in int32 [S,L] with values in [0,Kc)
+ *   (values outside are clamped into it); mu out fp32 [S,Kc,d]; workspace of
+ *   ca_centroid_update_workspace_size(S,L,d,Kc) bytes.
+ */
+ca_status_t ca_centroid_update(const void *Q, const int32_t *assign, int S,
+                               int L, int d, int Kc, ca_dtype_t dt, float *mu,
+                               int32_t *counts, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+size_t ca_centroid_update_workspace_size(int S, int L, int d, int Kc);
+
+/*
+ * Centroid cross-attention (model card pipeline figure; ClusterFormer 3):
+ * vcent[s,k] = sum_j softmax_j(mu_k . k_j / sqrt(d)) v_j over all L keys.
+ *   mu in fp32 [S,Kc,d]; K, V in [S,L,d] dtype dt; vcent out fp32 [S,Kc,d];
+ *   workspace of ca_centroid_xattn_workspace_size(S,L,d,Kc) bytes (split-key
+ *   partials combined in a fixed order).
+ */
+ca_status_t ca_centroid_xattn(const float *mu, const void *K, const void *V,
+                              int S, int L, int d, int Kc, ca_dtype_t dt,
+                              float *vcent, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+size_t ca_centroid_xattn_workspace_size(int S, int L, int d, int Kc);
+
+/*
+ * Local sliding-window branch (model card pipeline figure; ClusterFormer 3):
+ * oloc[s,i] = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over
+ * j in [max(0, i - r), min(L - 1, i + r)], r = floor(W/2).
+ *   Q, K, V in [S,L,d] dtype dt; oloc out fp32 [S,L,d].
+ */
+ca_status_t ca_local_window_attn(const void *Q, const void *K, const void *V,
+                                 int S, int L, int d, int W, ca_dtype_t dt,
+                                 float *oloc, hipStream_t stream);
+
+/*
+ * Gather and convex fusion (model card Architecture Overview item 2):
+ * out[s,i] = (1 - alpha) vcent[s, assign[s,i]] + alpha oloc[s,i].
+ *   vcent fp32 [S,Kc,d]; assign int32 [S,L] in [0,Kc) (values outside are
+ *   clamped into it); oloc fp32 [S,L,d];
+ *   out [S,L,d] dtype dt.
+ */
+ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign,
+                           const float *oloc, int S, int L, int d, int Kc,
+                           float alpha, ca_dtype_t dt, void *out,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * Full attention layer (model card pipeline figure: multi-head projections
+ * of X, cluster attention, output projection Y = O W_O), bf16 storage:
+ *   Q = X Wq, K = X Wk, V = X Wv  (X [B,L,Dm], W [Dm, H*d], no bias; head h
+ *   is columns h*d .. h*d+d-1), each rounded to bf16; O = cluster attention
+ *   (as cluster_attn_forward, bf16); Y = O_merged Wo (Wo [H*d, Dm]) in bf16.
+ *   X, Wq, Wk, Wv, Wo, Y: device bf16 bits (uint16). Dm == H*d, d == 64,
+ *   Dm a multiple of 64. assign_out int32 [B,H,L] or NULL. qkv_out: NULL,
+ *   or device bf16 [3,B,H,L,d] receiving Q, K, V. Workspace of
+ *   cluster_attn_layer_workspace_size(...) bytes.
+ * --------------------------------------------------------------------- */
+size_t cluster_attn_layer_workspace_size(int B, int L, int Dm, int H, int d,
+                                         int nclust);
+
+ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq,
+                                       const void *Wk, const void *Wv,
+                                       const void *Wo, int B, int L, int Dm,
+                                       int H, int d, int nclust, int iters,
+                                       int W, float alpha, void *Y,
+                                       int32_t *assign_out, void *qkv_out,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
+ * Plain bf16 GEMM used by the layer: C[M,N] = A[M,Kd] B[Kd,N], fp32
+ * accumulation, bf16 (nearest-even) output. All row-major bf16 bits; M, N, Kd
+ * multiples of 64 (CA_ERR_UNSUPPORTED otherwise).
+ */
+ca_status_t ca_gemm_bf16(const void *A, const void *Bm, int M, int N, int Kd,
+                         void *C, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLUSTERATTN_H */

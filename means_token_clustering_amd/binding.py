@@ -1,0 +1,255 @@
+"""ctypes binding of libclusterattn.so (the C ABI in include/clusterattn.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels. There is no fallback: if the library is missing, every call raises.
+The Python names match the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libclusterattn.so")
+
+CA_OK, CA_ERR_INVALID_ARG, CA_ERR_UNSUPPORTED, CA_ERR_HIP = 0, 1, 2, 3
+CA_F32, CA_BF16 = 0, 1
+CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED = 0, 1, 2
+
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "ca_status_string": (ctypes.c_char_p, [_i]),
+    "ca_version": (_i, []),
+    "cluster_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "cluster_attn_workspace_size_ex": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "cluster_attn_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
+                                  _vp, _sz, _vp]),
+    "cluster_attn_forward_ex": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                     _i, _vp, _sz, _i, _vp]),
+    "ca_kmeans_assign": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "ca_centroid_update": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "ca_centroid_update_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "ca_centroid_xattn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
+    "ca_centroid_xattn_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "ca_local_window_attn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "ca_gather_fuse": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _vp]),
+    "cluster_attn_layer_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "cluster_attn_layer_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
+                                        _f, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ca_gemm_bf16": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+}
+
+
+class CaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libclusterattn.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it first "
+                    "(python -m means_token_clustering_amd.build)")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ca_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != CA_OK:
+        raise CaError(status, where)
+
+
+# ------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return CA_F32
+    if t.dtype == torch.bfloat16:
+        return CA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        return workspace
+    return torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned_ptr(ws) -> Optional[int]:
+    if ws is None:
+        return None
+    p = ws.data_ptr()
+    return (p + 255) // 256 * 256
+
+
+def _ws_bytes(ws) -> int:
+    if ws is None:
+        return 0
+    p = ws.data_ptr()
+    return ws.numel() * ws.element_size() - ((p + 255) // 256 * 256 - p)
+
+
+def cluster_attn_workspace_size(B, H, L, d, nclust, dtype=CA_F32, path=CA_PATH_AUTO) -> int:
+    return lib().cluster_attn_workspace_size_ex(B, H, L, d, nclust, dtype, path)
+
+
+def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float, out=None,
+                         assign_out=None, path: int = CA_PATH_AUTO, workspace=None,
+                         stream=None, want_assign: bool = True):
+    """Q, K, V: contiguous [B, H, L, d] float32 or bfloat16 GPU tensors.
+
+    Returns (out, assign_out); allocates out/assign_out/workspace with torch
+    when not given.
+    """
+    torch = _torch()
+    B, H, L, d = Q.shape
+    dt = _dtype_code(Q)
+    if out is None:
+        out = torch.empty_like(Q)
+    if assign_out is None and want_assign:
+        assign_out = torch.empty((B, H, L), dtype=torch.int32, device=Q.device)
+    need = cluster_attn_workspace_size(B, H, L, d, nclust, dt, path)
+    ws = _workspace(need, Q.device, workspace)
+    st = lib().cluster_attn_forward_ex(
+        _ptr(Q), _ptr(K), _ptr(V), B, H, L, d, nclust, iters, W, float(alpha), _ptr(out),
+        _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws), path, _stream(stream))
+    _check(st, "cluster_attn_forward")
+    return out, assign_out
+
+
+def ca_kmeans_assign(Q, mu, Kc: int, assign=None, stream=None):
+    torch = _torch()
+    B, H, L, d = Q.shape
+    if assign is None:
+        assign = torch.empty((B, H, L), dtype=torch.int32, device=Q.device)
+    st = lib().ca_kmeans_assign(_ptr(Q), _ptr(mu), B * H, L, d, Kc, _dtype_code(Q), _ptr(assign),
+                                _stream(stream))
+    _check(st, "ca_kmeans_assign")
+    return assign
+
+
+def ca_centroid_update(Q, assign, Kc: int, stream=None):
+    torch = _torch()
+    B, H, L, d = Q.shape
+    mu = torch.empty((B, H, Kc, d), dtype=torch.float32, device=Q.device)
+    counts = torch.empty((B, H, Kc), dtype=torch.int32, device=Q.device)
+    need = lib().ca_centroid_update_workspace_size(B * H, L, d, Kc)
+    ws = _workspace(need, Q.device, None)
+    st = lib().ca_centroid_update(_ptr(Q), _ptr(assign), B * H, L, d, Kc, _dtype_code(Q),
+                                  _ptr(mu), _ptr(counts), _aligned_ptr(ws), _ws_bytes(ws),
+                                  _stream(stream))
+    _check(st, "ca_centroid_update")
+    return mu, counts
+
+
+def ca_centroid_xattn(mu, K, V, stream=None):
+    torch = _torch()
+    B, H, L, d = K.shape
+    Kc = mu.shape[-2]
+    vcent = torch.empty((B, H, Kc, d), dtype=torch.float32, device=K.device)
+    need = lib().ca_centroid_xattn_workspace_size(B * H, L, d, Kc)
+    ws = _workspace(need, K.device, None)
+    st = lib().ca_centroid_xattn(_ptr(mu), _ptr(K), _ptr(V), B * H, L, d, Kc, _dtype_code(K),
+                                 _ptr(vcent), _aligned_ptr(ws), _ws_bytes(ws), _stream(stream))
+    _check(st, "ca_centroid_xattn")
+    return vcent
+
+
+def ca_local_window_attn(Q, K, V, W: int, stream=None):
+    torch = _torch()
+    B, H, L, d = Q.shape
+    oloc = torch.empty((B, H, L, d), dtype=torch.float32, device=Q.device)
+    st = lib().ca_local_window_attn(_ptr(Q), _ptr(K), _ptr(V), B * H, L, d, W, _dtype_code(Q),
+                                    _ptr(oloc), _stream(stream))
+    _check(st, "ca_local_window_attn")
+    return oloc
+
+
+def ca_gather_fuse(vcent, assign, oloc, alpha: float, dtype, stream=None):
+    torch = _torch()
+    B, H, L, d = oloc.shape
+    Kc = vcent.shape[-2]
+    out = torch.empty((B, H, L, d), dtype=dtype, device=oloc.device)
+    st = lib().ca_gather_fuse(_ptr(vcent), _ptr(assign), _ptr(oloc), B * H, L, d, Kc,
+                              float(alpha), _dtype_code(out), _ptr(out), _stream(stream))
+    _check(st, "ca_gather_fuse")
+    return out
+
+
+def cluster_attn_layer_forward(X, Wq, Wk, Wv, Wo, H: int, nclust: int, iters: int, W: int,
+                               alpha: float, want_qkv: bool = False, stream=None):
+    """X [B, L, Dm] and W* [Dm, Dm] bfloat16 GPU tensors; returns (Y, assign, qkv)."""
+    torch = _torch()
+    B, L, Dm = X.shape
+    d = Dm // H
+    Y = torch.empty((B, L, Dm), dtype=torch.bfloat16, device=X.device)
+    assign = torch.empty((B, H, L), dtype=torch.int32, device=X.device)
+    qkv = torch.empty((3, B, H, L, d), dtype=torch.bfloat16, device=X.device) if want_qkv else None
+    need = lib().cluster_attn_layer_workspace_size(B, L, Dm, H, d, nclust)
+    ws = _workspace(need, X.device, None)
+    st = lib().cluster_attn_layer_forward(
+        _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo), B, L, Dm, H, d, nclust, iters, W,
+        float(alpha), _ptr(Y), _ptr(assign), _ptr(qkv), _aligned_ptr(ws), _ws_bytes(ws),
+        _stream(stream))
+    _check(st, "cluster_attn_layer_forward")
+    return Y, assign, qkv
+
+
+def ca_gemm_bf16(A, Bm, stream=None):
+    torch = _torch()
+    M, Kd = A.shape
+    _, N = Bm.shape
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    st = lib().ca_gemm_bf16(_ptr(A), _ptr(Bm), M, N, Kd, _ptr(C), _stream(stream))
+    _check(st, "ca_gemm_bf16")
+    return C

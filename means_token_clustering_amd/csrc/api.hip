@@ -1,0 +1,267 @@
+// C ABI of the cluster attention library: argument checks on the host,
+// workspace layout, and the launch sequence of each entry point. The
+// operation and every convention are stated in include/clusterattn.h.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace {
+
+using namespace ca;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t elem_bytes(ca_dtype_t dt) { return dt == CA_BF16 ? 2 : 4; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int clusters(int nclust, int L) { return nclust < L ? nclust : L; }
+
+// Shape checks shared by the whole-forward entry points. Returns CA_OK,
+// CA_ERR_INVALID_ARG or CA_ERR_UNSUPPORTED.
+ca_status_t check_shape(int B, int H, int L, int d, int nclust, int iters, int W, float alpha,
+                        ca_dtype_t dt) {
+    if (B < 1 || H < 1 || L < 1 || d < 1 || nclust < 1 || iters < 1 || W < 0)
+        return CA_ERR_INVALID_ARG;
+    if (!(alpha >= 0.f && alpha <= 1.f)) return CA_ERR_INVALID_ARG;   // also NaN
+    if (dt != CA_F32 && dt != CA_BF16) return CA_ERR_INVALID_ARG;
+    if ((long long)B * H * L * d > (1LL << 40)) return CA_ERR_INVALID_ARG;
+    if ((long long)B * H * L > (1LL << 31) - 1) return CA_ERR_UNSUPPORTED;
+    if (d != kD) return CA_ERR_UNSUPPORTED;
+    if (clusters(nclust, L) > kMaxClusters) return CA_ERR_UNSUPPORTED;
+    return CA_OK;
+}
+
+// Workspace of the staged path, carved in this order (each 256-B aligned).
+struct StagedLayout {
+    size_t mu, assign, part_sum, part_cnt, vcent, xpart, total;
+};
+
+StagedLayout staged_layout(long S, int L, int Kc) {
+    StagedLayout w{};
+    const long ntile = kmeans_tiles(L);
+    const long nsplit = xattn_splits(L);
+    size_t off = 0;
+    w.mu = off;       off += align_up(sizeof(float) * S * Kc * kD);
+    w.assign = off;   off += align_up(sizeof(int32_t) * S * L);
+    w.part_sum = off; off += align_up(sizeof(float) * S * ntile * Kc * kD);
+    w.part_cnt = off; off += align_up(sizeof(int32_t) * S * ntile * Kc);
+    w.vcent = off;    off += align_up(sizeof(float) * S * Kc * kD);
+    w.xpart = off;    off += nsplit > 1 ? align_up(sizeof(float) * S * nsplit * Kc * (kD + 2)) : 0;
+    w.total = off;
+    return w;
+}
+
+bool use_fused(ca_path_t path, int L, int Kc) {
+    if (path == CA_PATH_STAGED) return false;
+    return fused_supported(L, Kc);
+}
+
+ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_HIP; }
+
+#define CA_TRY(expr)                                  \
+    do {                                              \
+        hipError_t _e = (expr);                       \
+        if (_e != hipSuccess) return CA_ERR_HIP;      \
+    } while (0)
+
+ca_status_t forward_impl(const void *Q, const void *K, const void *V, int B, int H, int L, int d,
+                         int nclust, int iters, int W, float alpha, void *out,
+                         int32_t *assign_out, ca_dtype_t dt, void *workspace,
+                         size_t workspace_bytes, ca_path_t path, hipStream_t stream) {
+    ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
+    if (st != CA_OK) return st;
+    if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED)
+        return CA_ERR_INVALID_ARG;
+    if (!Q || !K || !V || !out) return CA_ERR_INVALID_ARG;
+    const long S = (long)B * H;
+    const size_t tbytes = (size_t)S * L * d * elem_bytes(dt);
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+        return CA_ERR_INVALID_ARG;
+    if (assign_out && !aligned(assign_out, 4)) return CA_ERR_INVALID_ARG;
+    if (overlap(out, tbytes, Q, tbytes) || overlap(out, tbytes, K, tbytes) ||
+        overlap(out, tbytes, V, tbytes))
+        return CA_ERR_INVALID_ARG;
+    const size_t abytes = sizeof(int32_t) * (size_t)S * L;
+    if (assign_out && (overlap(assign_out, abytes, out, tbytes) ||
+                       overlap(assign_out, abytes, Q, tbytes) ||
+                       overlap(assign_out, abytes, K, tbytes) ||
+                       overlap(assign_out, abytes, V, tbytes)))
+        return CA_ERR_INVALID_ARG;
+    const int Kc = clusters(nclust, L);
+    if (path == CA_PATH_FUSED && !fused_supported(L, Kc)) return CA_ERR_UNSUPPORTED;
+
+    if (use_fused(path, L, Kc)) {
+        return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, W, alpha, dt, out,
+                                               assign_out, stream));
+    }
+    const StagedLayout lay = staged_layout(S, L, Kc);
+    if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;
+    char *ws = static_cast<char *>(workspace);
+    if (overlap(ws, lay.total, out, tbytes) || overlap(ws, lay.total, Q, tbytes) ||
+        overlap(ws, lay.total, K, tbytes) || overlap(ws, lay.total, V, tbytes) ||
+        (assign_out && overlap(ws, lay.total, assign_out, abytes)))
+        return CA_ERR_INVALID_ARG;
+    float *mu = reinterpret_cast<float *>(ws + lay.mu);
+    int32_t *c = assign_out ? assign_out : reinterpret_cast<int32_t *>(ws + lay.assign);
+    float *psum = reinterpret_cast<float *>(ws + lay.part_sum);
+    int32_t *pcnt = reinterpret_cast<int32_t *>(ws + lay.part_cnt);
+    float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
+    float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
+    const int ntile = kmeans_tiles(L);
+    for (int t = 1; t <= iters; ++t) {
+        CA_TRY(launch_kmeans_assign(Q, t == 1 ? nullptr : mu, (int)S, L, Kc, dt, c, psum, pcnt,
+                                    stream));
+        CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream));
+    }
+    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, vcent, xpart, stream));
+    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, out, nullptr,
+                               stream));
+    return CA_OK;
+}
+
+// Checks shared by the single-step entry points.
+ca_status_t check_step(int S, int L, int d, int Kc, ca_dtype_t dt) {
+    if (S < 1 || L < 1 || d < 1 || Kc < 1) return CA_ERR_INVALID_ARG;
+    if (dt != CA_F32 && dt != CA_BF16) return CA_ERR_INVALID_ARG;
+    if ((long long)S * L > (1LL << 31) - 1) return CA_ERR_UNSUPPORTED;
+    if (d != kD || Kc > kMaxClusters) return CA_ERR_UNSUPPORTED;
+    return CA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ca_status_string(ca_status_t s) {
+    switch (s) {
+        case CA_OK: return "ok";
+        case CA_ERR_INVALID_ARG: return "invalid argument";
+        case CA_ERR_UNSUPPORTED: return "unsupported shape or type";
+        case CA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int ca_version(void) { return 100; }
+
+size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust, ca_dtype_t dt,
+                                      ca_path_t path) {
+    if (check_shape(B, H, L, d, nclust, 1, 0, 0.f, dt) != CA_OK) return 0;
+    const int Kc = clusters(nclust, L);
+    if (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && use_fused(path, L, Kc))) return 0;
+    return staged_layout((long)B * H, L, Kc).total;
+}
+
+size_t cluster_attn_workspace_size(int B, int H, int L, int d, int nclust, ca_dtype_t dt) {
+    return cluster_attn_workspace_size_ex(B, H, L, d, nclust, dt, CA_PATH_AUTO);
+}
+
+ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V, int B, int H, int L,
+                                 int d, int nclust, int iters, int W, float alpha, void *out,
+                                 int32_t *assign_out, ca_dtype_t dt, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+    return forward_impl(Q, K, V, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
+                        workspace, workspace_bytes, CA_PATH_AUTO, stream);
+}
+
+ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V, int B, int H,
+                                    int L, int d, int nclust, int iters, int W, float alpha,
+                                    void *out, int32_t *assign_out, ca_dtype_t dt,
+                                    void *workspace, size_t workspace_bytes, ca_path_t path,
+                                    hipStream_t stream) {
+    return forward_impl(Q, K, V, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
+                        workspace, workspace_bytes, path, stream);
+}
+
+ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d, int Kc,
+                             ca_dtype_t dt, int32_t *assign, hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, Kc, dt);
+    if (st != CA_OK) return st;
+    if (!Q || !assign) return CA_ERR_INVALID_ARG;
+    if (!mu && Kc > L) return CA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || (mu && !aligned(mu, 16)) || !aligned(assign, 4))
+        return CA_ERR_INVALID_ARG;
+    return hip_status(launch_kmeans_assign(Q, mu, S, L, Kc, dt, assign, nullptr, nullptr, stream));
+}
+
+size_t ca_centroid_update_workspace_size(int S, int L, int d, int Kc) {
+    if (check_step(S, L, d, Kc, CA_F32) != CA_OK) return 0;
+    const size_t n = (size_t)S * kmeans_tiles(L) * Kc;
+    return align_up(sizeof(float) * n * kD) + align_up(sizeof(int32_t) * n);
+}
+
+ca_status_t ca_centroid_update(const void *Q, const int32_t *assign, int S, int L, int d, int Kc,
+                               ca_dtype_t dt, float *mu, int32_t *counts, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, Kc, dt);
+    if (st != CA_OK) return st;
+    if (!Q || !assign || !mu || !workspace) return CA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(mu, 16) || !aligned(assign, 4) ||
+        (counts && !aligned(counts, 4)) || !aligned(workspace, kAlign))
+        return CA_ERR_INVALID_ARG;
+    if (workspace_bytes < ca_centroid_update_workspace_size(S, L, d, Kc)) return CA_ERR_INVALID_ARG;
+    // per-tile partial sums of the given assignment, then the tile-order sum
+    const size_t n = (size_t)S * kmeans_tiles(L) * Kc;
+    char *ws = static_cast<char *>(workspace);
+    float *psum = reinterpret_cast<float *>(ws);
+    int32_t *pcnt = reinterpret_cast<int32_t *>(ws + align_up(sizeof(float) * n * kD));
+    CA_TRY(launch_centroid_partials(Q, assign, S, L, Kc, dt, psum, pcnt, stream));
+    return hip_status(launch_centroid_reduce(psum, pcnt, kmeans_tiles(L), S, Kc, mu, counts, stream));
+}
+
+size_t ca_centroid_xattn_workspace_size(int S, int L, int d, int Kc) {
+    if (check_step(S, L, d, Kc, CA_F32) != CA_OK) return 0;
+    const int nsplit = xattn_splits(L);
+    return nsplit > 1 ? align_up(sizeof(float) * (size_t)S * nsplit * Kc * (kD + 2)) : 0;
+}
+
+ca_status_t ca_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L, int d,
+                              int Kc, ca_dtype_t dt, float *vcent, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, Kc, dt);
+    if (st != CA_OK) return st;
+    if (!mu || !K || !V || !vcent) return CA_ERR_INVALID_ARG;
+    if (!aligned(mu, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(vcent, 16))
+        return CA_ERR_INVALID_ARG;
+    const size_t need = ca_centroid_xattn_workspace_size(S, L, d, Kc);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
+        return CA_ERR_INVALID_ARG;
+    return hip_status(launch_centroid_xattn(mu, K, V, S, L, Kc, dt, vcent,
+                                            static_cast<float *>(workspace), stream));
+}
+
+ca_status_t ca_local_window_attn(const void *Q, const void *K, const void *V, int S, int L, int d,
+                                 int W, ca_dtype_t dt, float *oloc, hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, 1, dt);
+    if (st != CA_OK) return st;
+    if (W < 0 || !Q || !K || !V || !oloc) return CA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(oloc, 16))
+        return CA_ERR_INVALID_ARG;
+    return hip_status(launch_local_window(Q, K, V, S, L, W, dt, nullptr, nullptr, 1, 1.f, nullptr,
+                                          oloc, stream));
+}
+
+ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
+                           int L, int d, int Kc, float alpha, ca_dtype_t dt, void *out,
+                           hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, Kc, dt);
+    if (st != CA_OK) return st;
+    if (!(alpha >= 0.f && alpha <= 1.f)) return CA_ERR_INVALID_ARG;
+    if (!vcent || !assign || !oloc || !out) return CA_ERR_INVALID_ARG;
+    if (!aligned(vcent, 16) || !aligned(oloc, 16) || !aligned(out, 16) || !aligned(assign, 4))
+        return CA_ERR_INVALID_ARG;
+    return hip_status(launch_gather_fuse(vcent, assign, oloc, S, L, Kc, alpha, dt, out, stream));
+}
+
+}  // extern "C"

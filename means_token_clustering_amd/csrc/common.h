@@ -1,0 +1,129 @@
+// Shared device helpers of the cluster attention library (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "clusterattn.h"
+
+namespace ca {
+
+constexpr int kD = 64;          // head dimension supported by the kernels
+constexpr int kMaxClusters = 256;
+constexpr int kWave = 64;
+
+// bf16 storage is carried as raw uint16 bit patterns.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Load 4 consecutive elements (16 B for fp32, 8 B for bf16) as floats.
+template <typename T>
+__device__ __forceinline__ float4 load4(const T *p);
+
+template <>
+__device__ __forceinline__ float4 load4<float>(const float *p) {
+    return *reinterpret_cast<const float4 *>(p);
+}
+
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t *p) {
+    uint2 u = *reinterpret_cast<const uint2 *>(p);
+    float4 r;
+    r.x = __uint_as_float(u.x << 16);
+    r.y = __uint_as_float(u.x & 0xffff0000u);
+    r.z = __uint_as_float(u.y << 16);
+    r.w = __uint_as_float(u.y & 0xffff0000u);
+    return r;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *p, float4 v);
+
+template <>
+__device__ __forceinline__ void store4<float>(float *p, float4 v) {
+    *reinterpret_cast<float4 *>(p) = v;
+}
+
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float4 v) {
+    uint2 u;
+    u.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+    u.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+    *reinterpret_cast<uint2 *>(p) = u;
+}
+
+// (value, index) lexicographic minimum: the smaller value wins, and on equal
+// values the smaller index wins. NaN never wins against a number.
+__device__ __forceinline__ bool lex_less(float a, int ia, float b, int ib) {
+    return (a < b) || (a == b && ia < ib) || (b != b && a == a);
+}
+
+// Wave-wide integer min / max (all 64 lanes must be active and converged).
+__device__ __forceinline__ int wave_min_i32(int v) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) v = max(v, __shfl_xor(v, off));
+    return v;
+}
+
+// exp(x) for softmax weights, as 2^(x log2 e) on the hardware exp2 unit.
+__device__ __forceinline__ float exp_f32(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+}  // namespace ca
+
+// Host-side launch helpers live in the .hip files; declared here so the
+// C-ABI translation unit can call them.
+namespace ca {
+
+hipError_t launch_kmeans_assign(const void *Q, const float *mu, int S, int L, int Kc,
+                                ca_dtype_t dt, int32_t *assign, float *part_sum,
+                                int32_t *part_cnt, hipStream_t st);
+hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S, int L, int Kc,
+                                    ca_dtype_t dt, float *part_sum, int32_t *part_cnt,
+                                    hipStream_t st);
+int kmeans_tiles(int L);
+hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt, int nblk,
+                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st);
+
+int xattn_splits(int L);
+hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
+                                 int Kc, ca_dtype_t dt, float *vcent, float *partials,
+                                 hipStream_t st);
+
+hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
+                               ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
+                               float alpha, void *out, float *oloc, hipStream_t st);
+hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
+                              int L, int Kc, float alpha, ca_dtype_t dt, void *out,
+                              hipStream_t st);
+
+bool fused_supported(int L, int Kc);
+hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                                int iters, int W, float alpha, ca_dtype_t dt, void *out,
+                                int32_t *assign, hipStream_t st);
+
+hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *Bm, int M, int N, int Kd,
+                            uint16_t *C, int a_mode, int c_mode, int B, int L, int H,
+                            hipStream_t st);
+
+}  // namespace ca

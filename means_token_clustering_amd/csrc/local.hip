@@ -1,0 +1,209 @@
+// Local sliding-window attention with the fused gather + convex-fusion
+// epilogue (staged path, any L).
+//
+// Branch: model card "Hooshaai/distilbert-sst2-cluster-attention",
+// Architecture Overview figure (LocalAttn(Q, K, V, W=32), then
+// O = (1 - alpha) V^gathered + alpha O^local with V^gathered_i = Vc_{c_i});
+// "ClusterFormer" spec 3 (band-masked attention) and 4 (2W+1 band). Window
+// reading used throughout the library: key j belongs to query i iff
+// |i - j| <= floor(W/2), clipped to [0, L).
+//
+// Work split: one workgroup per 64-query tile; the tile's keys
+// [i0 - r, i0 + 63 + r] stream through LDS in 64-row K/V tiles (the halo).
+// Four lanes share a query, each holding 16 of its 64 dims: partial dot
+// products meet through two butterfly adds that every lane performs in the
+// same order, so all four see the same score. Scores of one key tile go to
+// LDS, then an online softmax folds the tile in.
+#include "common.h"
+
+namespace ca {
+
+constexpr int kQTile = 64;
+constexpr int kLTile = 64;
+constexpr int kLPad = kD + 1;
+
+template <typename T, bool FUSE>
+__global__ __launch_bounds__(256) void local_window_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int r,
+    int ntile, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
+    float alpha, T *__restrict__ out, float *__restrict__ oloc) {
+    __shared__ float sm_k[kLTile * kLPad];
+    __shared__ float sm_v[kLTile * kLPad];
+    __shared__ float sm_s[kQTile * kLPad];
+
+    const int tid = threadIdx.x;
+    const int tile = blockIdx.x % ntile;
+    const long s = blockIdx.x / ntile;
+    const long base = s * (long)L * kD;
+    const int i0 = tile * kQTile;
+    const int nq = min(kQTile, L - i0);
+    const int qi = tid >> 2, g = tid & 3;
+    const int i = i0 + qi;
+    const bool active = qi < nq;
+    // window of this query and of the whole tile (64-bit: r may be huge)
+    const int lo = (int)max(0L, (long)i - r);
+    const int hi = (int)min((long)L - 1, (long)i + r);
+    const int tlo = (int)max(0L, (long)i0 - r);
+    const int thi = (int)min((long)L, (long)i0 + nq + r);   // exclusive
+    const float scale = 1.0f / sqrtf((float)kD);
+
+    float qr[16];
+    if (active) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float4 v = load4<T>(Q + base + (long)i * kD + 16 * g + 4 * c);
+            qr[4 * c] = v.x * scale; qr[4 * c + 1] = v.y * scale;
+            qr[4 * c + 2] = v.z * scale; qr[4 * c + 3] = v.w * scale;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) qr[c] = 0.f;
+    }
+    float m = -__builtin_inff(), l = 0.f;
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+
+    for (int jt = tlo; jt < thi; jt += kLTile) {
+        const int nk = min(kLTile, thi - jt);
+        __syncthreads();
+        for (int e = tid; e < nk * (kD / 4); e += 256) {
+            const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
+            float4 kv = load4<T>(Kx + base + (long)(jt + rr) * kD + c4);
+            float4 vv = load4<T>(Vx + base + (long)(jt + rr) * kD + c4);
+            float *dk = sm_k + rr * kLPad + c4;
+            float *dv = sm_v + rr * kLPad + c4;
+            dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
+            dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
+        }
+        __syncthreads();
+        // keys of this tile inside this query's window
+        const int a = active ? max(lo, jt) - jt : 0;
+        const int b = active ? min(hi, jt + nk - 1) - jt : -1;   // inclusive
+        // the four lanes of a query share a and b, so the shuffles below
+        // stay within converged groups; loop bounds of the wave are the
+        // union of its queries' ranges
+        const int wa = wave_min_i32(a < b + 1 ? a : kLTile);
+        const int wb = wave_max_i32(b);
+        float mt = -__builtin_inff();
+        for (int key = wa; key <= wb; ++key) {
+            const float *kr = sm_k + key * kLPad + 16 * g;
+            float part = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
+            float sum2 = part + __shfl_xor(part, 1);
+            float sc = sum2 + __shfl_xor(sum2, 2);
+            if (key >= a && key <= b) {
+                mt = fmaxf(mt, sc);
+                if (g == 0) sm_s[qi * kLPad + key] = sc;
+            }
+        }
+        __syncthreads();
+        if (b >= a) {
+            const float mn = fmaxf(m, mt);
+            const float corr = (m == -__builtin_inff()) ? 0.f : exp_f32(m - mn);
+            l *= corr;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) acc[c] *= corr;
+            for (int key = a; key <= b; ++key) {
+                const float p = exp_f32(sm_s[qi * kLPad + key] - mn);
+                l += p;
+                const float *vr = sm_v + key * kLPad + 16 * g;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, vr[c], acc[c]);
+            }
+            m = mn;
+        }
+    }
+    if (!active) return;
+    const float inv = 1.0f / l;
+    const long o = base + (long)i * kD + 16 * g;
+    if (FUSE) {
+        const int c = assign[s * L + i];
+        const float *gv = vcent + (s * Kc + c) * kD + 16 * g;
+        const float wg = 1.0f - alpha;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 v;
+            v.x = wg * gv[4 * q + 0] + alpha * (acc[4 * q + 0] * inv);
+            v.y = wg * gv[4 * q + 1] + alpha * (acc[4 * q + 1] * inv);
+            v.z = wg * gv[4 * q + 2] + alpha * (acc[4 * q + 2] * inv);
+            v.w = wg * gv[4 * q + 3] + alpha * (acc[4 * q + 3] * inv);
+            store4<T>(out + o + 4 * q, v);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float4 v = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv,
+                                   acc[4 * q + 3] * inv);
+            store4<float>(oloc + o + 4 * q, v);
+        }
+    }
+}
+
+// out = (1 - alpha) vcent[assign] + alpha oloc, one thread per 4 elements.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_fuse_kernel(const float *__restrict__ vcent,
+                                                          const int32_t *__restrict__ assign,
+                                                          const float *__restrict__ oloc,
+                                                          int L, int Kc, float alpha, long total4,
+                                                          T *__restrict__ out) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= total4) return;
+    const long row = e / (kD / 4);       // s * L + i
+    const int c4 = (int)(e % (kD / 4)) * 4;
+    const long s = row / L;
+    const int c = min(max(assign[row], 0), Kc - 1);   // clamp a caller's bad index
+    const float4 gv = load4<float>(vcent + (s * Kc + c) * kD + c4);
+    const float4 lv = load4<float>(oloc + row * kD + c4);
+    const float wg = 1.0f - alpha;
+    float4 v;
+    v.x = wg * gv.x + alpha * lv.x;
+    v.y = wg * gv.y + alpha * lv.y;
+    v.z = wg * gv.z + alpha * lv.z;
+    v.w = wg * gv.w + alpha * lv.w;
+    store4<T>(out + row * kD + c4, v);
+}
+
+template <typename T>
+static hipError_t local_dispatch(const void *Q, const void *K, const void *V, int S, int L, int W,
+                                 const float *vcent, const int32_t *assign, int Kc, float alpha,
+                                 void *out, float *oloc, hipStream_t st) {
+    const int ntile = (L + kQTile - 1) / kQTile;
+    const int r = W / 2;
+    const dim3 grid((unsigned)((long)S * ntile)), block(256);
+    const T *q = static_cast<const T *>(Q);
+    const T *k = static_cast<const T *>(K);
+    const T *v = static_cast<const T *>(V);
+    if (oloc == nullptr)
+        hipLaunchKernelGGL((local_window_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, ntile,
+                           vcent, assign, Kc, alpha, static_cast<T *>(out), oloc);
+    else
+        hipLaunchKernelGGL((local_window_kernel<T, false>), grid, block, 0, st, q, k, v, L, r,
+                           ntile, vcent, assign, Kc, alpha, static_cast<T *>(out), oloc);
+    return hipGetLastError();
+}
+
+hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
+                               ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
+                               float alpha, void *out, float *oloc, hipStream_t st) {
+    if (dt == CA_BF16)
+        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, out, oloc, st);
+    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, out, oloc, st);
+}
+
+hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
+                              int L, int Kc, float alpha, ca_dtype_t dt, void *out,
+                              hipStream_t st) {
+    const long total4 = (long)S * L * (kD / 4);
+    const dim3 grid((unsigned)((total4 + 255) / 256)), block(256);
+    if (dt == CA_BF16)
+        hipLaunchKernelGGL(gather_fuse_kernel<bf16_t>, grid, block, 0, st, vcent, assign, oloc, L,
+                           Kc, alpha, total4, static_cast<bf16_t *>(out));
+    else
+        hipLaunchKernelGGL(gather_fuse_kernel<float>, grid, block, 0, st, vcent, assign, oloc, L,
+                           Kc, alpha, total4, static_cast<float *>(out));
+    return hipGetLastError();
+}
+
+}  // namespace ca

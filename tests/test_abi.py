@@ -1,0 +1,106 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments on the host (before any
+launch), with the documented status codes. Pointers here are fake, aligned
+addresses: every call below must fail validation and never touch them."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from means_token_clustering_amd import binding as b
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "clusterattn.h")
+
+INV, UNS = b.CA_ERR_INVALID_ARG, b.CA_ERR_UNSUPPORTED
+
+# distinct, non-overlapping, 256-aligned fake device addresses
+Q, K, V, OUT, ASG, WS = (0x10000000 * (i + 1) for i in range(6))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:ca|cluster_attn)_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = b.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in b.SIGNATURES, name
+
+
+def test_status_strings():
+    assert b.status_string(b.CA_OK) == "ok"
+    assert b.status_string(INV) == "invalid argument"
+    assert b.status_string(UNS).startswith("unsupported")
+    assert b.status_string(b.CA_ERR_HIP).startswith("HIP")
+    assert b.lib().ca_version() >= 100
+
+
+def fwd(**kw):
+    a = dict(Q=Q, K=K, V=V, B=2, H=3, L=128, d=64, nclust=16, iters=3, W=32, alpha=0.5,
+             out=OUT, assign=ASG, dt=b.CA_F32, ws=WS, wsb=1 << 30, path=b.CA_PATH_STAGED)
+    a.update(kw)
+    return b.lib().cluster_attn_forward_ex(a["Q"], a["K"], a["V"], a["B"], a["H"], a["L"], a["d"],
+                                           a["nclust"], a["iters"], a["W"], a["alpha"], a["out"],
+                                           a["assign"], a["dt"], a["ws"], a["wsb"], a["path"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(K=None), INV), (dict(V=None), INV), (dict(out=None), INV),
+    (dict(B=0), INV), (dict(H=-1), INV), (dict(L=0), INV), (dict(d=0), INV),
+    (dict(nclust=0), INV), (dict(iters=0), INV), (dict(W=-1), INV),
+    (dict(alpha=-0.1), INV), (dict(alpha=1.5), INV), (dict(alpha=float("nan")), INV),
+    (dict(dt=7), INV), (dict(path=9), INV),
+    (dict(Q=Q + 4), INV), (dict(out=OUT + 8), INV), (dict(assign=ASG + 2), INV),
+    (dict(out=Q), INV), (dict(out=K + 1024), INV), (dict(assign=OUT + 4096), INV),
+    (dict(ws=None), INV), (dict(wsb=16), INV), (dict(ws=WS + 16), INV), (dict(ws=OUT), INV),
+    (dict(d=32), UNS), (dict(d=128), UNS), (dict(nclust=300, L=400), UNS),
+    (dict(B=1 << 12, H=1 << 8, L=4096), UNS), (dict(B=1 << 16, H=1 << 10, L=4096), INV),
+])
+def test_forward_rejects(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_fused_path_unsupported_shapes():
+    # the single-launch path only takes short sequences
+    assert fwd(path=b.CA_PATH_FUSED, L=5000) == UNS
+
+
+def test_workspace_sizes():
+    lib = b.lib()
+    staged = b.cluster_attn_workspace_size(32, 12, 128, 64, 16, b.CA_F32, b.CA_PATH_STAGED)
+    assert staged > 0 and staged % 256 == 0
+    assert b.cluster_attn_workspace_size(1, 12, 8192, 64, 64, b.CA_F32, b.CA_PATH_STAGED) > 0
+    assert b.cluster_attn_workspace_size(1, 1, 128, 32, 16) == 0          # unsupported d
+    assert lib.ca_centroid_update_workspace_size(4, 100, 64, 8) > 0
+    assert lib.ca_centroid_xattn_workspace_size(4, 128, 64, 8) == 0        # one key range
+    assert lib.ca_centroid_xattn_workspace_size(4, 8192, 64, 8) > 0
+
+
+def test_step_entry_points_reject():
+    lib = b.lib()
+    assert lib.ca_kmeans_assign(None, None, 1, 8, 64, 2, 0, ASG, None) == INV
+    assert lib.ca_kmeans_assign(Q, None, 1, 8, 64, 9, 0, ASG, None) == INV   # init needs Kc <= L
+    assert lib.ca_kmeans_assign(Q, None, 1, 8, 64, 300, 0, ASG, None) == UNS
+    assert lib.ca_kmeans_assign(Q, None, 1, 8, 48, 2, 0, ASG, None) == UNS
+    assert lib.ca_centroid_update(Q, ASG, 1, 8, 64, 2, 0, OUT, None, None, 0, None) == INV
+    assert lib.ca_centroid_update(Q, ASG, 1, 8, 64, 2, 0, OUT, None, WS, 1, None) == INV
+    assert lib.ca_centroid_xattn(None, K, V, 1, 8, 64, 2, 0, OUT, None, 0, None) == INV
+    assert lib.ca_local_window_attn(Q, K, V, 1, 8, 64, -2, 0, OUT, None) == INV
+    assert lib.ca_gather_fuse(Q, ASG, V, 1, 8, 64, 2, 2.0, 0, OUT, None) == INV
+    assert lib.ca_gather_fuse(Q, ASG, V, 1, 8, 64, 2, 0.5, 5, OUT, None) == INV
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        b.cluster_attn_forward(x, x, x, 2, 1, 4, 0.5, path=b.CA_PATH_STAGED,
+                               out=torch.zeros(1, 1, 8, 64), assign_out=None, want_assign=False,
+                               workspace=None)

@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle.
+
+Every test here needs an MI355X and the built library; run with -m gpu.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from means_token_clustering_amd import inputs as gen
+from tests import parity
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+def _b():
+    from means_token_clustering_amd import binding
+    return binding
+
+
+def _dev(a: np.ndarray, dtype: str):
+    if dtype == gen.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _host(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_iters(x: gen.AttnInputs, path: int):
+    """GPU assignments for iters = 1..I and the output of the full run."""
+    b = _b()
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    assigns = []
+    out = None
+    for t in range(1, x.iters + 1):
+        o, c = b.cluster_attn_forward(q, k, v, x.nclust, t, x.W, x.alpha, path=path)
+        assigns.append(c.cpu().numpy())
+        out = o
+    torch.cuda.synchronize()
+    return assigns, _host(out), (q, k, v)
+
+
+def check(x: gen.AttnInputs, path: int, tol=None):
+    _say(f"[parity] {x.name or 'case'} B={x.B} H={x.H} L={x.L} K={x.nclust} I={x.iters} "
+         f"W={x.W} a={x.alpha} {x.dtype} seed={x.seed} path={path}")
+    assigns, out, _ = run_iters(x, path)
+    reports, err, tol, ref = parity.check_forward(
+        x.values("q"), x.values("k"), x.values("v"), x.nclust, x.iters, x.W, x.alpha, x.dtype,
+        assigns, out, tol)
+    _say(f"  {parity.summarize(reports)}; max|out-ref|={err:.3e} (tol {tol})")
+    for r in reports:
+        assert r.bad == 0, parity.summarize(reports)
+    assert err <= tol
+    return assigns, out, ref
+
+
+PATHS = [0, 2]   # auto, staged
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("name", ["tiny", "distilbert", "bf16_l512", "long_l8192"])
+def test_workloads(name, path):
+    check(gen.workload(name), path)
+
+
+@pytest.mark.parametrize("seed", range(101, 117))
+def test_tiny_seed_sweep(seed):
+    check(gen.workload("tiny", seed=seed), 0)
+
+
+EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
+    (1, 1, 1, 16, 2, 32, 0.5, "f32", None),       # single token
+    (2, 3, 65, 16, 3, 32, 0.5, "f32", 4),          # one full tile + ragged
+    (1, 2, 200, 16, 3, 32, 0.5, "bf16", 8),        # several tiles, ragged tail
+    (2, 2, 130, 7, 4, 17, 0.3, "f32", 5),          # odd W, K not dividing L
+    (1, 2, 40, 64, 2, 10, 0.5, "f32", None),       # nclust > L: K = L
+    (1, 3, 96, 1, 3, 8, 0.5, "f32", 3),            # single cluster
+    (1, 2, 150, 16, 3, 0, 0.5, "f32", 6),          # W = 0: self only
+    (1, 2, 150, 16, 3, 1, 0.5, "bf16", 6),         # W = 1: radius 0
+    (1, 2, 150, 16, 3, 400, 0.5, "f32", 6),        # W >= 2L: dense local branch
+    (1, 2, 128, 16, 3, 32, 0.0, "f32", 6),         # pure centroid branch
+    (1, 2, 128, 16, 3, 32, 1.0, "f32", 6),         # pure local branch
+    (1, 1, 300, 256, 2, 32, 0.5, "f32", 40),       # maximum cluster count
+    (3, 5, 128, 16, 3, 32, 0.5, "bf16", 16),       # more slices
+    (1, 1, 1100, 32, 3, 64, 0.5, "f32", 32),       # split-key centroid attention
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", EDGE)
+def test_edge_cases(case, path):
+    B, H, L, nclust, iters, W, alpha, dtype, blobs = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
+                        dtype=dtype, seed=1000 + L + W, blobs=blobs, name="edge")
+    check(x, path)
+
+
+def test_empty_cluster_and_exact_ties():
+    """L=8, K=2, Q[4] = Q[0]: identical initial centroids tie exactly, so all
+    tokens take cluster 0; cluster 1 becomes the zero vector; at iteration 2
+    token i joins cluster 1 iff q_i . m < ||m||^2 / 2 (m = mean query)."""
+    rng = np.random.default_rng(4)
+    Q = rng.standard_normal((1, 1, 8, 64)).astype(np.float32) + 0.5
+    Q[0, 0, 4] = Q[0, 0, 0]
+    Kt = rng.standard_normal((1, 1, 8, 64)).astype(np.float32)
+    V = rng.standard_normal((1, 1, 8, 64)).astype(np.float32)
+    b = _b()
+    q, k, v = _dev(Q, "f32"), _dev(Kt, "f32"), _dev(V, "f32")
+    for path in PATHS:
+        _, c1 = b.cluster_attn_forward(q, k, v, 2, 1, 4, 0.5, path=path)
+        out, c2 = b.cluster_attn_forward(q, k, v, 2, 2, 4, 0.5, path=path)
+        assert c1.cpu().numpy().ravel().tolist() == [0] * 8
+        Qd = Q[0, 0].astype(np.float64)
+        m = Qd.mean(axis=0)
+        want = [1 if float(qq @ m) < float(m @ m) / 2 else 0 for qq in Qd]
+        assert c2.cpu().numpy().ravel().tolist() == want
+        ref = oracle.forward_from_assign(Q.astype(np.float64), Kt.astype(np.float64),
+                                         V.astype(np.float64), c2.cpu().numpy(), 2, 4, 0.5)
+        assert np.abs(_host(out) - ref["out"]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_determinism_and_slice_independence(path):
+    x = gen.make_inputs(2, 3, 160, 64, nclust=16, iters=3, W=32, alpha=0.5, seed=21, blobs=8)
+    b = _b()
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    o1, c1 = b.cluster_attn_forward(q, k, v, 16, 3, 32, 0.5, path=path)
+    o2, c2 = b.cluster_attn_forward(q, k, v, 16, 3, 32, 0.5, path=path)
+    assert torch.equal(o1, o2) and torch.equal(c1, c2)
+    # duplicate heads in a permuted order: outputs follow bitwise
+    perm = [2, 0, 1]
+    qq, kk, vv = (torch.cat([t, t[:, perm]], dim=1).contiguous() for t in (q, k, v))
+    o3, c3 = b.cluster_attn_forward(qq, kk, vv, 16, 3, 32, 0.5, path=path)
+    assert torch.equal(o3[:, :3], o1) and torch.equal(o3[:, 3:], o1[:, perm])
+    assert torch.equal(c3[:, 3:], c1[:, perm])
+
+
+def test_alpha_is_convex_weight():
+    x = gen.make_inputs(1, 4, 128, 64, nclust=16, iters=3, W=32, seed=22, blobs=16)
+    b = _b()
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    outs = {a: _host(b.cluster_attn_forward(q, k, v, 16, 3, 32, a)[0]) for a in (0.0, 0.5, 1.0)}
+    assert np.abs(outs[0.5] - 0.5 * (outs[0.0] + outs[1.0])).max() <= 1e-6
+
+
+# ------------------------------------------------------------ single steps
+def test_step_assign_and_update():
+    x = gen.make_inputs(2, 3, 200, 64, nclust=12, seed=31, blobs=10, dtype="bf16")
+    b = _b()
+    q = _dev(x.q, x.dtype)
+    Qd = x.values("q")
+    # strided init (mu = NULL)
+    c0 = b.ca_kmeans_assign(q, None, 12).cpu().numpy()
+    mu0 = oracle.init_centroids(Qd, 12)
+    r = parity.check_assignment_step(Qd, mu0, c0, 1)
+    assert r.bad == 0, r
+    # update from that assignment, then assign against the GPU centroids
+    mu_g, cnt_g = b.ca_centroid_update(q, torch.from_numpy(c0).cuda(), 12)
+    mu_o, cnt_o = oracle.update(Qd, c0, 12)
+    assert np.array_equal(cnt_g.cpu().numpy(), cnt_o)
+    assert np.abs(mu_g.cpu().numpy() - mu_o).max() <= 1e-5
+    c1 = b.ca_kmeans_assign(q, mu_g, 12).cpu().numpy()
+    r = parity.check_assignment_step(Qd, mu_g.cpu().numpy().astype(np.float64), c1, 2)
+    assert r.bad == 0, r
+
+
+@pytest.mark.parametrize("L", [128, 1100])
+def test_step_xattn_local_fuse(L):
+    x = gen.make_inputs(1, 3, L, 64, nclust=16, seed=32 + L, blobs=8)
+    b = _b()
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    Qd, Kd, Vd = x.values("q"), x.values("k"), x.values("v")
+    mu = oracle.init_centroids(Qd, 16).astype(np.float32)
+    vc = b.ca_centroid_xattn(torch.from_numpy(mu).cuda(), k, v).cpu().numpy()
+    vc_o, _ = oracle.centroid_xattn(mu.astype(np.float64), Kd, Vd)
+    assert np.abs(vc - vc_o).max() <= 1e-5
+    for W in (0, 5, 32, 3 * L):
+        ol = b.ca_local_window_attn(q, k, v, W).cpu().numpy()
+        ol_o, _ = oracle.local_attn(Qd, Kd, Vd, W)
+        assert np.abs(ol - ol_o).max() <= 1e-5, W
+    c = np.random.default_rng(0).integers(0, 16, size=(1, 3, L)).astype(np.int32)
+    ol = b.ca_local_window_attn(q, k, v, 32)
+    out = b.ca_gather_fuse(torch.from_numpy(vc).cuda(), torch.from_numpy(c).cuda(), ol, 0.25,
+                           torch.float32)
+    want = oracle.fuse(vc.astype(np.float64), c, ol.cpu().numpy().astype(np.float64), 0.25)
+    assert np.abs(_host(out) - want).max() <= 1e-6
