@@ -1,0 +1,150 @@
+"""Benchmark: cluster-attention forward throughput on one MI355X.
+
+A step is one whole forward pass (k-means, centroid cross-attention, local
+window branch, gather + fusion) over one batch of the DistilBERT-shaped
+workload: B=32, H=12, L=128, d=64, K=16 clusters, 3 Lloyd iterations,
+W=32, alpha=0.5, fp32 (queries from a 16-blob Gaussian mixture, keys and
+values N(0,1)). Inputs are resident in HBM before timing starts; input/output
+sets rotate so the working set exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line with throughput (tokens/s = B*L per second, all heads),
+the roofline record of the dominant kernel and the CPU-oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "cluster-attention fwd tokens/s (B·L per s, all heads) + % HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MALL_BYTES = 256 << 20         # Infinity Cache
+
+
+def algorithmic_bytes(B, H, L, d, elem) -> int:
+    """Read Q, K, V once; write the output and the int32 assignment."""
+    return 4 * B * H * L * d * elem + 4 * B * H * L
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="distilbert",
+                   choices=["tiny", "distilbert", "bf16_l512", "long_l8192"])
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
+    p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0 = auto)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of the CPU-oracle baseline (0 disables it)")
+    return p.parse_args()
+
+
+def cpu_baseline(x, seconds: float):
+    import oracle
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False)   # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    tokens = x.B * x.L * reps
+    return {"value": tokens / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}) run {reps} times "
+                      f"back to back, {el:.1f} s, fp64 C oracle with OpenMP over slices"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the slices are "
+              "independent, so more GPUs would each run their own batch share.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from means_token_clustering_amd import binding as b
+    from means_token_clustering_amd import inputs as gen
+
+    x = gen.workload(args.workload)
+    elem = 2 if x.dtype == gen.BF16 else 4
+    path = {"auto": b.CA_PATH_AUTO, "fused": b.CA_PATH_FUSED, "staged": b.CA_PATH_STAGED}[args.path]
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if x.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    set_bytes = algorithmic_bytes(x.B, x.H, x.L, x.d, elem)
+    nsets = args.sets or max(2, MALL_BYTES // set_bytes + 2)
+    base = [to_dev(getattr(x, n)) for n in ("q", "k", "v")]
+    sets = []
+    for _ in range(nsets):
+        q, k, v = (t.clone() for t in base)
+        sets.append((q, k, v, torch.empty_like(q),
+                     torch.empty((x.B, x.H, x.L), dtype=torch.int32, device=dev)))
+    ws_bytes = b.cluster_attn_workspace_size(x.B, x.H, x.L, x.d, x.nclust,
+                                             b.CA_BF16 if elem == 2 else b.CA_F32, path)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev) if ws_bytes else None
+    lib = b.lib()
+    dt = b.CA_BF16 if elem == 2 else b.CA_F32
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    wsp = b._aligned_ptr(ws)
+    wsn = b._ws_bytes(ws)
+
+    def step(i):
+        q, k, v, o, c = sets[i % nsets]
+        st = lib.cluster_attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), x.B, x.H, x.L,
+                                         x.d, x.nclust, x.iters, x.W, float(x.alpha),
+                                         o.data_ptr(), c.data_ptr(), dt, wsp, wsn, path, sptr)
+        if st != b.CA_OK:
+            raise b.CaError(st, "cluster_attn_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tokens = x.B * x.L
+    value = tokens / (ms / 1e3)
+
+    # the hot path is one kernel launch per step on the fused path; on the
+    # staged path the roofline record covers the whole launch sequence
+    fused = ws_bytes == 0
+    achieved = set_bytes / (ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "cluster_attn_fused_kernel" if fused else "staged sequence (7+ launches)",
+            "bytes_per_launch": set_bytes}
+    rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
+           "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d, "K": x.nclust,
+                      "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
+                      "path": "fused" if fused else "staged", "input_sets": nsets},
+           "roofline": roof}
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
