@@ -59,8 +59,9 @@ typedef enum {
 typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype_t;
 
 /* Execution strategy of cluster_attn_forward_ex. AUTO picks FUSED when the
- * shape allows it (L <= 128), else STAGED. FUSED: one launch, one workgroup
- * per slice, the whole slice staged in LDS. STAGED: one kernel per step. */
+ * shape allows it (L <= 128 and min(nclust, L) <= 16), else STAGED. FUSED:
+ * one launch, one workgroup per slice, the whole slice on chip. STAGED: one
+ * kernel per step, any supported shape. */
 typedef enum { CA_PATH_AUTO = 0, CA_PATH_FUSED = 1, CA_PATH_STAGED = 2 } ca_path_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
