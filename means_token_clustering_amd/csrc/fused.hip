@@ -1,8 +1,10 @@
 // Single-launch cluster attention forward for short sequences (L <= 128,
-// K <= 16, d = 64). Each workgroup (512 threads, 8 waves) runs the whole path
+// K <= 16, d = 64). One workgroup (512 threads, 8 waves) runs the whole path
 // of one (b, h) slice on chip - Lloyd's k-means, centroid cross-attention,
 // the local window branch and the gather + convex fusion - and touches HBM
 // only to read Q, K, V once and to write the output and the assignment.
+// The LDS footprint (80,000 B) lets two slices share a CU, so one slice's
+// loads overlap another's arithmetic.
 //
 // Method: model card "Hooshaai/distilbert-sst2-cluster-attention",
 // Architecture Overview figure and Mathematical Formulation 1; "ClusterFormer"
@@ -10,31 +12,41 @@
 // staged kernels: ties to the lowest cluster, empty cluster -> zero vector,
 // window |i - j| <= floor(W/2), scale 1/sqrt(d).
 //
-// Arithmetic: every contraction runs on the bf16 matrix cores
-// (v_mfma_f32_16x16x32_bf16 / 16x16x16) with fp32 accumulation. Each fp32
-// operand x is split exactly into three bf16 parts x = h + m + l (truncation:
-// h keeps the top 8 significand bits, m the next 8, l the last 8), and a
-// product a.b is accumulated from the six partial products whose weight is
-// at least 2^-16 of the leading one (l.h, h.l, m.m, m.h, h.m, h.h), which
-// leaves a relative error of order 2^-24, i.e. fp32 grade. The one-hot
-// products (centroid sums and counts) need three and one (exact 0/1 side).
+// Arithmetic. Every contraction runs on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation). Each operand tensor of a
+// slice is first scaled by a power of two 2^-s (exact) so that its largest
+// magnitude is below 2^15; each scaled fp32 value x is then split into two
+// fp16 parts x = h + m + e (h = x rounded toward zero to fp16, m = the
+// remainder x - h, exact in fp32, rounded toward zero to fp16), which leaves
+// |e| <= 2^-21 |x| (2^-24 absolute below the fp16 normal range). A product
+// a.b accumulates h.h, h.m and m.h: relative error of order 2^-20, absolute
+// error far below the tolerances of the outputs and below the near-tie
+// margin of the distance comparisons. Products with an exact 0/1 operand
+// (one-hot cluster sums, counts) are exact up to fp32 accumulation. The
+// scale factors are undone on the fp32 results (scores, outputs); distances
+// stay in the scaled units of Q, which leaves every comparison unchanged.
 //
 // Layouts (confirmed on gfx950): for 16x16x32, lane l holds A[l%16][8(l/16)+i]
 // and B[8(l/16)+i][l%16], i = 0..7; the 16x16 result has lane l, register r
-// at D[4(l/16)+r][l%16]. 16x16x16 is the same with 4 values per lane.
+// at D[4(l/16)+r][l%16]. Write l16 = l%16 and g = l/16.
 //
-// Work split per slice (token tile = 16 tokens, NT = ceil(L/16) <= 8):
-//   wave w owns token tile w: its Q fragments stay in registers for the
-//   distance products and the local-window scores; waves 0-3 own dim tile w
-//   of the centroid sums (one-hot^T Q) and keep Q in that layout too;
-//   K and V live in LDS as split planes (V transposed) for all waves.
+// Work split per slice (tile = 16 tokens, NT = ceil(L/16) <= 8):
+//   every wave w < NT: the distances of token tile w (its Q fragments stay in
+//     registers) and the centroid-key scores of key tile w;
+//   waves 0-3: the cluster sums of dim tile w (Q kept in the token-depth
+//     layout) and the centroid context of dim tile w;
+//   waves 4-7: the local window branch of query tiles w-4 and w, run while
+//     waves 0-3 update centroids in the first two iterations (the branch does
+//     not depend on the clustering), and the final gather + fusion of those
+//     tiles.
+//   K and V^T live in LDS as fp16 planes (16-byte chunks XOR-swizzled by the
+//   row against bank conflicts).
 #include "common.h"
 
 namespace ca {
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -42,175 +54,125 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kFL = 128;              // max tokens
 constexpr int kFK = 16;               // max clusters
 constexpr int kThreads = 512;         // 8 waves
-constexpr int kKRow = 72;             // K / centroid plane row stride in bf16 (64 + 8)
-constexpr int kVRow = 136;            // V^T plane row stride in bf16 (128 + 8)
-constexpr int kKPlane = kFL * kKRow;  // bf16 elements per K plane
-constexpr int kVPlane = kD * kVRow;   // bf16 elements per V^T plane
-constexpr int kMuPlane = kFK * kKRow; // bf16 elements per centroid plane
-constexpr int kMuRow = 68;            // fp32 row stride of mu and vcent
-constexpr int kPartW = kD * kFK;      // fp32 partial V^cent per wave
 
-constexpr size_t kLdsK = sizeof(uint16_t) * 3 * kKPlane;
-constexpr size_t kLdsV = sizeof(uint16_t) * 3 * kVPlane;
-constexpr size_t kLdsMuP = sizeof(uint16_t) * 3 * kMuPlane;
-constexpr size_t kLdsMu = sizeof(float) * kFK * kMuRow;
-constexpr size_t kLdsPart = sizeof(float) * 8 * kPartW;
-// wave maxima [16][8], wave sums [16][8], ||mu||^2 partials [4][16], assignment [128]
-constexpr size_t kLdsSmall = sizeof(float) * (2 * kFK * 8 + 4 * kFK) + sizeof(int) * kFL;
-constexpr size_t kLdsTotal = kLdsK + kLdsV + kLdsMuP + 2 * kLdsMu + kLdsPart + kLdsSmall;
-static_assert(kLdsTotal <= 160 * 1024, "LDS budget");
+// LDS map (bytes)
+constexpr int kPlaneK = kFL * kD * 2;         // one fp16 plane of K: [128 keys][64 dims]
+constexpr int kPlaneV = kD * kFL * 2;         // one fp16 plane of V^T: [64 dims][128 keys]
+constexpr int kPlaneMu = kFK * kD * 2;        // one fp16 plane of mu: [16][64]
+constexpr int kPlaneRow128 = kFK * kFL * 2;   // [16][128] fp16 (one-hot, P)
+constexpr int kOffK = 0;
+constexpr int kOffV = kOffK + 2 * kPlaneK;
+constexpr int kOffR = kOffV + 2 * kPlaneV;    // shared region: mu planes + one-hot, later P planes
+constexpr int kOffMuP = kOffR;
+constexpr int kOffOH = kOffR + 2 * kPlaneMu;
+constexpr int kOffP = kOffR;
+constexpr int kSizeR = 2 * kPlaneRow128;
+constexpr int kOffVc = kOffR + kSizeR;        // fp32 V^cent [16][68]
+constexpr int kVcRow = 68;
+constexpr int kOffXm = kOffVc + kFK * kVcRow * 4;   // fp32 [16][8] wave maxima
+constexpr int kOffXl = kOffXm + kFK * 8 * 4;        // fp32 [16][8] wave sums
+constexpr int kOffN2 = kOffXl + kFK * 8 * 4;        // fp32 [4][16] partial ||mu||^2
+constexpr int kOffC = kOffN2 + 4 * kFK * 4;         // int [128] assignment
+constexpr int kOffMax = kOffC + kFL * 4;            // uint [8][4] max |x| bits
+constexpr int kLdsTotal = kOffMax + 8 * 4 * 4;
+static_assert(2 * kPlaneMu + kPlaneRow128 <= kSizeR, "region R");
+static_assert(kLdsTotal <= 81920, "two workgroups per CU");
 
-struct Split8 {  // 8 values as three bf16x8 planes (pairs packed low-first)
-    u32x4_t h, m, l;
+struct Sp8 {  // 8 values as two fp16 planes (pairs packed low-first)
+    u32x4_t h, m;
 };
-struct Split4 {  // 4 values as three bf16x4 planes
-    u32x2_t h, m, l;
-};
 
-__device__ __forceinline__ uint32_t pack_hi(uint32_t lo_elem, uint32_t hi_elem) {
-    return (lo_elem >> 16) | (hi_elem & 0xffff0000u);
+// x0, x1 -> packed fp16 pairs h and m with x = h + m + e
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m) {
+    const auto a = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+    const float r0 = x0 - (float)a[0];
+    const float r1 = x1 - (float)a[1];
+    const auto b = __builtin_amdgcn_cvt_pkrtz(r0, r1);
+    h = __builtin_bit_cast(uint32_t, a);
+    m = __builtin_bit_cast(uint32_t, b);
 }
 
-// Exact split of two floats: x = h + m + l, each part a bf16 (truncation).
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m, uint32_t &l) {
-    const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
-    h = pack_hi(u0, u1);
-    const float r0 = x0 - __uint_as_float(u0 & 0xffff0000u);
-    const float r1 = x1 - __uint_as_float(u1 & 0xffff0000u);
-    const uint32_t v0 = __float_as_uint(r0), v1 = __float_as_uint(r1);
-    m = pack_hi(v0, v1);
-    const float s0 = r0 - __uint_as_float(v0 & 0xffff0000u);
-    const float s1 = r1 - __uint_as_float(v1 & 0xffff0000u);
-    l = pack_hi(__float_as_uint(s0), __float_as_uint(s1));
-}
-
-__device__ __forceinline__ Split8 split8(const float *x) {
-    uint32_t h[4], m[4], l[4];
+__device__ __forceinline__ Sp8 split8(const float *x) {
+    uint32_t h[4], m[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i], l[i]);
-    Split8 s;
-    s.h = u32x4_t{h[0], h[1], h[2], h[3]};
-    s.m = u32x4_t{m[0], m[1], m[2], m[3]};
-    s.l = u32x4_t{l[0], l[1], l[2], l[3]};
-    return s;
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
+    return Sp8{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{m[0], m[1], m[2], m[3]}};
 }
 
-__device__ __forceinline__ Split4 split4(const float *x) {
-    uint32_t h[2], m[2], l[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i], l[i]);
-    Split4 s;
-    s.h = u32x2_t{h[0], h[1]};
-    s.m = u32x2_t{m[0], m[1]};
-    s.l = u32x2_t{l[0], l[1]};
-    return s;
+__device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4_t mma32(u32x4_t a, u32x4_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4_t mma16(u32x2_t a, u32x2_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
-}
-
-// c += a . b to fp32 grade (six partial products, smallest first)
-__device__ __forceinline__ f32x4_t mma32x6(const Split8 &a, const Split8 &b, f32x4_t c) {
-    c = mma32(a.l, b.h, c);
-    c = mma32(a.h, b.l, c);
-    c = mma32(a.m, b.m, c);
-    c = mma32(a.m, b.h, c);
-    c = mma32(a.h, b.m, c);
-    c = mma32(a.h, b.h, c);
+// c += a . b from the three leading partial products (smallest first)
+__device__ __forceinline__ f32x4_t mma3(const Sp8 &a, const Sp8 &b, f32x4_t c) {
+    c = mma(a.m, b.h, c);
+    c = mma(a.h, b.m, c);
+    c = mma(a.h, b.h, c);
     return c;
 }
 
-__device__ __forceinline__ f32x4_t mma16x6(const Split4 &a, const Split4 &b, f32x4_t c) {
-    c = mma16(a.l, b.h, c);
-    c = mma16(a.h, b.l, c);
-    c = mma16(a.m, b.m, c);
-    c = mma16(a.m, b.h, c);
-    c = mma16(a.h, b.m, c);
-    c = mma16(a.h, b.h, c);
-    return c;
-}
-
-__device__ __forceinline__ f32x4_t add4(f32x4_t a, f32x4_t b) {
-    return f32x4_t{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
-}
+constexpr f32x4_t kZero4 = {0.f, 0.f, 0.f, 0.f};
 
 // ---- cross-lane helpers (no LDS traffic)
-// Combine lane l with lane l^32 (resp. l^16): both lanes receive the two
-// values, the lower lane's first, in the same order.
-__device__ __forceinline__ void pair32(float v, float &lo, float &hi) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
+// lanes l and l^32 (resp. l^16) both receive (lower lane value, upper lane value)
+__device__ __forceinline__ void pair32(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
 }
-__device__ __forceinline__ void pair16(float v, float &lo, float &hi) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
+__device__ __forceinline__ void pair16(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    lo = r[0];
+    hi = r[1];
 }
-__device__ __forceinline__ void pair32i(int v, int &lo, int &hi) {
-    const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-    lo = (int)r[0];
-    hi = (int)r[1];
-}
-__device__ __forceinline__ void pair16i(int v, int &lo, int &hi) {
-    const auto r = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-    lo = (int)r[0];
-    hi = (int)r[1];
-}
-
-// sum / max over the four lane groups g of a column (lanes l16, l16+16, ...);
-// every lane of the column gets the same bits
+// sum / max over the four lane groups g of a column; every lane of the
+// column gets the same bits
 __device__ __forceinline__ float col_sum(float v) {
-    float a, b;
-    pair16(v, a, b);
-    v = a + b;
-    pair32(v, a, b);
-    return a + b;
+    uint32_t a, b;
+    pair16(__float_as_uint(v), a, b);
+    v = __uint_as_float(a) + __uint_as_float(b);
+    pair32(__float_as_uint(v), a, b);
+    return __uint_as_float(a) + __uint_as_float(b);
 }
 __device__ __forceinline__ float col_max(float v) {
-    float a, b;
-    pair16(v, a, b);
-    v = fmaxf(a, b);
-    pair32(v, a, b);
-    return fmaxf(a, b);
+    uint32_t a, b;
+    pair16(__float_as_uint(v), a, b);
+    v = fmaxf(__uint_as_float(a), __uint_as_float(b));
+    pair32(__float_as_uint(v), a, b);
+    return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
-
 // lexicographic (value, index) minimum over the four lane groups of a column
 __device__ __forceinline__ void col_argmin(float &best, int &bk) {
-    float a, b;
-    int ia, ib;
-    pair16(best, a, b);
-    pair16i(bk, ia, ib);
-    if (lex_less(b, ib, a, ia)) { a = b; ia = ib; }
-    pair32(a, best, b);
-    pair32i(ia, bk, ib);
-    if (lex_less(b, ib, best, bk)) { best = b; bk = ib; }
+    uint32_t a, b, ia, ib;
+    pair16(__float_as_uint(best), a, b);
+    pair16((uint32_t)bk, ia, ib);
+    float fa = __uint_as_float(a), fb = __uint_as_float(b);
+    int ka = (int)ia, kb = (int)ib;
+    if (lex_less(fb, kb, fa, ka)) { fa = fb; ka = kb; }
+    pair32(__float_as_uint(fa), a, b);
+    pair32((uint32_t)ka, ia, ib);
+    fa = __uint_as_float(a); fb = __uint_as_float(b);
+    ka = (int)ia; kb = (int)ib;
+    if (lex_less(fb, kb, fa, ka)) { fa = fb; ka = kb; }
+    best = fa;
+    bk = ka;
 }
-
-// DPP move within a row of 16 lanes
+// maximum of an unsigned value over the whole wave
 template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
 }
-constexpr int kDppXor1 = 0xB1;    // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;    // quad_perm [2,3,0,1]
-constexpr int kDppRor4 = 0x124;   // row_ror:4
-constexpr int kDppRor8 = 0x128;   // row_ror:8
-
-// sum over the 16 lanes of a row; lane l16 == 0 holds a fixed-order total
-__device__ __forceinline__ float row_sum(float v) {
-    v += dpp<kDppXor1>(v);
-    v += dpp<kDppXor2>(v);
-    v += dpp<kDppRor4>(v);
-    v += dpp<kDppRor8>(v);
-    return v;
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+    v = max(v, dpp_u<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp_u<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max(v, dpp_u<0x124>(v));   // row_ror:4
+    v = max(v, dpp_u<0x128>(v));   // row_ror:8
+    uint32_t a, b;
+    pair16(v, a, b);
+    v = max(a, b);
+    pair32(v, a, b);
+    return max(a, b);
 }
 
 // ---- storage access
@@ -220,7 +182,6 @@ __device__ __forceinline__ void load8(const T *p, float *x) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
-
 template <typename T>
 __device__ __forceinline__ float load1(const T *p);
 template <>
@@ -242,7 +203,6 @@ __device__ __forceinline__ void load_row8(const T *base, int row, int L, int col
         }
     }
 }
-
 // rows r0..r0+7 of column `col` (zeros for rows >= L)
 template <typename T, bool FULL>
 __device__ __forceinline__ void load_col8(const T *base, int r0, int L, int col, float *x) {
@@ -259,107 +219,198 @@ __device__ __forceinline__ void load_col8(const T *base, int r0, int L, int col,
     }
 }
 
-__device__ __forceinline__ u32x4_t lds_u32x4(const uint16_t *p) {
-    return *reinterpret_cast<const u32x4_t *>(p);
+__device__ __forceinline__ uint32_t absmax8(const float *x, uint32_t m) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+    return m;
 }
-__device__ __forceinline__ u32x2_t lds_u32x2(const uint16_t *p) {
-    return *reinterpret_cast<const u32x2_t *>(p);
-}
-__device__ __forceinline__ void put_split8(uint16_t *dst, int plane, const Split8 &s) {
-    *reinterpret_cast<u32x4_t *>(dst) = s.h;
-    *reinterpret_cast<u32x4_t *>(dst + plane) = s.m;
-    *reinterpret_cast<u32x4_t *>(dst + 2 * plane) = s.l;
-}
-
-// K fragment (rows = keys 16*kt + l16, dims 32c + 8g ..)
-__device__ __forceinline__ Split8 k_frag(const uint16_t *sK, int kt, int c, int l16, int g) {
-    const uint16_t *p = sK + (16 * kt + l16) * kKRow + 32 * c + 8 * g;
-    Split8 s;
-    s.h = lds_u32x4(p);
-    s.m = lds_u32x4(p + kKPlane);
-    s.l = lds_u32x4(p + 2 * kKPlane);
-    return s;
+// power-of-two scale that brings the largest magnitude below 2^15
+__device__ __forceinline__ int scale_shift(uint32_t maxbits) {
+    const int e = (int)(maxbits >> 23) - 127;   // max < 2^(e+1)
+    return e + 1 > 15 ? e + 1 - 15 : 0;
 }
 
-// centroid fragment (rows = centroids l16, dims 32c + 8g ..)
-__device__ __forceinline__ Split8 mu_frag(const uint16_t *sMuP, int c, int l16, int g) {
-    const uint16_t *p = sMuP + l16 * kKRow + 32 * c + 8 * g;
-    Split8 s;
-    s.h = lds_u32x4(p);
-    s.m = lds_u32x4(p + kMuPlane);
-    s.l = lds_u32x4(p + 2 * kMuPlane);
-    return s;
+// ---- swizzled fp16 planes (element offsets). 64-wide rows: 8 chunks of 8
+// elements, chunk index XOR (row & 7); 128-wide rows: 16 chunks, XOR (row & 15).
+__device__ __forceinline__ int off64(int row, int col) {
+    return row * 64 + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+__device__ __forceinline__ int off128(int row, int col) {
+    return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
+}
+__device__ __forceinline__ u32x4_t ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
+__device__ __forceinline__ u32x2_t ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2_t *>(p); }
+__device__ __forceinline__ void st16(uint16_t *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
+__device__ __forceinline__ void st8(uint16_t *p, u32x2_t v) { *reinterpret_cast<u32x2_t *>(p) = v; }
+
+// fragment of a 64-wide plane pair (row `row`, cols 32c + 8g ..)
+__device__ __forceinline__ Sp8 frag64(const uint16_t *planes, int plane, int row, int c, int g) {
+    const int o = off64(row, 32 * c + 8 * g);
+    return Sp8{ld16(planes + o), ld16(planes + plane + o)};
+}
+// fragment of a 128-wide plane pair (row `row`, cols 32c + 8g ..)
+__device__ __forceinline__ Sp8 frag128(const uint16_t *planes, int plane, int row, int c, int g) {
+    const int o = off128(row, 32 * c + 8 * g);
+    return Sp8{ld16(planes + o), ld16(planes + plane + o)};
+}
+// Keys are stored in V^T and P planes in "score-tile order": within each
+// chunk of 32 keys (two key tiles), position 8g + 4h + i holds key
+// 16h + 4g + i (h = tile of the pair, g = lane group, i = 0..3). That is the
+// order in which a 16x16 score tile leaves keys in the registers of lane
+// group g, so a 32-deep product over a tile pair reads one 16-byte run.
+__device__ __forceinline__ int vpos(int key) {
+    const int r = key & 31;
+    return (key & ~31) + (((r & 15) >> 2) << 3) + ((r >> 4) << 2) + (r & 3);
 }
 
-// V^T fragment for 16x16x16 (rows = dims 16j + l16, keys 16kt + 4g + i)
-__device__ __forceinline__ Split4 v_frag_tile(const uint16_t *sV, int j, int kt, int l16, int g) {
-    const uint16_t *p = sV + (16 * j + l16) * kVRow + 16 * kt + 4 * g;
-    Split4 s;
-    s.h = lds_u32x2(p);
-    s.m = lds_u32x2(p + kVPlane);
-    s.l = lds_u32x2(p + 2 * kVPlane);
-    return s;
-}
-
-// V^T fragment over key tiles ka, kb for 16x16x32 in the order the score
-// tiles hold them: lane group g takes keys 16ka + 4g + (0..3), 16kb + 4g + (0..3)
-__device__ __forceinline__ Split8 v_frag_two(const uint16_t *sV, int j, int ka, int kb, int l16,
-                                             int g) {
-    const uint16_t *pa = sV + (16 * j + l16) * kVRow + 16 * ka + 4 * g;
-    const uint16_t *pb = sV + (16 * j + l16) * kVRow + 16 * kb + 4 * g;
-    Split8 s;
-    u32x2_t a, b;
-    a = lds_u32x2(pa);               b = lds_u32x2(pb);
-    s.h = u32x4_t{a.x, a.y, b.x, b.y};
-    a = lds_u32x2(pa + kVPlane);     b = lds_u32x2(pb + kVPlane);
-    s.m = u32x4_t{a.x, a.y, b.x, b.y};
-    a = lds_u32x2(pa + 2 * kVPlane); b = lds_u32x2(pb + 2 * kVPlane);
-    s.l = u32x4_t{a.x, a.y, b.x, b.y};
-    return s;
-}
-
-// store the split of two adjacent dims (d, d+1) of centroid k
-__device__ __forceinline__ void put_mu_pair(uint16_t *sMuP, int k, int d, float x0, float x1) {
-    uint32_t h, m, l;
-    split2(x0, x1, h, m, l);
-    uint16_t *p = sMuP + k * kKRow + d;
-    *reinterpret_cast<uint32_t *>(p) = h;
-    *reinterpret_cast<uint32_t *>(p + kMuPlane) = m;
-    *reinterpret_cast<uint32_t *>(p + 2 * kMuPlane) = l;
-}
-
-// Raw (unsplit) inputs of one slice held by one thread between the fetch and
-// the split: K items (row, 8-dim chunk) and V items (dim, 8-key group) -
-// waves 0-3 take one of each, waves 4-7 three - the thread's Q row chunk
-// pair, and for waves 0-3 the Q column block of the centroid sums.
-struct Raw {
-    float k[3][8];
-    float v[3][8];
-    float q[2][8];
-    float qc[4][8];
+// Local window state of one query tile: scores, then probabilities, of the
+// key tile pairs c0 .. c0 + nch - 1 (tiles 2c, 2c+1), register-resident and
+// statically indexed; keys outside the window get probability 0.
+template <bool NARROW>
+struct LocalTile {
+    static constexpr int kMaxC = NARROW ? 2 : 4;
+    float sc[2 * kMaxC][4];
+    float lsum;
+    int c0, nch;
 };
 
-template <typename T, bool FULL>
-__device__ __forceinline__ void fetch_slice(const T *Q, const T *Kx, const T *Vx, long slice,
-                                            int L, int tid, int w, int l16, int g, Raw &raw) {
-    const long base = slice * (long)L * kD;
-    const T *Qs = Q + base;
-    const T *Ks = Kx + base;
-    const T *Vs = Vx + base;
-    const int nitems = w < 4 ? 1 : 3;
+template <bool FULL, bool NARROW>
+__device__ __forceinline__ void local_scores(const uint16_t *sK, const Sp8 *qf, int qt, int NT,
+                                             int L, int r, float sscale, int l16, int g,
+                                             LocalTile<NARROW> &st) {
+    constexpr int MAXC = LocalTile<NARROW>::kMaxC;
+    const int qi = 16 * qt + l16;
+    // key tiles touched by the window of the tile (radius <= 16: qt-1 .. qt+1)
+    const int lo_key = 16 * qt - r, hi_key = 16 * qt + 15 + r;
+    const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
+    const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
+    st.c0 = kt_lo >> 1;
+    st.nch = (kt_hi >> 1) - st.c0 + 1;
+    float m = -__builtin_inff();
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        if (n < nitems) {
-            const int it = tid + 256 * n;
-            load_row8<T, FULL>(Ks, it >> 3, L, (it & 7) * 8, raw.k[n]);
-            load_col8<T, FULL>(Vs, (it >> 6) * 8, L, it & 63, raw.v[n]);
+    for (int q = 0; q < 2 * MAXC; ++q) {
+        if ((q >> 1) < st.nch) {
+            const int kt = 2 * st.c0 + q;   // may lie past NT: zero rows, masked below
+            f32x4_t a0 = kZero4, a1 = kZero4;
+            a0 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 0, g), qf[0], a0);
+            a1 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 1, g), qf[1], a1);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int key = 16 * kt + 4 * g + rr;   // a[rr] = k_key . q_qi
+                const int dist = key > qi ? key - qi : qi - key;
+                const bool in = (FULL || key < L) && dist <= r;
+                st.sc[q][rr] = in ? (a0[rr] + a1[rr]) * sscale : -__builtin_inff();
+                m = fmaxf(m, st.sc[q][rr]);
+            }
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) st.sc[q][rr] = -__builtin_inff();
         }
     }
+    m = col_max(m);
+    float ls = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Qs, 16 * w + l16, L, 32 * c + 8 * g, raw.q[c]);
-    if (w < 4) {
+    for (int q = 0; q < 2 * MAXC; ++q) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) load_col8<T, FULL>(Qs, 32 * c + 8 * g, L, 16 * w + l16, raw.qc[c]);
+        for (int rr = 0; rr < 4; ++rr) {
+            const float p = __builtin_amdgcn_exp2f(st.sc[q][rr] - m);   // exp2(-inf) = 0
+            st.sc[q][rr] = p;
+            ls += p;
+        }
+    }
+    st.lsum = col_sum(ls);
+}
+
+// Window of radius <= 16 (key tiles qt-1, qt, qt+1): score + band bias in
+// one fma (bias[d][rr] = 0 inside the band, -inf outside, precomputed per
+// lane), base-2 softmax (the score scale carries log2 e), then P V over the
+// aligned tile pairs that hold the three tiles.
+template <bool FULL>
+__device__ __forceinline__ void local_tile_narrow(const uint16_t *sK, const uint16_t *sV,
+                                                  const Sp8 *qf, int qt, int NT, int L,
+                                                  float sscale2, const float (*bias)[4], int l16,
+                                                  int g, f32x4_t *o, float &lsum) {
+    float s[3][4];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int kt = qt + d - 1;
+        if (kt >= 0 && kt < NT) {
+            f32x4_t a0 = kZero4, a1 = kZero4;
+            a0 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 0, g), qf[0], a0);
+            a1 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 1, g), qf[1], a1);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
+                float v = fmaf(a0[rr] + a1[rr], sscale2, bias[d][rr]);
+                if (!FULL && 16 * kt + 4 * g + rr >= L) v = -__builtin_inff();
+                s[d][rr] = v;
+                m = fmaxf(m, v);
+            }
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s[d][rr] = -__builtin_inff();
+        }
+    }
+    m = col_max(m);
+    float ls = 0.f;
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            s[d][rr] = __builtin_amdgcn_exp2f(s[d][rr] - m);   // exp2(-inf) = 0
+            ls += s[d][rr];
+        }
+    }
+    lsum = col_sum(ls);
+    if ((qt & 1) == 0) {
+        if (qt >= 1) {   // pair (qt-2, qt-1): only tile qt-1
+            const float pv[8] = {0.f, 0.f, 0.f, 0.f, s[0][0], s[0][1], s[0][2], s[0][3]};
+            const Sp8 pf = split8(pv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, (qt >> 1) - 1, g), pf, o[j]);
+        }
+        {   // pair (qt, qt+1)
+            const float pv[8] = {s[1][0], s[1][1], s[1][2], s[1][3], s[2][0], s[2][1], s[2][2], s[2][3]};
+            const Sp8 pf = split8(pv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, qt >> 1, g), pf, o[j]);
+        }
+    } else {
+        {   // pair (qt-1, qt)
+            const float pv[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
+            const Sp8 pf = split8(pv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, qt >> 1, g), pf, o[j]);
+        }
+        if (qt + 1 < NT) {   // pair (qt+1, qt+2): only tile qt+1
+            const float pv[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
+            const Sp8 pf = split8(pv);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, (qt >> 1) + 1, g), pf, o[j]);
+        }
+    }
+}
+
+// o[j] += P V over the tile pairs of st (32-deep products)
+template <bool NARROW>
+__device__ __forceinline__ void local_pv(const uint16_t *sV, int l16, int g,
+                                         const LocalTile<NARROW> &st, f32x4_t *o) {
+    constexpr int MAXC = LocalTile<NARROW>::kMaxC;
+#pragma unroll
+    for (int q = 0; q < MAXC; ++q) {
+        if (q < st.nch) {
+            const float pv[8] = {st.sc[2 * q][0],     st.sc[2 * q][1],     st.sc[2 * q][2],
+                                 st.sc[2 * q][3],     st.sc[2 * q + 1][0], st.sc[2 * q + 1][1],
+                                 st.sc[2 * q + 1][2], st.sc[2 * q + 1][3]};
+            const Sp8 pf = split8(pv);
+            const int c = st.c0 + q;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, c, g), pf, o[j]);
+        }
     }
 }
 
@@ -371,357 +422,390 @@ __global__ __launch_bounds__(kThreads, 1) void cluster_attn_fused_kernel(
     int Kc, int iters, int radius, float alpha, T *__restrict__ out,
     int32_t *__restrict__ assign_out) {
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t *sK = reinterpret_cast<uint16_t *>(smem);
-    uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kLdsK);
-    uint16_t *sMuP = reinterpret_cast<uint16_t *>(smem + kLdsK + kLdsV);
-    float *sMu = reinterpret_cast<float *>(smem + kLdsK + kLdsV + kLdsMuP);
-    float *sVc = sMu + kFK * kMuRow;
-    float *sPart = sVc + kFK * kMuRow;           // [8][kPartW]
-    float *sXm = sPart + 8 * kPartW;             // [16][8] wave maxima
-    float *sXl = sXm + 8 * kFK;                  // [16][8] wave sums
-    float *sN2 = sXl + 8 * kFK;                  // [4][16] partial ||mu_k||^2
-    int *sC = reinterpret_cast<int *>(sN2 + 4 * kFK);   // [128]
+    uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
+    uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kOffV);
+    uint16_t *sMuP = reinterpret_cast<uint16_t *>(smem + kOffMuP);
+    uint16_t *sOH = reinterpret_cast<uint16_t *>(smem + kOffOH);
+    uint16_t *sP = reinterpret_cast<uint16_t *>(smem + kOffP);
+    float *sVc = reinterpret_cast<float *>(smem + kOffVc);
+    float *sXm = reinterpret_cast<float *>(smem + kOffXm);
+    float *sXl = reinterpret_cast<float *>(smem + kOffXl);
+    float *sN2 = reinterpret_cast<float *>(smem + kOffN2);
+    int *sC = reinterpret_cast<int *>(smem + kOffC);
+    uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kOffMax);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const long slice = blockIdx.x;
+    if (slice >= S) return;
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;
-    const float scale = 0.125f;   // 1/sqrt(64), exact
-    const int nitems = w < 4 ? 1 : 3;
+    const long base = slice * (long)L * kD;
+    const T *Qs = Q + base;
+    const T *Ks = Kx + base;
+    const T *Vs = Vx + base;
+    const int nitems = w < 4 ? 1 : 3;     // K and V^T items of this thread
+    const bool lower = w < 4;             // waves 0-3: cluster sums / centroid context
+    const int tileA = w - 4, tileB = w;   // waves 4-7: local query tiles
 
-    // the token this lane owns starts centroid k = ceil(tok Kc / L) when
-    // floor(k L / Kc) == tok (the strided initial rows are distinct)
-    int init_k = -1;
-    {
-        const int k = (tok * Kc + L - 1) / L;
-        if (tok < L && k < Kc && (k * L) / Kc == tok) init_k = k;
+    // ------------------------------------------------------------ fetch
+    float kraw[3][8], vraw[3][8], qraw[2][8], qxraw[4][8];
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        if (n < nitems) {
+            const int it = tid + 256 * n;
+            load_row8<T, FULL>(Ks, it >> 3, L, (it & 7) * 8, kraw[n]);
+            load_col8<T, FULL>(Vs, (it >> 6) * 8, L, it & 63, vraw[n]);
+        }
     }
-
-    const long slice = blockIdx.x;
-    if (slice < S) {
-        Raw raw;
-        fetch_slice<T, FULL>(Q, Kx, Vx, slice, L, tid, w, l16, g, raw);
-        // ------------- split this slice's inputs: K, V planes in LDS, Q in registers
+#pragma unroll
+    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Qs, tok, L, 32 * c + 8 * g, qraw[c]);
+    if (lower) {
+        // dim tile w over tokens 32c + 8g + i (depth of the cluster sums)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) load_col8<T, FULL>(Qs, 32 * c + 8 * g, L, 16 * w + l16, qxraw[c]);
+    } else {
+        // query tile w-4 for the local branch
+#pragma unroll
+        for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Qs, 16 * tileA + l16, L, 32 * c + 8 * g, qxraw[c]);
+    }
+    {   // per-tensor largest magnitude (bit patterns of |x| order like the values)
+        uint32_t mq = 0, mk = 0, mv = 0;
+        mq = absmax8(qraw[0], absmax8(qraw[1], mq));
 #pragma unroll
         for (int n = 0; n < 3; ++n) {
             if (n < nitems) {
-                const int it = tid + 256 * n;
-                put_split8(sK + (it >> 3) * kKRow + (it & 7) * 8, kKPlane, split8(raw.k[n]));
-                put_split8(sV + (it & 63) * kVRow + (it >> 6) * 8, kVPlane, split8(raw.v[n]));
+                mk = absmax8(kraw[n], mk);
+                mv = absmax8(vraw[n], mv);
             }
         }
-        Split8 qf[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) qf[c] = split8(raw.q[c]);
-        Split8 qc[4];
-        if (w < 4) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) qc[c] = split8(raw.qc[c]);
+        mq = wave_max_u(mq);
+        mk = wave_max_u(mk);
+        mv = wave_max_u(mv);
+        if (lane == 0) {
+            sMax[w * 4 + 0] = mq;
+            sMax[w * 4 + 1] = mk;
+            sMax[w * 4 + 2] = mv;
         }
-        // strided initial centroids mu_k = Q[floor(k L / Kc)] from the owning lanes
-        if (init_k >= 0) {
-            float n2 = 0.f;
+    }
+    // clear the one-hot matrix; padded tokens join no cluster
+    reinterpret_cast<u32x2_t *>(sOH)[tid] = u32x2_t{0u, 0u};
+    if (!FULL && tid < kFL && tid >= L) sC[tid] = -1;
+    __syncthreads();
+
+    int sq, sk, sv;
+    {
+        uint32_t mq = 0, mk = 0, mv = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+            mq = max(mq, sMax[ww * 4 + 0]);
+            mk = max(mk, sMax[ww * 4 + 1]);
+            mv = max(mv, sMax[ww * 4 + 2]);
+        }
+        sq = scale_shift(mq);
+        sk = scale_shift(mk);
+        sv = scale_shift(mv);
+    }
+    const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk),
+                fv = __builtin_ldexpf(1.f, -sv);
+    const float sscale = __builtin_ldexpf(0.125f, sq + sk);   // scores: 1/sqrt(64) * 2^(sq+sk)
+    const float sscale2 = sscale * 1.4426950408889634f;      // the same in base-2 exponent units
+    const float vunscale = __builtin_ldexpf(1.f, sv);
+
+    // ------------------------------------------------------------ split
+    if (sk != 0 || sv != 0) {
+#pragma unroll
+        for (int n = 0; n < 3; ++n) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kraw[n][i] *= fk;
+                vraw[n][i] *= fv;
+            }
+        }
+    }
+    if (sq != 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qraw[c][i] *= fq;
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qxraw[c][i] *= fq;
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < 3; ++n) {
+        if (n < nitems) {
+            const int it = tid + 256 * n;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
+            const Sp8 sp = split8(x);
+            const int o = off64(it >> 3, (it & 7) * 8);
+            st16(sK + o, sp.h);
+            st16(sK + kPlaneK / 2 + o, sp.m);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = vraw[n][i];
+            const Sp8 sv8 = split8(x);
+            const int p0 = vpos((it >> 6) * 8);          // keys 8kg..8kg+3; +4..+7 sit 8 further
+            const int ov0 = off128(it & 63, p0), ov1 = off128(it & 63, p0 + 8);
+            st8(sV + ov0, u32x2_t{sv8.h.x, sv8.h.y});
+            st8(sV + ov1, u32x2_t{sv8.h.z, sv8.h.w});
+            st8(sV + kPlaneV / 2 + ov0, u32x2_t{sv8.m.x, sv8.m.y});
+            st8(sV + kPlaneV / 2 + ov1, u32x2_t{sv8.m.z, sv8.m.w});
+        }
+    }
+    Sp8 qf[2], qx[4];
+    float n2init = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = qraw[c][i];
+            n2init = fmaf(x[i], x[i], n2init);
+        }
+        qf[c] = split8(x);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        if (c < 2 || lower) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = qxraw[c][i];
+            qx[c] = split8(x);
+        }
+    }
+    // strided initial centroids mu_k = Q[floor(k L / Kc)]: the lanes holding
+    // token floor(k L / Kc) store its planes and partial squared norms
+    {
+        const int k = (tok * Kc + L - 1) / L;   // the only k that can start at tok
+        if (tok < L && k < Kc && (k * L) / Kc == tok) {
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                const int d0 = 32 * c + 8 * g;
-                put_split8(sMuP + init_k * kKRow + d0, kMuPlane, qf[c]);
-                float *m = sMu + init_k * kMuRow + d0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    m[i] = raw.q[c][i];
-                    n2 = fmaf(raw.q[c][i], raw.q[c][i], n2);
-                }
+                const int o = off64(k, 32 * c + 8 * g);
+                st16(sMuP + o, qf[c].h);
+                st16(sMuP + kPlaneMu / 2 + o, qf[c].m);
             }
-            sN2[g * kFK + init_k] = n2;
+            sN2[g * kFK + k] = n2init;
         }
-        // centroids beyond Kc stay zero (never chosen)
+        // centroids beyond Kc stay zero and are never chosen
         for (int e = tid; e < (kFK - Kc) * kD; e += kThreads) {
-            const int k = Kc + e / kD, dd = e % kD;
-            sMu[k * kMuRow + dd] = 0.f;
-            sMuP[k * kKRow + dd] = 0;
-            sMuP[kMuPlane + k * kKRow + dd] = 0;
-            sMuP[2 * kMuPlane + k * kKRow + dd] = 0;
-            if (dd < 4) sN2[dd * kFK + k] = 0.f;
+            const int kk = Kc + e / kD, dd = e % kD;
+            sMuP[off64(kk, dd)] = 0;
+            sMuP[kPlaneMu / 2 + off64(kk, dd)] = 0;
+            if (dd < 4) sN2[dd * kFK + kk] = 0.f;
         }
-        if (!FULL && tid < kFL && tid >= L) sC[tid] = -1;   // padded tokens join no cluster
-        __syncthreads();
+    }
+    __syncthreads();
 
-        // ------------- Lloyd iterations
-        for (int t = 1; t <= iters; ++t) {
-            if (w < NT) {
-                // acc[r] = mu_{4g+r} . q_tok - ||mu_{4g+r}||^2 / 2 (exact halving)
-                f32x4_t a0, a1 = {0.f, 0.f, 0.f, 0.f};
-                {
-                    const float4 p0 = *reinterpret_cast<const float4 *>(sN2 + 0 * kFK + 4 * g);
-                    const float4 p1 = *reinterpret_cast<const float4 *>(sN2 + 1 * kFK + 4 * g);
-                    const float4 p2 = *reinterpret_cast<const float4 *>(sN2 + 2 * kFK + 4 * g);
-                    const float4 p3 = *reinterpret_cast<const float4 *>(sN2 + 3 * kFK + 4 * g);
-                    a0[0] = -0.5f * (((p0.x + p1.x) + p2.x) + p3.x);
-                    a0[1] = -0.5f * (((p0.y + p1.y) + p2.y) + p3.y);
-                    a0[2] = -0.5f * (((p0.z + p1.z) + p2.z) + p3.z);
-                    a0[3] = -0.5f * (((p0.w + p1.w) + p2.w) + p3.w);
-                }
-                a0 = mma32x6(mu_frag(sMuP, 0, l16, g), qf[0], a0);
-                a1 = mma32x6(mu_frag(sMuP, 1, l16, g), qf[1], a1);
-                // D = ||mu||^2 - 2 mu.q = -2 (a0 + a1)
-                float best = __builtin_inff();
-                int bk = 0x7fffffff;
+    // local window branch of waves 4-7 (query tiles w-4 and w): tile A runs in
+    // the slot of iteration 1, tile B in the slot of iteration 2 (both in
+    // iteration 1 when there is only one); each tile has its own registers
+    f32x4_t oA[4], oB[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k = 4 * g + r;
-                    const float D = k < Kc ? -2.f * (a0[r] + a1[r]) : __builtin_inff();
-                    if (lex_less(D, k, best, bk)) { best = D; bk = k; }
-                }
-                col_argmin(best, bk);
-                if (bk >= Kc) bk = 0;   // only if every distance was NaN
-                if (g == 0 && (FULL || tok < L)) sC[tok] = bk;
+    for (int j = 0; j < 4; ++j) oA[j] = oB[j] = kZero4;
+    float lsumA = 1.f, lsumB = 1.f;
+    const int rad = radius < L ? radius : L;
+    const int slotB = iters < 2 ? 1 : 2;
+    // band bias of the narrow window for key tiles qt-1, qt, qt+1 (d = 0, 1, 2)
+    float bias[3][4];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int rel = 16 * (d - 1) + 4 * g + rr - l16;   // key - query
+            bias[d][rr] = (rel <= rad && -rel <= rad) ? 0.f : -__builtin_inff();
+        }
+    }
+
+    // ------------------------------------------------------------ Lloyd
+    int cprev = -1;
+    for (int t = 1; t <= iters; ++t) {
+        if (w < NT) {
+            // a[r] = mu_{4g+r} . q_tok - ||mu_{4g+r}||^2 / 2 (halving is exact)
+            f32x4_t a0, a1 = kZero4;
+            {
+                const float4 p0 = *reinterpret_cast<const float4 *>(sN2 + 0 * kFK + 4 * g);
+                const float4 p1 = *reinterpret_cast<const float4 *>(sN2 + 1 * kFK + 4 * g);
+                const float4 p2 = *reinterpret_cast<const float4 *>(sN2 + 2 * kFK + 4 * g);
+                const float4 p3 = *reinterpret_cast<const float4 *>(sN2 + 3 * kFK + 4 * g);
+                a0[0] = -0.5f * (((p0.x + p1.x) + p2.x) + p3.x);
+                a0[1] = -0.5f * (((p0.y + p1.y) + p2.y) + p3.y);
+                a0[2] = -0.5f * (((p0.z + p1.z) + p2.z) + p3.z);
+                a0[3] = -0.5f * (((p0.w + p1.w) + p2.w) + p3.w);
             }
-            __syncthreads();
-            if (w < 4) {
-                // (one-hot^T Q)[centroid 4g+r][dim 16w + l16] and the cluster sizes
-                f32x4_t sl = {0.f, 0.f, 0.f, 0.f}, sm = sl, sh = sl, cnt = sl;
-                const u32x4_t ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+            a0 = mma3(frag64(sMuP, kPlaneMu / 2, l16, 0, g), qf[0], a0);
+            a1 = mma3(frag64(sMuP, kPlaneMu / 2, l16, 1, g), qf[1], a1);
+            // D = ||mu||^2 - 2 mu.q = -2 (a0 + a1), in the scaled units of Q
+            float best = __builtin_inff();
+            int bk = 0x7fffffff;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int4 ca = *reinterpret_cast<const int4 *>(sC + 32 * c + 8 * g);
-                    const int4 cb = *reinterpret_cast<const int4 *>(sC + 32 * c + 8 * g + 4);
-                    u32x4_t oh;
-                    oh.x = (ca.x == l16 ? 0x3f80u : 0u) | (ca.y == l16 ? 0x3f800000u : 0u);
-                    oh.y = (ca.z == l16 ? 0x3f80u : 0u) | (ca.w == l16 ? 0x3f800000u : 0u);
-                    oh.z = (cb.x == l16 ? 0x3f80u : 0u) | (cb.y == l16 ? 0x3f800000u : 0u);
-                    oh.w = (cb.z == l16 ? 0x3f80u : 0u) | (cb.w == l16 ? 0x3f800000u : 0u);
-                    sl = mma32(oh, qc[c].l, sl);
-                    sm = mma32(oh, qc[c].m, sm);
-                    sh = mma32(oh, qc[c].h, sh);
-                    cnt = mma32(oh, ones, cnt);
-                }
-                float v[4], n2p[4];
+            for (int rr = 0; rr < 4; ++rr) {
+                const int k = 4 * g + rr;
+                const float D = k < Kc ? -2.f * (a0[rr] + a1[rr]) : __builtin_inff();
+                if (lex_less(D, k, best, bk)) { best = D; bk = k; }
+            }
+            col_argmin(best, bk);
+            if (bk >= Kc) bk = 0;   // only if every distance was NaN
+            if (g == 0 && (FULL || tok < L)) {
+                sC[tok] = bk;
+                if (cprev >= 0) sOH[off128(cprev, tok)] = 0;
+                sOH[off128(bk, tok)] = 0x3c00;   // fp16 1.0
+                cprev = bk;
+            }
+        }
+        __syncthreads();
+        if (lower) {
+            // (Q^T one-hot)[dim 16w + 4g + rr][centroid l16] and the sizes n_l16
+            f32x4_t sh = kZero4, sm = kZero4, cnt = kZero4;
+            const u32x4_t ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v[r] = ((sl[r] + sm[r]) + sh[r]) / fmaxf(cnt[r], 1.f);
-                    sMu[(4 * g + r) * kMuRow + 16 * w + l16] = v[r];
-                    n2p[r] = row_sum(v[r] * v[r]);
-                }
-                if (l16 == 0)
-                    *reinterpret_cast<float4 *>(sN2 + w * kFK + 4 * g) =
-                        make_float4(n2p[0], n2p[1], n2p[2], n2p[3]);
-                // split planes: lanes l16 and l16^1 hold adjacent dims; the even
-                // lane stores centroids 4g, 4g+1, the odd lane 4g+2, 4g+3
-                float o[4];
+            for (int c = 0; c < 4; ++c) {
+                const u32x4_t oh = ld16(sOH + off128(l16, 32 * c + 8 * g));
+                sm = mma(qx[c].m, oh, sm);
+                sh = mma(qx[c].h, oh, sh);
+                cnt = mma(ones, oh, cnt);
+            }
+            const float inv = 1.0f / fmaxf(cnt[0], 1.f);
+            float v[4];
+            float n2p = 0.f;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = dpp<kDppXor1>(v[r]);
-                const int d = 16 * w + (l16 & ~1);
-                if ((l16 & 1) == 0) {
-                    put_mu_pair(sMuP, 4 * g + 0, d, v[0], o[0]);
-                    put_mu_pair(sMuP, 4 * g + 1, d, v[1], o[1]);
+            for (int rr = 0; rr < 4; ++rr) {
+                v[rr] = (sm[rr] + sh[rr]) * inv;
+                n2p = fmaf(v[rr], v[rr], n2p);
+            }
+            uint32_t h01, m01, h23, m23;
+            split2(v[0], v[1], h01, m01);
+            split2(v[2], v[3], h23, m23);
+            const int o = off64(l16, 16 * w + 4 * g);
+            st8(sMuP + o, u32x2_t{h01, h23});
+            st8(sMuP + kPlaneMu / 2 + o, u32x2_t{m01, m23});
+            n2p = col_sum(n2p);   // over the 16 dims of tile w
+            if (g == 0) sN2[w * kFK + l16] = n2p;
+        } else {
+            if (t == 1 && tileA < NT) {
+                if (NARROW) {
+                    local_tile_narrow<FULL>(sK, sV, qx, tileA, NT, L, sscale2, bias, l16, g, oA, lsumA);
                 } else {
-                    put_mu_pair(sMuP, 4 * g + 2, d, o[2], v[2]);
-                    put_mu_pair(sMuP, 4 * g + 3, d, o[3], v[3]);
+                    LocalTile<NARROW> lt;
+                    local_scores<FULL, NARROW>(sK, qx, tileA, NT, L, rad, sscale2, l16, g, lt);
+                    lsumA = lt.lsum;
+                    local_pv<NARROW>(sV, l16, g, lt, oA);
                 }
             }
-            __syncthreads();
-        }
-
-        // ------------- centroid cross-attention (wave w: key tile w)
-        float sx[4];
-        float mloc = -__builtin_inff();
-        if (w < NT) {
-            f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-            a0 = mma32x6(k_frag(sK, w, 0, l16, g), mu_frag(sMuP, 0, l16, g), a0);
-            a1 = mma32x6(k_frag(sK, w, 1, l16, g), mu_frag(sMuP, 1, l16, g), a1);
-            // a[r] = k_{16w+4g+r} . mu_{l16}
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = 16 * w + 4 * g + r;
-                sx[r] = (FULL || key < L) ? (a0[r] + a1[r]) * scale : -__builtin_inff();
-                mloc = fmaxf(mloc, sx[r]);
+            if (t == slotB && tileB < NT) {
+                if (NARROW) {
+                    local_tile_narrow<FULL>(sK, sV, qf, tileB, NT, L, sscale2, bias, l16, g, oB, lsumB);
+                } else {
+                    LocalTile<NARROW> lt;
+                    local_scores<FULL, NARROW>(sK, qf, tileB, NT, L, rad, sscale2, l16, g, lt);
+                    lsumB = lt.lsum;
+                    local_pv<NARROW>(sV, l16, g, lt, oB);
+                }
             }
-            mloc = col_max(mloc);
         }
-        if (g == 0) sXm[l16 * 8 + w] = mloc;
         __syncthreads();
-        float M;
-        {
-            const float4 m0 = *reinterpret_cast<const float4 *>(sXm + l16 * 8);
-            const float4 m1 = *reinterpret_cast<const float4 *>(sXm + l16 * 8 + 4);
-            M = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
-                      fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
-        }
-        if (w < NT) {
-            float p[4];
-            float ls = 0.f;
+    }
+
+    // ------------------------------------------------------------ centroid cross-attention
+    float sx[4];
+    float mloc = -__builtin_inff();
+    if (w < NT) {
+        f32x4_t a0 = kZero4, a1 = kZero4;
+        a0 = mma3(frag64(sK, kPlaneK / 2, 16 * w + l16, 0, g), frag64(sMuP, kPlaneMu / 2, l16, 0, g), a0);
+        a1 = mma3(frag64(sK, kPlaneK / 2, 16 * w + l16, 1, g), frag64(sMuP, kPlaneMu / 2, l16, 1, g), a1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[r] = sx[r] == -__builtin_inff() ? 0.f : exp_f32(sx[r] - M);
-                ls += p[r];
+        for (int rr = 0; rr < 4; ++rr) {
+            const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
+            sx[rr] = (FULL || key < L) ? (a0[rr] + a1[rr]) * sscale2 : -__builtin_inff();
+            mloc = fmaxf(mloc, sx[rr]);
+        }
+        mloc = col_max(mloc);
+    }
+    if (g == 0) sXm[l16 * 8 + w] = mloc;
+    __syncthreads();   // the centroid planes are dead from here on (P reuses them)
+    {
+        const float4 m0 = *reinterpret_cast<const float4 *>(sXm + l16 * 8);
+        const float4 m1 = *reinterpret_cast<const float4 *>(sXm + l16 * 8 + 4);
+        const float M = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
+                              fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        float ls = 0.f;
+        if (w < NT) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                p[rr] = __builtin_amdgcn_exp2f(sx[rr] - M);   // exp2(-inf) = 0
+                ls += p[rr];
             }
             ls = col_sum(ls);
-            const Split4 pf = split4(p);
-            float *part = sPart + w * kPartW;
+        }
+        uint32_t h01, m01, h23, m23;
+        split2(p[0], p[1], h01, m01);
+        split2(p[2], p[3], h23, m23);
+        const int o = off128(l16, vpos(16 * w + 4 * g));   // P[centroid l16][keys 16w + 4g ..]
+        st8(sP + o, u32x2_t{h01, h23});
+        st8(sP + kPlaneRow128 / 2 + o, u32x2_t{m01, m23});
+        if (g == 0) sXl[l16 * 8 + w] = ls;
+    }
+    __syncthreads();
+    if (lower) {
+        // V^cent^T[dim 16w + 4g + rr][centroid l16] = sum over keys of V^T P^T
+        f32x4_t a0 = kZero4, a1 = kZero4;
+        const int nch = (NT + 1) >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma16x6(v_frag_tile(sV, j, w, l16, g), pf, acc);
-                // acc[r] = partial Vc[centroid l16][dim 16j + 4g + r]
-#pragma unroll
-                for (int r = 0; r < 4; ++r) part[(16 * j + 4 * g + r) * kFK + l16] = acc[r];
+        for (int ch = 0; ch < 4; ++ch) {
+            if (ch < nch) {
+                const Sp8 vf = frag128(sV, kPlaneV / 2, 16 * w + l16, ch, g);
+                const Sp8 pf = frag128(sP, kPlaneRow128 / 2, l16, ch, g);
+                if (ch & 1)
+                    a1 = mma3(vf, pf, a1);
+                else
+                    a0 = mma3(vf, pf, a0);
             }
-            if (g == 0) sXl[l16 * 8 + w] = ls;
-        } else if (g == 0) {
-            sXl[l16 * 8 + w] = 0.f;
         }
-        __syncthreads();
-        for (int e = tid; e < kFK * kD; e += kThreads) {
-            const int k = e & 15, dim = e >> 4;
-            float num = 0.f;
-            for (int ww = 0; ww < NT; ++ww) num += sPart[ww * kPartW + dim * kFK + k];
-            const float4 l0 = *reinterpret_cast<const float4 *>(sXl + k * 8);
-            const float4 l1 = *reinterpret_cast<const float4 *>(sXl + k * 8 + 4);
-            const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
-            sVc[k * kMuRow + dim] = num / den;
-        }
-        __syncthreads();
+        const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
+        const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
+        const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
+        const float f = vunscale / den;
+        float4 vc;
+        vc.x = (a0[0] + a1[0]) * f;
+        vc.y = (a0[1] + a1[1]) * f;
+        vc.z = (a0[2] + a1[2]) * f;
+        vc.w = (a0[3] + a1[3]) * f;
+        *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) = vc;
+    }
+    __syncthreads();
 
-        // ------------- local window branch + gather + fusion (wave w: query tile w)
-        if (w < NT) {
-            const int qi = tok;
-            const int r = radius < L ? radius : L;
-            f32x4_t o[4], o2[4];
+    // ------------------------------------------------------------ gather + fusion (waves 4-7)
+    if (!lower) {
+        const float wg = 1.0f - alpha;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = o2[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            float lsum;
-            if (NARROW) {
-                // radius <= 16: the tile's keys lie in tiles w-1, w, w+1
-                const int kt0 = w > 0 ? w - 1 : 0;
-                const int kt2 = w + 1 < NT ? w + 1 : NT - 1;
-                const int ntile = kt2 - kt0 + 1;          // 1, 2 or 3
-                float sc[3][4];
-                float m = -__builtin_inff();
-#pragma unroll
-                for (int q = 0; q < 3; ++q) {
-                    const int kt = kt0 + q;
-                    if (q < ntile) {
-                        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-                        a0 = mma32x6(k_frag(sK, kt, 0, l16, g), qf[0], a0);
-                        a1 = mma32x6(k_frag(sK, kt, 1, l16, g), qf[1], a1);
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int key = 16 * kt + 4 * g + rr;
-                            const int dist = key > qi ? key - qi : qi - key;
-                            const bool in = (FULL || key < L) && dist <= r;
-                            sc[q][rr] = in ? (a0[rr] + a1[rr]) * scale : -__builtin_inff();
-                            m = fmaxf(m, sc[q][rr]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) sc[q][rr] = -__builtin_inff();
-                    }
-                }
-                m = col_max(m);
-                float ls = 0.f;
-#pragma unroll
-                for (int q = 0; q < 3; ++q) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const float pp = sc[q][rr] == -__builtin_inff() ? 0.f : exp_f32(sc[q][rr] - m);
-                        sc[q][rr] = pp;
-                        ls += pp;
-                    }
-                }
-                lsum = col_sum(ls);
-                {   // tiles (kt0, kt0+1); the second may not exist (then p = 0)
-                    const float pv[8] = {sc[0][0], sc[0][1], sc[0][2], sc[0][3],
-                                         sc[1][0], sc[1][1], sc[1][2], sc[1][3]};
-                    const Split8 pf = split8(pv);
-                    const int kb = ntile > 1 ? kt0 + 1 : kt0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = mma32x6(v_frag_two(sV, j, kt0, kb, l16, g), pf, o[j]);
-                }
-                if (ntile == 3) {   // tile kt0+2 with an empty partner (p = 0)
-                    const float pv[8] = {sc[2][0], sc[2][1], sc[2][2], sc[2][3], 0.f, 0.f, 0.f, 0.f};
-                    const Split8 pf = split8(pv);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        o2[j] = mma32x6(v_frag_two(sV, j, kt0 + 2, kt0 + 2, l16, g), pf, o2[j]);
-                }
-            } else {
-                const int lo_key = 16 * w - r;                 // window of the whole tile
-                const int hi_key = 16 * w + 15 + r;
-                const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
-                const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
-                float sc[8][4];
-                float m = -__builtin_inff();
-#pragma unroll
-                for (int kt = 0; kt < 8; ++kt) {
-                    if (kt >= kt_lo && kt <= kt_hi) {
-                        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-                        a0 = mma32x6(k_frag(sK, kt, 0, l16, g), qf[0], a0);
-                        a1 = mma32x6(k_frag(sK, kt, 1, l16, g), qf[1], a1);
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const int key = 16 * kt + 4 * g + rr;
-                            const int dist = key > qi ? key - qi : qi - key;
-                            const bool in = (FULL || key < L) && dist <= r;
-                            sc[kt][rr] = in ? (a0[rr] + a1[rr]) * scale : -__builtin_inff();
-                            m = fmaxf(m, sc[kt][rr]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) sc[kt][rr] = -__builtin_inff();
-                    }
-                }
-                m = col_max(m);
-                float ls = 0.f;
-#pragma unroll
-                for (int kt = 0; kt < 8; ++kt) {
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const float pp = sc[kt][rr] == -__builtin_inff() ? 0.f : exp_f32(sc[kt][rr] - m);
-                        sc[kt][rr] = pp;
-                        ls += pp;
-                    }
-                }
-                lsum = col_sum(ls);
-#pragma unroll
-                for (int ch = 0; ch < 4; ++ch) {
-                    if (2 * ch + 1 >= kt_lo && 2 * ch <= kt_hi) {
-                        const float pv[8] = {sc[2 * ch][0], sc[2 * ch][1], sc[2 * ch][2],
-                                             sc[2 * ch][3], sc[2 * ch + 1][0], sc[2 * ch + 1][1],
-                                             sc[2 * ch + 1][2], sc[2 * ch + 1][3]};
-                        const Split8 pf = split8(pv);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            if (ch & 1)
-                                o2[j] = mma32x6(v_frag_two(sV, j, 2 * ch, 2 * ch + 1, l16, g), pf, o2[j]);
-                            else
-                                o[j] = mma32x6(v_frag_two(sV, j, 2 * ch, 2 * ch + 1, l16, g), pf, o[j]);
-                        }
-                    }
-                }
-            }
-            // o + o2 = sum p v[dim 16j + 4g + rr] for query qi
-            if (FULL || qi < L) {
-                const float inv = 1.0f / lsum;
+        for (int which = 0; which < 2; ++which) {
+            const int qt = which == 0 ? tileA : tileB;
+            const int qi = 16 * qt + l16;
+            if (qt < NT && (FULL || qi < L)) {
+                const float f = alpha * vunscale / (which == 0 ? lsumA : lsumB);
                 const int cq = sC[qi];
-                const float wg = 1.0f - alpha;
-                const float *vc = sVc + cq * kMuRow;
-                T *dst = out + slice * (long)L * kD + (long)qi * kD;
+                const float *vc = sVc + cq * kVcRow;
+                T *dst = out + base + (long)qi * kD;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int d0 = 16 * j + 4 * g;
-                    const f32x4_t ol = add4(o[j], o2[j]);
+                    const f32x4_t ol = which == 0 ? oA[j] : oB[j];
                     float4 v;
-                    v.x = wg * vc[d0 + 0] + alpha * (ol[0] * inv);
-                    v.y = wg * vc[d0 + 1] + alpha * (ol[1] * inv);
-                    v.z = wg * vc[d0 + 2] + alpha * (ol[2] * inv);
-                    v.w = wg * vc[d0 + 3] + alpha * (ol[3] * inv);
+                    v.x = wg * vc[d0 + 0] + ol[0] * f;
+                    v.y = wg * vc[d0 + 1] + ol[1] * f;
+                    v.z = wg * vc[d0 + 2] + ol[2] * f;
+                    v.w = wg * vc[d0 + 3] + ol[3] * f;
                     store4<T>(dst + d0, v);
                 }
             }
         }
-        if (assign_out) {
-            for (int i = tid; i < L; i += kThreads) assign_out[slice * L + i] = sC[i];
-        }
+    } else if (assign_out) {
+        for (int i = tid; i < L; i += 256) assign_out[slice * L + i] = sC[i];
     }
 }
 
@@ -733,11 +817,9 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
                                  hipStream_t st) {
     auto kern = cluster_attn_fused_kernel<T, FULL, NARROW>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsTotal);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTotal);
     if (e != hipSuccess) return e;
-    // one workgroup per slice (the LDS footprint admits one per CU)
-    const int grid = S;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), kLdsTotal, st,
+    hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), kLdsTotal, st,
                        static_cast<const T *>(Q), static_cast<const T *>(K),
                        static_cast<const T *>(V), S, L, Kc, iters, radius, alpha,
                        static_cast<T *>(out), assign);
