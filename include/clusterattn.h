@@ -178,15 +178,31 @@ ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign,
                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------
- * Full attention layer (model card pipeline figure: multi-head projections
- * of X, cluster attention, output projection Y = O W_O), bf16 storage:
- *   Q = X Wq, K = X Wk, V = X Wv  (X [B,L,Dm], W [Dm, H*d], no bias; head h
- *   is columns h*d .. h*d+d-1), each rounded to bf16; O = cluster attention
- *   (as cluster_attn_forward, bf16); Y = O_merged Wo (Wo [H*d, Dm]) in bf16.
- *   X, Wq, Wk, Wv, Wo, Y: device bf16 bits (uint16). Dm == H*d, d == 64,
- *   Dm a multiple of 64. assign_out int32 [B,H,L] or NULL. qkv_out: NULL,
- *   or device bf16 [3,B,H,L,d] receiving Q, K, V. Workspace of
- *   cluster_attn_layer_workspace_size(...) bytes.
+ * Full attention layer (model card Architecture Overview: multi-head
+ * projections of X, cluster attention, output projection Y = O W_O;
+ * ClusterFormer 3, first and last rows of the tensor trace), bf16 storage:
+ *   Q = X Wq, K = X Wk, V = X Wv   X [B, L, Dm]; W [Dm, H*d] ([in, out]),
+ *                                  no bias; head h is columns h*d .. h*d+d-1;
+ *                                  each product accumulated in fp32 and
+ *                                  rounded to bf16 (nearest even)
+ *   O = cluster attention of (Q, K, V) exactly as cluster_attn_forward with
+ *       dt = CA_BF16 (O rounded to bf16)
+ *   Y = O_merged Wo                O_merged [B, L, H*d] (heads concatenated),
+ *                                  Wo [H*d, Dm], Y [B, L, Dm] rounded to bf16
+ * Arguments:
+ *   X, Wq, Wk, Wv, Wo  in   device bf16 bits (uint16), 16-byte aligned.
+ *   B, L, H >= 1; d == 64 and Dm == H * d (CA_ERR_UNSUPPORTED otherwise);
+ *   nclust, iters, W, alpha as in cluster_attn_forward.
+ *   Y           out  device bf16 [B, L, Dm].
+ *   assign_out  out  device int32 [B, H, L] or NULL.
+ *   qkv_out     out  device bf16 [3, B, H, L, d] receiving Q, K, V, or NULL.
+ *   workspace        device, cluster_attn_layer_workspace_size(...) bytes,
+ *                    256-byte aligned; it holds the transposed weights, Q,
+ *                    K, V (when qkv_out is NULL), O and the attention
+ *                    workspace.
+ *   Outputs and workspace must not overlap each other or the inputs.
+ *   Launches: one weight transpose, one GEMM for Q, K and V together, the
+ *   cluster attention launches, one GEMM for Y.
  * --------------------------------------------------------------------- */
 size_t cluster_attn_layer_workspace_size(int B, int L, int Dm, int H, int d,
                                          int nclust);
@@ -201,11 +217,14 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq,
                                        hipStream_t stream);
 
 /*
- * Plain bf16 GEMM used by the layer: C[M,N] = A[M,Kd] B[Kd,N], fp32
- * accumulation, bf16 (nearest-even) output. All row-major bf16 bits; M, N, Kd
- * multiples of 64 (CA_ERR_UNSUPPORTED otherwise).
+ * The layer's bf16 GEMM on its own: C[M, N] = A[M, Kd] . Bt[N, Kd]^T, i.e.
+ * C[m][n] = sum_k A[m][k] Bt[n][k] (Bt in the [out, in] layout of a linear
+ * layer's weight), fp32 accumulation, one round-to-nearest-even to bf16.
+ *   A, Bt in, C out: device bf16 bits, row-major, 16-byte aligned; C must
+ *   not overlap A or Bt. M, N, Kd >= 1 (CA_ERR_INVALID_ARG otherwise); N and
+ *   Kd multiples of 64 (CA_ERR_UNSUPPORTED otherwise); any M.
  */
-ca_status_t ca_gemm_bf16(const void *A, const void *Bm, int M, int N, int Kd,
+ca_status_t ca_gemm_bf16(const void *A, const void *Bt, int M, int N, int Kd,
                          void *C, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -245,11 +245,14 @@ def cluster_attn_layer_forward(X, Wq, Wk, Wv, Wo, H: int, nclust: int, iters: in
     return Y, assign, qkv
 
 
-def ca_gemm_bf16(A, Bm, stream=None):
+def ca_gemm_bf16(A, Bt, stream=None):
+    """C = A Bt^T for bfloat16 GPU tensors A [M, Kd] and Bt [N, Kd]; returns C [M, N]."""
     torch = _torch()
     M, Kd = A.shape
-    _, N = Bm.shape
+    N, Kb = Bt.shape
+    if Kb != Kd:
+        raise ValueError("A and Bt disagree on the contraction length")
     C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
-    st = lib().ca_gemm_bf16(_ptr(A), _ptr(Bm), M, N, Kd, _ptr(C), _stream(stream))
+    st = lib().ca_gemm_bf16(_ptr(A), _ptr(Bt), M, N, Kd, _ptr(C), _stream(stream))
     _check(st, "ca_gemm_bf16")
     return C

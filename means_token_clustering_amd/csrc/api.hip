@@ -139,6 +139,51 @@ ca_status_t check_step(int S, int L, int d, int Kc, ca_dtype_t dt) {
     return CA_OK;
 }
 
+// Workspace of the full layer, carved in this order (each 256-B aligned):
+// the four transposed weights, Q/K/V ([3, B, H, L, 64]; unused when the
+// caller passes qkv_out), the attention output O ([B, H, L, 64]) and the
+// cluster attention workspace of the bf16 [B, H, L, 64] problem.
+struct LayerLayout {
+    size_t wt, qkv, o, attn, attn_bytes, total;
+};
+
+LayerLayout layer_layout(int B, int L, int Dm, int H, int nclust) {
+    LayerLayout w{};
+    const size_t tok = (size_t)B * L;
+    size_t off = 0;
+    w.wt = off;   off += align_up(sizeof(uint16_t) * 4 * (size_t)Dm * Dm);
+    w.qkv = off;  off += align_up(sizeof(uint16_t) * 3 * tok * Dm);
+    w.o = off;    off += align_up(sizeof(uint16_t) * tok * Dm);
+    w.attn = off;
+    w.attn_bytes = align_up(cluster_attn_workspace_size_ex(B, H, L, kD, nclust, CA_BF16,
+                                                           CA_PATH_AUTO));
+    off += w.attn_bytes;
+    w.total = off;
+    return w;
+}
+
+ca_status_t check_layer(int B, int L, int Dm, int H, int d, int nclust, int iters, int W,
+                        float alpha) {
+    if (Dm < 1) return CA_ERR_INVALID_ARG;
+    ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, CA_BF16);
+    if (st != CA_OK) return st;
+    if ((long long)B * L * Dm > (1LL << 40)) return CA_ERR_INVALID_ARG;
+    if ((long long)Dm != (long long)H * d) return CA_ERR_UNSUPPORTED;
+    return CA_OK;
+}
+
+struct Span {
+    const void *p;
+    size_t n;
+};
+
+bool any_overlap(const Span *s, int count) {
+    for (int i = 0; i < count; ++i)
+        for (int j = i + 1; j < count; ++j)
+            if (s[i].p && s[j].p && overlap(s[i].p, s[i].n, s[j].p, s[j].n)) return true;
+    return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -262,6 +307,78 @@ ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign, const floa
     if (!aligned(vcent, 16) || !aligned(oloc, 16) || !aligned(out, 16) || !aligned(assign, 4))
         return CA_ERR_INVALID_ARG;
     return hip_status(launch_gather_fuse(vcent, assign, oloc, S, L, Kc, alpha, dt, out, stream));
+}
+
+size_t cluster_attn_layer_workspace_size(int B, int L, int Dm, int H, int d, int nclust) {
+    if (check_layer(B, L, Dm, H, d, nclust, 1, 0, 0.f) != CA_OK) return 0;
+    return layer_layout(B, L, Dm, H, nclust).total;
+}
+
+ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq, const void *Wk,
+                                       const void *Wv, const void *Wo, int B, int L, int Dm,
+                                       int H, int d, int nclust, int iters, int W, float alpha,
+                                       void *Y, int32_t *assign_out, void *qkv_out,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    ca_status_t st = check_layer(B, L, Dm, H, d, nclust, iters, W, alpha);
+    if (st != CA_OK) return st;
+    if (!X || !Wq || !Wk || !Wv || !Wo || !Y || !workspace) return CA_ERR_INVALID_ARG;
+    const void *ptrs16[] = {X, Wq, Wk, Wv, Wo, Y, qkv_out};
+    for (const void *q : ptrs16)
+        if (q && !aligned(q, 16)) return CA_ERR_INVALID_ARG;
+    if (assign_out && !aligned(assign_out, 4)) return CA_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;
+    const LayerLayout lay = layer_layout(B, L, Dm, H, nclust);
+    if (workspace_bytes < lay.total) return CA_ERR_INVALID_ARG;
+    const size_t tok = (size_t)B * L;
+    const size_t act = sizeof(uint16_t) * tok * Dm, wbytes = sizeof(uint16_t) * (size_t)Dm * Dm;
+    // outputs and workspace must not overlap each other or the inputs
+    const Span outs[] = {{Y, act}, {assign_out, sizeof(int32_t) * tok * H},
+                         {qkv_out, 3 * act}, {workspace, lay.total}};
+    if (any_overlap(outs, 4)) return CA_ERR_INVALID_ARG;
+    const Span ins[] = {{X, act}, {Wq, wbytes}, {Wk, wbytes}, {Wv, wbytes}, {Wo, wbytes}};
+    for (const Span &o : outs)
+        for (const Span &i : ins)
+            if (o.p && overlap(o.p, o.n, i.p, i.n)) return CA_ERR_INVALID_ARG;
+
+    char *ws = static_cast<char *>(workspace);
+    uint16_t *wt[4];
+    for (int i = 0; i < 4; ++i)
+        wt[i] = reinterpret_cast<uint16_t *>(ws + lay.wt) + (size_t)i * Dm * Dm;
+    const uint16_t *wsrc[4] = {static_cast<const uint16_t *>(Wq), static_cast<const uint16_t *>(Wk),
+                               static_cast<const uint16_t *>(Wv), static_cast<const uint16_t *>(Wo)};
+    uint16_t *qkv = qkv_out ? static_cast<uint16_t *>(qkv_out)
+                            : reinterpret_cast<uint16_t *>(ws + lay.qkv);
+    uint16_t *heads[3] = {qkv, qkv + tok * Dm, qkv + 2 * tok * Dm};
+    uint16_t *O = reinterpret_cast<uint16_t *>(ws + lay.o);
+    // W is [in, out]; the matrix cores read both operands along the contraction
+    CA_TRY(launch_transpose_bf16(wsrc, wt, 4, Dm, Dm, stream));
+    const uint16_t *wqkv[3] = {wt[0], wt[1], wt[2]};
+    CA_TRY(launch_gemm_nt(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
+                          false, true, L, H, stream));
+    st = forward_impl(heads[0], heads[1], heads[2], B, H, L, d, nclust, iters, W, alpha, O,
+                      assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO, stream);
+    if (st != CA_OK) return st;
+    const uint16_t *wo[1] = {wt[3]};
+    uint16_t *yv[1] = {static_cast<uint16_t *>(Y)};
+    return hip_status(launch_gemm_nt(O, wo, yv, 1, (int)tok, Dm, Dm, true, false, L, H, stream));
+}
+
+ca_status_t ca_gemm_bf16(const void *A, const void *Bt, int M, int N, int Kd, void *C,
+                         hipStream_t stream) {
+    if (!A || !Bt || !C || M < 1 || N < 1 || Kd < 1) return CA_ERR_INVALID_ARG;
+    if ((long long)M * Kd > (1LL << 40) || (long long)N * Kd > (1LL << 40) ||
+        (long long)M * N > (1LL << 40))
+        return CA_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(Bt, 16) || !aligned(C, 16)) return CA_ERR_INVALID_ARG;
+    const size_t ca = sizeof(uint16_t) * (size_t)M * Kd, cb = sizeof(uint16_t) * (size_t)N * Kd,
+                 cc = sizeof(uint16_t) * (size_t)M * N;
+    if (overlap(C, cc, A, ca) || overlap(C, cc, Bt, cb)) return CA_ERR_INVALID_ARG;
+    if (N % 64 != 0 || Kd % 64 != 0 || M > (1 << 30) || N > (1 << 30)) return CA_ERR_UNSUPPORTED;
+    const uint16_t *b[1] = {static_cast<const uint16_t *>(Bt)};
+    uint16_t *c[1] = {static_cast<uint16_t *>(C)};
+    return hip_status(launch_gemm_nt(static_cast<const uint16_t *>(A), b, c, 1, M, N, Kd, false,
+                                     false, 1, 1, stream));
 }
 
 }  // extern "C"

@@ -122,8 +122,14 @@ hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int
                                 int iters, int W, float alpha, ca_dtype_t dt, void *out,
                                 int32_t *assign, hipStream_t st);
 
-hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *Bm, int M, int N, int Kd,
-                            uint16_t *C, int a_mode, int c_mode, int B, int L, int H,
-                            hipStream_t st);
+// C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
+// A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as
+// [B, H, L, 64] from [B*L, 64 H]. N and K multiples of 64.
+hipError_t launch_gemm_nt(const uint16_t *A, const uint16_t *const *Bt, uint16_t *const *C,
+                          int count, int M, int N, int K, bool a_heads, bool c_heads, int L, int H,
+                          hipStream_t st);
+// dst[z] = src[z]^T for z < count; src [R, Cc], R and Cc multiples of 64.
+hipError_t launch_transpose_bf16(const uint16_t *const *src, uint16_t *const *dst, int count,
+                                 int R, int Cc, hipStream_t st);
 
 }  // namespace ca

@@ -104,3 +104,46 @@ def test_binding_refuses_cpu_tensors():
         b.cluster_attn_forward(x, x, x, 2, 1, 4, 0.5, path=b.CA_PATH_STAGED,
                                out=torch.zeros(1, 1, 8, 64), assign_out=None, want_assign=False,
                                workspace=None)
+
+
+def layer(**kw):
+    X, WQ, WK, WV, WO, Y, LWS = (0x10000000 * (i + 10) for i in range(7))
+    a = dict(X=X, Wq=WQ, Wk=WK, Wv=WV, Wo=WO, B=2, L=160, Dm=256, H=4, d=64, nclust=16,
+             iters=3, W=32, alpha=0.5, Y=Y, assign=None, qkv=None, ws=LWS, wsb=1 << 28)
+    a.update(kw)
+    return b.lib().cluster_attn_layer_forward(
+        a["X"], a["Wq"], a["Wk"], a["Wv"], a["Wo"], a["B"], a["L"], a["Dm"], a["H"], a["d"],
+        a["nclust"], a["iters"], a["W"], a["alpha"], a["Y"], a["assign"], a["qkv"], a["ws"],
+        a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), INV), (dict(Wo=None), INV), (dict(Y=None), INV), (dict(ws=None), INV),
+    (dict(B=0), INV), (dict(Dm=0), INV), (dict(iters=0), INV), (dict(alpha=2.0), INV),
+    (dict(X=0x100000a8), INV), (dict(ws=0x10000000 * 16 + 64), INV), (dict(wsb=4096), INV),
+    (dict(Y=0x10000000 * 10 + 512), INV),                  # Y inside X
+    (dict(qkv=0x10000000 * 16 + 4096), INV),               # qkv_out inside the workspace
+    (dict(d=32, Dm=128), UNS), (dict(Dm=320), UNS),        # d != 64; Dm != H d
+])
+def test_layer_rejects(kw, code):
+    assert layer(**kw) == code
+
+
+def test_layer_workspace_size():
+    lib = b.lib()
+    n = lib.cluster_attn_layer_workspace_size(16, 512, 768, 12, 64, 16)
+    # transposed weights + Q/K/V + O + staged attention workspace
+    assert n >= 4 * 768 * 768 * 2 + 4 * 16 * 512 * 768 * 2 and n % 256 == 0
+    assert lib.cluster_attn_layer_workspace_size(16, 512, 768, 12, 32, 16) == 0
+    assert lib.cluster_attn_layer_workspace_size(16, 512, 700, 12, 64, 16) == 0
+
+
+def test_gemm_rejects():
+    lib = b.lib()
+    A_, B_, C_ = Q, K, V
+    assert lib.ca_gemm_bf16(None, B_, 64, 64, 64, C_, None) == INV
+    assert lib.ca_gemm_bf16(A_, B_, 0, 64, 64, C_, None) == INV
+    assert lib.ca_gemm_bf16(A_, B_, 64, 64, 64, A_ + 1024, None) == INV   # C overlaps A
+    assert lib.ca_gemm_bf16(A_ + 8, B_, 64, 64, 64, C_, None) == INV
+    assert lib.ca_gemm_bf16(A_, B_, 64, 100, 64, C_, None) == UNS
+    assert lib.ca_gemm_bf16(A_, B_, 64, 64, 96, C_, None) == UNS
