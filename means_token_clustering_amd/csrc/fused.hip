@@ -2,9 +2,9 @@
 // K <= 16, d = 64). One workgroup (512 threads, 8 waves) runs the whole path
 // of one (b, h) slice on chip - Lloyd's k-means, centroid cross-attention,
 // the local window branch and the gather + convex fusion - and touches HBM
-// only to read Q, K, V once and to write the output and the assignment.
-// The LDS footprint (80,000 B) lets two slices share a CU, so one slice's
-// loads overlap another's arithmetic.
+// only to read Q, K, V once and to write the output and the assignment. At
+// most 128 VGPRs per lane and 80,768 bytes of LDS let two slices share a CU,
+// so one slice's loads and barriers overlap the other's arithmetic.
 //
 // Method: model card "Hooshaai/distilbert-sst2-cluster-attention",
 // Architecture Overview figure and Mathematical Formulation 1; "ClusterFormer"
@@ -13,40 +13,48 @@
 // window |i - j| <= floor(W/2), scale 1/sqrt(d).
 //
 // Arithmetic. Every contraction runs on the fp16 matrix cores
-// (v_mfma_f32_16x16x32_f16, fp32 accumulation). Each operand tensor of a
-// slice is first scaled by a power of two 2^-s (exact) so that its largest
-// magnitude is below 2^15; each scaled fp32 value x is then split into two
-// fp16 parts x = h + m + e (h = x rounded toward zero to fp16, m = the
-// remainder x - h, exact in fp32, rounded toward zero to fp16), which leaves
-// |e| <= 2^-21 |x| (2^-24 absolute below the fp16 normal range). A product
-// a.b accumulates h.h, h.m and m.h: relative error of order 2^-20, absolute
-// error far below the tolerances of the outputs and below the near-tie
-// margin of the distance comparisons. Products with an exact 0/1 operand
-// (one-hot cluster sums, counts) are exact up to fp32 accumulation. The
-// scale factors are undone on the fp32 results (scores, outputs); distances
-// stay in the scaled units of Q, which leaves every comparison unchanged.
+// (v_mfma_f32_16x16x32_f16, fp32 accumulation). Each operand
+// tensor of a slice is first scaled by a power of two 2^-s (exact, only when
+// its largest magnitude is outside [2^-3, 2^5) for Q or [2^-3, 2^15) for K
+// and V, and then into the top binade of that range); each
+// scaled fp32 value x is then split into two fp16 parts x = h + m + e (h = x
+// rounded toward zero to fp16, m = the exact fp32 remainder x - h rounded
+// toward zero), which leaves |e| < 2^-20 |x| (2^-24 absolute below the fp16
+// normal range). A product a.b accumulates h.h, h.m and m.h: the dropped
+// terms are below 3 2^-20 |a||b| per element pair. Products with an exact 0/1
+// operand (one-hot cluster sums, counts) are exact up to fp32 accumulation.
+// The scale factors are undone on the fp32 results (scores, outputs);
+// distances stay in the scaled units of Q, which leaves every comparison
+// unchanged.
+//
+// Distances. The score of cluster k for token i is mu_k . q_i - ||mu_k||^2/2
+// (the largest score is the nearest centroid). The -||mu_k||^2/2 term rides in
+// the same MFMA chain as an extra 32-deep chunk: row k of that chunk holds the
+// fp16 split parts of four partial sums over 16 dimensions each, and the
+// query side holds ones, so the matrix core adds them.
 //
 // Layouts (confirmed on gfx950): for 16x16x32, lane l holds A[l%16][8(l/16)+i]
 // and B[8(l/16)+i][l%16], i = 0..7; the 16x16 result has lane l, register r
-// at D[4(l/16)+r][l%16]. Write l16 = l%16 and g = l/16.
+// at D[4(l/16)+r][l%16]. Write
+// l16 = l%16 and g = l/16. ds_read_b64_tr_b16: within each group of 16 lanes,
+// if lane j points at 4 consecutive 16-bit values X_j[0..3], lane i receives
+// X_{4e + i/4}[i%4] for e = 0..3; pointing lane j at row r0 + j/4, column
+// c0 + 4(j%4) of a row-major plane therefore hands lane i the column c0 + i,
+// rows r0 .. r0+3: a transposed MFMA operand straight from LDS.
 //
-// Work split per slice (tile = 16 tokens, NT = ceil(L/16) <= 8):
-//   every wave w < NT: the distances of token tile w (its Q fragments stay in
-//     registers) and the centroid-key scores of key tile w;
-//   waves 0-3: the cluster sums of dim tile w (Q kept in the token-depth
-//     layout) and the centroid context of dim tile w;
-//   waves 4-7: the local window branch of query tiles w-4 and w, run while
-//     waves 0-3 update centroids in the first two iterations (the branch does
-//     not depend on the clustering), and the final gather + fusion of those
-//     tiles.
-//   K and V^T live in LDS as fp16 planes (16-byte chunks XOR-swizzled by the
-//   row against bank conflicts).
+// Work split per slice (tile = 16 tokens, NT = ceil(L/16) <= 8): wave w owns
+// token tile w (distances, local branch, output rows) and key tile w
+// (centroid-key scores); waves 0-3 also own dimension tile w (cluster sums and
+// the centroid context). Q, K, V live in LDS as fp16 h/m planes [128][64]
+// with 16-byte chunks XOR-swizzled by the row; V takes the place of Q once
+// the clustering is done.
 #include "common.h"
 
 namespace ca {
 namespace {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -54,62 +62,81 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kFL = 128;              // max tokens
 constexpr int kFK = 16;               // max clusters
 constexpr int kThreads = 512;         // 8 waves
+constexpr int kQLimit = 5;            // scaled |q| < 2^5 keeps 16 q^2 in fp16 range
+constexpr int kKVLimit = 15;          // scaled |k|, |v| < 2^15
 
 // LDS map (bytes)
-constexpr int kPlaneK = kFL * kD * 2;         // one fp16 plane of K: [128 keys][64 dims]
-constexpr int kPlaneV = kD * kFL * 2;         // one fp16 plane of V^T: [64 dims][128 keys]
-constexpr int kPlaneMu = kFK * kD * 2;        // one fp16 plane of mu: [16][64]
-constexpr int kPlaneRow128 = kFK * kFL * 2;   // [16][128] fp16 (one-hot, P)
+constexpr int kPlane = kFL * kD * 2;          // one fp16 plane [128][64]
+constexpr int kPlaneE = kPlane / 2;           // ... in elements
+constexpr int kPlaneMu = kFK * kD * 2;        // one fp16 plane [16][64]
+constexpr int kPlaneMuE = kPlaneMu / 2;
+constexpr int kPlaneRow = kFK * kFL * 2;      // one fp16 plane [16][128] (one-hot, P)
+constexpr int kPlaneRowE = kPlaneRow / 2;
+constexpr int kMuXCols = 32;                  // [16][32] fp16: -||mu||^2/2 parts
+constexpr int kVcRow = 68;                    // fp32 V^cent row stride
 constexpr int kOffK = 0;
-constexpr int kOffV = kOffK + 2 * kPlaneK;
-constexpr int kOffR = kOffV + 2 * kPlaneV;    // shared region: mu planes + one-hot, later P planes
-constexpr int kOffMuP = kOffR;
-constexpr int kOffOH = kOffR + 2 * kPlaneMu;
-constexpr int kOffP = kOffR;
-constexpr int kSizeR = 2 * kPlaneRow128;
-constexpr int kOffVc = kOffR + kSizeR;        // fp32 V^cent [16][68]
-constexpr int kVcRow = 68;
-constexpr int kOffXm = kOffVc + kFK * kVcRow * 4;   // fp32 [16][8] wave maxima
-constexpr int kOffXl = kOffXm + kFK * 8 * 4;        // fp32 [16][8] wave sums
-constexpr int kOffN2 = kOffXl + kFK * 8 * 4;        // fp32 [4][16] partial ||mu||^2
-constexpr int kOffC = kOffN2 + 4 * kFK * 4;         // int [128] assignment
-constexpr int kOffMax = kOffC + kFL * 4;            // uint [8][4] max |x| bits
+constexpr int kOffQV = kOffK + 2 * kPlane;    // Q planes, then V planes
+constexpr int kOffMu = kOffQV + 2 * kPlane;
+constexpr int kOffOH = kOffMu + 2 * kPlaneMu;
+constexpr int kOffP = kOffMu;                 // P planes reuse mu + one-hot
+constexpr int kOffMuX = kOffOH + kPlaneRow;
+constexpr int kOffVc = kOffMuX + kFK * kMuXCols * 2;
+constexpr int kOffC = kOffVc + kFK * kVcRow * 4;
+constexpr int kOffXm = kOffC + kFL * 4;
+constexpr int kOffXl = kOffXm + kFK * 8 * 4;
+constexpr int kOffMax = kOffXl + kFK * 8 * 4;
 constexpr int kLdsTotal = kOffMax + 8 * 4 * 4;
-static_assert(2 * kPlaneMu + kPlaneRow128 <= kSizeR, "region R");
+static_assert(2 * kPlaneRow == 2 * kPlaneMu + kPlaneRow, "P planes fill mu + one-hot exactly");
 static_assert(kLdsTotal <= 81920, "two workgroups per CU");
+
+constexpr uint32_t kOneH2 = 0x3c003c00u;      // two fp16 1.0
+constexpr uint16_t kNegInfH = 0xfc00u;        // fp16 -inf
 
 struct Sp8 {  // 8 values as two fp16 planes (pairs packed low-first)
     u32x4_t h, m;
 };
+struct Sp4 {  // 4 values as two fp16 planes
+    u32x2_t h, m;
+};
 
+// remainder x - h for the low / high fp16 half of h, in one exact fma
+__device__ __forceinline__ float rem_lo(float x, uint32_t h) {
+    float r;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+    return r;
+}
+__device__ __forceinline__ float rem_hi(float x, uint32_t h) {
+    float r;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
+    return r;
+}
 // x0, x1 -> packed fp16 pairs h and m with x = h + m + e
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m) {
-    const auto a = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-    const float r0 = x0 - (float)a[0];
-    const float r1 = x1 - (float)a[1];
-    const auto b = __builtin_amdgcn_cvt_pkrtz(r0, r1);
-    h = __builtin_bit_cast(uint32_t, a);
-    m = __builtin_bit_cast(uint32_t, b);
+    h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+    m = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rem_lo(x0, h), rem_hi(x1, h)));
 }
-
 __device__ __forceinline__ Sp8 split8(const float *x) {
     uint32_t h[4], m[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
     return Sp8{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{m[0], m[1], m[2], m[3]}};
 }
+__device__ __forceinline__ Sp4 split4(float x0, float x1, float x2, float x3) {
+    uint32_t h0, m0, h1, m1;
+    split2(x0, x1, h0, m0);
+    split2(x2, x3, h1, m1);
+    return Sp4{u32x2_t{h0, h1}, u32x2_t{m0, m1}};
+}
 
 __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
-
 // c += a . b from the three leading partial products (smallest first)
 __device__ __forceinline__ f32x4_t mma3(const Sp8 &a, const Sp8 &b, f32x4_t c) {
     c = mma(a.m, b.h, c);
     c = mma(a.h, b.m, c);
-    c = mma(a.h, b.h, c);
-    return c;
+    return mma(a.h, b.h, c);
 }
 
 constexpr f32x4_t kZero4 = {0.f, 0.f, 0.f, 0.f};
@@ -142,23 +169,21 @@ __device__ __forceinline__ float col_max(float v) {
     pair32(__float_as_uint(v), a, b);
     return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
-// lexicographic (value, index) minimum over the four lane groups of a column
-__device__ __forceinline__ void col_argmin(float &best, int &bk) {
+// (score, index) maximum over the four lane groups of a column. Lane group g
+// holds indices 4g .. 4g+3, so taking the upper half only when it is strictly
+// larger keeps the lowest index among equal scores.
+__device__ __forceinline__ int col_argmax(float best, int bk) {
     uint32_t a, b, ia, ib;
     pair16(__float_as_uint(best), a, b);
     pair16((uint32_t)bk, ia, ib);
-    float fa = __uint_as_float(a), fb = __uint_as_float(b);
-    int ka = (int)ia, kb = (int)ib;
-    if (lex_less(fb, kb, fa, ka)) { fa = fb; ka = kb; }
-    pair32(__float_as_uint(fa), a, b);
-    pair32((uint32_t)ka, ia, ib);
-    fa = __uint_as_float(a); fb = __uint_as_float(b);
-    ka = (int)ia; kb = (int)ib;
-    if (lex_less(fb, kb, fa, ka)) { fa = fb; ka = kb; }
-    best = fa;
-    bk = ka;
+    bool up = __uint_as_float(b) > __uint_as_float(a);
+    best = up ? __uint_as_float(b) : __uint_as_float(a);
+    bk = up ? (int)ib : (int)ia;
+    pair32(__float_as_uint(best), a, b);
+    pair32((uint32_t)bk, ia, ib);
+    up = __uint_as_float(b) > __uint_as_float(a);
+    return up ? (int)ib : (int)ia;
 }
-// maximum of an unsigned value over the whole wave
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
@@ -182,13 +207,6 @@ __device__ __forceinline__ void load8(const T *p, float *x) {
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
-template <typename T>
-__device__ __forceinline__ float load1(const T *p);
-template <>
-__device__ __forceinline__ float load1<float>(const float *p) { return *p; }
-template <>
-__device__ __forceinline__ float load1<bf16_t>(const bf16_t *p) { return bf16_to_f32(p->bits); }
-
 // 8 consecutive elements of row `row` (zeros when row >= L)
 template <typename T, bool FULL>
 __device__ __forceinline__ void load_row8(const T *base, int row, int L, int col, float *x) {
@@ -203,31 +221,22 @@ __device__ __forceinline__ void load_row8(const T *base, int row, int L, int col
         }
     }
 }
-// rows r0..r0+7 of column `col` (zeros for rows >= L)
-template <typename T, bool FULL>
-__device__ __forceinline__ void load_col8(const T *base, int r0, int L, int col, float *x) {
+__device__ __forceinline__ float absmax8(const float *x, float m) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = r0 + i;
-        if (FULL) {
-            x[i] = load1<T>(base + (long)row * kD + col);
-        } else {
-            const int rc = row < L ? row : L - 1;
-            const float v = load1<T>(base + (long)rc * kD + col);
-            x[i] = row < L ? v : 0.f;
-        }
-    }
-}
-
-__device__ __forceinline__ uint32_t absmax8(const float *x, uint32_t m) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(x[i]) & 0x7fffffffu);
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
     return m;
 }
-// power-of-two scale that brings the largest magnitude below 2^15
-__device__ __forceinline__ int scale_shift(uint32_t maxbits) {
-    const int e = (int)(maxbits >> 23) - 127;   // max < 2^(e+1)
-    return e + 1 > 15 ? e + 1 - 15 : 0;
+// Power-of-two shift s for a tensor whose largest magnitude has bits
+// `maxbits`: 0 when that maximum lies in [2^-3, 2^limit), where the fp16 split
+// keeps every element above 2^-14 to 2^-20 relative and the rest to 2^-21 of
+// the maximum; otherwise s brings the maximum into [2^(limit-1), 2^limit)
+// (at most 2^100 up). Zero or subnormal maxima need no scaling.
+__device__ __forceinline__ int scale_shift(uint32_t maxbits, int limit) {
+    if (maxbits < 0x00800000u) return 0;
+    const int e = (int)(maxbits >> 23) - 127;   // 2^e <= max < 2^(e+1)
+    if (e >= -3 && e < limit) return 0;
+    const int s = e + 1 - limit;
+    return s < -100 ? -100 : s;
 }
 
 // ---- swizzled fp16 planes (element offsets). 64-wide rows: 8 chunks of 8
@@ -239,119 +248,63 @@ __device__ __forceinline__ int off128(int row, int col) {
     return row * 128 + ((((col >> 3) ^ (row & 15))) << 3) + (col & 7);
 }
 __device__ __forceinline__ u32x4_t ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4_t *>(p); }
-__device__ __forceinline__ u32x2_t ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2_t *>(p); }
 __device__ __forceinline__ void st16(uint16_t *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 __device__ __forceinline__ void st8(uint16_t *p, u32x2_t v) { *reinterpret_cast<u32x2_t *>(p) = v; }
 
-// fragment of a 64-wide plane pair (row `row`, cols 32c + 8g ..)
+// row fragment of a 64-wide plane pair (row `row`, cols 32c + 8g ..)
 __device__ __forceinline__ Sp8 frag64(const uint16_t *planes, int plane, int row, int c, int g) {
     const int o = off64(row, 32 * c + 8 * g);
     return Sp8{ld16(planes + o), ld16(planes + plane + o)};
 }
-// fragment of a 128-wide plane pair (row `row`, cols 32c + 8g ..)
-__device__ __forceinline__ Sp8 frag128(const uint16_t *planes, int plane, int row, int c, int g) {
-    const int o = off128(row, 32 * c + 8 * g);
-    return Sp8{ld16(planes + o), ld16(planes + plane + o)};
+// transposed 4-deep read: lane l16 receives rows r0 .. r0+3 of column
+// c0 + l16 of a 64-wide plane (ds_read_b64_tr_b16; r0 may differ between
+// the four 16-lane groups)
+__device__ __forceinline__ u32x2_t col4(const uint16_t *plane, int r0, int c0, int l16) {
+    typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+    const uint16_t *p = plane + off64(r0 + (l16 >> 2), c0 + 4 * (l16 & 3));
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
+    return __builtin_bit_cast(u32x2_t, v);
 }
-// Keys are stored in V^T and P planes in "score-tile order": within each
-// chunk of 32 keys (two key tiles), position 8g + 4h + i holds key
-// 16h + 4g + i (h = tile of the pair, g = lane group, i = 0..3). That is the
-// order in which a 16x16 score tile leaves keys in the registers of lane
-// group g, so a 32-deep product over a tile pair reads one 16-byte run.
-__device__ __forceinline__ int vpos(int key) {
-    const int r = key & 31;
-    return (key & ~31) + (((r & 15) >> 2) << 3) + ((r >> 4) << 2) + (r & 3);
-}
-
-// Local window state of one query tile: scores, then probabilities, of the
-// key tile pairs c0 .. c0 + nch - 1 (tiles 2c, 2c+1), register-resident and
-// statically indexed; keys outside the window get probability 0.
-template <bool NARROW>
-struct LocalTile {
-    static constexpr int kMaxC = NARROW ? 2 : 4;
-    float sc[2 * kMaxC][4];
-    float lsum;
-    int c0, nch;
-};
-
-template <bool FULL, bool NARROW>
-__device__ __forceinline__ void local_scores(const uint16_t *sK, const Sp8 *qf, int qt, int NT,
-                                             int L, int r, float sscale, int l16, int g,
-                                             LocalTile<NARROW> &st) {
-    constexpr int MAXC = LocalTile<NARROW>::kMaxC;
-    const int qi = 16 * qt + l16;
-    // key tiles touched by the window of the tile (radius <= 16: qt-1 .. qt+1)
-    const int lo_key = 16 * qt - r, hi_key = 16 * qt + 15 + r;
-    const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
-    const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
-    st.c0 = kt_lo >> 1;
-    st.nch = (kt_hi >> 1) - st.c0 + 1;
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int q = 0; q < 2 * MAXC; ++q) {
-        if ((q >> 1) < st.nch) {
-            const int kt = 2 * st.c0 + q;   // may lie past NT: zero rows, masked below
-            f32x4_t a0 = kZero4, a1 = kZero4;
-            a0 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 0, g), qf[0], a0);
-            a1 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 1, g), qf[1], a1);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = 16 * kt + 4 * g + rr;   // a[rr] = k_key . q_qi
-                const int dist = key > qi ? key - qi : qi - key;
-                const bool in = (FULL || key < L) && dist <= r;
-                st.sc[q][rr] = in ? (a0[rr] + a1[rr]) * sscale : -__builtin_inff();
-                m = fmaxf(m, st.sc[q][rr]);
-            }
-        } else {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) st.sc[q][rr] = -__builtin_inff();
-        }
-    }
-    m = col_max(m);
-    float ls = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2 * MAXC; ++q) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const float p = __builtin_amdgcn_exp2f(st.sc[q][rr] - m);   // exp2(-inf) = 0
-            st.sc[q][rr] = p;
-            ls += p;
-        }
-    }
-    st.lsum = col_sum(ls);
+// 8-deep transposed fragment from rows r0 .. r0+3 and r1 .. r1+3
+__device__ __forceinline__ Sp8 colfrag8(const uint16_t *planes, int r0, int r1, int c0, int l16) {
+    const u32x2_t h0 = col4(planes, r0, c0, l16), h1 = col4(planes, r1, c0, l16);
+    const u32x2_t m0 = col4(planes + kPlaneE, r0, c0, l16), m1 = col4(planes + kPlaneE, r1, c0, l16);
+    return Sp8{u32x4_t{h0[0], h0[1], h1[0], h1[1]}, u32x4_t{m0[0], m0[1], m1[0], m1[1]}};
 }
 
-// Window of radius <= 16 (key tiles qt-1, qt, qt+1): score + band bias in
-// one fma (bias[d][rr] = 0 inside the band, -inf outside, precomputed per
-// lane), base-2 softmax (the score scale carries log2 e), then P V over the
-// aligned tile pairs that hold the three tiles.
+// Local window of radius <= 16 for query tile qt: scores against key tiles
+// qt-1, qt, qt+1 (others are outside every window of the tile), base-2
+// softmax, then O^T = V^T P^T: the pair (qt-1, qt) as one 32-deep product and
+// tile qt+1 as a 16-deep one. Tiles outside [0, NT) get probability 0; their
+// V reads are moved onto tile qt (finite values times zero).
 template <bool FULL>
-__device__ __forceinline__ void local_tile_narrow(const uint16_t *sK, const uint16_t *sV,
-                                                  const Sp8 *qf, int qt, int NT, int L,
-                                                  float sscale2, const float (*bias)[4], int l16,
-                                                  int g, f32x4_t *o, float &lsum) {
+__device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
+                                             int qt, int NT, int L, int rad, float sscale2,
+                                             int l16, int g, f32x4_t *o, float &lsum) {
     float s[3][4];
     float m = -__builtin_inff();
+    const int rel0 = 4 * g - l16;   // key - query within aligned tiles
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
         if (kt >= 0 && kt < NT) {
-            f32x4_t a0 = kZero4, a1 = kZero4;
-            a0 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 0, g), qf[0], a0);
-            a1 = mma3(frag64(sK, kPlaneK / 2, 16 * kt + l16, 1, g), qf[1], a1);
+            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * kt + l16, 0, g), qf[0], kZero4);
+            a = mma3(frag64(sK, kPlaneE, 16 * kt + l16, 1, g), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
-                float v = fmaf(a0[rr] + a1[rr], sscale2, bias[d][rr]);
-                if (!FULL && 16 * kt + 4 * g + rr >= L) v = -__builtin_inff();
-                s[d][rr] = v;
-                m = fmaxf(m, v);
+                const int rel = 16 * (d - 1) + rel0 + rr;
+                bool in = rel <= rad && -rel <= rad;
+                if (!FULL) in = in && 16 * kt + 4 * g + rr < L;
+                s[d][rr] = in ? a[rr] * sscale2 : -__builtin_inff();
+                m = fmaxf(m, s[d][rr]);
             }
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) s[d][rr] = -__builtin_inff();
         }
     }
-    m = col_max(m);
+    m = col_max(m);   // finite: every query sees itself
     float ls = 0.f;
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
@@ -362,76 +315,87 @@ __device__ __forceinline__ void local_tile_narrow(const uint16_t *sK, const uint
         }
     }
     lsum = col_sum(ls);
-    if ((qt & 1) == 0) {
-        if (qt >= 1) {   // pair (qt-2, qt-1): only tile qt-1
-            const float pv[8] = {0.f, 0.f, 0.f, 0.f, s[0][0], s[0][1], s[0][2], s[0][3]};
-            const Sp8 pf = split8(pv);
+    const float pa[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
+    const Sp8 pA = split8(pa);
+    const float pb[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
+    const Sp8 pB = split8(pb);
+    const int r0 = qt >= 1 ? 16 * (qt - 1) + 4 * g : 16 * qt + 4 * g;
+    const int r1 = 16 * qt + 4 * g;
+    const int r2 = qt + 1 < NT ? 16 * (qt + 1) + 4 * g : 16 * qt + 4 * g;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, (qt >> 1) - 1, g), pf, o[j]);
-        }
-        {   // pair (qt, qt+1)
-            const float pv[8] = {s[1][0], s[1][1], s[1][2], s[1][3], s[2][0], s[2][1], s[2][2], s[2][3]};
-            const Sp8 pf = split8(pv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, qt >> 1, g), pf, o[j]);
-        }
-    } else {
-        {   // pair (qt-1, qt)
-            const float pv[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
-            const Sp8 pf = split8(pv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, qt >> 1, g), pf, o[j]);
-        }
-        if (qt + 1 < NT) {   // pair (qt+1, qt+2): only tile qt+1
-            const float pv[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
-            const Sp8 pf = split8(pv);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, (qt >> 1) + 1, g), pf, o[j]);
-        }
+    for (int j = 0; j < 4; ++j) {
+        f32x4_t a = mma3(colfrag8(sV, r0, r1, 16 * j, l16), pA, kZero4);
+        o[j] = mma3(colfrag8(sV, r2, r2, 16 * j, l16), pB, a);   // second half: zero weights
     }
 }
 
-// o[j] += P V over the tile pairs of st (32-deep products)
-template <bool NARROW>
-__device__ __forceinline__ void local_pv(const uint16_t *sV, int l16, int g,
-                                         const LocalTile<NARROW> &st, f32x4_t *o) {
-    constexpr int MAXC = LocalTile<NARROW>::kMaxC;
+// Local window of any radius: key tiles in [qt - ceil(r/16), qt + ceil(r/16)]
+// two at a time with a running maximum (online softmax) and 32-deep P V
+// products; a missing second tile gets zero weights on repeated V rows.
+template <bool FULL>
+__device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
+                                           int qt, int NT, int L, int rad, float sscale2,
+                                           int l16, int g, f32x4_t *o, float &lsum) {
+    const int qi = 16 * qt + l16;
+    const int lo_key = 16 * qt - rad, hi_key = 16 * qt + 15 + rad;
+    const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
+    const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
+    float M = -__builtin_inff(), ls = 0.f;
+    for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+        const bool two = kt + 1 <= kt_hi;
+        float s[8];
+        float mt = -__builtin_inff();
 #pragma unroll
-    for (int q = 0; q < MAXC; ++q) {
-        if (q < st.nch) {
-            const float pv[8] = {st.sc[2 * q][0],     st.sc[2 * q][1],     st.sc[2 * q][2],
-                                 st.sc[2 * q][3],     st.sc[2 * q + 1][0], st.sc[2 * q + 1][1],
-                                 st.sc[2 * q + 1][2], st.sc[2 * q + 1][3]};
-            const Sp8 pf = split8(pv);
-            const int c = st.c0 + q;
+        for (int h = 0; h < 2; ++h) {
+            const int ktt = two ? kt + h : kt;
+            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * ktt + l16, 0, g), qf[0], kZero4);
+            a = mma3(frag64(sK, kPlaneE, 16 * ktt + l16, 1, g), qf[1], a);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = mma3(frag128(sV, kPlaneV / 2, 16 * j + l16, c, g), pf, o[j]);
+            for (int rr = 0; rr < 4; ++rr) {
+                const int key = 16 * ktt + 4 * g + rr;
+                const int dist = key > qi ? key - qi : qi - key;
+                const bool in = (FULL || key < L) && dist <= rad && (h == 0 || two);
+                s[4 * h + rr] = in ? a[rr] * sscale2 : -__builtin_inff();
+                mt = fmaxf(mt, s[4 * h + rr]);
+            }
         }
+        mt = col_max(mt);
+        const float Mn = fmaxf(M, mt);
+        const float Ms = Mn == -__builtin_inff() ? 0.f : Mn;   // nothing seen yet
+        const float f = __builtin_amdgcn_exp2f(M - Ms);
+        M = Mn;
+        ls *= f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            s[i] = __builtin_amdgcn_exp2f(s[i] - Ms);
+            ls += s[i];
+        }
+        const Sp8 p = split8(s);
+        const int r0 = 16 * kt + 4 * g, r1 = two ? 16 * (kt + 1) + 4 * g : r0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = mma3(colfrag8(sV, r0, r1, 16 * j, l16), p, o[j] * f);
     }
+    lsum = col_sum(ls);
 }
 
 }  // namespace
 
 template <typename T, bool FULL, bool NARROW>
-__global__ __launch_bounds__(kThreads, 1) void cluster_attn_fused_kernel(
+__global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, T *__restrict__ out,
     int32_t *__restrict__ assign_out) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
-    uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kOffV);
-    uint16_t *sMuP = reinterpret_cast<uint16_t *>(smem + kOffMuP);
+    uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
+    uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kOffMu);
     uint16_t *sOH = reinterpret_cast<uint16_t *>(smem + kOffOH);
     uint16_t *sP = reinterpret_cast<uint16_t *>(smem + kOffP);
+    uint16_t *sMuX = reinterpret_cast<uint16_t *>(smem + kOffMuX);
     float *sVc = reinterpret_cast<float *>(smem + kOffVc);
+    int *sC = reinterpret_cast<int *>(smem + kOffC);
     float *sXm = reinterpret_cast<float *>(smem + kOffXm);
     float *sXl = reinterpret_cast<float *>(smem + kOffXl);
-    float *sN2 = reinterpret_cast<float *>(smem + kOffN2);
-    int *sC = reinterpret_cast<int *>(smem + kOffC);
     uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kOffMax);
 
     const int tid = threadIdx.x;
@@ -441,56 +405,97 @@ __global__ __launch_bounds__(kThreads, 1) void cluster_attn_fused_kernel(
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;
     const long base = slice * (long)L * kD;
-    const T *Qs = Q + base;
-    const T *Ks = Kx + base;
-    const T *Vs = Vx + base;
-    const int nitems = w < 4 ? 1 : 3;     // K and V^T items of this thread
-    const bool lower = w < 4;             // waves 0-3: cluster sums / centroid context
-    const int tileA = w - 4, tileB = w;   // waves 4-7: local query tiles
 
     // ------------------------------------------------------------ fetch
-    float kraw[3][8], vraw[3][8], qraw[2][8], qxraw[4][8];
+    // Q rows of token tile w (dims 32c + 8g ..); K and V items (row it/8,
+    // dims 8 (it%8) ..), it = tid and tid + 512
+    float qraw[2][8], kraw[2][8], vraw[2][8];
 #pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        if (n < nitems) {
-            const int it = tid + 256 * n;
-            load_row8<T, FULL>(Ks, it >> 3, L, (it & 7) * 8, kraw[n]);
-            load_col8<T, FULL>(Vs, (it >> 6) * 8, L, it & 63, vraw[n]);
-        }
+    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Qs, tok, L, 32 * c + 8 * g, qraw[c]);
-    if (lower) {
-        // dim tile w over tokens 32c + 8g + i (depth of the cluster sums)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) load_col8<T, FULL>(Qs, 32 * c + 8 * g, L, 16 * w + l16, qxraw[c]);
-    } else {
-        // query tile w-4 for the local branch
-#pragma unroll
-        for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Qs, 16 * tileA + l16, L, 32 * c + 8 * g, qxraw[c]);
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
     }
     {   // per-tensor largest magnitude (bit patterns of |x| order like the values)
-        uint32_t mq = 0, mk = 0, mv = 0;
-        mq = absmax8(qraw[0], absmax8(qraw[1], mq));
-#pragma unroll
-        for (int n = 0; n < 3; ++n) {
-            if (n < nitems) {
-                mk = absmax8(kraw[n], mk);
-                mv = absmax8(vraw[n], mv);
-            }
-        }
-        mq = wave_max_u(mq);
-        mk = wave_max_u(mk);
-        mv = wave_max_u(mv);
+        const float mq = absmax8(qraw[1], absmax8(qraw[0], 0.f));
+        const float mk = absmax8(kraw[1], absmax8(kraw[0], 0.f));
+        const float mv = absmax8(vraw[1], absmax8(vraw[0], 0.f));
+        const uint32_t bq = wave_max_u(__float_as_uint(mq));
+        const uint32_t bk = wave_max_u(__float_as_uint(mk));
+        const uint32_t bv = wave_max_u(__float_as_uint(mv));
         if (lane == 0) {
-            sMax[w * 4 + 0] = mq;
-            sMax[w * 4 + 1] = mk;
-            sMax[w * 4 + 2] = mv;
+            sMax[w * 4 + 0] = bq;
+            sMax[w * 4 + 1] = bk;
+            sMax[w * 4 + 2] = bv;
         }
     }
-    // clear the one-hot matrix; padded tokens join no cluster
+
+    // ------------------------------------------------------------ split
+    // Q planes + the register fragments qf of token tile w, K planes, and the
+    // strided initial centroids mu_k = Q[floor(k L / Kc)] with their
+    // -||mu||^2/2 parts; first without scaling (the usual case), redone
+    // below if a tensor is too large for fp16.
+    Sp8 qf[2];
+    const int kinit = (tok * Kc + L - 1) / L;   // the only k that can start at tok
+    const bool owner = tok < L && kinit < Kc && (kinit * L) / Kc == tok;
+    auto split_qk = [&](float fq, float fk, bool scaled) {
+        float n2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                x[i] = scaled ? qraw[c][i] * fq : qraw[c][i];
+                n2 = fmaf(x[i], x[i], n2);
+            }
+            qf[c] = split8(x);
+            const int o = off64(tok, 32 * c + 8 * g);
+            st16(sQV + o, qf[c].h);
+            st16(sQV + kPlaneE + o, qf[c].m);
+            if (owner) {
+                const int om = off64(kinit, 32 * c + 8 * g);
+                st16(sMu + om, qf[c].h);
+                st16(sMu + kPlaneMuE + om, qf[c].m);
+            }
+        }
+        if (owner) {
+            uint32_t h, m;
+            split2(-0.5f * n2, 0.f, h, m);
+            sMuX[kinit * kMuXCols + 2 * g] = (uint16_t)(h & 0xffffu);
+            sMuX[kinit * kMuXCols + 2 * g + 1] = (uint16_t)(m & 0xffffu);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int it = tid + kThreads * n;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = scaled ? kraw[n][i] * fk : kraw[n][i];
+            const Sp8 sp = split8(x);
+            const int o = off64(it >> 3, (it & 7) * 8);
+            st16(sK + o, sp.h);
+            st16(sK + kPlaneE + o, sp.m);
+        }
+    };
+    split_qk(1.f, 1.f, false);
+    // one-hot matrix cleared; clusters >= Kc: zero centroid rows and a -inf
+    // score part, so they are never chosen; unused columns of the parts zero
     reinterpret_cast<u32x2_t *>(sOH)[tid] = u32x2_t{0u, 0u};
-    if (!FULL && tid < kFL && tid >= L) sC[tid] = -1;
+    for (int e = tid; e < kFK * kMuXCols; e += kThreads) {
+        const int kk = e / kMuXCols, j = e % kMuXCols;
+        if (kk >= Kc) sMuX[e] = j == 0 ? kNegInfH : (uint16_t)0;
+        else if (j >= 8) sMuX[e] = 0;
+    }
+    for (int e = tid; e < (kFK - Kc) * kD; e += kThreads) {
+        const int kk = Kc + e / kD, dd = e % kD;
+        sMu[off64(kk, dd)] = 0;
+        sMu[kPlaneMuE + off64(kk, dd)] = 0;
+    }
     __syncthreads();
 
     int sq, sk, sv;
@@ -498,178 +503,73 @@ __global__ __launch_bounds__(kThreads, 1) void cluster_attn_fused_kernel(
         uint32_t mq = 0, mk = 0, mv = 0;
 #pragma unroll
         for (int ww = 0; ww < 8; ++ww) {
-            mq = max(mq, sMax[ww * 4 + 0]);
-            mk = max(mk, sMax[ww * 4 + 1]);
-            mv = max(mv, sMax[ww * 4 + 2]);
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sMax + 4 * ww);
+            mq = max(mq, v[0]);
+            mk = max(mk, v[1]);
+            mv = max(mv, v[2]);
         }
-        sq = scale_shift(mq);
-        sk = scale_shift(mk);
-        sv = scale_shift(mv);
+        sq = scale_shift(mq, kQLimit);
+        sk = scale_shift(mk, kKVLimit);
+        sv = scale_shift(mv, kKVLimit);
     }
-    const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk),
-                fv = __builtin_ldexpf(1.f, -sv);
-    const float sscale = __builtin_ldexpf(0.125f, sq + sk);   // scores: 1/sqrt(64) * 2^(sq+sk)
-    const float sscale2 = sscale * 1.4426950408889634f;      // the same in base-2 exponent units
+    if (sq != 0 || sk != 0) {   // uniform over the workgroup; reload rather than keep
+#pragma unroll
+        for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int it = tid + kThreads * n;
+            load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
+        }
+        split_qk(__builtin_ldexpf(1.f, -sq), __builtin_ldexpf(1.f, -sk), true);
+        __syncthreads();
+    }
+    const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
     const float vunscale = __builtin_ldexpf(1.f, sv);
 
-    // ------------------------------------------------------------ split
-    if (sk != 0 || sv != 0) {
-#pragma unroll
-        for (int n = 0; n < 3; ++n) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                kraw[n][i] *= fk;
-                vraw[n][i] *= fv;
-            }
-        }
-    }
-    if (sq != 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qraw[c][i] *= fq;
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qxraw[c][i] *= fq;
-        }
-    }
-#pragma unroll
-    for (int n = 0; n < 3; ++n) {
-        if (n < nitems) {
-            const int it = tid + 256 * n;
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
-            const Sp8 sp = split8(x);
-            const int o = off64(it >> 3, (it & 7) * 8);
-            st16(sK + o, sp.h);
-            st16(sK + kPlaneK / 2 + o, sp.m);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = vraw[n][i];
-            const Sp8 sv8 = split8(x);
-            const int p0 = vpos((it >> 6) * 8);          // keys 8kg..8kg+3; +4..+7 sit 8 further
-            const int ov0 = off128(it & 63, p0), ov1 = off128(it & 63, p0 + 8);
-            st8(sV + ov0, u32x2_t{sv8.h.x, sv8.h.y});
-            st8(sV + ov1, u32x2_t{sv8.h.z, sv8.h.w});
-            st8(sV + kPlaneV / 2 + ov0, u32x2_t{sv8.m.x, sv8.m.y});
-            st8(sV + kPlaneV / 2 + ov1, u32x2_t{sv8.m.z, sv8.m.w});
-        }
-    }
-    Sp8 qf[2], qx[4];
-    float n2init = 0.f;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i] = qraw[c][i];
-            n2init = fmaf(x[i], x[i], n2init);
-        }
-        qf[c] = split8(x);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        if (c < 2 || lower) {
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = qxraw[c][i];
-            qx[c] = split8(x);
-        }
-    }
-    // strided initial centroids mu_k = Q[floor(k L / Kc)]: the lanes holding
-    // token floor(k L / Kc) store its planes and partial squared norms
-    {
-        const int k = (tok * Kc + L - 1) / L;   // the only k that can start at tok
-        if (tok < L && k < Kc && (k * L) / Kc == tok) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int o = off64(k, 32 * c + 8 * g);
-                st16(sMuP + o, qf[c].h);
-                st16(sMuP + kPlaneMu / 2 + o, qf[c].m);
-            }
-            sN2[g * kFK + k] = n2init;
-        }
-        // centroids beyond Kc stay zero and are never chosen
-        for (int e = tid; e < (kFK - Kc) * kD; e += kThreads) {
-            const int kk = Kc + e / kD, dd = e % kD;
-            sMuP[off64(kk, dd)] = 0;
-            sMuP[kPlaneMu / 2 + off64(kk, dd)] = 0;
-            if (dd < 4) sN2[dd * kFK + kk] = 0.f;
-        }
-    }
-    __syncthreads();
-
-    // local window branch of waves 4-7 (query tiles w-4 and w): tile A runs in
-    // the slot of iteration 1, tile B in the slot of iteration 2 (both in
-    // iteration 1 when there is only one); each tile has its own registers
-    f32x4_t oA[4], oB[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) oA[j] = oB[j] = kZero4;
-    float lsumA = 1.f, lsumB = 1.f;
-    const int rad = radius < L ? radius : L;
-    const int slotB = iters < 2 ? 1 : 2;
-    // band bias of the narrow window for key tiles qt-1, qt, qt+1 (d = 0, 1, 2)
-    float bias[3][4];
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int rel = 16 * (d - 1) + 4 * g + rr - l16;   // key - query
-            bias[d][rr] = (rel <= rad && -rel <= rad) ? 0.f : -__builtin_inff();
-        }
-    }
-
     // ------------------------------------------------------------ Lloyd
+    const u32x4_t ones_g0 = g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
     int cprev = -1;
     for (int t = 1; t <= iters; ++t) {
         if (w < NT) {
-            // a[r] = mu_{4g+r} . q_tok - ||mu_{4g+r}||^2 / 2 (halving is exact)
-            f32x4_t a0, a1 = kZero4;
-            {
-                const float4 p0 = *reinterpret_cast<const float4 *>(sN2 + 0 * kFK + 4 * g);
-                const float4 p1 = *reinterpret_cast<const float4 *>(sN2 + 1 * kFK + 4 * g);
-                const float4 p2 = *reinterpret_cast<const float4 *>(sN2 + 2 * kFK + 4 * g);
-                const float4 p3 = *reinterpret_cast<const float4 *>(sN2 + 3 * kFK + 4 * g);
-                a0[0] = -0.5f * (((p0.x + p1.x) + p2.x) + p3.x);
-                a0[1] = -0.5f * (((p0.y + p1.y) + p2.y) + p3.y);
-                a0[2] = -0.5f * (((p0.z + p1.z) + p2.z) + p3.z);
-                a0[3] = -0.5f * (((p0.w + p1.w) + p2.w) + p3.w);
-            }
-            a0 = mma3(frag64(sMuP, kPlaneMu / 2, l16, 0, g), qf[0], a0);
-            a1 = mma3(frag64(sMuP, kPlaneMu / 2, l16, 1, g), qf[1], a1);
-            // D = ||mu||^2 - 2 mu.q = -2 (a0 + a1), in the scaled units of Q
-            float best = __builtin_inff();
-            int bk = 0x7fffffff;
+            // a[r] = mu_k . q_tok - ||mu_k||^2 / 2, k = 4g + r (scaled units of Q)
+            f32x4_t a = mma(ld16(sMuX + l16 * kMuXCols + 8 * g), ones_g0, kZero4);
+            a = mma3(frag64(sMu, kPlaneMuE, l16, 0, g), qf[0], a);
+            a = mma3(frag64(sMu, kPlaneMuE, l16, 1, g), qf[1], a);
+            float best = a[0];
+            int bk = 4 * g;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int k = 4 * g + rr;
-                const float D = k < Kc ? -2.f * (a0[rr] + a1[rr]) : __builtin_inff();
-                if (lex_less(D, k, best, bk)) { best = D; bk = k; }
+            for (int rr = 1; rr < 4; ++rr) {
+                const bool up = a[rr] > best;
+                best = up ? a[rr] : best;
+                bk = up ? 4 * g + rr : bk;
             }
-            col_argmin(best, bk);
-            if (bk >= Kc) bk = 0;   // only if every distance was NaN
+            bk = col_argmax(best, bk);
             if (g == 0 && (FULL || tok < L)) {
-                sC[tok] = bk;
-                if (cprev >= 0) sOH[off128(cprev, tok)] = 0;
-                sOH[off128(bk, tok)] = 0x3c00;   // fp16 1.0
-                cprev = bk;
+                if (bk != cprev) {
+                    if (cprev >= 0) sOH[off128(cprev, tok)] = 0;
+                    sOH[off128(bk, tok)] = 0x3c00;   // fp16 1.0
+                    cprev = bk;
+                }
+                if (t == iters) sC[tok] = bk;
             }
         }
         __syncthreads();
-        if (lower) {
-            // (Q^T one-hot)[dim 16w + 4g + rr][centroid l16] and the sizes n_l16
+        if (w < 4) {
+            // (Q^T one-hot)[dim 16w + 4g + rr][cluster l16] and the sizes n_l16
             f32x4_t sh = kZero4, sm = kZero4, cnt = kZero4;
-            const u32x4_t ones = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};
+            const u32x4_t ones = {kOneH2, kOneH2, kOneH2, kOneH2};
+            const int nch = (NT + 1) >> 1;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const u32x4_t oh = ld16(sOH + off128(l16, 32 * c + 8 * g));
-                sm = mma(qx[c].m, oh, sm);
-                sh = mma(qx[c].h, oh, sh);
-                cnt = mma(ones, oh, cnt);
+                if (c < nch) {
+                    const u32x4_t oh = ld16(sOH + off128(l16, 32 * c + 8 * g));
+                    const Sp8 qt = colfrag8(sQV, 32 * c + 8 * g, 32 * c + 8 * g + 4, 16 * w, l16);
+                    sm = mma(qt.m, oh, sm);
+                    sh = mma(qt.h, oh, sh);
+                    cnt = mma(ones, oh, cnt);
+                }
             }
-            const float inv = 1.0f / fmaxf(cnt[0], 1.f);
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(cnt[0], 1.f));
             float v[4];
             float n2p = 0.f;
 #pragma unroll
@@ -677,136 +577,133 @@ __global__ __launch_bounds__(kThreads, 1) void cluster_attn_fused_kernel(
                 v[rr] = (sm[rr] + sh[rr]) * inv;
                 n2p = fmaf(v[rr], v[rr], n2p);
             }
-            uint32_t h01, m01, h23, m23;
-            split2(v[0], v[1], h01, m01);
-            split2(v[2], v[3], h23, m23);
-            const int o = off64(l16, 16 * w + 4 * g);
-            st8(sMuP + o, u32x2_t{h01, h23});
-            st8(sMuP + kPlaneMu / 2 + o, u32x2_t{m01, m23});
+            const Sp4 mu4 = split4(v[0], v[1], v[2], v[3]);
             n2p = col_sum(n2p);   // over the 16 dims of tile w
-            if (g == 0) sN2[w * kFK + l16] = n2p;
-        } else {
-            if (t == 1 && tileA < NT) {
-                if (NARROW) {
-                    local_tile_narrow<FULL>(sK, sV, qx, tileA, NT, L, sscale2, bias, l16, g, oA, lsumA);
-                } else {
-                    LocalTile<NARROW> lt;
-                    local_scores<FULL, NARROW>(sK, qx, tileA, NT, L, rad, sscale2, l16, g, lt);
-                    lsumA = lt.lsum;
-                    local_pv<NARROW>(sV, l16, g, lt, oA);
-                }
-            }
-            if (t == slotB && tileB < NT) {
-                if (NARROW) {
-                    local_tile_narrow<FULL>(sK, sV, qf, tileB, NT, L, sscale2, bias, l16, g, oB, lsumB);
-                } else {
-                    LocalTile<NARROW> lt;
-                    local_scores<FULL, NARROW>(sK, qf, tileB, NT, L, rad, sscale2, l16, g, lt);
-                    lsumB = lt.lsum;
-                    local_pv<NARROW>(sV, l16, g, lt, oB);
+            if (l16 < Kc) {
+                const int o = off64(l16, 16 * w + 4 * g);
+                st8(sMu + o, mu4.h);
+                st8(sMu + kPlaneMuE + o, mu4.m);
+                if (g == 0) {
+                    uint32_t h, m;
+                    split2(-0.5f * n2p, 0.f, h, m);
+                    sMuX[l16 * kMuXCols + 2 * w] = (uint16_t)(h & 0xffffu);
+                    sMuX[l16 * kMuXCols + 2 * w + 1] = (uint16_t)(m & 0xffffu);
                 }
             }
         }
         __syncthreads();
     }
 
-    // ------------------------------------------------------------ centroid cross-attention
-    float sx[4];
-    float mloc = -__builtin_inff();
-    if (w < NT) {
-        f32x4_t a0 = kZero4, a1 = kZero4;
-        a0 = mma3(frag64(sK, kPlaneK / 2, 16 * w + l16, 0, g), frag64(sMuP, kPlaneMu / 2, l16, 0, g), a0);
-        a1 = mma3(frag64(sK, kPlaneK / 2, 16 * w + l16, 1, g), frag64(sMuP, kPlaneMu / 2, l16, 1, g), a1);
+    // ------------------------------------------------------------ V planes, centroid-key scores
+    uint16_t *sV = sQV;   // Q planes are dead
+    {
+        const float fv = __builtin_ldexpf(1.f, -sv);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
-            sx[rr] = (FULL || key < L) ? (a0[rr] + a1[rr]) * sscale2 : -__builtin_inff();
-            mloc = fmaxf(mloc, sx[rr]);
+        for (int n = 0; n < 2; ++n) {
+            const int it = tid + kThreads * n;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = sv != 0 ? vraw[n][i] * fv : vraw[n][i];
+            const Sp8 sp = split8(x);
+            const int o = off64(it >> 3, (it & 7) * 8);
+            st16(sV + o, sp.h);
+            st16(sV + kPlaneE + o, sp.m);
         }
-        mloc = col_max(mloc);
     }
-    if (g == 0) sXm[l16 * 8 + w] = mloc;
-    __syncthreads();   // the centroid planes are dead from here on (P reuses them)
+    float sx[4];
+    {
+        float mloc = -__builtin_inff();
+        if (w < NT) {
+            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * w + l16, 0, g), frag64(sMu, kPlaneMuE, l16, 0, g), kZero4);
+            a = mma3(frag64(sK, kPlaneE, 16 * w + l16, 1, g), frag64(sMu, kPlaneMuE, l16, 1, g), a);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
+                sx[rr] = (FULL || key < L) ? a[rr] * sscale2 : -__builtin_inff();
+                mloc = fmaxf(mloc, sx[rr]);
+            }
+            mloc = col_max(mloc);
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sx[rr] = -__builtin_inff();
+        }
+        if (g == 0) sXm[l16 * 8 + w] = mloc;
+    }
+    __syncthreads();   // mu and the one-hot matrix are dead from here on (P reuses them)
     {
         const float4 m0 = *reinterpret_cast<const float4 *>(sXm + l16 * 8);
         const float4 m1 = *reinterpret_cast<const float4 *>(sXm + l16 * 8 + 4);
-        const float M = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
-                              fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        const float Mx = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
+                               fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
+        float p[4];
         float ls = 0.f;
-        if (w < NT) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                p[rr] = __builtin_amdgcn_exp2f(sx[rr] - M);   // exp2(-inf) = 0
-                ls += p[rr];
-            }
-            ls = col_sum(ls);
+        for (int rr = 0; rr < 4; ++rr) {
+            p[rr] = __builtin_amdgcn_exp2f(sx[rr] - Mx);   // exp2(-inf) = 0
+            ls += p[rr];
         }
-        uint32_t h01, m01, h23, m23;
-        split2(p[0], p[1], h01, m01);
-        split2(p[2], p[3], h23, m23);
-        const int o = off128(l16, vpos(16 * w + 4 * g));   // P[centroid l16][keys 16w + 4g ..]
-        st8(sP + o, u32x2_t{h01, h23});
-        st8(sP + kPlaneRow128 / 2 + o, u32x2_t{m01, m23});
+        ls = col_sum(ls);
+        const Sp4 ps = split4(p[0], p[1], p[2], p[3]);
+        const int o = off128(l16, 16 * w + 4 * g);   // P[centroid l16][keys 16w + 4g ..]
+        st8(sP + o, ps.h);
+        st8(sP + kPlaneRowE + o, ps.m);
         if (g == 0) sXl[l16 * 8 + w] = ls;
     }
     __syncthreads();
-    if (lower) {
+
+    // ------------------------------------------------------------ centroid context (waves 0-3)
+    if (w < 4) {
         // V^cent^T[dim 16w + 4g + rr][centroid l16] = sum over keys of V^T P^T
-        f32x4_t a0 = kZero4, a1 = kZero4;
+        f32x4_t a = kZero4;
         const int nch = (NT + 1) >> 1;
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-            if (ch < nch) {
-                const Sp8 vf = frag128(sV, kPlaneV / 2, 16 * w + l16, ch, g);
-                const Sp8 pf = frag128(sP, kPlaneRow128 / 2, l16, ch, g);
-                if (ch & 1)
-                    a1 = mma3(vf, pf, a1);
-                else
-                    a0 = mma3(vf, pf, a0);
+        for (int c = 0; c < 4; ++c) {
+            if (c < nch) {
+                const Sp8 vf = colfrag8(sV, 32 * c + 8 * g, 32 * c + 8 * g + 4, 16 * w, l16);
+                const int op = off128(l16, 32 * c + 8 * g);
+                const Sp8 pf = Sp8{ld16(sP + op), ld16(sP + kPlaneRowE + op)};
+                a = mma3(vf, pf, a);
             }
         }
         const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
         const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
         const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
-        const float f = vunscale / den;
-        float4 vc;
-        vc.x = (a0[0] + a1[0]) * f;
-        vc.y = (a0[1] + a1[1]) * f;
-        vc.z = (a0[2] + a1[2]) * f;
-        vc.w = (a0[3] + a1[3]) * f;
-        *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) = vc;
+        const float f = vunscale * __builtin_amdgcn_rcpf(den);
+        *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) =
+            make_float4(a[0] * f, a[1] * f, a[2] * f, a[3] * f);
+    }
+
+    // ------------------------------------------------------------ local window branch
+    f32x4_t o[4] = {kZero4, kZero4, kZero4, kZero4};
+    float lsum = 1.f;
+    if (w < NT) {
+        const int rad = radius < L ? radius : L;
+        if (NARROW)
+            local_narrow<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, o, lsum);
+        else
+            local_wide<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, o, lsum);
     }
     __syncthreads();
 
-    // ------------------------------------------------------------ gather + fusion (waves 4-7)
-    if (!lower) {
+    // ------------------------------------------------------------ gather + fusion
+    if (w < NT && (FULL || tok < L)) {
         const float wg = 1.0f - alpha;
+        const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
+        const float *vc = sVc + sC[tok] * kVcRow;
+        T *dst = out + base + (long)tok * kD;
 #pragma unroll
-        for (int which = 0; which < 2; ++which) {
-            const int qt = which == 0 ? tileA : tileB;
-            const int qi = 16 * qt + l16;
-            if (qt < NT && (FULL || qi < L)) {
-                const float f = alpha * vunscale / (which == 0 ? lsumA : lsumB);
-                const int cq = sC[qi];
-                const float *vc = sVc + cq * kVcRow;
-                T *dst = out + base + (long)qi * kD;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int d0 = 16 * j + 4 * g;
-                    const f32x4_t ol = which == 0 ? oA[j] : oB[j];
-                    float4 v;
-                    v.x = wg * vc[d0 + 0] + ol[0] * f;
-                    v.y = wg * vc[d0 + 1] + ol[1] * f;
-                    v.z = wg * vc[d0 + 2] + ol[2] * f;
-                    v.w = wg * vc[d0 + 3] + ol[3] * f;
-                    store4<T>(dst + d0, v);
-                }
-            }
+        for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
+            const int d0 = 16 * j + 4 * g;
+            const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
+            float4 v;
+            v.x = fmaf(wg, c4.x, o[j][0] * f);
+            v.y = fmaf(wg, c4.y, o[j][1] * f);
+            v.z = fmaf(wg, c4.z, o[j][2] * f);
+            v.w = fmaf(wg, c4.w, o[j][3] * f);
+            store4<T>(dst + d0, v);
         }
-    } else if (assign_out) {
-        for (int i = tid; i < L; i += 256) assign_out[slice * L + i] = sC[i];
     }
+    if (assign_out && tid < L) assign_out[slice * L + tid] = sC[tid];
 }
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }

@@ -93,6 +93,10 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 1, 300, 256, 2, 32, 0.5, "f32", 40),       # maximum cluster count
     (3, 5, 128, 16, 3, 32, 0.5, "bf16", 16),       # more slices
     (1, 1, 1100, 32, 3, 64, 0.5, "f32", 32),       # split-key centroid attention
+    (1, 2, 128, 16, 3, 100, 0.5, "f32", 6),        # wide window, single launch
+    (2, 2, 100, 16, 3, 60, 0.4, "bf16", 6),        # wide window, ragged, bf16
+    (1, 2, 128, 16, 3, 400, 0.5, "f32", 6),        # dense local branch, single launch
+    (1, 2, 37, 5, 2, 33, 0.5, "f32", 3),           # radius 16 on a short ragged slice
 ]
 
 
@@ -194,3 +198,34 @@ def test_step_xattn_local_fuse(L):
                            torch.float32)
     want = oracle.fuse(vc.astype(np.float64), c, ol.cpu().numpy().astype(np.float64), 0.25)
     assert np.abs(_host(out) - want).max() <= 1e-6
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("scales", [(1e3, 1e5, 1e5), (1e-3, 1e-6, 1e-7), (64.0, 1.0, 0.01),
+                                    (1e-4, 1e4, 1.0)])
+def test_extreme_magnitudes(scales, path):
+    """Inputs far from unit scale (the single-launch path rescales them by
+    powers of two before its fp16 split): same protocol, output tolerance
+    relative to the scale of V. The products of the Q and K scales are either
+    about 1 or so large that the softmax is a hard maximum (1e8): in between
+    (logits of order 1e3) any fp32 evaluation of the logits is already off by
+    more than the tolerance, so such cases pin nothing."""
+    sq, sk, sv = scales
+    x = gen.make_inputs(1, 3, 128, 64, nclust=16, iters=3, W=32, alpha=0.5, seed=77, blobs=8)
+    q = (x.q.astype(np.float64) * sq).astype(np.float32)
+    k = (x.k.astype(np.float64) * sk).astype(np.float32)
+    v = (x.v.astype(np.float64) * sv).astype(np.float32)
+    _say(f"[parity] magnitudes q*{sq} k*{sk} v*{sv} path={path}")
+    b = _b()
+    qd, kd, vd = _dev(q, "f32"), _dev(k, "f32"), _dev(v, "f32")
+    assigns = []
+    for t in range(1, 4):
+        out, c = b.cluster_attn_forward(qd, kd, vd, 16, t, 32, 0.5, path=path)
+        assigns.append(c.cpu().numpy())
+    reports, err, _, _ = parity.check_forward(
+        q.astype(np.float64), k.astype(np.float64), v.astype(np.float64), 16, 3, 32, 0.5, "f32",
+        assigns, _host(out))
+    _say(f"  {parity.summarize(reports)}; max|out-ref|/{sv}={err / sv:.3e}")
+    for r in reports:
+        assert r.bad == 0, parity.summarize(reports)
+    assert err <= 1e-4 * sv
