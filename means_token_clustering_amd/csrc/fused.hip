@@ -251,25 +251,42 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t *p) { return *reinterpret
 __device__ __forceinline__ void st16(uint16_t *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 __device__ __forceinline__ void st8(uint16_t *p, u32x2_t v) { *reinterpret_cast<u32x2_t *>(p) = v; }
 
-// row fragment of a 64-wide plane pair (row `row`, cols 32c + 8g ..)
-__device__ __forceinline__ Sp8 frag64(const uint16_t *planes, int plane, int row, int c, int g) {
-    const int o = off64(row, 32 * c + 8 * g);
+// Per-lane parts of the swizzled plane offsets, so that every fragment read
+// is one XOR (or none) plus an immediate offset:
+//   off64(R + l16, 32c + 8g)            = R*64 + (rl64 ^ 32c)       (R % 16 == 0)
+//   off128(l16, 32c + 8g)               = rl128 ^ 32c
+//   off64(B + l16/4, 16j + 4(l16%4))    = (B & ~7)*64 + (tr(B & 4) ^ 16j)
+struct LaneOffs {
+    int rl64, rl128, tr0, tr4;
+};
+__device__ __forceinline__ LaneOffs lane_offsets(int l16, int g) {
+    LaneOffs o;
+    o.rl64 = l16 * 64 + 8 * (g ^ (l16 & 3)) + 32 * ((l16 >> 2) & 1);
+    o.rl128 = l16 * 128 + 32 * (l16 >> 2) + 8 * (g ^ (l16 & 3));
+    const int b = (l16 >> 1) & 1;
+    int sw = l16 >> 2;   // row & 7 for B % 8 == 0
+    o.tr0 = (l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3);
+    sw += 4;             // B % 8 == 4
+    o.tr4 = 256 + (l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3);
+    return o;
+}
+// 16-byte row fragment of a plane pair at element offset o
+__device__ __forceinline__ Sp8 frag_at(const uint16_t *planes, int plane, int o) {
     return Sp8{ld16(planes + o), ld16(planes + plane + o)};
 }
-// transposed 4-deep read: lane l16 receives rows r0 .. r0+3 of column
-// c0 + l16 of a 64-wide plane (ds_read_b64_tr_b16; r0 may differ between
-// the four 16-lane groups)
-__device__ __forceinline__ u32x2_t col4(const uint16_t *plane, int r0, int c0, int l16) {
+// transposed 4-deep read (ds_read_b64_tr_b16) at element offset o: with o
+// from the tr(.) form above, lane l16 receives rows B .. B+3 of column
+// 16j + l16
+__device__ __forceinline__ u32x2_t tr_at(const uint16_t *plane, int o) {
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-    const uint16_t *p = plane + off64(r0 + (l16 >> 2), c0 + 4 * (l16 & 3));
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)(p)));
+        (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)(plane + o)));
     return __builtin_bit_cast(u32x2_t, v);
 }
-// 8-deep transposed fragment from rows r0 .. r0+3 and r1 .. r1+3
-__device__ __forceinline__ Sp8 colfrag8(const uint16_t *planes, int r0, int r1, int c0, int l16) {
-    const u32x2_t h0 = col4(planes, r0, c0, l16), h1 = col4(planes, r1, c0, l16);
-    const u32x2_t m0 = col4(planes + kPlaneE, r0, c0, l16), m1 = col4(planes + kPlaneE, r1, c0, l16);
+// 8-deep transposed fragment of a [128][64] plane pair from two row groups
+__device__ __forceinline__ Sp8 colfrag8_at(const uint16_t *planes, int o0, int o1) {
+    const u32x2_t h0 = tr_at(planes, o0), h1 = tr_at(planes, o1);
+    const u32x2_t m0 = tr_at(planes + kPlaneE, o0), m1 = tr_at(planes + kPlaneE, o1);
     return Sp8{u32x4_t{h0[0], h0[1], h1[0], h1[1]}, u32x4_t{m0[0], m0[1], m1[0], m1[1]}};
 }
 
@@ -281,7 +298,8 @@ __device__ __forceinline__ Sp8 colfrag8(const uint16_t *planes, int r0, int r1, 
 template <bool FULL>
 __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
-                                             int l16, int g, f32x4_t *o, float &lsum) {
+                                             int l16, int g, int rl64, int trv, f32x4_t *o,
+                                             float &lsum) {
     float s[3][4];
     float m = -__builtin_inff();
     const int rel0 = 4 * g - l16;   // key - query within aligned tiles
@@ -289,8 +307,8 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
         if (kt >= 0 && kt < NT) {
-            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * kt + l16, 0, g), qf[0], kZero4);
-            a = mma3(frag64(sK, kPlaneE, 16 * kt + l16, 1, g), qf[1], a);
+            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * kt + rl64), qf[0], kZero4);
+            a = mma3(frag_at(sK, kPlaneE, 1024 * kt + (rl64 ^ 32)), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
                 const int rel = 16 * (d - 1) + rel0 + rr;
@@ -319,13 +337,14 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
     const Sp8 pA = split8(pa);
     const float pb[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
     const Sp8 pB = split8(pb);
-    const int r0 = qt >= 1 ? 16 * (qt - 1) + 4 * g : 16 * qt + 4 * g;
-    const int r1 = 16 * qt + 4 * g;
-    const int r2 = qt + 1 < NT ? 16 * (qt + 1) + 4 * g : 16 * qt + 4 * g;
+    // V^T rows 16kt + 4g .. +3 of columns 16j + l16 start at 1024 kt + (trv ^ 16j)
+    const int b1 = 1024 * qt + trv;
+    const int b0 = qt >= 1 ? b1 - 1024 : b1;
+    const int b2 = qt + 1 < NT ? b1 + 1024 : b1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        f32x4_t a = mma3(colfrag8(sV, r0, r1, 16 * j, l16), pA, kZero4);
-        o[j] = mma3(colfrag8(sV, r2, r2, 16 * j, l16), pB, a);   // second half: zero weights
+        const f32x4_t a = mma3(colfrag8_at(sV, b0 ^ (16 * j), b1 ^ (16 * j)), pA, kZero4);
+        o[j] = mma3(colfrag8_at(sV, b2 ^ (16 * j), b2 ^ (16 * j)), pB, a);   // second half: zero weights
     }
 }
 
@@ -335,7 +354,8 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
 template <bool FULL>
 __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
                                            int qt, int NT, int L, int rad, float sscale2,
-                                           int l16, int g, f32x4_t *o, float &lsum) {
+                                           int l16, int g, int rl64, int trv, f32x4_t *o,
+                                           float &lsum) {
     const int qi = 16 * qt + l16;
     const int lo_key = 16 * qt - rad, hi_key = 16 * qt + 15 + rad;
     const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
@@ -348,8 +368,8 @@ __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *s
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ktt = two ? kt + h : kt;
-            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * ktt + l16, 0, g), qf[0], kZero4);
-            a = mma3(frag64(sK, kPlaneE, 16 * ktt + l16, 1, g), qf[1], a);
+            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * ktt + rl64), qf[0], kZero4);
+            a = mma3(frag_at(sK, kPlaneE, 1024 * ktt + (rl64 ^ 32)), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * ktt + 4 * g + rr;
@@ -371,9 +391,10 @@ __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *s
             ls += s[i];
         }
         const Sp8 p = split8(s);
-        const int r0 = 16 * kt + 4 * g, r1 = two ? 16 * (kt + 1) + 4 * g : r0;
+        const int b0 = 1024 * kt + trv, b1 = two ? b0 + 1024 : b0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = mma3(colfrag8(sV, r0, r1, 16 * j, l16), p, o[j] * f);
+        for (int j = 0; j < 4; ++j)
+            o[j] = mma3(colfrag8_at(sV, b0 ^ (16 * j), b1 ^ (16 * j)), p, o[j] * f);
     }
     lsum = col_sum(ls);
 }
@@ -405,46 +426,35 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;
     const long base = slice * (long)L * kD;
+    const LaneOffs lo = lane_offsets(l16, g);
+    // transposed reads of rows 32c + 8g (+4) .. of columns 16w + l16 (cluster
+    // sums and centroid context of dimension tile w): 2048 c + trq[h]
+    const int trq0 = 512 * g + (lo.tr0 ^ (16 * (w & 3)));
+    const int trq1 = 512 * g + (lo.tr4 ^ (16 * (w & 3)));
+    // ... of rows 16 kt + 4g .. of columns 16j + l16 (local branch): 1024 kt + (trv ^ 16j)
+    const int trv = 512 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
 
-    // ------------------------------------------------------------ fetch
-    // Q rows of token tile w (dims 32c + 8g ..); K and V items (row it/8,
-    // dims 8 (it%8) ..), it = tid and tid + 512
+    // ------------------------------------------------------------ fetch Q
+    // Q rows of token tile w (dims 32c + 8g ..). K and V are requested only
+    // once the Q planes are written, so that every slice's Q arrives first and
+    // the K and V traffic overlaps the clustering, which needs Q only.
     float qraw[2][8], kraw[2][8], vraw[2][8];
 #pragma unroll
     for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int it = tid + kThreads * n;
-        load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
-    }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int it = tid + kThreads * n;
-        load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
-    }
-    {   // per-tensor largest magnitude (bit patterns of |x| order like the values)
-        const float mq = absmax8(qraw[1], absmax8(qraw[0], 0.f));
-        const float mk = absmax8(kraw[1], absmax8(kraw[0], 0.f));
-        const float mv = absmax8(vraw[1], absmax8(vraw[0], 0.f));
-        const uint32_t bq = wave_max_u(__float_as_uint(mq));
-        const uint32_t bk = wave_max_u(__float_as_uint(mk));
-        const uint32_t bv = wave_max_u(__float_as_uint(mv));
-        if (lane == 0) {
-            sMax[w * 4 + 0] = bq;
-            sMax[w * 4 + 1] = bk;
-            sMax[w * 4 + 2] = bv;
-        }
+    {   // largest |q| of the slice (bit patterns of |x| order like the values)
+        const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
+        if (lane == 0) sMax[w * 4 + 0] = bq;
     }
 
-    // ------------------------------------------------------------ split
-    // Q planes + the register fragments qf of token tile w, K planes, and the
-    // strided initial centroids mu_k = Q[floor(k L / Kc)] with their
-    // -||mu||^2/2 parts; first without scaling (the usual case), redone
-    // below if a tensor is too large for fp16.
+    // ------------------------------------------------------------ split Q
+    // Q planes + the register fragments qf of token tile w, and the strided
+    // initial centroids mu_k = Q[floor(k L / Kc)] with their -||mu||^2/2
+    // parts; first without scaling (the usual case), redone below if Q is
+    // outside the range the fp16 split takes as is.
     Sp8 qf[2];
     const int kinit = (tok * Kc + L - 1) / L;   // the only k that can start at tok
     const bool owner = tok < L && kinit < Kc && (kinit * L) / Kc == tok;
-    auto split_qk = [&](float fq, float fk, bool scaled) {
+    auto split_q = [&](float fq, bool scaled) {
         float n2 = 0.f;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 n2 = fmaf(x[i], x[i], n2);
             }
             qf[c] = split8(x);
-            const int o = off64(tok, 32 * c + 8 * g);
+            const int o = 1024 * w + (lo.rl64 ^ (32 * c));   // row tok, cols 32c + 8g
             st16(sQV + o, qf[c].h);
             st16(sQV + kPlaneE + o, qf[c].m);
             if (owner) {
@@ -470,19 +480,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             sMuX[kinit * kMuXCols + 2 * g] = (uint16_t)(h & 0xffffu);
             sMuX[kinit * kMuXCols + 2 * g + 1] = (uint16_t)(m & 0xffffu);
         }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int it = tid + kThreads * n;
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = scaled ? kraw[n][i] * fk : kraw[n][i];
-            const Sp8 sp = split8(x);
-            const int o = off64(it >> 3, (it & 7) * 8);
-            st16(sK + o, sp.h);
-            st16(sK + kPlaneE + o, sp.m);
-        }
     };
-    split_qk(1.f, 1.f, false);
+    split_q(1.f, false);
     // one-hot matrix cleared; clusters >= Kc: zero centroid rows and a -inf
     // score part, so they are never chosen; unused columns of the parts zero
     reinterpret_cast<u32x2_t *>(sOH)[tid] = u32x2_t{0u, 0u};
@@ -498,33 +497,33 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     }
     __syncthreads();
 
-    int sq, sk, sv;
+    int sq;
     {
-        uint32_t mq = 0, mk = 0, mv = 0;
+        uint32_t mq = 0;
 #pragma unroll
-        for (int ww = 0; ww < 8; ++ww) {
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(sMax + 4 * ww);
-            mq = max(mq, v[0]);
-            mk = max(mk, v[1]);
-            mv = max(mv, v[2]);
-        }
+        for (int ww = 0; ww < 8; ++ww) mq = max(mq, sMax[4 * ww]);
         sq = scale_shift(mq, kQLimit);
-        sk = scale_shift(mk, kKVLimit);
-        sv = scale_shift(mv, kKVLimit);
     }
-    if (sq != 0 || sk != 0) {   // uniform over the workgroup; reload rather than keep
+    if (sq != 0) {   // uniform over the workgroup; reload rather than keep
 #pragma unroll
         for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int it = tid + kThreads * n;
-            load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
-        }
-        split_qk(__builtin_ldexpf(1.f, -sq), __builtin_ldexpf(1.f, -sk), true);
+        split_q(__builtin_ldexpf(1.f, -sq), true);
         __syncthreads();
     }
-    const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
-    const float vunscale = __builtin_ldexpf(1.f, sv);
+
+    // ------------------------------------------------------------ fetch K, V
+    // items (row it/8, dims 8 (it%8) ..), it = tid and tid + 512; consumed
+    // after the clustering
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
+    }
 
     // ------------------------------------------------------------ Lloyd
     const u32x4_t ones_g0 = g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
@@ -533,8 +532,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         if (w < NT) {
             // a[r] = mu_k . q_tok - ||mu_k||^2 / 2, k = 4g + r (scaled units of Q)
             f32x4_t a = mma(ld16(sMuX + l16 * kMuXCols + 8 * g), ones_g0, kZero4);
-            a = mma3(frag64(sMu, kPlaneMuE, l16, 0, g), qf[0], a);
-            a = mma3(frag64(sMu, kPlaneMuE, l16, 1, g), qf[1], a);
+            a = mma3(frag_at(sMu, kPlaneMuE, lo.rl64), qf[0], a);
+            a = mma3(frag_at(sMu, kPlaneMuE, lo.rl64 ^ 32), qf[1], a);
             float best = a[0];
             int bk = 4 * g;
 #pragma unroll
@@ -562,8 +561,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (c < nch) {
-                    const u32x4_t oh = ld16(sOH + off128(l16, 32 * c + 8 * g));
-                    const Sp8 qt = colfrag8(sQV, 32 * c + 8 * g, 32 * c + 8 * g + 4, 16 * w, l16);
+                    const u32x4_t oh = ld16(sOH + (lo.rl128 ^ (32 * c)));
+                    const Sp8 qt = colfrag8_at(sQV, 2048 * c + trq0, 2048 * c + trq1);
                     sm = mma(qt.m, oh, sm);
                     sh = mma(qt.h, oh, sh);
                     cnt = mma(ones, oh, cnt);
@@ -591,31 +590,60 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 }
             }
         }
+        if (t == iters) {   // largest |k| and |v| of the slice, published by the barrier below
+            const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
+            const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+            if (lane == 0) {
+                sMax[w * 4 + 1] = bk;
+                sMax[w * 4 + 2] = bv;
+            }
+        }
         __syncthreads();
     }
 
-    // ------------------------------------------------------------ V planes, centroid-key scores
+    // ------------------------------------------------------------ K and V planes
+    int sk, sv;
+    {
+        uint32_t mk = 0, mv = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+            mk = max(mk, sMax[4 * ww + 1]);
+            mv = max(mv, sMax[4 * ww + 2]);
+        }
+        sk = scale_shift(mk, kKVLimit);
+        sv = scale_shift(mv, kKVLimit);
+    }
+    const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
+    const float vunscale = __builtin_ldexpf(1.f, sv);
     uint16_t *sV = sQV;   // Q planes are dead
     {
-        const float fv = __builtin_ldexpf(1.f, -sv);
+        const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int it = tid + kThreads * n;
+            const int o = off64(it >> 3, (it & 7) * 8);
             float x[8];
 #pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = sk != 0 ? kraw[n][i] * fk : kraw[n][i];
+            const Sp8 kp = split8(x);
+            st16(sK + o, kp.h);
+            st16(sK + kPlaneE + o, kp.m);
+#pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = sv != 0 ? vraw[n][i] * fv : vraw[n][i];
-            const Sp8 sp = split8(x);
-            const int o = off64(it >> 3, (it & 7) * 8);
-            st16(sV + o, sp.h);
-            st16(sV + kPlaneE + o, sp.m);
+            const Sp8 vp = split8(x);
+            st16(sV + o, vp.h);
+            st16(sV + kPlaneE + o, vp.m);
         }
     }
+    __syncthreads();
+
+    // ------------------------------------------------------------ centroid-key scores
     float sx[4];
     {
         float mloc = -__builtin_inff();
         if (w < NT) {
-            f32x4_t a = mma3(frag64(sK, kPlaneE, 16 * w + l16, 0, g), frag64(sMu, kPlaneMuE, l16, 0, g), kZero4);
-            a = mma3(frag64(sK, kPlaneE, 16 * w + l16, 1, g), frag64(sMu, kPlaneMuE, l16, 1, g), a);
+            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * w + lo.rl64), frag_at(sMu, kPlaneMuE, lo.rl64), kZero4);
+            a = mma3(frag_at(sK, kPlaneE, 1024 * w + (lo.rl64 ^ 32)), frag_at(sMu, kPlaneMuE, lo.rl64 ^ 32), a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
@@ -659,9 +687,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (c < nch) {
-                const Sp8 vf = colfrag8(sV, 32 * c + 8 * g, 32 * c + 8 * g + 4, 16 * w, l16);
-                const int op = off128(l16, 32 * c + 8 * g);
-                const Sp8 pf = Sp8{ld16(sP + op), ld16(sP + kPlaneRowE + op)};
+                const Sp8 vf = colfrag8_at(sV, 2048 * c + trq0, 2048 * c + trq1);
+                const Sp8 pf = frag_at(sP, kPlaneRowE, lo.rl128 ^ (32 * c));
                 a = mma3(vf, pf, a);
             }
         }
@@ -679,9 +706,9 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     if (w < NT) {
         const int rad = radius < L ? radius : L;
         if (NARROW)
-            local_narrow<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, o, lsum);
+            local_narrow<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
         else
-            local_wide<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, o, lsum);
+            local_wide<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
     }
     __syncthreads();
 
