@@ -251,42 +251,47 @@ __device__ __forceinline__ u32x4_t ld16(const uint16_t *p) { return *reinterpret
 __device__ __forceinline__ void st16(uint16_t *p, u32x4_t v) { *reinterpret_cast<u32x4_t *>(p) = v; }
 __device__ __forceinline__ void st8(uint16_t *p, u32x2_t v) { *reinterpret_cast<u32x2_t *>(p) = v; }
 
-// Per-lane parts of the swizzled plane offsets, so that every fragment read
-// is one XOR (or none) plus an immediate offset:
-//   off64(R + l16, 32c + 8g)            = R*64 + (rl64 ^ 32c)       (R % 16 == 0)
-//   off128(l16, 32c + 8g)               = rl128 ^ 32c
-//   off64(B + l16/4, 16j + 4(l16%4))    = (B & ~7)*64 + (tr(B & 4) ^ 16j)
+// Per-lane parts of the swizzled plane offsets, in bytes, so that every
+// fragment read is one XOR (or none) plus an immediate offset (element
+// offsets above, times two):
+//   off64(R + l16, 32c + 8g)            -> 128 R + (rl64 ^ 64c)        (R % 16 == 0)
+//   off128(l16, 32c + 8g)               -> rl128 ^ 64c
+//   off64(B + l16/4, 16j + 4(l16%4))    -> 128 (B & ~7) + (tr(B & 4) ^ 32j)
 struct LaneOffs {
     int rl64, rl128, tr0, tr4;
 };
 __device__ __forceinline__ LaneOffs lane_offsets(int l16, int g) {
     LaneOffs o;
-    o.rl64 = l16 * 64 + 8 * (g ^ (l16 & 3)) + 32 * ((l16 >> 2) & 1);
-    o.rl128 = l16 * 128 + 32 * (l16 >> 2) + 8 * (g ^ (l16 & 3));
+    o.rl64 = 2 * (l16 * 64 + 8 * (g ^ (l16 & 3)) + 32 * ((l16 >> 2) & 1));
+    o.rl128 = 2 * (l16 * 128 + 32 * (l16 >> 2) + 8 * (g ^ (l16 & 3)));
     const int b = (l16 >> 1) & 1;
     int sw = l16 >> 2;   // row & 7 for B % 8 == 0
-    o.tr0 = (l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3);
+    o.tr0 = 2 * ((l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3));
     sw += 4;             // B % 8 == 4
-    o.tr4 = 256 + (l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3);
+    o.tr4 = 2 * (256 + (l16 >> 2) * 64 + 8 * (b ^ (sw & 1)) + 4 * (l16 & 1) + 16 * ((sw >> 1) & 3));
     return o;
 }
-// 16-byte row fragment of a plane pair at element offset o
-__device__ __forceinline__ Sp8 frag_at(const uint16_t *planes, int plane, int o) {
-    return Sp8{ld16(planes + o), ld16(planes + plane + o)};
+typedef unsigned char u8;
+__device__ __forceinline__ u32x4_t ldb16(const u8 *base, int off) {
+    return *reinterpret_cast<const u32x4_t *>(base + off);
 }
-// transposed 4-deep read (ds_read_b64_tr_b16) at element offset o: with o
+// 16-byte row fragment of a plane pair (planes `plane` bytes apart) at byte offset off
+__device__ __forceinline__ Sp8 frag_at(const u8 *base, int plane, int off) {
+    return Sp8{ldb16(base, off), ldb16(base, off + plane)};
+}
+// transposed 4-deep read (ds_read_b64_tr_b16) at byte offset off: with off
 // from the tr(.) form above, lane l16 receives rows B .. B+3 of column
 // 16j + l16
-__device__ __forceinline__ u32x2_t tr_at(const uint16_t *plane, int o) {
+__device__ __forceinline__ u32x2_t tr_at(const u8 *base, int off) {
     typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4 *)((__attribute__((address_space(3))) uint16_t *)(plane + o)));
+        (lds_i16x4 *)((__attribute__((address_space(3))) u8 *)(base + off)));
     return __builtin_bit_cast(u32x2_t, v);
 }
 // 8-deep transposed fragment of a [128][64] plane pair from two row groups
-__device__ __forceinline__ Sp8 colfrag8_at(const uint16_t *planes, int o0, int o1) {
-    const u32x2_t h0 = tr_at(planes, o0), h1 = tr_at(planes, o1);
-    const u32x2_t m0 = tr_at(planes + kPlaneE, o0), m1 = tr_at(planes + kPlaneE, o1);
+__device__ __forceinline__ Sp8 colfrag8_at(const u8 *base, int o0, int o1) {
+    const u32x2_t h0 = tr_at(base, o0), h1 = tr_at(base, o1);
+    const u32x2_t m0 = tr_at(base, o0 + kPlane), m1 = tr_at(base, o1 + kPlane);
     return Sp8{u32x4_t{h0[0], h0[1], h1[0], h1[1]}, u32x4_t{m0[0], m0[1], m1[0], m1[1]}};
 }
 
@@ -296,7 +301,7 @@ __device__ __forceinline__ Sp8 colfrag8_at(const uint16_t *planes, int o0, int o
 // tile qt+1 as a 16-deep one. Tiles outside [0, NT) get probability 0; their
 // V reads are moved onto tile qt (finite values times zero).
 template <bool FULL>
-__device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
+__device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
                                              int l16, int g, int rl64, int trv, f32x4_t *o,
                                              float &lsum) {
@@ -307,8 +312,8 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
         if (kt >= 0 && kt < NT) {
-            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * kt + rl64), qf[0], kZero4);
-            a = mma3(frag_at(sK, kPlaneE, 1024 * kt + (rl64 ^ 32)), qf[1], a);
+            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * kt + rl64), qf[0], kZero4);
+            a = mma3(frag_at(pK, kPlane, 2048 * kt + (rl64 ^ 64)), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
                 const int rel = 16 * (d - 1) + rel0 + rr;
@@ -337,14 +342,17 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
     const Sp8 pA = split8(pa);
     const float pb[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
     const Sp8 pB = split8(pb);
-    // V^T rows 16kt + 4g .. +3 of columns 16j + l16 start at 1024 kt + (trv ^ 16j)
-    const int b1 = 1024 * qt + trv;
-    const int b0 = qt >= 1 ? b1 - 1024 : b1;
-    const int b2 = qt + 1 < NT ? b1 + 1024 : b1;
+    // V^T rows 16kt + 4g .. +3 of columns 16j + l16 start at byte 2048 kt + (trv ^ 32j);
+    // the zero-weight half of the second product reads a fourth tile (any
+    // finite values do; a distinct tile avoids register copies)
+    const int b1 = 2048 * qt + trv;
+    const int b0 = qt >= 1 ? b1 - 2048 : b1;
+    const int b2 = qt + 1 < NT ? b1 + 2048 : b1;
+    const int b3 = qt + 2 < NT ? b1 + 4096 : (qt >= 2 ? b1 - 4096 : b1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const f32x4_t a = mma3(colfrag8_at(sV, b0 ^ (16 * j), b1 ^ (16 * j)), pA, kZero4);
-        o[j] = mma3(colfrag8_at(sV, b2 ^ (16 * j), b2 ^ (16 * j)), pB, a);   // second half: zero weights
+        const f32x4_t a = mma3(colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j)), pA, kZero4);
+        o[j] = mma3(colfrag8_at(pV, b2 ^ (32 * j), b3 ^ (32 * j)), pB, a);
     }
 }
 
@@ -352,7 +360,7 @@ __device__ __forceinline__ void local_narrow(const uint16_t *sK, const uint16_t 
 // two at a time with a running maximum (online softmax) and 32-deep P V
 // products; a missing second tile gets zero weights on repeated V rows.
 template <bool FULL>
-__device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *sV, const Sp8 *qf,
+__device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                            int qt, int NT, int L, int rad, float sscale2,
                                            int l16, int g, int rl64, int trv, f32x4_t *o,
                                            float &lsum) {
@@ -361,6 +369,8 @@ __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *s
     const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
     const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
     float M = -__builtin_inff(), ls = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = kZero4;
     for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
         const bool two = kt + 1 <= kt_hi;
         float s[8];
@@ -368,8 +378,8 @@ __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *s
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ktt = two ? kt + h : kt;
-            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * ktt + rl64), qf[0], kZero4);
-            a = mma3(frag_at(sK, kPlaneE, 1024 * ktt + (rl64 ^ 32)), qf[1], a);
+            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * ktt + rl64), qf[0], kZero4);
+            a = mma3(frag_at(pK, kPlane, 2048 * ktt + (rl64 ^ 64)), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * ktt + 4 * g + rr;
@@ -391,21 +401,28 @@ __device__ __forceinline__ void local_wide(const uint16_t *sK, const uint16_t *s
             ls += s[i];
         }
         const Sp8 p = split8(s);
-        const int b0 = 1024 * kt + trv, b1 = two ? b0 + 1024 : b0;
+        const int b0 = 2048 * kt + trv, b1 = two ? b0 + 2048 : b0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            o[j] = mma3(colfrag8_at(sV, b0 ^ (16 * j), b1 ^ (16 * j)), p, o[j] * f);
+            o[j] = mma3(colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j)), p, o[j] * f);
     }
     lsum = col_sum(ls);
 }
 
 }  // namespace
 
+// Tokens that start a cluster: bit t set iff t = floor(k L / Kc) for some
+// k < Kc (one bit per token, L <= 128). Token t then starts cluster
+// k = number of set bits below t.
+struct InitMask {
+    uint32_t w[4];
+};
+
 template <typename T, bool FULL, bool NARROW>
 __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, T *__restrict__ out,
-    int32_t *__restrict__ assign_out) {
+    int32_t *__restrict__ assign_out, InitMask init) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
@@ -427,12 +444,14 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const int tok = 16 * w + l16;
     const long base = slice * (long)L * kD;
     const LaneOffs lo = lane_offsets(l16, g);
+    const u8 *pK = smem + kOffK, *pQV = smem + kOffQV, *pMu = smem + kOffMu, *pOH = smem + kOffOH,
+             *pP = smem + kOffP, *pMuX = smem + kOffMuX;
     // transposed reads of rows 32c + 8g (+4) .. of columns 16w + l16 (cluster
-    // sums and centroid context of dimension tile w): 2048 c + trq[h]
-    const int trq0 = 512 * g + (lo.tr0 ^ (16 * (w & 3)));
-    const int trq1 = 512 * g + (lo.tr4 ^ (16 * (w & 3)));
-    // ... of rows 16 kt + 4g .. of columns 16j + l16 (local branch): 1024 kt + (trv ^ 16j)
-    const int trv = 512 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
+    // sums and centroid context of dimension tile w): byte 4096 c + trq[h]
+    const int trq0 = 1024 * g + (lo.tr0 ^ (32 * (w & 3)));
+    const int trq1 = 1024 * g + (lo.tr4 ^ (32 * (w & 3)));
+    // ... of rows 16 kt + 4g .. of columns 16j + l16 (local branch): byte 2048 kt + (trv ^ 32j)
+    const int trv = 1024 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
 
     // ------------------------------------------------------------ fetch Q
     // Q rows of token tile w (dims 32c + 8g ..). K and V are requested only
@@ -452,8 +471,17 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     // parts; first without scaling (the usual case), redone below if Q is
     // outside the range the fp16 split takes as is.
     Sp8 qf[2];
-    const int kinit = (tok * Kc + L - 1) / L;   // the only k that can start at tok
-    const bool owner = tok < L && kinit < Kc && (kinit * L) / Kc == tok;
+    int kinit;
+    bool owner;
+    {
+        const int wd = __builtin_amdgcn_readfirstlane(w) >> 1;   // word of tok = 16w + l16
+        const uint32_t word = init.w[wd];
+        int below = 0;
+        for (int i = 0; i < wd; ++i) below += __builtin_popcount(init.w[i]);
+        const int bit = tok & 31;
+        owner = (word >> bit) & 1u;
+        kinit = below + __builtin_popcount(word & ((1u << bit) - 1u));
+    }
     auto split_q = [&](float fq, bool scaled) {
         float n2 = 0.f;
 #pragma unroll
@@ -465,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 n2 = fmaf(x[i], x[i], n2);
             }
             qf[c] = split8(x);
-            const int o = 1024 * w + (lo.rl64 ^ (32 * c));   // row tok, cols 32c + 8g
+            const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
             st16(sQV + o, qf[c].h);
             st16(sQV + kPlaneE + o, qf[c].m);
             if (owner) {
@@ -529,11 +557,11 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const u32x4_t ones_g0 = g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
     int cprev = -1;
     for (int t = 1; t <= iters; ++t) {
-        if (w < NT) {
+        if (FULL || w < NT) {
             // a[r] = mu_k . q_tok - ||mu_k||^2 / 2, k = 4g + r (scaled units of Q)
-            f32x4_t a = mma(ld16(sMuX + l16 * kMuXCols + 8 * g), ones_g0, kZero4);
-            a = mma3(frag_at(sMu, kPlaneMuE, lo.rl64), qf[0], a);
-            a = mma3(frag_at(sMu, kPlaneMuE, lo.rl64 ^ 32), qf[1], a);
+            f32x4_t a = mma(ldb16(pMuX, 64 * l16 + 16 * g), ones_g0, kZero4);
+            a = mma3(frag_at(pMu, kPlaneMu, lo.rl64), qf[0], a);
+            a = mma3(frag_at(pMu, kPlaneMu, lo.rl64 ^ 64), qf[1], a);
             float best = a[0];
             int bk = 4 * g;
 #pragma unroll
@@ -561,8 +589,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if (c < nch) {
-                    const u32x4_t oh = ld16(sOH + (lo.rl128 ^ (32 * c)));
-                    const Sp8 qt = colfrag8_at(sQV, 2048 * c + trq0, 2048 * c + trq1);
+                    const u32x4_t oh = ldb16(pOH, lo.rl128 ^ (64 * c));
+                    const Sp8 qt = colfrag8_at(pQV, 4096 * c + trq0, 4096 * c + trq1);
                     sm = mma(qt.m, oh, sm);
                     sh = mma(qt.h, oh, sh);
                     cnt = mma(ones, oh, cnt);
@@ -617,19 +645,32 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const float vunscale = __builtin_ldexpf(1.f, sv);
     uint16_t *sV = sQV;   // Q planes are dead
     {
-        const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
+        if (__builtin_expect(sk != 0, 0)) {   // uniform; rare
+            const float fk = __builtin_ldexpf(1.f, -sk);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kraw[n][i] *= fk;
+        }
+        if (__builtin_expect(sv != 0, 0)) {
+            const float fv = __builtin_ldexpf(1.f, -sv);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vraw[n][i] *= fv;
+        }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int it = tid + kThreads * n;
             const int o = off64(it >> 3, (it & 7) * 8);
             float x[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = sk != 0 ? kraw[n][i] * fk : kraw[n][i];
+            for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
             const Sp8 kp = split8(x);
             st16(sK + o, kp.h);
             st16(sK + kPlaneE + o, kp.m);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = sv != 0 ? vraw[n][i] * fv : vraw[n][i];
+            for (int i = 0; i < 8; ++i) x[i] = vraw[n][i];
             const Sp8 vp = split8(x);
             st16(sV + o, vp.h);
             st16(sV + kPlaneE + o, vp.m);
@@ -641,9 +682,9 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     float sx[4];
     {
         float mloc = -__builtin_inff();
-        if (w < NT) {
-            f32x4_t a = mma3(frag_at(sK, kPlaneE, 1024 * w + lo.rl64), frag_at(sMu, kPlaneMuE, lo.rl64), kZero4);
-            a = mma3(frag_at(sK, kPlaneE, 1024 * w + (lo.rl64 ^ 32)), frag_at(sMu, kPlaneMuE, lo.rl64 ^ 32), a);
+        if (FULL || w < NT) {
+            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * w + lo.rl64), frag_at(pMu, kPlaneMu, lo.rl64), kZero4);
+            a = mma3(frag_at(pK, kPlane, 2048 * w + (lo.rl64 ^ 64)), frag_at(pMu, kPlaneMu, lo.rl64 ^ 64), a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
@@ -687,8 +728,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             if (c < nch) {
-                const Sp8 vf = colfrag8_at(sV, 2048 * c + trq0, 2048 * c + trq1);
-                const Sp8 pf = frag_at(sP, kPlaneRowE, lo.rl128 ^ (32 * c));
+                const Sp8 vf = colfrag8_at(pQV, 4096 * c + trq0, 4096 * c + trq1);
+                const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
                 a = mma3(vf, pf, a);
             }
         }
@@ -701,19 +742,19 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     }
 
     // ------------------------------------------------------------ local window branch
-    f32x4_t o[4] = {kZero4, kZero4, kZero4, kZero4};
-    float lsum = 1.f;
-    if (w < NT) {
+    f32x4_t o[4];   // set below for every wave that uses it
+    float lsum;
+    if (FULL || w < NT) {
         const int rad = radius < L ? radius : L;
         if (NARROW)
-            local_narrow<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
+            local_narrow<FULL>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
         else
-            local_wide<FULL>(sK, sV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
+            local_wide<FULL>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
     }
     __syncthreads();
 
     // ------------------------------------------------------------ gather + fusion
-    if (w < NT && (FULL || tok < L)) {
+    if (FULL || (w < NT && tok < L)) {
         const float wg = 1.0f - alpha;
         const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
         const float *vc = sVc + sC[tok] * kVcRow;
@@ -743,10 +784,15 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTotal);
     if (e != hipSuccess) return e;
+    InitMask init{};
+    for (int k = 0; k < Kc; ++k) {
+        const int t = (int)(((long)k * L) / Kc);
+        init.w[t >> 5] |= 1u << (t & 31);
+    }
     hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), kLdsTotal, st,
                        static_cast<const T *>(Q), static_cast<const T *>(K),
                        static_cast<const T *>(V), S, L, Kc, iters, radius, alpha,
-                       static_cast<T *>(out), assign);
+                       static_cast<T *>(out), assign, init);
     return hipGetLastError();
 }
 
