@@ -221,6 +221,20 @@ __device__ __forceinline__ void load_row8(const T *base, int row, int L, int col
         }
     }
 }
+// streaming (non-temporal) stores of 4 output elements: written once, never
+// read back by this kernel
+template <typename T>
+__device__ __forceinline__ void store4_nt(T *p, float4 v);
+template <>
+__device__ __forceinline__ void store4_nt<float>(float *p, float4 v) {
+    __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(p));
+}
+template <>
+__device__ __forceinline__ void store4_nt<bf16_t>(bf16_t *p, float4 v) {
+    const u32x2_t u = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                       (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x2_t *>(p));
+}
 __device__ __forceinline__ float absmax8(const float *x, float m) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
@@ -768,10 +782,10 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             v.y = fmaf(wg, c4.y, o[j][1] * f);
             v.z = fmaf(wg, c4.z, o[j][2] * f);
             v.w = fmaf(wg, c4.w, o[j][3] * f);
-            store4<T>(dst + d0, v);
+            store4_nt<T>(dst + d0, v);
         }
     }
-    if (assign_out && tid < L) assign_out[slice * L + tid] = sC[tid];
+    if (assign_out && tid < L) __builtin_nontemporal_store(sC[tid], assign_out + slice * L + tid);
 }
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }
