@@ -643,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         __syncthreads();
     }
 
-    // ------------------------------------------------------------ K and V planes
+    // ------------------------------------------------------------ K planes (V follows the scores)
     int sk, sv;
     {
         uint32_t mk = 0, mv = 0;
@@ -676,18 +676,13 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
             const int it = tid + kThreads * n;
-            const int o = off64(it >> 3, (it & 7) * 8);
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
             const Sp8 kp = split8(x);
+            const int o = off64(it >> 3, (it & 7) * 8);
             st16(sK + o, kp.h);
             st16(sK + kPlaneE + o, kp.m);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = vraw[n][i];
-            const Sp8 vp = split8(x);
-            st16(sV + o, vp.h);
-            st16(sV + kPlaneE + o, vp.m);
         }
     }
     __syncthreads();
@@ -711,6 +706,18 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             for (int rr = 0; rr < 4; ++rr) sx[rr] = -__builtin_inff();
         }
         if (g == 0) sXm[l16 * 8 + w] = mloc;
+    }
+    // V planes (first read after the next two barriers)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = vraw[n][i];
+        const Sp8 vp = split8(x);
+        const int o = off64(it >> 3, (it & 7) * 8);
+        st16(sV + o, vp.h);
+        st16(sV + kPlaneE + o, vp.m);
     }
     __syncthreads();   // mu and the one-hot matrix are dead from here on (P reuses them)
     {
