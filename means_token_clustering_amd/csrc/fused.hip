@@ -321,7 +321,12 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
                                              float &lsum) {
     float s[3][4];
     float m = -__builtin_inff();
-    const int rel0 = 4 * g - l16;   // key - query within aligned tiles
+    // key - query = 16 (d - 1) + rel0 + rr for key tile qt + d - 1; tile qt-1
+    // is in the window where key - query >= -rad, tile qt+1 where it is <= rad,
+    // and all of tile qt once rad >= 15
+    const int rel0 = 4 * g - l16;
+    const int lo0 = rel0 - 16 + rad, hi2 = rel0 + 16 - rad;
+    const bool whole1 = rad >= 15;
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
@@ -330,8 +335,10 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
             a = mma3(frag_at(pK, kPlane, 2048 * kt + (rl64 ^ 64)), qf[1], a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
-                const int rel = 16 * (d - 1) + rel0 + rr;
-                bool in = rel <= rad && -rel <= rad;
+                bool in;
+                if (d == 0) in = lo0 >= -rr;
+                else if (d == 2) in = hi2 <= -rr;
+                else in = whole1 || (rel0 + rr <= rad && -(rel0 + rr) <= rad);
                 if (!FULL) in = in && 16 * kt + 4 * g + rr < L;
                 s[d][rr] = in ? a[rr] * sscale2 : -__builtin_inff();
                 m = fmaxf(m, s[d][rr]);
