@@ -221,20 +221,6 @@ __device__ __forceinline__ void load_row8(const T *base, int row, int L, int col
         }
     }
 }
-// streaming (non-temporal) stores of 4 output elements: written once, never
-// read back by this kernel
-template <typename T>
-__device__ __forceinline__ void store4_nt(T *p, float4 v);
-template <>
-__device__ __forceinline__ void store4_nt<float>(float *p, float4 v) {
-    __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t *>(p));
-}
-template <>
-__device__ __forceinline__ void store4_nt<bf16_t>(bf16_t *p, float4 v) {
-    const u32x2_t u = {(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                       (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
-    __builtin_nontemporal_store(u, reinterpret_cast<u32x2_t *>(p));
-}
 __device__ __forceinline__ float absmax8(const float *x, float m) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
@@ -782,21 +768,45 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     __syncthreads();
 
     // ------------------------------------------------------------ gather + fusion
-    if (FULL || (w < NT && tok < L)) {
-        const float wg = 1.0f - alpha;
-        const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
-        const float *vc = sVc + sC[tok] * kVcRow;
-        T *dst = out + base + (long)tok * kD;
+    // The fused rows of token tile w go through a wave-private LDS tile (in
+    // the dead K planes; 16 rows, 16-byte chunks XOR-swizzled by the row) so
+    // that every store instruction writes whole rows: 64 lanes x 16 bytes of
+    // consecutive memory.
+    {
+        constexpr int kRowB = kD * (int)sizeof(T);   // bytes per output row
+        constexpr int kCpr = kRowB / 16;             // 16-byte chunks per row
+        u8 *stg = smem + kOffK + w * 16 * kRowB;
+        if (FULL || w < NT) {
+            const float wg = 1.0f - alpha;
+            const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
+            const float *vc = sVc + sC[tok] * kVcRow;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
-            const int d0 = 16 * j + 4 * g;
-            const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
-            float4 v;
-            v.x = fmaf(wg, c4.x, o[j][0] * f);
-            v.y = fmaf(wg, c4.y, o[j][1] * f);
-            v.z = fmaf(wg, c4.z, o[j][2] * f);
-            v.w = fmaf(wg, c4.w, o[j][3] * f);
-            store4_nt<T>(dst + d0, v);
+            for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
+                const int d0 = 16 * j + 4 * g;
+                const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
+                const float v0 = fmaf(wg, c4.x, o[j][0] * f), v1 = fmaf(wg, c4.y, o[j][1] * f);
+                const float v2 = fmaf(wg, c4.z, o[j][2] * f), v3 = fmaf(wg, c4.w, o[j][3] * f);
+                const int byte = d0 * (int)sizeof(T);   // within the row
+                u8 *p = stg + l16 * kRowB + ((((byte >> 4) ^ (l16 & (kCpr - 1)))) << 4) + (byte & 15);
+                if (sizeof(T) == 4) {
+                    *reinterpret_cast<f32x4_t *>(p) = f32x4_t{v0, v1, v2, v3};
+                } else {
+                    *reinterpret_cast<u32x2_t *>(p) =
+                        u32x2_t{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                                (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            u8 *dst = reinterpret_cast<u8 *>(out + base + (long)16 * w * kD);
+#pragma unroll
+            for (int i = 0; i < kCpr / 4; ++i) {   // 64 chunks = 64 / kCpr rows per store
+                const int flat = 64 * i + lane;
+                const int row = flat / kCpr, c = flat % kCpr;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                    stg + row * kRowB + (((c ^ (row & (kCpr - 1)))) << 4));
+                if (FULL || 16 * w + row < L)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + flat * 16));
+            }
         }
     }
     if (assign_out && tid < L) __builtin_nontemporal_store(sC[tid], assign_out + slice * L + tid);
