@@ -548,22 +548,27 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 
     // ------------------------------------------------------------ fetch K, V
     // items (row it/8, dims 8 (it%8) ..), it = tid and tid + 512; consumed
-    // after the clustering
+    // after the clustering. K is requested now and V at the start of the
+    // third iteration (or the last, if fewer), so that the address units of
+    // the CU never queue every load of both at once (measured fastest).
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n;
         load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
     }
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int it = tid + kThreads * n;
-        load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
-    }
+    const int tv = iters >= 3 ? 3 : iters;   // iteration that requests V
 
     // ------------------------------------------------------------ Lloyd
     const u32x4_t ones_g0 = g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
     int cprev = -1;
     for (int t = 1; t <= iters; ++t) {
+        if (t == tv) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int it = tid + kThreads * n;
+                load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
+            }
+        }
         if (FULL || w < NT) {
             // a[r] = mu_k . q_tok - ||mu_k||^2 / 2, k = 4g + r (scaled units of Q)
             f32x4_t a = mma(ldb16(pMuX, 64 * l16 + 16 * g), ones_g0, kZero4);
