@@ -630,31 +630,24 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 }
             }
         }
-        if (t == iters) {   // largest |k| and |v| of the slice, published by the barrier below
+        if (t == iters) {   // largest |k| of the slice, published by the barrier below
             const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
-            const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
-            if (lane == 0) {
-                sMax[w * 4 + 1] = bk;
-                sMax[w * 4 + 2] = bv;
-            }
+            if (lane == 0) sMax[w * 4 + 1] = bk;
         }
         __syncthreads();
     }
 
-    // ------------------------------------------------------------ K planes (V follows the scores)
-    int sk, sv;
+    // ------------------------------------------------------------ K planes
+    // (V, requested last, gets its maximum here and its planes in the next
+    // phase)
+    int sk;
     {
-        uint32_t mk = 0, mv = 0;
+        uint32_t mk = 0;
 #pragma unroll
-        for (int ww = 0; ww < 8; ++ww) {
-            mk = max(mk, sMax[4 * ww + 1]);
-            mv = max(mv, sMax[4 * ww + 2]);
-        }
+        for (int ww = 0; ww < 8; ++ww) mk = max(mk, sMax[4 * ww + 1]);
         sk = scale_shift(mk, kKVLimit);
-        sv = scale_shift(mv, kKVLimit);
     }
     const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
-    const float vunscale = __builtin_ldexpf(1.f, sv);
     uint16_t *sV = sQV;   // Q planes are dead
     {
         if (__builtin_expect(sk != 0, 0)) {   // uniform; rare
@@ -663,13 +656,6 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             for (int n = 0; n < 2; ++n)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) kraw[n][i] *= fk;
-        }
-        if (__builtin_expect(sv != 0, 0)) {
-            const float fv = __builtin_ldexpf(1.f, -sv);
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) vraw[n][i] *= fv;
         }
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -682,6 +668,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             st16(sK + o, kp.h);
             st16(sK + kPlaneE + o, kp.m);
         }
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        if (lane == 0) sMax[w * 4 + 2] = bv;
     }
     __syncthreads();
 
@@ -706,6 +694,21 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         if (g == 0) sXm[l16 * 8 + w] = mloc;
     }
     // V planes (first read after the next two barriers)
+    int sv;
+    {
+        uint32_t mv = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) mv = max(mv, sMax[4 * ww + 2]);
+        sv = scale_shift(mv, kKVLimit);
+    }
+    const float vunscale = __builtin_ldexpf(1.f, sv);
+    if (__builtin_expect(sv != 0, 0)) {   // uniform; rare
+        const float fv = __builtin_ldexpf(1.f, -sv);
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vraw[n][i] *= fv;
+    }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n;
