@@ -299,12 +299,36 @@ __device__ __forceinline__ Sp8 colfrag8_at(const u8 *base, int o0, int o1) {
 // qt-1, qt, qt+1 (others are outside every window of the tile), base-2
 // softmax, then O^T = V^T P^T: the pair (qt-1, qt) as one 32-deep product and
 // tile qt+1 as a 16-deep one. Tiles outside [0, NT) get probability 0; their
-// V reads are moved onto tile qt (finite values times zero).
+// K and V reads are moved onto tile qt (finite values times zero). Every LDS
+// read of a stage is issued before its first product, and the products of
+// independent tiles alternate, so that neither the LDS latency nor the
+// matrix-core latency is exposed per product.
 template <bool FULL>
 __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
                                              int l16, int g, int rl64, int trv, f32x4_t *o,
                                              float &lsum) {
+    bool valid[3];
+    Sp8 kfr[3][2];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int kt = qt + d - 1;
+        valid[d] = kt >= 0 && kt < NT;
+        const int kb = 2048 * (valid[d] ? kt : qt);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) kfr[d][c] = frag_at(pK, kPlane, kb + (rl64 ^ (64 * c)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t sc[3] = {kZero4, kZero4, kZero4};
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {   // the three mma3 chains, interleaved
+#pragma unroll
+        for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].m, qf[c].h, sc[d]);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].h, qf[c].m, sc[d]);
+#pragma unroll
+        for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].h, qf[c].h, sc[d]);
+    }
     float s[3][4];
     float m = -__builtin_inff();
     // key - query = 16 (d - 1) + rel0 + rr for key tile qt + d - 1; tile qt-1
@@ -316,22 +340,15 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
-        if (kt >= 0 && kt < NT) {
-            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * kt + rl64), qf[0], kZero4);
-            a = mma3(frag_at(pK, kPlane, 2048 * kt + (rl64 ^ 64)), qf[1], a);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {   // a[rr] = k_{16kt+4g+rr} . q_{16qt+l16}
-                bool in;
-                if (d == 0) in = lo0 >= -rr;
-                else if (d == 2) in = hi2 <= -rr;
-                else in = whole1 || (rel0 + rr <= rad && -(rel0 + rr) <= rad);
-                if (!FULL) in = in && 16 * kt + 4 * g + rr < L;
-                s[d][rr] = in ? a[rr] * sscale2 : -__builtin_inff();
-                m = fmaxf(m, s[d][rr]);
-            }
-        } else {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) s[d][rr] = -__builtin_inff();
+        for (int rr = 0; rr < 4; ++rr) {   // sc[d][rr] = k_{16kt+4g+rr} . q_{16qt+l16}
+            bool in;
+            if (d == 0) in = valid[0] && lo0 >= -rr;
+            else if (d == 2) in = valid[2] && hi2 <= -rr;
+            else in = whole1 || (rel0 + rr <= rad && -(rel0 + rr) <= rad);
+            if (!FULL) in = in && 16 * kt + 4 * g + rr < L;
+            s[d][rr] = in ? sc[d][rr] * sscale2 : -__builtin_inff();
+            m = fmaxf(m, s[d][rr]);
         }
     }
     m = col_max(m);   // finite: every query sees itself
@@ -353,13 +370,33 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
     // the zero-weight half of the second product reads a fourth tile (any
     // finite values do; a distinct tile avoids register copies)
     const int b1 = 2048 * qt + trv;
-    const int b0 = qt >= 1 ? b1 - 2048 : b1;
-    const int b2 = qt + 1 < NT ? b1 + 2048 : b1;
+    const int b0 = valid[0] ? b1 - 2048 : b1;
+    const int b2 = valid[2] ? b1 + 2048 : b1;
     const int b3 = qt + 2 < NT ? b1 + 4096 : (qt >= 2 ? b1 - 4096 : b1);
+    // two column tiles j per stage: 16 transposed reads, then 12 products
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4_t a = mma3(colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j)), pA, kZero4);
-        o[j] = mma3(colfrag8_at(pV, b2 ^ (32 * j), b3 ^ (32 * j)), pB, a);
+    for (int jj = 0; jj < 4; jj += 2) {
+        Sp8 va[2], vb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = jj + u;
+            va[u] = colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j));
+            vb[u] = colfrag8_at(pV, b2 ^ (32 * j), b3 ^ (32 * j));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t acc[2] = {kZero4, kZero4};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].m, pA.h, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].h, pA.m, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].h, pA.h, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mma(vb[u].m, pB.h, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc[u] = mma(vb[u].h, pB.m, acc[u]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) o[jj + u] = mma(vb[u].h, pB.h, acc[u]);
     }
 }
 
@@ -571,9 +608,12 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         }
         if (FULL || w < NT) {
             // a[r] = mu_k . q_tok - ||mu_k||^2 / 2, k = 4g + r (scaled units of Q)
-            f32x4_t a = mma(ldb16(pMuX, 64 * l16 + 16 * g), ones_g0, kZero4);
-            a = mma3(frag_at(pMu, kPlaneMu, lo.rl64), qf[0], a);
-            a = mma3(frag_at(pMu, kPlaneMu, lo.rl64 ^ 64), qf[1], a);
+            const u32x4_t mx = ldb16(pMuX, 64 * l16 + 16 * g);
+            const Sp8 mu0 = frag_at(pMu, kPlaneMu, lo.rl64), mu1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t a = mma(mx, ones_g0, kZero4);
+            a = mma3(mu0, qf[0], a);
+            a = mma3(mu1, qf[1], a);
             float best = a[0];
             int bk = 4 * g;
 #pragma unroll
@@ -678,8 +718,11 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     {
         float mloc = -__builtin_inff();
         if (FULL || w < NT) {
-            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * w + lo.rl64), frag_at(pMu, kPlaneMu, lo.rl64), kZero4);
-            a = mma3(frag_at(pK, kPlane, 2048 * w + (lo.rl64 ^ 64)), frag_at(pMu, kPlaneMu, lo.rl64 ^ 64), a);
+            const Sp8 k0 = frag_at(pK, kPlane, 2048 * w + lo.rl64), m0 = frag_at(pMu, kPlaneMu, lo.rl64);
+            const Sp8 k1 = frag_at(pK, kPlane, 2048 * w + (lo.rl64 ^ 64)), m1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4_t a = mma3(k0, m0, kZero4);
+            a = mma3(k1, m1, a);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
@@ -745,16 +788,21 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     // ------------------------------------------------------------ centroid context (waves 0-3)
     if (w < 4) {
         // V^cent^T[dim 16w + 4g + rr][centroid l16] = sum over keys of V^T P^T
-        f32x4_t a = kZero4;
         const int nch = (NT + 1) >> 1;
+        Sp8 vf[4], pf[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            if (c < nch) {
-                const Sp8 vf = colfrag8_at(pQV, 4096 * c + trq0, 4096 * c + trq1);
-                const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
-                a = mma3(vf, pf, a);
+            if (FULL || c < nch) {
+                vf[c] = colfrag8_at(pQV, 4096 * c + trq0, 4096 * c + trq1);
+                pf[c] = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t a2[2] = {kZero4, kZero4};   // even and odd key chunks
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (FULL || c < nch) a2[c & 1] = mma3(vf[c], pf[c], a2[c & 1]);
+        const f32x4_t a = a2[0] + a2[1];
         const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
         const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
         const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
