@@ -18,10 +18,10 @@
 // its largest magnitude is outside [2^-3, 2^5) for Q or [2^-3, 2^15) for K
 // and V, and then into the top binade of that range); each
 // scaled fp32 value x is then split into two fp16 parts x = h + m + e (h = x
-// rounded toward zero to fp16, m = the exact fp32 remainder x - h rounded
-// toward zero), which leaves |e| < 2^-20 |x| (2^-24 absolute below the fp16
-// normal range). A product a.b accumulates h.h, h.m and m.h: the dropped
-// terms are below 3 2^-20 |a||b| per element pair. Products with an exact 0/1
+// rounded toward zero to fp16, m = the remainder x - h rounded to nearest
+// fp16), which leaves |e| <= 2^-21 |x| (2^-25 absolute below the fp16 normal
+// range). A product a.b accumulates h.h, h.m and m.h: the dropped terms are
+// below 2^-19 |a||b| per element pair. Products with an exact 0/1
 // operand (one-hot cluster sums, counts) are exact up to fp32 accumulation.
 // The scale factors are undone on the fp32 results (scores, outputs);
 // distances stay in the scaled units of Q, which leaves every comparison
@@ -99,21 +99,15 @@ struct Sp4 {  // 4 values as two fp16 planes
     u32x2_t h, m;
 };
 
-// remainder x - h for the low / high fp16 half of h, in one exact fma
-__device__ __forceinline__ float rem_lo(float x, uint32_t h) {
-    float r;
-    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-    return r;
-}
-__device__ __forceinline__ float rem_hi(float x, uint32_t h) {
-    float r;
-    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x));
-    return r;
-}
-// x0, x1 -> packed fp16 pairs h and m with x = h + m + e
+// x0, x1 -> packed fp16 pairs h and m with x = h + m + e: h rounded toward
+// zero, m = x - h (exact inside the mixed-precision fma) rounded to nearest
+// into the low / high half of m
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m) {
     h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-    m = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rem_lo(x0, h), rem_hi(x1, h)));
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x0));
+    asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(x1));
+    m = r;
 }
 __device__ __forceinline__ Sp8 split8(const float *x) {
     uint32_t h[4], m[4];
@@ -352,15 +346,13 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
         }
     }
     m = col_max(m);   // finite: every query sees itself
-    float ls = 0.f;
 #pragma unroll
-    for (int d = 0; d < 3; ++d) {
+    for (int d = 0; d < 3; ++d)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            s[d][rr] = __builtin_amdgcn_exp2f(s[d][rr] - m);   // exp2(-inf) = 0
-            ls += s[d][rr];
-        }
-    }
+        for (int rr = 0; rr < 4; ++rr) s[d][rr] = __builtin_amdgcn_exp2f(s[d][rr] - m);   // exp2(-inf) = 0
+    float ls = s[0][0];
+#pragma unroll
+    for (int e = 1; e < 12; ++e) ls += s[e >> 2][e & 3];
     lsum = col_sum(ls);
     const float pa[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
     const Sp8 pA = split8(pa);
@@ -467,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, T *__restrict__ out,
     int32_t *__restrict__ assign_out, InitMask init) {
-    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kOffMu);
@@ -806,7 +798,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
         const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
         const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
-        const float f = vunscale * __builtin_amdgcn_rcpf(den);
+        const float f = (1.0f - alpha) * vunscale * __builtin_amdgcn_rcpf(den);   // (1 - alpha) V^cent
         *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) =
             make_float4(a[0] * f, a[1] * f, a[2] * f, a[3] * f);
     }
@@ -833,15 +825,14 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         constexpr int kCpr = kRowB / 16;             // 16-byte chunks per row
         u8 *stg = smem + kOffK + w * 16 * kRowB;
         if (FULL || w < NT) {
-            const float wg = 1.0f - alpha;
             const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
             const float *vc = sVc + sC[tok] * kVcRow;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
                 const int d0 = 16 * j + 4 * g;
                 const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
-                const float v0 = fmaf(wg, c4.x, o[j][0] * f), v1 = fmaf(wg, c4.y, o[j][1] * f);
-                const float v2 = fmaf(wg, c4.z, o[j][2] * f), v3 = fmaf(wg, c4.w, o[j][3] * f);
+                const float v0 = fmaf(o[j][0], f, c4.x), v1 = fmaf(o[j][1], f, c4.y);
+                const float v2 = fmaf(o[j][2], f, c4.z), v3 = fmaf(o[j][3], f, c4.w);
                 const int byte = d0 * (int)sizeof(T);   // within the row
                 u8 *p = stg + l16 * kRowB + ((((byte >> 4) ^ (l16 & (kCpr - 1)))) << 4) + (byte & 15);
                 if (sizeof(T) == 4) {
@@ -875,15 +866,12 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
                                  int iters, int radius, float alpha, void *out, int32_t *assign,
                                  hipStream_t st) {
     auto kern = cluster_attn_fused_kernel<T, FULL, NARROW>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsTotal);
-    if (e != hipSuccess) return e;
     InitMask init{};
     for (int k = 0; k < Kc; ++k) {
         const int t = (int)(((long)k * L) / Kc);
         init.w[t >> 5] |= 1u << (t & 31);
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), kLdsTotal, st,
+    hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), 0, st,
                        static_cast<const T *>(Q), static_cast<const T *>(K),
                        static_cast<const T *>(V), S, L, Kc, iters, radius, alpha,
                        static_cast<T *>(out), assign, init);
