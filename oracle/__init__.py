@@ -63,12 +63,12 @@ def _load():
             "ora_assign": (None, [_dp, _dp, L, i, i, i, _ip, _dp, _dp, _dp]),
             "ora_update": (None, [_dp, _ip, L, i, i, i, _dp, _ip]),
             "ora_objective": (None, [_dp, _dp, _ip, L, i, i, i, _dp]),
-            "ora_centroid_xattn": (None, [_dp, _dp, _dp, L, i, i, i, _dp, _dp]),
-            "ora_local_attn": (None, [_dp, _dp, _dp, L, i, i, i, _dp, _dp]),
-            "ora_fuse": (None, [_dp, _ip, _dp, L, i, i, i, d, _dp]),
-            "ora_forward": (i, [_dp, _dp, _dp, i, i, i, i, i, i, i, d, _dp, _ip,
+            "ora_centroid_xattn": (None, [_dp, _dp, _dp, L, i, i, i, _ip, _dp, _dp]),
+            "ora_local_attn": (None, [_dp, _dp, _dp, L, i, i, i, _ip, _dp, _dp]),
+            "ora_fuse": (None, [_dp, _ip, _dp, L, i, i, i, d, _ip, _dp]),
+            "ora_forward": (i, [_dp, _dp, _dp, i, i, i, i, i, i, i, d, _ip, _dp, _ip,
                                 _dp, _ip, _dp, _dp, _dp, _dp, _dp, _dp]),
-            "ora_forward_from_assign": (None, [_dp, _dp, _dp, L, i, i, i, _ip, i, d,
+            "ora_forward_from_assign": (None, [_dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip,
                                                _dp, _dp, _dp, _dp]),
             "ora_matmul": (None, [_dp, _dp, L, L, L, _dp]),
             "ora_round_bf16": (d, [d]),
@@ -114,6 +114,24 @@ def num_clusters(nclust: int, L: int) -> int:
 
 def radius(W: int) -> int:
     return _load().ora_radius(W)
+
+
+def _mask(valid, lead: tuple, L: int) -> Optional[np.ndarray]:
+    """Key-padding mask as int32 [*lead, L] (one row per slice), or None.
+
+    valid is either per slice ([*lead, L]) or per batch row ([B, L] for
+    tensors [B, H, L, d], shared by the H heads); nonzero = real token.
+    """
+    if valid is None:
+        return None
+    v = np.asarray(valid)
+    if v.shape == tuple(lead) + (L,):
+        out = v
+    elif len(lead) == 2 and v.shape == (lead[0], L):
+        out = np.broadcast_to(v[:, None, :], tuple(lead) + (L,))
+    else:
+        raise ValueError("mask shape %s does not fit slices %s x %d" % (v.shape, lead, L))
+    return np.ascontiguousarray(out != 0, dtype=np.int32)
 
 
 def _slices(x: np.ndarray):
@@ -163,45 +181,50 @@ def objective(Q, mu, c) -> np.ndarray:
     return J
 
 
-def centroid_xattn(mu, Kt, V):
-    """Returns (V^cent, probability row sums)."""
+def centroid_xattn(mu, Kt, V, valid=None):
+    """Returns (V^cent, probability row sums); valid: optional key-padding mask."""
     Kt, S, L, d = _slices(Kt)
     mu = _f64(mu)
     V = _f64(V)
     K = mu.shape[-2]
+    vm = _mask(valid, Kt.shape[:-2], L)
     vc = np.empty(mu.shape)
     ps = np.empty(mu.shape[:-1])
-    _load().ora_centroid_xattn(_p(mu), _p(Kt), _p(V), S, L, d, K, _p(vc), _p(ps))
+    _load().ora_centroid_xattn(_p(mu), _p(Kt), _p(V), S, L, d, K, _p(vm), _p(vc), _p(ps))
     return vc, ps
 
 
-def local_attn(Q, Kt, V, W: int):
-    """Returns (O^loc, probability row sums)."""
+def local_attn(Q, Kt, V, W: int, valid=None):
+    """Returns (O^loc, probability row sums); valid: optional key-padding mask."""
     Q, S, L, d = _slices(Q)
     Kt = _f64(Kt)
     V = _f64(V)
+    vm = _mask(valid, Q.shape[:-2], L)
     o = np.empty(Q.shape)
     ps = np.empty(Q.shape[:-1])
-    _load().ora_local_attn(_p(Q), _p(Kt), _p(V), S, L, d, W, _p(o), _p(ps))
+    _load().ora_local_attn(_p(Q), _p(Kt), _p(V), S, L, d, W, _p(vm), _p(o), _p(ps))
     return o, ps
 
 
-def fuse(vcent, c, oloc, alpha: float) -> np.ndarray:
+def fuse(vcent, c, oloc, alpha: float, valid=None) -> np.ndarray:
     oloc, S, L, d = _slices(oloc)
     vcent = _f64(vcent)
     c = _i32(c)
+    vm = _mask(valid, oloc.shape[:-2], L)
     out = np.empty(oloc.shape)
     _load().ora_fuse(_p(vcent), _p(c), _p(oloc), S, L, d, vcent.shape[-2],
-                     float(alpha), _p(out))
+                     float(alpha), _p(vm), _p(out))
     return out
 
 
 def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
-            trace: bool = True) -> Dict[str, np.ndarray]:
-    """Whole forward pass; Q, K, V are float64 [B, H, L, d]."""
+            trace: bool = True, valid=None) -> Dict[str, np.ndarray]:
+    """Whole forward pass; Q, K, V are float64 [B, H, L, d]; valid: optional
+    key-padding mask [B, L] or [B, H, L] (nonzero = real token)."""
     Q, Kt, V = _f64(Q), _f64(Kt), _f64(V)
     B, H, L, d = Q.shape
     S = B * H
+    vm = _mask(valid, (B, H), L)
     K = num_clusters(nclust, L)
     out = np.empty(Q.shape)
     c = np.empty((B, H, L), np.int32)
@@ -219,7 +242,7 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
         )
     g = res.get
     rc = _load().ora_forward(
-        _p(Q), _p(Kt), _p(V), B, H, L, d, nclust, iters, W, float(alpha),
+        _p(Q), _p(Kt), _p(V), B, H, L, d, nclust, iters, W, float(alpha), _p(vm),
         _p(out), _p(c), _p(g("mu_hist")), _p(g("c_hist")), _p(g("gap_hist")),
         _p(g("J")), _p(g("Jp")), _p(g("qn2")), _p(g("vcent")), _p(g("oloc")))
     if rc < 0:
@@ -229,9 +252,10 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
     return res
 
 
-def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float):
+def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None):
     """Steps after clustering from a given final assignment c (e.g. the GPU's)."""
     Q, S, L, d = _slices(Q)
+    vm = _mask(valid, Q.shape[:-2], L)
     Kt, V, c = _f64(Kt), _f64(V), _i32(c)
     if c.size and (c.min() < 0 or c.max() >= K):
         raise ValueError("assignment out of range")
@@ -240,7 +264,7 @@ def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float):
     vc = np.empty(Q.shape[:-2] + (K, d))
     ol = np.empty(Q.shape)
     _load().ora_forward_from_assign(_p(Q), _p(Kt), _p(V), S, L, d, K, _p(c), W,
-                                    float(alpha), _p(out), _p(mu), _p(vc), _p(ol))
+                                    float(alpha), _p(vm), _p(out), _p(mu), _p(vc), _p(ol))
     return {"out": out, "mu": mu, "vcent": vc, "oloc": ol}
 
 

@@ -19,7 +19,15 @@
  * clipped to [0, L); ties in the argmin go to the lowest cluster index; an
  * empty cluster's centroid is the zero vector (the max(1, n) denominator);
  * the returned pair is (c^(I), mu^(I)); softmax is max-subtracted, with no
- * mask and no dropout; the scale is 1/sqrt(d) in both branches.
+ * dropout; the scale is 1/sqrt(d) in both branches.
+ *
+ * Key-padding mask (optional; the ClusterAttention listing on the
+ * "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
+ * valid[s, j] != 0 marks a real token. A padded key's logit is replaced by
+ * -10000 (after the 1/sqrt(d) scale) in the centroid-key and in the local
+ * window softmax; the output row of a padded query is zero; the clustering
+ * runs over every token, padded ones included. A NULL mask means every token
+ * is real. Layout [S, L] int32, slice-major like Q.
  *
  * Layout: each (b, h) pair is one "slice"; a slice of Q, K or V is a
  * contiguous [L, d] row-major block and slices follow in b-major, h-minor
@@ -159,11 +167,13 @@ void ora_objective(const double *Q, const double *mu, const int32_t *c, long S,
 
 /*
  * Centroid cross-attention ([MC] pipeline figure, [CF] 3):
- * V^cent_k = sum_j softmax_j(mu_k . k_j / sqrt(d)) v_j over all L keys.
+ * V^cent_k = sum_j softmax_j(mu_k . k_j / sqrt(d)) v_j over all L keys; a
+ * padded key's logit is -10000 (valid nullable, see the header).
  * psum (nullable) receives each probability row's sum, for the pins.
  */
 void ora_centroid_xattn(const double *mu, const double *Kt, const double *V,
-                        long S, int L, int d, int K, double *vcent, double *psum) {
+                        long S, int L, int d, int K, const int32_t *valid,
+                        double *vcent, double *psum) {
     const double scale = 1.0 / sqrt((double)d);
 #pragma omp parallel for schedule(static)
     for (long s = 0; s < S; ++s) {
@@ -175,7 +185,7 @@ void ora_centroid_xattn(const double *mu, const double *Kt, const double *V,
                 const double *kr = Kt + (s * L + j) * (long)d;
                 double dot = 0.0;
                 for (int t = 0; t < d; ++t) dot += m[t] * kr[t];
-                e[j] = dot * scale;
+                e[j] = (valid && !valid[s * L + j]) ? -10000.0 : dot * scale;
                 if (e[j] > mx) mx = e[j];
             }
             double z = 0.0;
@@ -201,10 +211,12 @@ void ora_centroid_xattn(const double *mu, const double *Kt, const double *V,
 /*
  * Local sliding-window branch ([MC] pipeline figure, [CF] 3): for query i the
  * keys are j in [max(0, i - r), min(L - 1, i + r)], r = floor(W / 2);
- * O^loc_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over that window.
+ * O^loc_i = sum_j softmax_j(q_i . k_j / sqrt(d)) v_j over that window; a
+ * padded key inside the window has the logit -10000 (valid nullable).
  */
 void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
-                    int L, int d, int W, double *oloc, double *psum) {
+                    int L, int d, int W, const int32_t *valid, double *oloc,
+                    double *psum) {
     const double scale = 1.0 / sqrt((double)d);
     const int r = ora_radius(W);
 #pragma omp parallel for schedule(static)
@@ -219,7 +231,7 @@ void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
                 const double *kr = Kt + (s * L + j) * (long)d;
                 double dot = 0.0;
                 for (int t = 0; t < d; ++t) dot += q[t] * kr[t];
-                e[j] = dot * scale;
+                e[j] = (valid && !valid[s * L + j]) ? -10000.0 : dot * scale;
                 if (e[j] > mx) mx = e[j];
             }
             double z = 0.0;
@@ -244,16 +256,18 @@ void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
 
 /*
  * Gather and convex fusion ([MC] Architecture Overview item 2, [CF] 3):
- * O_i = (1 - alpha) V^cent_{c_i} + alpha O^loc_i.
+ * O_i = (1 - alpha) V^cent_{c_i} + alpha O^loc_i; the row of a padded query
+ * is zero (valid nullable).
  */
 void ora_fuse(const double *vcent, const int32_t *c, const double *oloc, long S,
-              int L, int d, int K, double alpha, double *out) {
+              int L, int d, int K, double alpha, const int32_t *valid, double *out) {
     for (long s = 0; s < S; ++s) {
         for (int i = 0; i < L; ++i) {
             const double *g = vcent + (s * K + c[s * L + i]) * (long)d;
             const double *l = oloc + (s * L + i) * (long)d;
             double *o = out + (s * L + i) * (long)d;
-            for (int t = 0; t < d; ++t) o[t] = (1.0 - alpha) * g[t] + alpha * l[t];
+            const int keep = !valid || valid[s * L + i];
+            for (int t = 0; t < d; ++t) o[t] = keep ? (1.0 - alpha) * g[t] + alpha * l[t] : 0.0;
         }
     }
 }
@@ -263,10 +277,12 @@ void ora_fuse(const double *vcent, const int32_t *c, const double *oloc, long S,
  * nullable): mu_hist [(iters+1), S, K, d] (mu^(0..I)), c_hist [iters, S, L],
  * gap_hist [iters, S, L], J [iters, S] (objective after assignment t, i.e.
  * against mu^(t-1)), Jp [iters, S] (objective after update t), qn2 [S, L],
- * vcent [S, K, d], oloc [S, L, d]. Returns K, or -1 on invalid arguments.
+ * vcent [S, K, d], oloc [S, L, d]. valid: key-padding mask [S, L] or NULL.
+ * Returns K, or -1 on invalid arguments.
  */
 int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H,
                 int L, int d, int nclust, int iters, int W, double alpha,
+                const int32_t *valid,
                 double *out, int32_t *assign, double *mu_hist, int32_t *c_hist,
                 double *gap_hist, double *J, double *Jp, double *qn2,
                 double *vcent_out, double *oloc_out) {
@@ -301,9 +317,9 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
             memcpy(Jp + (long)(t - 1) * S, Js, sizeof(double) * (size_t)S);
         }
     }
-    ora_centroid_xattn(mu, Kt, V, S, L, d, K, vcent, NULL);
-    ora_local_attn(Q, Kt, V, S, L, d, W, oloc, NULL);
-    ora_fuse(vcent, assign, oloc, S, L, d, K, alpha, out);
+    ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
+    ora_local_attn(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
+    ora_fuse(vcent, assign, oloc, S, L, d, K, alpha, valid, out);
     if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
     if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));
     free(mu); free(mu_next); free(gap); free(vcent); free(oloc); free(Js);
@@ -317,15 +333,15 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
  */
 void ora_forward_from_assign(const double *Q, const double *Kt, const double *V,
                              long S, int L, int d, int K, const int32_t *c, int W,
-                             double alpha, double *out, double *mu_out,
+                             double alpha, const int32_t *valid, double *out, double *mu_out,
                              double *vcent_out, double *oloc_out) {
     double *mu = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
     double *vcent = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
     double *oloc = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
     ora_update(Q, c, S, L, d, K, mu, NULL);
-    ora_centroid_xattn(mu, Kt, V, S, L, d, K, vcent, NULL);
-    ora_local_attn(Q, Kt, V, S, L, d, W, oloc, NULL);
-    ora_fuse(vcent, c, oloc, S, L, d, K, alpha, out);
+    ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
+    ora_local_attn(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
+    ora_fuse(vcent, c, oloc, S, L, d, K, alpha, valid, out);
     if (mu_out) memcpy(mu_out, mu, sizeof(double) * (size_t)(S * K * d));
     if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
     if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));

@@ -366,3 +366,100 @@ def test_matmul_and_heads():
         want = (X @ Wq[:, 8 * h:8 * h + 8])
         assert np.allclose(q[:, h], oracle.round_bf16(want), atol=1e-12)
     assert np.array_equal(oracle.merge_heads(q).reshape(2, 5, 24)[:, :, 8:16], q[:, 1])
+
+
+# ------------------------------------------------ P10: key-padding mask
+# Semantics (ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-
+# cluster" page, forward, bidirectional branch): a padded key's logit is -10000
+# in both softmaxes, padded query rows are zero, the clustering sees every
+# token.
+def _prefix_mask(B, L, lengths):
+    m = np.zeros((B, L), np.int32)
+    for b, n in enumerate(lengths):
+        m[b, :n] = 1
+    return m
+
+
+def test_mask_all_valid_is_unmasked_bit_exact():
+    x = gen.make_inputs(2, 3, 40, 8, nclust=5, seed=21, blobs=4)
+    args = (x.values("q"), x.values("k"), x.values("v"), 5, 3, 10, 0.4)
+    r0 = oracle.forward(*args)
+    r1 = oracle.forward(*args, valid=np.ones((2, 40), np.int32))
+    for key in ("out", "assign", "vcent", "oloc"):
+        assert np.array_equal(r0[key], r1[key]), key
+
+
+def test_mask_prefix_equals_truncated_sequence():
+    """Keys after a valid prefix of length n drop out exactly: the masked
+    branches on the valid rows equal the unmasked branches of the sequence
+    cut to n tokens (exp(-10000 - m) is 0 in float64)."""
+    x = gen.make_inputs(2, 2, 48, 8, nclust=6, seed=22, blobs=5)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    lengths = [31, 48]
+    m = _prefix_mask(2, 48, lengths)
+    mu = oracle.forward(q, k, v, 6, 3, 10, 0.5)["mu"]
+    ol, _ = oracle.local_attn(q, k, v, 10, valid=m)
+    vc, _ = oracle.centroid_xattn(mu, k, v, valid=m)
+    for b, n in enumerate(lengths):
+        olt, _ = oracle.local_attn(q[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 10)
+        vct, _ = oracle.centroid_xattn(mu[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n])
+        assert np.array_equal(ol[b:b + 1, :, :n], olt)
+        assert np.array_equal(vc[b:b + 1], vct)
+
+
+def test_mask_matches_library_masked_attention():
+    """A window wider than the sequence is dense attention, and so is the
+    centroid context with the centroids at the queries; with a key mask both
+    match torch's masked scaled-dot-product attention."""
+    x = gen.make_inputs(1, 2, 24, 8, nclust=24, seed=23, blobs=3)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    rng = np.random.default_rng(5)
+    m = (rng.random((1, 24)) < 0.6).astype(np.int32)
+    m[0, 3] = 1
+    ol, _ = oracle.local_attn(q, k, v, 1000, valid=m)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
+    keep = torch.from_numpy(m[0].astype(bool))[None, None, None, :]
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep).numpy()
+    assert np.allclose(ol, want, atol=1e-13)
+    mu = q.copy()   # centroids at the queries: the same product over all keys
+    vc, _ = oracle.centroid_xattn(mu, k, v, valid=m)
+    assert np.allclose(vc, want, atol=1e-13)
+
+
+def test_mask_padded_rows_zero_and_padded_kv_irrelevant():
+    x = gen.make_inputs(2, 2, 40, 8, nclust=5, seed=24, blobs=4)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    m = _prefix_mask(2, 40, [25, 33])
+    m[1, 5] = 0   # a hole inside the sequence as well
+    r = oracle.forward(q, k, v, 5, 3, 8, 0.3, valid=m)
+    pad = m == 0
+    assert np.all(r["out"][np.broadcast_to(pad[:, None, :], (2, 2, 40))] == 0.0)
+    k2, v2 = k.copy(), v.copy()
+    rng = np.random.default_rng(9)
+    for arr in (k2, v2):
+        sel = np.broadcast_to(pad[:, None, :, None], arr.shape)
+        arr[sel] = rng.standard_normal(int(sel.sum())) * 50.0
+    r2 = oracle.forward(q, k2, v2, 5, 3, 8, 0.3, valid=m)
+    assert np.array_equal(r2["out"], r["out"])
+    assert np.array_equal(r2["assign"], r["assign"])
+    # the clustering runs over every token: the mask leaves it unchanged
+    r0 = oracle.forward(q, k, v, 5, 3, 8, 0.3)
+    assert np.array_equal(r0["assign"], r["assign"])
+    assert np.array_equal(r0["mu"], r["mu"])
+
+
+def test_mask_fill_gives_uniform_weights_when_all_keys_padded():
+    """-10000 is a finite logit: a softmax over padded keys only is uniform,
+    so the centroid context of an all-padding row is the mean of V and the
+    local branch of a query surrounded by padding is the window mean."""
+    x = gen.make_inputs(1, 2, 20, 8, nclust=4, seed=25, blobs=3)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    m = np.zeros((1, 20), np.int32)
+    r = oracle.forward(q, k, v, 4, 2, 6, 0.5, valid=m)
+    assert np.all(r["out"] == 0.0)
+    assert np.allclose(r["vcent"], np.broadcast_to(v.mean(axis=2, keepdims=True), r["vcent"].shape),
+                       atol=1e-14)
+    m[0, 0] = 1   # token 0 valid; query 12's window [9, 15] is all padding
+    ol, _ = oracle.local_attn(q, k, v, 6, valid=m)
+    assert np.allclose(ol[:, :, 12], v[:, :, 9:16].mean(axis=2), atol=1e-14)
+    assert np.array_equal(ol[:, :, 0], oracle.local_attn(q[:, :, :1], k[:, :, :1], v[:, :, :1], 6)[0][:, :, 0])
