@@ -69,16 +69,19 @@ def parse():
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU-oracle baseline (0 disables it)")
+    p.add_argument("--masked", action="store_true",
+                   help="padded batch: key-padding mask with right padding, row lengths "
+                        "~ U{L/4..L} (cluster_attn_forward_masked)")
     return p.parse_args()
 
 
-def cpu_baseline(x, seconds: float):
+def cpu_baseline(x, seconds: float, mask=None):
     import oracle
     q, k, v = x.values("q"), x.values("k"), x.values("v")
-    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False)   # warm
+    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)   # warm
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False)
+        oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -112,6 +115,10 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     set_bytes = algorithmic_bytes(x.B, x.H, x.L, x.d, elem)
+    mask = gen.make_mask(x.B, x.L, seed=x.seed + 500) if args.masked else None
+    if mask is not None:
+        set_bytes += mask.size   # one byte per token, read once per launch
+    vdev = torch.from_numpy(mask).to(dev) if mask is not None else None
     nsets = args.sets or max(2, MALL_BYTES // set_bytes + 2)
     base = [to_dev(getattr(x, n)) for n in ("q", "k", "v")]
     sets = []
@@ -131,9 +138,15 @@ def main():
 
     def step(i):
         q, k, v, o, c = sets[i % nsets]
-        st = lib.cluster_attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), x.B, x.H, x.L,
-                                         x.d, x.nclust, x.iters, x.W, float(x.alpha),
-                                         o.data_ptr(), c.data_ptr(), dt, wsp, wsn, path, sptr)
+        if vdev is not None:
+            st = lib.cluster_attn_forward_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                 vdev.data_ptr(), x.B, x.H, x.L, x.d, x.nclust,
+                                                 x.iters, x.W, float(x.alpha), o.data_ptr(),
+                                                 c.data_ptr(), dt, wsp, wsn, path, sptr)
+        else:
+            st = lib.cluster_attn_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), x.B, x.H,
+                                             x.L, x.d, x.nclust, x.iters, x.W, float(x.alpha),
+                                             o.data_ptr(), c.data_ptr(), dt, wsp, wsn, path, sptr)
         if st != b.CA_OK:
             raise b.CaError(st, "cluster_attn_forward")
 
@@ -156,7 +169,8 @@ def main():
     fused = ws_bytes == 0
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
-    if fused and x.name == TRAFFIC["workload"] and code_digest() == TRAFFIC["digest"]:
+    if (fused and mask is None and x.name == TRAFFIC["workload"]
+            and code_digest() == TRAFFIC["digest"]):
         traffic = TRAFFIC["bytes"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -170,8 +184,11 @@ def main():
                       "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
                       "path": "fused" if fused else "staged", "input_sets": nsets},
            "roofline": roof}
+    if mask is not None:
+        rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "
+                                 f"{int(mask.sum())} of {mask.size} tokens real")
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, mask)
     print(json.dumps(rec), flush=True)
 
 

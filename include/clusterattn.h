@@ -14,7 +14,8 @@
  *     Vc_k    = softmax_j(mu_k . k_j / sqrt(d)) v_j     (all L keys)
  *     Ol_i    = softmax_j(q_i . k_j / sqrt(d)) v_j      (|i - j| <= floor(W/2))
  *     O_i     = (1 - alpha) Vc_{c_i} + alpha Ol_i
- *   The clustering returns (c^(iters), mu^(iters)); no mask, no dropout.
+ *   The clustering returns (c^(iters), mu^(iters)); no dropout; the key-
+ *   padding mask of padded batches is cluster_attn_forward_masked.
  *
  * Conventions shared by every entry point:
  *   - Tensors are device pointers to contiguous row-major arrays. "[B,H,L,d]"
@@ -110,6 +111,28 @@ ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
 
 size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust,
                                       ca_dtype_t dt, ca_path_t path);
+
+/*
+ * Cluster attention with a key-padding mask (padded batches): the
+ * ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page,
+ * forward, bidirectional branch (its attention_mask path).
+ *   valid       in   device, [B, L] uint8: nonzero = real token, 0 = padding;
+ *                    row b serves the H heads of batch element b. NULL is
+ *                    CA_ERR_INVALID_ARG (call cluster_attn_forward_ex).
+ *   Semantics: a padded key's scaled score is replaced by -10000 in the
+ *   centroid-key softmax and inside the local window; the output row of a
+ *   padded query is zero; the clustering runs over all L tokens, padded ones
+ *   included, and assign_out reports every token.
+ *   Every other argument, the workspace size and the paths are those of
+ *   cluster_attn_forward_ex; valid must not overlap out, assign_out or the
+ *   workspace.
+ */
+ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void *V,
+                                        const uint8_t *valid, int B, int H, int L, int d,
+                                        int nclust, int iters, int W, float alpha, void *out,
+                                        int32_t *assign_out, ca_dtype_t dt,
+                                        void *workspace, size_t workspace_bytes,
+                                        ca_path_t path, hipStream_t stream);
 
 /* ---------------------------------------------------------------------
  * Single steps (one kernel each), for callers composing their own loop and

@@ -37,6 +37,8 @@ SIGNATURES = {
                                   _vp, _sz, _vp]),
     "cluster_attn_forward_ex": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                      _i, _vp, _sz, _i, _vp]),
+    "cluster_attn_forward_masked": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                         _vp, _i, _vp, _sz, _i, _vp]),
     "ca_kmeans_assign": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "ca_centroid_update": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ca_centroid_update_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -145,11 +147,13 @@ def cluster_attn_workspace_size(B, H, L, d, nclust, dtype=CA_F32, path=CA_PATH_A
 
 def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float, out=None,
                          assign_out=None, path: int = CA_PATH_AUTO, workspace=None,
-                         stream=None, want_assign: bool = True):
+                         stream=None, want_assign: bool = True, valid=None):
     """Q, K, V: contiguous [B, H, L, d] float32 or bfloat16 GPU tensors.
 
-    Returns (out, assign_out); allocates out/assign_out/workspace with torch
-    when not given.
+    valid: optional key-padding mask, a contiguous [B, L] uint8 (or bool) GPU
+    tensor, nonzero = real token; given, the call goes to
+    cluster_attn_forward_masked. Returns (out, assign_out); allocates
+    out/assign_out/workspace with torch when not given.
     """
     torch = _torch()
     B, H, L, d = Q.shape
@@ -160,6 +164,15 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
         assign_out = torch.empty((B, H, L), dtype=torch.int32, device=Q.device)
     need = cluster_attn_workspace_size(B, H, L, d, nclust, dt, path)
     ws = _workspace(need, Q.device, workspace)
+    if valid is not None:
+        if tuple(valid.shape) != (B, L) or valid.element_size() != 1:
+            raise ValueError("valid must be a [B, L] tensor of one-byte elements")
+        st = lib().cluster_attn_forward_masked(
+            _ptr(Q), _ptr(K), _ptr(V), _ptr(valid), B, H, L, d, nclust, iters, W, float(alpha),
+            _ptr(out), _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws), path,
+            _stream(stream))
+        _check(st, "cluster_attn_forward_masked")
+        return out, assign_out
     st = lib().cluster_attn_forward_ex(
         _ptr(Q), _ptr(K), _ptr(V), B, H, L, d, nclust, iters, W, float(alpha), _ptr(out),
         _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws), path, _stream(stream))

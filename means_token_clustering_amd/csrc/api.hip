@@ -74,9 +74,10 @@ ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_H
         if (_e != hipSuccess) return CA_ERR_HIP;      \
     } while (0)
 
-ca_status_t forward_impl(const void *Q, const void *K, const void *V, int B, int H, int L, int d,
-                         int nclust, int iters, int W, float alpha, void *out,
-                         int32_t *assign_out, ca_dtype_t dt, void *workspace,
+// valid: key-padding mask [B, L] or nullptr (the unmasked operation).
+ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint8_t *valid, int B,
+                         int H, int L, int d, int nclust, int iters, int W, float alpha,
+                         void *out, int32_t *assign_out, ca_dtype_t dt, void *workspace,
                          size_t workspace_bytes, ca_path_t path, hipStream_t stream) {
     ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
     if (st != CA_OK) return st;
@@ -97,12 +98,16 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, int B, int
                        overlap(assign_out, abytes, K, tbytes) ||
                        overlap(assign_out, abytes, V, tbytes)))
         return CA_ERR_INVALID_ARG;
+    const size_t vbytes = (size_t)B * L;
+    if (valid && (overlap(valid, vbytes, out, tbytes) ||
+                  (assign_out && overlap(valid, vbytes, assign_out, abytes))))
+        return CA_ERR_INVALID_ARG;
     const int Kc = clusters(nclust, L);
     if (path == CA_PATH_FUSED && !fused_supported(L, Kc)) return CA_ERR_UNSUPPORTED;
 
     if (use_fused(path, L, Kc)) {
-        return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, W, alpha, dt, out,
-                                               assign_out, stream));
+        return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, W, alpha, dt, valid,
+                                               H, out, assign_out, stream));
     }
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
@@ -110,7 +115,8 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, int B, int
     char *ws = static_cast<char *>(workspace);
     if (overlap(ws, lay.total, out, tbytes) || overlap(ws, lay.total, Q, tbytes) ||
         overlap(ws, lay.total, K, tbytes) || overlap(ws, lay.total, V, tbytes) ||
-        (assign_out && overlap(ws, lay.total, assign_out, abytes)))
+        (assign_out && overlap(ws, lay.total, assign_out, abytes)) ||
+        (valid && overlap(ws, lay.total, valid, vbytes)))
         return CA_ERR_INVALID_ARG;
     float *mu = reinterpret_cast<float *>(ws + lay.mu);
     int32_t *c = assign_out ? assign_out : reinterpret_cast<int32_t *>(ws + lay.assign);
@@ -124,9 +130,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, int B, int
                                     stream));
         CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream));
     }
-    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, vcent, xpart, stream));
-    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, out, nullptr,
-                               stream));
+    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, vcent, xpart, stream));
+    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, valid, H, out,
+                               nullptr, stream));
     return CA_OK;
 }
 
@@ -216,8 +222,8 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V, in
                                  int d, int nclust, int iters, int W, float alpha, void *out,
                                  int32_t *assign_out, ca_dtype_t dt, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-    return forward_impl(Q, K, V, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
-                        workspace, workspace_bytes, CA_PATH_AUTO, stream);
+    return forward_impl(Q, K, V, nullptr, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
+                        dt, workspace, workspace_bytes, CA_PATH_AUTO, stream);
 }
 
 ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V, int B, int H,
@@ -225,7 +231,18 @@ ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     void *out, int32_t *assign_out, ca_dtype_t dt,
                                     void *workspace, size_t workspace_bytes, ca_path_t path,
                                     hipStream_t stream) {
-    return forward_impl(Q, K, V, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
+    return forward_impl(Q, K, V, nullptr, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
+                        dt, workspace, workspace_bytes, path, stream);
+}
+
+ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void *V,
+                                        const uint8_t *valid, int B, int H, int L, int d,
+                                        int nclust, int iters, int W, float alpha, void *out,
+                                        int32_t *assign_out, ca_dtype_t dt, void *workspace,
+                                        size_t workspace_bytes, ca_path_t path,
+                                        hipStream_t stream) {
+    if (!valid) return CA_ERR_INVALID_ARG;
+    return forward_impl(Q, K, V, valid, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
                         workspace, workspace_bytes, path, stream);
 }
 
@@ -282,7 +299,7 @@ ca_status_t ca_centroid_xattn(const float *mu, const void *K, const void *V, int
     const size_t need = ca_centroid_xattn_workspace_size(S, L, d, Kc);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
         return CA_ERR_INVALID_ARG;
-    return hip_status(launch_centroid_xattn(mu, K, V, S, L, Kc, dt, vcent,
+    return hip_status(launch_centroid_xattn(mu, K, V, S, L, Kc, dt, nullptr, 1, vcent,
                                             static_cast<float *>(workspace), stream));
 }
 
@@ -294,7 +311,7 @@ ca_status_t ca_local_window_attn(const void *Q, const void *K, const void *V, in
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(oloc, 16))
         return CA_ERR_INVALID_ARG;
     return hip_status(launch_local_window(Q, K, V, S, L, W, dt, nullptr, nullptr, 1, 1.f, nullptr,
-                                          oloc, stream));
+                                          1, nullptr, oloc, stream));
 }
 
 ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
@@ -356,8 +373,9 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq, const void
     const uint16_t *wqkv[3] = {wt[0], wt[1], wt[2]};
     CA_TRY(launch_gemm_nt(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
                           false, true, L, H, stream));
-    st = forward_impl(heads[0], heads[1], heads[2], B, H, L, d, nclust, iters, W, alpha, O,
-                      assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO, stream);
+    st = forward_impl(heads[0], heads[1], heads[2], nullptr, B, H, L, d, nclust, iters, W, alpha,
+                      O, assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO,
+                      stream);
     if (st != CA_OK) return st;
     const uint16_t *wo[1] = {wt[3]};
     uint16_t *yv[1] = {static_cast<uint16_t *>(Y)};

@@ -106,21 +106,24 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
                                   int S, int Kc, float *mu, int32_t *counts, hipStream_t st);
 
 int xattn_splits(int L);
+// valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
+// belongs to batch row s / H.
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, ca_dtype_t dt, float *vcent, float *partials,
-                                 hipStream_t st);
+                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H,
+                                 float *vcent, float *partials, hipStream_t st);
 
 hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
-                               float alpha, void *out, float *oloc, hipStream_t st);
+                               float alpha, const uint8_t *valid, int H, void *out, float *oloc,
+                               hipStream_t st);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);
 
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                int iters, int W, float alpha, ca_dtype_t dt, void *out,
-                                int32_t *assign, hipStream_t st);
+                                int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
+                                int H, void *out, int32_t *assign, hipStream_t st);
 
 // C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
 // A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as

@@ -289,6 +289,22 @@ __device__ __forceinline__ Sp8 colfrag8_at(const u8 *base, int o0, int o1) {
     return Sp8{u32x4_t{h0[0], h0[1], h1[0], h1[1]}, u32x4_t{m0[0], m0[1], m1[0], m1[1]}};
 }
 
+// Key-padding mask of a slice, one bit per token (bit t of word t / 32); all
+// bits set when the launch has no mask. A padded key's logit is -10000 in
+// natural units (ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-
+// cluster" page, forward, bidirectional branch), -10000 log2(e) in the base-2
+// units used here.
+struct KeyBits {
+    uint32_t w[4];
+    // the 16 bits of key tile t (t uniform over the wave)
+    __device__ __forceinline__ uint32_t tile(int t) const {
+        const int k = t >> 1;
+        const uint32_t x = k == 0 ? w[0] : (k == 1 ? w[1] : (k == 2 ? w[2] : w[3]));
+        return (x >> (16 * (t & 1))) & 0xffffu;
+    }
+};
+constexpr float kPadLogit2 = -14426.950408889634f;
+
 // Local window of radius <= 16 for query tile qt: scores against key tiles
 // qt-1, qt, qt+1 (others are outside every window of the tile), base-2
 // softmax, then O^T = V^T P^T: the pair (qt-1, qt) as one 32-deep product and
@@ -297,11 +313,11 @@ __device__ __forceinline__ Sp8 colfrag8_at(const u8 *base, int o0, int o1) {
 // read of a stage is issued before its first product, and the products of
 // independent tiles alternate, so that neither the LDS latency nor the
 // matrix-core latency is exposed per product.
-template <bool FULL>
+template <bool FULL, bool MASKED>
 __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
-                                             int l16, int g, int rl64, int trv, f32x4_t *o,
-                                             float &lsum) {
+                                             int l16, int g, int rl64, int trv, const KeyBits &kb,
+                                             f32x4_t *o, float &lsum) {
     bool valid[3];
     Sp8 kfr[3][2];
 #pragma unroll
@@ -334,6 +350,7 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
         const int kt = qt + d - 1;
+        const uint32_t nib = MASKED ? kb.tile(valid[d] ? kt : qt) >> (4 * g) : 0xfu;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {   // sc[d][rr] = k_{16kt+4g+rr} . q_{16qt+l16}
             bool in;
@@ -341,7 +358,8 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
             else if (d == 2) in = valid[2] && hi2 <= -rr;
             else in = whole1 || (rel0 + rr <= rad && -(rel0 + rr) <= rad);
             if (!FULL) in = in && 16 * kt + 4 * g + rr < L;
-            s[d][rr] = in ? sc[d][rr] * sscale2 : -__builtin_inff();
+            const float sv = (!MASKED || ((nib >> rr) & 1u)) ? sc[d][rr] * sscale2 : kPadLogit2;
+            s[d][rr] = in ? sv : -__builtin_inff();
             m = fmaxf(m, s[d][rr]);
         }
     }
@@ -395,11 +413,11 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 // Local window of any radius: key tiles in [qt - ceil(r/16), qt + ceil(r/16)]
 // two at a time with a running maximum (online softmax) and 32-deep P V
 // products; a missing second tile gets zero weights on repeated V rows.
-template <bool FULL>
+template <bool FULL, bool MASKED>
 __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                            int qt, int NT, int L, int rad, float sscale2,
-                                           int l16, int g, int rl64, int trv, f32x4_t *o,
-                                           float &lsum) {
+                                           int l16, int g, int rl64, int trv, const KeyBits &kb,
+                                           f32x4_t *o, float &lsum) {
     const int qi = 16 * qt + l16;
     const int lo_key = 16 * qt - rad, hi_key = 16 * qt + 15 + rad;
     const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
@@ -416,12 +434,14 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
             const int ktt = two ? kt + h : kt;
             f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * ktt + rl64), qf[0], kZero4);
             a = mma3(frag_at(pK, kPlane, 2048 * ktt + (rl64 ^ 64)), qf[1], a);
+            const uint32_t nib = MASKED ? kb.tile(ktt) >> (4 * g) : 0xfu;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * ktt + 4 * g + rr;
                 const int dist = key > qi ? key - qi : qi - key;
                 const bool in = (FULL || key < L) && dist <= rad && (h == 0 || two);
-                s[4 * h + rr] = in ? a[rr] * sscale2 : -__builtin_inff();
+                const float sv = (!MASKED || ((nib >> rr) & 1u)) ? a[rr] * sscale2 : kPadLogit2;
+                s[4 * h + rr] = in ? sv : -__builtin_inff();
                 mt = fmaxf(mt, s[4 * h + rr]);
             }
         }
@@ -454,11 +474,14 @@ struct InitMask {
     uint32_t w[4];
 };
 
-template <typename T, bool FULL, bool NARROW>
+// MASKED: valid is the key-padding mask [S / H, L] (nonzero = real token);
+// padded keys take the logit -10000 in both softmaxes, and the output rows of
+// padded queries are zero.
+template <typename T, bool FULL, bool NARROW, bool MASKED>
 __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
-    int Kc, int iters, int radius, float alpha, T *__restrict__ out,
-    int32_t *__restrict__ assign_out, InitMask init) {
+    int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H,
+    T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init) {
     __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
@@ -496,6 +519,12 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     float qraw[2][8], kraw[2][8], vraw[2][8];
 #pragma unroll
     for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+    // waves 0 and 1: the key-padding mask of tokens 64w .. 64w+63 (one byte each)
+    bool tok_ok = false;
+    if (MASKED && w < 2) {
+        const int t = 64 * w + lane;
+        tok_ok = t < L && valid[(slice / H) * (long)L + t] != 0;
+    }
     {   // largest |q| of the slice (bit patterns of |x| order like the values)
         const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
         if (lane == 0) sMax[w * 4 + 0] = bq;
@@ -559,7 +588,18 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         sMu[off64(kk, dd)] = 0;
         sMu[kPlaneMuE + off64(kk, dd)] = 0;
     }
+    if (MASKED && w < 2) {   // mask words 2w, 2w+1 into the spare slot of the maxima
+        const uint64_t bits = __ballot(tok_ok);
+        if (lane == 0) {
+            sMax[4 * (2 * w) + 3] = (uint32_t)bits;
+            sMax[4 * (2 * w + 1) + 3] = (uint32_t)(bits >> 32);
+        }
+    }
     __syncthreads();
+    KeyBits kb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[4 * k + 3]) : ~0u;
 
     int sq;
     {
@@ -715,10 +755,12 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             __builtin_amdgcn_sched_barrier(0);
             f32x4_t a = mma3(k0, m0, kZero4);
             a = mma3(k1, m1, a);
+            const uint32_t nib = MASKED ? kb.tile(w) >> (4 * g) : 0xfu;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * w + 4 * g + rr;   // a[rr] = k_key . mu_l16
-                sx[rr] = (FULL || key < L) ? a[rr] * sscale2 : -__builtin_inff();
+                const float sv = (!MASKED || ((nib >> rr) & 1u)) ? a[rr] * sscale2 : kPadLogit2;
+                sx[rr] = (FULL || key < L) ? sv : -__builtin_inff();
                 mloc = fmaxf(mloc, sx[rr]);
             }
             mloc = col_max(mloc);
@@ -809,9 +851,11 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     if (FULL || w < NT) {
         const int rad = radius < L ? radius : L;
         if (NARROW)
-            local_narrow<FULL>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
+            local_narrow<FULL, MASKED>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv,
+                                       kb, o, lsum);
         else
-            local_wide<FULL>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, o, lsum);
+            local_wide<FULL, MASKED>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, kb,
+                                     o, lsum);
     }
     __syncthreads();
 
@@ -827,12 +871,14 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         if (FULL || w < NT) {
             const float f = alpha * vunscale * __builtin_amdgcn_rcpf(lsum);
             const float *vc = sVc + sC[tok] * kVcRow;
+            const bool keep = !MASKED || ((kb.tile(w) >> l16) & 1u);   // padded query: zero row
 #pragma unroll
             for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
                 const int d0 = 16 * j + 4 * g;
                 const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
-                const float v0 = fmaf(o[j][0], f, c4.x), v1 = fmaf(o[j][1], f, c4.y);
-                const float v2 = fmaf(o[j][2], f, c4.z), v3 = fmaf(o[j][3], f, c4.w);
+                float v0 = fmaf(o[j][0], f, c4.x), v1 = fmaf(o[j][1], f, c4.y);
+                float v2 = fmaf(o[j][2], f, c4.z), v3 = fmaf(o[j][3], f, c4.w);
+                if (MASKED && !keep) v0 = v1 = v2 = v3 = 0.f;
                 const int byte = d0 * (int)sizeof(T);   // within the row
                 u8 *p = stg + l16 * kRowB + ((((byte >> 4) ^ (l16 & (kCpr - 1)))) << 4) + (byte & 15);
                 if (sizeof(T) == 4) {
@@ -861,11 +907,11 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }
 
-template <typename T, bool FULL, bool NARROW>
+template <typename T, bool FULL, bool NARROW, bool MASKED>
 static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                 int iters, int radius, float alpha, void *out, int32_t *assign,
-                                 hipStream_t st) {
-    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW>;
+                                 int iters, int radius, float alpha, const uint8_t *valid, int H,
+                                 void *out, int32_t *assign, hipStream_t st) {
+    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED>;
     InitMask init{};
     for (int k = 0; k < Kc; ++k) {
         const int t = (int)(((long)k * L) / Kc);
@@ -873,33 +919,48 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), 0, st,
                        static_cast<const T *>(Q), static_cast<const T *>(K),
-                       static_cast<const T *>(V), S, L, Kc, iters, radius, alpha,
+                       static_cast<const T *>(V), S, L, Kc, iters, radius, alpha, valid, H,
                        static_cast<T *>(out), assign, init);
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t fused_launch(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                               int iters, int W, float alpha, void *out, int32_t *assign,
-                               hipStream_t st) {
+template <typename T, bool MASKED>
+static hipError_t fused_launch_m(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                                 int iters, int W, float alpha, const uint8_t *valid, int H,
+                                 void *out, int32_t *assign, hipStream_t st) {
     const int radius = W / 2;
     const bool full = L == kFL;
     const bool narrow = radius <= 16;
     if (full && narrow)
-        return fused_launch_t<T, true, true>(Q, K, V, S, L, Kc, iters, radius, alpha, out, assign, st);
+        return fused_launch_t<T, true, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
+                                                     H, out, assign, st);
     if (full)
-        return fused_launch_t<T, true, false>(Q, K, V, S, L, Kc, iters, radius, alpha, out, assign, st);
+        return fused_launch_t<T, true, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
+                                                      valid, H, out, assign, st);
     if (narrow)
-        return fused_launch_t<T, false, true>(Q, K, V, S, L, Kc, iters, radius, alpha, out, assign, st);
-    return fused_launch_t<T, false, false>(Q, K, V, S, L, Kc, iters, radius, alpha, out, assign, st);
+        return fused_launch_t<T, false, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
+                                                      valid, H, out, assign, st);
+    return fused_launch_t<T, false, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
+                                                   H, out, assign, st);
+}
+
+template <typename T>
+static hipError_t fused_launch(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                               int iters, int W, float alpha, const uint8_t *valid, int H,
+                               void *out, int32_t *assign, hipStream_t st) {
+    if (valid)
+        return fused_launch_m<T, true>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign,
+                                       st);
+    return fused_launch_m<T, false>(Q, K, V, S, L, Kc, iters, W, alpha, nullptr, 1, out, assign,
+                                    st);
 }
 
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                int iters, int W, float alpha, ca_dtype_t dt, void *out,
-                                int32_t *assign, hipStream_t st) {
+                                int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
+                                int H, void *out, int32_t *assign, hipStream_t st) {
     if (dt == CA_BF16)
-        return fused_launch<bf16_t>(Q, K, V, S, L, Kc, iters, W, alpha, out, assign, st);
-    return fused_launch<float>(Q, K, V, S, L, Kc, iters, W, alpha, out, assign, st);
+        return fused_launch<bf16_t>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign, st);
+    return fused_launch<float>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign, st);
 }
 
 }  // namespace ca

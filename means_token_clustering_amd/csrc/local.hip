@@ -14,6 +14,11 @@
 // products meet through two butterfly adds that every lane performs in the
 // same order, so all four see the same score. Scores of one key tile go to
 // LDS, then an online softmax folds the tile in.
+//
+// Key-padding mask (optional; ClusterAttention listing on the
+// "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
+// a key with valid[b * L + j] == 0 takes the logit -10000 inside the window,
+// and the fused output row of a padded query is zero (b = s / H).
 #include "common.h"
 
 namespace ca {
@@ -26,10 +31,12 @@ template <typename T, bool FUSE>
 __global__ __launch_bounds__(256) void local_window_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int r,
     int ntile, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
-    float alpha, T *__restrict__ out, float *__restrict__ oloc) {
+    float alpha, const uint8_t *__restrict__ valid, int H, T *__restrict__ out,
+    float *__restrict__ oloc) {
     __shared__ float sm_k[kLTile * kLPad];
     __shared__ float sm_v[kLTile * kLPad];
     __shared__ float sm_s[kQTile * kLPad];
+    __shared__ uint8_t sm_ok[kLTile];
 
     const int tid = threadIdx.x;
     const int tile = blockIdx.x % ntile;
@@ -76,6 +83,8 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
             dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
         }
+        for (int rr = tid; rr < nk; rr += 256)
+            sm_ok[rr] = valid == nullptr || valid[(s / H) * L + jt + rr] != 0;
         __syncthreads();
         // keys of this tile inside this query's window
         const int a = active ? max(lo, jt) - jt : 0;
@@ -93,6 +102,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
             float sum2 = part + __shfl_xor(part, 1);
             float sc = sum2 + __shfl_xor(sum2, 2);
+            if (!sm_ok[key]) sc = -10000.f;
             if (key >= a && key <= b) {
                 mt = fmaxf(mt, sc);
                 if (g == 0) sm_s[qi * kLPad + key] = sc;
@@ -121,14 +131,16 @@ __global__ __launch_bounds__(256) void local_window_kernel(
     if (FUSE) {
         const int c = assign[s * L + i];
         const float *gv = vcent + (s * Kc + c) * kD + 16 * g;
-        const float wg = 1.0f - alpha;
+        const bool keep = valid == nullptr || valid[(s / H) * L + i] != 0;
+        const float wg = keep ? 1.0f - alpha : 0.f;
+        const float wl = keep ? alpha : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float4 v;
-            v.x = wg * gv[4 * q + 0] + alpha * (acc[4 * q + 0] * inv);
-            v.y = wg * gv[4 * q + 1] + alpha * (acc[4 * q + 1] * inv);
-            v.z = wg * gv[4 * q + 2] + alpha * (acc[4 * q + 2] * inv);
-            v.w = wg * gv[4 * q + 3] + alpha * (acc[4 * q + 3] * inv);
+            v.x = wg * gv[4 * q + 0] + wl * (acc[4 * q + 0] * inv);
+            v.y = wg * gv[4 * q + 1] + wl * (acc[4 * q + 1] * inv);
+            v.z = wg * gv[4 * q + 2] + wl * (acc[4 * q + 2] * inv);
+            v.w = wg * gv[4 * q + 3] + wl * (acc[4 * q + 3] * inv);
             store4<T>(out + o + 4 * q, v);
         }
     } else {
@@ -168,7 +180,8 @@ __global__ __launch_bounds__(256) void gather_fuse_kernel(const float *__restric
 template <typename T>
 static hipError_t local_dispatch(const void *Q, const void *K, const void *V, int S, int L, int W,
                                  const float *vcent, const int32_t *assign, int Kc, float alpha,
-                                 void *out, float *oloc, hipStream_t st) {
+                                 const uint8_t *valid, int H, void *out, float *oloc,
+                                 hipStream_t st) {
     const int ntile = (L + kQTile - 1) / kQTile;
     const int r = W / 2;
     const dim3 grid((unsigned)((long)S * ntile)), block(256);
@@ -177,19 +190,23 @@ static hipError_t local_dispatch(const void *Q, const void *K, const void *V, in
     const T *v = static_cast<const T *>(V);
     if (oloc == nullptr)
         hipLaunchKernelGGL((local_window_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, ntile,
-                           vcent, assign, Kc, alpha, static_cast<T *>(out), oloc);
+                           vcent, assign, Kc, alpha, valid, H, static_cast<T *>(out), oloc);
     else
         hipLaunchKernelGGL((local_window_kernel<T, false>), grid, block, 0, st, q, k, v, L, r,
-                           ntile, vcent, assign, Kc, alpha, static_cast<T *>(out), oloc);
+                           ntile, vcent, assign, Kc, alpha, valid, H, static_cast<T *>(out),
+                           oloc);
     return hipGetLastError();
 }
 
 hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
-                               float alpha, void *out, float *oloc, hipStream_t st) {
+                               float alpha, const uint8_t *valid, int H, void *out, float *oloc,
+                               hipStream_t st) {
     if (dt == CA_BF16)
-        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, out, oloc, st);
-    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, out, oloc, st);
+        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, out,
+                                      oloc, st);
+    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, out, oloc,
+                                 st);
 }
 
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,

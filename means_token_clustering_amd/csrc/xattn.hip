@@ -9,6 +9,10 @@
 // for 16 centroids at a time, 16 lanes per centroid. With one range the
 // result is written directly; otherwise each range stores (max, sum, acc)
 // and a combine kernel merges the ranges in range order (deterministic).
+//
+// Key-padding mask (optional; ClusterAttention listing on the
+// "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
+// a key with valid[b * L + j] == 0 takes the logit -10000 (b = s / H).
 #include "common.h"
 
 namespace ca {
@@ -35,11 +39,13 @@ static int keys_per_split(int L, int nsplit) {
 template <typename T>
 __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     const float *__restrict__ mu, const T *__restrict__ Kx, const T *__restrict__ Vx, int L,
-    int Kc, int nsplit, int kps, float *__restrict__ vcent, float *__restrict__ part) {
+    int Kc, int nsplit, int kps, const uint8_t *__restrict__ valid, int H,
+    float *__restrict__ vcent, float *__restrict__ part) {
     __shared__ float sm_k[kKeyTile * kXPad];
     __shared__ float sm_v[kKeyTile * kXPad];
     __shared__ float sm_mu[kChunk * kXPad];
     __shared__ float sm_p[kChunk * kKeyTile];
+    __shared__ uint8_t sm_ok[kKeyTile];
 
     const int tid = threadIdx.x;
     const int split = blockIdx.x % nsplit;
@@ -74,6 +80,8 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
                 dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
                 dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
             }
+            for (int r = tid; r < nk; r += 256)
+                sm_ok[r] = valid == nullptr || valid[(s / H) * L + jt + r] != 0;
             __syncthreads();
             float sc[4];
             float mt = -__builtin_inff();
@@ -85,7 +93,7 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
                     const float *kr = sm_k + key * kXPad;
                     float dot = 0.f;
                     for (int j = 0; j < kD; ++j) dot = fmaf(mr[j], kr[j], dot);
-                    sc[u] = dot * scale;
+                    sc[u] = sm_ok[key] ? dot * scale : -10000.f;
                 } else {
                     sc[u] = -__builtin_inff();
                 }
@@ -158,14 +166,15 @@ __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restr
 
 template <typename T>
 static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, float *vcent, float *partials, hipStream_t st) {
+                                 int Kc, const uint8_t *valid, int H, float *vcent,
+                                 float *partials, hipStream_t st) {
     const int nsplit = xattn_splits(L);
     const int kps = keys_per_split(L, nsplit);
     const int used = (L + kps - 1) / kps;   // ranges that hold keys
     const dim3 grid((unsigned)((long)S * used)), block(256);
     hipLaunchKernelGGL(centroid_xattn_kernel<T>, grid, block, 0, st, mu,
                        static_cast<const T *>(K), static_cast<const T *>(V), L, Kc, used, kps,
-                       vcent, partials);
+                       valid, H, vcent, partials);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || used == 1) return err;
     const long total = (long)S * Kc * kD;
@@ -175,10 +184,11 @@ static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, 
 }
 
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, ca_dtype_t dt, float *vcent, float *partials,
-                                 hipStream_t st) {
-    if (dt == CA_BF16) return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, vcent, partials, st);
-    return xattn_dispatch<float>(mu, K, V, S, L, Kc, vcent, partials, st);
+                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H,
+                                 float *vcent, float *partials, hipStream_t st) {
+    if (dt == CA_BF16)
+        return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, vcent, partials, st);
+    return xattn_dispatch<float>(mu, K, V, S, L, Kc, valid, H, vcent, partials, st);
 }
 
 }  // namespace ca

@@ -182,3 +182,28 @@ def workload(name: str, seed: Optional[int] = None):
 
 
 WORKLOADS = ("tiny", "distilbert", "bf16_l512", "long_l8192", "layer_bf16")
+
+
+def make_mask(B: int, L: int, *, seed: int = 0, kind: str = "prefix",
+              min_len: Optional[int] = None) -> np.ndarray:
+    """Key-padding mask [B, L] uint8 (1 = real token, 0 = padding).
+
+    kind "prefix": right padding as in a padded batch of sentences; row b keeps
+    its first n_b tokens, n_b ~ U{min_len .. L} (min_len defaults to L // 4,
+    at least 1), drawn with numpy.random.default_rng(seed). kind "holes":
+    every token is real with probability 0.7, independently (rows may lose
+    any token, including all of them). kind "ones" / "zeros": all real / all
+    padding.
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "ones":
+        return np.ones((B, L), np.uint8)
+    if kind == "zeros":
+        return np.zeros((B, L), np.uint8)
+    if kind == "holes":
+        return (rng.random((B, L)) < 0.7).astype(np.uint8)
+    if kind != "prefix":
+        raise ValueError(kind)
+    lo = max(1, L // 4 if min_len is None else min_len)
+    n = rng.integers(lo, L + 1, size=B)
+    return (np.arange(L)[None, :] < n[:, None]).astype(np.uint8)

@@ -54,9 +54,10 @@ def check_assignment_step(Q: np.ndarray, mu: np.ndarray, c_gpu: np.ndarray, t: i
 
 def check_forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float, dtype: str,
                   assign_by_iter: List[np.ndarray], out_gpu: np.ndarray,
-                  tol: Optional[float] = None):
+                  tol: Optional[float] = None, valid: Optional[np.ndarray] = None):
     """Full protocol. assign_by_iter[t-1] = GPU c^(t); out_gpu = GPU output
-    (as float64 values) of the run with `iters` iterations."""
+    (as float64 values) of the run with `iters` iterations; valid: the key-
+    padding mask of a masked run (the clustering ignores it)."""
     L = Q.shape[-2]
     K = oracle.num_clusters(nclust, L)
     reports = []
@@ -65,7 +66,7 @@ def check_forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float, dtype
         c_gpu = assign_by_iter[t - 1]
         reports.append(check_assignment_step(Q, mu, c_gpu, t))
         mu, _ = oracle.update(Q, c_gpu, K)
-    ref = oracle.forward_from_assign(Q, Kt, V, assign_by_iter[-1], K, W, alpha)
+    ref = oracle.forward_from_assign(Q, Kt, V, assign_by_iter[-1], K, W, alpha, valid=valid)
     err = np.abs(out_gpu - ref["out"])
     tol = TOL[dtype] if tol is None else tol
     return reports, float(err.max()) if err.size else 0.0, tol, ref

@@ -147,3 +147,29 @@ def test_gemm_rejects():
     assert lib.ca_gemm_bf16(A_ + 8, B_, 64, 64, 64, C_, None) == INV
     assert lib.ca_gemm_bf16(A_, B_, 64, 100, 64, C_, None) == UNS
     assert lib.ca_gemm_bf16(A_, B_, 64, 64, 96, C_, None) == UNS
+
+
+MASK = 0x10000000 * 8
+
+
+def fwd_masked(**kw):
+    a = dict(Q=Q, K=K, V=V, valid=MASK, B=2, H=3, L=128, d=64, nclust=16, iters=3, W=32,
+             alpha=0.5, out=OUT, assign=ASG, dt=b.CA_F32, ws=WS, wsb=1 << 30,
+             path=b.CA_PATH_STAGED)
+    a.update(kw)
+    return b.lib().cluster_attn_forward_masked(
+        a["Q"], a["K"], a["V"], a["valid"], a["B"], a["H"], a["L"], a["d"], a["nclust"],
+        a["iters"], a["W"], a["alpha"], a["out"], a["assign"], a["dt"], a["ws"], a["wsb"],
+        a["path"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(valid=None), INV), (dict(valid=OUT + 64), INV), (dict(valid=ASG), INV),
+    (dict(valid=WS + 1024), INV), (dict(Q=None), INV), (dict(alpha=2.0), INV),
+    (dict(iters=0), INV), (dict(ws=None), INV), (dict(d=32), UNS),
+    (dict(path=b.CA_PATH_FUSED, L=5000), UNS),
+])
+def test_masked_forward_rejects(kw, code):
+    """The masked entry point runs the same host checks, plus: a mask is
+    required and must not overlap the outputs or the workspace."""
+    assert fwd_masked(**kw) == code

@@ -229,3 +229,73 @@ def test_extreme_magnitudes(scales, path):
     for r in reports:
         assert r.bad == 0, parity.summarize(reports)
     assert err <= 1e-4 * sv
+
+
+# ---------------------------------------------------------------- key-padding mask
+def check_masked(x: gen.AttnInputs, mask: np.ndarray, path: int, tol=None):
+    """Masked forward: per-iteration assignments equal the unmasked run's (the
+    clustering ignores the mask), outputs match the oracle's masked steps on
+    the GPU's assignment, padded query rows are exactly zero."""
+    b = _b()
+    _say(f"[masked] {x.name or 'case'} B={x.B} H={x.H} L={x.L} K={x.nclust} I={x.iters} "
+         f"W={x.W} {x.dtype} seed={x.seed} path={path} real={int(mask.sum())}/{mask.size}")
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    vd = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda()
+    assigns, out = [], None
+    for t in range(1, x.iters + 1):
+        o, c = b.cluster_attn_forward(q, k, v, x.nclust, t, x.W, x.alpha, path=path, valid=vd)
+        o0, c0 = b.cluster_attn_forward(q, k, v, x.nclust, t, x.W, x.alpha, path=path)
+        assert torch.equal(c, c0), "the mask changed the clustering"
+        assigns.append(c.cpu().numpy())
+        out = o
+    torch.cuda.synchronize()
+    outh = _host(out)
+    pad = np.broadcast_to((mask == 0)[:, None, :], (x.B, x.H, x.L))
+    assert np.all(outh[pad] == 0.0), "padded query rows must be zero"
+    reports, err, tol, _ = parity.check_forward(
+        x.values("q"), x.values("k"), x.values("v"), x.nclust, x.iters, x.W, x.alpha, x.dtype,
+        assigns, outh, tol, valid=mask)
+    _say(f"  {parity.summarize(reports)}; max|out-ref|={err:.3e} (tol {tol})")
+    for r in reports:
+        assert r.bad == 0, parity.summarize(reports)
+    assert err <= tol
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("name", ["tiny", "distilbert", "bf16_l512"])
+def test_masked_workloads(name, path):
+    x = gen.workload(name)
+    check_masked(x, gen.make_mask(x.B, x.L, seed=x.seed + 500), path)
+
+
+MASK_EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, mask kind
+    (2, 3, 128, 16, 3, 32, 0.5, gen.F32, "holes"),
+    (3, 2, 100, 16, 3, 32, 0.3, gen.F32, "prefix"),   # L < 128: partial tiles
+    (2, 2, 128, 16, 3, 100, 0.5, gen.F32, "holes"),   # wide window
+    (2, 2, 90, 8, 2, 70, 0.6, gen.BF16, "holes"),
+    (1, 2, 300, 16, 3, 32, 0.5, gen.F32, "prefix"),   # staged only (L > 128)
+    (2, 2, 128, 16, 3, 32, 0.5, gen.F32, "zeros"),    # everything padded
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", MASK_EDGE)
+def test_masked_edge_cases(case, path):
+    B, H, L, nclust, iters, W, alpha, dtype, kind = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha, dtype=dtype,
+                        seed=700 + L + W, blobs=8)
+    check_masked(x, gen.make_mask(B, L, seed=L + W, kind=kind), path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_masked_all_real_equals_unmasked(path):
+    """An all-ones mask gives bit-identical outputs to the unmasked call."""
+    b = _b()
+    x = gen.workload("distilbert")
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    vd = torch.ones((x.B, x.L), dtype=torch.uint8, device="cuda")
+    o1, c1 = b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, path=path, valid=vd)
+    o0, c0 = b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, path=path)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c0)
+    assert torch.equal(o1, o0)
