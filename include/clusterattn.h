@@ -134,6 +134,35 @@ ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void
                                         void *workspace, size_t workspace_bytes,
                                         ca_path_t path, hipStream_t stream);
 
+/*
+ * Options of cluster_attn_forward_opts (zero-initialise, then set fields).
+ *   valid     key-padding mask as in cluster_attn_forward_masked, or NULL.
+ *   kv_heads  heads of K and V: 0 (or H) means H; otherwise H must be a
+ *             multiple of kv_heads and the G = H / kv_heads consecutive query
+ *             heads h = G*j .. G*j+G-1 share K/V head j (grouped-query
+ *             attention, the listing's repeat_kv on the "Hooshaai/svd-sst2-
+ *             roberta-cluster" page; K and V are then [B, kv_heads, L, d]).
+ *   flags     must be 0 (CA_ERR_UNSUPPORTED otherwise); reserved.
+ */
+typedef struct {
+    const uint8_t *valid;
+    int kv_heads;
+    int flags;
+} ca_options_t;
+
+/*
+ * cluster_attn_forward_ex with options (opts NULL = defaults, which is
+ * cluster_attn_forward_ex itself). Workspace size: cluster_attn_workspace_size_ex
+ * of the same B, H, L. K and V must not overlap out, assign_out or the
+ * workspace; the mask rules are those of cluster_attn_forward_masked.
+ */
+ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *V, int B,
+                                      int H, int L, int d, int nclust, int iters, int W,
+                                      float alpha, const ca_options_t *opts, void *out,
+                                      int32_t *assign_out, ca_dtype_t dt, void *workspace,
+                                      size_t workspace_bytes, ca_path_t path,
+                                      hipStream_t stream);
+
 /* ---------------------------------------------------------------------
  * Single steps (one kernel each), for callers composing their own loop and
  * for step-by-step checking. S = B*H slices; Kc = number of centroids.

@@ -39,6 +39,8 @@ SIGNATURES = {
                                      _i, _vp, _sz, _i, _vp]),
     "cluster_attn_forward_masked": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
                                          _vp, _i, _vp, _sz, _i, _vp]),
+    "cluster_attn_forward_opts": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
+                                       _vp, _i, _vp, _sz, _i, _vp]),
     "ca_kmeans_assign": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "ca_centroid_update": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ca_centroid_update_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -51,6 +53,11 @@ SIGNATURES = {
                                         _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ca_gemm_bf16": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
 }
+
+
+class CaOptions(ctypes.Structure):
+    """ca_options_t of the C ABI."""
+    _fields_ = [("valid", _vp), ("kv_heads", _i), ("flags", _i)]
 
 
 class CaError(RuntimeError):
@@ -148,12 +155,13 @@ def cluster_attn_workspace_size(B, H, L, d, nclust, dtype=CA_F32, path=CA_PATH_A
 def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float, out=None,
                          assign_out=None, path: int = CA_PATH_AUTO, workspace=None,
                          stream=None, want_assign: bool = True, valid=None):
-    """Q, K, V: contiguous [B, H, L, d] float32 or bfloat16 GPU tensors.
+    """Q: contiguous [B, H, L, d] float32 or bfloat16 GPU tensor; K, V:
+    [B, Hkv, L, d] of the same dtype, Hkv dividing H (Hkv < H: grouped K/V
+    heads, cluster_attn_forward_opts).
 
     valid: optional key-padding mask, a contiguous [B, L] uint8 (or bool) GPU
-    tensor, nonzero = real token; given, the call goes to
-    cluster_attn_forward_masked. Returns (out, assign_out); allocates
-    out/assign_out/workspace with torch when not given.
+    tensor, nonzero = real token (cluster_attn_forward_masked). Returns (out,
+    assign_out); allocates out/assign_out/workspace with torch when not given.
     """
     torch = _torch()
     B, H, L, d = Q.shape
@@ -164,9 +172,20 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
         assign_out = torch.empty((B, H, L), dtype=torch.int32, device=Q.device)
     need = cluster_attn_workspace_size(B, H, L, d, nclust, dt, path)
     ws = _workspace(need, Q.device, workspace)
+    hkv = K.shape[1]
+    if tuple(V.shape) != tuple(K.shape) or K.shape[0] != B or K.shape[2:] != Q.shape[2:]:
+        raise ValueError("K and V must be [B, Hkv, L, d] with Q's B, L and d")
+    if valid is not None and (tuple(valid.shape) != (B, L) or valid.element_size() != 1):
+        raise ValueError("valid must be a [B, L] tensor of one-byte elements")
+    if hkv != H:
+        opts = CaOptions(_ptr(valid), hkv, 0)
+        st = lib().cluster_attn_forward_opts(
+            _ptr(Q), _ptr(K), _ptr(V), B, H, L, d, nclust, iters, W, float(alpha),
+            ctypes.byref(opts), _ptr(out), _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws),
+            path, _stream(stream))
+        _check(st, "cluster_attn_forward_opts")
+        return out, assign_out
     if valid is not None:
-        if tuple(valid.shape) != (B, L) or valid.element_size() != 1:
-            raise ValueError("valid must be a [B, L] tensor of one-byte elements")
         st = lib().cluster_attn_forward_masked(
             _ptr(Q), _ptr(K), _ptr(V), _ptr(valid), B, H, L, d, nclust, iters, W, float(alpha),
             _ptr(out), _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws), path,

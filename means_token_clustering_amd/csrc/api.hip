@@ -74,9 +74,10 @@ ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_H
         if (_e != hipSuccess) return CA_ERR_HIP;      \
     } while (0)
 
-// valid: key-padding mask [B, L] or nullptr (the unmasked operation).
-ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint8_t *valid, int B,
-                         int H, int L, int d, int nclust, int iters, int W, float alpha,
+// valid: key-padding mask [B, L] or nullptr (the unmasked operation); G:
+// query heads per K/V head (K and V are [B, H / G, L, d]).
+ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint8_t *valid, int G,
+                         int B, int H, int L, int d, int nclust, int iters, int W, float alpha,
                          void *out, int32_t *assign_out, ca_dtype_t dt, void *workspace,
                          size_t workspace_bytes, ca_path_t path, hipStream_t stream) {
     ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
@@ -84,19 +85,21 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED)
         return CA_ERR_INVALID_ARG;
     if (!Q || !K || !V || !out) return CA_ERR_INVALID_ARG;
+    if (G < 1 || H % G != 0) return CA_ERR_INVALID_ARG;
     const long S = (long)B * H;
     const size_t tbytes = (size_t)S * L * d * elem_bytes(dt);
+    const size_t kvbytes = tbytes / (size_t)G;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
         return CA_ERR_INVALID_ARG;
     if (assign_out && !aligned(assign_out, 4)) return CA_ERR_INVALID_ARG;
-    if (overlap(out, tbytes, Q, tbytes) || overlap(out, tbytes, K, tbytes) ||
-        overlap(out, tbytes, V, tbytes))
+    if (overlap(out, tbytes, Q, tbytes) || overlap(out, tbytes, K, kvbytes) ||
+        overlap(out, tbytes, V, kvbytes))
         return CA_ERR_INVALID_ARG;
     const size_t abytes = sizeof(int32_t) * (size_t)S * L;
     if (assign_out && (overlap(assign_out, abytes, out, tbytes) ||
                        overlap(assign_out, abytes, Q, tbytes) ||
-                       overlap(assign_out, abytes, K, tbytes) ||
-                       overlap(assign_out, abytes, V, tbytes)))
+                       overlap(assign_out, abytes, K, kvbytes) ||
+                       overlap(assign_out, abytes, V, kvbytes)))
         return CA_ERR_INVALID_ARG;
     const size_t vbytes = (size_t)B * L;
     if (valid && (overlap(valid, vbytes, out, tbytes) ||
@@ -107,14 +110,14 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
 
     if (use_fused(path, L, Kc)) {
         return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, W, alpha, dt, valid,
-                                               H, out, assign_out, stream));
+                                               H, G, out, assign_out, stream));
     }
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;
     char *ws = static_cast<char *>(workspace);
     if (overlap(ws, lay.total, out, tbytes) || overlap(ws, lay.total, Q, tbytes) ||
-        overlap(ws, lay.total, K, tbytes) || overlap(ws, lay.total, V, tbytes) ||
+        overlap(ws, lay.total, K, kvbytes) || overlap(ws, lay.total, V, kvbytes) ||
         (assign_out && overlap(ws, lay.total, assign_out, abytes)) ||
         (valid && overlap(ws, lay.total, valid, vbytes)))
         return CA_ERR_INVALID_ARG;
@@ -130,8 +133,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
                                     stream));
         CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream));
     }
-    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, vcent, xpart, stream));
-    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, valid, H, out,
+    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
+                                 stream));
+    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, valid, H, G, out,
                                nullptr, stream));
     return CA_OK;
 }
@@ -222,8 +226,8 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V, in
                                  int d, int nclust, int iters, int W, float alpha, void *out,
                                  int32_t *assign_out, ca_dtype_t dt, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-    return forward_impl(Q, K, V, nullptr, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
-                        dt, workspace, workspace_bytes, CA_PATH_AUTO, stream);
+    return forward_impl(Q, K, V, nullptr, 1, B, H, L, d, nclust, iters, W, alpha, out,
+                        assign_out, dt, workspace, workspace_bytes, CA_PATH_AUTO, stream);
 }
 
 ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V, int B, int H,
@@ -231,8 +235,8 @@ ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     void *out, int32_t *assign_out, ca_dtype_t dt,
                                     void *workspace, size_t workspace_bytes, ca_path_t path,
                                     hipStream_t stream) {
-    return forward_impl(Q, K, V, nullptr, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
-                        dt, workspace, workspace_bytes, path, stream);
+    return forward_impl(Q, K, V, nullptr, 1, B, H, L, d, nclust, iters, W, alpha, out,
+                        assign_out, dt, workspace, workspace_bytes, path, stream);
 }
 
 ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void *V,
@@ -242,8 +246,27 @@ ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void
                                         size_t workspace_bytes, ca_path_t path,
                                         hipStream_t stream) {
     if (!valid) return CA_ERR_INVALID_ARG;
-    return forward_impl(Q, K, V, valid, B, H, L, d, nclust, iters, W, alpha, out, assign_out, dt,
-                        workspace, workspace_bytes, path, stream);
+    return forward_impl(Q, K, V, valid, 1, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
+                        dt, workspace, workspace_bytes, path, stream);
+}
+
+ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *V, int B, int H,
+                                      int L, int d, int nclust, int iters, int W, float alpha,
+                                      const ca_options_t *opts, void *out, int32_t *assign_out,
+                                      ca_dtype_t dt, void *workspace, size_t workspace_bytes,
+                                      ca_path_t path, hipStream_t stream) {
+    const uint8_t *valid = opts ? opts->valid : nullptr;
+    int G = 1;
+    if (opts) {
+        if (opts->flags != 0) return CA_ERR_UNSUPPORTED;
+        if (opts->kv_heads < 0) return CA_ERR_INVALID_ARG;
+        if (opts->kv_heads > 0) {
+            if (H < 1 || opts->kv_heads > H || H % opts->kv_heads != 0) return CA_ERR_INVALID_ARG;
+            G = H / opts->kv_heads;
+        }
+    }
+    return forward_impl(Q, K, V, valid, G, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
+                        dt, workspace, workspace_bytes, path, stream);
 }
 
 ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d, int Kc,
@@ -299,7 +322,7 @@ ca_status_t ca_centroid_xattn(const float *mu, const void *K, const void *V, int
     const size_t need = ca_centroid_xattn_workspace_size(S, L, d, Kc);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kAlign)))
         return CA_ERR_INVALID_ARG;
-    return hip_status(launch_centroid_xattn(mu, K, V, S, L, Kc, dt, nullptr, 1, vcent,
+    return hip_status(launch_centroid_xattn(mu, K, V, S, L, Kc, dt, nullptr, 1, 1, vcent,
                                             static_cast<float *>(workspace), stream));
 }
 
@@ -311,7 +334,7 @@ ca_status_t ca_local_window_attn(const void *Q, const void *K, const void *V, in
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(oloc, 16))
         return CA_ERR_INVALID_ARG;
     return hip_status(launch_local_window(Q, K, V, S, L, W, dt, nullptr, nullptr, 1, 1.f, nullptr,
-                                          1, nullptr, oloc, stream));
+                                          1, 1, nullptr, oloc, stream));
 }
 
 ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
@@ -373,8 +396,8 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq, const void
     const uint16_t *wqkv[3] = {wt[0], wt[1], wt[2]};
     CA_TRY(launch_gemm_nt(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
                           false, true, L, H, stream));
-    st = forward_impl(heads[0], heads[1], heads[2], nullptr, B, H, L, d, nclust, iters, W, alpha,
-                      O, assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO,
+    st = forward_impl(heads[0], heads[1], heads[2], nullptr, 1, B, H, L, d, nclust, iters, W,
+                      alpha, O, assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO,
                       stream);
     if (st != CA_OK) return st;
     const uint16_t *wo[1] = {wt[3]};

@@ -12,6 +12,12 @@ constexpr int kD = 64;          // head dimension supported by the kernels
 constexpr int kMaxClusters = 256;
 constexpr int kWave = 64;
 
+// Grouped K/V heads: query slice s = b * H + h reads K and V of slice
+// b * (H / G) + h / G, G query heads sharing one K/V head (G = 1: its own).
+__host__ __device__ __forceinline__ long kv_slice(long s, int H, int G) {
+    return G == 1 ? s : (s / H) * (H / G) + (s % H) / G;
+}
+
 // bf16 storage is carried as raw uint16 bit patterns.
 struct bf16_t {
     uint16_t bits;
@@ -107,15 +113,15 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
 
 int xattn_splits(int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
-// belongs to batch row s / H.
+// belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H,
+                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
                                  float *vcent, float *partials, hipStream_t st);
 
 hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
-                               float alpha, const uint8_t *valid, int H, void *out, float *oloc,
-                               hipStream_t st);
+                               float alpha, const uint8_t *valid, int H, int G, void *out,
+                               float *oloc, hipStream_t st);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);
@@ -123,7 +129,7 @@ hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const f
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
-                                int H, void *out, int32_t *assign, hipStream_t st);
+                                int H, int G, void *out, int32_t *assign, hipStream_t st);
 
 // C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
 // A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as

@@ -480,7 +480,7 @@ struct InitMask {
 template <typename T, bool FULL, bool NARROW, bool MASKED>
 __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
-    int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H,
+    int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H, int G,
     T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init) {
     __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
@@ -502,6 +502,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;
     const long base = slice * (long)L * kD;
+    const long kvbase = kv_slice(slice, H, G) * (long)L * kD;   // K and V (grouped heads)
     const LaneOffs lo = lane_offsets(l16, g);
     const u8 *pK = smem + kOffK, *pQV = smem + kOffQV, *pMu = smem + kOffMu, *pOH = smem + kOffOH,
              *pP = smem + kOffP, *pMuX = smem + kOffMuX;
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n;
-        load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
+        load_row8<T, FULL>(Kx + kvbase, it >> 3, L, (it & 7) * 8, kraw[n]);
     }
     const int tv = iters >= 3 ? 3 : iters;   // iteration that requests V
 
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int it = tid + kThreads * n;
-                load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
+                load_row8<T, FULL>(Vx + kvbase, it >> 3, L, (it & 7) * 8, vraw[n]);
             }
         }
         if (FULL || w < NT) {
@@ -910,7 +911,7 @@ bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc
 template <typename T, bool FULL, bool NARROW, bool MASKED>
 static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                  int iters, int radius, float alpha, const uint8_t *valid, int H,
-                                 void *out, int32_t *assign, hipStream_t st) {
+                                 int G, void *out, int32_t *assign, hipStream_t st) {
     auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED>;
     InitMask init{};
     for (int k = 0; k < Kc; ++k) {
@@ -919,7 +920,7 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), 0, st,
                        static_cast<const T *>(Q), static_cast<const T *>(K),
-                       static_cast<const T *>(V), S, L, Kc, iters, radius, alpha, valid, H,
+                       static_cast<const T *>(V), S, L, Kc, iters, radius, alpha, valid, H, G,
                        static_cast<T *>(out), assign, init);
     return hipGetLastError();
 }
@@ -927,40 +928,41 @@ static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, in
 template <typename T, bool MASKED>
 static hipError_t fused_launch_m(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                  int iters, int W, float alpha, const uint8_t *valid, int H,
-                                 void *out, int32_t *assign, hipStream_t st) {
+                                 int G, void *out, int32_t *assign, hipStream_t st) {
     const int radius = W / 2;
     const bool full = L == kFL;
     const bool narrow = radius <= 16;
     if (full && narrow)
         return fused_launch_t<T, true, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
-                                                     H, out, assign, st);
+                                                     H, G, out, assign, st);
     if (full)
         return fused_launch_t<T, true, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
-                                                      valid, H, out, assign, st);
+                                                      valid, H, G, out, assign, st);
     if (narrow)
         return fused_launch_t<T, false, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
-                                                      valid, H, out, assign, st);
+                                                      valid, H, G, out, assign, st);
     return fused_launch_t<T, false, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
-                                                   H, out, assign, st);
+                                                   H, G, out, assign, st);
 }
 
 template <typename T>
 static hipError_t fused_launch(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                int iters, int W, float alpha, const uint8_t *valid, int H,
-                               void *out, int32_t *assign, hipStream_t st) {
+                               int G, void *out, int32_t *assign, hipStream_t st) {
     if (valid)
-        return fused_launch_m<T, true>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign,
-                                       st);
-    return fused_launch_m<T, false>(Q, K, V, S, L, Kc, iters, W, alpha, nullptr, 1, out, assign,
-                                    st);
+        return fused_launch_m<T, true>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out,
+                                       assign, st);
+    return fused_launch_m<T, false>(Q, K, V, S, L, Kc, iters, W, alpha, nullptr, H, G, out,
+                                    assign, st);
 }
 
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
-                                int H, void *out, int32_t *assign, hipStream_t st) {
+                                int H, int G, void *out, int32_t *assign, hipStream_t st) {
     if (dt == CA_BF16)
-        return fused_launch<bf16_t>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign, st);
-    return fused_launch<float>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, out, assign, st);
+        return fused_launch<bf16_t>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out, assign,
+                                    st);
+    return fused_launch<float>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out, assign, st);
 }
 
 }  // namespace ca

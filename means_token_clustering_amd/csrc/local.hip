@@ -31,7 +31,7 @@ template <typename T, bool FUSE>
 __global__ __launch_bounds__(256) void local_window_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int r,
     int ntile, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
-    float alpha, const uint8_t *__restrict__ valid, int H, T *__restrict__ out,
+    float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out,
     float *__restrict__ oloc) {
     __shared__ float sm_k[kLTile * kLPad];
     __shared__ float sm_v[kLTile * kLPad];
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
     const int tile = blockIdx.x % ntile;
     const long s = blockIdx.x / ntile;
     const long base = s * (long)L * kD;
+    const long kvbase = kv_slice(s, H, G) * (long)L * kD;
     const int i0 = tile * kQTile;
     const int nq = min(kQTile, L - i0);
     const int qi = tid >> 2, g = tid & 3;
@@ -76,8 +77,8 @@ __global__ __launch_bounds__(256) void local_window_kernel(
         __syncthreads();
         for (int e = tid; e < nk * (kD / 4); e += 256) {
             const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
-            float4 kv = load4<T>(Kx + base + (long)(jt + rr) * kD + c4);
-            float4 vv = load4<T>(Vx + base + (long)(jt + rr) * kD + c4);
+            float4 kv = load4<T>(Kx + kvbase + (long)(jt + rr) * kD + c4);
+            float4 vv = load4<T>(Vx + kvbase + (long)(jt + rr) * kD + c4);
             float *dk = sm_k + rr * kLPad + c4;
             float *dv = sm_v + rr * kLPad + c4;
             dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(256) void gather_fuse_kernel(const float *__restric
 template <typename T>
 static hipError_t local_dispatch(const void *Q, const void *K, const void *V, int S, int L, int W,
                                  const float *vcent, const int32_t *assign, int Kc, float alpha,
-                                 const uint8_t *valid, int H, void *out, float *oloc,
+                                 const uint8_t *valid, int H, int G, void *out, float *oloc,
                                  hipStream_t st) {
     const int ntile = (L + kQTile - 1) / kQTile;
     const int r = W / 2;
@@ -190,23 +191,23 @@ static hipError_t local_dispatch(const void *Q, const void *K, const void *V, in
     const T *v = static_cast<const T *>(V);
     if (oloc == nullptr)
         hipLaunchKernelGGL((local_window_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, ntile,
-                           vcent, assign, Kc, alpha, valid, H, static_cast<T *>(out), oloc);
+                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), oloc);
     else
         hipLaunchKernelGGL((local_window_kernel<T, false>), grid, block, 0, st, q, k, v, L, r,
-                           ntile, vcent, assign, Kc, alpha, valid, H, static_cast<T *>(out),
+                           ntile, vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out),
                            oloc);
     return hipGetLastError();
 }
 
 hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
-                               float alpha, const uint8_t *valid, int H, void *out, float *oloc,
-                               hipStream_t st) {
+                               float alpha, const uint8_t *valid, int H, int G, void *out,
+                               float *oloc, hipStream_t st) {
     if (dt == CA_BF16)
-        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, out,
-                                      oloc, st);
-    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, out, oloc,
-                                 st);
+        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, G,
+                                      out, oloc, st);
+    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, G, out,
+                                 oloc, st);
 }
 
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,

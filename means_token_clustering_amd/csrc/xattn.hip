@@ -39,7 +39,7 @@ static int keys_per_split(int L, int nsplit) {
 template <typename T>
 __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     const float *__restrict__ mu, const T *__restrict__ Kx, const T *__restrict__ Vx, int L,
-    int Kc, int nsplit, int kps, const uint8_t *__restrict__ valid, int H,
+    int Kc, int nsplit, int kps, const uint8_t *__restrict__ valid, int H, int G,
     float *__restrict__ vcent, float *__restrict__ part) {
     __shared__ float sm_k[kKeyTile * kXPad];
     __shared__ float sm_v[kKeyTile * kXPad];
@@ -52,8 +52,9 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     const long s = blockIdx.x / nsplit;
     const int j0 = split * kps;
     const int j1 = min(L, j0 + kps);
-    const T *Ks = Kx + s * (long)L * kD;
-    const T *Vs = Vx + s * (long)L * kD;
+    const long skv = kv_slice(s, H, G);
+    const T *Ks = Kx + skv * (long)L * kD;
+    const T *Vs = Vx + skv * (long)L * kD;
     const int cl = tid >> 4, t = tid & 15;
     const float scale = 1.0f / sqrtf((float)kD);
 
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restr
 
 template <typename T>
 static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, const uint8_t *valid, int H, float *vcent,
+                                 int Kc, const uint8_t *valid, int H, int G, float *vcent,
                                  float *partials, hipStream_t st) {
     const int nsplit = xattn_splits(L);
     const int kps = keys_per_split(L, nsplit);
@@ -174,7 +175,7 @@ static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, 
     const dim3 grid((unsigned)((long)S * used)), block(256);
     hipLaunchKernelGGL(centroid_xattn_kernel<T>, grid, block, 0, st, mu,
                        static_cast<const T *>(K), static_cast<const T *>(V), L, Kc, used, kps,
-                       valid, H, vcent, partials);
+                       valid, H, G, vcent, partials);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || used == 1) return err;
     const long total = (long)S * Kc * kD;
@@ -184,11 +185,11 @@ static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, 
 }
 
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H,
+                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
                                  float *vcent, float *partials, hipStream_t st) {
     if (dt == CA_BF16)
-        return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, vcent, partials, st);
-    return xattn_dispatch<float>(mu, K, V, S, L, Kc, valid, H, vcent, partials, st);
+        return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, st);
+    return xattn_dispatch<float>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, st);
 }
 
 }  // namespace ca

@@ -284,6 +284,15 @@ def round_bf16(x) -> np.ndarray:
     return x
 
 
+def repeat_kv(x, G: int) -> np.ndarray:
+    """Grouped K/V heads: [B, Hkv, L, d] -> [B, Hkv*G, L, d], query head h
+    reading K/V head h // G (the repeat_kv step of the ClusterAttention
+    listing on the "Hooshaai/svd-sst2-roberta-cluster" page, read as the
+    usual consecutive grouping)."""
+    x = _f64(x)
+    return np.ascontiguousarray(np.repeat(x, int(G), axis=1))
+
+
 def split_heads(x2d: np.ndarray, B: int, L: int, H: int, d: int) -> np.ndarray:
     """[B*L, H*d] -> [B, H, L, d]; head h is columns h*d .. h*d+d-1."""
     return np.ascontiguousarray(x2d.reshape(B, L, H, d).transpose(0, 2, 1, 3))

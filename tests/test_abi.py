@@ -173,3 +173,31 @@ def test_masked_forward_rejects(kw, code):
     """The masked entry point runs the same host checks, plus: a mask is
     required and must not overlap the outputs or the workspace."""
     assert fwd_masked(**kw) == code
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("valid", ctypes.c_void_p), ("kv_heads", ctypes.c_int), ("flags", ctypes.c_int)]
+
+
+def fwd_opts(opts, **kw):
+    a = dict(Q=Q, K=K, V=V, B=2, H=12, L=128, d=64, nclust=16, iters=3, W=32, alpha=0.5,
+             out=OUT, assign=ASG, dt=b.CA_F32, ws=WS, wsb=1 << 30, path=b.CA_PATH_STAGED)
+    a.update(kw)
+    return b.lib().cluster_attn_forward_opts(
+        a["Q"], a["K"], a["V"], a["B"], a["H"], a["L"], a["d"], a["nclust"], a["iters"], a["W"],
+        a["alpha"], ctypes.byref(opts) if opts is not None else None, a["out"], a["assign"],
+        a["dt"], a["ws"], a["wsb"], a["path"], None)
+
+
+@pytest.mark.parametrize("opts,kw,code", [
+    (_Opts(None, 5, 0), {}, INV),          # 12 heads do not split into 5 groups
+    (_Opts(None, 24, 0), {}, INV),         # more K/V heads than query heads
+    (_Opts(None, -1, 0), {}, INV),
+    (_Opts(None, 4, 1), {}, UNS),          # reserved flags
+    (_Opts(None, 4, 0), dict(Q=None), INV),
+    (_Opts(None, 4, 0), dict(out=K + 4096), INV),   # out overlaps the smaller K
+    (_Opts(MASK, 3, 0), dict(alpha=-1.0), INV),
+    (None, dict(ws=None), INV),
+])
+def test_opts_forward_rejects(opts, kw, code):
+    assert fwd_opts(opts, **kw) == code

@@ -299,3 +299,43 @@ def test_masked_all_real_equals_unmasked(path):
     torch.cuda.synchronize()
     assert torch.equal(c1, c0)
     assert torch.equal(o1, o0)
+
+
+# ---------------------------------------------------------------- grouped K/V heads
+GQA = [  # B, H, Hkv, L, W, dtype, mask kind (None: no mask)
+    (2, 12, 4, 128, 32, gen.F32, None),
+    (2, 12, 1, 128, 32, gen.F32, "prefix"),
+    (2, 6, 3, 100, 70, gen.BF16, None),
+    (1, 4, 2, 300, 32, gen.F32, "holes"),
+]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", GQA)
+def test_grouped_kv_heads(case, path):
+    """K and V with Hkv < H heads: query head h reads K/V head h // (H / Hkv);
+    the oracle runs on K and V repeated to H heads."""
+    b = _b()
+    B, H, Hkv, L, W, dtype, kind = case
+    G = H // Hkv
+    x = gen.make_inputs(B, H, L, 64, nclust=16, iters=3, W=W, alpha=0.4, dtype=dtype,
+                        seed=900 + H + Hkv + L, blobs=8)
+    kv = gen.make_inputs(B, Hkv, L, 64, dtype=dtype, seed=901 + L)
+    mask = gen.make_mask(B, L, seed=L, kind=kind) if kind else None
+    _say(f"[gqa] B={B} H={H} Hkv={Hkv} L={L} W={W} {dtype} mask={kind} path={path}")
+    q = _dev(x.q, dtype)
+    k, v = _dev(kv.k, dtype), _dev(kv.v, dtype)
+    vd = torch.from_numpy(mask).cuda() if mask is not None else None
+    assigns, out = [], None
+    for t in range(1, 4):
+        o, c = b.cluster_attn_forward(q, k, v, 16, t, W, 0.4, path=path, valid=vd)
+        assigns.append(c.cpu().numpy())
+        out = o
+    torch.cuda.synchronize()
+    kr, vr = oracle.repeat_kv(kv.values("k"), G), oracle.repeat_kv(kv.values("v"), G)
+    reports, err, tol, _ = parity.check_forward(x.values("q"), kr, vr, 16, 3, W, 0.4, dtype,
+                                                assigns, _host(out), valid=mask)
+    _say(f"  {parity.summarize(reports)}; max|out-ref|={err:.3e} (tol {tol})")
+    for r in reports:
+        assert r.bad == 0, parity.summarize(reports)
+    assert err <= tol

@@ -463,3 +463,14 @@ def test_mask_fill_gives_uniform_weights_when_all_keys_padded():
     ol, _ = oracle.local_attn(q, k, v, 6, valid=m)
     assert np.allclose(ol[:, :, 12], v[:, :, 9:16].mean(axis=2), atol=1e-14)
     assert np.array_equal(ol[:, :, 0], oracle.local_attn(q[:, :, :1], k[:, :, :1], v[:, :, :1], 6)[0][:, :, 0])
+
+
+# ------------------------------------------------ P11: grouped K/V heads
+def test_repeat_kv_matches_library():
+    x = np.random.default_rng(3).standard_normal((2, 3, 5, 4))
+    for G in (1, 2, 4):
+        want = torch.from_numpy(x).repeat_interleave(G, dim=1).numpy()
+        assert np.array_equal(oracle.repeat_kv(x, G), want)
+    r = oracle.repeat_kv(x, 4)
+    for h in range(12):
+        assert np.array_equal(r[:, h], x[:, h // 4])
