@@ -60,16 +60,18 @@ def _load():
             "ora_num_clusters": (i, [i, i]),
             "ora_radius": (i, [i]),
             "ora_init_centroids": (None, [_dp, L, i, i, i, _dp]),
+            "ora_init_centroids_step": (None, [_dp, L, i, i, i, _dp]),
+            "ora_soft_gather": (None, [_dp, _dp, _dp, L, i, i, i, _dp]),
             "ora_assign": (None, [_dp, _dp, L, i, i, i, _ip, _dp, _dp, _dp]),
-            "ora_update": (None, [_dp, _ip, L, i, i, i, _dp, _ip]),
+            "ora_update": (None, [_dp, _ip, L, i, i, i, _dp, _dp, _ip]),
             "ora_objective": (None, [_dp, _dp, _ip, L, i, i, i, _dp]),
             "ora_centroid_xattn": (None, [_dp, _dp, _dp, L, i, i, i, _ip, _dp, _dp]),
             "ora_local_attn": (None, [_dp, _dp, _dp, L, i, i, i, _ip, _dp, _dp]),
-            "ora_fuse": (None, [_dp, _ip, _dp, L, i, i, i, d, _ip, _dp]),
-            "ora_forward": (i, [_dp, _dp, _dp, i, i, i, i, i, i, i, d, _ip, _dp, _ip,
+            "ora_fuse": (None, [_dp, _ip, _dp, L, i, i, i, d, _ip, _dp, _dp]),
+            "ora_forward": (i, [_dp, _dp, _dp, i, i, i, i, i, i, i, d, _ip, i, _dp, _ip,
                                 _dp, _ip, _dp, _dp, _dp, _dp, _dp, _dp]),
-            "ora_forward_from_assign": (None, [_dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip,
-                                               _dp, _dp, _dp, _dp]),
+            "ora_forward_from_assign": (None, [_dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip, i,
+                                               _dp, _dp, _dp, _dp, _dp]),
             "ora_matmul": (None, [_dp, _dp, L, L, L, _dp]),
             "ora_round_bf16": (d, [d]),
             "ora_round_bf16_array": (None, [_dp, L]),
@@ -142,10 +144,17 @@ def _slices(x: np.ndarray):
     return x, S, L, d
 
 
-def init_centroids(Q, K: int) -> np.ndarray:
+# listing-compatible variants (flags of forward), see oracle.c
+INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND = 1, 2, 4, 8
+LISTING = INIT_STEP | KEEP_EMPTY | SOFT_GATHER | BAND
+
+
+def init_centroids(Q, K: int, step: bool = False) -> np.ndarray:
+    """mu^(0) = Q[floor(k L / K)], or Q[k * max(1, L // K)] with step=True."""
     Q, S, L, d = _slices(Q)
     mu = np.empty(Q.shape[:-2] + (K, d))
-    _load().ora_init_centroids(_p(Q), S, L, d, K, _p(mu))
+    fn = _load().ora_init_centroids_step if step else _load().ora_init_centroids
+    fn(_p(Q), S, L, d, K, _p(mu))
     return mu
 
 
@@ -162,14 +171,25 @@ def assign(Q, mu):
     return c, dbest, gap, qn2
 
 
-def update(Q, c, K: int):
-    """Returns (mu, counts) for one update step from assignment c."""
+def update(Q, c, K: int, prev=None):
+    """Returns (mu, counts) for one update step from assignment c; with prev
+    (the previous centroids) an empty cluster keeps its previous centroid."""
     Q, S, L, d = _slices(Q)
     c = _i32(c)
+    pv = _f64(prev) if prev is not None else None
     mu = np.empty(Q.shape[:-2] + (K, d))
     counts = np.empty(Q.shape[:-2] + (K,), np.int32)
-    _load().ora_update(_p(Q), _p(c), S, L, d, K, _p(mu), _p(counts))
+    _load().ora_update(_p(Q), _p(c), S, L, d, K, _p(pv), _p(mu), _p(counts))
     return mu, counts
+
+
+def soft_gather(Q, mu, vcent) -> np.ndarray:
+    """G_i = sum_k softmax_k(q_i . mu_k / sqrt(d)) vcent_k."""
+    Q, S, L, d = _slices(Q)
+    mu, vcent = _f64(mu), _f64(vcent)
+    G = np.empty(Q.shape)
+    _load().ora_soft_gather(_p(Q), _p(mu), _p(vcent), S, L, d, mu.shape[-2], _p(G))
+    return G
 
 
 def objective(Q, mu, c) -> np.ndarray:
@@ -213,14 +233,15 @@ def fuse(vcent, c, oloc, alpha: float, valid=None) -> np.ndarray:
     vm = _mask(valid, oloc.shape[:-2], L)
     out = np.empty(oloc.shape)
     _load().ora_fuse(_p(vcent), _p(c), _p(oloc), S, L, d, vcent.shape[-2],
-                     float(alpha), _p(vm), _p(out))
+                     float(alpha), _p(vm), None, _p(out))
     return out
 
 
 def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
-            trace: bool = True, valid=None) -> Dict[str, np.ndarray]:
+            trace: bool = True, valid=None, flags: int = 0) -> Dict[str, np.ndarray]:
     """Whole forward pass; Q, K, V are float64 [B, H, L, d]; valid: optional
-    key-padding mask [B, L] or [B, H, L] (nonzero = real token)."""
+    key-padding mask [B, L] or [B, H, L] (nonzero = real token); flags:
+    listing-compatible variants (INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND)."""
     Q, Kt, V = _f64(Q), _f64(Kt), _f64(V)
     B, H, L, d = Q.shape
     S = B * H
@@ -242,7 +263,7 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
         )
     g = res.get
     rc = _load().ora_forward(
-        _p(Q), _p(Kt), _p(V), B, H, L, d, nclust, iters, W, float(alpha), _p(vm),
+        _p(Q), _p(Kt), _p(V), B, H, L, d, nclust, iters, W, float(alpha), _p(vm), int(flags),
         _p(out), _p(c), _p(g("mu_hist")), _p(g("c_hist")), _p(g("gap_hist")),
         _p(g("J")), _p(g("Jp")), _p(g("qn2")), _p(g("vcent")), _p(g("oloc")))
     if rc < 0:
@@ -252,10 +273,13 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
     return res
 
 
-def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None):
-    """Steps after clustering from a given final assignment c (e.g. the GPU's)."""
+def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None,
+                        flags: int = 0, mu=None):
+    """Steps after clustering from a given final assignment c (e.g. the GPU's);
+    mu: the final centroids (default: the update of c)."""
     Q, S, L, d = _slices(Q)
     vm = _mask(valid, Q.shape[:-2], L)
+    mu_in = _f64(mu) if mu is not None else None
     Kt, V, c = _f64(Kt), _f64(V), _i32(c)
     if c.size and (c.min() < 0 or c.max() >= K):
         raise ValueError("assignment out of range")
@@ -264,7 +288,8 @@ def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None):
     vc = np.empty(Q.shape[:-2] + (K, d))
     ol = np.empty(Q.shape)
     _load().ora_forward_from_assign(_p(Q), _p(Kt), _p(V), S, L, d, K, _p(c), W,
-                                    float(alpha), _p(vm), _p(out), _p(mu), _p(vc), _p(ol))
+                                    float(alpha), _p(vm), int(flags), _p(mu_in), _p(out),
+                                    _p(mu), _p(vc), _p(ol))
     return {"out": out, "mu": mu, "vcent": vc, "oloc": ol}
 
 

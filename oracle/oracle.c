@@ -29,6 +29,13 @@
  * runs over every token, padded ones included. A NULL mask means every token
  * is real. Layout [S, L] int32, slice-major like Q.
  *
+ * Listing-compatible variants (flags of ora_forward; the same
+ * ClusterAttention listing, its _kmeans_cluster and forward): 1 = initial
+ * centroids Q[k * max(1, L / K)]; 2 = an empty cluster keeps its previous
+ * centroid; 4 = soft gather, G_i = sum_k softmax_k(q_i . mu_k / sqrt(d))
+ * V^cent_k instead of V^cent_{c_i}; 8 = band |i - j| <= W (radius W), and no
+ * local branch at all (O = G) when W == 0 or W >= L.
+ *
  * Layout: each (b, h) pair is one "slice"; a slice of Q, K or V is a
  * contiguous [L, d] row-major block and slices follow in b-major, h-minor
  * order, i.e. the whole tensor is contiguous [B, H, L, d].
@@ -61,6 +68,10 @@ void ora_set_num_threads(int n) {
 #endif
 }
 
+void ora_local_attn_r(const double *Q, const double *Kt, const double *V, long S,
+                      int L, int d, int r, const int32_t *valid, double *oloc,
+                      double *psum);
+
 /* K = min(num_clusters, L)  ([CF] 2.1). */
 int ora_num_clusters(int nclust, int L) { return nclust < L ? nclust : L; }
 
@@ -73,6 +84,18 @@ void ora_init_centroids(const double *Q, long S, int L, int d, int K, double *mu
         for (int k = 0; k < K; ++k) {
             long row = ((long)k * (long)L) / (long)K;
             const double *src = Q + (s * L + row) * (long)d;
+            double *dst = mu + (s * K + k) * (long)d;
+            for (int j = 0; j < d; ++j) dst[j] = src[j];
+        }
+    }
+}
+
+/* Listing variant of the initialisation: mu_k^(0) = Q[k * max(1, floor(L / K))]. */
+void ora_init_centroids_step(const double *Q, long S, int L, int d, int K, double *mu) {
+    const long step = L / K > 1 ? L / K : 1;
+    for (long s = 0; s < S; ++s) {
+        for (int k = 0; k < K; ++k) {
+            const double *src = Q + (s * L + (long)k * step) * (long)d;
             double *dst = mu + (s * K + k) * (long)d;
             for (int j = 0; j < d; ++j) dst[j] = src[j];
         }
@@ -124,10 +147,11 @@ void ora_assign(const double *Q, const double *mu, long S, int L, int d, int K,
 /*
  * Update step ([MC] 1, [CF] 2.1): n_k = #{i : c_i = k};
  * mu_k = (sum over c_i = k of q_i) / max(1, n_k), so an empty cluster gets the
- * zero vector. counts may be NULL.
+ * zero vector; with prev (nullable, the listing's variant) an empty cluster
+ * keeps prev_k instead. counts may be NULL.
  */
 void ora_update(const double *Q, const int32_t *c, long S, int L, int d, int K,
-                double *mu, int32_t *counts) {
+                const double *prev, double *mu, int32_t *counts) {
 #pragma omp parallel for schedule(static)
     for (long s = 0; s < S; ++s) {
         double *sum = mu + s * K * (long)d;
@@ -142,6 +166,8 @@ void ora_update(const double *Q, const int32_t *c, long S, int L, int d, int K,
         for (int k = 0; k < K; ++k) {
             double den = n[k] > 1 ? (double)n[k] : 1.0;
             for (int j = 0; j < d; ++j) sum[(long)k * d + j] /= den;
+            if (prev && n[k] == 0)
+                for (int j = 0; j < d; ++j) sum[(long)k * d + j] = prev[(s * K + k) * (long)d + j];
             if (counts) counts[s * K + k] = n[k];
         }
         free(n);
@@ -217,8 +243,15 @@ void ora_centroid_xattn(const double *mu, const double *Kt, const double *V,
 void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
                     int L, int d, int W, const int32_t *valid, double *oloc,
                     double *psum) {
+    ora_local_attn_r(Q, Kt, V, S, L, d, ora_radius(W), valid, oloc, psum);
+}
+
+/* The same branch with the window given by its radius r (the listing's band
+ * |i - j| <= W is r = W). */
+void ora_local_attn_r(const double *Q, const double *Kt, const double *V, long S,
+                      int L, int d, int r, const int32_t *valid, double *oloc,
+                      double *psum) {
     const double scale = 1.0 / sqrt((double)d);
-    const int r = ora_radius(W);
 #pragma omp parallel for schedule(static)
     for (long s = 0; s < S; ++s) {
         double *e = (double *)malloc(sizeof(double) * (size_t)L);
@@ -257,13 +290,16 @@ void ora_local_attn(const double *Q, const double *Kt, const double *V, long S,
 /*
  * Gather and convex fusion ([MC] Architecture Overview item 2, [CF] 3):
  * O_i = (1 - alpha) V^cent_{c_i} + alpha O^loc_i; the row of a padded query
- * is zero (valid nullable).
+ * is zero (valid nullable). gdense (nullable, [S, L, d]) replaces the gathered
+ * V^cent_{c_i} (the listing's soft gather).
  */
 void ora_fuse(const double *vcent, const int32_t *c, const double *oloc, long S,
-              int L, int d, int K, double alpha, const int32_t *valid, double *out) {
+              int L, int d, int K, double alpha, const int32_t *valid, const double *gdense,
+              double *out) {
     for (long s = 0; s < S; ++s) {
         for (int i = 0; i < L; ++i) {
-            const double *g = vcent + (s * K + c[s * L + i]) * (long)d;
+            const double *g = gdense ? gdense + (s * L + i) * (long)d
+                                     : vcent + (s * K + c[s * L + i]) * (long)d;
             const double *l = oloc + (s * L + i) * (long)d;
             double *o = out + (s * L + i) * (long)d;
             const int keep = !valid || valid[s * L + i];
@@ -273,16 +309,82 @@ void ora_fuse(const double *vcent, const int32_t *c, const double *oloc, long S,
 }
 
 /*
+ * Soft gather of the listing's forward: G_i = sum_k softmax_k(q_i . mu_k /
+ * sqrt(d)) V^cent_k (max-subtracted softmax over the K centroids).
+ */
+void ora_soft_gather(const double *Q, const double *mu, const double *vcent, long S,
+                     int L, int d, int K, double *G) {
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double *e = (double *)malloc(sizeof(double) * (size_t)K);
+        for (int i = 0; i < L; ++i) {
+            const double *q = Q + (s * L + i) * (long)d;
+            double mx = -INFINITY;
+            for (int k = 0; k < K; ++k) {
+                const double *m = mu + (s * K + k) * (long)d;
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += q[t] * m[t];
+                e[k] = dot * scale;
+                if (e[k] > mx) mx = e[k];
+            }
+            double z = 0.0;
+            for (int k = 0; k < K; ++k) {
+                e[k] = exp(e[k] - mx);
+                z += e[k];
+            }
+            double *g = G + (s * L + i) * (long)d;
+            for (int t = 0; t < d; ++t) g[t] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                const double p = e[k] / z;
+                const double *vc = vcent + (s * K + k) * (long)d;
+                for (int t = 0; t < d; ++t) g[t] += p * vc[t];
+            }
+        }
+        free(e);
+    }
+}
+
+/* The steps after the clustering, from the final centroids mu and the final
+ * assignment c: centroid context, gather (hard, or soft with flag 4), local
+ * branch (radius floor(W/2), or the band of flag 8), fusion. */
+static void after_clustering(const double *Q, const double *Kt, const double *V, long S,
+                             int L, int d, int K, const int32_t *c, const double *mu, int W,
+                             double alpha, const int32_t *valid, int flags, double *out,
+                             double *vcent, double *oloc) {
+    double *G = NULL;
+    ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
+    if (flags & 4) {
+        G = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
+        ora_soft_gather(Q, mu, vcent, S, L, d, K, G);
+    }
+    if (flags & 8) {
+        /* the listing's band: radius W; no local branch when W == 0 or W >= L */
+        if (W > 0 && W < L) {
+            ora_local_attn_r(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
+        } else {
+            for (long e = 0; e < S * L * (long)d; ++e) oloc[e] = 0.0;
+            alpha = 0.0;
+        }
+    } else {
+        ora_local_attn(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
+    }
+    ora_fuse(vcent, c, oloc, S, L, d, K, alpha, valid, G, out);
+    free(G);
+}
+
+/*
  * Whole forward pass for one batch. K = min(nclust, L). Traces (all
  * nullable): mu_hist [(iters+1), S, K, d] (mu^(0..I)), c_hist [iters, S, L],
  * gap_hist [iters, S, L], J [iters, S] (objective after assignment t, i.e.
  * against mu^(t-1)), Jp [iters, S] (objective after update t), qn2 [S, L],
  * vcent [S, K, d], oloc [S, L, d]. valid: key-padding mask [S, L] or NULL.
- * Returns K, or -1 on invalid arguments.
+ * flags: listing-compatible variants (header). Returns K, or -1 on invalid
+ * arguments.
  */
 int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H,
                 int L, int d, int nclust, int iters, int W, double alpha,
-                const int32_t *valid,
+                const int32_t *valid, int flags,
                 double *out, int32_t *assign, double *mu_hist, int32_t *c_hist,
                 double *gap_hist, double *J, double *Jp, double *qn2,
                 double *vcent_out, double *oloc_out) {
@@ -297,7 +399,8 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
     double *oloc = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
     double *Js = (double *)malloc(sizeof(double) * (size_t)S);
 
-    ora_init_centroids(Q, S, L, d, K, mu);
+    if (flags & 1) ora_init_centroids_step(Q, S, L, d, K, mu);
+    else ora_init_centroids(Q, S, L, d, K, mu);
     if (mu_hist) memcpy(mu_hist, mu, sizeof(double) * (size_t)(S * K * d));
     for (int t = 1; t <= iters; ++t) {
         ora_assign(Q, mu, S, L, d, K, assign, NULL, gap, t == 1 ? qn2 : NULL);
@@ -307,7 +410,7 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
             ora_objective(Q, mu, assign, S, L, d, K, Js);
             memcpy(J + (long)(t - 1) * S, Js, sizeof(double) * (size_t)S);
         }
-        ora_update(Q, assign, S, L, d, K, mu_next, NULL);
+        ora_update(Q, assign, S, L, d, K, (flags & 2) ? mu : NULL, mu_next, NULL);
         double *tmp = mu;
         mu = mu_next;
         mu_next = tmp;
@@ -317,9 +420,7 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
             memcpy(Jp + (long)(t - 1) * S, Js, sizeof(double) * (size_t)S);
         }
     }
-    ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
-    ora_local_attn(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
-    ora_fuse(vcent, assign, oloc, S, L, d, K, alpha, valid, out);
+    after_clustering(Q, Kt, V, S, L, d, K, assign, mu, W, alpha, valid, flags, out, vcent, oloc);
     if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
     if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));
     free(mu); free(mu_next); free(gap); free(vcent); free(oloc); free(Js);
@@ -328,20 +429,21 @@ int ora_forward(const double *Q, const double *Kt, const double *V, int B, int H
 
 /*
  * The steps after clustering, from a given final assignment c (length S*L,
- * values in [0, K)): mu = update(c), V^cent from mu, local branch, fusion.
- * Used to check a GPU output against the GPU's own assignment.
+ * values in [0, K)): mu = update(c) (or mu_in when given: the final centroids,
+ * e.g. with flag 2 where they depend on earlier iterations), V^cent from mu,
+ * gather, local branch, fusion. Used to check a GPU output against the GPU's
+ * own assignment.
  */
 void ora_forward_from_assign(const double *Q, const double *Kt, const double *V,
                              long S, int L, int d, int K, const int32_t *c, int W,
-                             double alpha, const int32_t *valid, double *out, double *mu_out,
-                             double *vcent_out, double *oloc_out) {
+                             double alpha, const int32_t *valid, int flags, const double *mu_in,
+                             double *out, double *mu_out, double *vcent_out, double *oloc_out) {
     double *mu = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
     double *vcent = (double *)malloc(sizeof(double) * (size_t)(S * K * d));
     double *oloc = (double *)malloc(sizeof(double) * (size_t)(S * L * d));
-    ora_update(Q, c, S, L, d, K, mu, NULL);
-    ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
-    ora_local_attn(Q, Kt, V, S, L, d, W, valid, oloc, NULL);
-    ora_fuse(vcent, c, oloc, S, L, d, K, alpha, valid, out);
+    if (mu_in) memcpy(mu, mu_in, sizeof(double) * (size_t)(S * K * d));
+    else ora_update(Q, c, S, L, d, K, NULL, mu, NULL);
+    after_clustering(Q, Kt, V, S, L, d, K, c, mu, W, alpha, valid, flags, out, vcent, oloc);
     if (mu_out) memcpy(mu_out, mu, sizeof(double) * (size_t)(S * K * d));
     if (vcent_out) memcpy(vcent_out, vcent, sizeof(double) * (size_t)(S * K * d));
     if (oloc_out) memcpy(oloc_out, oloc, sizeof(double) * (size_t)(S * L * d));

@@ -474,3 +474,119 @@ def test_repeat_kv_matches_library():
     r = oracle.repeat_kv(x, 4)
     for h in range(12):
         assert np.array_equal(r[:, h], x[:, h // 4])
+
+
+# ------------------------------------- P12: listing-compatible variants
+# The ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster"
+# page: initial rows k * max(1, L // K), an empty cluster keeps its previous
+# centroid, soft gather over the final centroids, band |i - j| <= W and no
+# local branch when W == 0 or W >= L.
+def test_init_step_indices_golden():
+    for row in _rows(os.path.join(GOLDEN, "init_indices_step.txt")):
+        L, nclust = int(row[0]), int(row[1])
+        want = [int(x) for x in row[2:]]
+        K = oracle.num_clusters(nclust, L)
+        assert K == len(want)
+        Q = np.repeat(np.arange(L, dtype=np.float64)[:, None], 3, axis=1)[None]
+        assert oracle.init_centroids(Q, K, step=True)[0, :, 0].astype(int).tolist() == want
+        # the forward pass starts from these rows (its first trace entry)
+        r = oracle.forward(Q[None], Q[None], Q[None], nclust, 1, 2, 0.5, flags=oracle.INIT_STEP)
+        assert r["mu_hist"][0, 0, 0, :, 0].astype(int).tolist() == want
+
+
+def test_keep_empty_worked_example():
+    rows = _rows(os.path.join(GOLDEN, "keep_empty_L4.txt"))
+    q = np.array([float(x) for x in rows[0][1:]]).reshape(1, 1, 4, 1)
+    for rule, iters, m0, m1, *c in rows[1:]:
+        flags = oracle.INIT_STEP | (oracle.KEEP_EMPTY if rule == "keep" else 0)
+        r = oracle.forward(q, q, q, 2, int(iters), 2, 0.5, flags=flags)
+        assert r["mu"][0, 0, :, 0].tolist() == [float(m0), float(m1)], (rule, iters)
+        assert r["assign"][0, 0].tolist() == [int(x) for x in c], (rule, iters)
+    # update() alone: the empty cluster takes prev only when prev is given
+    c0 = np.zeros((1, 1, 4), np.int32)
+    prev = np.array([2.0, 2.0]).reshape(1, 1, 2, 1)
+    assert oracle.update(q, c0, 2)[0][0, 0, :, 0].tolist() == [4.25, 0.0]
+    assert oracle.update(q, c0, 2, prev=prev)[0][0, 0, :, 0].tolist() == [4.25, 2.0]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_keep_empty_objective_non_increasing(seed):
+    # duplicated rows make empty clusters common; Lloyd's objective still
+    # never rises when empty clusters keep their centroid
+    base = _randn(seed, 1, 2, 6, 3)
+    q = np.concatenate([base, base, base[:, :, :2]], axis=2)
+    r = oracle.forward(q, q, q, 5, 6, 2, 0.5, flags=oracle.KEEP_EMPTY | oracle.INIT_STEP)
+    J, Jp = r["J"], r["Jp"]
+    assert np.all(Jp <= J + 1e-12)
+    assert np.all(J[1:] <= Jp[:-1] + 1e-12)
+
+
+def test_soft_gather_matches_library_attention():
+    x = gen.make_inputs(2, 3, 40, 8, nclust=6, seed=31, blobs=4)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    mu = _randn(4, 2, 3, 6, 8)
+    vc = _randn(5, 2, 3, 6, 8)
+    assert np.allclose(oracle.soft_gather(q, mu, vc), _sdpa(q, mu, vc), atol=1e-13)
+    # one centroid: every weight is 1
+    g1 = oracle.soft_gather(q, mu[:, :, :1], vc[:, :, :1])
+    assert np.array_equal(g1, np.broadcast_to(vc[:, :, :1], g1.shape))
+
+
+def test_listing_forward_uses_final_centroids():
+    """Soft gather and centroid context both come from the returned (final)
+    centroids; the output is the convex mix of the library's attention
+    products with the local branch."""
+    x = gen.make_inputs(2, 2, 48, 8, nclust=6, seed=32, blobs=5)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    r = oracle.forward(q, k, v, 6, 3, 5, 0.3, flags=oracle.LISTING)
+    mu = r["mu"]
+    assert np.allclose(r["vcent"], _sdpa(mu, k, v), atol=1e-13)
+    g = _sdpa(q, mu, r["vcent"])
+    ol, _ = oracle.local_attn(q, k, v, 10)   # band radius 5 = window 10
+    assert np.array_equal(r["oloc"], ol)
+    assert np.allclose(r["out"], 0.7 * g + 0.3 * ol, atol=1e-13)
+    f = oracle.forward_from_assign(q, k, v, r["assign"], 6, 5, 0.3, flags=oracle.LISTING, mu=mu)
+    assert np.array_equal(f["out"], r["out"])
+
+
+@pytest.mark.parametrize("W", [0, 48, 60])
+def test_band_skip_gives_gather_exactly(W):
+    x = gen.make_inputs(1, 2, 48, 8, nclust=5, seed=33, blobs=4)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    r = oracle.forward(q, k, v, 5, 3, W, 0.4, flags=oracle.BAND)
+    hard = np.take_along_axis(r["vcent"], r["assign"][..., None].astype(np.int64), axis=2)
+    assert np.array_equal(r["out"], hard)
+    r = oracle.forward(q, k, v, 5, 3, W, 0.4, flags=oracle.BAND | oracle.SOFT_GATHER)
+    assert np.array_equal(r["out"], oracle.soft_gather(q, r["mu"], r["vcent"]))
+
+
+@pytest.mark.parametrize("W", [1, 7, 47])
+def test_band_is_window_of_twice_the_radius(W):
+    x = gen.make_inputs(1, 2, 48, 8, nclust=5, seed=34, blobs=4)
+    args = (x.values("q"), x.values("k"), x.values("v"), 5, 3)
+    a = oracle.forward(*args, W, 0.4, flags=oracle.BAND)
+    b = oracle.forward(*args, 2 * W, 0.4)
+    assert np.array_equal(a["out"], b["out"])
+
+
+def test_listing_with_k_equal_L_is_dense():
+    """K = L: the listing's initial rows are every row, no cluster is empty
+    and each token is its own centroid, so V^cent is dense attention and
+    the soft gather is attention of the queries over themselves."""
+    x = gen.make_inputs(1, 2, 24, 8, nclust=24, seed=35)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    r = oracle.forward(q, k, v, 24, 2, 0, 0.5, flags=oracle.LISTING)
+    assert np.array_equal(r["mu"], q)
+    dense = _sdpa(q, k, v)
+    assert np.allclose(r["vcent"], dense, atol=1e-13)
+    assert np.allclose(r["out"], _sdpa(q, q, dense), atol=1e-13)
+
+
+def test_listing_mask_padded_rows_zero():
+    x = gen.make_inputs(2, 2, 40, 8, nclust=5, seed=36, blobs=4)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    m = _prefix_mask(2, 40, [25, 40])
+    r = oracle.forward(q, k, v, 5, 3, 6, 0.3, valid=m, flags=oracle.LISTING)
+    assert np.all(r["out"][0, :, 25:] == 0.0)
+    r0 = oracle.forward(q, k, v, 5, 3, 6, 0.3, flags=oracle.LISTING)
+    assert np.array_equal(r0["mu"], r["mu"])
