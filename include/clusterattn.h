@@ -142,13 +142,35 @@ ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void
  *             heads h = G*j .. G*j+G-1 share K/V head j (grouped-query
  *             attention, the listing's repeat_kv on the "Hooshaai/svd-sst2-
  *             roberta-cluster" page; K and V are then [B, kv_heads, L, d]).
- *   flags     must be 0 (CA_ERR_UNSUPPORTED otherwise); reserved.
+ *   flags     OR of CA_FLAG_* below, each a rule of the ClusterAttention
+ *             listing on the "Hooshaai/svd-sst2-roberta-cluster" page where it
+ *             departs from the model card's equations (0 = the equations);
+ *             another bit is CA_ERR_INVALID_ARG.
  */
 typedef struct {
     const uint8_t *valid;
     int kv_heads;
     int flags;
 } ca_options_t;
+
+/* Initial centroids mu_k = Q[k * max(1, floor(L / K))] (the listing's k-means
+ * routine) instead of Q[floor(k L / K)]. */
+#define CA_FLAG_INIT_STEP 1
+/* An empty cluster keeps its previous centroid (the listing's update) instead
+ * of becoming the zero vector. */
+#define CA_FLAG_KEEP_EMPTY 2
+/* Soft gather (the listing's forward): token i takes sum_k softmax_k(q_i .
+ * mu_k / sqrt(d)) V^cent_k over the final centroids instead of V^cent_{c_i}
+ * (the key-padding mask does not enter this softmax). assign_out still
+ * reports the last assignment. */
+#define CA_FLAG_SOFT_GATHER 4
+/* Band of radius W (|i - j| <= W, the listing's local mask) instead of
+ * floor(W / 2); with W == 0 or W >= L there is no local branch and the
+ * output is the gathered context alone (alpha is then ignored). */
+#define CA_FLAG_BAND 8
+/* All four: the listing's forward (alpha is the weight itself; the listing's
+ * sigmoid of a parameter is the caller's to apply). */
+#define CA_FLAG_LISTING 15
 
 /*
  * cluster_attn_forward_ex with options (opts NULL = defaults, which is

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(HERE, "libclusterattn.so")
 CA_OK, CA_ERR_INVALID_ARG, CA_ERR_UNSUPPORTED, CA_ERR_HIP = 0, 1, 2, 3
 CA_F32, CA_BF16 = 0, 1
 CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED = 0, 1, 2
+# listing-compatible variants (ca_options_t.flags)
+CA_FLAG_INIT_STEP, CA_FLAG_KEEP_EMPTY, CA_FLAG_SOFT_GATHER, CA_FLAG_BAND = 1, 2, 4, 8
+CA_FLAG_LISTING = 15
 
 _lib = None
 _lock = threading.Lock()
@@ -154,14 +157,16 @@ def cluster_attn_workspace_size(B, H, L, d, nclust, dtype=CA_F32, path=CA_PATH_A
 
 def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float, out=None,
                          assign_out=None, path: int = CA_PATH_AUTO, workspace=None,
-                         stream=None, want_assign: bool = True, valid=None):
+                         stream=None, want_assign: bool = True, valid=None, flags: int = 0):
     """Q: contiguous [B, H, L, d] float32 or bfloat16 GPU tensor; K, V:
     [B, Hkv, L, d] of the same dtype, Hkv dividing H (Hkv < H: grouped K/V
     heads, cluster_attn_forward_opts).
 
     valid: optional key-padding mask, a contiguous [B, L] uint8 (or bool) GPU
-    tensor, nonzero = real token (cluster_attn_forward_masked). Returns (out,
-    assign_out); allocates out/assign_out/workspace with torch when not given.
+    tensor, nonzero = real token (cluster_attn_forward_masked). flags: OR of
+    CA_FLAG_* (listing-compatible variants, cluster_attn_forward_opts).
+    Returns (out, assign_out); allocates out/assign_out/workspace with torch
+    when not given.
     """
     torch = _torch()
     B, H, L, d = Q.shape
@@ -177,8 +182,8 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
         raise ValueError("K and V must be [B, Hkv, L, d] with Q's B, L and d")
     if valid is not None and (tuple(valid.shape) != (B, L) or valid.element_size() != 1):
         raise ValueError("valid must be a [B, L] tensor of one-byte elements")
-    if hkv != H:
-        opts = CaOptions(_ptr(valid), hkv, 0)
+    if hkv != H or flags:
+        opts = CaOptions(_ptr(valid), hkv, int(flags))
         st = lib().cluster_attn_forward_opts(
             _ptr(Q), _ptr(K), _ptr(V), B, H, L, d, nclust, iters, W, float(alpha),
             ctypes.byref(opts), _ptr(out), _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws),

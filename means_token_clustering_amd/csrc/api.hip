@@ -75,11 +75,12 @@ ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_H
     } while (0)
 
 // valid: key-padding mask [B, L] or nullptr (the unmasked operation); G:
-// query heads per K/V head (K and V are [B, H / G, L, d]).
+// query heads per K/V head (K and V are [B, H / G, L, d]); flags: CA_FLAG_*.
 ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint8_t *valid, int G,
-                         int B, int H, int L, int d, int nclust, int iters, int W, float alpha,
-                         void *out, int32_t *assign_out, ca_dtype_t dt, void *workspace,
-                         size_t workspace_bytes, ca_path_t path, hipStream_t stream) {
+                         int flags, int B, int H, int L, int d, int nclust, int iters, int W,
+                         float alpha, void *out, int32_t *assign_out, ca_dtype_t dt,
+                         void *workspace, size_t workspace_bytes, ca_path_t path,
+                         hipStream_t stream) {
     ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
     if (st != CA_OK) return st;
     if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED)
@@ -105,12 +106,27 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (valid && (overlap(valid, vbytes, out, tbytes) ||
                   (assign_out && overlap(valid, vbytes, assign_out, abytes))))
         return CA_ERR_INVALID_ARG;
+    if (flags & ~CA_FLAG_LISTING) return CA_ERR_INVALID_ARG;
     const int Kc = clusters(nclust, L);
     if (path == CA_PATH_FUSED && !fused_supported(L, Kc)) return CA_ERR_UNSUPPORTED;
+    Variant var{};
+    if (flags & CA_FLAG_INIT_STEP) var.init_step = L / Kc > 1 ? L / Kc : 1;
+    var.keep_empty = (flags & CA_FLAG_KEEP_EMPTY) != 0;
+    var.soft = (flags & CA_FLAG_SOFT_GATHER) != 0;
+    // window radius; the listing's band drops the local branch when W == 0 or
+    // W >= L (radius 0 with weight 0 leaves exactly the gathered context)
+    int radius = W / 2;
+    if (flags & CA_FLAG_BAND) {
+        radius = W;
+        if (W == 0 || W >= L) {
+            radius = 0;
+            alpha = 0.f;
+        }
+    }
 
     if (use_fused(path, L, Kc)) {
-        return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, W, alpha, dt, valid,
-                                               H, G, out, assign_out, stream));
+        return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var,
+                                               dt, valid, H, G, out, assign_out, stream));
     }
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
@@ -129,14 +145,17 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
     const int ntile = kmeans_tiles(L);
     for (int t = 1; t <= iters; ++t) {
+        // a kept empty cluster of the first update needs mu^(0) in place
         CA_TRY(launch_kmeans_assign(Q, t == 1 ? nullptr : mu, (int)S, L, Kc, dt, c, psum, pcnt,
-                                    stream));
-        CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream));
+                                    stream, var.init_step,
+                                    t == 1 && var.keep_empty ? mu : nullptr));
+        CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream,
+                                      var.keep_empty));
     }
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                  stream));
-    CA_TRY(launch_local_window(Q, K, V, (int)S, L, W, dt, vcent, c, Kc, alpha, valid, H, G, out,
-                               nullptr, stream));
+    CA_TRY(launch_local_window(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha, valid, H, G,
+                               out, nullptr, stream, var.soft ? mu : nullptr));
     return CA_OK;
 }
 
@@ -226,7 +245,7 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V, in
                                  int d, int nclust, int iters, int W, float alpha, void *out,
                                  int32_t *assign_out, ca_dtype_t dt, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
-    return forward_impl(Q, K, V, nullptr, 1, B, H, L, d, nclust, iters, W, alpha, out,
+    return forward_impl(Q, K, V, nullptr, 1, 0, B, H, L, d, nclust, iters, W, alpha, out,
                         assign_out, dt, workspace, workspace_bytes, CA_PATH_AUTO, stream);
 }
 
@@ -235,7 +254,7 @@ ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     void *out, int32_t *assign_out, ca_dtype_t dt,
                                     void *workspace, size_t workspace_bytes, ca_path_t path,
                                     hipStream_t stream) {
-    return forward_impl(Q, K, V, nullptr, 1, B, H, L, d, nclust, iters, W, alpha, out,
+    return forward_impl(Q, K, V, nullptr, 1, 0, B, H, L, d, nclust, iters, W, alpha, out,
                         assign_out, dt, workspace, workspace_bytes, path, stream);
 }
 
@@ -246,7 +265,7 @@ ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void
                                         size_t workspace_bytes, ca_path_t path,
                                         hipStream_t stream) {
     if (!valid) return CA_ERR_INVALID_ARG;
-    return forward_impl(Q, K, V, valid, 1, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
+    return forward_impl(Q, K, V, valid, 1, 0, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
                         dt, workspace, workspace_bytes, path, stream);
 }
 
@@ -256,17 +275,17 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
                                       ca_dtype_t dt, void *workspace, size_t workspace_bytes,
                                       ca_path_t path, hipStream_t stream) {
     const uint8_t *valid = opts ? opts->valid : nullptr;
+    const int flags = opts ? opts->flags : 0;
     int G = 1;
     if (opts) {
-        if (opts->flags != 0) return CA_ERR_UNSUPPORTED;
         if (opts->kv_heads < 0) return CA_ERR_INVALID_ARG;
         if (opts->kv_heads > 0) {
             if (H < 1 || opts->kv_heads > H || H % opts->kv_heads != 0) return CA_ERR_INVALID_ARG;
             G = H / opts->kv_heads;
         }
     }
-    return forward_impl(Q, K, V, valid, G, B, H, L, d, nclust, iters, W, alpha, out, assign_out,
-                        dt, workspace, workspace_bytes, path, stream);
+    return forward_impl(Q, K, V, valid, G, flags, B, H, L, d, nclust, iters, W, alpha, out,
+                        assign_out, dt, workspace, workspace_bytes, path, stream);
 }
 
 ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d, int Kc,
@@ -333,8 +352,8 @@ ca_status_t ca_local_window_attn(const void *Q, const void *K, const void *V, in
     if (W < 0 || !Q || !K || !V || !oloc) return CA_ERR_INVALID_ARG;
     if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(oloc, 16))
         return CA_ERR_INVALID_ARG;
-    return hip_status(launch_local_window(Q, K, V, S, L, W, dt, nullptr, nullptr, 1, 1.f, nullptr,
-                                          1, 1, nullptr, oloc, stream));
+    return hip_status(launch_local_window(Q, K, V, S, L, W / 2, dt, nullptr, nullptr, 1, 1.f,
+                                          nullptr, 1, 1, nullptr, oloc, stream));
 }
 
 ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
@@ -396,7 +415,7 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq, const void
     const uint16_t *wqkv[3] = {wt[0], wt[1], wt[2]};
     CA_TRY(launch_gemm_nt(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
                           false, true, L, H, stream));
-    st = forward_impl(heads[0], heads[1], heads[2], nullptr, 1, B, H, L, d, nclust, iters, W,
+    st = forward_impl(heads[0], heads[1], heads[2], nullptr, 1, 0, B, H, L, d, nclust, iters, W,
                       alpha, O, assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO,
                       stream);
     if (st != CA_OK) return st;

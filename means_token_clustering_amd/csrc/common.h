@@ -101,15 +101,34 @@ __device__ __forceinline__ float exp_f32(float x) {
 // C-ABI translation unit can call them.
 namespace ca {
 
+// Listing-compatible variants of the clustering and the gather (the
+// ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page,
+// its k-means routine and forward).
+struct Variant {
+    int init_step;     // 0: initial rows floor(k L / Kc); > 0: rows k * init_step
+    bool keep_empty;   // an empty cluster keeps its previous centroid (else zero)
+    bool soft;         // gather sum_k softmax_k(q . mu_k / sqrt(d)) V^cent_k
+};
+
+// Row of Q that initialises cluster k (increasing in k, below L for Kc <= L).
+__host__ __device__ inline int init_row(int k, int L, int Kc, int init_step) {
+    return init_step > 0 ? k * init_step : (int)(((long)k * L) / Kc);
+}
+
+// mu == nullptr: the centroids are the initial rows of Q (init_row with
+// init_step); mu_init, if not null, then receives them.
 hipError_t launch_kmeans_assign(const void *Q, const float *mu, int S, int L, int Kc,
                                 ca_dtype_t dt, int32_t *assign, float *part_sum,
-                                int32_t *part_cnt, hipStream_t st);
+                                int32_t *part_cnt, hipStream_t st, int init_step = 0,
+                                float *mu_init = nullptr);
 hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S, int L, int Kc,
                                     ca_dtype_t dt, float *part_sum, int32_t *part_cnt,
                                     hipStream_t st);
 int kmeans_tiles(int L);
+// keep_empty: an empty cluster leaves its row of mu as it was
 hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt, int nblk,
-                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st);
+                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st,
+                                  bool keep_empty = false);
 
 int xattn_splits(int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
@@ -118,18 +137,21 @@ hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, 
                                  int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
                                  float *vcent, float *partials, hipStream_t st);
 
-hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
+// Window |i - j| <= r. With oloc == nullptr the gather + fusion epilogue
+// writes out; mu != nullptr selects the soft gather over the centroids mu.
+hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int r,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
                                float alpha, const uint8_t *valid, int H, int G, void *out,
-                               float *oloc, hipStream_t st);
+                               float *oloc, hipStream_t st, const float *mu = nullptr);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);
 
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
-                                int H, int G, void *out, int32_t *assign, hipStream_t st);
+                                int iters, int radius, float alpha, const Variant &var,
+                                ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
+                                int32_t *assign, hipStream_t st);
 
 // C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
 // A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as

@@ -10,7 +10,9 @@
 // Architecture Overview figure and Mathematical Formulation 1; "ClusterFormer"
 // spec (svd-sst2-roberta-cluster page) 2.1 and 3. Conventions as in the
 // staged kernels: ties to the lowest cluster, empty cluster -> zero vector,
-// window |i - j| <= floor(W/2), scale 1/sqrt(d).
+// window |i - j| <= radius (floor(W/2) by default), scale 1/sqrt(d); the
+// listing-compatible variants (initial rows, kept empty clusters, soft
+// gather) are selected per launch.
 //
 // Arithmetic. Every contraction runs on the fp16 matrix cores
 // (v_mfma_f32_16x16x32_f16, fp32 accumulation). Each operand
@@ -54,6 +56,7 @@ namespace ca {
 namespace {
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -101,25 +104,44 @@ struct Sp4 {  // 4 values as two fp16 planes
 
 // x0, x1 -> packed fp16 pairs h and m with x = h + m + e: h rounded toward
 // zero, m = x - h (exact inside the mixed-precision fma) rounded to nearest
-// into the low / high half of m
+// into the low / high half of m.
+// MFMA = true: m feeds a matrix instruction at once. The compiler inserts
+// the wait states that a matrix read of a vector-ALU result needs only after
+// instructions it can see, not after asm, so the asm supplies them with a
+// trailing s_nop. split8 / split4 put it after their last pair, which covers
+// every part of the group.
+template <bool MFMA = false>
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m) {
     h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
     uint32_t r;
     asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x0));
-    asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(x1));
+    if (MFMA)
+        asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 3"
+            : "+v"(r) : "v"(h), "v"(x1));
+    else
+        asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+            : "+v"(r) : "v"(h), "v"(x1));
     m = r;
 }
+template <bool MFMA = false>
 __device__ __forceinline__ Sp8 split8(const float *x) {
     uint32_t h[4], m[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
+    for (int i = 0; i < 3; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
+    split2<MFMA>(x[6], x[7], h[3], m[3]);
     return Sp8{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{m[0], m[1], m[2], m[3]}};
 }
+template <bool MFMA = false>
 __device__ __forceinline__ Sp4 split4(float x0, float x1, float x2, float x3) {
     uint32_t h0, m0, h1, m1;
     split2(x0, x1, h0, m0);
-    split2(x2, x3, h1, m1);
+    split2<MFMA>(x2, x3, h1, m1);
     return Sp4{u32x2_t{h0, h1}, u32x2_t{m0, m1}};
+}
+
+// fp16 value i (0..3) of a packed pair of pairs, widened
+__device__ __forceinline__ float half_at(u32x2_t p, int i) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p[i >> 1] >> (16 * (i & 1))));
 }
 
 __device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -131,6 +153,17 @@ __device__ __forceinline__ f32x4_t mma3(const Sp8 &a, const Sp8 &b, f32x4_t c) {
     c = mma(a.m, b.h, c);
     c = mma(a.h, b.m, c);
     return mma(a.h, b.h, c);
+}
+// the same on 16-deep operands (v_mfma_f32_16x16x16_f16: lane l holds
+// A[l%16][4(l/16)+i] and B[4(l/16)+i][l%16], i = 0..3; D as for 16x16x32)
+__device__ __forceinline__ f32x4_t mma16(u32x2_t a, u32x2_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mma3_16(const Sp4 &a, const Sp4 &b, f32x4_t c) {
+    c = mma16(a.m, b.h, c);
+    c = mma16(a.h, b.m, c);
+    return mma16(a.h, b.h, c);
 }
 
 constexpr f32x4_t kZero4 = {0.f, 0.f, 0.f, 0.f};
@@ -373,9 +406,9 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
     for (int e = 1; e < 12; ++e) ls += s[e >> 2][e & 3];
     lsum = col_sum(ls);
     const float pa[8] = {s[0][0], s[0][1], s[0][2], s[0][3], s[1][0], s[1][1], s[1][2], s[1][3]};
-    const Sp8 pA = split8(pa);
+    const Sp8 pA = split8<true>(pa);
     const float pb[8] = {s[2][0], s[2][1], s[2][2], s[2][3], 0.f, 0.f, 0.f, 0.f};
-    const Sp8 pB = split8(pb);
+    const Sp8 pB = split8<true>(pb);
     // V^T rows 16kt + 4g .. +3 of columns 16j + l16 start at byte 2048 kt + (trv ^ 32j);
     // the zero-weight half of the second product reads a fourth tile (any
     // finite values do; a distinct tile avoids register copies)
@@ -456,7 +489,7 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
             s[i] = __builtin_amdgcn_exp2f(s[i] - Ms);
             ls += s[i];
         }
-        const Sp8 p = split8(s);
+        const Sp8 p = split8<true>(s);
         const int b0 = 2048 * kt + trv, b1 = two ? b0 + 2048 : b0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -467,9 +500,9 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
 
 }  // namespace
 
-// Tokens that start a cluster: bit t set iff t = floor(k L / Kc) for some
-// k < Kc (one bit per token, L <= 128). Token t then starts cluster
-// k = number of set bits below t.
+// Tokens that start a cluster: bit t set iff token t is the initial centroid
+// of some cluster k < Kc (one bit per token, L <= 128). The initial rows
+// increase with k, so token t starts cluster k = number of set bits below t.
 struct InitMask {
     uint32_t w[4];
 };
@@ -477,11 +510,16 @@ struct InitMask {
 // MASKED: valid is the key-padding mask [S / H, L] (nonzero = real token);
 // padded keys take the logit -10000 in both softmaxes, and the output rows of
 // padded queries are zero.
-template <typename T, bool FULL, bool NARROW, bool MASKED>
+// SOFT: the gathered context of token i is sum_k softmax_k(q_i . mu_k /
+// sqrt(d)) V^cent_k over the final centroids instead of V^cent_{c_i}.
+// keep_empty: an empty cluster keeps its previous centroid instead of
+// becoming the zero vector. (Both are the ClusterAttention listing's rules,
+// "Hooshaai/svd-sst2-roberta-cluster" page, k-means routine and forward.)
+template <typename T, bool FULL, bool NARROW, bool MASKED, bool SOFT>
 __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H, int G,
-    T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init) {
+    T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init, int keep_empty) {
     __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
@@ -682,17 +720,29 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 }
             }
             const float inv = __builtin_amdgcn_rcpf(fmaxf(cnt[0], 1.f));
+            const int o = off64(l16, 16 * w + 4 * g);
             float v[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) v[rr] = (sm[rr] + sh[rr]) * inv;
+            if (keep_empty && cnt[0] == 0.f) {   // empty: the stored centroid stays
+                const u32x2_t oh = *reinterpret_cast<const u32x2_t *>(sMu + o);
+                const u32x2_t om = *reinterpret_cast<const u32x2_t *>(sMu + kPlaneMuE + o);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v[rr] = half_at(oh, rr) + half_at(om, rr);
+            }
+            const Sp4 mu4 = split4(v[0], v[1], v[2], v[3]);
+            // With kept centroids the norm is taken of the stored vector
+            // itself, by this code only, so that a kept centroid and a fresh
+            // mean with the same stored value score every token alike (an
+            // exact tie then goes to the lower index, as it should).
             float n2p = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                v[rr] = (sm[rr] + sh[rr]) * inv;
-                n2p = fmaf(v[rr], v[rr], n2p);
+                const float x = keep_empty ? half_at(mu4.h, rr) + half_at(mu4.m, rr) : v[rr];
+                n2p = fmaf(x, x, n2p);
             }
-            const Sp4 mu4 = split4(v[0], v[1], v[2], v[3]);
             n2p = col_sum(n2p);   // over the 16 dims of tile w
             if (l16 < Kc) {
-                const int o = off64(l16, 16 * w + 4 * g);
                 st8(sMu + o, mu4.h);
                 st8(sMu + kPlaneMuE + o, mu4.m);
                 if (g == 0) {
@@ -721,6 +771,31 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         sk = scale_shift(mk, kKVLimit);
     }
     const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
+    // SOFT: softmax over the final centroids of token tok, clusters 4g .. 4g+3
+    // (the B operand of the gather product below, already normalised)
+    Sp4 psoft;
+    if (SOFT && (FULL || w < NT)) {
+        const Sp8 mu0 = frag_at(pMu, kPlaneMu, lo.rl64), mu1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4_t a = mma3(mu0, qf[0], kZero4);   // a[rr] = mu_{4g+rr} . q_tok (scaled units)
+        a = mma3(mu1, qf[1], a);
+        const float s2 = __builtin_ldexpf(0.125f, 2 * sq) * 1.4426950408889634f;
+        float x[4], mx = -__builtin_inff();
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            x[rr] = 4 * g + rr < Kc ? a[rr] * s2 : -__builtin_inff();
+            mx = fmaxf(mx, x[rr]);
+        }
+        mx = col_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            x[rr] = __builtin_amdgcn_exp2f(x[rr] - mx);
+            z += x[rr];
+        }
+        const float iz = 1.0f / col_sum(z);
+        psoft = split4<true>(x[0] * iz, x[1] * iz, x[2] * iz, x[3] * iz);
+    }
     uint16_t *sV = sQV;   // Q planes are dead
     {
         if (__builtin_expect(sk != 0, 0)) {   // uniform; rare
@@ -841,7 +916,9 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
         const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
         const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
-        const float f = (1.0f - alpha) * vunscale * __builtin_amdgcn_rcpf(den);   // (1 - alpha) V^cent
+        // (1 - alpha) V^cent; kept in the scaled units of V for the soft
+        // gather, whose fp16 operands need them
+        const float f = (1.0f - alpha) * (SOFT ? 1.f : vunscale) * __builtin_amdgcn_rcpf(den);
         *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) =
             make_float4(a[0] * f, a[1] * f, a[2] * f, a[3] * f);
     }
@@ -876,7 +953,18 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
                 const int d0 = 16 * j + 4 * g;
-                const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
+                float4 c4;
+                if (SOFT) {
+                    // G^T[dim 16j + 4g + rr][token tok] = sum_k V^cent^T[dim][k] p[k][tok]:
+                    // A[dim 16j + l16][k = 4g + i] from the fp32 rows of V^cent
+                    const float *vk = sVc + 4 * g * kVcRow + 16 * j + l16;
+                    const Sp4 va = split4<true>(vk[0], vk[kVcRow], vk[2 * kVcRow], vk[3 * kVcRow]);
+                    const f32x4_t gs = mma3_16(va, psoft, kZero4);
+                    c4 = make_float4(gs[0] * vunscale, gs[1] * vunscale, gs[2] * vunscale,
+                                     gs[3] * vunscale);
+                } else {
+                    c4 = *reinterpret_cast<const float4 *>(vc + d0);
+                }
                 float v0 = fmaf(o[j][0], f, c4.x), v1 = fmaf(o[j][1], f, c4.y);
                 float v2 = fmaf(o[j][2], f, c4.z), v3 = fmaf(o[j][3], f, c4.w);
                 if (MASKED && !keep) v0 = v1 = v2 = v3 = 0.f;
@@ -908,61 +996,59 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }
 
-template <typename T, bool FULL, bool NARROW, bool MASKED>
-static hipError_t fused_launch_t(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                 int iters, int radius, float alpha, const uint8_t *valid, int H,
-                                 int G, void *out, int32_t *assign, hipStream_t st) {
-    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED>;
-    InitMask init{};
-    for (int k = 0; k < Kc; ++k) {
-        const int t = (int)(((long)k * L) / Kc);
-        init.w[t >> 5] |= 1u << (t & 31);
-    }
-    hipLaunchKernelGGL(kern, dim3((unsigned)S), dim3(kThreads), 0, st,
-                       static_cast<const T *>(Q), static_cast<const T *>(K),
-                       static_cast<const T *>(V), S, L, Kc, iters, radius, alpha, valid, H, G,
-                       static_cast<T *>(out), assign, init);
+// Arguments of one launch, fixed on the host.
+struct FusedArgs {
+    const void *Q, *K, *V;
+    int S, L, Kc, iters, radius;
+    float alpha;
+    const uint8_t *valid;
+    int H, G;
+    void *out;
+    int32_t *assign;
+    InitMask init;
+    int keep_empty;
+};
+
+template <typename T, bool FULL, bool NARROW, bool MASKED, bool SOFT>
+static hipError_t fused_launch_t(const FusedArgs &a, hipStream_t st) {
+    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED, SOFT>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)a.S), dim3(kThreads), 0, st,
+                       static_cast<const T *>(a.Q), static_cast<const T *>(a.K),
+                       static_cast<const T *>(a.V), a.S, a.L, a.Kc, a.iters, a.radius, a.alpha,
+                       a.valid, a.H, a.G, static_cast<T *>(a.out), a.assign, a.init,
+                       a.keep_empty);
     return hipGetLastError();
 }
 
-template <typename T, bool MASKED>
-static hipError_t fused_launch_m(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                 int iters, int W, float alpha, const uint8_t *valid, int H,
-                                 int G, void *out, int32_t *assign, hipStream_t st) {
-    const int radius = W / 2;
-    const bool full = L == kFL;
-    const bool narrow = radius <= 16;
-    if (full && narrow)
-        return fused_launch_t<T, true, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
-                                                     H, G, out, assign, st);
-    if (full)
-        return fused_launch_t<T, true, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
-                                                      valid, H, G, out, assign, st);
-    if (narrow)
-        return fused_launch_t<T, false, true, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha,
-                                                      valid, H, G, out, assign, st);
-    return fused_launch_t<T, false, false, MASKED>(Q, K, V, S, L, Kc, iters, radius, alpha, valid,
-                                                   H, G, out, assign, st);
+template <typename T, bool MASKED, bool SOFT>
+static hipError_t fused_launch_m(const FusedArgs &a, hipStream_t st) {
+    const bool full = a.L == kFL;
+    const bool narrow = a.radius <= 16;
+    if (full && narrow) return fused_launch_t<T, true, true, MASKED, SOFT>(a, st);
+    if (full) return fused_launch_t<T, true, false, MASKED, SOFT>(a, st);
+    if (narrow) return fused_launch_t<T, false, true, MASKED, SOFT>(a, st);
+    return fused_launch_t<T, false, false, MASKED, SOFT>(a, st);
 }
 
 template <typename T>
-static hipError_t fused_launch(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                               int iters, int W, float alpha, const uint8_t *valid, int H,
-                               int G, void *out, int32_t *assign, hipStream_t st) {
-    if (valid)
-        return fused_launch_m<T, true>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out,
-                                       assign, st);
-    return fused_launch_m<T, false>(Q, K, V, S, L, Kc, iters, W, alpha, nullptr, H, G, out,
-                                    assign, st);
+static hipError_t fused_launch(const FusedArgs &a, bool soft, hipStream_t st) {
+    if (a.valid)
+        return soft ? fused_launch_m<T, true, true>(a, st) : fused_launch_m<T, true, false>(a, st);
+    return soft ? fused_launch_m<T, false, true>(a, st) : fused_launch_m<T, false, false>(a, st);
 }
 
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                int iters, int W, float alpha, ca_dtype_t dt, const uint8_t *valid,
-                                int H, int G, void *out, int32_t *assign, hipStream_t st) {
-    if (dt == CA_BF16)
-        return fused_launch<bf16_t>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out, assign,
-                                    st);
-    return fused_launch<float>(Q, K, V, S, L, Kc, iters, W, alpha, valid, H, G, out, assign, st);
+                                int iters, int radius, float alpha, const Variant &var,
+                                ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
+                                int32_t *assign, hipStream_t st) {
+    FusedArgs a{Q, K, V, S, L, Kc, iters, radius, alpha, valid, H, G, out, assign, InitMask{},
+                var.keep_empty ? 1 : 0};
+    for (int k = 0; k < Kc; ++k) {
+        const int t = init_row(k, L, Kc, var.init_step);
+        a.init.w[t >> 5] |= 1u << (t & 31);
+    }
+    if (dt == CA_BF16) return fused_launch<bf16_t>(a, var.soft, st);
+    return fused_launch<float>(a, var.soft, st);
 }
 
 }  // namespace ca

@@ -23,12 +23,15 @@ constexpr int kPad = kD + 1;   // LDS row stride (breaks bank conflicts)
 int kmeans_tiles(int L) { return (L + kTile - 1) / kTile; }
 
 // MODE: 0 = assign only, 1 = assign and emit partials, 2 = partials of a
-// given assignment (read from `assign`). INIT: centroids are the strided
-// rows Q[floor(k L / Kc)] instead of `mu`.
+// given assignment (read from `assign`). INIT: centroids are the initial
+// rows of Q (init_row: floor(k L / Kc), or k * init_step in the listing's
+// variant) instead of `mu`; the first tile of each slice then also writes
+// them to mu_init when that is not null.
 template <typename T, bool INIT, int MODE>
 __global__ __launch_bounds__(256) void kmeans_assign_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int ntile,
-    int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt) {
+    int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
+    int init_step, float *__restrict__ mu_init) {
     extern __shared__ float smem[];
     float *sm_mu = smem;                    // [Kc][kPad]
     float *sm_mn = sm_mu + Kc * kPad;       // [Kc]
@@ -49,8 +52,10 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
             const int k = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
             float4 v;
             if (INIT) {
-                const long row = ((long)k * L) / Kc;
+                const long row = init_row(k, L, Kc, init_step);
                 v = load4<T>(Qs + row * kD + c4);
+                if (mu_init && tile == 0)
+                    *reinterpret_cast<float4 *>(mu_init + (s * Kc + k) * kD + c4) = v;
             } else {
                 v = load4<float>(mu + (s * Kc + k) * kD + c4);
             }
@@ -126,9 +131,11 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
 }
 
 // mu[s,k,:] = (sum over tiles, in tile order) / max(1, n); counts optional.
+// keep_empty (the listing's rule): a cluster with n = 0 leaves mu[s,k,:] as
+// it was.
 __global__ __launch_bounds__(256) void centroid_reduce_kernel(
     const float *__restrict__ part_sum, const int32_t *__restrict__ part_cnt, int nblk, int Kc,
-    long total, float *__restrict__ mu, int32_t *__restrict__ counts) {
+    long total, float *__restrict__ mu, int32_t *__restrict__ counts, int keep_empty) {
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= total) return;
     const long per = (long)Kc * kD;
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256) void centroid_reduce_kernel(
         acc += part_sum[(s * nblk + b) * per + r];
         n += part_cnt[(s * nblk + b) * Kc + k];
     }
-    mu[e] = acc / (float)(n > 1 ? n : 1);
+    if (!(keep_empty && n == 0)) mu[e] = acc / (float)(n > 1 ? n : 1);
     if (counts && (r % kD) == 0) counts[s * Kc + k] = n;
 }
 
@@ -154,7 +161,7 @@ static size_t assign_lds_bytes(int Kc, bool partials) {
 template <typename T, bool INIT, int MODE>
 static hipError_t assign_launch(const void *Q, const float *mu, int S, int L, int Kc,
                                 int32_t *assign, float *part_sum, int32_t *part_cnt,
-                                hipStream_t st) {
+                                hipStream_t st, int init_step = 0, float *mu_init = nullptr) {
     auto kern = kmeans_assign_kernel<T, INIT, MODE>;
     const size_t lds = assign_lds_bytes(Kc, MODE != 0);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -162,27 +169,34 @@ static hipError_t assign_launch(const void *Q, const float *mu, int S, int L, in
     if (e != hipSuccess) return e;
     const int ntile = kmeans_tiles(L);
     hipLaunchKernelGGL(kern, dim3((unsigned)((long)S * ntile)), dim3(256), lds, st,
-                       static_cast<const T *>(Q), mu, L, Kc, ntile, assign, part_sum, part_cnt);
+                       static_cast<const T *>(Q), mu, L, Kc, ntile, assign, part_sum, part_cnt,
+                       init_step, mu_init);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t assign_dispatch(const void *Q, const float *mu, int S, int L, int Kc,
                                   int32_t *assign, float *part_sum, int32_t *part_cnt,
-                                  hipStream_t st) {
+                                  hipStream_t st, int init_step, float *mu_init) {
     const bool partials = part_sum != nullptr;
     if (mu == nullptr)
-        return partials ? assign_launch<T, true, 1>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st)
-                        : assign_launch<T, true, 0>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st);
+        return partials ? assign_launch<T, true, 1>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
+                                                    init_step, mu_init)
+                        : assign_launch<T, true, 0>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
+                                                    init_step, mu_init);
     return partials ? assign_launch<T, false, 1>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st)
                     : assign_launch<T, false, 0>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st);
 }
 
 hipError_t launch_kmeans_assign(const void *Q, const float *mu, int S, int L, int Kc,
                                 ca_dtype_t dt, int32_t *assign, float *part_sum,
-                                int32_t *part_cnt, hipStream_t st) {
-    if (dt == CA_BF16) return assign_dispatch<bf16_t>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st);
-    return assign_dispatch<float>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st);
+                                int32_t *part_cnt, hipStream_t st, int init_step,
+                                float *mu_init) {
+    if (dt == CA_BF16)
+        return assign_dispatch<bf16_t>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st, init_step,
+                                       mu_init);
+    return assign_dispatch<float>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st, init_step,
+                                  mu_init);
 }
 
 hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S, int L, int Kc,
@@ -195,11 +209,12 @@ hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S,
 }
 
 hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt, int nblk,
-                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st) {
+                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st,
+                                  bool keep_empty) {
     const long total = (long)S * Kc * kD;
     const dim3 grid((unsigned)((total + 255) / 256)), block(256);
     hipLaunchKernelGGL(centroid_reduce_kernel, grid, block, 0, st, part_sum, part_cnt, nblk, Kc,
-                       total, mu, counts);
+                       total, mu, counts, keep_empty ? 1 : 0);
     return hipGetLastError();
 }
 

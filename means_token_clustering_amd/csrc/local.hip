@@ -6,7 +6,8 @@
 // O = (1 - alpha) V^gathered + alpha O^local with V^gathered_i = Vc_{c_i});
 // "ClusterFormer" spec 3 (band-masked attention) and 4 (2W+1 band). Window
 // reading used throughout the library: key j belongs to query i iff
-// |i - j| <= floor(W/2), clipped to [0, L).
+// |i - j| <= r, clipped to [0, L), with r = floor(W/2) (r = W in the
+// ClusterAttention listing's band).
 //
 // Work split: one workgroup per 64-query tile; the tile's keys
 // [i0 - r, i0 + 63 + r] stream through LDS in 64-row K/V tiles (the halo).
@@ -19,6 +20,10 @@
 // "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
 // a key with valid[b * L + j] == 0 takes the logit -10000 inside the window,
 // and the fused output row of a padded query is zero (b = s / H).
+//
+// Soft gather (the same listing's forward): with mu given, the gathered
+// context of query i is sum_k softmax_k(q_i . mu_k / sqrt(d)) vcent_k,
+// folded in 64-centroid chunks staged through LDS with an online softmax.
 #include "common.h"
 
 namespace ca {
@@ -27,12 +32,12 @@ constexpr int kQTile = 64;
 constexpr int kLTile = 64;
 constexpr int kLPad = kD + 1;
 
-template <typename T, bool FUSE>
+template <typename T, bool FUSE, bool SOFT>
 __global__ __launch_bounds__(256) void local_window_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int r,
     int ntile, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
     float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out,
-    float *__restrict__ oloc) {
+    float *__restrict__ oloc, const float *__restrict__ mu) {
     __shared__ float sm_k[kLTile * kLPad];
     __shared__ float sm_v[kLTile * kLPad];
     __shared__ float sm_s[kQTile * kLPad];
@@ -126,12 +131,61 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             m = mn;
         }
     }
+    float gsoft[16];
+    if (SOFT) {
+        // centroids and their contexts in chunks of 64 rows (sm_k, sm_v)
+        float m2 = -__builtin_inff(), l2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) gsoft[c] = 0.f;
+        for (int k0 = 0; k0 < Kc; k0 += kLTile) {
+            const int nk = min(kLTile, Kc - k0);
+            __syncthreads();
+            for (int e = tid; e < nk * (kD / 4); e += 256) {
+                const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
+                const float4 mv = load4<float>(mu + (s * Kc + k0 + rr) * kD + c4);
+                const float4 gv = load4<float>(vcent + (s * Kc + k0 + rr) * kD + c4);
+                float *dm = sm_k + rr * kLPad + c4;
+                float *dg = sm_v + rr * kLPad + c4;
+                dm[0] = mv.x; dm[1] = mv.y; dm[2] = mv.z; dm[3] = mv.w;
+                dg[0] = gv.x; dg[1] = gv.y; dg[2] = gv.z; dg[3] = gv.w;
+            }
+            __syncthreads();
+            float mt = -__builtin_inff();
+            for (int k = 0; k < nk; ++k) {   // every lane runs every k: shuffles converge
+                const float *mr = sm_k + k * kLPad + 16 * g;
+                float part = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) part = fmaf(qr[c], mr[c], part);
+                const float sum2 = part + __shfl_xor(part, 1);
+                const float sc = sum2 + __shfl_xor(sum2, 2);
+                mt = fmaxf(mt, sc);
+                if (g == 0) sm_s[qi * kLPad + k] = sc;
+            }
+            __syncthreads();
+            const float mn = fmaxf(m2, mt);
+            const float corr = (m2 == -__builtin_inff()) ? 0.f : exp_f32(m2 - mn);
+            l2 *= corr;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) gsoft[c] *= corr;
+            for (int k = 0; k < nk; ++k) {
+                const float p = exp_f32(sm_s[qi * kLPad + k] - mn);
+                l2 += p;
+                const float *gr = sm_v + k * kLPad + 16 * g;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) gsoft[c] = fmaf(p, gr[c], gsoft[c]);
+            }
+            m2 = mn;
+        }
+        const float iz = 1.0f / l2;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) gsoft[c] *= iz;
+    }
     if (!active) return;
     const float inv = 1.0f / l;
     const long o = base + (long)i * kD + 16 * g;
     if (FUSE) {
-        const int c = assign[s * L + i];
-        const float *gv = vcent + (s * Kc + c) * kD + 16 * g;
+        const int c = SOFT ? 0 : assign[s * L + i];
+        const float *gv = SOFT ? gsoft : vcent + (s * Kc + c) * kD + 16 * g;
         const bool keep = valid == nullptr || valid[(s / H) * L + i] != 0;
         const float wg = keep ? 1.0f - alpha : 0.f;
         const float wl = keep ? alpha : 0.f;
@@ -179,35 +233,39 @@ __global__ __launch_bounds__(256) void gather_fuse_kernel(const float *__restric
 }
 
 template <typename T>
-static hipError_t local_dispatch(const void *Q, const void *K, const void *V, int S, int L, int W,
+static hipError_t local_dispatch(const void *Q, const void *K, const void *V, int S, int L, int r,
                                  const float *vcent, const int32_t *assign, int Kc, float alpha,
                                  const uint8_t *valid, int H, int G, void *out, float *oloc,
-                                 hipStream_t st) {
+                                 const float *mu, hipStream_t st) {
     const int ntile = (L + kQTile - 1) / kQTile;
-    const int r = W / 2;
     const dim3 grid((unsigned)((long)S * ntile)), block(256);
     const T *q = static_cast<const T *>(Q);
     const T *k = static_cast<const T *>(K);
     const T *v = static_cast<const T *>(V);
-    if (oloc == nullptr)
-        hipLaunchKernelGGL((local_window_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, ntile,
-                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), oloc);
-    else
-        hipLaunchKernelGGL((local_window_kernel<T, false>), grid, block, 0, st, q, k, v, L, r,
+    if (oloc == nullptr && mu != nullptr)
+        hipLaunchKernelGGL((local_window_kernel<T, true, true>), grid, block, 0, st, q, k, v, L, r,
                            ntile, vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out),
-                           oloc);
+                           oloc, mu);
+    else if (oloc == nullptr)
+        hipLaunchKernelGGL((local_window_kernel<T, true, false>), grid, block, 0, st, q, k, v, L, r,
+                           ntile, vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out),
+                           oloc, mu);
+    else
+        hipLaunchKernelGGL((local_window_kernel<T, false, false>), grid, block, 0, st, q, k, v, L,
+                           r, ntile, vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out),
+                           oloc, mu);
     return hipGetLastError();
 }
 
-hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int W,
+hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int r,
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
                                float alpha, const uint8_t *valid, int H, int G, void *out,
-                               float *oloc, hipStream_t st) {
+                               float *oloc, hipStream_t st, const float *mu) {
     if (dt == CA_BF16)
-        return local_dispatch<bf16_t>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, G,
-                                      out, oloc, st);
-    return local_dispatch<float>(Q, K, V, S, L, W, vcent, assign, Kc, alpha, valid, H, G, out,
-                                 oloc, st);
+        return local_dispatch<bf16_t>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H, G,
+                                      out, oloc, mu, st);
+    return local_dispatch<float>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H, G, out,
+                                 oloc, mu, st);
 }
 
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,

@@ -4,7 +4,7 @@ Assignments: Lloyd's k-means with floating-point distances can legitimately
 disagree where two centroids are (nearly) equidistant, and one early flip
 changes every later centroid. So each iteration t is checked teacher-forced:
 the oracle rebuilds mu^(t-1) in fp64 from the GPU's own c^(t-1) (mu^(0) is the
-strided init), assigns, and compares with the GPU's c^(t) (obtained by a run
+initial rows; with kept empty clusters the rebuild carries mu^(t-2) along), assigns, and compares with the GPU's c^(t) (obtained by a run
 with iters = t, which reproduces the first t iterations of any longer run).
 A mismatch is excused only at a near-tie, where the oracle's best-to-second
 gap is below NEAR_TIE * ||q_i||^2 and the two centroids are not identical
@@ -54,19 +54,24 @@ def check_assignment_step(Q: np.ndarray, mu: np.ndarray, c_gpu: np.ndarray, t: i
 
 def check_forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float, dtype: str,
                   assign_by_iter: List[np.ndarray], out_gpu: np.ndarray,
-                  tol: Optional[float] = None, valid: Optional[np.ndarray] = None):
+                  tol: Optional[float] = None, valid: Optional[np.ndarray] = None,
+                  flags: int = 0):
     """Full protocol. assign_by_iter[t-1] = GPU c^(t); out_gpu = GPU output
     (as float64 values) of the run with `iters` iterations; valid: the key-
-    padding mask of a masked run (the clustering ignores it)."""
+    padding mask of a masked run (the clustering ignores it); flags: the
+    listing-compatible variants of the run (oracle.INIT_STEP, ...), which
+    the rebuilt centroids follow too."""
     L = Q.shape[-2]
     K = oracle.num_clusters(nclust, L)
+    keep = bool(flags & oracle.KEEP_EMPTY)
     reports = []
-    mu = oracle.init_centroids(Q, K)
+    mu = oracle.init_centroids(Q, K, step=bool(flags & oracle.INIT_STEP))
     for t in range(1, iters + 1):
         c_gpu = assign_by_iter[t - 1]
         reports.append(check_assignment_step(Q, mu, c_gpu, t))
-        mu, _ = oracle.update(Q, c_gpu, K)
-    ref = oracle.forward_from_assign(Q, Kt, V, assign_by_iter[-1], K, W, alpha, valid=valid)
+        mu, _ = oracle.update(Q, c_gpu, K, prev=mu if keep else None)
+    ref = oracle.forward_from_assign(Q, Kt, V, assign_by_iter[-1], K, W, alpha, valid=valid,
+                                     flags=flags, mu=mu if flags else None)
     err = np.abs(out_gpu - ref["out"])
     tol = TOL[dtype] if tol is None else tol
     return reports, float(err.max()) if err.size else 0.0, tol, ref

@@ -339,3 +339,120 @@ def test_grouped_kv_heads(case, path):
     for r in reports:
         assert r.bad == 0, parity.summarize(reports)
     assert err <= tol
+
+
+# ---------------------------------------------------------------- listing-compatible variants
+LF = oracle.LISTING
+LISTING = [  # B, H, L, nclust, iters, W, alpha, dtype, flags, mask kind (None: no mask)
+    (2, 12, 128, 16, 3, 16, 0.5, gen.F32, LF, None),           # band radius 16, single launch
+    (2, 4, 120, 16, 3, 40, 0.5, gen.F32, LF, None),            # step rows differ from floor(kL/K)
+    (2, 4, 100, 16, 3, 8, 0.3, gen.BF16, LF, "holes"),
+    (2, 3, 128, 16, 3, 0, 0.5, gen.F32, LF, None),             # W = 0: soft gather only
+    (2, 3, 128, 16, 3, 128, 0.5, gen.F32, oracle.BAND, None),  # W >= L: hard gather only
+    (1, 2, 300, 16, 3, 32, 0.5, gen.F32, LF, "prefix"),        # staged only (L > 128)
+    (1, 2, 130, 7, 4, 17, 0.4, gen.F32, LF, None),             # K not dividing L, odd W
+    (2, 3, 128, 16, 3, 32, 0.5, gen.F32, oracle.INIT_STEP, None),
+    (2, 3, 128, 16, 3, 32, 0.5, gen.F32, oracle.SOFT_GATHER, None),
+    (2, 3, 90, 5, 3, 20, 0.6, gen.BF16, oracle.SOFT_GATHER | oracle.BAND, None),
+    (1, 1, 300, 256, 2, 32, 0.5, gen.F32, LF, None),           # soft gather over 256 centroids
+]
+
+
+def check_listing(x: gen.AttnInputs, flags: int, mask, path: int):
+    b = _b()
+    _say(f"[listing] B={x.B} H={x.H} L={x.L} K={x.nclust} I={x.iters} W={x.W} a={x.alpha} "
+         f"{x.dtype} flags={flags} mask={mask is not None} seed={x.seed} path={path}")
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    vd = torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).cuda() if mask is not None else None
+    assigns, out = [], None
+    for t in range(1, x.iters + 1):
+        o, c = b.cluster_attn_forward(q, k, v, x.nclust, t, x.W, x.alpha, path=path, valid=vd,
+                                      flags=flags)
+        assigns.append(c.cpu().numpy())
+        out = o
+    torch.cuda.synchronize()
+    outh = _host(out)
+    reports, err, tol, ref = parity.check_forward(
+        x.values("q"), x.values("k"), x.values("v"), x.nclust, x.iters, x.W, x.alpha, x.dtype,
+        assigns, outh, valid=mask, flags=flags)
+    _say(f"  {parity.summarize(reports)}; max|out-ref|={err:.3e} (tol {tol})")
+    for r in reports:
+        assert r.bad == 0, parity.summarize(reports)
+    assert err <= tol
+    if mask is not None:
+        pad = np.broadcast_to((mask == 0)[:, None, :], (x.B, x.H, x.L))
+        assert np.all(outh[pad] == 0.0), "padded query rows must be zero"
+    return outh, ref
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("case", LISTING)
+def test_listing_variants(case, path):
+    B, H, L, nclust, iters, W, alpha, dtype, flags, kind = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha, dtype=dtype,
+                        seed=1300 + L + W + flags, blobs=8)
+    mask = gen.make_mask(B, L, seed=L + 3, kind=kind) if kind else None
+    check_listing(x, flags, mask, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_listing_kept_empty_clusters(path):
+    """Queries repeating with period 4 (rows r0..r3, r3 close to -(r0+r1+r2))
+    and step-initial rows 8k: every initial centroid is r0, so the first
+    assignment puts every token in cluster 0 (exact ties, lowest index) and
+    clusters 1..15 are empty. Cluster 0 becomes the small mean m. The
+    listing's rule keeps r0 in clusters 1..15, so at the second assignment
+    the r0 tokens tie exactly among them and take cluster 1; the default
+    rule's zero centroids take the r3 tokens (q . m < ||m||^2 / 2) instead.
+    At the third, cluster 1 is the mean of 32 copies of r0: the rows carry
+    bf16 precision so that this mean is r0 exactly in fp32 too, and its tie
+    with the kept copies of r0 is exact on the GPU as in the oracle."""
+    rng = np.random.default_rng(31)
+    base = rng.standard_normal((2, 3, 4, 64))
+    base[:, :, 3] = -(base[:, :, 0] + base[:, :, 1] + base[:, :, 2]) + 0.1 * base[:, :, 0]
+    base = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(base.astype(np.float32)))
+    Q = np.tile(base, (1, 1, 32, 1))   # L = 128, token i = base[i % 4]
+    x = gen.make_inputs(2, 3, 128, 64, nclust=16, iters=3, W=32, alpha=0.5, seed=32)
+    x.q = Q
+    b = _b()
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    keep = oracle.INIT_STEP | oracle.KEEP_EMPTY
+    phase = np.arange(128) % 4
+    for flags in (keep, oracle.INIT_STEP):
+        _, c1 = b.cluster_attn_forward(q, k, v, 16, 1, 32, 0.5, path=path, flags=flags)
+        assert int(c1.max()) == 0
+    _, c2 = b.cluster_attn_forward(q, k, v, 16, 2, 32, 0.5, path=path, flags=keep)
+    c2 = c2.cpu().numpy()
+    assert np.all(c2[..., phase == 0] == 1), "kept centroids: r0 tokens take cluster 1"
+    _, c2d = b.cluster_attn_forward(q, k, v, 16, 2, 32, 0.5, path=path, flags=oracle.INIT_STEP)
+    c2d = c2d.cpu().numpy()
+    assert np.all(c2d[..., phase == 0] == 0) and np.all(c2d[..., phase == 3] == 1)
+    check_listing(x, keep, None, path)
+    check_listing(x, oracle.LISTING, None, path)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_listing_skip_is_gather_exactly(path):
+    """With the band flag and W = 0 or W >= L the output is the gathered
+    context alone: alpha does not change it, bit for bit."""
+    b = _b()
+    x = gen.make_inputs(2, 3, 128, 64, nclust=16, iters=3, seed=33, blobs=8)
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    for W in (0, 128, 500):
+        o1, _ = b.cluster_attn_forward(q, k, v, 16, 3, W, 0.0, path=path, flags=oracle.LISTING)
+        o2, _ = b.cluster_attn_forward(q, k, v, 16, 3, W, 0.9, path=path, flags=oracle.LISTING)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), W
+
+
+def test_listing_flags_zero_is_default():
+    b = _b()
+    x = gen.workload("distilbert")
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    kk = k[:, :4].contiguous()
+    vv = v[:, :4].contiguous()
+    o0, c0 = b.cluster_attn_forward(q, kk.repeat_interleave(3, dim=1), vv.repeat_interleave(3, dim=1),
+                                    16, 3, 32, 0.5)
+    o1, c1 = b.cluster_attn_forward(q, kk, vv, 16, 3, 32, 0.5, flags=0)
+    torch.cuda.synchronize()
+    assert torch.equal(c0, c1) and torch.equal(o0, o1)
