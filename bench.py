@@ -13,6 +13,7 @@ the roofline record of the dominant kernel and the CPU-oracle baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import re
@@ -31,12 +32,12 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 # HBM traffic of the fused kernel on the distilbert workload, measured with
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch), each
 # scaled by what the same counter reads for the 12 MiB copy kernel that clones
-# the input sets below (FETCH 12288 / 6156.7 = 1.996, WRITE 12288 / 12288 = 1).
+# the input sets below (FETCH 12288 / 6156.6 = 1.996, WRITE 12288 / 12288 = 1).
 # It is reported only while the kernel source (comments aside) is the one the
 # counters were taken on.
-TRAFFIC = {"workload": "distilbert", "bytes": 50_615_887,
-           "read_kib": 36_949.6, "write_kib": 12_480.0,
-           "digest": "cbdd7faaac30516a1c595700e67ffc00754dec583a05ad49407f9b77523ca52a"}
+TRAFFIC = {"workload": "distilbert", "bytes": 50_637_278,
+           "read_kib": 36_970.5, "write_kib": 12_480.0,
+           "digest": "5a516b5dfdc665547a9c40418219ae5bdf3465e212323704bed7f5d2a5d1941a"}
 KERNEL_SOURCES = ("means_token_clustering_amd/csrc/fused.hip",
                   "means_token_clustering_amd/csrc/common.h")
 
@@ -72,16 +73,21 @@ def parse():
     p.add_argument("--masked", action="store_true",
                    help="padded batch: key-padding mask with right padding, row lengths "
                         "~ U{L/4..L} (cluster_attn_forward_masked)")
+    p.add_argument("--flags", type=int, default=0,
+                   help="listing-compatible variants, OR of CA_FLAG_* (15 = all four; "
+                        "cluster_attn_forward_opts)")
     return p.parse_args()
 
 
-def cpu_baseline(x, seconds: float, mask=None):
+def cpu_baseline(x, seconds: float, mask=None, flags: int = 0):
     import oracle
     q, k, v = x.values("q"), x.values("k"), x.values("v")
-    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)   # warm
+    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask,
+                   flags=flags)   # warm
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)
+        oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask,
+                       flags=flags)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -136,9 +142,16 @@ def main():
     wsp = b._aligned_ptr(ws)
     wsn = b._ws_bytes(ws)
 
+    opts = b.CaOptions(vdev.data_ptr() if vdev is not None else None, 0, args.flags)
+
     def step(i):
         q, k, v, o, c = sets[i % nsets]
-        if vdev is not None:
+        if args.flags:
+            st = lib.cluster_attn_forward_opts(q.data_ptr(), k.data_ptr(), v.data_ptr(), x.B, x.H,
+                                               x.L, x.d, x.nclust, x.iters, x.W, float(x.alpha),
+                                               ctypes.byref(opts), o.data_ptr(), c.data_ptr(), dt,
+                                               wsp, wsn, path, sptr)
+        elif vdev is not None:
             st = lib.cluster_attn_forward_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                  vdev.data_ptr(), x.B, x.H, x.L, x.d, x.nclust,
                                                  x.iters, x.W, float(x.alpha), o.data_ptr(),
@@ -169,7 +182,7 @@ def main():
     fused = ws_bytes == 0
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
-    if (fused and mask is None and x.name == TRAFFIC["workload"]
+    if (fused and mask is None and not args.flags and x.name == TRAFFIC["workload"]
             and code_digest() == TRAFFIC["digest"]):
         traffic = TRAFFIC["bytes"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -187,8 +200,10 @@ def main():
     if mask is not None:
         rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "
                                  f"{int(mask.sum())} of {mask.size} tokens real")
+    if args.flags:
+        rec["config"]["flags"] = args.flags
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, mask)
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, mask, args.flags)
     print(json.dumps(rec), flush=True)
 
 

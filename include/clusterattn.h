@@ -168,9 +168,12 @@ typedef struct {
  * floor(W / 2); with W == 0 or W >= L there is no local branch and the
  * output is the gathered context alone (alpha is then ignored). */
 #define CA_FLAG_BAND 8
-/* All four: the listing's forward (alpha is the weight itself; the listing's
- * sigmoid of a parameter is the caller's to apply). */
-#define CA_FLAG_LISTING 15
+/* alpha is the listing's parameter and the weight is its logistic sigmoid
+ * 1 / (1 + exp(-alpha)) (any value but NaN; the weight is rounded to float);
+ * without this flag alpha is the weight itself, in [0, 1]. */
+#define CA_FLAG_ALPHA_LOGIT 16
+/* All five: the listing's forward. */
+#define CA_FLAG_LISTING 31
 
 /*
  * cluster_attn_forward_ex with options (opts NULL = defaults, which is

@@ -20,7 +20,8 @@ CA_F32, CA_BF16 = 0, 1
 CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED = 0, 1, 2
 # listing-compatible variants (ca_options_t.flags)
 CA_FLAG_INIT_STEP, CA_FLAG_KEEP_EMPTY, CA_FLAG_SOFT_GATHER, CA_FLAG_BAND = 1, 2, 4, 8
-CA_FLAG_LISTING = 15
+CA_FLAG_ALPHA_LOGIT = 16
+CA_FLAG_LISTING = 31
 
 _lib = None
 _lock = threading.Lock()

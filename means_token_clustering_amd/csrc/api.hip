@@ -81,6 +81,11 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
                          float alpha, void *out, int32_t *assign_out, ca_dtype_t dt,
                          void *workspace, size_t workspace_bytes, ca_path_t path,
                          hipStream_t stream) {
+    if (flags & ~CA_FLAG_LISTING) return CA_ERR_INVALID_ARG;
+    if (flags & CA_FLAG_ALPHA_LOGIT) {   // the listing's sigmoid of its parameter
+        if (alpha != alpha) return CA_ERR_INVALID_ARG;
+        alpha = (float)(1.0 / (1.0 + exp(-(double)alpha)));
+    }
     ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
     if (st != CA_OK) return st;
     if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED)
@@ -106,7 +111,6 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (valid && (overlap(valid, vbytes, out, tbytes) ||
                   (assign_out && overlap(valid, vbytes, assign_out, abytes))))
         return CA_ERR_INVALID_ARG;
-    if (flags & ~CA_FLAG_LISTING) return CA_ERR_INVALID_ARG;
     const int Kc = clusters(nclust, L);
     if (path == CA_PATH_FUSED && !fused_supported(L, Kc)) return CA_ERR_UNSUPPORTED;
     Variant var{};

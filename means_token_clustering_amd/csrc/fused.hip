@@ -510,16 +510,19 @@ struct InitMask {
 // MASKED: valid is the key-padding mask [S / H, L] (nonzero = real token);
 // padded keys take the logit -10000 in both softmaxes, and the output rows of
 // padded queries are zero.
-// SOFT: the gathered context of token i is sum_k softmax_k(q_i . mu_k /
-// sqrt(d)) V^cent_k over the final centroids instead of V^cent_{c_i}.
-// keep_empty: an empty cluster keeps its previous centroid instead of
-// becoming the zero vector. (Both are the ClusterAttention listing's rules,
-// "Hooshaai/svd-sst2-roberta-cluster" page, k-means routine and forward.)
-template <typename T, bool FULL, bool NARROW, bool MASKED, bool SOFT>
+// EXT: the listing's variants below are switched by the runtime flags
+// (without EXT both are off and compiled out). soft: the gathered context
+// of token i is sum_k softmax_k(q_i . mu_k / sqrt(d)) V^cent_k over the
+// final centroids instead of V^cent_{c_i}. keep_empty: an empty cluster
+// keeps its previous centroid instead of becoming the zero vector. (Both are
+// rules of the ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-
+// cluster" page, its k-means routine and forward.)
+template <typename T, bool FULL, bool NARROW, bool MASKED, bool EXT>
 __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H, int G,
-    T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init, int keep_empty) {
+    T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init, int keep_empty,
+    int soft) {
     __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
@@ -535,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const bool keep_old = EXT && keep_empty != 0, soft_g = EXT && soft != 0;   // uniform
     const long slice = blockIdx.x;
     if (slice >= S) return;
     const int NT = FULL ? 8 : (L + 15) >> 4;
@@ -724,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             float v[4];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) v[rr] = (sm[rr] + sh[rr]) * inv;
-            if (keep_empty && cnt[0] == 0.f) {   // empty: the stored centroid stays
+            if (keep_old && cnt[0] == 0.f) {   // empty: the stored centroid stays
                 const u32x2_t oh = *reinterpret_cast<const u32x2_t *>(sMu + o);
                 const u32x2_t om = *reinterpret_cast<const u32x2_t *>(sMu + kPlaneMuE + o);
 #pragma unroll
@@ -738,7 +742,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             float n2p = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const float x = keep_empty ? half_at(mu4.h, rr) + half_at(mu4.m, rr) : v[rr];
+                const float x = keep_old ? half_at(mu4.h, rr) + half_at(mu4.m, rr) : v[rr];
                 n2p = fmaf(x, x, n2p);
             }
             n2p = col_sum(n2p);   // over the 16 dims of tile w
@@ -771,10 +775,10 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         sk = scale_shift(mk, kKVLimit);
     }
     const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
-    // SOFT: softmax over the final centroids of token tok, clusters 4g .. 4g+3
-    // (the B operand of the gather product below, already normalised)
+    // soft gather: softmax over the final centroids of token tok, clusters
+    // 4g .. 4g+3 (the B operand of the gather product below, normalised)
     Sp4 psoft;
-    if (SOFT && (FULL || w < NT)) {
+    if (soft_g && (FULL || w < NT)) {
         const Sp8 mu0 = frag_at(pMu, kPlaneMu, lo.rl64), mu1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t a = mma3(mu0, qf[0], kZero4);   // a[rr] = mu_{4g+rr} . q_tok (scaled units)
@@ -918,7 +922,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
         // (1 - alpha) V^cent; kept in the scaled units of V for the soft
         // gather, whose fp16 operands need them
-        const float f = (1.0f - alpha) * (SOFT ? 1.f : vunscale) * __builtin_amdgcn_rcpf(den);
+        const float f = (1.0f - alpha) * (soft_g ? 1.f : vunscale) * __builtin_amdgcn_rcpf(den);
         *reinterpret_cast<float4 *>(sVc + l16 * kVcRow + 16 * w + 4 * g) =
             make_float4(a[0] * f, a[1] * f, a[2] * f, a[3] * f);
     }
@@ -954,7 +958,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
                 const int d0 = 16 * j + 4 * g;
                 float4 c4;
-                if (SOFT) {
+                if (soft_g) {
                     // G^T[dim 16j + 4g + rr][token tok] = sum_k V^cent^T[dim][k] p[k][tok]:
                     // A[dim 16j + l16][k = 4g + i] from the fp32 rows of V^cent
                     const float *vk = sVc + 4 * g * kVcRow + 16 * j + l16;
@@ -1006,35 +1010,36 @@ struct FusedArgs {
     void *out;
     int32_t *assign;
     InitMask init;
-    int keep_empty;
+    int keep_empty, soft;
 };
 
-template <typename T, bool FULL, bool NARROW, bool MASKED, bool SOFT>
+template <typename T, bool FULL, bool NARROW, bool MASKED, bool EXT>
 static hipError_t fused_launch_t(const FusedArgs &a, hipStream_t st) {
-    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED, SOFT>;
+    auto kern = cluster_attn_fused_kernel<T, FULL, NARROW, MASKED, EXT>;
     hipLaunchKernelGGL(kern, dim3((unsigned)a.S), dim3(kThreads), 0, st,
                        static_cast<const T *>(a.Q), static_cast<const T *>(a.K),
                        static_cast<const T *>(a.V), a.S, a.L, a.Kc, a.iters, a.radius, a.alpha,
                        a.valid, a.H, a.G, static_cast<T *>(a.out), a.assign, a.init,
-                       a.keep_empty);
+                       a.keep_empty, a.soft);
     return hipGetLastError();
 }
 
-template <typename T, bool MASKED, bool SOFT>
+template <typename T, bool MASKED, bool EXT>
 static hipError_t fused_launch_m(const FusedArgs &a, hipStream_t st) {
     const bool full = a.L == kFL;
     const bool narrow = a.radius <= 16;
-    if (full && narrow) return fused_launch_t<T, true, true, MASKED, SOFT>(a, st);
-    if (full) return fused_launch_t<T, true, false, MASKED, SOFT>(a, st);
-    if (narrow) return fused_launch_t<T, false, true, MASKED, SOFT>(a, st);
-    return fused_launch_t<T, false, false, MASKED, SOFT>(a, st);
+    if (full && narrow) return fused_launch_t<T, true, true, MASKED, EXT>(a, st);
+    if (full) return fused_launch_t<T, true, false, MASKED, EXT>(a, st);
+    if (narrow) return fused_launch_t<T, false, true, MASKED, EXT>(a, st);
+    return fused_launch_t<T, false, false, MASKED, EXT>(a, st);
 }
 
 template <typename T>
-static hipError_t fused_launch(const FusedArgs &a, bool soft, hipStream_t st) {
+static hipError_t fused_launch(const FusedArgs &a, hipStream_t st) {
+    const bool ext = a.keep_empty || a.soft;
     if (a.valid)
-        return soft ? fused_launch_m<T, true, true>(a, st) : fused_launch_m<T, true, false>(a, st);
-    return soft ? fused_launch_m<T, false, true>(a, st) : fused_launch_m<T, false, false>(a, st);
+        return ext ? fused_launch_m<T, true, true>(a, st) : fused_launch_m<T, true, false>(a, st);
+    return ext ? fused_launch_m<T, false, true>(a, st) : fused_launch_m<T, false, false>(a, st);
 }
 
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
@@ -1042,13 +1047,13 @@ hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int
                                 ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
                                 int32_t *assign, hipStream_t st) {
     FusedArgs a{Q, K, V, S, L, Kc, iters, radius, alpha, valid, H, G, out, assign, InitMask{},
-                var.keep_empty ? 1 : 0};
+                var.keep_empty ? 1 : 0, var.soft ? 1 : 0};
     for (int k = 0; k < Kc; ++k) {
         const int t = init_row(k, L, Kc, var.init_step);
         a.init.w[t >> 5] |= 1u << (t & 31);
     }
-    if (dt == CA_BF16) return fused_launch<bf16_t>(a, var.soft, st);
-    return fused_launch<float>(a, var.soft, st);
+    if (dt == CA_BF16) return fused_launch<bf16_t>(a, st);
+    return fused_launch<float>(a, st);
 }
 
 }  // namespace ca

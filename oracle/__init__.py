@@ -145,8 +145,8 @@ def _slices(x: np.ndarray):
 
 
 # listing-compatible variants (flags of forward), see oracle.c
-INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND = 1, 2, 4, 8
-LISTING = INIT_STEP | KEEP_EMPTY | SOFT_GATHER | BAND
+INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND, ALPHA_LOGIT = 1, 2, 4, 8, 16
+LISTING = INIT_STEP | KEEP_EMPTY | SOFT_GATHER | BAND | ALPHA_LOGIT
 
 
 def init_centroids(Q, K: int, step: bool = False) -> np.ndarray:
@@ -241,7 +241,8 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
             trace: bool = True, valid=None, flags: int = 0) -> Dict[str, np.ndarray]:
     """Whole forward pass; Q, K, V are float64 [B, H, L, d]; valid: optional
     key-padding mask [B, L] or [B, H, L] (nonzero = real token); flags:
-    listing-compatible variants (INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND)."""
+    listing-compatible variants (INIT_STEP, KEEP_EMPTY, SOFT_GATHER, BAND,
+    ALPHA_LOGIT)."""
     Q, Kt, V = _f64(Q), _f64(Kt), _f64(V)
     B, H, L, d = Q.shape
     S = B * H

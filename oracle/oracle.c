@@ -34,7 +34,9 @@
  * centroids Q[k * max(1, L / K)]; 2 = an empty cluster keeps its previous
  * centroid; 4 = soft gather, G_i = sum_k softmax_k(q_i . mu_k / sqrt(d))
  * V^cent_k instead of V^cent_{c_i}; 8 = band |i - j| <= W (radius W), and no
- * local branch at all (O = G) when W == 0 or W >= L.
+ * local branch at all (O = G) when W == 0 or W >= L; 16 = the given alpha is
+ * the listing's parameter, and the weight is its logistic sigmoid
+ * 1 / (1 + exp(-alpha)).
  *
  * Layout: each (b, h) pair is one "slice"; a slice of Q, K or V is a
  * contiguous [L, d] row-major block and slices follow in b-major, h-minor
@@ -353,6 +355,7 @@ static void after_clustering(const double *Q, const double *Kt, const double *V,
                              double alpha, const int32_t *valid, int flags, double *out,
                              double *vcent, double *oloc) {
     double *G = NULL;
+    if (flags & 16) alpha = 1.0 / (1.0 + exp(-alpha));
     ora_centroid_xattn(mu, Kt, V, S, L, d, K, valid, vcent, NULL);
     if (flags & 4) {
         G = (double *)malloc(sizeof(double) * (size_t)(S * L * d));

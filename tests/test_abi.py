@@ -38,7 +38,7 @@ def test_flag_values_match_header():
     text = open(HEADER).read()
     defs = {m[0]: int(m[1]) for m in re.findall(r"#define (CA_FLAG_\w+) (\d+)", text)}
     assert defs == {"CA_FLAG_INIT_STEP": 1, "CA_FLAG_KEEP_EMPTY": 2, "CA_FLAG_SOFT_GATHER": 4,
-                    "CA_FLAG_BAND": 8, "CA_FLAG_LISTING": 15}
+                    "CA_FLAG_BAND": 8, "CA_FLAG_ALPHA_LOGIT": 16, "CA_FLAG_LISTING": 31}
     for name, value in defs.items():
         assert getattr(b, name) == value, name
 
@@ -202,9 +202,11 @@ def fwd_opts(opts, **kw):
     (_Opts(None, 5, 0), {}, INV),          # 12 heads do not split into 5 groups
     (_Opts(None, 24, 0), {}, INV),         # more K/V heads than query heads
     (_Opts(None, -1, 0), {}, INV),
-    (_Opts(None, 4, 16), {}, INV),         # no such flag
+    (_Opts(None, 4, 32), {}, INV),         # no such flag
     (_Opts(None, 4, -1), {}, INV),
-    (_Opts(None, 4, 15), dict(W=-1), INV),  # the listing's flags keep the other checks
+    (_Opts(None, 4, 31), dict(W=-1), INV),  # the listing's flags keep the other checks
+    (_Opts(None, 4, 16), dict(alpha=float("nan")), INV),
+    (_Opts(None, 4, 16), dict(alpha=7.5, Q=None), INV),   # any finite parameter passes the alpha check
     (_Opts(None, 4, 0), dict(Q=None), INV),
     (_Opts(None, 4, 0), dict(out=K + 4096), INV),   # out overlaps the smaller K
     (_Opts(MASK, 3, 0), dict(alpha=-1.0), INV),

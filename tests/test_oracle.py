@@ -538,14 +538,15 @@ def test_listing_forward_uses_final_centroids():
     products with the local branch."""
     x = gen.make_inputs(2, 2, 48, 8, nclust=6, seed=32, blobs=5)
     q, k, v = x.values("q"), x.values("k"), x.values("v")
-    r = oracle.forward(q, k, v, 6, 3, 5, 0.3, flags=oracle.LISTING)
+    a = math.log(0.3 / 0.7)   # the listing's parameter: sigmoid(a) = 0.3
+    r = oracle.forward(q, k, v, 6, 3, 5, a, flags=oracle.LISTING)
     mu = r["mu"]
     assert np.allclose(r["vcent"], _sdpa(mu, k, v), atol=1e-13)
     g = _sdpa(q, mu, r["vcent"])
     ol, _ = oracle.local_attn(q, k, v, 10)   # band radius 5 = window 10
     assert np.array_equal(r["oloc"], ol)
     assert np.allclose(r["out"], 0.7 * g + 0.3 * ol, atol=1e-13)
-    f = oracle.forward_from_assign(q, k, v, r["assign"], 6, 5, 0.3, flags=oracle.LISTING, mu=mu)
+    f = oracle.forward_from_assign(q, k, v, r["assign"], 6, 5, a, flags=oracle.LISTING, mu=mu)
     assert np.array_equal(f["out"], r["out"])
 
 
@@ -590,3 +591,19 @@ def test_listing_mask_padded_rows_zero():
     assert np.all(r["out"][0, :, 25:] == 0.0)
     r0 = oracle.forward(q, k, v, 5, 3, 6, 0.3, flags=oracle.LISTING)
     assert np.array_equal(r0["mu"], r["mu"])
+
+
+def test_alpha_logit_is_sigmoid_of_parameter():
+    x = gen.make_inputs(1, 2, 40, 8, nclust=5, seed=37, blobs=4)
+    args = (x.values("q"), x.values("k"), x.values("v"), 5, 3, 10)
+    # sigmoid(0) = 1/2 exactly
+    assert np.array_equal(oracle.forward(*args, 0.0, flags=oracle.ALPHA_LOGIT)["out"],
+                          oracle.forward(*args, 0.5)["out"])
+    for w in (0.1, 0.8):
+        a = math.log(w / (1 - w))
+        assert np.allclose(oracle.forward(*args, a, flags=oracle.ALPHA_LOGIT)["out"],
+                           oracle.forward(*args, w)["out"], atol=1e-14)
+    # a very negative parameter leaves the gathered context alone
+    r = oracle.forward(*args, -800.0, flags=oracle.ALPHA_LOGIT)
+    g = np.take_along_axis(r["vcent"], r["assign"][..., None].astype(np.int64), axis=2)
+    assert np.array_equal(r["out"], g)
