@@ -72,6 +72,8 @@ def _load():
                                 _dp, _ip, _dp, _dp, _dp, _dp, _dp, _dp]),
             "ora_forward_from_assign": (None, [_dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip, i,
                                                _dp, _dp, _dp, _dp, _dp]),
+            "ora_backward": (None, [_dp, _dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip,
+                                    _dp, _dp, _dp, _dp]),
             "ora_matmul": (None, [_dp, _dp, L, L, L, _dp]),
             "ora_round_bf16": (d, [d]),
             "ora_round_bf16_array": (None, [_dp, L]),
@@ -274,6 +276,22 @@ def forward(Q, Kt, V, nclust: int, iters: int, W: int, alpha: float,
     return res
 
 
+def backward(Q, Kt, V, dO, c, K: int, W: int, alpha: float, valid=None):
+    """Gradients of sum(dO * O) for the forward with the final assignment c
+    held fixed (equations' rules): returns dQ, dK, dV (shapes of Q, K, V) and
+    dalpha (a float, summed over every slice)."""
+    Q, S, L, d = _slices(Q)
+    vm = _mask(valid, Q.shape[:-2], L)
+    Kt, V, dO, c = _f64(Kt), _f64(V), _f64(dO), _i32(c)
+    if c.size and (c.min() < 0 or c.max() >= K):
+        raise ValueError("assignment out of range")
+    dQ, dK, dV = np.empty(Q.shape), np.empty(Q.shape), np.empty(Q.shape)
+    da = ctypes.c_double(0.0)
+    _load().ora_backward(_p(Q), _p(Kt), _p(V), _p(dO), S, L, d, K, _p(c), W, float(alpha),
+                         _p(vm), _p(dQ), _p(dK), _p(dV), ctypes.byref(da))
+    return dQ, dK, dV, da.value
+
+
 def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None,
                         flags: int = 0, mu=None):
     """Steps after clustering from a given final assignment c (e.g. the GPU's);
@@ -317,6 +335,14 @@ def repeat_kv(x, G: int) -> np.ndarray:
     usual consecutive grouping)."""
     x = _f64(x)
     return np.ascontiguousarray(np.repeat(x, int(G), axis=1))
+
+
+def fold_kv(x, G: int) -> np.ndarray:
+    """Adjoint of repeat_kv: [B, Hkv*G, L, d] -> [B, Hkv, L, d], summing the
+    G query heads that share a K/V head (their K/V gradients add up)."""
+    x = _f64(x)
+    B, H = x.shape[:2]
+    return np.ascontiguousarray(x.reshape(B, H // int(G), int(G), *x.shape[2:]).sum(axis=2))
 
 
 def split_heads(x2d: np.ndarray, B: int, L: int, H: int, d: int) -> np.ndarray:

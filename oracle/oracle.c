@@ -453,6 +453,147 @@ void ora_forward_from_assign(const double *Q, const double *Kt, const double *V,
     free(mu); free(vcent); free(oloc);
 }
 
+/*
+ * Backward pass of the forward above (equations' rules: strided init, zero
+ * empty clusters, radius floor(W/2), hard gather; optional key-padding mask),
+ * for the loss sum(dO * O). The pages call the clustering differentiable
+ * ("Architectural Support" section of the svd-sst2-roberta-cluster page) and
+ * fine-tune through it ("Post-KD Recovery" column of the model card's
+ * benchmark table); the assignment itself is a piecewise-constant argmin, so
+ * the derivative holds c (the final assignment) fixed and flows through
+ * everything else:
+ *   mu_k = sum_{c_i = k} q_i / max(1, n_k)      (d mu_k / d q_i = 1 / n_k)
+ *   Pc = softmax_j(mu_k . k_j / sqrt(d)),  V^cent = Pc V
+ *   Pl = softmax_{j in window(i)}(q_i . k_j / sqrt(d)),  O^loc = Pl V
+ *   O_i = keep_i ((1 - alpha) V^cent_{c_i} + alpha O^loc_i)
+ * A padded key's logit is the constant -10000, so no gradient reaches q or k
+ * through it. Outputs dQ, dK, dV [S, L, d] and dalpha (summed over all
+ * slices). Dense probability matrices per slice; plain loops.
+ */
+void ora_backward(const double *Q, const double *Kt, const double *V, const double *dO,
+                  long S, int L, int d, int K, const int32_t *c, int W, double alpha,
+                  const int32_t *valid, double *dQ, double *dK, double *dV, double *dalpha) {
+    const double scale = 1.0 / sqrt((double)d);
+    const int r = ora_radius(W);
+    double *part = (double *)calloc((size_t)S, sizeof(double));   /* dalpha per slice */
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double total = 0.0;
+        const double *q = Q + s * L * (long)d, *kk = Kt + s * L * (long)d;
+        const double *v = V + s * L * (long)d, *go = dO + s * L * (long)d;
+        const int32_t *cs = c + s * L;
+        const int32_t *ok = valid ? valid + s * L : NULL;
+        double *gq = dQ + s * L * (long)d, *gk = dK + s * L * (long)d, *gv = dV + s * L * (long)d;
+        double *mu = (double *)calloc((size_t)K * d, sizeof(double));
+        int *n = (int *)calloc((size_t)K, sizeof(int));
+        double *pc = (double *)malloc(sizeof(double) * (size_t)K * L);
+        double *vc = (double *)calloc((size_t)K * d, sizeof(double));
+        double *pl = (double *)calloc((size_t)L * L, sizeof(double));
+        double *ol = (double *)calloc((size_t)L * d, sizeof(double));
+        double *g = (double *)malloc(sizeof(double) * (size_t)L * d);      /* keep * dO */
+        double *dvc = (double *)calloc((size_t)K * d, sizeof(double));
+        double *dmu = (double *)calloc((size_t)K * d, sizeof(double));
+        double *row = (double *)malloc(sizeof(double) * (size_t)L);
+        for (long e = 0; e < (long)L * d; ++e) gq[e] = gk[e] = gv[e] = 0.0;
+
+        /* forward quantities with c fixed */
+        for (int i = 0; i < L; ++i) {
+            n[cs[i]] += 1;
+            for (int t = 0; t < d; ++t) mu[(long)cs[i] * d + t] += q[(long)i * d + t];
+        }
+        for (int k = 0; k < K; ++k)
+            for (int t = 0; t < d; ++t) mu[(long)k * d + t] /= (n[k] > 1 ? (double)n[k] : 1.0);
+        for (int k = 0; k < K; ++k) {
+            double mx = -INFINITY, z = 0.0;
+            for (int j = 0; j < L; ++j) {
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += mu[(long)k * d + t] * kk[(long)j * d + t];
+                row[j] = (ok && !ok[j]) ? -10000.0 : dot * scale;
+                if (row[j] > mx) mx = row[j];
+            }
+            for (int j = 0; j < L; ++j) z += (row[j] = exp(row[j] - mx));
+            for (int j = 0; j < L; ++j) {
+                pc[(long)k * L + j] = row[j] / z;
+                for (int t = 0; t < d; ++t) vc[(long)k * d + t] += pc[(long)k * L + j] * v[(long)j * d + t];
+            }
+        }
+        for (int i = 0; i < L; ++i) {
+            const int lo = i - r < 0 ? 0 : i - r, hi = i + r > L - 1 ? L - 1 : i + r;
+            double mx = -INFINITY, z = 0.0;
+            for (int j = lo; j <= hi; ++j) {
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += q[(long)i * d + t] * kk[(long)j * d + t];
+                row[j] = (ok && !ok[j]) ? -10000.0 : dot * scale;
+                if (row[j] > mx) mx = row[j];
+            }
+            for (int j = lo; j <= hi; ++j) z += (row[j] = exp(row[j] - mx));
+            for (int j = lo; j <= hi; ++j) {
+                pl[(long)i * L + j] = row[j] / z;
+                for (int t = 0; t < d; ++t) ol[(long)i * d + t] += pl[(long)i * L + j] * v[(long)j * d + t];
+            }
+        }
+        /* output side: keep, alpha, gather */
+        for (int i = 0; i < L; ++i) {
+            const double kp = (ok && !ok[i]) ? 0.0 : 1.0;
+            for (int t = 0; t < d; ++t) {
+                const double gi = kp * go[(long)i * d + t];
+                g[(long)i * d + t] = gi;
+                total += gi * (ol[(long)i * d + t] - vc[(long)cs[i] * d + t]);
+                dvc[(long)cs[i] * d + t] += (1.0 - alpha) * gi;
+            }
+        }
+        /* local branch: dS_ij = Pl_ij (dO^loc_i . v_j - dO^loc_i . O^loc_i) */
+        for (int i = 0; i < L; ++i) {
+            double D = 0.0;
+            for (int t = 0; t < d; ++t) D += alpha * g[(long)i * d + t] * ol[(long)i * d + t];
+            for (int j = 0; j < L; ++j) {
+                const double p = pl[(long)i * L + j];
+                if (p == 0.0 && (j < i - r || j > i + r)) continue;
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) {
+                    dp += alpha * g[(long)i * d + t] * v[(long)j * d + t];
+                    gv[(long)j * d + t] += p * alpha * g[(long)i * d + t];
+                }
+                if (ok && !ok[j]) continue;   /* constant logit */
+                const double ds = p * (dp - D) * scale;
+                for (int t = 0; t < d; ++t) {
+                    gq[(long)i * d + t] += ds * kk[(long)j * d + t];
+                    gk[(long)j * d + t] += ds * q[(long)i * d + t];
+                }
+            }
+        }
+        /* centroid branch: dS_kj = Pc_kj (dVc_k . v_j - dVc_k . V^cent_k) */
+        for (int k = 0; k < K; ++k) {
+            double D = 0.0;
+            for (int t = 0; t < d; ++t) D += dvc[(long)k * d + t] * vc[(long)k * d + t];
+            for (int j = 0; j < L; ++j) {
+                const double p = pc[(long)k * L + j];
+                double dp = 0.0;
+                for (int t = 0; t < d; ++t) {
+                    dp += dvc[(long)k * d + t] * v[(long)j * d + t];
+                    gv[(long)j * d + t] += p * dvc[(long)k * d + t];
+                }
+                if (ok && !ok[j]) continue;
+                const double ds = p * (dp - D) * scale;
+                for (int t = 0; t < d; ++t) {
+                    dmu[(long)k * d + t] += ds * kk[(long)j * d + t];
+                    gk[(long)j * d + t] += ds * mu[(long)k * d + t];
+                }
+            }
+        }
+        /* the mean: every member of cluster k receives dmu_k / n_k */
+        for (int i = 0; i < L; ++i)
+            for (int t = 0; t < d; ++t) gq[(long)i * d + t] += dmu[(long)cs[i] * d + t] / (double)n[cs[i]];
+        free(mu); free(n); free(pc); free(vc); free(pl); free(ol); free(g); free(dvc); free(dmu);
+        free(row);
+        part[s] = total;
+    }
+    double total = 0.0;
+    for (long s = 0; s < S; ++s) total += part[s];
+    free(part);
+    *dalpha = total;
+}
+
 /* C = A B with A [M, P] and B [P, N], row-major, plain sums over p in order. */
 void ora_matmul(const double *A, const double *Bm, long M, long P, long N, double *C) {
 #pragma omp parallel for schedule(static)

@@ -607,3 +607,107 @@ def test_alpha_logit_is_sigmoid_of_parameter():
     r = oracle.forward(*args, -800.0, flags=oracle.ALPHA_LOGIT)
     g = np.take_along_axis(r["vcent"], r["assign"][..., None].astype(np.int64), axis=2)
     assert np.array_equal(r["out"], g)
+
+
+# ------------------------------------------------- P13: backward pass
+# Gradients of sum(dO * O) with the final assignment held fixed (the argmin is
+# piecewise constant; the pages train through the clustering: "Architectural
+# Support" on the svd-sst2-roberta-cluster page, "Post-KD Recovery" in the
+# model card's benchmark table).
+def _loss(q, k, v, dO, c, K, W, alpha, valid=None):
+    return float(np.sum(dO * oracle.forward_from_assign(q, k, v, c, K, W, alpha,
+                                                        valid=valid)["out"]))
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_backward_matches_central_differences(masked):
+    x = gen.make_inputs(1, 2, 24, 8, nclust=4, seed=41, blobs=3)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    dO = _randn(42, 1, 2, 24, 8)
+    valid = None
+    if masked:
+        valid = np.ones((1, 24), np.int32)
+        valid[0, [3, 10, 11, 19]] = 0
+    c = oracle.forward(q, k, v, 4, 3, 6, 0.3)["assign"]
+    dq, dk, dv, da = oracle.backward(q, k, v, dO, c, 4, 6, 0.3, valid=valid)
+    rng = np.random.default_rng(43)
+    h = 1e-5
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(25):
+            idx = tuple(rng.integers(0, n) for n in arr.shape)
+            args = {"q": q, "k": k, "v": v}
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += h
+            minus[idx] -= h
+            args[name] = plus
+            fp = _loss(args["q"], args["k"], args["v"], dO, c, 4, 6, 0.3, valid)
+            args[name] = minus
+            fm = _loss(args["q"], args["k"], args["v"], dO, c, 4, 6, 0.3, valid)
+            fd = (fp - fm) / (2 * h)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+    fd = (_loss(q, k, v, dO, c, 4, 6, 0.3 + h, valid) - _loss(q, k, v, dO, c, 4, 6, 0.3 - h, valid)) / (2 * h)
+    assert abs(fd - da) <= 1e-7 * max(1.0, abs(fd))
+    if masked:   # padded keys take no gradient through their constant logit
+        assert np.all(dk[0, :, [3, 10, 11, 19]] == 0.0)
+
+
+def test_backward_dense_special_case_matches_library_autograd():
+    """K = L with c_i = i makes mu = Q and alpha = 0 leaves softmax(Q K^T) V:
+    torch's autograd of its own attention gives dQ, dK, dV."""
+    x = gen.make_inputs(1, 2, 16, 8, nclust=16, seed=44)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    dO = _randn(45, 1, 2, 16, 8)
+    c = np.broadcast_to(np.arange(16, dtype=np.int32), (1, 2, 16)).copy()
+    dq, dk, dv, _ = oracle.backward(q, k, v, dO, c, 16, 4, 0.0)
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_() for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv)
+    out.backward(torch.from_numpy(dO))
+    for mine, lib in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.allclose(mine, lib.numpy(), atol=1e-12)
+
+
+def test_backward_local_only_matches_library_autograd():
+    """alpha = 1: the output is banded attention; with a key mask whose every
+    window keeps a real key, the -10000 fill equals exclusion, so torch's
+    masked attention and its autograd give the same gradients (padded query
+    rows carry no gradient)."""
+    x = gen.make_inputs(1, 2, 20, 8, nclust=4, seed=46, blobs=3)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    dO = _randn(47, 1, 2, 20, 8)
+    valid = np.ones((1, 20), np.int32)
+    valid[0, [4, 9, 15]] = 0
+    c = oracle.forward(q, k, v, 4, 2, 6, 1.0)["assign"]
+    dq, dk, dv, _ = oracle.backward(q, k, v, dO, c, 4, 6, 1.0, valid=valid)
+    i = np.arange(20)
+    band = np.abs(i[:, None] - i[None, :]) <= 3
+    allowed = torch.from_numpy(band & (valid[0] != 0)[None, :])[None, None]
+    tq, tk, tv = (torch.from_numpy(a.copy()).requires_grad_() for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=allowed)
+    g = dO * valid[0][None, None, :, None]
+    out.backward(torch.from_numpy(g))
+    for mine, lib in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.allclose(mine, lib.numpy(), atol=1e-12)
+
+
+def test_backward_alpha_gradient_closed_form():
+    """d/dalpha of sum(dO * O) is sum(dO * (O^loc - V^cent_c)) over real
+    queries; at alpha = 0 and 1 the output equals one branch exactly."""
+    x = gen.make_inputs(2, 2, 32, 8, nclust=5, seed=48, blobs=4)
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    dO = _randn(49, 2, 2, 32, 8)
+    c = oracle.forward(q, k, v, 5, 3, 8, 0.5)["assign"]
+    _, _, _, da = oracle.backward(q, k, v, dO, c, 5, 8, 0.5)
+    o0 = oracle.forward_from_assign(q, k, v, c, 5, 8, 0.0)["out"]
+    o1 = oracle.forward_from_assign(q, k, v, c, 5, 8, 1.0)["out"]
+    assert abs(da - float(np.sum(dO * (o1 - o0)))) <= 1e-10 * max(1.0, abs(da))
+
+
+def test_fold_kv_is_adjoint_of_repeat_kv():
+    rng = np.random.default_rng(50)
+    a = rng.standard_normal((2, 3, 5, 4))
+    for G in (1, 2, 4):
+        b = rng.standard_normal((2, 3 * G, 5, 4))
+        lhs = float(np.sum(oracle.repeat_kv(a, G) * b))
+        rhs = float(np.sum(a * oracle.fold_kv(b, G)))
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+    assert np.array_equal(oracle.fold_kv(a, 1), a)
