@@ -188,6 +188,42 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
                                       size_t workspace_bytes, ca_path_t path,
                                       hipStream_t stream);
 
+/*
+ * Backward pass of the forward above (equations' rules, no listing flags):
+ * the gradients of sum(dO * O) with the final assignment held fixed. The
+ * pages fine-tune through the clustering (the svd-sst2-roberta-cluster page,
+ * "Architectural Support": differentiable k-means; the model card's benchmark
+ * table, "Post-KD Recovery"); the argmin itself is piecewise constant, so
+ * the gradient flows through the final means mu_k = sum_{c_i = k} q_i / n_k
+ * (each member receives dmu_k / n_k), both softmaxes, the gather and the
+ * fusion. A padded key's -10000 logit is a constant (no gradient to q or k);
+ * padded query rows pass no gradient through the output.
+ *   Q, dO     in   device, [B, H, L, d], dtype dt (dO: the upstream gradient).
+ *   K, V      in   device, [B, kv_heads, L, d] (kv_heads 0 means H).
+ *   assign    in   device int32 [B, H, L]: the final assignment that the
+ *                  forward wrote to assign_out (values outside [0, K) are
+ *                  clamped into it).
+ *   valid     in   nullable key-padding mask [B, L] (as in the forward).
+ *   nclust, W, alpha: the forward's values (K = min(nclust, L)).
+ *   dQ        out  [B, H, L, d]; dK, dV out [B, kv_heads, L, d]; dtype dt
+ *                  (fp32 arithmetic, rounded once to bf16 for bf16 storage).
+ *                  The G = H / kv_heads query heads of a group add into
+ *                  their shared dK, dV.
+ *   dalpha    out  nullable device pointer to one float: d/dalpha.
+ *   workspace      device, 256-byte aligned, at least
+ *                  cluster_attn_backward_workspace_size bytes.
+ * Deterministic (fixed summation orders, no float atomics). Outputs and the
+ * workspace must not overlap each other or the inputs. d = 64, K <= 256.
+ * Errors are caught on the host before any launch.
+ */
+size_t cluster_attn_backward_workspace_size(int B, int H, int kv_heads, int L, int d,
+                                            int nclust, ca_dtype_t dt);
+ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, const void *dO,
+                                  const int32_t *assign, const uint8_t *valid, int B, int H,
+                                  int kv_heads, int L, int d, int nclust, int W, float alpha,
+                                  void *dQ, void *dK, void *dV, float *dalpha, ca_dtype_t dt,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------
  * Single steps (one kernel each), for callers composing their own loop and
  * for step-by-step checking. S = B*H slices; Kc = number of centroids.

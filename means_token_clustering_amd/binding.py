@@ -56,6 +56,9 @@ SIGNATURES = {
     "cluster_attn_layer_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                         _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ca_gemm_bf16": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "cluster_attn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "cluster_attn_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
+                                   _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
 }
 
 
@@ -203,6 +206,33 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
         _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws), path, _stream(stream))
     _check(st, "cluster_attn_forward")
     return out, assign_out
+
+
+def cluster_attn_backward(Q, K, V, dO, assign, nclust: int, W: int, alpha: float, valid=None,
+                          dQ=None, dK=None, dV=None, workspace=None, stream=None,
+                          want_dalpha: bool = True):
+    """Gradients of sum(dO * O) of the forward with its final assignment
+    `assign` held fixed. Q, dO: [B, H, L, d]; K, V: [B, Hkv, L, d]; valid:
+    the forward's key-padding mask or None. Returns (dQ, dK, dV, dalpha), with
+    dalpha a one-element float32 GPU tensor (None unless want_dalpha)."""
+    torch = _torch()
+    B, H, L, d = Q.shape
+    hkv = K.shape[1]
+    dt = _dtype_code(Q)
+    if tuple(V.shape) != tuple(K.shape) or tuple(dO.shape) != tuple(Q.shape):
+        raise ValueError("K, V must share a shape and dO must match Q")
+    dQ = torch.empty_like(Q) if dQ is None else dQ
+    dK = torch.empty_like(K) if dK is None else dK
+    dV = torch.empty_like(V) if dV is None else dV
+    da = torch.empty(1, dtype=torch.float32, device=Q.device) if want_dalpha else None
+    need = lib().cluster_attn_backward_workspace_size(B, H, hkv, L, d, nclust, dt)
+    ws = _workspace(need, Q.device, workspace)
+    st = lib().cluster_attn_backward(
+        _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(assign), _ptr(valid), B, H, hkv, L, d, nclust,
+        W, float(alpha), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(da), dt, _aligned_ptr(ws),
+        _ws_bytes(ws), _stream(stream))
+    _check(st, "cluster_attn_backward")
+    return dQ, dK, dV, da
 
 
 def ca_kmeans_assign(Q, mu, Kc: int, assign=None, stream=None):

@@ -163,6 +163,31 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     return CA_OK;
 }
 
+// Workspace of the backward pass, carved in this order (each 256-B aligned).
+struct BwdLayout {
+    size_t mu, counts, part, pcnt, vcent, cstat, xpart, dvc, dmu, lstat, dal, total;
+};
+
+BwdLayout bwd_layout(long S, int L, int Kc) {
+    BwdLayout w{};
+    const long ntile = bwd_tiles(L) > kmeans_tiles(L) ? bwd_tiles(L) : kmeans_tiles(L);
+    const long nsplit = xattn_splits(L);
+    size_t off = 0;
+    w.mu = off;     off += align_up(sizeof(float) * S * Kc * kD);
+    w.counts = off; off += align_up(sizeof(int32_t) * S * Kc);
+    w.part = off;   off += align_up(sizeof(float) * S * ntile * Kc * kD);
+    w.pcnt = off;   off += align_up(sizeof(int32_t) * S * ntile * Kc);
+    w.vcent = off;  off += align_up(sizeof(float) * S * Kc * kD);
+    w.cstat = off;  off += align_up(sizeof(float) * S * Kc * 2);
+    w.xpart = off;  off += nsplit > 1 ? align_up(sizeof(float) * S * nsplit * Kc * (kD + 2)) : 0;
+    w.dvc = off;    off += align_up(sizeof(float) * S * Kc * kD);
+    w.dmu = off;    off += align_up(sizeof(float) * S * Kc * kD);
+    w.lstat = off;  off += align_up(sizeof(float) * 4 * S * L);
+    w.dal = off;    off += align_up(sizeof(float) * S * ntile);
+    w.total = off;
+    return w;
+}
+
 // Checks shared by the single-step entry points.
 ca_status_t check_step(int S, int L, int d, int Kc, ca_dtype_t dt) {
     if (S < 1 || L < 1 || d < 1 || Kc < 1) return CA_ERR_INVALID_ARG;
@@ -290,6 +315,70 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
     }
     return forward_impl(Q, K, V, valid, G, flags, B, H, L, d, nclust, iters, W, alpha, out,
                         assign_out, dt, workspace, workspace_bytes, path, stream);
+}
+
+size_t cluster_attn_backward_workspace_size(int B, int H, int kv_heads, int L, int d,
+                                            int nclust, ca_dtype_t dt) {
+    if (check_shape(B, H, L, d, nclust, 1, 0, 0.f, dt) != CA_OK) return 0;
+    if (kv_heads < 0 || kv_heads > H || (kv_heads > 0 && H % kv_heads != 0)) return 0;
+    return bwd_layout((long)B * H, L, clusters(nclust, L)).total;
+}
+
+ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, const void *dO,
+                                  const int32_t *assign, const uint8_t *valid, int B, int H,
+                                  int kv_heads, int L, int d, int nclust, int W, float alpha,
+                                  void *dQ, void *dK, void *dV, float *dalpha, ca_dtype_t dt,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    ca_status_t st = check_shape(B, H, L, d, nclust, 1, W, alpha, dt);
+    if (st != CA_OK) return st;
+    if (kv_heads < 0 || kv_heads > H || (kv_heads > 0 && H % kv_heads != 0))
+        return CA_ERR_INVALID_ARG;
+    const int Hkv = kv_heads > 0 ? kv_heads : H;
+    if (!Q || !K || !V || !dO || !assign || !dQ || !dK || !dV || !workspace)
+        return CA_ERR_INVALID_ARG;
+    const void *p16[] = {Q, K, V, dO, dQ, dK, dV};
+    for (const void *p : p16)
+        if (!aligned(p, 16)) return CA_ERR_INVALID_ARG;
+    if (!aligned(assign, 4) || (dalpha && !aligned(dalpha, 4)) || !aligned(workspace, kAlign))
+        return CA_ERR_INVALID_ARG;
+    const long S = (long)B * H;
+    const int Kc = clusters(nclust, L);
+    const BwdLayout lay = bwd_layout(S, L, Kc);
+    if (workspace_bytes < lay.total) return CA_ERR_INVALID_ARG;
+    const size_t tb = (size_t)S * L * d * elem_bytes(dt), kvb = tb / (size_t)(H / Hkv);
+    const Span outs[] = {{dQ, tb}, {dK, kvb}, {dV, kvb}, {dalpha, sizeof(float)},
+                         {workspace, lay.total}};
+    if (any_overlap(outs, 5)) return CA_ERR_INVALID_ARG;
+    const Span ins[] = {{Q, tb}, {K, kvb}, {V, kvb}, {dO, tb}, {assign, sizeof(int32_t) * S * L},
+                        {valid, (size_t)B * L}};
+    for (const Span &o : outs)
+        for (const Span &i : ins)
+            if (o.p && i.p && overlap(o.p, o.n, i.p, i.n)) return CA_ERR_INVALID_ARG;
+
+    char *ws = static_cast<char *>(workspace);
+    float *mu = reinterpret_cast<float *>(ws + lay.mu);
+    int32_t *counts = reinterpret_cast<int32_t *>(ws + lay.counts);
+    float *part = reinterpret_cast<float *>(ws + lay.part);
+    int32_t *pcnt = reinterpret_cast<int32_t *>(ws + lay.pcnt);
+    float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
+    float *cstat = reinterpret_cast<float *>(ws + lay.cstat);
+    float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
+    // the forward's final means and centroid attention, from the given assignment
+    CA_TRY(launch_centroid_partials(Q, assign, (int)S, L, Kc, dt, part, pcnt, stream));
+    CA_TRY(launch_centroid_reduce(part, pcnt, kmeans_tiles(L), (int)S, Kc, mu, counts, stream));
+    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, H / Hkv, vcent, xpart,
+                                 stream, cstat));
+    BwdArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.assign = assign; a.valid = valid;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.L = L; a.Kc = Kc; a.r = W / 2; a.alpha = alpha;
+    a.mu = mu; a.counts = counts; a.vcent = vcent; a.cstat = cstat;
+    a.dvc = reinterpret_cast<float *>(ws + lay.dvc);
+    a.dmu = reinterpret_cast<float *>(ws + lay.dmu);
+    a.part = part;
+    a.lstat = reinterpret_cast<float4 *>(ws + lay.lstat);
+    a.dal = reinterpret_cast<float *>(ws + lay.dal);
+    a.dQ = dQ; a.dK = dK; a.dV = dV; a.dalpha = dalpha;
+    return hip_status(launch_backward(a, dt, stream));
 }
 
 ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d, int Kc,

@@ -133,9 +133,12 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
 int xattn_splits(int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
 // belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
+// stats (nullable, [S, Kc, 2]): per row the largest scaled logit and the sum
+// of exp(logit - largest).
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
-                                 float *vcent, float *partials, hipStream_t st);
+                                 float *vcent, float *partials, hipStream_t st,
+                                 float *stats = nullptr);
 
 // Window |i - j| <= r. With oloc == nullptr the gather + fusion epilogue
 // writes out; mu != nullptr selects the soft gather over the centroids mu.
@@ -146,6 +149,30 @@ hipError_t launch_local_window(const void *Q, const void *K, const void *V, int 
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);
+
+// Backward pass (backward.hip): buffers and sizes of one launch sequence.
+// Q, dO, dQ [B, H, L, 64]; K, V, dK, dV [B, Hkv, L, 64] (storage dtype);
+// assign [B, H, L]; the rest fp32 workspace: mu, vcent, dvc, dmu [S, Kc, 64],
+// counts [S, Kc], cstat [S, Kc, 2] (row max and sum of the centroid
+// softmax), part [S, tiles, Kc, 64], lstat [S, L] (max, sum, D, 0 of the
+// local softmax), dal [S * tiles]; dalpha (nullable) one float.
+struct BwdArgs {
+    const void *Q, *K, *V, *dO;
+    const int32_t *assign;
+    const uint8_t *valid;
+    int B, H, Hkv, L, Kc, r;
+    float alpha;
+    const float *mu;
+    const int32_t *counts;
+    const float *vcent, *cstat;
+    float *dvc, *dmu, *part;
+    float4 *lstat;
+    float *dal;
+    void *dQ, *dK, *dV;
+    float *dalpha;
+};
+int bwd_tiles(int L);
+hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
 
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,

@@ -13,6 +13,10 @@
 // Key-padding mask (optional; ClusterAttention listing on the
 // "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
 // a key with valid[b * L + j] == 0 takes the logit -10000 (b = s / H).
+//
+// stats (optional, [S, Kc, 2]): each row's largest scaled logit m and
+// sum_j exp(logit_j - m), which the backward pass uses to rebuild the
+// probabilities.
 #include "common.h"
 
 namespace ca {
@@ -40,7 +44,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     const float *__restrict__ mu, const T *__restrict__ Kx, const T *__restrict__ Vx, int L,
     int Kc, int nsplit, int kps, const uint8_t *__restrict__ valid, int H, int G,
-    float *__restrict__ vcent, float *__restrict__ part) {
+    float *__restrict__ vcent, float *__restrict__ part, float *__restrict__ stats) {
     __shared__ float sm_k[kKeyTile * kXPad];
     __shared__ float sm_v[kKeyTile * kXPad];
     __shared__ float sm_mu[kChunk * kXPad];
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
                 const float inv = 1.0f / l;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) vcent[k * kD + 4 * t + q] = acc[q] * inv;
+                if (stats && t == 0) { stats[2 * k] = m; stats[2 * k + 1] = l; }
             } else {
                 float *pp = part + ((s * nsplit + split) * (long)Kc + c0 + cl) * kPartStride;
 #pragma unroll
@@ -146,7 +151,8 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
 // sum e^(m_r-M) l_r.
 __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restrict__ part,
                                                             int nsplit, int Kc, long total,
-                                                            float *__restrict__ vcent) {
+                                                            float *__restrict__ vcent,
+                                                            float *__restrict__ stats) {
     const long e = (long)blockIdx.x * 256 + threadIdx.x;
     if (e >= total) return;
     const long sk = e / kD;           // s * Kc + k
@@ -163,33 +169,35 @@ __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restr
         den = fmaf(w, pp[kD + 1], den);
     }
     vcent[e] = num / den;
+    if (stats && j == 0) { stats[2 * sk] = M; stats[2 * sk + 1] = den; }
 }
 
 template <typename T>
 static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, const uint8_t *valid, int H, int G, float *vcent,
-                                 float *partials, hipStream_t st) {
+                                 float *partials, float *stats, hipStream_t st) {
     const int nsplit = xattn_splits(L);
     const int kps = keys_per_split(L, nsplit);
     const int used = (L + kps - 1) / kps;   // ranges that hold keys
     const dim3 grid((unsigned)((long)S * used)), block(256);
     hipLaunchKernelGGL(centroid_xattn_kernel<T>, grid, block, 0, st, mu,
                        static_cast<const T *>(K), static_cast<const T *>(V), L, Kc, used, kps,
-                       valid, H, G, vcent, partials);
+                       valid, H, G, vcent, partials, stats);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || used == 1) return err;
     const long total = (long)S * Kc * kD;
     hipLaunchKernelGGL(xattn_combine_kernel, dim3((unsigned)((total + 255) / 256)), block, 0, st,
-                       partials, used, Kc, total, vcent);
+                       partials, used, Kc, total, vcent, stats);
     return hipGetLastError();
 }
 
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
-                                 float *vcent, float *partials, hipStream_t st) {
+                                 float *vcent, float *partials, hipStream_t st, float *stats) {
     if (dt == CA_BF16)
-        return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, st);
-    return xattn_dispatch<float>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, st);
+        return xattn_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, stats,
+                                      st);
+    return xattn_dispatch<float>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, stats, st);
 }
 
 }  // namespace ca

@@ -214,3 +214,37 @@ def fwd_opts(opts, **kw):
 ])
 def test_opts_forward_rejects(opts, kw, code):
     assert fwd_opts(opts, **kw) == code
+
+
+def bwd(**kw):
+    a = dict(Q=Q, K=K, V=V, dO=OUT, assign=ASG, valid=None, B=2, H=4, Hkv=0, L=128, d=64,
+             nclust=16, W=32, alpha=0.5, dQ=WS + (1 << 28), dK=WS + (2 << 28), dV=WS + (3 << 28),
+             da=None, dt=b.CA_F32, ws=WS, wsb=1 << 27)
+    a.update(kw)
+    return b.lib().cluster_attn_backward(
+        a["Q"], a["K"], a["V"], a["dO"], a["assign"], a["valid"], a["B"], a["H"], a["Hkv"], a["L"],
+        a["d"], a["nclust"], a["W"], a["alpha"], a["dQ"], a["dK"], a["dV"], a["da"], a["dt"],
+        a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(dO=None), INV), (dict(assign=None), INV), (dict(dK=None), INV),
+    (dict(ws=None), INV), (dict(wsb=1024), INV), (dict(Hkv=3), INV), (dict(Hkv=8), INV),
+    (dict(Hkv=-1), INV), (dict(W=-1), INV), (dict(alpha=float("nan")), INV),
+    (dict(alpha=1.5), INV), (dict(dt=5), INV), (dict(B=0), INV),
+    (dict(Q=Q + 4), INV), (dict(assign=ASG + 2), INV), (dict(da=WS + (4 << 28) + 2), INV),
+    (dict(ws=WS + 64), INV),
+    (dict(dQ=Q), INV),                  # an output over an input
+    (dict(dK=WS + (1 << 28)), INV),     # two outputs over each other
+    (dict(d=32), UNS), (dict(nclust=300, L=300), UNS),
+])
+def test_backward_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_backward_workspace_size():
+    lib = b.lib()
+    n = lib.cluster_attn_backward_workspace_size(32, 12, 0, 128, 64, 16, b.CA_F32)
+    assert n > 0 and n % 256 == 0
+    assert lib.cluster_attn_backward_workspace_size(32, 12, 5, 128, 64, 16, b.CA_F32) == 0
+    assert lib.cluster_attn_backward_workspace_size(32, 12, 4, 128, 32, 16, b.CA_F32) == 0

@@ -1,0 +1,140 @@
+"""GPU parity of the backward pass (cluster_attn_backward) against the fp64
+oracle's backward, on the GPU forward's own final assignment.
+
+Gradients are compared element by element with a tolerance scaled by the
+largest reference magnitude of each tensor: |err| <= tol * max(1, max|ref|),
+tol = 1e-4 for fp32 storage and 2e-2 for bf16 (whose gradients are rounded
+to bf16 once). dalpha is a sum of B*H*L*64 products; it is compared within
+1e-5 of the sum of their magnitudes plus 1e-6 absolute.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from means_token_clustering_amd import inputs as gen
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {gen.F32: 1e-4, gen.BF16: 2e-2}
+
+
+def _b():
+    from means_token_clustering_amd import binding
+    return binding
+
+
+def _dev(a, dtype):
+    if dtype == gen.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _store(a64, dtype):
+    x32 = np.asarray(a64, dtype=np.float32)
+    return gen.f32_to_bf16_bits(x32) if dtype == gen.BF16 else x32
+
+
+def _vals(a, dtype):
+    return gen.bf16_bits_to_f32(a).astype(np.float64) if dtype == gen.BF16 else a.astype(np.float64)
+
+
+def _host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(B, H, Hkv, L, nclust, iters, W, alpha, dtype, seed, mask_kind=None, blobs=8):
+    b = _b()
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha, dtype=dtype,
+                        seed=seed, blobs=blobs)
+    kv = gen.make_inputs(B, Hkv, L, 64, dtype=dtype, seed=seed + 1) if Hkv != H else x
+    rng = np.random.default_rng(seed + 2)
+    dO = _store(rng.standard_normal((B, H, L, 64)), dtype)
+    mask = gen.make_mask(B, L, seed=seed + 3, kind=mask_kind) if mask_kind else None
+    _say(f"[backward] B={B} H={H} Hkv={Hkv} L={L} K={nclust} I={iters} W={W} a={alpha} "
+         f"{dtype} mask={mask_kind} seed={seed}")
+    q, k, v, go = _dev(x.q, dtype), _dev(kv.k, dtype), _dev(kv.v, dtype), _dev(dO, dtype)
+    vd = torch.from_numpy(mask).cuda() if mask is not None else None
+    _, c = b.cluster_attn_forward(q, k, v, nclust, iters, W, alpha, valid=vd)
+    dq, dk, dv, da = b.cluster_attn_backward(q, k, v, go, c, nclust, W, alpha, valid=vd)
+    torch.cuda.synchronize()
+    G = H // Hkv
+    Q = x.values("q")
+    Kr, Vr = oracle.repeat_kv(kv.values("k"), G), oracle.repeat_kv(kv.values("v"), G)
+    dO64 = _vals(dO, dtype)
+    Kc = oracle.num_clusters(nclust, L)
+    cc = c.cpu().numpy()
+    rq, rk, rv, ra = oracle.backward(Q, Kr, Vr, dO64, cc, Kc, W, alpha, valid=mask)
+    rk, rv = oracle.fold_kv(rk, G), oracle.fold_kv(rv, G)
+    tol = TOL[dtype]
+    errs = {}
+    for name, mine, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        err = float(np.abs(_host(mine) - ref).max())
+        bound = tol * max(1.0, float(np.abs(ref).max()))
+        errs[name] = (err, bound)
+    f = oracle.forward_from_assign(Q, Kr, Vr, cc, Kc, W, alpha, valid=mask)
+    gat = np.take_along_axis(f["vcent"], cc[..., None].astype(np.int64), axis=2)
+    keep = 1.0 if mask is None else np.broadcast_to(mask[:, None, :, None] != 0, dO64.shape)
+    mag = float(np.sum(np.abs(dO64 * keep * (f["oloc"] - gat))))
+    aerr = abs(float(da.item()) - ra)
+    _say("  " + "; ".join(f"{n} err={e:.3e} (bound {bd:.3e})" for n, (e, bd) in errs.items())
+         + f"; dalpha {float(da.item()):.6e} vs {ra:.6e}")
+    for n, (e, bd) in errs.items():
+        assert e <= bd, n
+    assert aerr <= 1e-5 * mag + 1e-6
+    return dq, dk, dv, da
+
+
+CASES = [  # B, H, Hkv, L, nclust, iters, W, alpha, dtype, seed, mask kind
+    (1, 2, 2, 128, 16, 3, 32, 0.5, gen.F32, 1, None),
+    (32, 12, 12, 128, 16, 3, 32, 0.5, gen.F32, 2, None),      # the distilbert shape
+    (2, 3, 3, 100, 16, 3, 32, 0.3, gen.F32, 3, "prefix"),    # ragged tiles, padded batch
+    (2, 2, 2, 128, 16, 3, 32, 0.5, gen.F32, 4, "holes"),
+    (2, 12, 4, 128, 16, 3, 32, 0.4, gen.F32, 5, None),        # grouped K/V heads
+    (2, 6, 3, 90, 8, 2, 70, 0.6, gen.BF16, 6, "holes"),       # bf16, wide window
+    (1, 2, 2, 200, 7, 4, 17, 0.3, gen.F32, 7, None),          # K not dividing L, odd W
+    (1, 2, 2, 150, 16, 3, 0, 0.5, gen.F32, 8, None),          # W = 0: self only
+    (1, 2, 2, 150, 16, 3, 400, 0.5, gen.F32, 9, None),        # dense local branch
+    (1, 3, 3, 96, 1, 3, 8, 0.5, gen.F32, 10, None),           # one cluster
+    (1, 2, 2, 40, 64, 2, 10, 0.5, gen.F32, 11, None),         # nclust > L: K = L
+    (1, 1, 1, 300, 256, 2, 32, 0.5, gen.F32, 12, None),       # the largest K
+    (1, 2, 2, 1100, 32, 3, 64, 0.5, gen.F32, 13, "prefix"),   # split-key centroid attention
+    (8, 12, 12, 512, 16, 3, 32, 0.5, gen.BF16, 14, None),     # the bf16 L = 512 shape
+    (1, 1, 1, 1, 16, 2, 32, 0.5, gen.F32, 15, None),          # a single token
+    (2, 2, 2, 128, 16, 3, 32, 0.0, gen.F32, 16, None),        # alpha = 0
+    (2, 2, 2, 128, 16, 3, 32, 1.0, gen.F32, 17, "holes"),     # alpha = 1
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_backward_matches_oracle(case):
+    run_case(*case)
+
+
+def test_backward_deterministic_and_all_padding():
+    b = _b()
+    dq1, dk1, dv1, da1 = run_case(2, 3, 3, 128, 16, 3, 32, 0.5, gen.F32, 20, None)
+    x = gen.make_inputs(2, 3, 128, 64, nclust=16, seed=20, blobs=8)
+    q, k, v = (_dev(getattr(x, n), gen.F32) for n in ("q", "k", "v"))
+    dO = _store(np.random.default_rng(22).standard_normal((2, 3, 128, 64)), gen.F32)
+    go = _dev(dO, gen.F32)
+    _, c = b.cluster_attn_forward(q, k, v, 16, 3, 32, 0.5)
+    r1 = b.cluster_attn_backward(q, k, v, go, c, 16, 32, 0.5)
+    r2 = b.cluster_attn_backward(q, k, v, go, c, 16, 32, 0.5)
+    torch.cuda.synchronize()
+    for t1, t2 in zip(r1, r2):
+        assert torch.equal(t1, t2)
+    # every token padded: no gradient reaches the output; K takes none either
+    zero = torch.zeros((2, 128), dtype=torch.uint8, device="cuda")
+    dq, dk, dv, da = b.cluster_attn_backward(q, k, v, go, c, 16, 32, 0.5, valid=zero)
+    torch.cuda.synchronize()
+    assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+    assert float(dv.abs().max()) == 0.0 and float(da.item()) == 0.0
