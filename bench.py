@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--flags", type=int, default=0,
                    help="listing-compatible variants, OR of CA_FLAG_* (15 = all four; "
                         "cluster_attn_forward_opts)")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (cluster_attn_backward) on the forward's "
+                        "assignment instead of the forward")
     return p.parse_args()
 
 
@@ -99,6 +102,102 @@ def cpu_baseline(x, seconds: float, mask=None, flags: int = 0):
                       f"back to back, {el:.1f} s, fp64 C oracle with OpenMP over slices"}
 
 
+def cpu_baseline_backward(x, seconds: float, mask=None):
+    import numpy as np
+    import oracle
+    q, k, v = x.values("q"), x.values("k"), x.values("v")
+    dO = np.random.default_rng(x.seed + 600).standard_normal(q.shape)
+    c = oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)["assign"]
+    K = oracle.num_clusters(x.nclust, x.L)
+    oracle.backward(q, k, v, dO, c, K, x.W, x.alpha, valid=mask)   # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.backward(q, k, v, dO, c, K, x.W, x.alpha, valid=mask)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": x.B * x.L * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the backward pass of the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}) "
+                      f"on the oracle's own assignment, {reps} times back to back, {el:.1f} s, "
+                      f"fp64 C oracle with OpenMP over slices"}
+
+
+def bench_backward(args, x, mask, b, gen, torch, np):
+    """A step is one backward pass (cluster_attn_backward) over the batch,
+    on the assignment of a forward run made before timing."""
+    elem = 2 if x.dtype == gen.BF16 else 4
+    dt = b.CA_BF16 if elem == 2 else b.CA_F32
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if x.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    n = x.B * x.H * x.L * x.d
+    set_bytes = 7 * n * elem + 4 * x.B * x.H * x.L + (mask.size if mask is not None else 0)
+    nsets = args.sets or max(2, MALL_BYTES // set_bytes + 2)
+    vdev = torch.from_numpy(mask).to(dev) if mask is not None else None
+    base = [to_dev(getattr(x, nm)) for nm in ("q", "k", "v")]
+    dO = torch.randn(base[0].shape, generator=torch.Generator().manual_seed(x.seed + 600))
+    dO = dO.to(base[0].dtype).to(dev)
+    sets = []
+    for _ in range(nsets):
+        q, k, v, g = (t.clone() for t in (*base, dO))
+        _, c = b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, valid=vdev)
+        sets.append((q, k, v, g, c, torch.empty_like(q), torch.empty_like(k),
+                     torch.empty_like(v), torch.empty(1, dtype=torch.float32, device=dev)))
+    need = b.lib().cluster_attn_backward_workspace_size(x.B, x.H, 0, x.L, x.d, x.nclust, dt)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wsp, wsn = b._aligned_ptr(ws), b._ws_bytes(ws)
+    lib = b.lib()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    vptr = vdev.data_ptr() if vdev is not None else None
+
+    def step(i):
+        q, k, v, g, c, dq, dk, dv, da = sets[i % nsets]
+        st = lib.cluster_attn_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                       c.data_ptr(), vptr, x.B, x.H, 0, x.L, x.d, x.nclust, x.W,
+                                       float(x.alpha), dq.data_ptr(), dk.data_ptr(),
+                                       dv.data_ptr(), da.data_ptr(), dt, wsp, wsn, sptr)
+        if st != b.CA_OK:
+            raise b.CaError(st, "cluster_attn_backward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    achieved = set_bytes / (ms / 1e3) / 1e9
+    rec = {"metric": "cluster-attention bwd tokens/s (B·L per s, all heads) + % HBM roofline",
+           "value": round(x.B * x.L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
+           "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d, "K": x.nclust,
+                      "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
+                      "pass": "backward", "input_sets": nsets},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "kernel": "backward sequence (10 launches)",
+                        "bytes_per_launch": set_bytes}}
+    if mask is not None:
+        rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "
+                                 f"{int(mask.sum())} of {mask.size} tokens real")
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_backward(x, args.cpu_seconds, mask)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -111,6 +210,10 @@ def main():
     from means_token_clustering_amd import inputs as gen
 
     x = gen.workload(args.workload)
+    if args.backward:
+        mask = gen.make_mask(x.B, x.L, seed=x.seed + 500) if args.masked else None
+        bench_backward(args, x, mask, b, gen, torch, np)
+        return
     elem = 2 if x.dtype == gen.BF16 else 4
     path = {"auto": b.CA_PATH_AUTO, "fused": b.CA_PATH_FUSED, "staged": b.CA_PATH_STAGED}[args.path]
     dev = torch.device("cuda:0")

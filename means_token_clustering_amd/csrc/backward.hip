@@ -38,14 +38,9 @@
 namespace ca {
 
 constexpr int kBT = 64;          // rows per tile
-constexpr int kBPad = kD + 1;    // LDS row stride
+constexpr int kBPad = kD + 1;    // LDS stride of rows that lanes read at different rows
+constexpr int kRow = kD;         // LDS stride of rows that a whole wave reads at once
 constexpr int kBChunk = 32;      // centroids per pass of the key kernel
-
-// sum over the four lanes 4q .. 4q+3 (every lane gets the same bits)
-__device__ __forceinline__ float quad_sum(float x) {
-    const float y = x + __shfl_xor(x, 1);
-    return y + __shfl_xor(y, 2);
-}
 
 template <typename T>
 __device__ __forceinline__ void load16(const T *p, float *x) {
@@ -125,8 +120,8 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
     const T *__restrict__ dO, const int32_t *__restrict__ assign, const float *__restrict__ vcent,
     const uint8_t *__restrict__ valid, int L, int r, int ntile, int Kc, float alpha, int H, int G,
     float4 *__restrict__ lstat, float *__restrict__ dal) {
-    __shared__ float sm_k[kBT * kBPad];
-    __shared__ float sm_v[kBT * kBPad];
+    __shared__ __align__(16) float sm_k[kBT * kRow];
+    __shared__ __align__(16) float sm_v[kBT * kRow];
     __shared__ float sm_s[kBT * kBPad];
     __shared__ uint8_t sm_ok[kBT];
     __shared__ float sm_red[kBT];
@@ -164,8 +159,8 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
             const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
             const float4 kv = load4<T>(Kx + kvbase + (long)(jt + rr) * kD + c4);
             const float4 vv = load4<T>(Vx + kvbase + (long)(jt + rr) * kD + c4);
-            float *dk = sm_k + rr * kBPad + c4;
-            float *dv = sm_v + rr * kBPad + c4;
+            float *dk = sm_k + rr * kRow + c4;
+            float *dv = sm_v + rr * kRow + c4;
             dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
             dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
         }
@@ -177,7 +172,7 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
         const int wb = wave_max_i32(b);
         float mt = -__builtin_inff();
         for (int key = wa; key <= wb; ++key) {
-            const float *kr = sm_k + key * kBPad + 16 * g;
+            const float *kr = sm_k + key * kRow + 16 * g;
             float part = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
@@ -198,7 +193,7 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
             for (int key = a; key <= b; ++key) {
                 const float p = exp_f32(sm_s[qi * kBPad + key] - mn);
                 l += p;
-                const float *vr = sm_v + key * kBPad + 16 * g;
+                const float *vr = sm_v + key * kRow + 16 * g;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, vr[c], acc[c]);
             }
@@ -248,9 +243,9 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
     const float4 *__restrict__ lstat, const uint8_t *__restrict__ valid, int L, int r, int ntile,
     int Kc, float alpha, int H, int G, T *__restrict__ dK, T *__restrict__ dV,
     float *__restrict__ dmu_part) {
-    __shared__ float sm_k[kBT * kBPad];       // this tile's keys (for dmu)
-    __shared__ float sm_a[kBT * kBPad];       // mu chunk, then query rows
-    __shared__ float sm_b[kBT * kBPad];       // dVc chunk, then alpha keep dO rows
+    __shared__ __align__(16) float sm_k[kBT * kRow];       // this tile's keys (for dmu)
+    __shared__ __align__(16) float sm_a[kBT * kRow];       // mu chunk, then query rows
+    __shared__ __align__(16) float sm_b[kBT * kRow];       // dVc chunk, then alpha keep dO rows
     __shared__ float sm_ds[kBChunk * kBT];    // dSc of the chunk [k][j]
     __shared__ float sm_st[kBT * 4];          // (m, l, D) per centroid or query
     __shared__ uint8_t sm_kok[kBT];
@@ -278,7 +273,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
     for (int e = tid; e < nk * (kD / 4); e += 256) {
         const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
         const float4 kv = load4<T>(Kx + kvbase + (long)(j0 + rr) * kD + c4);
-        float *dk = sm_k + rr * kBPad + c4;
+        float *dk = sm_k + rr * kRow + c4;
         dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
     }
     for (int rr = tid; rr < nk; rr += 256) sm_kok[rr] = token_ok(valid, bb, L, j0 + rr);
@@ -298,8 +293,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
                 const int k = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
                 const float4 mv = load4<float>(mu + (s * Kc + c0 + k) * kD + c4);
                 const float4 dv = load4<float>(dvc + (s * Kc + c0 + k) * kD + c4);
-                float *da = sm_a + k * kBPad + c4;
-                float *db = sm_b + k * kBPad + c4;
+                float *da = sm_a + k * kRow + c4;
+                float *db = sm_b + k * kRow + c4;
                 da[0] = mv.x; da[1] = mv.y; da[2] = mv.z; da[3] = mv.w;
                 db[0] = dv.x; db[1] = dv.y; db[2] = dv.z; db[3] = dv.w;
             }
@@ -313,19 +308,18 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
 #pragma unroll
                     for (int e = 0; e < 8; ++e) dd = fmaf(gc[e], vc[e], dd);
                 }
-                dd += __shfl_xor(dd, 1);
-                dd += __shfl_xor(dd, 2);
+                dd = quad_sum(dd);
                 dd += __shfl_xor(dd, 4);
                 if (k < ck && part == 0) {
                     sm_st[4 * k] = cstat[2 * (s * Kc + c0 + k)];
-                    sm_st[4 * k + 1] = cstat[2 * (s * Kc + c0 + k) + 1];
+                    sm_st[4 * k + 1] = 1.0f / cstat[2 * (s * Kc + c0 + k) + 1];
                     sm_st[4 * k + 2] = dd;
                 }
             }
             __syncthreads();
             for (int k = 0; k < ck; ++k) {
-                const float *mr = sm_a + k * kBPad + 16 * g;
-                const float *gr = sm_b + k * kBPad + 16 * g;
+                const float *mr = sm_a + k * kRow + 16 * g;
+                const float *gr = sm_b + k * kRow + 16 * g;
                 float ps = 0.f, pd = 0.f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
@@ -335,7 +329,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
                 const float dot = quad_sum(ps);   // every lane, before any select
                 const float dp = quad_sum(pd);
                 const float sc = kok ? dot * scale : -10000.f;
-                const float p = active ? exp_f32(sc - sm_st[4 * k]) / sm_st[4 * k + 1] : 0.f;
+                const float p = active ? exp_f32(sc - sm_st[4 * k]) * sm_st[4 * k + 1] : 0.f;
                 const float ds = kok ? p * (dp - sm_st[4 * k + 2]) * scale : 0.f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
@@ -349,7 +343,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
             for (int e = tid; e < ck * kD; e += 256) {
                 const int k = e / kD, t = e % kD;
                 float acc = 0.f;
-                for (int q = 0; q < nk; ++q) acc = fmaf(sm_ds[k * kBT + q], sm_k[q * kBPad + t], acc);
+                for (int q = 0; q < nk; ++q) acc = fmaf(sm_ds[k * kBT + q], sm_k[q * kRow + t], acc);
                 dmu_part[((s * ntile + tile) * (long)Kc + c0 + k) * kD + t] = acc;
             }
         }
@@ -363,15 +357,15 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
                 const float4 qv = load4<T>(Q + base + (long)(it + rr) * kD + c4);
                 const float4 gv4 = load4<T>(dO + base + (long)(it + rr) * kD + c4);
                 const float w = keep ? alpha : 0.f;
-                float *da = sm_a + rr * kBPad + c4;
-                float *db = sm_b + rr * kBPad + c4;
+                float *da = sm_a + rr * kRow + c4;
+                float *db = sm_b + rr * kRow + c4;
                 da[0] = qv.x; da[1] = qv.y; da[2] = qv.z; da[3] = qv.w;
                 db[0] = w * gv4.x; db[1] = w * gv4.y; db[2] = w * gv4.z; db[3] = w * gv4.w;
             }
             for (int rr = tid; rr < nq; rr += 256) {
                 const float4 st = lstat[s * L + it + rr];
                 sm_st[4 * rr] = st.x;
-                sm_st[4 * rr + 1] = st.y;
+                sm_st[4 * rr + 1] = 1.0f / st.y;
                 sm_st[4 * rr + 2] = st.z;
             }
             __syncthreads();
@@ -382,8 +376,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
             const int wa = wave_min_i32(aa < b + 1 ? aa : kBT);
             const int wb = wave_max_i32(b);
             for (int q = wa; q <= wb; ++q) {
-                const float *qr = sm_a + q * kBPad + 16 * g;
-                const float *gr = sm_b + q * kBPad + 16 * g;
+                const float *qr = sm_a + q * kRow + 16 * g;
+                const float *gr = sm_b + q * kRow + 16 * g;
                 float ps = 0.f, pd = 0.f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
@@ -394,7 +388,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
                 const float dp = quad_sum(pd);
                 const float sc = kok ? dot * scale : -10000.f;
                 if (q >= aa && q <= b) {
-                    const float p = exp_f32(sc - sm_st[4 * q]) / sm_st[4 * q + 1];
+                    const float p = exp_f32(sc - sm_st[4 * q]) * sm_st[4 * q + 1];
                     const float ds = kok ? p * (dp - sm_st[4 * q + 2]) * scale : 0.f;
 #pragma unroll
                     for (int c = 0; c < 16; ++c) {
@@ -419,8 +413,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
     const int32_t *__restrict__ counts, const float4 *__restrict__ lstat,
     const uint8_t *__restrict__ valid, int L, int r, int ntile, int Kc, float alpha, int H, int G,
     T *__restrict__ dQ) {
-    __shared__ float sm_k[kBT * kBPad];
-    __shared__ float sm_v[kBT * kBPad];
+    __shared__ __align__(16) float sm_k[kBT * kRow];
+    __shared__ __align__(16) float sm_v[kBT * kRow];
     __shared__ uint8_t sm_ok[kBT];
 
     const int tid = threadIdx.x;
@@ -461,8 +455,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
             const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
             const float4 kv = load4<T>(Kx + kvbase + (long)(jt + rr) * kD + c4);
             const float4 vv = load4<T>(Vx + kvbase + (long)(jt + rr) * kD + c4);
-            float *dk = sm_k + rr * kBPad + c4;
-            float *dv = sm_v + rr * kBPad + c4;
+            float *dk = sm_k + rr * kRow + c4;
+            float *dv = sm_v + rr * kRow + c4;
             dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
             dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
         }
@@ -473,8 +467,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         const int wa = wave_min_i32(a < b + 1 ? a : kBT);
         const int wb = wave_max_i32(b);
         for (int key = wa; key <= wb; ++key) {
-            const float *kk = sm_k + key * kBPad + 16 * g;
-            const float *vv = sm_v + key * kBPad + 16 * g;
+            const float *kk = sm_k + key * kRow + 16 * g;
+            const float *vv = sm_v + key * kRow + 16 * g;
             float ps = 0.f, pd = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) {

@@ -77,6 +77,15 @@ __device__ __forceinline__ bool lex_less(float a, int ia, float b, int ib) {
     return (a < b) || (a == b && ia < ib) || (b != b && a == a);
 }
 
+// Sum over the four lanes 4q .. 4q+3 through DPP quad permutes (no LDS
+// round trip); the adds are commutative, so all four lanes get the same bits.
+__device__ __forceinline__ float quad_sum(float x) {
+    const float y = x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                            __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    return y + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                   __builtin_bit_cast(int, y), 0x4E, 0xF, 0xF, false));            // [2,3,0,1]
+}
+
 // Wave-wide integer min / max (all 64 lanes must be active and converged).
 __device__ __forceinline__ int wave_min_i32(int v) {
 #pragma unroll

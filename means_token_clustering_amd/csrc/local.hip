@@ -30,7 +30,8 @@ namespace ca {
 
 constexpr int kQTile = 64;
 constexpr int kLTile = 64;
-constexpr int kLPad = kD + 1;
+constexpr int kLPad = kD + 1;   // LDS stride of the per-query score rows
+constexpr int kLRow = kD;       // LDS stride of K/V rows (a whole wave reads one row)
 
 template <typename T, bool FUSE, bool SOFT>
 __global__ __launch_bounds__(256) void local_window_kernel(
@@ -38,8 +39,8 @@ __global__ __launch_bounds__(256) void local_window_kernel(
     int ntile, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
     float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out,
     float *__restrict__ oloc, const float *__restrict__ mu) {
-    __shared__ float sm_k[kLTile * kLPad];
-    __shared__ float sm_v[kLTile * kLPad];
+    __shared__ __align__(16) float sm_k[kLTile * kLRow];
+    __shared__ __align__(16) float sm_v[kLTile * kLRow];
     __shared__ float sm_s[kQTile * kLPad];
     __shared__ uint8_t sm_ok[kLTile];
 
@@ -84,8 +85,8 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
             float4 kv = load4<T>(Kx + kvbase + (long)(jt + rr) * kD + c4);
             float4 vv = load4<T>(Vx + kvbase + (long)(jt + rr) * kD + c4);
-            float *dk = sm_k + rr * kLPad + c4;
-            float *dv = sm_v + rr * kLPad + c4;
+            float *dk = sm_k + rr * kLRow + c4;
+            float *dv = sm_v + rr * kLRow + c4;
             dk[0] = kv.x; dk[1] = kv.y; dk[2] = kv.z; dk[3] = kv.w;
             dv[0] = vv.x; dv[1] = vv.y; dv[2] = vv.z; dv[3] = vv.w;
         }
@@ -102,12 +103,11 @@ __global__ __launch_bounds__(256) void local_window_kernel(
         const int wb = wave_max_i32(b);
         float mt = -__builtin_inff();
         for (int key = wa; key <= wb; ++key) {
-            const float *kr = sm_k + key * kLPad + 16 * g;
+            const float *kr = sm_k + key * kLRow + 16 * g;
             float part = 0.f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
-            float sum2 = part + __shfl_xor(part, 1);
-            float sc = sum2 + __shfl_xor(sum2, 2);
+            float sc = quad_sum(part);
             if (!sm_ok[key]) sc = -10000.f;
             if (key >= a && key <= b) {
                 mt = fmaxf(mt, sc);
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             for (int key = a; key <= b; ++key) {
                 const float p = exp_f32(sm_s[qi * kLPad + key] - mn);
                 l += p;
-                const float *vr = sm_v + key * kLPad + 16 * g;
+                const float *vr = sm_v + key * kLRow + 16 * g;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) acc[c] = fmaf(p, vr[c], acc[c]);
             }
@@ -144,20 +144,19 @@ __global__ __launch_bounds__(256) void local_window_kernel(
                 const int rr = e / (kD / 4), c4 = (e % (kD / 4)) * 4;
                 const float4 mv = load4<float>(mu + (s * Kc + k0 + rr) * kD + c4);
                 const float4 gv = load4<float>(vcent + (s * Kc + k0 + rr) * kD + c4);
-                float *dm = sm_k + rr * kLPad + c4;
-                float *dg = sm_v + rr * kLPad + c4;
+                float *dm = sm_k + rr * kLRow + c4;
+                float *dg = sm_v + rr * kLRow + c4;
                 dm[0] = mv.x; dm[1] = mv.y; dm[2] = mv.z; dm[3] = mv.w;
                 dg[0] = gv.x; dg[1] = gv.y; dg[2] = gv.z; dg[3] = gv.w;
             }
             __syncthreads();
             float mt = -__builtin_inff();
             for (int k = 0; k < nk; ++k) {   // every lane runs every k: shuffles converge
-                const float *mr = sm_k + k * kLPad + 16 * g;
+                const float *mr = sm_k + k * kLRow + 16 * g;
                 float part = 0.f;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) part = fmaf(qr[c], mr[c], part);
-                const float sum2 = part + __shfl_xor(part, 1);
-                const float sc = sum2 + __shfl_xor(sum2, 2);
+                const float sc = quad_sum(part);
                 mt = fmaxf(mt, sc);
                 if (g == 0) sm_s[qi * kLPad + k] = sc;
             }
@@ -170,7 +169,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             for (int k = 0; k < nk; ++k) {
                 const float p = exp_f32(sm_s[qi * kLPad + k] - mn);
                 l2 += p;
-                const float *gr = sm_v + k * kLPad + 16 * g;
+                const float *gr = sm_v + k * kLRow + 16 * g;
 #pragma unroll
                 for (int c = 0; c < 16; ++c) gsoft[c] = fmaf(p, gr[c], gsoft[c]);
             }
