@@ -74,6 +74,7 @@ def _load():
                                                _dp, _dp, _dp, _dp, _dp]),
             "ora_backward": (None, [_dp, _dp, _dp, _dp, L, i, i, i, _ip, i, d, _ip,
                                     _dp, _dp, _dp, _dp]),
+            "ora_exact_attention": (None, [_dp, _dp, _dp, L, i, i, i, i, _ip, _ip, _dp]),
             "ora_matmul": (None, [_dp, _dp, L, L, L, _dp]),
             "ora_round_bf16": (d, [d]),
             "ora_round_bf16_array": (None, [_dp, L]),
@@ -290,6 +291,22 @@ def backward(Q, Kt, V, dO, c, K: int, W: int, alpha: float, valid=None):
     _load().ora_backward(_p(Q), _p(Kt), _p(V), _p(dO), S, L, d, K, _p(c), W, float(alpha),
                          _p(vm), _p(dQ), _p(dK), _p(dV), ctypes.byref(da))
     return dQ, dK, dV, da.value
+
+
+def exact_attention(Q, Kt, V, causal: bool, qvalid=None, kvalid=None) -> np.ndarray:
+    """Decoder / cross-attention branch: exact attention over all keys with the
+    -10000 fill for padded keys and (causal) future keys; padded queries give
+    zero rows. Q [B, H, L, d]; K, V [B, H, Nk, d]; qvalid [B, L] and kvalid
+    [B, Nk] (or per slice), nonzero = real token."""
+    Q, S, L, d = _slices(Q)
+    Kt, V = _f64(Kt), _f64(V)
+    Nk = Kt.shape[-2]
+    qm = _mask(qvalid, Q.shape[:-2], L)
+    km = _mask(kvalid, Q.shape[:-2], Nk)
+    out = np.empty(Q.shape)
+    _load().ora_exact_attention(_p(Q), _p(Kt), _p(V), S, L, Nk, d, int(bool(causal)), _p(qm),
+                                _p(km), _p(out))
+    return out
 
 
 def forward_from_assign(Q, Kt, V, c, K: int, W: int, alpha: float, valid=None,

@@ -594,6 +594,48 @@ void ora_backward(const double *Q, const double *Kt, const double *V, const doub
     *dalpha = total;
 }
 
+/*
+ * Exact attention of the decoder and cross-attention branch (the
+ * ClusterAttention listing on the svd-sst2-roberta-cluster page, forward,
+ * decoder / cross-attention branch; its "Architectural Support" section):
+ * no clustering; O_i = sum_j softmax_j(s_ij) v_j over all Nk keys with
+ * s_ij = q_i . k_j / sqrt(d), replaced by -10000 where key j is padded
+ * (kvalid[s, j] == 0) or, with causal, where j > i; a padded query's row
+ * (qvalid[s, i] == 0) is zero. Q [S, L, d]; K, V [S, Nk, d]; masks nullable.
+ */
+void ora_exact_attention(const double *Q, const double *Kt, const double *V, long S, int L,
+                         int Nk, int d, int causal, const int32_t *qvalid,
+                         const int32_t *kvalid, double *out) {
+    const double scale = 1.0 / sqrt((double)d);
+#pragma omp parallel for schedule(static)
+    for (long s = 0; s < S; ++s) {
+        double *e = (double *)malloc(sizeof(double) * (size_t)Nk);
+        for (int i = 0; i < L; ++i) {
+            const double *q = Q + (s * L + i) * (long)d;
+            double mx = -INFINITY;
+            for (int j = 0; j < Nk; ++j) {
+                const double *kr = Kt + (s * Nk + j) * (long)d;
+                double dot = 0.0;
+                for (int t = 0; t < d; ++t) dot += q[t] * kr[t];
+                const int masked = (kvalid && !kvalid[s * Nk + j]) || (causal && j > i);
+                e[j] = masked ? -10000.0 : dot * scale;
+                if (e[j] > mx) mx = e[j];
+            }
+            double z = 0.0;
+            for (int j = 0; j < Nk; ++j) z += (e[j] = exp(e[j] - mx));
+            double *o = out + (s * L + i) * (long)d;
+            for (int t = 0; t < d; ++t) o[t] = 0.0;
+            if (qvalid && !qvalid[s * L + i]) continue;
+            for (int j = 0; j < Nk; ++j) {
+                const double p = e[j] / z;
+                const double *vr = V + (s * Nk + j) * (long)d;
+                for (int t = 0; t < d; ++t) o[t] += p * vr[t];
+            }
+        }
+        free(e);
+    }
+}
+
 /* C = A B with A [M, P] and B [P, N], row-major, plain sums over p in order. */
 void ora_matmul(const double *A, const double *Bm, long M, long P, long N, double *C) {
 #pragma omp parallel for schedule(static)

@@ -711,3 +711,49 @@ def test_fold_kv_is_adjoint_of_repeat_kv():
         rhs = float(np.sum(a * oracle.fold_kv(b, G)))
         assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
     assert np.array_equal(oracle.fold_kv(a, 1), a)
+
+
+# ------------------------------------- P14: decoder / cross-attention branch
+# Exact attention of the ClusterAttention listing's decoder and cross-attention
+# branch (svd-sst2-roberta-cluster page): -10000 for padded and (causal)
+# future keys, zero rows for padded queries.
+def test_exact_attention_matches_library():
+    rng = np.random.default_rng(60)
+    q = rng.standard_normal((2, 3, 20, 8))
+    k = rng.standard_normal((2, 3, 20, 8))
+    v = rng.standard_normal((2, 3, 20, 8))
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    assert np.allclose(oracle.exact_attention(q, k, v, True), sdpa(tq, tk, tv, is_causal=True).numpy(),
+                       atol=1e-13)
+    # cross-attention: 13 keys, no causal mask
+    k2, v2 = k[:, :, :13], v[:, :, :13]
+    assert np.allclose(oracle.exact_attention(q, k2, v2, False),
+                       sdpa(tq, torch.from_numpy(k2), torch.from_numpy(v2)).numpy(), atol=1e-13)
+    # key mask with key 0 real: every causal row keeps a real key, so the fill
+    # equals exclusion
+    km = (rng.random((2, 20)) < 0.6).astype(np.int32)
+    km[:, 0] = 1
+    allowed = torch.from_numpy(np.tril(np.ones((20, 20), bool))[None, None] & (km[:, None, None, :] != 0))
+    assert np.allclose(oracle.exact_attention(q, k, v, True, kvalid=km),
+                       sdpa(tq, tk, tv, attn_mask=allowed).numpy(), atol=1e-13)
+
+
+def test_exact_attention_fill_and_query_rows():
+    rng = np.random.default_rng(61)
+    q = rng.standard_normal((1, 2, 10, 8))
+    k = rng.standard_normal((1, 2, 10, 8))
+    v = rng.standard_normal((1, 2, 10, 8))
+    km = np.ones((1, 10), np.int32)
+    km[0, :4] = 0   # rows 0..3 see only padded keys among j <= i
+    qm = np.ones((1, 10), np.int32)
+    qm[0, 7] = 0
+    o = oracle.exact_attention(q, k, v, True, qvalid=qm, kvalid=km)
+    # every logit of rows 0..3 is -10000: uniform over all ten keys, future ones included
+    for i in range(4):
+        assert np.allclose(o[0, :, i], v[0].mean(axis=1), atol=1e-14)
+    assert np.all(o[0, :, 7] == 0.0)
+    # row 5 sees keys 4, 5 only
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[:, :, 5:6]), torch.from_numpy(k[:, :, 4:6]), torch.from_numpy(v[:, :, 4:6])).numpy()
+    assert np.allclose(o[:, :, 5:6], want, atol=1e-13)
