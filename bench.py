@@ -76,6 +76,9 @@ def parse():
     p.add_argument("--flags", type=int, default=0,
                    help="listing-compatible variants, OR of CA_FLAG_* (15 = all four; "
                         "cluster_attn_forward_opts)")
+    p.add_argument("--decoder", action="store_true",
+                   help="time the decoder branch (cluster_attn_exact_forward, causal exact "
+                        "attention) instead of the clustering forward")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (cluster_attn_backward) on the forward's "
                         "assignment instead of the forward")
@@ -198,6 +201,76 @@ def bench_backward(args, x, mask, b, gen, torch, np):
     print(json.dumps(rec), flush=True)
 
 
+def bench_decoder(args, x, mask, b, gen, torch, np):
+    """A step is one causal exact attention (the decoder branch) over the batch."""
+    elem = 2 if x.dtype == gen.BF16 else 4
+    dt = b.CA_BF16 if elem == 2 else b.CA_F32
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if x.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    n = x.B * x.H * x.L * x.d
+    set_bytes = 4 * n * elem + (2 * mask.size if mask is not None else 0)
+    nsets = args.sets or max(2, MALL_BYTES // set_bytes + 2)
+    vdev = torch.from_numpy(mask).to(dev) if mask is not None else None
+    vptr = vdev.data_ptr() if vdev is not None else None
+    base = [to_dev(getattr(x, nm)) for nm in ("q", "k", "v")]
+    sets = [(*(t.clone() for t in base), torch.empty_like(base[0])) for _ in range(nsets)]
+    lib = b.lib()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(i):
+        q, k, v, o = sets[i % nsets]
+        st = lib.cluster_attn_exact_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), vptr, vptr,
+                                            x.B, x.H, 0, x.L, x.L, x.d, 1, o.data_ptr(), dt, sptr)
+        if st != b.CA_OK:
+            raise b.CaError(st, "cluster_attn_exact_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    achieved = set_bytes / (ms / 1e3) / 1e9
+    rec = {"metric": "causal exact attention (decoder branch) tokens/s + % HBM roofline",
+           "value": round(x.B * x.L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
+           "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d,
+                      "storage": x.dtype, "pass": "decoder", "input_sets": nsets},
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": None, "kernel": "exact_attn_kernel",
+                        "bytes_per_launch": set_bytes}}
+    if args.cpu_seconds > 0:
+        import oracle
+        q, k, v = x.values("q"), x.values("k"), x.values("v")
+        oracle.exact_attention(q, k, v, True, qvalid=mask, kvalid=mask)
+        reps, c0 = 0, time.perf_counter()
+        while True:
+            oracle.exact_attention(q, k, v, True, qvalid=mask, kvalid=mask)
+            reps += 1
+            el = time.perf_counter() - c0
+            if el >= args.cpu_seconds:
+                break
+        rec["cpu_baseline"] = {"value": x.B * x.L * reps / el, "unit": "tokens/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"causal exact attention of the whole {x.name} batch, "
+                                         f"{reps} times back to back, {el:.1f} s, fp64 C oracle"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,9 +283,9 @@ def main():
     from means_token_clustering_amd import inputs as gen
 
     x = gen.workload(args.workload)
-    if args.backward:
+    if args.backward or args.decoder:
         mask = gen.make_mask(x.B, x.L, seed=x.seed + 500) if args.masked else None
-        bench_backward(args, x, mask, b, gen, torch, np)
+        (bench_backward if args.backward else bench_decoder)(args, x, mask, b, gen, torch, np)
         return
     elem = 2 if x.dtype == gen.BF16 else 4
     path = {"auto": b.CA_PATH_AUTO, "fused": b.CA_PATH_FUSED, "staged": b.CA_PATH_STAGED}[args.path]

@@ -224,6 +224,29 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
                                   void *dQ, void *dK, void *dV, float *dalpha, ca_dtype_t dt,
                                   void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Exact attention of the decoder and cross-attention branch: the
+ * ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page
+ * sends causal decoders and cross-attention to exact attention instead of
+ * clustering ("Architectural Support" section; forward, decoder branch).
+ *   out_i = sum_j softmax_j(s_ij) v_j over all Nk keys, s_ij = q_i . k_j /
+ *   sqrt(d), replaced by -10000 where key j is padded (k_valid) or, with
+ *   causal != 0, where j > i; the row of a padded query (q_valid) is zero.
+ *   The -10000 is a fill: a row whose allowed keys are all padded is uniform
+ *   over all Nk keys.
+ *   Q, out    device, [B, H, L, d], dtype dt.
+ *   K, V      device, [B, kv_heads, Nk, d] (kv_heads 0 means H; query head h
+ *             reads K/V head h / (H / kv_heads)).
+ *   q_valid   nullable device uint8 [B, L]; k_valid nullable [B, Nk];
+ *             nonzero = real token (for self-attention pass one mask twice).
+ * d = 64. Needs no workspace. out must not overlap the inputs. Errors are
+ * caught on the host before any launch.
+ */
+ca_status_t cluster_attn_exact_forward(const void *Q, const void *K, const void *V,
+                                       const uint8_t *q_valid, const uint8_t *k_valid, int B,
+                                       int H, int kv_heads, int L, int Nk, int d, int causal,
+                                       void *out, ca_dtype_t dt, hipStream_t stream);
+
 /* ---------------------------------------------------------------------
  * Single steps (one kernel each), for callers composing their own loop and
  * for step-by-step checking. S = B*H slices; Kc = number of centroids.

@@ -56,6 +56,8 @@ SIGNATURES = {
     "cluster_attn_layer_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                         _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ca_gemm_bf16": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "cluster_attn_exact_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp,
+                                        _i, _vp]),
     "cluster_attn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "cluster_attn_backward": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                    _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -233,6 +235,24 @@ def cluster_attn_backward(Q, K, V, dO, assign, nclust: int, W: int, alpha: float
         _ws_bytes(ws), _stream(stream))
     _check(st, "cluster_attn_backward")
     return dQ, dK, dV, da
+
+
+def cluster_attn_exact_forward(Q, K, V, causal: bool, q_valid=None, k_valid=None, out=None,
+                               stream=None):
+    """Exact attention of the decoder / cross-attention branch. Q: [B, H, L, d];
+    K, V: [B, Hkv, Nk, d]; q_valid [B, L] and k_valid [B, Nk] one-byte masks or
+    None. Returns out [B, H, L, d]."""
+    torch = _torch()
+    B, H, L, d = Q.shape
+    hkv, Nk = K.shape[1], K.shape[2]
+    if tuple(V.shape) != tuple(K.shape):
+        raise ValueError("K and V must share a shape")
+    out = torch.empty_like(Q) if out is None else out
+    st = lib().cluster_attn_exact_forward(_ptr(Q), _ptr(K), _ptr(V), _ptr(q_valid), _ptr(k_valid),
+                                          B, H, hkv, L, Nk, d, int(bool(causal)), _ptr(out),
+                                          _dtype_code(Q), _stream(stream))
+    _check(st, "cluster_attn_exact_forward")
+    return out
 
 
 def ca_kmeans_assign(Q, mu, Kc: int, assign=None, stream=None):

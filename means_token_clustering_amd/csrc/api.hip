@@ -381,6 +381,34 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
     return hip_status(launch_backward(a, dt, stream));
 }
 
+ca_status_t cluster_attn_exact_forward(const void *Q, const void *K, const void *V,
+                                       const uint8_t *q_valid, const uint8_t *k_valid, int B,
+                                       int H, int kv_heads, int L, int Nk, int d, int causal,
+                                       void *out, ca_dtype_t dt, hipStream_t stream) {
+    if (B < 1 || H < 1 || L < 1 || Nk < 1 || d < 1) return CA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return CA_ERR_INVALID_ARG;
+    if (dt != CA_F32 && dt != CA_BF16) return CA_ERR_INVALID_ARG;
+    if (kv_heads < 0 || kv_heads > H || (kv_heads > 0 && H % kv_heads != 0))
+        return CA_ERR_INVALID_ARG;
+    if ((long long)B * H * L * d > (1LL << 40) || (long long)B * H * Nk * d > (1LL << 40))
+        return CA_ERR_INVALID_ARG;
+    if ((long long)B * H * L > (1LL << 31) - 1 || (long long)B * H * Nk > (1LL << 31) - 1)
+        return CA_ERR_UNSUPPORTED;
+    if (d != kD) return CA_ERR_UNSUPPORTED;
+    if (!Q || !K || !V || !out) return CA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(out, 16))
+        return CA_ERR_INVALID_ARG;
+    const int Hkv = kv_heads > 0 ? kv_heads : H;
+    const size_t e = elem_bytes(dt);
+    const size_t qb = (size_t)B * H * L * d * e, kb = (size_t)B * Hkv * Nk * d * e;
+    const Span ins[] = {{Q, qb}, {K, kb}, {V, kb}, {q_valid, (size_t)B * L},
+                        {k_valid, (size_t)B * Nk}};
+    for (const Span &i : ins)
+        if (i.p && overlap(out, qb, i.p, i.n)) return CA_ERR_INVALID_ARG;
+    return hip_status(launch_exact_attention(Q, K, V, B * H, L, Nk, causal != 0, dt, q_valid,
+                                             k_valid, H, H / Hkv, out, stream));
+}
+
 ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d, int Kc,
                              ca_dtype_t dt, int32_t *assign, hipStream_t stream) {
     ca_status_t st = check_step(S, L, d, Kc, dt);

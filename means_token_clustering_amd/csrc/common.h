@@ -183,6 +183,13 @@ struct BwdArgs {
 int bwd_tiles(int L);
 hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
 
+// Exact attention (decoder / cross-attention branch): Q [S, L, 64], K, V
+// [S / G, Nk, 64] (grouped heads as in kv_slice); qvalid [S / H, L], kvalid
+// [S / H, Nk] nullable.
+hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int S, int L,
+                                  int Nk, bool causal, ca_dtype_t dt, const uint8_t *qvalid,
+                                  const uint8_t *kvalid, int H, int G, void *out, hipStream_t st);
+
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int radius, float alpha, const Variant &var,

@@ -248,3 +248,21 @@ def test_backward_workspace_size():
     assert n > 0 and n % 256 == 0
     assert lib.cluster_attn_backward_workspace_size(32, 12, 5, 128, 64, 16, b.CA_F32) == 0
     assert lib.cluster_attn_backward_workspace_size(32, 12, 4, 128, 32, 16, b.CA_F32) == 0
+
+
+def exact(**kw):
+    a = dict(Q=Q, K=K, V=V, qv=None, kv=None, B=2, H=4, Hkv=0, L=128, Nk=128, d=64, causal=1,
+             out=OUT, dt=b.CA_F32)
+    a.update(kw)
+    return b.lib().cluster_attn_exact_forward(a["Q"], a["K"], a["V"], a["qv"], a["kv"], a["B"],
+                                              a["H"], a["Hkv"], a["L"], a["Nk"], a["d"],
+                                              a["causal"], a["out"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), INV), (dict(out=None), INV), (dict(causal=2), INV), (dict(Nk=0), INV),
+    (dict(L=0), INV), (dict(Hkv=3), INV), (dict(dt=9), INV), (dict(Q=Q + 8), INV),
+    (dict(out=Q), INV), (dict(qv=OUT + 64), INV), (dict(d=128), UNS),
+])
+def test_exact_rejects(kw, code):
+    assert exact(**kw) == code

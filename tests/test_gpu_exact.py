@@ -1,0 +1,94 @@
+"""GPU parity of the decoder / cross-attention branch (cluster_attn_exact_forward)
+against the fp64 oracle's exact attention: outputs within 1e-4 (fp32 storage)
+or 2e-2 (bf16), padded query rows exactly zero."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from means_token_clustering_amd import inputs as gen
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = {gen.F32: 1e-4, gen.BF16: 2e-2}
+
+
+def _dev(a, dtype):
+    if dtype == gen.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run(B, H, Hkv, L, Nk, causal, dtype, seed, qkind=None, kkind=None, kmask=None):
+    from means_token_clustering_amd import binding as b
+    x = gen.make_inputs(B, H, L, 64, dtype=dtype, seed=seed, blobs=8)
+    kv = gen.make_inputs(B, Hkv, Nk, 64, dtype=dtype, seed=seed + 1)
+    qm = gen.make_mask(B, L, seed=seed + 2, kind=qkind) if qkind else None
+    km = kmask if kmask is not None else (gen.make_mask(B, Nk, seed=seed + 3, kind=kkind)
+                                          if kkind else None)
+    _say(f"[exact] B={B} H={H} Hkv={Hkv} L={L} Nk={Nk} causal={causal} {dtype} q={qkind} "
+         f"k={kkind if kmask is None else 'given'} seed={seed}")
+    q, k, v = _dev(x.q, dtype), _dev(kv.k, dtype), _dev(kv.v, dtype)
+    qd = torch.from_numpy(qm).cuda() if qm is not None else None
+    kd = torch.from_numpy(np.ascontiguousarray(km, dtype=np.uint8)).cuda() if km is not None else None
+    out = b.cluster_attn_exact_forward(q, k, v, causal, q_valid=qd, k_valid=kd)
+    torch.cuda.synchronize()
+    G = H // Hkv
+    ref = oracle.exact_attention(x.values("q"), oracle.repeat_kv(kv.values("k"), G),
+                                 oracle.repeat_kv(kv.values("v"), G), causal, qvalid=qm, kvalid=km)
+    got = out.float().cpu().numpy().astype(np.float64)
+    err = float(np.abs(got - ref).max())
+    _say(f"  max|out-ref|={err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+    if qm is not None:
+        pad = np.broadcast_to((qm == 0)[:, None, :, None], got.shape)
+        assert np.all(got[pad] == 0.0)
+    return got, ref
+
+
+CASES = [  # B, H, Hkv, L, Nk, causal, dtype, seed, q mask, k mask
+    (32, 12, 12, 128, 128, True, gen.F32, 1, None, None),      # the distilbert shape, causal
+    (2, 3, 3, 100, 77, False, gen.F32, 2, None, "holes"),     # cross-attention, ragged
+    (2, 4, 4, 128, 128, True, gen.F32, 3, "prefix", "prefix"),
+    (2, 12, 4, 128, 128, True, gen.F32, 4, None, None),       # grouped K/V heads
+    (2, 6, 2, 90, 300, False, gen.BF16, 5, "holes", "holes"),
+    (1, 2, 2, 1100, 1100, True, gen.F32, 6, None, "holes"),   # many key tiles
+    (1, 2, 2, 200, 70, True, gen.F32, 7, None, None),         # L > Nk: late rows see every key
+    (1, 2, 2, 1, 1, True, gen.F32, 8, None, None),
+    (1, 1, 1, 5, 300, False, gen.F32, 9, None, None),
+    (8, 12, 12, 512, 512, True, gen.BF16, 10, None, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_exact_matches_oracle(case):
+    run(*case)
+
+
+def test_exact_rows_of_padded_keys_are_uniform_over_all_keys():
+    """Keys 0..69 padded: causal rows 0..69 see padded keys alone, so all 200
+    logits are -10000 and the row is the mean of every V row (the second
+    pass over the later keys)."""
+    km = np.ones((1, 200), np.uint8)
+    km[0, :70] = 0
+    got, ref = run(1, 2, 2, 200, 200, True, gen.F32, 11, kmask=km)
+    x = gen.make_inputs(1, 2, 200, 64, seed=12)
+    assert np.allclose(ref[0, :, 5], x.values("v")[0].mean(axis=1), atol=1e-12)
+
+
+def test_exact_bf16_causal_is_self_consistent():
+    """The first causal row attends to key 0 alone: its output is v_0."""
+    from means_token_clustering_amd import binding as b
+    x = gen.make_inputs(1, 2, 64, 64, dtype=gen.BF16, seed=13)
+    q, k, v = (_dev(getattr(x, n), gen.BF16) for n in ("q", "k", "v"))
+    out = b.cluster_attn_exact_forward(q, k, v, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :, 0], v[:, :, 0])
