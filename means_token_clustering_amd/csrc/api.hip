@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "common.h"
+#include "launch.h"
 
 namespace {
 

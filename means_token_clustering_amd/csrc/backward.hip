@@ -33,7 +33,7 @@
 // Arithmetic is fp32 (the storage dtype is read and written); four lanes
 // share a row, each holding 16 of its 64 dims, and meet through two
 // butterfly adds, as in the forward's staged kernels.
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 

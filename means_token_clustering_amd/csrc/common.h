@@ -105,105 +105,3 @@ __device__ __forceinline__ float exp_f32(float x) {
 }
 
 }  // namespace ca
-
-// Host-side launch helpers live in the .hip files; declared here so the
-// C-ABI translation unit can call them.
-namespace ca {
-
-// Listing-compatible variants of the clustering and the gather (the
-// ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page,
-// its k-means routine and forward).
-struct Variant {
-    int init_step;     // 0: initial rows floor(k L / Kc); > 0: rows k * init_step
-    bool keep_empty;   // an empty cluster keeps its previous centroid (else zero)
-    bool soft;         // gather sum_k softmax_k(q . mu_k / sqrt(d)) V^cent_k
-};
-
-// Row of Q that initialises cluster k (increasing in k, below L for Kc <= L).
-__host__ __device__ inline int init_row(int k, int L, int Kc, int init_step) {
-    return init_step > 0 ? k * init_step : (int)(((long)k * L) / Kc);
-}
-
-// mu == nullptr: the centroids are the initial rows of Q (init_row with
-// init_step); mu_init, if not null, then receives them.
-hipError_t launch_kmeans_assign(const void *Q, const float *mu, int S, int L, int Kc,
-                                ca_dtype_t dt, int32_t *assign, float *part_sum,
-                                int32_t *part_cnt, hipStream_t st, int init_step = 0,
-                                float *mu_init = nullptr);
-hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S, int L, int Kc,
-                                    ca_dtype_t dt, float *part_sum, int32_t *part_cnt,
-                                    hipStream_t st);
-int kmeans_tiles(int L);
-// keep_empty: an empty cluster leaves its row of mu as it was
-hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt, int nblk,
-                                  int S, int Kc, float *mu, int32_t *counts, hipStream_t st,
-                                  bool keep_empty = false);
-
-int xattn_splits(int L);
-// valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
-// belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
-// stats (nullable, [S, Kc, 2]): per row the largest scaled logit and the sum
-// of exp(logit - largest).
-hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
-                                 int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
-                                 float *vcent, float *partials, hipStream_t st,
-                                 float *stats = nullptr);
-
-// Window |i - j| <= r. With oloc == nullptr the gather + fusion epilogue
-// writes out; mu != nullptr selects the soft gather over the centroids mu.
-hipError_t launch_local_window(const void *Q, const void *K, const void *V, int S, int L, int r,
-                               ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
-                               float alpha, const uint8_t *valid, int H, int G, void *out,
-                               float *oloc, hipStream_t st, const float *mu = nullptr);
-hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
-                              int L, int Kc, float alpha, ca_dtype_t dt, void *out,
-                              hipStream_t st);
-
-// Backward pass (backward.hip): buffers and sizes of one launch sequence.
-// Q, dO, dQ [B, H, L, 64]; K, V, dK, dV [B, Hkv, L, 64] (storage dtype);
-// assign [B, H, L]; the rest fp32 workspace: mu, vcent, dvc, dmu [S, Kc, 64],
-// counts [S, Kc], cstat [S, Kc, 2] (row max and sum of the centroid
-// softmax), part [S, tiles, Kc, 64], lstat [S, L] (max, sum, D, 0 of the
-// local softmax), dal [S * tiles]; dalpha (nullable) one float.
-struct BwdArgs {
-    const void *Q, *K, *V, *dO;
-    const int32_t *assign;
-    const uint8_t *valid;
-    int B, H, Hkv, L, Kc, r;
-    float alpha;
-    const float *mu;
-    const int32_t *counts;
-    const float *vcent, *cstat;
-    float *dvc, *dmu, *part;
-    float4 *lstat;
-    float *dal;
-    void *dQ, *dK, *dV;
-    float *dalpha;
-};
-int bwd_tiles(int L);
-hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
-
-// Exact attention (decoder / cross-attention branch): Q [S, L, 64], K, V
-// [S / G, Nk, 64] (grouped heads as in kv_slice); qvalid [S / H, L], kvalid
-// [S / H, Nk] nullable.
-hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, int S, int L,
-                                  int Nk, bool causal, ca_dtype_t dt, const uint8_t *qvalid,
-                                  const uint8_t *kvalid, int H, int G, void *out, hipStream_t st);
-
-bool fused_supported(int L, int Kc);
-hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
-                                int iters, int radius, float alpha, const Variant &var,
-                                ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
-                                int32_t *assign, hipStream_t st);
-
-// C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
-// A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as
-// [B, H, L, 64] from [B*L, 64 H]. N and K multiples of 64.
-hipError_t launch_gemm_nt(const uint16_t *A, const uint16_t *const *Bt, uint16_t *const *C,
-                          int count, int M, int N, int K, bool a_heads, bool c_heads, int L, int H,
-                          hipStream_t st);
-// dst[z] = src[z]^T for z < count; src [R, Cc], R and Cc multiples of 64.
-hipError_t launch_transpose_bf16(const uint16_t *const *src, uint16_t *const *dst, int count,
-                                 int R, int Cc, hipStream_t st);
-
-}  // namespace ca

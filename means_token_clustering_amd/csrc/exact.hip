@@ -15,7 +15,7 @@
 // A causal tile stops at its last query; a second pass over the later keys
 // runs only if some query of the tile saw padded keys alone (every later
 // key then weighs exactly as much as those).
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 

@@ -50,7 +50,7 @@
 // the centroid context). Q, K, V live in LDS as fp16 h/m planes [128][64]
 // with 16-byte chunks XOR-swizzled by the row; V takes the place of Q once
 // the clustering is done.
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 namespace {

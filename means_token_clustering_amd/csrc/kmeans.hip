@@ -13,7 +13,7 @@
 // The same workgroup emits its tile's per-cluster partial sums in token
 // order; a second kernel adds the tiles' partials in tile order. No float
 // atomics anywhere, so the result is bitwise reproducible.
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 

@@ -21,7 +21,7 @@
 // row 16a + 4j + r is stored at LDS row 16j + 4a + r, so that the 16 x 16
 // result blocks j = 0..3 of a wave leave each lane with 16 consecutive output
 // columns (two 16-byte stores per row).
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 namespace {

@@ -24,7 +24,7 @@
 // Soft gather (the same listing's forward): with mu given, the gathered
 // context of query i is sum_k softmax_k(q_i . mu_k / sqrt(d)) vcent_k,
 // folded in 64-centroid chunks staged through LDS with an online softmax.
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 

@@ -17,7 +17,7 @@
 // stats (optional, [S, Kc, 2]): each row's largest scaled logit m and
 // sum_j exp(logit_j - m), which the backward pass uses to rebuild the
 // probabilities.
-#include "common.h"
+#include "launch.h"
 
 namespace ca {
 
