@@ -251,7 +251,8 @@ def bench_decoder(args, x, mask, b, gen, torch, np):
                       "storage": x.dtype, "pass": "decoder", "input_sets": nsets},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "kernel": "exact_attn_kernel",
+                        "traffic": None,
+                        "kernel": "exact_fused_kernel" if x.L <= 128 else "exact_attn_kernel",
                         "bytes_per_launch": set_bytes}}
     if args.cpu_seconds > 0:
         import oracle

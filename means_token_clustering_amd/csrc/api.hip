@@ -405,6 +405,10 @@ ca_status_t cluster_attn_exact_forward(const void *Q, const void *K, const void 
                         {k_valid, (size_t)B * Nk}};
     for (const Span &i : ins)
         if (i.p && overlap(out, qb, i.p, i.n)) return CA_ERR_INVALID_ARG;
+    // single launch when the future-key exclusion equals the listing's fill
+    if (exact_fused_supported(L, Nk) && (!causal || !k_valid || k_valid == q_valid))
+        return hip_status(launch_exact_fused(Q, K, V, B * H, L, causal != 0, dt, q_valid, k_valid,
+                                             H, H / Hkv, out, stream));
     return hip_status(launch_exact_attention(Q, K, V, B * H, L, Nk, causal != 0, dt, q_valid,
                                              k_valid, H, H / Hkv, out, stream));
 }

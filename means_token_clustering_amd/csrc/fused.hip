@@ -446,13 +446,14 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 // Local window of any radius: key tiles in [qt - ceil(r/16), qt + ceil(r/16)]
 // two at a time with a running maximum (online softmax) and 32-deep P V
 // products; a missing second tile gets zero weights on repeated V rows.
-template <bool FULL, bool MASKED>
+// CAUSAL: the window is keys 0 .. qi instead (rad unused).
+template <bool FULL, bool MASKED, bool CAUSAL = false>
 __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                            int qt, int NT, int L, int rad, float sscale2,
                                            int l16, int g, int rl64, int trv, const KeyBits &kb,
                                            f32x4_t *o, float &lsum) {
     const int qi = 16 * qt + l16;
-    const int lo_key = 16 * qt - rad, hi_key = 16 * qt + 15 + rad;
+    const int lo_key = CAUSAL ? 0 : 16 * qt - rad, hi_key = CAUSAL ? 16 * qt + 15 : 16 * qt + 15 + rad;
     const int kt_lo = lo_key < 0 ? 0 : (lo_key >> 4);
     const int kt_hi = (hi_key >> 4) < NT - 1 ? (hi_key >> 4) : NT - 1;
     float M = -__builtin_inff(), ls = 0.f;
@@ -472,7 +473,8 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
             for (int rr = 0; rr < 4; ++rr) {
                 const int key = 16 * ktt + 4 * g + rr;
                 const int dist = key > qi ? key - qi : qi - key;
-                const bool in = (FULL || key < L) && dist <= rad && (h == 0 || two);
+                const bool in = (FULL || key < L) && (CAUSAL ? key <= qi : dist <= rad) &&
+                                (h == 0 || two);
                 const float sv = (!MASKED || ((nib >> rr) & 1u)) ? a[rr] * sscale2 : kPadLogit2;
                 s[4 * h + rr] = in ? sv : -__builtin_inff();
                 mt = fmaxf(mt, s[4 * h + rr]);
@@ -996,6 +998,190 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         }
     }
     if (assign_out && tid < L) __builtin_nontemporal_store(sC[tid], assign_out + slice * L + tid);
+}
+
+// Exact attention of one slice (the decoder / cross-attention branch of the
+// ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page)
+// for L = Nk <= 128: the forward kernel's loads, range scaling, fp16 split
+// planes and wide local window, with the window [0, qi] (CAUSAL) or every key,
+// and no clustering. Padded keys take the -10000 logit; padded query rows are
+// zero. With CAUSAL the future keys are excluded rather than filled, which is
+// the same result whenever every real query has a real key at or before it
+// (the host routes other masks to the staged kernel).
+constexpr int kXOffV = 2 * kPlane;                 // K planes, then V planes
+constexpr int kXOffMax = kXOffV + 2 * kPlane;
+constexpr int kXLds = kXOffMax + 8 * 4 * 4;
+
+template <typename T, bool FULL, bool CAUSAL, bool MASKED>
+__global__ __launch_bounds__(kThreads, 4) void exact_fused_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
+    const uint8_t *__restrict__ qvalid, const uint8_t *__restrict__ kvalid, int H, int G,
+    T *__restrict__ out) {
+    __shared__ __align__(16) unsigned char smem[kXLds];
+    uint16_t *sK = reinterpret_cast<uint16_t *>(smem);
+    uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kXOffV);
+    uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kXOffMax);
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const long slice = blockIdx.x;
+    if (slice >= S) return;
+    const int NT = FULL ? 8 : (L + 15) >> 4;
+    const int tok = 16 * w + l16;
+    const long base = slice * (long)L * kD;
+    const long kvbase = kv_slice(slice, H, G) * (long)L * kD;
+    const long brow = (slice / H) * (long)L;
+    const LaneOffs lo = lane_offsets(l16, g);
+    const int trv = 1024 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
+
+    float qraw[2][8], kraw[2][8], vraw[2][8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Kx + kvbase, it >> 3, L, (it & 7) * 8, kraw[n]);
+        load_row8<T, FULL>(Vx + kvbase, it >> 3, L, (it & 7) * 8, vraw[n]);
+    }
+    bool tok_ok = false;
+    if (MASKED && w < 2) {
+        const int t = 64 * w + lane;
+        tok_ok = t < L && (kvalid == nullptr || kvalid[brow + t] != 0);
+    }
+    {
+        const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
+        const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        if (lane == 0) {
+            sMax[4 * w] = bq;
+            sMax[4 * w + 1] = bk;
+            sMax[4 * w + 2] = bv;
+        }
+    }
+    if (MASKED && w < 2) {   // key mask words 2w, 2w+1 into the spare slots
+        const uint64_t bits = __ballot(tok_ok);
+        if (lane == 0) {
+            sMax[4 * (2 * w) + 3] = (uint32_t)bits;
+            sMax[4 * (2 * w + 1) + 3] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+    KeyBits kb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[4 * k + 3]) : ~0u;
+    uint32_t mq = 0, mk = 0, mv = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+        mq = max(mq, sMax[4 * ww]);
+        mk = max(mk, sMax[4 * ww + 1]);
+        mv = max(mv, sMax[4 * ww + 2]);
+    }
+    const int sq = scale_shift(mq, kQLimit), sk = scale_shift(mk, kKVLimit);
+    const int sv = scale_shift(mv, kKVLimit);
+    const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk);
+    const float fv = __builtin_ldexpf(1.f, -sv);
+    Sp8 qf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;   // exact power-of-two scaling
+        qf[c] = split8(x);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        const int o = off64(it >> 3, (it & 7) * 8);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = kraw[n][i] * fk;
+        const Sp8 kp = split8(x);
+        st16(sK + o, kp.h);
+        st16(sK + kPlaneE + o, kp.m);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = vraw[n][i] * fv;
+        const Sp8 vp = split8(x);
+        st16(sV + o, vp.h);
+        st16(sV + kPlaneE + o, vp.m);
+    }
+    __syncthreads();
+    const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
+    f32x4_t o[4];
+    float lsum = 1.f;
+    if (FULL || w < NT)
+        local_wide<FULL, MASKED, CAUSAL>(smem, smem + kXOffV, qf, w, NT, L, L, sscale2, l16, g,
+                                         lo.rl64, trv, kb, o, lsum);
+    __syncthreads();   // K planes are dead: they stage the output rows
+    constexpr int kRowB = kD * (int)sizeof(T);
+    constexpr int kCpr = kRowB / 16;
+    u8 *stg = smem + w * 16 * kRowB;
+    if (FULL || w < NT) {
+        const bool keep = !MASKED || qvalid == nullptr || tok >= L || qvalid[brow + tok] != 0;
+        const float f = keep ? __builtin_ldexpf(1.f, sv) * __builtin_amdgcn_rcpf(lsum) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int byte = (16 * j + 4 * g) * (int)sizeof(T);
+            u8 *p = stg + l16 * kRowB + ((((byte >> 4) ^ (l16 & (kCpr - 1)))) << 4) + (byte & 15);
+            const float v0 = o[j][0] * f, v1 = o[j][1] * f, v2 = o[j][2] * f, v3 = o[j][3] * f;
+            if (sizeof(T) == 4) {
+                *reinterpret_cast<f32x4_t *>(p) = f32x4_t{v0, v1, v2, v3};
+            } else {
+                *reinterpret_cast<u32x2_t *>(p) =
+                    u32x2_t{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                            (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        u8 *dst = reinterpret_cast<u8 *>(out + base + (long)16 * w * kD);
+#pragma unroll
+        for (int i = 0; i < kCpr / 4; ++i) {
+            const int flat = 64 * i + lane;
+            const int row = flat / kCpr, c = flat % kCpr;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(
+                stg + row * kRowB + (((c ^ (row & (kCpr - 1)))) << 4));
+            if (FULL || 16 * w + row < L)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + flat * 16));
+        }
+    }
+}
+
+bool exact_fused_supported(int L, int Nk) { return L == Nk && L >= 1 && L <= kFL; }
+
+template <typename T, bool CAUSAL, bool MASKED>
+static hipError_t exact_fused_launch_t(const void *Q, const void *K, const void *V, int S, int L,
+                                       const uint8_t *qvalid, const uint8_t *kvalid, int H, int G,
+                                       void *out, hipStream_t st) {
+    const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K);
+    const T *v = static_cast<const T *>(V);
+    if (L == kFL)
+        hipLaunchKernelGGL((exact_fused_kernel<T, true, CAUSAL, MASKED>), dim3((unsigned)S),
+                           dim3(kThreads), 0, st, q, k, v, S, L, qvalid, kvalid, H, G,
+                           static_cast<T *>(out));
+    else
+        hipLaunchKernelGGL((exact_fused_kernel<T, false, CAUSAL, MASKED>), dim3((unsigned)S),
+                           dim3(kThreads), 0, st, q, k, v, S, L, qvalid, kvalid, H, G,
+                           static_cast<T *>(out));
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t exact_fused_dispatch(const void *Q, const void *K, const void *V, int S, int L,
+                                       bool causal, const uint8_t *qvalid, const uint8_t *kvalid,
+                                       int H, int G, void *out, hipStream_t st) {
+    const bool masked = qvalid != nullptr || kvalid != nullptr;
+    if (causal)
+        return masked ? exact_fused_launch_t<T, true, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st)
+                      : exact_fused_launch_t<T, true, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st);
+    return masked ? exact_fused_launch_t<T, false, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st)
+                  : exact_fused_launch_t<T, false, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st);
+}
+
+hipError_t launch_exact_fused(const void *Q, const void *K, const void *V, int S, int L,
+                              bool causal, ca_dtype_t dt, const uint8_t *qvalid,
+                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st) {
+    if (dt == CA_BF16)
+        return exact_fused_dispatch<bf16_t>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st);
+    return exact_fused_dispatch<float>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st);
 }
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }

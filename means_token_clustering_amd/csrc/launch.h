@@ -89,6 +89,14 @@ hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, i
                                   int Nk, bool causal, ca_dtype_t dt, const uint8_t *qvalid,
                                   const uint8_t *kvalid, int H, int G, void *out, hipStream_t st);
 
+// Single-launch exact attention for L = Nk <= 128 (fused.hip); the host sends
+// a causal launch here only when every real query has a real key at or
+// before it (no key mask, or the query mask itself).
+bool exact_fused_supported(int L, int Nk);
+hipError_t launch_exact_fused(const void *Q, const void *K, const void *V, int S, int L,
+                              bool causal, ca_dtype_t dt, const uint8_t *qvalid,
+                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st);
+
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int radius, float alpha, const Variant &var,

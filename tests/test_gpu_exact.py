@@ -27,18 +27,24 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def run(B, H, Hkv, L, Nk, causal, dtype, seed, qkind=None, kkind=None, kmask=None):
+def run(B, H, Hkv, L, Nk, causal, dtype, seed, qkind=None, kkind=None, kmask=None, shared=False):
+    """shared: one mask for queries and keys, passed as the same tensor (the
+    single-launch path takes causal masked calls only then)."""
     from means_token_clustering_amd import binding as b
     x = gen.make_inputs(B, H, L, 64, dtype=dtype, seed=seed, blobs=8)
     kv = gen.make_inputs(B, Hkv, Nk, 64, dtype=dtype, seed=seed + 1)
     qm = gen.make_mask(B, L, seed=seed + 2, kind=qkind) if qkind else None
     km = kmask if kmask is not None else (gen.make_mask(B, Nk, seed=seed + 3, kind=kkind)
                                           if kkind else None)
+    if shared:
+        km = qm
     _say(f"[exact] B={B} H={H} Hkv={Hkv} L={L} Nk={Nk} causal={causal} {dtype} q={qkind} "
          f"k={kkind if kmask is None else 'given'} seed={seed}")
     q, k, v = _dev(x.q, dtype), _dev(kv.k, dtype), _dev(kv.v, dtype)
     qd = torch.from_numpy(qm).cuda() if qm is not None else None
     kd = torch.from_numpy(np.ascontiguousarray(km, dtype=np.uint8)).cuda() if km is not None else None
+    if shared:
+        kd = qd
     out = b.cluster_attn_exact_forward(q, k, v, causal, q_valid=qd, k_valid=kd)
     torch.cuda.synchronize()
     G = H // Hkv
@@ -66,6 +72,25 @@ CASES = [  # B, H, Hkv, L, Nk, causal, dtype, seed, q mask, k mask
     (1, 1, 1, 5, 300, False, gen.F32, 9, None, None),
     (8, 12, 12, 512, 512, True, gen.BF16, 10, None, None),
 ]
+
+# L = Nk <= 128 runs as a single launch (the forward kernel's machinery)
+FUSED = [  # B, H, Hkv, L, causal, dtype, seed, mask kind (shared by queries and keys)
+    (2, 3, 3, 100, True, gen.F32, 20, None),          # partial tiles
+    (2, 4, 4, 128, True, gen.F32, 21, "prefix"),
+    (2, 4, 4, 128, True, gen.F32, 22, "holes"),
+    (2, 4, 4, 128, False, gen.F32, 23, "holes"),
+    (2, 3, 3, 77, False, gen.BF16, 24, None),
+    (4, 12, 12, 128, True, gen.BF16, 25, "prefix"),
+    (2, 12, 3, 128, True, gen.F32, 26, None),          # grouped K/V heads
+    (1, 2, 2, 17, True, gen.F32, 27, "holes"),
+    (2, 2, 2, 128, True, gen.F32, 28, "zeros"),        # every row padded: zero output
+]
+
+
+@pytest.mark.parametrize("case", FUSED)
+def test_exact_single_launch_matches_oracle(case):
+    B, H, Hkv, L, causal, dtype, seed, kind = case
+    run(B, H, Hkv, L, L, causal, dtype, seed, qkind=kind, shared=kind is not None)
 
 
 @pytest.mark.parametrize("case", CASES)
