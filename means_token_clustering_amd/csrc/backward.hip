@@ -173,10 +173,7 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
         float mt = -__builtin_inff();
         for (int key = wa; key <= wb; ++key) {
             const float *kr = sm_k + key * kRow + 16 * g;
-            float part = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
-            float sc = quad_sum(part);
+            float sc = quad_sum(dot16(qr, kr));
             if (!sm_ok[key]) sc = -10000.f;
             if (key >= a && key <= b) {
                 mt = fmaxf(mt, sc);
@@ -246,7 +243,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
     __shared__ __align__(16) float sm_k[kBT * kRow];       // this tile's keys (for dmu)
     __shared__ __align__(16) float sm_a[kBT * kRow];       // mu chunk, then query rows
     __shared__ __align__(16) float sm_b[kBT * kRow];       // dVc chunk, then alpha keep dO rows
-    __shared__ float sm_ds[kBChunk * kBT];    // dSc of the chunk [k][j]
+    __shared__ __align__(16) float sm_ds[kBChunk * kBT];   // dSc of the chunk [k][j]
     __shared__ float sm_st[kBT * 4];          // (m, l, D) per centroid or query
     __shared__ uint8_t sm_kok[kBT];
 
@@ -320,14 +317,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
             for (int k = 0; k < ck; ++k) {
                 const float *mr = sm_a + k * kRow + 16 * g;
                 const float *gr = sm_b + k * kRow + 16 * g;
-                float ps = 0.f, pd = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    ps = fmaf(mr[c], kr[c], ps);
-                    pd = fmaf(gr[c], vr[c], pd);
-                }
-                const float dot = quad_sum(ps);   // every lane, before any select
-                const float dp = quad_sum(pd);
+                const float dot = quad_sum(dot16(mr, kr));   // every lane, before any select
+                const float dp = quad_sum(dot16(gr, vr));
                 const float sc = kok ? dot * scale : -10000.f;
                 const float p = active ? exp_f32(sc - sm_st[4 * k]) * sm_st[4 * k + 1] : 0.f;
                 const float ds = kok ? p * (dp - sm_st[4 * k + 2]) * scale : 0.f;
@@ -339,12 +330,33 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
                 if (g == 0) sm_ds[k * kBT + jl] = ds;   // 0 for keys past the tile
             }
             __syncthreads();
-            // dmu partial of the chunk: [k][t] = sum_j ds[k][j] k_j[t]
-            for (int e = tid; e < ck * kD; e += 256) {
-                const int k = e / kD, t = e % kD;
-                float acc = 0.f;
-                for (int q = 0; q < nk; ++q) acc = fmaf(sm_ds[k * kBT + q], sm_k[q * kRow + t], acc);
-                dmu_part[((s * ntile + tile) * (long)Kc + c0 + k) * kD + t] = acc;
+            // dmu partial of the chunk: [k][t] = sum_j ds[k][j] k_j[t]. Lane t
+            // of wave kw sums clusters kw, kw + 4, ...: one read of K feeds all
+            // of them, and the wave reads each ds row four keys at a time
+            // (ds is 0 for keys past the tile).
+            {
+                const int t = tid & (kD - 1), kw = tid >> 6;
+                float acc[kBChunk / 4];
+#pragma unroll
+                for (int u = 0; u < kBChunk / 4; ++u) acc[u] = 0.f;
+                for (int q = 0; q < nk; q += 4) {
+                    float kq[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kq[i] = q + i < nk ? sm_k[(q + i) * kRow + t] : 0.f;
+#pragma unroll
+                    for (int u = 0; u < kBChunk / 4; ++u) {
+                        if (kw + 4 * u < ck) {
+                            const float4 d4 =
+                                *reinterpret_cast<const float4 *>(sm_ds + (kw + 4 * u) * kBT + q);
+                            acc[u] = fmaf(d4.w, kq[3], fmaf(d4.z, kq[2],
+                                          fmaf(d4.y, kq[1], fmaf(d4.x, kq[0], acc[u]))));
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kBChunk / 4; ++u)
+                    if (kw + 4 * u < ck)
+                        dmu_part[((s * ntile + tile) * (long)Kc + c0 + kw + 4 * u) * kD + t] = acc[u];
             }
         }
         // ------------------------------------------ local branch
@@ -378,14 +390,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
             for (int q = wa; q <= wb; ++q) {
                 const float *qr = sm_a + q * kRow + 16 * g;
                 const float *gr = sm_b + q * kRow + 16 * g;
-                float ps = 0.f, pd = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    ps = fmaf(qr[c], kr[c], ps);
-                    pd = fmaf(gr[c], vr[c], pd);
-                }
-                const float dot = quad_sum(ps);
-                const float dp = quad_sum(pd);
+                const float dot = quad_sum(dot16(qr, kr));
+                const float dp = quad_sum(dot16(gr, vr));
                 const float sc = kok ? dot * scale : -10000.f;
                 if (q >= aa && q <= b) {
                     const float p = exp_f32(sc - sm_st[4 * q]) * sm_st[4 * q + 1];
@@ -469,14 +475,8 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(
         for (int key = wa; key <= wb; ++key) {
             const float *kk = sm_k + key * kRow + 16 * g;
             const float *vv = sm_v + key * kRow + 16 * g;
-            float ps = 0.f, pd = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                ps = fmaf(qr[c], kk[c], ps);
-                pd = fmaf(gr[c], vv[c], pd);
-            }
-            const float sc = quad_sum(ps);
-            const float dp = quad_sum(pd);
+            const float sc = quad_sum(dot16(qr, kk));
+            const float dp = quad_sum(dot16(gr, vv));
             if (key >= a && key <= b && sm_ok[key]) {
                 const float p = exp_f32(sc - m) * inv;
                 const float ds = p * (dp - D) * scale;

@@ -86,10 +86,7 @@ __global__ __launch_bounds__(256) void exact_attn_kernel(
             float mt = -__builtin_inff();
             for (int key = wa; key <= wb; ++key) {
                 const float *kr = sm_k + key * kERow + 16 * g;
-                float part = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
-                float sc = quad_sum(part);
+                float sc = quad_sum(dot16(qr, kr));
                 if (!sm_ok[key]) sc = -10000.f;
                 if (key >= a && key <= bb) {
                     mt = fmaxf(mt, sc);

@@ -89,8 +89,7 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
             const float *q = sm_q + t * kPad;
             for (int k = g; k < Kc; k += 4) {
                 const float *m = sm_mu + k * kPad;
-                float dot = 0.f;
-                for (int j = 0; j < kD; ++j) dot = fmaf(q[j], m[j], dot);
+                const float dot = dot64(q, m);
                 const float D = fmaf(-2.f, dot, sm_mn[k]);
                 if (lex_less(D, k, best, bk)) { best = D; bk = k; }
             }

@@ -3,7 +3,7 @@
 // unit (api.hip) can call it. Device helpers live in common.h.
 #pragma once
 
-#include "common.h"
+#include "staged.h"
 
 // Host-side launch helpers live in the .hip files; declared here so the
 // C-ABI translation unit can call them.

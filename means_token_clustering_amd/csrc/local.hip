@@ -104,10 +104,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
         float mt = -__builtin_inff();
         for (int key = wa; key <= wb; ++key) {
             const float *kr = sm_k + key * kLRow + 16 * g;
-            float part = 0.f;
-#pragma unroll
-            for (int c = 0; c < 16; ++c) part = fmaf(qr[c], kr[c], part);
-            float sc = quad_sum(part);
+            float sc = quad_sum(dot16(qr, kr));
             if (!sm_ok[key]) sc = -10000.f;
             if (key >= a && key <= b) {
                 mt = fmaxf(mt, sc);
@@ -153,10 +150,7 @@ __global__ __launch_bounds__(256) void local_window_kernel(
             float mt = -__builtin_inff();
             for (int k = 0; k < nk; ++k) {   // every lane runs every k: shuffles converge
                 const float *mr = sm_k + k * kLRow + 16 * g;
-                float part = 0.f;
-#pragma unroll
-                for (int c = 0; c < 16; ++c) part = fmaf(qr[c], mr[c], part);
-                const float sc = quad_sum(part);
+                const float sc = quad_sum(dot16(qr, mr));
                 mt = fmaxf(mt, sc);
                 if (g == 0) sm_s[qi * kLPad + k] = sc;
             }

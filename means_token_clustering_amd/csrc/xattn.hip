@@ -96,8 +96,7 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
                 const int key = t + 16 * u;
                 if (key < nk && cl < ck) {
                     const float *kr = sm_k + key * kXPad;
-                    float dot = 0.f;
-                    for (int j = 0; j < kD; ++j) dot = fmaf(mr[j], kr[j], dot);
+                    const float dot = dot64(mr, kr);
                     sc[u] = sm_ok[key] ? dot * scale : -10000.f;
                 } else {
                     sc[u] = -__builtin_inff();
