@@ -344,6 +344,8 @@ def test_grouped_kv_heads(case, path):
 # ---------------------------------------------------------------- listing-compatible variants
 LF = oracle.LISTING
 LISTING = [  # B, H, L, nclust, iters, W, alpha, dtype, flags, mask kind (None: no mask)
+    (32, 12, 128, 16, 3, 32, 0.5, gen.F32, LF, "prefix"),      # the distilbert batch, padded
+    (8, 12, 512, 16, 3, 32, 0.5, gen.BF16, LF, None),          # the bf16 L = 512 batch
     (2, 12, 128, 16, 3, 16, 0.5, gen.F32, LF, None),           # band radius 16, single launch
     (2, 4, 120, 16, 3, 40, 0.5, gen.F32, LF, None),            # step rows differ from floor(kL/K)
     (2, 4, 100, 16, 3, 8, 0.3, gen.BF16, LF, "holes"),
