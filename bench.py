@@ -39,6 +39,7 @@ TRAFFIC = {"workload": "distilbert", "bytes": 50_637_287,
            "read_kib": 36_970.5, "write_kib": 12_480.0,
            "digest": "067446303fa8e29add575498717607489f92bf0b9ec01e558a652cb945a812cb"}
 KERNEL_SOURCES = ("means_token_clustering_amd/csrc/fused.hip",   # device code only
+                  "means_token_clustering_amd/csrc/mfma_split.h",
                   "means_token_clustering_amd/csrc/common.h")
 
 
@@ -191,7 +192,7 @@ def bench_backward(args, x, mask, b, gen, torch, np):
                       "pass": "backward", "input_sets": nsets},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": None, "kernel": "backward sequence (10 launches)",
+                        "traffic": None, "kernel": "backward launch sequence",
                         "bytes_per_launch": set_bytes}}
     if mask is not None:
         rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "

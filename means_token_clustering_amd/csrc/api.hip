@@ -165,7 +165,7 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
 
 // Workspace of the backward pass, carved in this order (each 256-B aligned).
 struct BwdLayout {
-    size_t mu, counts, part, pcnt, vcent, cstat, xpart, dvc, dmu, lstat, dal, total;
+    size_t mu, counts, part, pcnt, vcent, cstat, xpart, dvc, dmu, lstat, dal, dkc, dvl, total;
 };
 
 BwdLayout bwd_layout(long S, int L, int Kc) {
@@ -184,6 +184,8 @@ BwdLayout bwd_layout(long S, int L, int Kc) {
     w.dmu = off;    off += align_up(sizeof(float) * S * Kc * kD);
     w.lstat = off;  off += align_up(sizeof(float) * 4 * S * L);
     w.dal = off;    off += align_up(sizeof(float) * S * ntile);
+    w.dkc = off;    off += align_up(sizeof(float) * S * L * kD);
+    w.dvl = off;    off += align_up(sizeof(float) * S * L * kD);
     w.total = off;
     return w;
 }
@@ -378,6 +380,8 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
     a.lstat = reinterpret_cast<float4 *>(ws + lay.lstat);
     a.dal = reinterpret_cast<float *>(ws + lay.dal);
     a.dQ = dQ; a.dK = dK; a.dV = dV; a.dalpha = dalpha;
+    a.dkc = reinterpret_cast<float *>(ws + lay.dkc);
+    a.dvl = reinterpret_cast<float *>(ws + lay.dvl);
     return hip_status(launch_backward(a, dt, stream));
 }
 

@@ -33,6 +33,8 @@
 // Arithmetic is fp32 (the storage dtype is read and written); four lanes
 // share a row, each holding 16 of its 64 dims, and meet through two
 // butterfly adds, as in the forward's staged kernels.
+#include <type_traits>
+
 #include "launch.h"
 
 namespace ca {
@@ -231,14 +233,15 @@ __global__ __launch_bounds__(256) void bwd_query_stats_kernel(
 // key j0 + j. For each query head sharing the K/V slice: the centroid branch
 // (all clusters, in chunks of 32) and the local branch (every query whose
 // window holds a key of the tile). dmu_part[s, tile, k, :] receives the
-// tile's sum_j dSc_kj k_j / 8 for query slice s.
-template <typename T>
+// tile's sum_j dSc_kj k_j / 8 for query slice s. Without LOCAL only the
+// centroid branch runs and dK, dV (of type TO) hold its share alone.
+template <typename T, bool LOCAL, typename TO>
 __global__ __launch_bounds__(256) void bwd_key_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx,
     const T *__restrict__ dO, const float *__restrict__ mu, const float *__restrict__ vcent,
     const float *__restrict__ cstat, const float *__restrict__ dvc,
     const float4 *__restrict__ lstat, const uint8_t *__restrict__ valid, int L, int r, int ntile,
-    int Kc, float alpha, int H, int G, T *__restrict__ dK, T *__restrict__ dV,
+    int Kc, float alpha, int H, int G, TO *__restrict__ dK, TO *__restrict__ dV,
     float *__restrict__ dmu_part) {
     __shared__ __align__(16) float sm_k[kBT * kRow];       // this tile's keys (for dmu)
     __shared__ __align__(16) float sm_a[kBT * kRow];       // mu chunk, then query rows
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(
             }
         }
         // ------------------------------------------ local branch
-        for (int it = qlo; it < qhi; it += kBT) {
+        for (int it = qlo; LOCAL && it < qhi; it += kBT) {
             const int nq = min(kBT, qhi - it);
             __syncthreads();
             for (int e = tid; e < nq * (kD / 4); e += 256) {
@@ -513,8 +516,43 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const float *__restrict__ 
 // ---------------------------------------------------------------- host side
 int bwd_tiles(int L) { return (L + kBT - 1) / kBT; }
 
+// The sequence with the local branch in one launch per slice (L <= 128, one
+// query head per K/V head): dVc, the centroid branch's dK, dV shares (fp32)
+// and dmu partials, dmu, then bwd_local_fused_kernel for dQ, dK, dV and the
+// slices' dalpha shares.
+template <typename T>
+static hipError_t bwd_dispatch_fused(const BwdArgs &a, hipStream_t st) {
+    const int ntile = bwd_tiles(a.L);
+    const long S = (long)a.B * a.H;
+    const T *Q = static_cast<const T *>(a.Q), *K = static_cast<const T *>(a.K);
+    const T *V = static_cast<const T *>(a.V), *dO = static_cast<const T *>(a.dO);
+    const dim3 block(256);
+    const size_t lds = sizeof(float) * ((size_t)kBT * kBPad + (size_t)a.Kc * kD) + sizeof(int) * kBT;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_cluster_sum_kernel<T>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_cluster_sum_kernel<T>, dim3((unsigned)(S * ntile)), block, lds, st, dO,
+                       a.assign, a.valid, a.L, a.Kc, a.H, ntile, a.part);
+    const long total = S * a.Kc * kD;
+    const dim3 rgrid((unsigned)((total + 255) / 256));
+    hipLaunchKernelGGL(bwd_partial_reduce_kernel, rgrid, block, 0, st, a.part, ntile, a.Kc, total,
+                       1.0f - a.alpha, a.dvc);
+    hipLaunchKernelGGL((bwd_key_kernel<T, false, float>), dim3((unsigned)(S * ntile)), block, 0, st,
+                       Q, K, V, dO, a.mu, a.vcent, a.cstat, a.dvc, a.lstat, a.valid, a.L, a.r,
+                       ntile, a.Kc, a.alpha, a.H, 1, a.dkc, a.dvl, a.part);
+    hipLaunchKernelGGL(bwd_partial_reduce_kernel, rgrid, block, 0, st, a.part, ntile, a.Kc, total,
+                       1.0f, a.dmu);
+    e = launch_backward_local_fused(a, a.dkc, a.dvl, std::is_same<T, bf16_t>::value ? CA_BF16 : CA_F32,
+                                    st);
+    if (e != hipSuccess) return e;
+    if (a.dalpha)
+        hipLaunchKernelGGL(bwd_sum_kernel, dim3(1), block, 0, st, a.dal, S, a.dalpha);
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
+    if (a.dkc && bwd_fused_supported(a.L, a.H / a.Hkv)) return bwd_dispatch_fused<T>(a, st);
     const int ntile = bwd_tiles(a.L);
     const int G = a.H / a.Hkv;
     const long S = (long)a.B * a.H, Skv = (long)a.B * a.Hkv;
@@ -537,7 +575,7 @@ static hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
                        V, dO, a.assign, a.vcent, a.valid, a.L, a.r, ntile, a.Kc, a.alpha, a.H, G,
                        a.lstat, a.dal);
     // 3. key side (dK, dV; dmu partials in a.part)
-    hipLaunchKernelGGL(bwd_key_kernel<T>, dim3((unsigned)(Skv * ntile)), block, 0, st, Q, K, V, dO,
+    hipLaunchKernelGGL((bwd_key_kernel<T, true, T>), dim3((unsigned)(Skv * ntile)), block, 0, st, Q, K, V, dO,
                        a.mu, a.vcent, a.cstat, a.dvc, a.lstat, a.valid, a.L, a.r, ntile, a.Kc,
                        a.alpha, a.H, G, static_cast<T *>(a.dK), static_cast<T *>(a.dV), a.part);
     // 4. dmu

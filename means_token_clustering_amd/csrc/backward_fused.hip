@@ -1,0 +1,373 @@
+// Local-branch backward of one slice in one launch (L <= 128, one query head
+// per K/V head): the band part of the backward pass on the fp16 matrix cores,
+// with the forward kernel's split planes and fragment readers.
+//
+// Per slice the local branch is O^loc = P V with P = softmax over the window
+// |i - j| <= r of q_i . k_j / 8 (a padded key's logit is -10000). For the
+// loss sum(dO * O) with O = keep ((1 - alpha) V^cent_c + alpha O^loc) and
+// g = keep dO, its gradients are (the softmax rule dS = P (dP - D)):
+//   dP_ij = alpha g_i . v_j,  D_i = alpha g_i . O^loc_i,
+//   dS_ij = P_ij (dP_ij - D_i) / 8   (0 for a padded key: constant logit),
+//   dQ_i += sum_j dS_ij k_j,  dK_j += sum_i dS_ij q_i,  dV_j += alpha sum_i P_ij g_i.
+// The centroid branch's shares (dK_c, dV_c in fp32, dmu with the counts) come
+// from the staged kernels and are added here: dQ_i += dmu_{c_i} / n_{c_i}.
+// Also dalpha's share of the slice: sum keep dO . (O^loc - V^cent_c).
+//
+// Two passes over the band, each the mirror of the other:
+//   query pass (wave w owns query tile w; K and V planes in LDS, its Q and g
+//     rows as B fragments): the forward's wide window gives O^loc and the
+//     softmax statistics; a second sweep recomputes S^T and dP^T tile pairs
+//     and accumulates dQ^T = K^T dS^T, exactly like P V;
+//   key pass (wave w owns key tile w; Q and g planes in LDS, its K and V rows
+//     as B fragments): S and dP in [query][key] orientation, probabilities
+//     from the query statistics of the first pass, dK^T = Q^T dS and
+//     dV^T = g^T P.
+// Scaling: Q and K are scaled by powers of two as in the forward; V and g to
+// magnitudes below 2^4, so that dP (64 products) and dS stay below 2^14 and
+// fit the fp16 split; the factors are undone on the fp32 results.
+#include "launch.h"
+#include "mfma_split.h"
+
+namespace ca {
+namespace {
+
+constexpr int kBVLimit = 4;                   // scaled |v|, |g| < 2^4
+constexpr int kBOffB = 2 * kPlane;            // V planes, later g planes
+constexpr int kBOffStat = 4 * kPlane;         // per query: max, 1/sum, D, dalpha share
+constexpr int kBOffMax = kBOffStat + kFL * 16;
+constexpr int kBLds = kBOffMax + 8 * 8 * 4;
+
+}  // namespace
+
+template <typename T, bool FULL, bool MASKED>
+__global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx,
+    const T *__restrict__ dO, const int32_t *__restrict__ assign,
+    const uint8_t *__restrict__ valid, const float *__restrict__ vcent,
+    const float *__restrict__ dmu, const int32_t *__restrict__ counts,
+    const float *__restrict__ dKc, const float *__restrict__ dVc, int S, int L, int Kc,
+    int radius, float alpha, int H, T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV,
+    float *__restrict__ dal) {
+    __shared__ __align__(16) unsigned char smem[kBLds];
+    uint16_t *sA = reinterpret_cast<uint16_t *>(smem);            // K, then Q planes
+    uint16_t *sB = reinterpret_cast<uint16_t *>(smem + kBOffB);   // V, then g planes
+    float4 *sStat = reinterpret_cast<float4 *>(smem + kBOffStat);
+    uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kBOffMax);   // [8 waves][8]
+    const u8 *pA = smem, *pB = smem + kBOffB;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const long slice = blockIdx.x;
+    if (slice >= S) return;
+    const int NT = FULL ? 8 : (L + 15) >> 4;
+    const bool tile_on = FULL || w < NT;
+    const int tok = 16 * w + l16;                // query (first pass) and key (second) of the lane
+    const bool tok_in = FULL || tok < L;
+    const long base = slice * (long)L * kD;
+    const long brow = (slice / H) * (long)L;
+    const LaneOffs lo = lane_offsets(l16, g);
+    const int trv = 1024 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
+    const int nr = (radius + 15) >> 4;           // tiles on each side of a tile's window
+
+    // ------------------------------------------------------------ loads
+    float qraw[2][8], graw[2][8], kraw[2][8], vraw[2][8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+        load_row8<T, FULL>(dO + base, tok, L, 32 * c + 8 * g, graw[c]);
+    }
+    const bool tok_keep = !MASKED || !tok_in || valid[brow + tok] != 0;
+    if (!tok_keep) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) graw[c][i] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
+        load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
+    }
+    {
+        const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
+        const uint32_t bg = wave_max_u(__float_as_uint(absmax8(graw[1], absmax8(graw[0], 0.f))));
+        const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        if (lane == 0) {
+            sMax[8 * w] = bq;
+            sMax[8 * w + 1] = bk;
+            sMax[8 * w + 2] = bv;
+            sMax[8 * w + 3] = bg;
+        }
+    }
+    if (MASKED && w < 2) {   // key mask of tokens 64w .. 64w+63, words 2w and 2w+1
+        const int t = 64 * w + lane;
+        const uint64_t bits = __ballot(t < L && valid[brow + t] != 0);
+        if (lane == 0) {
+            sMax[8 * (2 * w) + 4] = (uint32_t)bits;
+            sMax[8 * (2 * w + 1) + 4] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+    KeyBits kb;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[8 * k + 4]) : ~0u;
+    uint32_t mq = 0, mk = 0, mv = 0, mg = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+        mq = max(mq, sMax[8 * ww]);
+        mk = max(mk, sMax[8 * ww + 1]);
+        mv = max(mv, sMax[8 * ww + 2]);
+        mg = max(mg, sMax[8 * ww + 3]);
+    }
+    const int sq = scale_shift(mq, kQLimit), sk = scale_shift(mk, kKVLimit);
+    const int sv = scale_shift(mv, kBVLimit), sg = scale_shift(mg, kBVLimit);
+    const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk);
+    const float fv = __builtin_ldexpf(1.f, -sv), fg = __builtin_ldexpf(1.f, -sg);
+    Sp8 qf[2], gf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float x[8], y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] = qraw[c][i] * fq;
+            y[i] = graw[c][i] * fg;
+        }
+        qf[c] = split8(x);
+        gf[c] = split8(y);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        const int o = off64(it >> 3, (it & 7) * 8);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = kraw[n][i] * fk;
+        const Sp8 kp = split8(x);
+        st16(sA + o, kp.h);
+        st16(sA + kPlaneE + o, kp.m);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = vraw[n][i] * fv;
+        const Sp8 vp = split8(x);
+        st16(sB + o, vp.h);
+        st16(sB + kPlaneE + o, vp.m);
+    }
+    __syncthreads();
+    const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
+    const float du_scale = __builtin_ldexpf(1.f, -(sg + sv));   // real D -> units of dP
+
+    // ------------------------------------------------------------ query pass
+    if (tile_on) {
+        f32x4_t o[4];
+        float lsum = 1.f, M = 0.f;
+        local_wide<FULL, MASKED>(pA, pB, qf, w, NT, L, radius, sscale2, l16, g, lo.rl64, trv, kb,
+                                 o, lsum, &M);
+        const float invl = 1.0f / lsum;
+        // D and the dalpha share from O^loc, g and V^cent in the same lane layout
+        // (dims 16j + 4g .. +3 of query tok)
+        float dpart = 0.f, apart = 0.f;
+        const int c = tok_in ? min(max(assign[slice * L + tok], 0), Kc - 1) : 0;
+        if (tok_in && tok_keep) {
+            const float olf = __builtin_ldexpf(1.f, sv) * invl;
+            const float *vc = vcent + (slice * Kc + c) * kD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 16 * j + 4 * g;
+                const float4 g4 = load4<T>(dO + base + (long)tok * kD + d0);
+                const float4 v4 = load4<float>(vc + d0);
+                const float gg[4] = {g4.x, g4.y, g4.z, g4.w}, vv[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const float ol = o[j][rr] * olf;
+                    dpart = fmaf(gg[rr], ol, dpart);
+                    apart = fmaf(gg[rr], ol - vv[rr], apart);
+                }
+            }
+        }
+        const float D = alpha * col_sum(dpart);
+        const float A = col_sum(apart);
+        if (g == 0 && tok_in) sStat[tok] = make_float4(M, invl, D, A);
+        // second sweep: dQ^T = K^T dS^T over the window's key tile pairs
+        const float Du = D * du_scale;
+        const int kt_lo = w - nr < 0 ? 0 : w - nr;
+        const int kt_hi = w + nr < NT - 1 ? w + nr : NT - 1;
+        f32x4_t dq[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dq[j] = kZero4;
+        for (int kt = kt_lo; kt <= kt_hi; kt += 2) {
+            const bool two = kt + 1 <= kt_hi;
+            float ds[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ktt = two ? kt + h : kt;
+                const Sp8 k0 = frag_at(pA, kPlane, 2048 * ktt + lo.rl64);
+                const Sp8 k1 = frag_at(pA, kPlane, 2048 * ktt + (lo.rl64 ^ 64));
+                const Sp8 v0 = frag_at(pB, kPlane, 2048 * ktt + lo.rl64);
+                const Sp8 v1 = frag_at(pB, kPlane, 2048 * ktt + (lo.rl64 ^ 64));
+                f32x4_t a = mma3(k0, qf[0], kZero4);
+                a = mma3(k1, qf[1], a);
+                f32x4_t a2 = mma3(v0, gf[0], kZero4);
+                a2 = mma3(v1, gf[1], a2);
+                const uint32_t nib = MASKED ? kb.tile(ktt) >> (4 * g) : 0xfu;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int key = 16 * ktt + 4 * g + rr;
+                    const int dist = key > tok ? key - tok : tok - key;
+                    const bool in = (FULL || key < L) && dist <= radius && (h == 0 || two);
+                    const bool kok = !MASKED || ((nib >> rr) & 1u);
+                    const float s2 = kok ? a[rr] * sscale2 : kPadLogit2;
+                    const float p = in ? __builtin_amdgcn_exp2f(s2 - M) * invl : 0.f;
+                    ds[4 * h + rr] = (in && kok) ? p * (alpha * a2[rr] - Du) : 0.f;
+                }
+            }
+            const Sp8 dsp = split8<true>(ds);
+            const int b0 = 2048 * kt + trv, b1 = two ? b0 + 2048 : b0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                dq[j] = mma3(colfrag8_at(pA, b0 ^ (32 * j), b1 ^ (32 * j)), dsp, dq[j]);
+        }
+        if (tok_in) {
+            const float f = __builtin_ldexpf(0.125f, sg + sv + sk);
+            const int n = counts[slice * Kc + c];
+            const float invn = 1.0f / (float)(n > 1 ? n : 1);
+            const float *dm = dmu + (slice * Kc + c) * kD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 16 * j + 4 * g;
+                const float4 m4 = load4<float>(dm + d0);
+                store4<T>(dQ + base + (long)tok * kD + d0,
+                          make_float4(fmaf(dq[j][0], f, m4.x * invn), fmaf(dq[j][1], f, m4.y * invn),
+                                      fmaf(dq[j][2], f, m4.z * invn), fmaf(dq[j][3], f, m4.w * invn)));
+            }
+        }
+    }
+    __syncthreads();
+    // own key tile's K and V rows as B fragments, before the planes change
+    Sp8 kf[2], vf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        kf[c] = frag_at(pA, kPlane, 2048 * w + (lo.rl64 ^ (64 * c)));
+        vf[c] = frag_at(pB, kPlane, 2048 * w + (lo.rl64 ^ (64 * c)));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        const int row = it >> 3;
+        const int o = off64(row, (it & 7) * 8);
+        float x[8], y[8];
+        load_row8<T, FULL>(Q + base, row, L, (it & 7) * 8, x);
+        load_row8<T, FULL>(dO + base, row, L, (it & 7) * 8, y);
+        const float keep = (!MASKED || row >= L || valid[brow + row] != 0) ? fg : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[i] *= fq;
+            y[i] *= keep;
+        }
+        const Sp8 qp = split8(x), gp = split8(y);
+        st16(sA + o, qp.h);
+        st16(sA + kPlaneE + o, qp.m);
+        st16(sB + o, gp.h);
+        st16(sB + kPlaneE + o, gp.m);
+    }
+    __syncthreads();
+
+    // ------------------------------------------------------------ key pass
+    if (tile_on) {
+        const bool kok = !MASKED || ((kb.tile(w) >> l16) & 1u);   // the lane's own key
+        const int qt_lo = w - nr < 0 ? 0 : w - nr;
+        const int qt_hi = w + nr < NT - 1 ? w + nr : NT - 1;
+        f32x4_t dk[4], dv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dk[j] = dv[j] = kZero4;
+        for (int qt = qt_lo; qt <= qt_hi; qt += 2) {
+            const bool two = qt + 1 <= qt_hi;
+            float ds[8], pp[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int qtt = two ? qt + h : qt;
+                const Sp8 q0 = frag_at(pA, kPlane, 2048 * qtt + lo.rl64);
+                const Sp8 q1 = frag_at(pA, kPlane, 2048 * qtt + (lo.rl64 ^ 64));
+                const Sp8 g0 = frag_at(pB, kPlane, 2048 * qtt + lo.rl64);
+                const Sp8 g1 = frag_at(pB, kPlane, 2048 * qtt + (lo.rl64 ^ 64));
+                f32x4_t a = mma3(q0, kf[0], kZero4);    // [query 4g + rr][key l16]
+                a = mma3(q1, kf[1], a);
+                f32x4_t a2 = mma3(g0, vf[0], kZero4);
+                a2 = mma3(g1, vf[1], a2);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int qi = 16 * qtt + 4 * g + rr;
+                    const int dist = qi > tok ? qi - tok : tok - qi;
+                    const bool in = (FULL || qi < L) && tok_in && dist <= radius && (h == 0 || two);
+                    const float4 st = sStat[in ? qi : 0];
+                    const float s2 = kok ? a[rr] * sscale2 : kPadLogit2;
+                    const float p = in ? __builtin_amdgcn_exp2f(s2 - st.x) * st.y : 0.f;
+                    pp[4 * h + rr] = p;
+                    ds[4 * h + rr] = (in && kok) ? p * (alpha * a2[rr] - st.z * du_scale) : 0.f;
+                }
+            }
+            const Sp8 dsp = split8<true>(ds), ppp = split8<true>(pp);
+            const int b0 = 2048 * qt + trv, b1 = two ? b0 + 2048 : b0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dk[j] = mma3(colfrag8_at(pA, b0 ^ (32 * j), b1 ^ (32 * j)), dsp, dk[j]);
+                dv[j] = mma3(colfrag8_at(pB, b0 ^ (32 * j), b1 ^ (32 * j)), ppp, dv[j]);
+            }
+        }
+        if (tok_in) {
+            const float fkk = __builtin_ldexpf(0.125f, sg + sv + sq);
+            const float fvv = alpha * __builtin_ldexpf(1.f, sg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 16 * j + 4 * g;
+                const long r0 = base + (long)tok * kD + d0;
+                const float4 ck = load4<float>(dKc + r0), cv = load4<float>(dVc + r0);
+                store4<T>(dK + r0, make_float4(fmaf(dk[j][0], fkk, ck.x), fmaf(dk[j][1], fkk, ck.y),
+                                               fmaf(dk[j][2], fkk, ck.z), fmaf(dk[j][3], fkk, ck.w)));
+                store4<T>(dV + r0, make_float4(fmaf(dv[j][0], fvv, cv.x), fmaf(dv[j][1], fvv, cv.y),
+                                               fmaf(dv[j][2], fvv, cv.z), fmaf(dv[j][3], fvv, cv.w)));
+            }
+        }
+    }
+    if (tid == 0) {   // the slice's dalpha share, in token order
+        float t = 0.f;
+        for (int i = 0; i < L; ++i) t += sStat[i].w;
+        dal[slice] = t;
+    }
+}
+
+bool bwd_fused_supported(int L, int G) { return G == 1 && L >= 1 && L <= kFL; }
+
+template <typename T, bool MASKED>
+static hipError_t bwd_fused_launch_t(const BwdArgs &a, const float *dkc, const float *dvc2,
+                                     hipStream_t st) {
+    const T *q = static_cast<const T *>(a.Q), *k = static_cast<const T *>(a.K);
+    const T *v = static_cast<const T *>(a.V), *go = static_cast<const T *>(a.dO);
+    const int S = a.B * a.H;
+    if (a.L == kFL)
+        hipLaunchKernelGGL((bwd_local_fused_kernel<T, true, MASKED>), dim3((unsigned)S),
+                           dim3(kThreads), 0, st, q, k, v, go, a.assign, a.valid, a.vcent, a.dmu,
+                           a.counts, dkc, dvc2, S, a.L, a.Kc, a.r, a.alpha, a.H,
+                           static_cast<T *>(a.dQ), static_cast<T *>(a.dK), static_cast<T *>(a.dV),
+                           a.dal);
+    else
+        hipLaunchKernelGGL((bwd_local_fused_kernel<T, false, MASKED>), dim3((unsigned)S),
+                           dim3(kThreads), 0, st, q, k, v, go, a.assign, a.valid, a.vcent, a.dmu,
+                           a.counts, dkc, dvc2, S, a.L, a.Kc, a.r, a.alpha, a.H,
+                           static_cast<T *>(a.dQ), static_cast<T *>(a.dK), static_cast<T *>(a.dV),
+                           a.dal);
+    return hipGetLastError();
+}
+
+hipError_t launch_backward_local_fused(const BwdArgs &a, const float *dkc, const float *dvc2,
+                                       ca_dtype_t dt, hipStream_t st) {
+    if (dt == CA_BF16)
+        return a.valid ? bwd_fused_launch_t<bf16_t, true>(a, dkc, dvc2, st)
+                       : bwd_fused_launch_t<bf16_t, false>(a, dkc, dvc2, st);
+    return a.valid ? bwd_fused_launch_t<float, true>(a, dkc, dvc2, st)
+                   : bwd_fused_launch_t<float, false>(a, dkc, dvc2, st);
+}
+
+}  // namespace ca

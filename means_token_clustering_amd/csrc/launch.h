@@ -78,9 +78,16 @@ struct BwdArgs {
     float *dal;
     void *dQ, *dK, *dV;
     float *dalpha;
+    // fp32 [S, L, 64] shares of the centroid branch in dK and dV; nullable
+    // (then the staged sequence runs for every shape)
+    float *dkc, *dvl;
 };
 int bwd_tiles(int L);
 hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
+// Local-branch backward in one launch per slice (backward_fused.hip).
+bool bwd_fused_supported(int L, int G);
+hipError_t launch_backward_local_fused(const BwdArgs &a, const float *dkc, const float *dvc2,
+                                       ca_dtype_t dt, hipStream_t st);
 
 // Exact attention (decoder / cross-attention branch): Q [S, L, 64], K, V
 // [S / G, Nk, 64] (grouped heads as in kv_slice); qvalid [S / H, L], kvalid
