@@ -111,6 +111,13 @@ CASES = [  # B, H, Hkv, L, nclust, iters, W, alpha, dtype, seed, mask kind
     (1, 1, 1, 1, 16, 2, 32, 0.5, gen.F32, 15, None),          # a single token
     (2, 2, 2, 128, 16, 3, 32, 0.0, gen.F32, 16, None),        # alpha = 0
     (2, 2, 2, 128, 16, 3, 32, 1.0, gen.F32, 17, "holes"),     # alpha = 1
+    # the single-launch local branch (L <= 128, one query head per K/V head)
+    (4, 4, 4, 128, 16, 3, 32, 0.5, gen.BF16, 18, "prefix"),   # bf16
+    (2, 3, 3, 77, 16, 3, 32, 0.4, gen.BF16, 19, "holes"),     # bf16, partial tiles
+    (1, 2, 2, 128, 16, 3, 0, 0.5, gen.F32, 21, None),         # W = 0
+    (1, 2, 2, 128, 16, 3, 400, 0.5, gen.F32, 22, "holes"),    # window wider than L
+    (2, 2, 2, 128, 16, 3, 70, 0.6, gen.F32, 23, None),        # radius 35: three tile pairs
+    (1, 2, 2, 17, 5, 2, 9, 0.5, gen.F32, 24, None),           # two tiles, K = 5
 ]
 
 
