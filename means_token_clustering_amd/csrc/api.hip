@@ -365,11 +365,6 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
     float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
     float *cstat = reinterpret_cast<float *>(ws + lay.cstat);
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
-    // the forward's final means and centroid attention, from the given assignment
-    CA_TRY(launch_centroid_partials(Q, assign, (int)S, L, Kc, dt, part, pcnt, stream));
-    CA_TRY(launch_centroid_reduce(part, pcnt, kmeans_tiles(L), (int)S, Kc, mu, counts, stream));
-    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, H / Hkv, vcent, xpart,
-                                 stream, cstat));
     BwdArgs a{};
     a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.assign = assign; a.valid = valid;
     a.B = B; a.H = H; a.Hkv = Hkv; a.L = L; a.Kc = Kc; a.r = W / 2; a.alpha = alpha;
@@ -382,6 +377,16 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
     a.dQ = dQ; a.dK = dK; a.dV = dV; a.dalpha = dalpha;
     a.dkc = reinterpret_cast<float *>(ws + lay.dkc);
     a.dvl = reinterpret_cast<float *>(ws + lay.dvl);
+    if (bwd_fused_supported(L, Kc, H / Hkv)) {   // two launches per slice, then dalpha
+        CA_TRY(launch_backward_fused(a, dt, stream));
+        return hip_status(launch_bwd_sum(a.dal, S, dalpha, stream));
+    }
+    // staged: the forward's final means and centroid attention from the given
+    // assignment, then the backward kernels
+    CA_TRY(launch_centroid_partials(Q, assign, (int)S, L, Kc, dt, part, pcnt, stream));
+    CA_TRY(launch_centroid_reduce(part, pcnt, kmeans_tiles(L), (int)S, Kc, mu, counts, stream));
+    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, H / Hkv, vcent, xpart,
+                                 stream, cstat));
     return hip_status(launch_backward(a, dt, stream));
 }
 

@@ -33,8 +33,6 @@
 // Arithmetic is fp32 (the storage dtype is read and written); four lanes
 // share a row, each holding 16 of its 64 dims, and meet through two
 // butterfly adds, as in the forward's staged kernels.
-#include <type_traits>
-
 #include "launch.h"
 
 namespace ca {
@@ -516,43 +514,8 @@ __global__ __launch_bounds__(256) void bwd_sum_kernel(const float *__restrict__ 
 // ---------------------------------------------------------------- host side
 int bwd_tiles(int L) { return (L + kBT - 1) / kBT; }
 
-// The sequence with the local branch in one launch per slice (L <= 128, one
-// query head per K/V head): dVc, the centroid branch's dK, dV shares (fp32)
-// and dmu partials, dmu, then bwd_local_fused_kernel for dQ, dK, dV and the
-// slices' dalpha shares.
-template <typename T>
-static hipError_t bwd_dispatch_fused(const BwdArgs &a, hipStream_t st) {
-    const int ntile = bwd_tiles(a.L);
-    const long S = (long)a.B * a.H;
-    const T *Q = static_cast<const T *>(a.Q), *K = static_cast<const T *>(a.K);
-    const T *V = static_cast<const T *>(a.V), *dO = static_cast<const T *>(a.dO);
-    const dim3 block(256);
-    const size_t lds = sizeof(float) * ((size_t)kBT * kBPad + (size_t)a.Kc * kD) + sizeof(int) * kBT;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_cluster_sum_kernel<T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_cluster_sum_kernel<T>, dim3((unsigned)(S * ntile)), block, lds, st, dO,
-                       a.assign, a.valid, a.L, a.Kc, a.H, ntile, a.part);
-    const long total = S * a.Kc * kD;
-    const dim3 rgrid((unsigned)((total + 255) / 256));
-    hipLaunchKernelGGL(bwd_partial_reduce_kernel, rgrid, block, 0, st, a.part, ntile, a.Kc, total,
-                       1.0f - a.alpha, a.dvc);
-    hipLaunchKernelGGL((bwd_key_kernel<T, false, float>), dim3((unsigned)(S * ntile)), block, 0, st,
-                       Q, K, V, dO, a.mu, a.vcent, a.cstat, a.dvc, a.lstat, a.valid, a.L, a.r,
-                       ntile, a.Kc, a.alpha, a.H, 1, a.dkc, a.dvl, a.part);
-    hipLaunchKernelGGL(bwd_partial_reduce_kernel, rgrid, block, 0, st, a.part, ntile, a.Kc, total,
-                       1.0f, a.dmu);
-    e = launch_backward_local_fused(a, a.dkc, a.dvl, std::is_same<T, bf16_t>::value ? CA_BF16 : CA_F32,
-                                    st);
-    if (e != hipSuccess) return e;
-    if (a.dalpha)
-        hipLaunchKernelGGL(bwd_sum_kernel, dim3(1), block, 0, st, a.dal, S, a.dalpha);
-    return hipGetLastError();
-}
-
 template <typename T>
 static hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
-    if (a.dkc && bwd_fused_supported(a.L, a.H / a.Hkv)) return bwd_dispatch_fused<T>(a, st);
     const int ntile = bwd_tiles(a.L);
     const int G = a.H / a.Hkv;
     const long S = (long)a.B * a.H, Skv = (long)a.B * a.Hkv;
@@ -588,6 +551,12 @@ static hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
     // 6. dalpha
     if (a.dalpha)
         hipLaunchKernelGGL(bwd_sum_kernel, dim3(1), block, 0, st, a.dal, S * ntile, a.dalpha);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_sum(const float *part, long n, float *out, hipStream_t st) {
+    if (!out) return hipSuccess;
+    hipLaunchKernelGGL(bwd_sum_kernel, dim3(1), dim3(256), 0, st, part, n, out);
     return hipGetLastError();
 }
 

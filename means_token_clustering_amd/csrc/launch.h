@@ -84,10 +84,15 @@ struct BwdArgs {
 };
 int bwd_tiles(int L);
 hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
-// Local-branch backward in one launch per slice (backward_fused.hip).
-bool bwd_fused_supported(int L, int G);
-hipError_t launch_backward_local_fused(const BwdArgs &a, const float *dkc, const float *dvc2,
-                                       ca_dtype_t dt, hipStream_t st);
+// out[0] = sum of part[0 .. n) in a fixed order (nothing when out is null)
+hipError_t launch_bwd_sum(const float *part, long n, float *out, hipStream_t st);
+// The backward pass in two launches per slice (backward_fused.hip) for
+// L <= 128, K <= 16 and one query head per K/V head: the centroid branch
+// (dK, dV shares in dkc, dvl; dmu; counts; the centroid term of dalpha in
+// lstat's first S floats), then the local branch with the final dQ, dK, dV
+// and the slices' dalpha in dal.
+bool bwd_fused_supported(int L, int Kc, int G);
+hipError_t launch_backward_fused(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
 
 // Exact attention (decoder / cross-attention branch): Q [S, L, 64], K, V
 // [S / G, Nk, 64] (grouped heads as in kv_slice); qvalid [S / H, L], kvalid
