@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 
 METRIC = "cluster-attention fwd tokens/s (B·L per s, all heads) + % HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
 MALL_BYTES = 256 << 20         # Infinity Cache
 
 
@@ -60,6 +61,16 @@ def algorithmic_bytes(B, H, L, d, elem) -> int:
     return 4 * B * H * L * d * elem + 4 * B * H * L
 
 
+def algorithmic_flops(B, H, L, d, K, iters, W) -> int:
+    """FLOPs of one forward (an FMA is 2): distances 2ILKd, centroid sums ILd,
+    centroid attention 4KLd, local window 4Pd (P in-window pairs), fusion 3Ld,
+    per slice."""
+    r = W // 2
+    P = sum(min(L - 1, i + r) - max(0, i - r) + 1 for i in range(L))
+    per = 2 * iters * L * K * d + iters * L * d + 4 * K * L * d + 4 * P * d + 3 * L * d
+    return B * H * per
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -80,10 +91,52 @@ def parse():
     p.add_argument("--decoder", action="store_true",
                    help="time the decoder branch (cluster_attn_exact_forward, causal exact "
                         "attention) instead of the clustering forward")
+    p.add_argument("--no-probe", action="store_true",
+                   help="skip the HBM copy probe (achievable copy rates reported beside the "
+                        "nominal peak)")
     p.add_argument("--backward", action="store_true",
                    help="time the backward pass (cluster_attn_backward) on the forward's "
                         "assignment instead of the forward")
     return p.parse_args()
+
+
+def hbm_probe(torch, set_bytes: int) -> dict:
+    """Achievable HBM rates from plain device-to-device copies (torch copy_, one
+    kernel per copy, timed with events on the current stream): a 1 GiB copy,
+    and copies whose read + write bytes equal one forward launch's algorithmic
+    bytes, rotating through enough buffer pairs to miss the Infinity Cache."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def rate(pairs, reps):
+        for i in range(3):
+            pairs[i % len(pairs)][1].copy_(pairs[i % len(pairs)][0])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(reps):
+            src, dst = pairs[i % len(pairs)]
+            dst.copy_(src)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        s = t0.elapsed_time(t1) / 1e3 / reps
+        return 2 * pairs[0][0].numel() * pairs[0][0].element_size() / s / 1e9, s
+
+    big = [(torch.empty(1 << 28, dtype=torch.float32, device=dev),
+            torch.empty(1 << 28, dtype=torch.float32, device=dev))]
+    big[0][0].fill_(1.0)
+    big_rate, _ = rate(big, 10)
+    del big
+    n = set_bytes // 2 // 4
+    npairs = max(2, MALL_BYTES // (2 * 4 * n) + 2)
+    small = [(torch.ones(n, dtype=torch.float32, device=dev),
+              torch.empty(n, dtype=torch.float32, device=dev)) for _ in range(npairs)]
+    small_rate, small_s = rate(small, 200)
+    return {"copy_1GiB_GBps": round(big_rate, 1), "copy_same_bytes_GBps": round(small_rate, 1),
+            "copy_same_bytes_us": round(small_s * 1e6, 3), "same_bytes": 2 * 4 * n,
+            "note": "device-to-device copies; same_bytes = one launch's algorithmic bytes, "
+                    "half read and half written"}
 
 
 def cpu_baseline(x, seconds: float, mask=None, flags: int = 0):
@@ -380,6 +433,14 @@ def main():
                                  f"{int(mask.sum())} of {mask.size} tokens real")
     if args.flags:
         rec["config"]["flags"] = args.flags
+    flops = algorithmic_flops(x.B, x.H, x.L, x.d, min(x.nclust, x.L), x.iters, x.W)
+    tflops = flops / (ms / 1e3) / 1e12
+    rec["compute"] = {"flops_per_launch": flops, "achieved_TFLOPs": round(tflops, 2),
+                      "peak_fp32_TFLOPs": FP32_PEAK_TFLOPS,
+                      "frac": round(tflops / FP32_PEAK_TFLOPS, 4)}
+    if not args.no_probe:
+        rec["hbm_probe"] = hbm_probe(torch, set_bytes)
+        roof["frac_of_copy"] = round(achieved / rec["hbm_probe"]["copy_same_bytes_GBps"], 4)
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, mask, args.flags)
     print(json.dumps(rec), flush=True)
