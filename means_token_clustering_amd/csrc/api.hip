@@ -49,7 +49,7 @@ struct StagedLayout {
 StagedLayout staged_layout(long S, int L, int Kc) {
     StagedLayout w{};
     const long ntile = kmeans_tiles(L);
-    const long nsplit = xattn_splits(L);
+    const long nsplit = xattn_splits(S, L);
     size_t off = 0;
     w.mu = off;       off += align_up(sizeof(float) * S * Kc * kD);
     w.assign = off;   off += align_up(sizeof(int32_t) * S * L);
@@ -158,6 +158,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     }
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                  stream));
+    if (!var.soft && local_mfma_supported(radius))
+        return hip_status(launch_local_mfma(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha,
+                                            valid, H, G, out, stream));
     CA_TRY(launch_local_window(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha, valid, H, G,
                                out, nullptr, stream, var.soft ? mu : nullptr));
     return CA_OK;
@@ -171,7 +174,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(long S, int L, int Kc) {
     BwdLayout w{};
     const long ntile = bwd_tiles(L) > kmeans_tiles(L) ? bwd_tiles(L) : kmeans_tiles(L);
-    const long nsplit = xattn_splits(L);
+    const long nsplit = xattn_splits(S, L);
     size_t off = 0;
     w.mu = off;     off += align_up(sizeof(float) * S * Kc * kD);
     w.counts = off; off += align_up(sizeof(int32_t) * S * Kc);
@@ -460,7 +463,7 @@ ca_status_t ca_centroid_update(const void *Q, const int32_t *assign, int S, int 
 
 size_t ca_centroid_xattn_workspace_size(int S, int L, int d, int Kc) {
     if (check_step(S, L, d, Kc, CA_F32) != CA_OK) return 0;
-    const int nsplit = xattn_splits(L);
+    const int nsplit = xattn_splits(S, L);
     return nsplit > 1 ? align_up(sizeof(float) * (size_t)S * nsplit * Kc * (kD + 2)) : 0;
 }
 

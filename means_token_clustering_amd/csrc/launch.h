@@ -38,7 +38,8 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
                                   int S, int Kc, float *mu, int32_t *counts, hipStream_t st,
                                   bool keep_empty = false);
 
-int xattn_splits(int L);
+// key ranges per slice of the centroid cross-attention (partials when > 1)
+int xattn_splits(long S, int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
 // belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
 // stats (nullable, [S, Kc, 2]): per row the largest scaled logit and the sum
@@ -54,6 +55,13 @@ hipError_t launch_local_window(const void *Q, const void *K, const void *V, int 
                                ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
                                float alpha, const uint8_t *valid, int H, int G, void *out,
                                float *oloc, hipStream_t st, const float *mu = nullptr);
+// The same window branch with the fused epilogue on the matrix cores
+// (local_mfma.hip), for radius r <= 16 and the hard gather.
+bool local_mfma_supported(int r);
+hipError_t launch_local_mfma(const void *Q, const void *K, const void *V, int S, int L, int r,
+                             ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
+                             float alpha, const uint8_t *valid, int H, int G, void *out,
+                             hipStream_t st);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);

@@ -1,0 +1,243 @@
+// Local window branch with the fused gather + convex fusion for any L
+// (staged path), on the fp16 matrix cores, for window radius r <= 16.
+//
+// Branch: model card "Hooshaai/distilbert-sst2-cluster-attention",
+// Architecture Overview figure (LocalAttn(Q, K, V, W=32), then
+// O = (1 - alpha) V^gathered + alpha O^local with V^gathered_i = Vc_{c_i});
+// "ClusterFormer" spec 3 (band-masked attention). Key j belongs to query i
+// iff |i - j| <= r, clipped to [0, L).
+//
+// Work split: one workgroup (8 waves) per 128-query block of a slice; wave w
+// owns query tile w of the block (16 queries) as in the single-launch
+// forward. The block's keys, a 16-row halo on each side, are staged once as
+// fp16 h/m planes of 160 rows (K, then V), so every query tile finds its
+// three key tiles in LDS. Q stays in registers. The arithmetic (power-of-two
+// range scaling per tensor and block, the fp16 split x = h + m + e, three
+// partial products per contraction, base-2 softmax) is the single-launch
+// forward's; the scale factors are undone on the fp32 results.
+//
+// Key-padding mask (optional; ClusterAttention listing on the
+// "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
+// a padded key takes the logit -10000 inside the window, and the fused
+// output row of a padded query is zero.
+#include "launch.h"
+#include "mfma_split.h"
+
+namespace ca {
+namespace {
+
+constexpr int kMRows = 160;                  // 16 halo + 128 + 16 halo key rows
+constexpr int kMPlane = kMRows * kD * 2;     // bytes of one fp16 plane
+constexpr int kMPlaneE = kMPlane / 2;
+constexpr int kMOffV = 2 * kMPlane;
+constexpr int kMLds = 4 * kMPlane;           // 81,920 B: two workgroups per CU
+constexpr int kMChunks = kMRows * kD / 8;    // 8-element chunks per staged tensor
+constexpr int kMItems = (kMChunks + kThreads - 1) / kThreads;
+
+}  // namespace
+
+template <typename T, bool MASKED>
+__global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int rad,
+    int nblk, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
+    float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out) {
+    __shared__ __align__(16) unsigned char smem[kMLds];
+    uint16_t *sK = reinterpret_cast<uint16_t *>(smem);
+    uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kMOffV);
+    // per-wave maxima [8][4] and the five key-mask words, in the last 256
+    // bytes of the V m plane until the planes are written
+    uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kMLds - 256);
+    const u8 *pK = smem, *pV = smem + kMOffV;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    const int blk = blockIdx.x % nblk;
+    const long s = blockIdx.x / nblk;
+    const long brow = (s / H) * (long)L;
+    const long base = s * (long)L * kD;
+    const long kvbase = kv_slice(s, H, G) * (long)L * kD;
+    const int i0 = 128 * blk;                      // first query of the block
+    const int t0 = blk == 0 ? 0 : 8 * blk - 1;     // first staged key tile
+    const int r0 = 16 * t0;                        // ... and row
+    const int Lp = min(L, i0 + 144) - r0;          // staged rows that hold keys
+    const int NTp = (Lp + 15) >> 4;
+    const int qt = 8 * blk - t0 + w;               // the wave's query tile among the staged rows
+    const int tok = i0 + 16 * w + l16;             // the lane's query
+    const bool wave_on = i0 + 16 * w < L;
+    const LaneOffs lo = lane_offsets(l16, g);
+    const int trv = 1024 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
+
+    float qraw[2][8], kraw[kMItems][8], vraw[kMItems][8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) load_row8<T, false>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
+    const T *Ks = Kx + kvbase + (long)r0 * kD, *Vs = Vx + kvbase + (long)r0 * kD;
+#pragma unroll
+    for (int n = 0; n < kMItems; ++n) {
+        const int it = tid + kThreads * n;   // row it / 8, dims 8 (it % 8) ..
+        if (it < kMChunks) {
+            load_row8<T, false>(Ks, it >> 3, Lp, (it & 7) * 8, kraw[n]);
+            load_row8<T, false>(Vs, it >> 3, Lp, (it & 7) * 8, vraw[n]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kraw[n][i] = vraw[n][i] = 0.f;
+        }
+    }
+    {
+        float mk = 0.f, mv = 0.f;
+#pragma unroll
+        for (int n = 0; n < kMItems; ++n) {
+            mk = absmax8(kraw[n], mk);
+            mv = absmax8(vraw[n], mv);
+        }
+        const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
+        const uint32_t bk = wave_max_u(__float_as_uint(mk));
+        const uint32_t bv = wave_max_u(__float_as_uint(mv));
+        if (lane == 0) {
+            sMax[4 * w] = bq;
+            sMax[4 * w + 1] = bk;
+            sMax[4 * w + 2] = bv;
+        }
+    }
+    if (MASKED && w < 3) {   // key mask of staged rows 64w .. 64w+63
+        const int row = 64 * w + lane;
+        const uint64_t bits = __ballot(row < Lp && valid[brow + r0 + row] != 0);
+        if (lane == 0) {
+            sMax[32 + 2 * w] = (uint32_t)bits;
+            if (w < 2) sMax[32 + 2 * w + 1] = (uint32_t)(bits >> 32);
+        }
+    }
+    __syncthreads();
+    uint32_t mq = 0, mk = 0, mv = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+        mq = max(mq, sMax[4 * ww]);
+        mk = max(mk, sMax[4 * ww + 1]);
+        mv = max(mv, sMax[4 * ww + 2]);
+    }
+    KeyBits160 kb;
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+        kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[32 + k]) : ~0u;
+    const int sq = scale_shift(mq, kQLimit), sk = scale_shift(mk, kKVLimit);
+    const int sv = scale_shift(mv, kKVLimit);
+    __syncthreads();   // the maxima are read: the planes may cover them
+
+    Sp8 qf[2];
+    {
+        const float fq = __builtin_ldexpf(1.f, -sq);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
+            qf[c] = split8(x);
+        }
+    }
+    {
+        const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
+#pragma unroll
+        for (int n = 0; n < kMItems; ++n) {
+            const int it = tid + kThreads * n;
+            if (it < kMChunks) {
+                float x[8], y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[i] = kraw[n][i] * fk;
+                    y[i] = vraw[n][i] * fv;
+                }
+                const Sp8 kp = split8(x), vp = split8(y);
+                const int o = off64(it >> 3, (it & 7) * 8);
+                st16(sK + o, kp.h);
+                st16(sK + kMPlaneE + o, kp.m);
+                st16(sV + o, vp.h);
+                st16(sV + kMPlaneE + o, vp.m);
+            }
+        }
+    }
+    __syncthreads();
+
+    f32x4_t o[4];
+    float lsum = 1.f;
+    if (wave_on) {
+        const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
+        local_narrow<false, MASKED, KeyBits160, kMPlane>(pK, pV, qf, qt, NTp, Lp, rad, sscale2,
+                                                         l16, g, lo.rl64, trv, kb, o, lsum);
+    }
+    __syncthreads();   // the K planes become the output staging area
+
+    // fused rows of the wave's tile through a wave-private LDS tile (16 rows,
+    // 16-byte chunks XOR-swizzled by the row), then whole-row stores
+    if (!wave_on) return;
+    constexpr int kRowB = kD * (int)sizeof(T);
+    constexpr int kCpr = kRowB / 16;
+    u8 *stg = smem + w * 16 * kRowB;
+    {
+        const bool tok_in = tok < L;
+        const float f = alpha * __builtin_ldexpf(1.f, sv) * __builtin_amdgcn_rcpf(lsum);
+        const int c = tok_in ? min(max(assign[s * L + tok], 0), Kc - 1) : 0;
+        const float *vc = vcent + (s * Kc + c) * kD;
+        const bool keep = tok_in && (!MASKED || valid[brow + tok] != 0);
+        const float wg = 1.0f - alpha;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
+            const int d0 = 16 * j + 4 * g;
+            const float4 c4 = load4<float>(vc + d0);
+            float v0 = fmaf(o[j][0], f, wg * c4.x), v1 = fmaf(o[j][1], f, wg * c4.y);
+            float v2 = fmaf(o[j][2], f, wg * c4.z), v3 = fmaf(o[j][3], f, wg * c4.w);
+            if (!keep) v0 = v1 = v2 = v3 = 0.f;
+            const int byte = d0 * (int)sizeof(T);
+            u8 *p = stg + l16 * kRowB + ((((byte >> 4) ^ (l16 & (kCpr - 1)))) << 4) + (byte & 15);
+            if (sizeof(T) == 4) {
+                *reinterpret_cast<f32x4_t *>(p) = f32x4_t{v0, v1, v2, v3};
+            } else {
+                *reinterpret_cast<u32x2_t *>(p) =
+                    u32x2_t{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                            (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+            }
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    u8 *dst = reinterpret_cast<u8 *>(out + base + (long)(i0 + 16 * w) * kD);
+    const int nrow = min(16, L - (i0 + 16 * w));
+#pragma unroll
+    for (int i = 0; i < kCpr / 4; ++i) {   // 64 chunks = 64 / kCpr rows per store
+        const int flat = 64 * i + lane;
+        const int row = flat / kCpr, ch = flat % kCpr;
+        const u32x4_t v =
+            *reinterpret_cast<const u32x4_t *>(stg + row * kRowB + (((ch ^ (row & (kCpr - 1)))) << 4));
+        if (row < nrow) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + flat * 16));
+    }
+}
+
+bool local_mfma_supported(int r) { return r >= 0 && r <= 16; }
+
+template <typename T>
+static hipError_t local_mfma_dispatch(const void *Q, const void *K, const void *V, int S, int L,
+                                      int r, const float *vcent, const int32_t *assign, int Kc,
+                                      float alpha, const uint8_t *valid, int H, int G, void *out,
+                                      hipStream_t st) {
+    const int nblk = (L + 127) / 128;
+    const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
+    const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K);
+    const T *v = static_cast<const T *>(V);
+    if (valid)
+        hipLaunchKernelGGL((local_mfma_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, nblk,
+                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out));
+    else
+        hipLaunchKernelGGL((local_mfma_kernel<T, false>), grid, block, 0, st, q, k, v, L, r, nblk,
+                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_local_mfma(const void *Q, const void *K, const void *V, int S, int L, int r,
+                             ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
+                             float alpha, const uint8_t *valid, int H, int G, void *out,
+                             hipStream_t st) {
+    if (dt == CA_BF16)
+        return local_mfma_dispatch<bf16_t>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H,
+                                           G, out, st);
+    return local_mfma_dispatch<float>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H, G,
+                                      out, st);
+}
+
+}  // namespace ca

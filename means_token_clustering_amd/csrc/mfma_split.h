@@ -257,10 +257,12 @@ __device__ __forceinline__ u32x2_t tr_at(const u8 *base, int off) {
         (lds_i16x4 *)((__attribute__((address_space(3))) u8 *)(base + off)));
     return __builtin_bit_cast(u32x2_t, v);
 }
-// 8-deep transposed fragment of a [128][64] plane pair from two row groups
+// 8-deep transposed fragment of a [rows][64] plane pair (planes PLANE bytes
+// apart; [128][64] by default) from two row groups
+template <int PLANE = kPlane>
 __device__ __forceinline__ Sp8 colfrag8_at(const u8 *base, int o0, int o1) {
     const u32x2_t h0 = tr_at(base, o0), h1 = tr_at(base, o1);
-    const u32x2_t m0 = tr_at(base, o0 + kPlane), m1 = tr_at(base, o1 + kPlane);
+    const u32x2_t m0 = tr_at(base, o0 + PLANE), m1 = tr_at(base, o1 + PLANE);
     return Sp8{u32x4_t{h0[0], h0[1], h1[0], h1[1]}, u32x4_t{m0[0], m0[1], m1[0], m1[1]}};
 }
 
@@ -280,6 +282,18 @@ struct KeyBits {
 };
 constexpr float kPadLogit2 = -14426.950408889634f;
 
+// The same for up to 160 keys (a 128-query block with a 16-key halo on each
+// side), keys counted from the first staged row.
+struct KeyBits160 {
+    uint32_t w[5];
+    __device__ __forceinline__ uint32_t tile(int t) const {
+        const int k = t >> 1;
+        const uint32_t x =
+            k == 0 ? w[0] : (k == 1 ? w[1] : (k == 2 ? w[2] : (k == 3 ? w[3] : w[4])));
+        return (x >> (16 * (t & 1))) & 0xffffu;
+    }
+};
+
 // Local window of radius <= 16 for query tile qt: scores against key tiles
 // qt-1, qt, qt+1 (others are outside every window of the tile), base-2
 // softmax, then O^T = V^T P^T: the pair (qt-1, qt) as one 32-deep product and
@@ -287,11 +301,13 @@ constexpr float kPadLogit2 = -14426.950408889634f;
 // K and V reads are moved onto tile qt (finite values times zero). Every LDS
 // read of a stage is issued before its first product, and the products of
 // independent tiles alternate, so that neither the LDS latency nor the
-// matrix-core latency is exposed per product.
-template <bool FULL, bool MASKED>
+// matrix-core latency is exposed per product. PLANE: byte distance of the
+// h and m planes (rows of the planes: NT tiles of 16, L valid; KB: the key
+// mask of those rows).
+template <bool FULL, bool MASKED, typename KB = KeyBits, int PLANE = kPlane>
 __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
-                                             int l16, int g, int rl64, int trv, const KeyBits &kb,
+                                             int l16, int g, int rl64, int trv, const KB &kb,
                                              f32x4_t *o, float &lsum) {
     bool valid[3];
     Sp8 kfr[3][2];
@@ -301,7 +317,7 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
         valid[d] = kt >= 0 && kt < NT;
         const int kb = 2048 * (valid[d] ? kt : qt);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) kfr[d][c] = frag_at(pK, kPlane, kb + (rl64 ^ (64 * c)));
+        for (int c = 0; c < 2; ++c) kfr[d][c] = frag_at(pK, PLANE, kb + (rl64 ^ (64 * c)));
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4_t sc[3] = {kZero4, kZero4, kZero4};
@@ -365,8 +381,8 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int j = jj + u;
-            va[u] = colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j));
-            vb[u] = colfrag8_at(pV, b2 ^ (32 * j), b3 ^ (32 * j));
+            va[u] = colfrag8_at<PLANE>(pV, b0 ^ (32 * j), b1 ^ (32 * j));
+            vb[u] = colfrag8_at<PLANE>(pV, b2 ^ (32 * j), b3 ^ (32 * j));
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t acc[2] = {kZero4, kZero4};

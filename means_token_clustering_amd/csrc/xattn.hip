@@ -4,11 +4,11 @@
 // Overview figure, Softmax(mu K^T / 8) V with d = 64; "ClusterFormer" spec 3).
 //
 // Work split: the keys of a slice are cut into `nsplit` contiguous ranges
-// (a multiple of 64 keys each); one workgroup per (slice, range) streams its
-// keys through LDS in 64-row K/V tiles with an online (running max) softmax
-// for 16 centroids at a time, 16 lanes per centroid. With one range the
-// result is written directly; otherwise each range stores (max, sum, acc)
-// and a combine kernel merges the ranges in range order (deterministic).
+// (a multiple of 64 keys each); one workgroup per (slice, range, group of 16
+// centroids) streams its keys through LDS in 64-row K/V tiles with an online
+// (running max) softmax, 16 lanes per centroid. With one range the result is
+// written directly; otherwise each range stores (max, sum, acc) and a
+// combine kernel merges the ranges in range order (deterministic).
 //
 // Key-padding mask (optional; ClusterAttention listing on the
 // "Hooshaai/svd-sst2-roberta-cluster" page, forward, bidirectional branch):
@@ -26,12 +26,13 @@ constexpr int kXPad = kD + 1;
 constexpr int kChunk = 16;               // centroids per pass
 constexpr int kPartStride = kD + 2;      // acc[64], max, sum
 
-int xattn_splits(int L) {
-    // enough ranges to occupy the chip for few long slices; 1 for short L
-    const int tiles = (L + kKeyTile - 1) / kKeyTile;
-    if (L <= 1024) return 1;
-    int split = tiles < 64 ? tiles : 64;
-    return split;
+int xattn_splits(long S, int L) {
+    // enough (slice, range) workgroups to fill the chip (about 1024), at
+    // most one range per 64-key tile and 64 ranges per slice
+    const long tiles = (L + kKeyTile - 1) / kKeyTile;
+    const long want = (1024 + S - 1) / S;
+    long split = tiles < want ? tiles : want;
+    return (int)(split < 64 ? split : 64);
 }
 
 static int keys_per_split(int L, int nsplit) {
@@ -52,8 +53,10 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     __shared__ uint8_t sm_ok[kKeyTile];
 
     const int tid = threadIdx.x;
-    const int split = blockIdx.x % nsplit;
-    const long s = blockIdx.x / nsplit;
+    const int nchunk = (Kc + kChunk - 1) / kChunk;
+    const int chunk = blockIdx.x % nchunk;
+    const int split = (blockIdx.x / nchunk) % nsplit;
+    const long s = blockIdx.x / nchunk / nsplit;
     const int j0 = split * kps;
     const int j1 = min(L, j0 + kps);
     const long skv = kv_slice(s, H, G);
@@ -62,7 +65,8 @@ __global__ __launch_bounds__(256) void centroid_xattn_kernel(
     const int cl = tid >> 4, t = tid & 15;
     const float scale = 1.0f / sqrtf((float)kD);
 
-    for (int c0 = 0; c0 < Kc; c0 += kChunk) {
+    {
+        const int c0 = chunk * kChunk;
         const int ck = min(kChunk, Kc - c0);
         __syncthreads();
         for (int e = tid; e < ck * (kD / 4); e += 256) {
@@ -175,10 +179,11 @@ template <typename T>
 static hipError_t xattn_dispatch(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, const uint8_t *valid, int H, int G, float *vcent,
                                  float *partials, float *stats, hipStream_t st) {
-    const int nsplit = xattn_splits(L);
+    const int nsplit = xattn_splits(S, L);
     const int kps = keys_per_split(L, nsplit);
     const int used = (L + kps - 1) / kps;   // ranges that hold keys
-    const dim3 grid((unsigned)((long)S * used)), block(256);
+    const int nchunk = (Kc + kChunk - 1) / kChunk;
+    const dim3 grid((unsigned)((long)S * used * nchunk)), block(256);
     hipLaunchKernelGGL(centroid_xattn_kernel<T>, grid, block, 0, st, mu,
                        static_cast<const T *>(K), static_cast<const T *>(V), L, Kc, used, kps,
                        valid, H, G, vcent, partials, stats);

@@ -88,7 +88,8 @@ def test_workspace_sizes():
     assert b.cluster_attn_workspace_size(1, 12, 8192, 64, 64, b.CA_F32, b.CA_PATH_STAGED) > 0
     assert b.cluster_attn_workspace_size(1, 1, 128, 32, 16) == 0          # unsupported d
     assert lib.ca_centroid_update_workspace_size(4, 100, 64, 8) > 0
-    assert lib.ca_centroid_xattn_workspace_size(4, 128, 64, 8) == 0        # one key range
+    assert lib.ca_centroid_xattn_workspace_size(4, 64, 64, 8) == 0         # one key range
+    assert lib.ca_centroid_xattn_workspace_size(1024, 128, 64, 8) == 0     # enough slices
     assert lib.ca_centroid_xattn_workspace_size(4, 8192, 64, 8) > 0
 
 
