@@ -147,13 +147,19 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     int32_t *pcnt = reinterpret_cast<int32_t *>(ws + lay.part_cnt);
     float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
-    const int ntile = kmeans_tiles(L);
+    const bool km_mfma = kmeans_mfma_supported(Kc);
+    const int nblk = km_mfma ? kmeans_mfma_blocks(L) : kmeans_tiles(L);
     for (int t = 1; t <= iters; ++t) {
         // a kept empty cluster of the first update needs mu^(0) in place
-        CA_TRY(launch_kmeans_assign(Q, t == 1 ? nullptr : mu, (int)S, L, Kc, dt, c, psum, pcnt,
-                                    stream, var.init_step,
-                                    t == 1 && var.keep_empty ? mu : nullptr));
-        CA_TRY(launch_centroid_reduce(psum, pcnt, ntile, (int)S, Kc, mu, nullptr, stream,
+        const float *mu_in = t == 1 ? nullptr : mu;
+        float *mu0 = t == 1 && var.keep_empty ? mu : nullptr;
+        if (km_mfma)
+            CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, c, psum, pcnt, stream,
+                                      var.init_step, mu0));
+        else
+            CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, c, psum, pcnt, stream,
+                                        var.init_step, mu0));
+        CA_TRY(launch_centroid_reduce(psum, pcnt, nblk, (int)S, Kc, mu, nullptr, stream,
                                       var.keep_empty));
     }
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
