@@ -49,7 +49,7 @@ struct StagedLayout {
 StagedLayout staged_layout(long S, int L, int Kc) {
     StagedLayout w{};
     const long ntile = kmeans_tiles(L);
-    const long nsplit = xattn_splits(S, L);
+    const long nsplit = xattn_splits(L);
     size_t off = 0;
     w.mu = off;       off += align_up(sizeof(float) * S * Kc * kD);
     w.assign = off;   off += align_up(sizeof(int32_t) * S * L);
@@ -180,7 +180,7 @@ struct BwdLayout {
 BwdLayout bwd_layout(long S, int L, int Kc) {
     BwdLayout w{};
     const long ntile = bwd_tiles(L) > kmeans_tiles(L) ? bwd_tiles(L) : kmeans_tiles(L);
-    const long nsplit = xattn_splits(S, L);
+    const long nsplit = xattn_splits(L);
     size_t off = 0;
     w.mu = off;     off += align_up(sizeof(float) * S * Kc * kD);
     w.counts = off; off += align_up(sizeof(int32_t) * S * Kc);
@@ -469,7 +469,7 @@ ca_status_t ca_centroid_update(const void *Q, const int32_t *assign, int S, int 
 
 size_t ca_centroid_xattn_workspace_size(int S, int L, int d, int Kc) {
     if (check_step(S, L, d, Kc, CA_F32) != CA_OK) return 0;
-    const int nsplit = xattn_splits(S, L);
+    const int nsplit = xattn_splits(L);
     return nsplit > 1 ? align_up(sizeof(float) * (size_t)S * nsplit * Kc * (kD + 2)) : 0;
 }
 

@@ -141,12 +141,23 @@ __global__ __launch_bounds__(256) void centroid_reduce_kernel(
     const long s = e / per;
     const long r = e % per;
     const int k = (int)(r / kD);
-    float acc = 0.f;
+    // eight running sums over blocks b = u mod 8 keep eight loads in flight;
+    // they meet in a fixed order
+    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int n = 0;
-    for (int b = 0; b < nblk; ++b) {
-        acc += part_sum[(s * nblk + b) * per + r];
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            a8[u] += part_sum[(s * nblk + b + u) * per + r];
+            n += part_cnt[(s * nblk + b + u) * Kc + k];
+        }
+    }
+    for (int u = 0; b < nblk; ++b, ++u) {
+        a8[u] += part_sum[(s * nblk + b) * per + r];
         n += part_cnt[(s * nblk + b) * Kc + k];
     }
+    const float acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
     if (!(keep_empty && n == 0)) mu[e] = acc / (float)(n > 1 ? n : 1);
     if (counts && (r % kD) == 0) counts[s * Kc + k] = n;
 }

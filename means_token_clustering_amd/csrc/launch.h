@@ -49,7 +49,7 @@ hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int 
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr);
 
 // key ranges per slice of the centroid cross-attention (partials when > 1)
-int xattn_splits(long S, int L);
+int xattn_splits(int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
 // belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
 // stats (nullable, [S, Kc, 2]): per row the largest scaled logit and the sum
