@@ -236,7 +236,8 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
 }
 
 // Merge key ranges in range order: M = max m_r, out = sum e^(m_r-M) acc_r /
-// sum e^(m_r-M) l_r.
+// sum e^(m_r-M) l_r. Eight running sums over ranges r = u mod 8 keep eight
+// loads in flight; they meet in a fixed order.
 __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restrict__ part,
                                                             int nsplit, int Kc, long total,
                                                             float *__restrict__ vcent,
@@ -246,16 +247,40 @@ __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restr
     const long sk = e / kD;           // s * Kc + k
     const int j = (int)(e % kD);
     const long s = sk / Kc, k = sk % Kc;
-    float M = -__builtin_inff();
-    for (int r = 0; r < nsplit; ++r)
-        M = fmaxf(M, part[((s * nsplit + r) * Kc + k) * kXPartStride + kD]);
-    float num = 0.f, den = 0.f;
-    for (int r = 0; r < nsplit; ++r) {
-        const float *pp = part + ((s * nsplit + r) * Kc + k) * kXPartStride;
-        const float w = exp_f32(pp[kD] - M);
-        num = fmaf(w, pp[j], num);
-        den = fmaf(w, pp[kD + 1], den);
+    const float *p0 = part + (s * nsplit * (long)Kc + k) * kXPartStride;
+    const long rs = (long)Kc * kXPartStride;   // from one range to the next
+    float m8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m8[u] = -__builtin_inff();
+    int r = 0;
+    for (; r + 8 <= nsplit; r += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], p0[(r + u) * rs + kD]);
     }
+    for (int u = 0; r < nsplit; ++r, ++u) m8[u] = fmaxf(m8[u], p0[r * rs + kD]);
+    const float M = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                          fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+    float n8[8], d8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) n8[u] = d8[u] = 0.f;
+    r = 0;
+    for (; r + 8 <= nsplit; r += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float *pp = p0 + (r + u) * rs;
+            const float wgt = exp_f32(pp[kD] - M);
+            n8[u] = fmaf(wgt, pp[j], n8[u]);
+            d8[u] = fmaf(wgt, pp[kD + 1], d8[u]);
+        }
+    }
+    for (int u = 0; r < nsplit; ++r, ++u) {
+        const float *pp = p0 + r * rs;
+        const float wgt = exp_f32(pp[kD] - M);
+        n8[u] = fmaf(wgt, pp[j], n8[u]);
+        d8[u] = fmaf(wgt, pp[kD + 1], d8[u]);
+    }
+    const float num = ((n8[0] + n8[1]) + (n8[2] + n8[3])) + ((n8[4] + n8[5]) + (n8[6] + n8[7]));
+    const float den = ((d8[0] + d8[1]) + (d8[2] + d8[3])) + ((d8[4] + d8[5]) + (d8[6] + d8[7]));
     vcent[e] = num / den;
     if (stats && j == 0) { stats[2 * sk] = M; stats[2 * sk + 1] = den; }
 }
