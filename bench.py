@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 METRIC = "cluster-attention fwd tokens/s (B·L per s, all heads) + % HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 MALL_BYTES = 256 << 20         # Infinity Cache
 
 
@@ -77,7 +78,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="distilbert",
-                   choices=["tiny", "distilbert", "bf16_l512", "long_l8192"])
+                   choices=["tiny", "distilbert", "bf16_l512", "long_l8192", "layer_bf16"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -255,6 +256,113 @@ def bench_backward(args, x, mask, b, gen, torch, np):
     print(json.dumps(rec), flush=True)
 
 
+def bench_layer(args, x, b, gen, torch, np):
+    """A step is one whole attention layer (cluster_attn_layer_forward: the
+    Q/K/V projections, cluster attention, the output projection) over the
+    batch X [B, L, 768] in bf16. The roofline record covers the dominant
+    kernel, the Q/K/V projection GEMM, timed on its own with the same
+    shape ([B*L, 768] x [768, 3*768])."""
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    B, L, Dm, H, d = x.B, x.L, x.Dm, x.H, x.d
+    Xb = to_dev(x.x)
+    Wq, Wk, Wv, Wo = (to_dev(getattr(x, nm)) for nm in ("wq", "wk", "wv", "wo"))
+    set_bytes = 2 * 2 * B * L * Dm   # X read, Y written
+    nsets = args.sets or max(2, MALL_BYTES // set_bytes + 2)
+    sets = [(Xb.clone(), torch.empty_like(Xb),
+             torch.empty((B, H, L), dtype=torch.int32, device=dev)) for _ in range(nsets)]
+    lib = b.lib()
+    need = lib.cluster_attn_layer_workspace_size(B, L, Dm, H, d, x.nclust)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    wsp, wsn = b._aligned_ptr(ws), b._ws_bytes(ws)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def step(i):
+        X, Y, c = sets[i % nsets]
+        st = lib.cluster_attn_layer_forward(X.data_ptr(), Wq.data_ptr(), Wk.data_ptr(),
+                                            Wv.data_ptr(), Wo.data_ptr(), B, L, Dm, H, d,
+                                            x.nclust, x.iters, x.W, float(x.alpha), Y.data_ptr(),
+                                            c.data_ptr(), None, wsp, wsn, sptr)
+        if st != b.CA_OK:
+            raise b.CaError(st, "cluster_attn_layer_forward")
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    ms = timed(step, args.steps, args.warmup)
+    # the projection GEMM alone: C [B*L, 3*768] = X [B*L, 768] . Wqkv, with
+    # Bt = Wqkv^T [3*768, 768] as the layer's own transpose launch prepares it
+    Bt = torch.cat([Wq.t(), Wk.t(), Wv.t()], dim=0).contiguous()
+    C = torch.empty((B * L, 3 * Dm), dtype=torch.bfloat16, device=dev)
+    gsets = [X.view(B * L, Dm) for X, _, _ in sets]
+
+    def gstep(i):
+        A = gsets[i % nsets]
+        st = lib.ca_gemm_bf16(A.data_ptr(), Bt.data_ptr(), B * L, 3 * Dm, Dm, C.data_ptr(), sptr)
+        if st != b.CA_OK:
+            raise b.CaError(st, "ca_gemm_bf16")
+
+    gms = timed(gstep, 100, 10)
+    gflops = 2.0 * B * L * Dm * 3 * Dm
+    g_tflops = gflops / (gms / 1e3) / 1e12
+    proj = 2.0 * B * L * Dm * Dm * 4
+    att = algorithmic_flops(B, H, L, d, min(x.nclust, L), x.iters, x.W)
+    rec = {"metric": "cluster-attention layer tokens/s (B·L per s) + % MFMA roofline of the "
+                     "projection GEMM",
+           "value": round(B * L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": x.name, "B": B, "L": L, "Dm": Dm, "H": H, "d": d,
+                      "K": x.nclust, "iters": x.iters, "W": x.W, "alpha": x.alpha,
+                      "input_sets": nsets},
+           "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "gemm_nt_kernel, [%d x %d] x [%d x %d]" % (B * L, Dm, Dm, 3 * Dm),
+                        "kernel_us": round(gms * 1e3, 3), "flops_per_launch": int(gflops)},
+           "compute": {"flops_per_step": int(proj + att),
+                       "achieved_TFLOPs": round((proj + att) / (ms / 1e3) / 1e12, 2),
+                       "projection_flops": int(proj), "attention_flops": int(att)}}
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_layer(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_layer(x, seconds: float):
+    """The oracle's layer on a sample of the batch: the first batch row (the
+    fp64 projections dominate; one row is 1/B of the work)."""
+    import oracle
+    X1 = x.values("x")[:1]
+    args = (x.values("wq"), x.values("wk"), x.values("wv"), x.values("wo"))
+    oracle.layer_forward(X1, *args, x.H, x.nclust, x.iters, x.W, x.alpha)   # warm
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.layer_forward(X1, *args, x.H, x.nclust, x.iters, x.W, x.alpha)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": x.L * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"batch row 0 of {x.name} (1 x {x.L} tokens, all 12 heads) run {reps} "
+                      f"times, {el:.1f} s, fp64 projections (numpy) and the C oracle"}
+
+
 def bench_decoder(args, x, mask, b, gen, torch, np):
     """A step is one causal exact attention (the decoder branch) over the batch."""
     elem = 2 if x.dtype == gen.BF16 else 4
@@ -338,6 +446,9 @@ def main():
     from means_token_clustering_amd import inputs as gen
 
     x = gen.workload(args.workload)
+    if args.workload == "layer_bf16":
+        bench_layer(args, x, b, gen, torch, np)
+        return
     if args.backward or args.decoder:
         mask = gen.make_mask(x.B, x.L, seed=x.seed + 500) if args.masked else None
         (bench_backward if args.backward else bench_decoder)(args, x, mask, b, gen, torch, np)
