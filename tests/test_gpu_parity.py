@@ -97,6 +97,10 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (2, 2, 100, 16, 3, 60, 0.4, "bf16", 6),        # wide window, ragged, bf16
     (1, 2, 128, 16, 3, 400, 0.5, "f32", 6),        # dense local branch, single launch
     (1, 2, 37, 5, 2, 33, 0.5, "f32", 3),           # radius 16 on a short ragged slice
+    (1, 2, 257, 48, 3, 32, 0.5, "f32", 12),        # one-token last block, three full groups
+    (2, 2, 129, 17, 2, 32, 0.5, "f32", 9),         # 17 clusters: a one-row last group
+    (1, 1, 640, 64, 2, 24, 0.5, "bf16", 20),       # most clusters of the matrix-core step
+    (1, 2, 200, 65, 2, 32, 0.5, "f32", 20),        # first count above it (scalar step)
 ]
 
 
@@ -274,6 +278,7 @@ MASK_EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, mask kind
     (2, 2, 128, 16, 3, 100, 0.5, gen.F32, "holes"),   # wide window
     (2, 2, 90, 8, 2, 70, 0.6, gen.BF16, "holes"),
     (1, 2, 300, 16, 3, 32, 0.5, gen.F32, "prefix"),   # staged only (L > 128)
+    (2, 2, 260, 40, 3, 20, 0.5, gen.F32, "holes"),    # staged, ragged last block
     (2, 2, 128, 16, 3, 32, 0.5, gen.F32, "zeros"),    # everything padded
 ]
 
