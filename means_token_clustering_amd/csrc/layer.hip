@@ -88,19 +88,22 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs p) {
     }
     const long astep = AHEADS ? (long)p.L * kD : kBK;   // A advance per k step
 
-    u32x4_t ra[4], rb[4];
-    auto gload = [&](int kt) {
+    const int nk = p.K / kBK;
+    // two register stages: tile t is loaded into stage t % 2 two steps before
+    // its products and stored to LDS buffer t % 2 one step before
+    u32x4_t ra[2][4], rb[2][4];
+    auto gload = [&](int kt, int sl) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            ra[q] = *reinterpret_cast<const u32x4_t *>(p.A + abase[q] + kt * astep);
-            rb[q] = *reinterpret_cast<const u32x4_t *>(Bt + bbase[q] + (long)kt * kBK);
+            ra[sl][q] = *reinterpret_cast<const u32x4_t *>(p.A + abase[q] + kt * astep);
+            rb[sl][q] = *reinterpret_cast<const u32x4_t *>(Bt + bbase[q] + (long)kt * kBK);
         }
     };
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<u32x4_t *>(&sA[buf][aoff[q]]) = ra[q];
-            *reinterpret_cast<u32x4_t *>(&sB[buf][boff[q]]) = rb[q];
+            *reinterpret_cast<u32x4_t *>(&sA[buf][aoff[q]]) = ra[buf][q];
+            *reinterpret_cast<u32x4_t *>(&sB[buf][boff[q]]) = rb[buf][q];
         }
     };
 
@@ -110,13 +113,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = p.K / kBK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    auto products = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             u32x4_t af[4], bf[4];
@@ -132,8 +129,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_nt_kernel(GemmArgs p) {
                         __builtin_bit_cast(bf16x8_t, af[j]), __builtin_bit_cast(bf16x8_t, bf[i]),
                         acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
+    };
+    // one k step on LDS buffer b (= kt % 2): request tile kt + 2, multiply
+    // tile kt, store tile kt + 1
+    auto step = [&](int kt, int b) {
+        if (kt + 2 < nk) gload(kt + 2, b);
+        products(b);
+        if (kt + 1 < nk) sstore(b ^ 1);
         __syncthreads();
+    };
+
+    gload(0, 0);
+    sstore(0);
+    if (nk > 1) gload(1, 1);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, 0);
+        if (kt + 1 < nk) step(kt + 1, 1);
     }
 
     // acc[i][j][r] = C[m0 + 64 wm + 16 i + l16][n0 + 64 wn + 16 g + 4 j + r]
