@@ -248,25 +248,15 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
         vf[c] = frag_at(pB, kPlane, 2048 * w + (lo.rl64 ^ (64 * c)));
     }
     __syncthreads();
+    // Q and g planes from the query pass's own fragments (each wave's tile
+    // rows, already scaled and split; zero rows past L and for padded queries)
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int it = tid + kThreads * n;
-        const int row = it >> 3;
-        const int o = off64(row, (it & 7) * 8);
-        float x[8], y[8];
-        load_row8<T, FULL>(Q + base, row, L, (it & 7) * 8, x);
-        load_row8<T, FULL>(dO + base, row, L, (it & 7) * 8, y);
-        const float keep = (!MASKED || row >= L || valid[brow + row] != 0) ? fg : 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i] *= fq;
-            y[i] *= keep;
-        }
-        const Sp8 qp = split8(x), gp = split8(y);
-        st16(sA + o, qp.h);
-        st16(sA + kPlaneE + o, qp.m);
-        st16(sB + o, gp.h);
-        st16(sB + kPlaneE + o, gp.m);
+    for (int c = 0; c < 2; ++c) {
+        const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
+        st16(sA + o, qf[c].h);
+        st16(sA + kPlaneE + o, qf[c].m);
+        st16(sB + o, gf[c].h);
+        st16(sB + kPlaneE + o, gf[c].m);
     }
     __syncthreads();
 
