@@ -43,18 +43,29 @@ ca_status_t check_shape(int B, int H, int L, int d, int nclust, int iters, int W
 
 // Workspace of the staged path, carved in this order (each 256-B aligned).
 struct StagedLayout {
-    size_t mu, assign, part_sum, part_cnt, vcent, xpart, total;
+    size_t mu, assign, part_sum, part_cnt, part_sum2, part_cnt2, vcent, xpart, total;
 };
+
+// Lloyd steps on the matrix cores pass their block sums straight to the next
+// step (two partial buffers, no reduce launch in between) when a slice has
+// at most this many 128-token blocks.
+constexpr int kChainBlocks = 8;
+bool chain_steps(int L, int Kc) {
+    return kmeans_mfma_supported(Kc) && kmeans_mfma_blocks(L) <= kChainBlocks;
+}
 
 StagedLayout staged_layout(long S, int L, int Kc) {
     StagedLayout w{};
     const long ntile = kmeans_tiles(L);
     const long nsplit = xattn_splits(L);
+    const long nchain = chain_steps(L, Kc) ? kmeans_mfma_blocks(L) : 0;
     size_t off = 0;
     w.mu = off;       off += align_up(sizeof(float) * S * Kc * kD);
     w.assign = off;   off += align_up(sizeof(int32_t) * S * L);
     w.part_sum = off; off += align_up(sizeof(float) * S * ntile * Kc * kD);
     w.part_cnt = off; off += align_up(sizeof(int32_t) * S * ntile * Kc);
+    w.part_sum2 = off; off += nchain ? align_up(sizeof(float) * S * nchain * Kc * kD) : 0;
+    w.part_cnt2 = off; off += nchain ? align_up(sizeof(int32_t) * S * nchain * Kc) : 0;
     w.vcent = off;    off += align_up(sizeof(float) * S * Kc * kD);
     w.xpart = off;    off += nsplit > 1 ? align_up(sizeof(float) * S * nsplit * Kc * (kD + 2)) : 0;
     w.total = off;
@@ -149,18 +160,25 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
     const bool km_mfma = kmeans_mfma_supported(Kc);
     const int nblk = km_mfma ? kmeans_mfma_blocks(L) : kmeans_tiles(L);
+    // kept empty clusters need every step's centroids in place: no chaining
+    const bool chain = chain_steps(L, Kc) && !var.keep_empty;
+    float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
+    int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
     for (int t = 1; t <= iters; ++t) {
+        const int cur = chain ? (t - 1) & 1 : 0;
         // a kept empty cluster of the first update needs mu^(0) in place
         const float *mu_in = t == 1 ? nullptr : mu;
         float *mu0 = t == 1 && var.keep_empty ? mu : nullptr;
         if (km_mfma)
-            CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, c, psum, pcnt, stream,
-                                      var.init_step, mu0));
+            CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, c, ps[cur], pc[cur], stream,
+                                      var.init_step, mu0, chain && t > 1 ? ps[cur ^ 1] : nullptr,
+                                      chain && t > 1 ? pc[cur ^ 1] : nullptr));
         else
             CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, c, psum, pcnt, stream,
                                         var.init_step, mu0));
-        CA_TRY(launch_centroid_reduce(psum, pcnt, nblk, (int)S, Kc, mu, nullptr, stream,
-                                      var.keep_empty));
+        if (!chain || t == iters)
+            CA_TRY(launch_centroid_reduce(ps[cur], pc[cur], nblk, (int)S, Kc, mu, nullptr, stream,
+                                          var.keep_empty));
     }
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                  stream));

@@ -15,7 +15,8 @@
 // running best over the groups keeps the earlier group on equal scores. The
 // block's cluster sums and sizes are one-hot products of the same planes
 // (Q^T times the [cluster][token] one-hot matrix, exact 0/1 weights), stored
-// per block; centroid_reduce_kernel adds the blocks in block order.
+// per block; centroid_reduce_kernel adds the blocks in block order, or, for
+// few blocks, the next step's workgroups add them themselves.
 // Q and the centroids are scaled by one power of two per block (the largest
 // |q| or |mu|), which leaves every comparison unchanged; the sums are scaled
 // back exactly.
@@ -43,7 +44,8 @@ template <typename T, bool INIT>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
-    int init_step, float *__restrict__ mu_init) {
+    int init_step, float *__restrict__ mu_init, const float *__restrict__ prev_sum,
+    const int32_t *__restrict__ prev_cnt) {
     __shared__ __align__(16) unsigned char smem[kKLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kKOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kKOffMu);
@@ -81,6 +83,23 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
                 *reinterpret_cast<float4 *>(mu_init + (s * Kc + mrow) * kD + mcol + 4) =
                     make_float4(mraw[4], mraw[5], mraw[6], mraw[7]);
             }
+        } else if (prev_sum) {
+            // the previous step's block sums of this slice, added in block
+            // order, over max(1, n) (the update of centroid_reduce_kernel)
+            float x[8];
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mraw[i] = 0.f;
+            for (int b2 = 0; b2 < nblk; ++b2) {
+                const long pr = (s * nblk + b2) * (long)Kc + mrow;
+                load8<float>(prev_sum + pr * kD + mcol, x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) mraw[i] += x[i];
+                n += prev_cnt[pr];
+            }
+            const float dn = (float)(n > 1 ? n : 1);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mraw[i] /= dn;
         } else {
             load8<float>(mu + (s * Kc + mrow) * kD + mcol, mraw);
         }
@@ -228,27 +247,29 @@ int kmeans_mfma_blocks(int L) { return (L + 127) / 128; }
 template <typename T>
 static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, int L, int Kc,
                                        int32_t *assign, float *part_sum, int32_t *part_cnt,
-                                       hipStream_t st, int init_step, float *mu_init) {
+                                       hipStream_t st, int init_step, float *mu_init,
+                                       const float *prev_sum, const int32_t *prev_cnt) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
     const T *q = static_cast<const T *>(Q);
     if (mu == nullptr)
         hipLaunchKernelGGL((kmeans_mfma_kernel<T, true>), grid, block, 0, st, q, mu, L, Kc, nblk,
-                           assign, part_sum, part_cnt, init_step, mu_init);
+                           assign, part_sum, part_cnt, init_step, mu_init, prev_sum, prev_cnt);
     else
         hipLaunchKernelGGL((kmeans_mfma_kernel<T, false>), grid, block, 0, st, q, mu, L, Kc, nblk,
-                           assign, part_sum, part_cnt, init_step, mu_init);
+                           assign, part_sum, part_cnt, init_step, mu_init, prev_sum, prev_cnt);
     return hipGetLastError();
 }
 
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
-                              hipStream_t st, int init_step, float *mu_init) {
+                              hipStream_t st, int init_step, float *mu_init,
+                              const float *prev_sum, const int32_t *prev_cnt) {
     if (dt == CA_BF16)
         return kmeans_mfma_dispatch<bf16_t>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                            init_step, mu_init);
+                                            init_step, mu_init, prev_sum, prev_cnt);
     return kmeans_mfma_dispatch<float>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                       init_step, mu_init);
+                                       init_step, mu_init, prev_sum, prev_cnt);
 }
 
 }  // namespace ca

@@ -41,12 +41,15 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
 // One Lloyd step on the matrix cores (kmeans_mfma.hip) for K <= 64: the
 // assignment and per-block (128 tokens) cluster sums / sizes laid out as
 // launch_kmeans_assign's partials with kmeans_mfma_blocks(L) blocks per
-// slice; part_sum == nullptr: assignment only.
+// slice; part_sum == nullptr: assignment only. With prev_sum / prev_cnt (the
+// previous step's partials) the centroids are formed from them in block
+// order instead of being read from mu.
 bool kmeans_mfma_supported(int Kc);
 int kmeans_mfma_blocks(int L);
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
-                              hipStream_t st, int init_step = 0, float *mu_init = nullptr);
+                              hipStream_t st, int init_step = 0, float *mu_init = nullptr,
+                              const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr);
 
 // key ranges per slice of the centroid cross-attention (partials when > 1)
 int xattn_splits(int L);
