@@ -164,7 +164,10 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     const bool chain = chain_steps(L, Kc) && !var.keep_empty;
     float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
     int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
-    for (int t = 1; t <= iters; ++t) {
+    const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
+    if (one_launch)
+        CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream));
+    for (int t = 1; !one_launch && t <= iters; ++t) {
         const int cur = chain ? (t - 1) & 1 : 0;
         // a kept empty cluster of the first update needs mu^(0) in place
         const float *mu_in = t == 1 ? nullptr : mu;

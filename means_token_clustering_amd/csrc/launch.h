@@ -51,6 +51,12 @@ hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int 
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr,
                               const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr);
 
+// All Lloyd iterations of each slice in one launch (kmeans_slice.hip) for
+// L <= 512, K <= 16: the last assignment and the final centroids mu [S, K, 64].
+bool kmeans_slice_supported(int L, int Kc);
+hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, ca_dtype_t dt,
+                               int32_t *assign, float *mu, int init_step, hipStream_t st);
+
 // key ranges per slice of the centroid cross-attention (partials when > 1)
 int xattn_splits(int L);
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
