@@ -522,6 +522,16 @@ def main():
     # the hot path is one kernel launch per step on the fused path; on the
     # staged path the roofline record covers the whole launch sequence
     fused = ws_bytes == 0
+    # the library's dispatch rule: one launch per slice for L <= 128 and
+    # K <= 16 (cluster_attn_fused_kernel), or for 128 < L <= 512, K <= 16,
+    # radius <= 16 without mask or listing flags (the 16-wave kernel) when
+    # forced or when the slices fill half to all of the CUs
+    kc = min(x.nclust, x.L)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = x.B * x.H
+    fused512 = (128 < x.L <= 512 and kc <= 16 and x.W // 2 <= 16 and mask is None
+                and not args.flags
+                and (args.path == "fused" or (args.path == "auto" and cus < 2 * S <= 2 * cus)))
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
     if (fused and mask is None and not args.flags and x.name == TRAFFIC["workload"]
@@ -529,7 +539,9 @@ def main():
         traffic = TRAFFIC["bytes"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": "cluster_attn_fused_kernel" if fused else "staged sequence (7+ launches)",
+            "kernel": ("cluster_attn_fused_kernel" if fused else
+                       "cluster_attn_fused512_kernel" if fused512 else
+                       "staged sequence (one launch per step)"),
             "bytes_per_launch": set_bytes}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
@@ -537,7 +549,8 @@ def main():
            "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
            "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d, "K": x.nclust,
                       "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
-                      "path": "fused" if fused else "staged", "input_sets": nsets},
+                      "path": ("fused" if fused else "fused512" if fused512 else "staged"),
+                      "input_sets": nsets},
            "roofline": roof}
     if mask is not None:
         rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "

@@ -99,8 +99,13 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V,
                                  void *workspace, size_t workspace_bytes,
                                  hipStream_t stream);
 
-/* Same as cluster_attn_forward with an explicit strategy. CA_PATH_FUSED on a
- * shape it cannot take returns CA_ERR_UNSUPPORTED. STAGED needs
+/* Same as cluster_attn_forward with an explicit strategy. CA_PATH_FUSED runs
+ * one launch per slice: any supported call with L <= 128 and nclust <= 16, or
+ * 128 < L <= 512 with min(nclust, L) <= 16, a window radius <= 16 and neither
+ * a key-padding mask nor the kept-centroid or soft-gather variants; on other
+ * shapes it returns CA_ERR_UNSUPPORTED. CA_PATH_AUTO picks the single launch
+ * for L <= 128, and for the longer shapes when the slice count fills between
+ * half and all of the device's compute units. STAGED needs
  * cluster_attn_workspace_size_ex(..., CA_PATH_STAGED) bytes. */
 ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     int B, int H, int L, int d, int nclust,

@@ -72,6 +72,20 @@ StagedLayout staged_layout(long S, int L, int Kc) {
     return w;
 }
 
+// The 16-wave single launch for 128 < L <= 512 holds one slice per CU; it
+// beats the staged launches when the slices fill between half and all of the
+// CUs in one round (measured on MI355X, bf16 L = 512: 43.5 against 50.0 us at
+// 144 slices, 47.1 against 60.1 us at 252, but 41.4 against 38.8 us at 96 and
+// 83.5 against 79.0 us at 264).
+bool fused512_pays(long S) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return false;
+    return 2 * S > cus && S <= cus;
+}
+
 bool use_fused(ca_path_t path, int L, int Kc) {
     if (path == CA_PATH_STAGED) return false;
     return fused_supported(L, Kc);
@@ -123,7 +137,6 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
                   (assign_out && overlap(valid, vbytes, assign_out, abytes))))
         return CA_ERR_INVALID_ARG;
     const int Kc = clusters(nclust, L);
-    if (path == CA_PATH_FUSED && !fused_supported(L, Kc)) return CA_ERR_UNSUPPORTED;
     Variant var{};
     if (flags & CA_FLAG_INIT_STEP) var.init_step = L / Kc > 1 ? L / Kc : 1;
     var.keep_empty = (flags & CA_FLAG_KEEP_EMPTY) != 0;
@@ -143,6 +156,13 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var,
                                                dt, valid, H, G, out, assign_out, stream));
     }
+    // 128 < L <= 512: the 16-wave single launch (forced by CA_PATH_FUSED, by
+    // the auto path when it pays)
+    const bool f512 = !valid && !var.soft && !var.keep_empty && fused512_supported(L, Kc, radius);
+    if (path == CA_PATH_FUSED && !f512) return CA_ERR_UNSUPPORTED;
+    if (f512 && (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && fused512_pays(S))))
+        return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
+                                          var.init_step, dt, H, G, out, assign_out, stream));
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;

@@ -51,6 +51,13 @@ hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int 
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr,
                               const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr);
 
+// The whole forward in one launch per slice for 128 < L <= 512, K <= 16,
+// radius <= 16, without a key-padding mask (fused512.hip); assign nullable.
+bool fused512_supported(int L, int Kc, int r);
+hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                           int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
+                           int G, void *out, int32_t *assign, hipStream_t st);
+
 // All Lloyd iterations of each slice in one launch (kmeans_slice.hip) for
 // L <= 512, K <= 16: the last assignment and the final centroids mu [S, K, 64].
 bool kmeans_slice_supported(int L, int Kc);

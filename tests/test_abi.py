@@ -77,8 +77,13 @@ def test_forward_rejects(kw, code):
 
 
 def test_fused_path_unsupported_shapes():
-    # the single-launch path only takes short sequences
+    # the single-launch paths take L <= 512 with at most 16 clusters, and
+    # beyond 128 tokens a window radius <= 16
     assert fwd(path=b.CA_PATH_FUSED, L=5000) == UNS
+    assert fwd(path=b.CA_PATH_FUSED, L=300, nclust=17) == UNS
+    assert fwd(path=b.CA_PATH_FUSED, L=513) == UNS
+    assert fwd(path=b.CA_PATH_FUSED, L=300, W=34) == UNS
+    assert fwd(path=b.CA_PATH_FUSED, L=128, nclust=17) == UNS
 
 
 def test_workspace_sizes():
@@ -178,6 +183,7 @@ def fwd_masked(**kw):
     (dict(valid=WS + 1024), INV), (dict(Q=None), INV), (dict(alpha=2.0), INV),
     (dict(iters=0), INV), (dict(ws=None), INV), (dict(d=32), UNS),
     (dict(path=b.CA_PATH_FUSED, L=5000), UNS),
+    (dict(path=b.CA_PATH_FUSED, L=300), UNS),   # no single launch with a mask beyond 128
 ])
 def test_masked_forward_rejects(kw, code):
     """The masked entry point runs the same host checks, plus: a mask is

@@ -101,6 +101,8 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (2, 2, 129, 17, 2, 32, 0.5, "f32", 9),         # 17 clusters: a one-row last group
     (1, 1, 640, 64, 2, 24, 0.5, "bf16", 20),       # most clusters of the matrix-core step
     (1, 2, 200, 65, 2, 32, 0.5, "f32", 20),        # first count above it (scalar step)
+    (2, 2, 512, 16, 3, 33, 0.5, "f32", 16),        # longest single-launch slice, radius 16
+    (1, 3, 385, 9, 2, 12, 0.7, "bf16", 9),         # three key chunks and a one-token fourth
 ]
 
 
@@ -111,6 +113,31 @@ def test_edge_cases(case, path):
     x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
                         dtype=dtype, seed=1000 + L + W, blobs=blobs, name="edge")
     check(x, path)
+
+
+# the 16-wave single launch for 128 < L <= 512, forced with CA_PATH_FUSED
+# (the auto path takes it only when the slices fill half to all of the CUs)
+SINGLE512 = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
+    (1, 2, 129, 16, 3, 32, 0.5, "f32", 8),         # two key chunks, the second of one key
+    (1, 2, 300, 16, 3, 32, 0.5, "f32", 12),        # ragged last chunk and pass
+    (2, 3, 512, 16, 3, 33, 0.5, "f32", 16),        # four full chunks, radius 16
+    (1, 3, 385, 9, 2, 12, 0.7, "bf16", 9),         # a one-token fourth chunk
+    (1, 2, 272, 4, 4, 0, 0.3, "f32", 4),           # W = 0, first pass ends on its halo
+    (2, 2, 200, 16, 1, 20, 1.0, "bf16", 6),        # one iteration, pure local branch
+    (1, 2, 450, 16, 3, 32, 0.0, "f32", 16),        # pure centroid branch
+]
+
+
+@pytest.mark.parametrize("case", SINGLE512)
+def test_single_launch_long(case):
+    B, H, L, nclust, iters, W, alpha, dtype, blobs = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
+                        dtype=dtype, seed=3000 + L + W, blobs=blobs, name="single512")
+    check(x, 1)
+
+
+def test_single_launch_long_full_batch():
+    check(gen.workload("bf16_l512"), 1)
 
 
 def test_empty_cluster_and_exact_ties():
@@ -312,6 +339,7 @@ GQA = [  # B, H, Hkv, L, W, dtype, mask kind (None: no mask)
     (2, 12, 1, 128, 32, gen.F32, "prefix"),
     (2, 6, 3, 100, 70, gen.BF16, None),
     (1, 4, 2, 300, 32, gen.F32, "holes"),
+    (2, 8, 2, 400, 24, gen.BF16, None),
 ]
 
 
