@@ -236,60 +236,72 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
 }
 
 // Merge key ranges in range order: M = max m_r, out = sum e^(m_r-M) acc_r /
-// sum e^(m_r-M) l_r. Eight running sums over ranges r = u mod 8 keep eight
-// loads in flight; they meet in a fixed order.
+// sum e^(m_r-M) l_r. One workgroup per centroid row, lane j = dimension j:
+// wave q folds ranges q, q + 4, ... (eight loads in flight per lane) into
+// (M_q, num_q, den_q), and wave 0 merges the four records in wave order.
 __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restrict__ part,
-                                                            int nsplit, int Kc, long total,
+                                                            int nsplit, int Kc,
                                                             float *__restrict__ vcent,
                                                             float *__restrict__ stats) {
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
-    const long sk = e / kD;           // s * Kc + k
-    const int j = (int)(e % kD);
+    __shared__ float rec[4][kD + 2];
+    const int q = threadIdx.x >> 6, j = threadIdx.x & 63;
+    const long sk = blockIdx.x;       // s * Kc + k
     const long s = sk / Kc, k = sk % Kc;
     const float *p0 = part + (s * nsplit * (long)Kc + k) * kXPartStride;
     const long rs = (long)Kc * kXPartStride;   // from one range to the next
-    float m8[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m8[u] = -__builtin_inff();
-    int r = 0;
-    for (; r + 8 <= nsplit; r += 8) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], p0[(r + u) * rs + kD]);
-    }
-    for (int u = 0; r < nsplit; ++r, ++u) m8[u] = fmaxf(m8[u], p0[r * rs + kD]);
-    const float M = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                          fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
-    float n8[8], d8[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) n8[u] = d8[u] = 0.f;
-    r = 0;
-    for (; r + 8 <= nsplit; r += 8) {
+    float Mq = -__builtin_inff();
+    for (int r0 = q; r0 < nsplit; r0 += 32) {
+        float m8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const float *pp = p0 + (r + u) * rs;
-            const float wgt = exp_f32(pp[kD] - M);
-            n8[u] = fmaf(wgt, pp[j], n8[u]);
-            d8[u] = fmaf(wgt, pp[kD + 1], d8[u]);
+            const int r = r0 + 4 * u;
+            m8[u] = r < nsplit ? p0[r * rs + kD] : -__builtin_inff();
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Mq = fmaxf(Mq, m8[u]);
+    }
+    float num = 0.f, den = 0.f;
+    for (int r0 = q; r0 < nsplit; r0 += 32) {
+        float w8[8], a8[8], l8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int r = r0 + 4 * u;
+            const float *pp = p0 + (r < nsplit ? r : q) * rs;
+            w8[u] = r < nsplit ? exp_f32(pp[kD] - Mq) : 0.f;
+            a8[u] = pp[j];
+            l8[u] = pp[kD + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            num = fmaf(w8[u], a8[u], num);
+            den = fmaf(w8[u], l8[u], den);
         }
     }
-    for (int u = 0; r < nsplit; ++r, ++u) {
-        const float *pp = p0 + r * rs;
-        const float wgt = exp_f32(pp[kD] - M);
-        n8[u] = fmaf(wgt, pp[j], n8[u]);
-        d8[u] = fmaf(wgt, pp[kD + 1], d8[u]);
+    rec[q][j] = num;
+    if (j == 0) {
+        rec[q][kD] = Mq;
+        rec[q][kD + 1] = den;
     }
-    const float num = ((n8[0] + n8[1]) + (n8[2] + n8[3])) + ((n8[4] + n8[5]) + (n8[6] + n8[7]));
-    const float den = ((d8[0] + d8[1]) + (d8[2] + d8[3])) + ((d8[4] + d8[5]) + (d8[6] + d8[7]));
-    vcent[e] = num / den;
-    if (stats && j == 0) { stats[2 * sk] = M; stats[2 * sk + 1] = den; }
+    __syncthreads();
+    if (q != 0) return;
+    float M = rec[0][kD];
+#pragma unroll
+    for (int u = 1; u < 4; ++u) M = fmaxf(M, rec[u][kD]);
+    float n = 0.f, d = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float f = exp_f32(rec[u][kD] - M);   // exp(-inf) = 0 for a wave without ranges
+        n = fmaf(f, rec[u][j], n);
+        d = fmaf(f, rec[u][kD + 1], d);
+    }
+    vcent[sk * kD + j] = n / d;
+    if (stats && j == 0) { stats[2 * sk] = M; stats[2 * sk + 1] = d; }
 }
 
 static hipError_t launch_xattn_combine(const float *partials, long S, int nsplit, int Kc,
                                        float *vcent, float *stats, hipStream_t st) {
-    const long total = S * Kc * kD;
-    hipLaunchKernelGGL(xattn_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                       st, partials, nsplit, Kc, total, vcent, stats);
+    hipLaunchKernelGGL(xattn_combine_kernel, dim3((unsigned)(S * Kc)), dim3(256), 0, st, partials,
+                       nsplit, Kc, vcent, stats);
     return hipGetLastError();
 }
 
