@@ -129,37 +129,47 @@ __global__ __launch_bounds__(256) void kmeans_assign_kernel(
     for (int k = tid; k < Kc; k += 256) part_cnt[base + k] = sm_n[k];
 }
 
-// mu[s,k,:] = (sum over tiles, in tile order) / max(1, n); counts optional.
+// mu[s,k,:] = (sum over the blocks) / max(1, n); counts optional.
 // keep_empty (the listing's rule): a cluster with n = 0 leaves mu[s,k,:] as
-// it was.
+// it was. One workgroup per centroid row, lane j = dimension j: wave q adds
+// blocks q, q + 4, ... (eight loads in flight per lane), and wave 0 adds the
+// four sums in wave order.
 __global__ __launch_bounds__(256) void centroid_reduce_kernel(
     const float *__restrict__ part_sum, const int32_t *__restrict__ part_cnt, int nblk, int Kc,
-    long total, float *__restrict__ mu, int32_t *__restrict__ counts, int keep_empty) {
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= total) return;
+    float *__restrict__ mu, int32_t *__restrict__ counts, int keep_empty) {
+    __shared__ float rec[4][kD];
+    __shared__ int rcnt[4];
+    const int q = threadIdx.x >> 6, j = threadIdx.x & 63;
+    const long sk = blockIdx.x;   // s * Kc + k
+    const long s = sk / Kc, k = sk % Kc;
     const long per = (long)Kc * kD;
-    const long s = e / per;
-    const long r = e % per;
-    const int k = (int)(r / kD);
-    // eight running sums over blocks b = u mod 8 keep eight loads in flight;
-    // they meet in a fixed order
-    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float *p0 = part_sum + s * nblk * per + k * kD + j;
+    const int32_t *c0 = part_cnt + s * nblk * (long)Kc + k;
+    float acc = 0.f;
     int n = 0;
-    int b = 0;
-    for (; b + 8 <= nblk; b += 8) {
+    for (int b0 = q; b0 < nblk; b0 += 32) {
+        float a8[8];
+        int n8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            a8[u] += part_sum[(s * nblk + b + u) * per + r];
-            n += part_cnt[(s * nblk + b + u) * Kc + k];
+            const int b = b0 + 4 * u;
+            a8[u] = b < nblk ? p0[b * per] : 0.f;
+            n8[u] = b < nblk ? c0[(long)b * Kc] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            acc += a8[u];
+            n += n8[u];
         }
     }
-    for (int u = 0; b < nblk; ++b, ++u) {
-        a8[u] += part_sum[(s * nblk + b) * per + r];
-        n += part_cnt[(s * nblk + b) * Kc + k];
-    }
-    const float acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
-    if (!(keep_empty && n == 0)) mu[e] = acc / (float)(n > 1 ? n : 1);
-    if (counts && (r % kD) == 0) counts[s * Kc + k] = n;
+    rec[q][j] = acc;
+    if (j == 0) rcnt[q] = n;
+    __syncthreads();
+    if (q != 0) return;
+    const float tot = ((rec[0][j] + rec[1][j]) + rec[2][j]) + rec[3][j];
+    const int nt = rcnt[0] + rcnt[1] + rcnt[2] + rcnt[3];
+    if (!(keep_empty && nt == 0)) mu[sk * kD + j] = tot / (float)(nt > 1 ? nt : 1);
+    if (counts && j == 0) counts[sk] = nt;
 }
 
 static size_t assign_lds_bytes(int Kc, bool partials) {
@@ -221,10 +231,8 @@ hipError_t launch_centroid_partials(const void *Q, const int32_t *assign, int S,
 hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt, int nblk,
                                   int S, int Kc, float *mu, int32_t *counts, hipStream_t st,
                                   bool keep_empty) {
-    const long total = (long)S * Kc * kD;
-    const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-    hipLaunchKernelGGL(centroid_reduce_kernel, grid, block, 0, st, part_sum, part_cnt, nblk, Kc,
-                       total, mu, counts, keep_empty ? 1 : 0);
+    hipLaunchKernelGGL(centroid_reduce_kernel, dim3((unsigned)((long)S * Kc)), dim3(256), 0, st,
+                       part_sum, part_cnt, nblk, Kc, mu, counts, keep_empty ? 1 : 0);
     return hipGetLastError();
 }
 

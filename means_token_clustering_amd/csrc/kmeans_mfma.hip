@@ -15,7 +15,7 @@
 // running best over the groups keeps the earlier group on equal scores. The
 // block's cluster sums and sizes are one-hot products of the same planes
 // (Q^T times the [cluster][token] one-hot matrix, exact 0/1 weights), stored
-// per block; centroid_reduce_kernel adds the blocks in block order, or, for
+// per block; centroid_reduce_kernel adds the blocks in a fixed order, or, for
 // few blocks, the next step's workgroups add them themselves.
 // Q and the centroids are scaled by one power of two per block (the largest
 // |q| or |mu|), which leaves every comparison unchanged; the sums are scaled
