@@ -374,6 +374,13 @@ def test_grouped_kv_heads(case, path):
     assert err <= tol
 
 
+@pytest.mark.parametrize("case", [(2, 8, 2, 400, 24, gen.BF16, None),
+                                  (1, 12, 4, 300, 32, gen.F32, None)])
+def test_grouped_kv_heads_single_launch_long(case):
+    """The 16-wave single launch (forced) on grouped K/V heads."""
+    test_grouped_kv_heads(case, 1)
+
+
 # ---------------------------------------------------------------- listing-compatible variants
 LF = oracle.LISTING
 LISTING = [  # B, H, L, nclust, iters, W, alpha, dtype, flags, mask kind (None: no mask)
@@ -428,6 +435,19 @@ def test_listing_variants(case, path):
                         seed=1300 + L + W + flags, blobs=8)
     mask = gen.make_mask(B, L, seed=L + 3, kind=kind) if kind else None
     check_listing(x, flags, mask, path)
+
+
+@pytest.mark.parametrize("flags,W", [
+    (oracle.INIT_STEP | oracle.BAND | oracle.ALPHA_LOGIT, 16),   # band radius 16
+    (oracle.BAND, 0),                                              # the listing's skip
+    (oracle.INIT_STEP, 32),
+])
+def test_listing_variants_single_launch_long(flags, W):
+    """The listing variants that the 16-wave single launch takes (initial
+    rows, band radius, alpha logit), forced on a 300-token batch."""
+    x = gen.make_inputs(2, 3, 300, 64, nclust=16, iters=3, W=W, alpha=0.5, dtype=gen.F32,
+                        seed=1700 + W + flags, blobs=8)
+    check_listing(x, flags, None, 1)
 
 
 @pytest.mark.parametrize("path", PATHS)
