@@ -410,14 +410,14 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
     const int trq1 = 1024 * g + (lo.tr4 ^ (32 * (w & 3)));
 
     // ------------------------------------------------------------ loads
+    // Q and dO now; K and V once the Q and g planes are written, so that
+    // they arrive during the mean and cluster-sum products
     float qraw[2][8], graw[2][8], kraw[2][8], vraw[2][8];
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n, row = it >> 3, col = (it & 7) * 8;
         load_row8<T, FULL>(Q + base, row, L, col, qraw[n]);
         load_row8<T, FULL>(dO + base, row, L, col, graw[n]);
-        load_row8<T, FULL>(Kx + base, row, L, col, kraw[n]);
-        load_row8<T, FULL>(Vx + base, row, L, col, vraw[n]);
         if (MASKED && row < L && valid[brow + row] == 0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) graw[n][i] = 0.f;
@@ -428,12 +428,8 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
     {
         const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
         const uint32_t bg = wave_max_u(__float_as_uint(absmax8(graw[1], absmax8(graw[0], 0.f))));
-        const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
-        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
         if (lane == 0) {
             sMax[8 * w] = bq;
-            sMax[8 * w + 1] = bk;
-            sMax[8 * w + 2] = bv;
             sMax[8 * w + 3] = bg;
         }
     }
@@ -450,18 +446,14 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[8 * k + 4]) : ~0u;
-    uint32_t mq = 0, mk = 0, mv = 0, mg = 0;
+    uint32_t mq = 0, mg = 0;
 #pragma unroll
     for (int ww = 0; ww < 8; ++ww) {
         mq = max(mq, sMax[8 * ww]);
-        mk = max(mk, sMax[8 * ww + 1]);
-        mv = max(mv, sMax[8 * ww + 2]);
         mg = max(mg, sMax[8 * ww + 3]);
     }
-    const int sq = scale_shift(mq, kQLimit), sk = scale_shift(mk, kKVLimit);
-    const int sv = scale_shift(mv, kBVLimit), sg = scale_shift(mg, kBVLimit);
-    const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk);
-    const float fv = __builtin_ldexpf(1.f, -sv), fg = __builtin_ldexpf(1.f, -sg);
+    const int sq = scale_shift(mq, kQLimit), sg = scale_shift(mg, kBVLimit);
+    const float fq = __builtin_ldexpf(1.f, -sq), fg = __builtin_ldexpf(1.f, -sg);
     __syncthreads();   // maxima and mask words read: the m plane of R is free
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -482,6 +474,12 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
     if (g == 0 && tok_in) {   // one-hot of the given assignment
         const int c = min(max(assign[slice * L + tok], 0), Kc - 1);
         sR[off128(c, tok)] = 0x3c00;   // fp16 1.0
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n, row = it >> 3, col = (it & 7) * 8;
+        load_row8<T, FULL>(Kx + base, row, L, col, kraw[n]);
+        load_row8<T, FULL>(Vx + base, row, L, col, vraw[n]);
     }
     __syncthreads();
 
@@ -533,7 +531,23 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
             st8(sGk + kPlaneMuE + o, p4.m);
         }
     }
+    {   // K and V maxima (slots 1 and 2 are free since the first barrier)
+        const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        if (lane == 0) {
+            sMax[8 * w + 1] = bk;
+            sMax[8 * w + 2] = bv;
+        }
+    }
     __syncthreads();
+    uint32_t mk = 0, mv = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+        mk = max(mk, sMax[8 * ww + 1]);
+        mv = max(mv, sMax[8 * ww + 2]);
+    }
+    const int sk = scale_shift(mk, kKVLimit), sv = scale_shift(mv, kBVLimit);
+    const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
     // K and V planes replace Q and g
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
