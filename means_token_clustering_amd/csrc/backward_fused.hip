@@ -71,35 +71,30 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
     const int nr = (radius + 15) >> 4;           // tiles on each side of a tile's window
 
     // ------------------------------------------------------------ loads
+    // Q and K first: their planes and fragments are formed while V and dO
+    // are still arriving
     float qraw[2][8], graw[2][8], kraw[2][8], vraw[2][8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
-        load_row8<T, FULL>(dO + base, tok, L, 32 * c + 8 * g, graw[c]);
-    }
-    const bool tok_keep = !MASKED || !tok_in || valid[brow + tok] != 0;
-    if (!tok_keep) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) graw[c][i] = 0.f;
-    }
+    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(Q + base, tok, L, 32 * c + 8 * g, qraw[c]);
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n;
         load_row8<T, FULL>(Kx + base, it >> 3, L, (it & 7) * 8, kraw[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
         load_row8<T, FULL>(Vx + base, it >> 3, L, (it & 7) * 8, vraw[n]);
     }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) load_row8<T, FULL>(dO + base, tok, L, 32 * c + 8 * g, graw[c]);
+    const bool tok_keep = !MASKED || !tok_in || valid[brow + tok] != 0;
     {
         const uint32_t bq = wave_max_u(__float_as_uint(absmax8(qraw[1], absmax8(qraw[0], 0.f))));
-        const uint32_t bg = wave_max_u(__float_as_uint(absmax8(graw[1], absmax8(graw[0], 0.f))));
         const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
-        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
         if (lane == 0) {
             sMax[8 * w] = bq;
             sMax[8 * w + 1] = bk;
-            sMax[8 * w + 2] = bv;
-            sMax[8 * w + 3] = bg;
         }
     }
     if (MASKED && w < 2) {   // key mask of tokens 64w .. 64w+63, words 2w and 2w+1
@@ -115,29 +110,21 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         kb.w[k] = MASKED ? (uint32_t)__builtin_amdgcn_readfirstlane((int)sMax[8 * k + 4]) : ~0u;
-    uint32_t mq = 0, mk = 0, mv = 0, mg = 0;
+    uint32_t mq = 0, mk = 0;
 #pragma unroll
     for (int ww = 0; ww < 8; ++ww) {
         mq = max(mq, sMax[8 * ww]);
         mk = max(mk, sMax[8 * ww + 1]);
-        mv = max(mv, sMax[8 * ww + 2]);
-        mg = max(mg, sMax[8 * ww + 3]);
     }
     const int sq = scale_shift(mq, kQLimit), sk = scale_shift(mk, kKVLimit);
-    const int sv = scale_shift(mv, kBVLimit), sg = scale_shift(mg, kBVLimit);
     const float fq = __builtin_ldexpf(1.f, -sq), fk = __builtin_ldexpf(1.f, -sk);
-    const float fv = __builtin_ldexpf(1.f, -sv), fg = __builtin_ldexpf(1.f, -sg);
     Sp8 qf[2], gf[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        float x[8], y[8];
+        float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x[i] = qraw[c][i] * fq;
-            y[i] = graw[c][i] * fg;
-        }
+        for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
         qf[c] = split8(x);
-        gf[c] = split8(y);
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -149,6 +136,43 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
         const Sp8 kp = split8(x);
         st16(sA + o, kp.h);
         st16(sA + kPlaneE + o, kp.m);
+    }
+    // V and dO (slots 2 and 3 of the maxima are free)
+    if (!tok_keep) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) graw[c][i] = 0.f;
+    }
+    {
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        const uint32_t bg = wave_max_u(__float_as_uint(absmax8(graw[1], absmax8(graw[0], 0.f))));
+        if (lane == 0) {
+            sMax[8 * w + 2] = bv;
+            sMax[8 * w + 3] = bg;
+        }
+    }
+    __syncthreads();
+    uint32_t mv = 0, mg = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) {
+        mv = max(mv, sMax[8 * ww + 2]);
+        mg = max(mg, sMax[8 * ww + 3]);
+    }
+    const int sv = scale_shift(mv, kBVLimit), sg = scale_shift(mg, kBVLimit);
+    const float fv = __builtin_ldexpf(1.f, -sv), fg = __builtin_ldexpf(1.f, -sg);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = graw[c][i] * fg;
+        gf[c] = split8(y);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int it = tid + kThreads * n;
+        const int o = off64(it >> 3, (it & 7) * 8);
+        float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = vraw[n][i] * fv;
         const Sp8 vp = split8(x);
