@@ -164,7 +164,7 @@ def test_empty_cluster_and_exact_ties():
         assert np.abs(_host(out) - ref["out"]).max() <= 1e-4
 
 
-@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("path", PATHS + [1])   # 1: the 16-wave single launch (L = 160)
 def test_determinism_and_slice_independence(path):
     x = gen.make_inputs(2, 3, 160, 64, nclust=16, iters=3, W=32, alpha=0.5, seed=21, blobs=8)
     b = _b()
