@@ -287,8 +287,9 @@ size_t ca_centroid_update_workspace_size(int S, int L, int d, int Kc);
  * Centroid cross-attention (model card pipeline figure; ClusterFormer 3):
  * vcent[s,k] = sum_j softmax_j(mu_k . k_j / sqrt(d)) v_j over all L keys.
  *   mu in fp32 [S,Kc,d]; K, V in [S,L,d] dtype dt; vcent out fp32 [S,Kc,d];
- *   workspace of ca_centroid_xattn_workspace_size(S,L,d,Kc) bytes (split-key
- *   partials combined in a fixed order).
+ *   workspace of ca_centroid_xattn_workspace_size(S,L,d,Kc) bytes (0 for
+ *   L <= 128; otherwise the partials of the 128-key ranges, combined in a
+ *   fixed order).
  */
 ca_status_t ca_centroid_xattn(const float *mu, const void *K, const void *V,
                               int S, int L, int d, int Kc, ca_dtype_t dt,
