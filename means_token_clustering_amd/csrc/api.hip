@@ -203,11 +203,16 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
             CA_TRY(launch_centroid_reduce(ps[cur], pc[cur], nblk, (int)S, Kc, mu, nullptr, stream,
                                           var.keep_empty));
     }
+    const bool mfma_local = !var.soft && local_mfma_supported(radius);
+    // a few key ranges: the window kernel merges them, no combine launch
+    const bool merge_in_local =
+        mfma_local && xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
-                                 stream));
-    if (!var.soft && local_mfma_supported(radius))
+                                 stream, nullptr, !merge_in_local));
+    if (mfma_local)
         return hip_status(launch_local_mfma(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha,
-                                            valid, H, G, out, stream));
+                                            valid, H, G, out, stream,
+                                            merge_in_local ? xpart : nullptr));
     CA_TRY(launch_local_window(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha, valid, H, G,
                                out, nullptr, stream, var.soft ? mu : nullptr));
     return CA_OK;

@@ -66,14 +66,20 @@ hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, c
 
 // key ranges per slice of the centroid cross-attention (partials when > 1)
 int xattn_splits(int L);
+// one range partial: acc[64] (unnormalised context), largest logit (natural-log
+// units), sum of exp(logit - largest); [S, nsplit, Kc] of them
+constexpr int kXPartStride = 64 + 2;
+// ranges whose partials the window kernel merges itself (no combine launch)
+constexpr int kXMergeInLocal = 4;
 // valid: key-padding mask [B, L] (nonzero = real token) or nullptr; slice s
 // belongs to batch row s / H. G: query heads per K/V head (see kv_slice).
 // stats (nullable, [S, Kc, 2]): per row the largest scaled logit and the sum
-// of exp(logit - largest).
+// of exp(logit - largest). combine = false leaves more than one range as
+// partials only (vcent untouched), for launch_local_mfma to merge.
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
                                  float *vcent, float *partials, hipStream_t st,
-                                 float *stats = nullptr);
+                                 float *stats = nullptr, bool combine = true);
 
 // Window |i - j| <= r. With oloc == nullptr the gather + fusion epilogue
 // writes out; mu != nullptr selects the soft gather over the centroids mu.
@@ -82,12 +88,14 @@ hipError_t launch_local_window(const void *Q, const void *K, const void *V, int 
                                float alpha, const uint8_t *valid, int H, int G, void *out,
                                float *oloc, hipStream_t st, const float *mu = nullptr);
 // The same window branch with the fused epilogue on the matrix cores
-// (local_mfma.hip), for radius r <= 16 and the hard gather.
+// (local_mfma.hip), for radius r <= 16 and the hard gather. With xpart set
+// (xattn_splits(L) ranges, 2 .. kXMergeInLocal), the gathered row is merged
+// from the unmerged range partials instead of read from vcent.
 bool local_mfma_supported(int r);
 hipError_t launch_local_mfma(const void *Q, const void *K, const void *V, int S, int L, int r,
                              ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
                              float alpha, const uint8_t *valid, int H, int G, void *out,
-                             hipStream_t st);
+                             hipStream_t st, const float *xpart = nullptr);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);

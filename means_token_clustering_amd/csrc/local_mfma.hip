@@ -33,6 +33,8 @@ constexpr int kMOffV = 2 * kMPlane;
 constexpr int kMLds = 4 * kMPlane;           // 81,920 B: two workgroups per CU
 constexpr int kMChunks = kMRows * kD / 8;    // 8-element chunks per staged tensor
 constexpr int kMItems = (kMChunks + kThreads - 1) / kThreads;
+constexpr int kTabRows = 16;                 // V^cent table in LDS for Kc <= 16
+constexpr int kTabStride = kD + 4;           // floats per table row (bank spread)
 
 }  // namespace
 
@@ -40,7 +42,8 @@ template <typename T, bool MASKED>
 __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int rad,
     int nblk, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
-    float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out) {
+    float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out,
+    const float *__restrict__ xpart, int nsplit) {
     __shared__ __align__(16) unsigned char smem[kMLds];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem);
     uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kMOffV);
@@ -82,6 +85,26 @@ __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
             for (int i = 0; i < 8; ++i) kraw[n][i] = vraw[n][i] = 0.f;
         }
     }
+    // V^cent rows of the slice, requested with the inputs (Kc <= 16): thread
+    // t holds row t / 32, dims 2 (t % 32) .. of the table; with xpart the rows
+    // are merged from the key-range partials (range order, as the combine)
+    const bool table = Kc <= kTabRows;
+    const int tk = tid >> 5, td = 2 * (tid & 31);
+    float2 tpa[kXMergeInLocal], tpml[kXMergeInLocal];
+    if (table && tk < Kc) {
+        if (xpart) {
+            const float *p0 = xpart + (s * nsplit * (long)Kc + tk) * kXPartStride;
+#pragma unroll
+            for (int r = 0; r < kXMergeInLocal; ++r) {
+                const float *pr = p0 + (r < nsplit ? r : 0) * (long)Kc * kXPartStride;
+                tpml[r] = *reinterpret_cast<const float2 *>(pr + kD);
+                tpa[r] = *reinterpret_cast<const float2 *>(pr + td);
+            }
+        } else {
+            tpa[0] = *reinterpret_cast<const float2 *>(vcent + (s * Kc + tk) * kD + td);
+        }
+    }
+    const int cpre = tok < L ? assign[s * L + tok] : 0;
     {
         float mk = 0.f, mv = 0.f;
 #pragma unroll
@@ -154,6 +177,29 @@ __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
             }
         }
     }
+    float2 tab = {0.f, 0.f};
+    if (table && tk < Kc) {
+        if (xpart) {
+            float M = tpml[0].x;
+#pragma unroll
+            for (int r = 1; r < kXMergeInLocal; ++r) M = r < nsplit ? fmaxf(M, tpml[r].x) : M;
+            float e[kXMergeInLocal], den = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+            for (int r = 0; r < kXMergeInLocal; ++r) {
+                e[r] = r < nsplit ? exp_f32(tpml[r].x - M) : 0.f;
+                den = fmaf(e[r], tpml[r].y, den);
+            }
+            const float inv = 1.0f / den;
+#pragma unroll
+            for (int r = 0; r < kXMergeInLocal; ++r) {
+                n0 = fmaf(e[r], tpa[r].x, n0);
+                n1 = fmaf(e[r], tpa[r].y, n1);
+            }
+            tab = make_float2(n0 * inv, n1 * inv);
+        } else {
+            tab = tpa[0];
+        }
+    }
     __syncthreads();
 
     f32x4_t o[4];
@@ -163,7 +209,14 @@ __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
         local_narrow<false, MASKED, KeyBits160, kMPlane>(pK, pV, qf, qt, NTp, Lp, rad, sscale2,
                                                          l16, g, lo.rl64, trv, kb, o, lsum);
     }
-    __syncthreads();   // the K planes become the output staging area
+    __syncthreads();   // the K planes become the output staging area, the V
+                       // planes the V^cent table
+    const float *sTab = reinterpret_cast<const float *>(smem + kMOffV);
+    if (table) {
+        if (tk < Kc)
+            *reinterpret_cast<float2 *>(smem + kMOffV + 4 * (tk * kTabStride + td)) = tab;
+        __syncthreads();
+    }
 
     // fused rows of the wave's tile through a wave-private LDS tile (16 rows,
     // 16-byte chunks XOR-swizzled by the row), then whole-row stores
@@ -174,14 +227,64 @@ __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
     {
         const bool tok_in = tok < L;
         const float f = alpha * __builtin_ldexpf(1.f, sv) * __builtin_amdgcn_rcpf(lsum);
-        const int c = tok_in ? min(max(assign[s * L + tok], 0), Kc - 1) : 0;
-        const float *vc = vcent + (s * Kc + c) * kD;
+        const int c = tok_in ? min(max(cpre, 0), Kc - 1) : 0;
         const bool keep = tok_in && (!MASKED || valid[brow + tok] != 0);
         const float wg = 1.0f - alpha;
+        float4 cv[4];   // V^cent_c, dims 16j + 4g ..
+        if (table) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cv[j] = *reinterpret_cast<const float4 *>(sTab + c * kTabStride + 16 * j + 4 * g);
+        } else if (xpart) {
+            // merge the key-range partials of row (s, c) in range order:
+            // V^cent = sum_r e^(m_r - M) acc_r / sum_r e^(m_r - M) l_r
+            const float *p0 = xpart + (s * nsplit * (long)Kc + c) * kXPartStride;
+            const long rs = (long)Kc * kXPartStride;
+            float m[kXMergeInLocal], l[kXMergeInLocal];
+            float2 a[kXMergeInLocal][4][2];
+#pragma unroll
+            for (int r = 0; r < kXMergeInLocal; ++r) {
+                const float *pr = p0 + (r < nsplit ? r : 0) * rs;
+                const float2 ml = *reinterpret_cast<const float2 *>(pr + kD);
+                m[r] = r < nsplit ? ml.x : -__builtin_inff();
+                l[r] = ml.y;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {   // 8-byte aligned: the stride is 66 floats
+                    a[r][j][0] = *reinterpret_cast<const float2 *>(pr + 16 * j + 4 * g);
+                    a[r][j][1] = *reinterpret_cast<const float2 *>(pr + 16 * j + 4 * g + 2);
+                }
+            }
+            float M = m[0];
+#pragma unroll
+            for (int r = 1; r < kXMergeInLocal; ++r) M = fmaxf(M, m[r]);
+            float e[kXMergeInLocal], den = 0.f;
+#pragma unroll
+            for (int r = 0; r < kXMergeInLocal; ++r) {
+                e[r] = r < nsplit ? exp_f32(m[r] - M) : 0.f;
+                den = fmaf(e[r], l[r], den);
+            }
+            const float inv = 1.0f / den;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float n0 = 0.f, n1 = 0.f, n2 = 0.f, n3 = 0.f;
+#pragma unroll
+                for (int r = 0; r < kXMergeInLocal; ++r) {
+                    n0 = fmaf(e[r], a[r][j][0].x, n0);
+                    n1 = fmaf(e[r], a[r][j][0].y, n1);
+                    n2 = fmaf(e[r], a[r][j][1].x, n2);
+                    n3 = fmaf(e[r], a[r][j][1].y, n3);
+                }
+                cv[j] = make_float4(n0 * inv, n1 * inv, n2 * inv, n3 * inv);
+            }
+        } else {
+            const float *vc = vcent + (s * Kc + c) * kD;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cv[j] = load4<float>(vc + 16 * j + 4 * g);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
             const int d0 = 16 * j + 4 * g;
-            const float4 c4 = load4<float>(vc + d0);
+            const float4 c4 = cv[j];
             float v0 = fmaf(o[j][0], f, wg * c4.x), v1 = fmaf(o[j][1], f, wg * c4.y);
             float v2 = fmaf(o[j][2], f, wg * c4.z), v3 = fmaf(o[j][3], f, wg * c4.w);
             if (!keep) v0 = v1 = v2 = v3 = 0.f;
@@ -215,29 +318,33 @@ template <typename T>
 static hipError_t local_mfma_dispatch(const void *Q, const void *K, const void *V, int S, int L,
                                       int r, const float *vcent, const int32_t *assign, int Kc,
                                       float alpha, const uint8_t *valid, int H, int G, void *out,
-                                      hipStream_t st) {
+                                      hipStream_t st, const float *xpart) {
     const int nblk = (L + 127) / 128;
+    const int nsplit = xattn_splits(L);
+    if (xpart && (nsplit < 2 || nsplit > kXMergeInLocal)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
     const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K);
     const T *v = static_cast<const T *>(V);
     if (valid)
         hipLaunchKernelGGL((local_mfma_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, nblk,
-                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out));
+                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), xpart,
+                           nsplit);
     else
         hipLaunchKernelGGL((local_mfma_kernel<T, false>), grid, block, 0, st, q, k, v, L, r, nblk,
-                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out));
+                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), xpart,
+                           nsplit);
     return hipGetLastError();
 }
 
 hipError_t launch_local_mfma(const void *Q, const void *K, const void *V, int S, int L, int r,
                              ca_dtype_t dt, const float *vcent, const int32_t *assign, int Kc,
                              float alpha, const uint8_t *valid, int H, int G, void *out,
-                             hipStream_t st) {
+                             hipStream_t st, const float *xpart) {
     if (dt == CA_BF16)
         return local_mfma_dispatch<bf16_t>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H,
-                                           G, out, st);
+                                           G, out, st, xpart);
     return local_mfma_dispatch<float>(Q, K, V, S, L, r, vcent, assign, Kc, alpha, valid, H, G,
-                                      out, st);
+                                      out, st, xpart);
 }
 
 }  // namespace ca

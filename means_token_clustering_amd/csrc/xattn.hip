@@ -36,7 +36,6 @@ constexpr int kXOffXl = kXOffXm + kFK * 8 * 4;       // [16][8] per-wave sums
 constexpr int kXOffMax = kXOffXl + kFK * 8 * 4;      // [8][4] tensor maxima, mask words
 constexpr int kXLdsM = kXOffMax + 8 * 4 * 4;
 static_assert(kXLdsM <= 81920, "two workgroups per CU");
-constexpr int kXPartStride = kD + 2;                 // acc[64], max, sum
 
 }  // namespace
 
@@ -249,33 +248,32 @@ __global__ __launch_bounds__(256) void xattn_combine_kernel(const float *__restr
     const long s = sk / Kc, k = sk % Kc;
     const float *p0 = part + (s * nsplit * (long)Kc + k) * kXPartStride;
     const long rs = (long)Kc * kXPartStride;   // from one range to the next
-    float Mq = -__builtin_inff();
+    // one pass over the wave's ranges (r = q, q + 4, ...), eight loads of each
+    // kind in flight, with a running maximum: a single pass up to 32 ranges
+    float Mq = -__builtin_inff(), num = 0.f, den = 0.f;
     for (int r0 = q; r0 < nsplit; r0 += 32) {
-        float m8[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int r = r0 + 4 * u;
-            m8[u] = r < nsplit ? p0[r * rs + kD] : -__builtin_inff();
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) Mq = fmaxf(Mq, m8[u]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int r0 = q; r0 < nsplit; r0 += 32) {
-        float w8[8], a8[8], l8[8];
+        float m8[8], a8[8], l8[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int r = r0 + 4 * u;
             const float *pp = p0 + (r < nsplit ? r : q) * rs;
-            w8[u] = r < nsplit ? exp_f32(pp[kD] - Mq) : 0.f;
+            m8[u] = r < nsplit ? pp[kD] : -__builtin_inff();
             a8[u] = pp[j];
             l8[u] = pp[kD + 1];
         }
+        float Mn = Mq;   // finite: range r0 exists
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Mn = fmaxf(Mn, m8[u]);
+        const float f = exp_f32(Mq - Mn);   // 0 on the first pass
+        num *= f;
+        den *= f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            num = fmaf(w8[u], a8[u], num);
-            den = fmaf(w8[u], l8[u], den);
+            const float w = exp_f32(m8[u] - Mn);   // 0 past the last range
+            num = fmaf(w, a8[u], num);
+            den = fmaf(w, l8[u], den);
         }
+        Mq = Mn;
     }
     rec[q][j] = num;
     if (j == 0) {
@@ -310,7 +308,8 @@ int xattn_splits(int L) { return (L + 127) / 128; }
 template <typename T>
 static hipError_t xattn_mfma_dispatch(const float *mu, const void *K, const void *V, int S, int L,
                                       int Kc, const uint8_t *valid, int H, int G, float *vcent,
-                                      float *partials, float *stats, hipStream_t st) {
+                                      float *partials, float *stats, bool combine,
+                                      hipStream_t st) {
     const int nsplit = xattn_splits(L);
     const dim3 grid((unsigned)((long)S * nsplit)), block(kThreads);
     const T *k = static_cast<const T *>(K), *v = static_cast<const T *>(V);
@@ -321,18 +320,19 @@ static hipError_t xattn_mfma_dispatch(const float *mu, const void *K, const void
         hipLaunchKernelGGL((xattn_mfma_kernel<T, false>), grid, block, 0, st, mu, k, v, L, Kc,
                            nsplit, valid, H, G, vcent, partials, stats);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || nsplit == 1) return err;
+    if (err != hipSuccess || nsplit == 1 || !combine) return err;
     return launch_xattn_combine(partials, S, nsplit, Kc, vcent, stats, st);
 }
 
 hipError_t launch_centroid_xattn(const float *mu, const void *K, const void *V, int S, int L,
                                  int Kc, ca_dtype_t dt, const uint8_t *valid, int H, int G,
-                                 float *vcent, float *partials, hipStream_t st, float *stats) {
+                                 float *vcent, float *partials, hipStream_t st, float *stats,
+                                 bool combine) {
     if (dt == CA_BF16)
         return xattn_mfma_dispatch<bf16_t>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials,
-                                           stats, st);
+                                           stats, combine, st);
     return xattn_mfma_dispatch<float>(mu, K, V, S, L, Kc, valid, H, G, vcent, partials, stats,
-                                      st);
+                                      combine, st);
 }
 
 }  // namespace ca
