@@ -43,7 +43,7 @@ ca_status_t check_shape(int B, int H, int L, int d, int nclust, int iters, int W
 
 // Workspace of the staged path, carved in this order (each 256-B aligned).
 struct StagedLayout {
-    size_t mu, assign, part_sum, part_cnt, part_sum2, part_cnt2, vcent, xpart, total;
+    size_t mu, assign, part_sum, part_cnt, part_sum2, part_cnt2, vcent, xpart, oloc, total;
 };
 
 // Lloyd steps on the matrix cores pass their block sums straight to the next
@@ -68,6 +68,8 @@ StagedLayout staged_layout(long S, int L, int Kc) {
     w.part_cnt2 = off; off += nchain ? align_up(sizeof(int32_t) * S * nchain * Kc) : 0;
     w.vcent = off;    off += align_up(sizeof(float) * S * Kc * kD);
     w.xpart = off;    off += nsplit > 1 ? align_up(sizeof(float) * S * nsplit * Kc * (kD + 2)) : 0;
+    // alpha O^loc rows when the window runs beside the clustering
+    w.oloc = off;     off += kmeans_slice_supported(L, Kc) ? align_up(sizeof(float) * S * L * kD) : 0;
     w.total = off;
     return w;
 }
@@ -77,13 +79,27 @@ StagedLayout staged_layout(long S, int L, int Kc) {
 // CUs in one round (measured on MI355X, bf16 L = 512: 43.5 against 50.0 us at
 // 144 slices, 47.1 against 60.1 us at 252, but 41.4 against 38.8 us at 96 and
 // 83.5 against 79.0 us at 264).
-bool fused512_pays(long S) {
+int device_cus() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-        return false;
-    return 2 * S > cus && S <= cus;
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return cus;
+}
+
+bool fused512_pays(long S) {
+    const int cus = device_cus();
+    return cus > 0 && 2 * S > cus && S <= cus;
+}
+
+// The window blocks beside the clustering fill CUs that the clustering
+// (one workgroup per slice) leaves idle: taken when the clustering and the
+// window workgroups (two 128-query blocks each) fit the CUs in one round
+// (measured, bf16 L = 512: 25.9 against 30.7 us at 48 slices; at 96 slices,
+// which need 288 workgroups, 36.6 against 35.4 us).
+bool window_beside_pays(long S, int L) {
+    const int cus = device_cus();
+    return cus > 0 && S + S * ((L + 127) / 128) / 2 <= cus;
 }
 
 bool use_fused(ca_path_t path, int L, int Kc) {
@@ -185,6 +201,20 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
     int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
     const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
+    if (one_launch && !var.soft && !valid && kmeans_window_supported(S, L, Kc, radius) &&
+        window_beside_pays(S, L)) {
+        // clustering and window blocks in one launch, then the centroid
+        // attention (its key ranges left unmerged up to kXMergeInLocal) and
+        // the gather of (1 - alpha) V^cent_{c_i} onto alpha O^loc
+        float *oloc = reinterpret_cast<float *>(ws + lay.oloc);
+        const bool merge = xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+        CA_TRY(launch_kmeans_window(Q, K, V, (int)S, L, Kc, iters, dt, c, mu, var.init_step,
+                                    radius, alpha, H, G, oloc, stream));
+        CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, nullptr, H, G, vcent, xpart,
+                                     stream, nullptr, !merge));
+        return hip_status(launch_gather_oloc(oloc, c, vcent, merge ? xpart : nullptr, (int)S, L,
+                                             Kc, alpha, dt, out, stream));
+    }
     if (one_launch)
         CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream));
     for (int t = 1; !one_launch && t <= iters; ++t) {

@@ -20,8 +20,7 @@
 // as the single-launch forward does. Q is scaled by one power of two per
 // slice (the centroids, means of its rows, follow); the centroids are scaled
 // back exactly when stored.
-#include "launch.h"
-#include "mfma_split.h"
+#include "local_mfma_body.h"
 
 namespace ca {
 namespace {
@@ -42,10 +41,11 @@ static_assert(kSLds <= 163840, "one workgroup per CU");
 }  // namespace
 
 template <typename T>
-__global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
-    const T *__restrict__ Q, int L, int Kc, int iters, int init_step,
-    int32_t *__restrict__ assign, float *__restrict__ mu_out) {
-    __shared__ __align__(16) unsigned char smem[kSLds];
+__device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L, int Kc,
+                                                  int iters, int init_step,
+                                                  int32_t *__restrict__ assign,
+                                                  float *__restrict__ mu_out, long s, int tid,
+                                                  unsigned char *smem) {
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kSOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kSOffMu);
     uint16_t *sMuX = reinterpret_cast<uint16_t *>(smem + kSOffMuX);
@@ -54,9 +54,7 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
     uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kSOffMax);
     const u8 *pQ = smem + kSOffQ, *pMu = smem + kSOffMu, *pMuX = smem + kSOffMuX;
 
-    const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const long s = blockIdx.x;
     const T *Qs = Q + s * (long)L * kD;
     const int NT = (L + 15) >> 4;
     const LaneOffs lo = lane_offsets(l16, g);
@@ -237,6 +235,75 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
         }
         __syncthreads();
     }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
+    const T *__restrict__ Q, int L, int Kc, int iters, int init_step,
+    int32_t *__restrict__ assign, float *__restrict__ mu_out) {
+    __shared__ __align__(16) unsigned char smem[kSLds];
+    kmeans_slice_body<T>(Q, L, Kc, iters, init_step, assign, mu_out, blockIdx.x, threadIdx.x,
+                         smem);
+}
+
+// The clustering of S slices (workgroups 0 .. S-1) and, beside it, the window
+// branch of every 128-query block (two blocks per later workgroup, one per
+// half of its 16 waves, each with its own 80 KB of LDS), which stores
+// alpha O^loc for a later gather: the window needs no clustering result.
+constexpr int kKWLds = kSLds > 2 * kMLds ? kSLds : 2 * kMLds;
+static_assert(kKWLds <= 163840, "one workgroup per CU");
+
+template <typename T>
+__global__ __launch_bounds__(kSThreads, 1) void kmeans_window_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
+    int iters, int init_step, int32_t *__restrict__ assign_out, float *__restrict__ mu_out, int S,
+    int rad, int nblk, float alpha, int H, int G, float *__restrict__ oloc) {
+    __shared__ __align__(16) unsigned char smem[kKWLds];
+    if ((int)blockIdx.x < S) {
+        kmeans_slice_body<T>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
+                             threadIdx.x, smem);
+        return;
+    }
+    // window blocks: alpha O^loc only (no mask, no gather)
+    const int half = threadIdx.x >> 9;   // uniform per wave
+    unsigned char *const smem_all = smem;
+    {
+        unsigned char *const smem = smem_all + half * kMLds;
+        constexpr bool OLOC = true, MASKED = false;
+        const int tid = threadIdx.x & (kThreads - 1);
+        const unsigned bid = 2 * (blockIdx.x - S) + half;
+        const float *const vcent = nullptr, *const xpart = nullptr;
+        const int32_t *const assign = nullptr;
+        const uint8_t *const valid = nullptr;
+        T *const out = nullptr;
+        const int nsplit = 0;
+#include "local_mfma_body.inc"
+    }
+}
+
+bool kmeans_window_supported(long S, int L, int Kc, int r) {
+    return kmeans_slice_supported(L, Kc) && local_mfma_supported(r) &&
+           (S * ((L + 127) / 128)) % 2 == 0;
+}
+
+hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int S, int L,
+                                int Kc, int iters, ca_dtype_t dt, int32_t *assign, float *mu,
+                                int init_step, int r, float alpha, int H, int G, float *oloc,
+                                hipStream_t st) {
+    const int nblk = (L + 127) / 128;
+    if (!kmeans_window_supported(S, L, Kc, r)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(S + (long)S * nblk / 2)), block(kSThreads);
+    if (dt == CA_BF16)
+        hipLaunchKernelGGL(kmeans_window_kernel<bf16_t>, grid, block, 0, st,
+                           static_cast<const bf16_t *>(Q), static_cast<const bf16_t *>(K),
+                           static_cast<const bf16_t *>(V), L, Kc, iters, init_step, assign, mu,
+                           S, r, nblk, alpha, H, G, oloc);
+    else
+        hipLaunchKernelGGL(kmeans_window_kernel<float>, grid, block, 0, st,
+                           static_cast<const float *>(Q), static_cast<const float *>(K),
+                           static_cast<const float *>(V), L, Kc, iters, init_step, assign, mu,
+                           S, r, nblk, alpha, H, G, oloc);
+    return hipGetLastError();
 }
 
 bool kmeans_slice_supported(int L, int Kc) { return L >= 1 && L <= kSL && Kc >= 1 && Kc <= kFK; }
