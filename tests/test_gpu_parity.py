@@ -103,6 +103,11 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 2, 200, 65, 2, 32, 0.5, "f32", 20),        # first count above it (scalar step)
     (2, 2, 512, 16, 3, 33, 0.5, "f32", 16),        # longest single-launch slice, radius 16
     (1, 3, 385, 9, 2, 12, 0.7, "bf16", 9),         # three key chunks and a one-token fourth
+    # staged: window blocks in the clustering launch (S x blocks even), gather after
+    (1, 3, 160, 16, 3, 32, 0.5, "f32", 8),         # six window blocks, two key ranges
+    (1, 2, 384, 12, 3, 20, 0.6, "bf16", 10),       # three ranges, ragged clusters
+    # staged: S x blocks odd, the launches in sequence
+    (1, 1, 300, 16, 3, 32, 0.5, "bf16", 10),       # three blocks
 ]
 
 
