@@ -201,7 +201,7 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
     int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
     const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
-    if (one_launch && !var.soft && !valid && kmeans_window_supported(S, L, Kc, radius) &&
+    if (one_launch && !var.soft && kmeans_window_supported(S, L, Kc, radius) &&
         window_beside_pays(S, L)) {
         // clustering and window blocks in one launch, then the centroid
         // attention (its key ranges left unmerged up to kXMergeInLocal) and
@@ -209,11 +209,11 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         float *oloc = reinterpret_cast<float *>(ws + lay.oloc);
         const bool merge = xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
         CA_TRY(launch_kmeans_window(Q, K, V, (int)S, L, Kc, iters, dt, c, mu, var.init_step,
-                                    radius, alpha, H, G, oloc, stream));
-        CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, nullptr, H, G, vcent, xpart,
+                                    radius, alpha, valid, H, G, oloc, stream));
+        CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                      stream, nullptr, !merge));
         return hip_status(launch_gather_oloc(oloc, c, vcent, merge ? xpart : nullptr, (int)S, L,
-                                             Kc, alpha, dt, out, stream));
+                                             Kc, alpha, valid, H, dt, out, stream));
     }
     if (one_launch)
         CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream));

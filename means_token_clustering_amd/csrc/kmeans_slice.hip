@@ -253,28 +253,29 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
 constexpr int kKWLds = kSLds > 2 * kMLds ? kSLds : 2 * kMLds;
 static_assert(kKWLds <= 163840, "one workgroup per CU");
 
-template <typename T>
+template <typename T, bool MASKED_IN>
 __global__ __launch_bounds__(kSThreads, 1) void kmeans_window_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
     int iters, int init_step, int32_t *__restrict__ assign_out, float *__restrict__ mu_out, int S,
-    int rad, int nblk, float alpha, int H, int G, float *__restrict__ oloc) {
+    int rad, int nblk, float alpha, const uint8_t *__restrict__ valid_in, int H, int G,
+    float *__restrict__ oloc) {
     __shared__ __align__(16) unsigned char smem[kKWLds];
     if ((int)blockIdx.x < S) {
         kmeans_slice_body<T>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
                              threadIdx.x, smem);
         return;
     }
-    // window blocks: alpha O^loc only (no mask, no gather)
+    // window blocks: alpha O^loc only (no gather; padded query rows zero)
     const int half = threadIdx.x >> 9;   // uniform per wave
     unsigned char *const smem_all = smem;
     {
         unsigned char *const smem = smem_all + half * kMLds;
-        constexpr bool OLOC = true, MASKED = false;
+        constexpr bool OLOC = true, MASKED = MASKED_IN;
         const int tid = threadIdx.x & (kThreads - 1);
         const unsigned bid = 2 * (blockIdx.x - S) + half;
         const float *const vcent = nullptr, *const xpart = nullptr;
         const int32_t *const assign = nullptr;
-        const uint8_t *const valid = nullptr;
+        const uint8_t *const valid = valid_in;
         T *const out = nullptr;
         const int nsplit = 0;
 #include "local_mfma_body.inc"
@@ -288,21 +289,22 @@ bool kmeans_window_supported(long S, int L, int Kc, int r) {
 
 hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int S, int L,
                                 int Kc, int iters, ca_dtype_t dt, int32_t *assign, float *mu,
-                                int init_step, int r, float alpha, int H, int G, float *oloc,
-                                hipStream_t st) {
+                                int init_step, int r, float alpha, const uint8_t *valid, int H,
+                                int G, float *oloc, hipStream_t st) {
     const int nblk = (L + 127) / 128;
     if (!kmeans_window_supported(S, L, Kc, r)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(S + (long)S * nblk / 2)), block(kSThreads);
-    if (dt == CA_BF16)
-        hipLaunchKernelGGL(kmeans_window_kernel<bf16_t>, grid, block, 0, st,
-                           static_cast<const bf16_t *>(Q), static_cast<const bf16_t *>(K),
-                           static_cast<const bf16_t *>(V), L, Kc, iters, init_step, assign, mu,
-                           S, r, nblk, alpha, H, G, oloc);
-    else
-        hipLaunchKernelGGL(kmeans_window_kernel<float>, grid, block, 0, st,
-                           static_cast<const float *>(Q), static_cast<const float *>(K),
-                           static_cast<const float *>(V), L, Kc, iters, init_step, assign, mu,
-                           S, r, nblk, alpha, H, G, oloc);
+#define CA_KW_LAUNCH(TT, M)                                                                      \
+    hipLaunchKernelGGL((kmeans_window_kernel<TT, M>), grid, block, 0, st,                        \
+                       static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
+                       static_cast<const TT *>(V), L, Kc, iters, init_step, assign, mu, S, r,    \
+                       nblk, alpha, valid, H, G, oloc)
+    if (dt == CA_BF16) {
+        if (valid) CA_KW_LAUNCH(bf16_t, true); else CA_KW_LAUNCH(bf16_t, false);
+    } else {
+        if (valid) CA_KW_LAUNCH(float, true); else CA_KW_LAUNCH(float, false);
+    }
+#undef CA_KW_LAUNCH
     return hipGetLastError();
 }
 

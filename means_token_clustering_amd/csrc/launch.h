@@ -98,17 +98,19 @@ hipError_t launch_local_mfma(const void *Q, const void *K, const void *V, int S,
                              hipStream_t st, const float *xpart = nullptr);
 // The clustering (kmeans_slice) with the window blocks of the same slices
 // beside it in one launch (every slice's block count times S even): the
-// window blocks store alpha O^loc as fp32 [S, L, 64] rows in oloc, and
+// window blocks store alpha O^loc as fp32 [S, L, 64] rows in oloc (zero for
+// padded queries when valid is set), and
 // launch_gather_oloc forms out = (1 - alpha) V^cent_{c_i} + that row (with
 // xpart: V^cent merged from 2 .. kXMergeInLocal key-range partials).
 bool kmeans_window_supported(long S, int L, int Kc, int r);
 hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int S, int L,
                                 int Kc, int iters, ca_dtype_t dt, int32_t *assign, float *mu,
-                                int init_step, int r, float alpha, int H, int G, float *oloc,
-                                hipStream_t st);
+                                int init_step, int r, float alpha, const uint8_t *valid, int H,
+                                int G, float *oloc, hipStream_t st);
 hipError_t launch_gather_oloc(const float *oloc, const int32_t *assign, const float *vcent,
                               const float *xpart, int S, int L, int Kc, float alpha,
-                              ca_dtype_t dt, void *out, hipStream_t st);
+                              const uint8_t *valid, int H, ca_dtype_t dt, void *out,
+                              hipStream_t st);
 hipError_t launch_gather_fuse(const float *vcent, const int32_t *assign, const float *oloc, int S,
                               int L, int Kc, float alpha, ca_dtype_t dt, void *out,
                               hipStream_t st);

@@ -49,7 +49,7 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void gather_oloc_kernel(
     const float *__restrict__ oloc, const int32_t *__restrict__ assign,
     const float *__restrict__ vcent, const float *__restrict__ xpart, int nsplit, int L, int Kc,
-    float alpha, T *__restrict__ out) {
+    float alpha, const uint8_t *__restrict__ valid, int H, T *__restrict__ out) {
     __shared__ __align__(16) float tab[kTabRows * kTabStride];
     const int nb = (L + 127) / 128, tid = threadIdx.x;
     const long s = blockIdx.x / nb;
@@ -99,8 +99,9 @@ __global__ __launch_bounds__(kThreads) void gather_oloc_kernel(
         const f32x4_t ol =
             __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(oloc + row));
         const float4 vc = *reinterpret_cast<const float4 *>(tab + c * kTabStride + d0);
-        const float v0 = fmaf(wg, vc.x, ol[0]), v1 = fmaf(wg, vc.y, ol[1]);
-        const float v2 = fmaf(wg, vc.z, ol[2]), v3 = fmaf(wg, vc.w, ol[3]);
+        float v0 = fmaf(wg, vc.x, ol[0]), v1 = fmaf(wg, vc.y, ol[1]);
+        float v2 = fmaf(wg, vc.z, ol[2]), v3 = fmaf(wg, vc.w, ol[3]);
+        if (valid && valid[(s / H) * (long)L + i] == 0) v0 = v1 = v2 = v3 = 0.f;   // padded query
         if (sizeof(T) == 4) {
             __builtin_nontemporal_store(f32x4_t{v0, v1, v2, v3},
                                         reinterpret_cast<f32x4_t *>(out + row));
@@ -115,17 +116,18 @@ __global__ __launch_bounds__(kThreads) void gather_oloc_kernel(
 
 hipError_t launch_gather_oloc(const float *oloc, const int32_t *assign, const float *vcent,
                               const float *xpart, int S, int L, int Kc, float alpha,
-                              ca_dtype_t dt, void *out, hipStream_t st) {
+                              const uint8_t *valid, int H, ca_dtype_t dt, void *out,
+                              hipStream_t st) {
     const int nsplit = xattn_splits(L);
     if ((xpart && (nsplit < 2 || nsplit > kXMergeInLocal)) || Kc > kTabRows)
         return hipErrorInvalidValue;
     const dim3 grid((unsigned)((long)S * ((L + 127) / 128))), block(kThreads);
     if (dt == CA_BF16)
         hipLaunchKernelGGL(gather_oloc_kernel<bf16_t>, grid, block, 0, st, oloc, assign, vcent,
-                           xpart, nsplit, L, Kc, alpha, static_cast<bf16_t *>(out));
+                           xpart, nsplit, L, Kc, alpha, valid, H, static_cast<bf16_t *>(out));
     else
         hipLaunchKernelGGL(gather_oloc_kernel<float>, grid, block, 0, st, oloc, assign, vcent,
-                           xpart, nsplit, L, Kc, alpha, static_cast<float *>(out));
+                           xpart, nsplit, L, Kc, alpha, valid, H, static_cast<float *>(out));
     return hipGetLastError();
 }
 
