@@ -80,6 +80,8 @@ def parse():
     p.add_argument("--workload", default="distilbert",
                    choices=["tiny", "distilbert", "bf16_l512", "long_l8192", "layer_bf16"])
     p.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
+    p.add_argument("--batch", type=int, default=0,
+                   help="batch size B of the attention workload (0 = the workload's own)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0 = auto)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU-oracle baseline (0 disables it)")
@@ -445,7 +447,7 @@ def main():
     from means_token_clustering_amd import binding as b
     from means_token_clustering_amd import inputs as gen
 
-    x = gen.workload(args.workload)
+    x = gen.workload(args.workload, B=args.batch or None)
     if args.workload == "layer_bf16":
         bench_layer(args, x, b, gen, torch, np)
         return
@@ -534,7 +536,8 @@ def main():
                 and (args.path == "fused" or (args.path == "auto" and cus < 2 * S <= 2 * cus)))
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
-    if (fused and mask is None and not args.flags and x.name == TRAFFIC["workload"]
+    if (fused and mask is None and not args.flags and not args.batch
+            and x.name == TRAFFIC["workload"]
             and code_digest() == TRAFFIC["digest"]):
         traffic = TRAFFIC["bytes"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

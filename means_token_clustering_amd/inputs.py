@@ -157,21 +157,22 @@ def make_layer_inputs(B: int = 16, L: int = 512, Dm: int = 768, H: int = 12,
 
 # The five workloads: name -> constructor. Sizes follow the model card's
 # DistilBERT shape (12 heads of 64, L=128, B=32) and three variations of it.
-def workload(name: str, seed: Optional[int] = None):
+def workload(name: str, seed: Optional[int] = None, B: Optional[int] = None):
+    """The named workload; B overrides the batch size of the attention ones."""
     if name == "tiny":
-        return make_inputs(1, 2, 128, 64, nclust=16, iters=3, W=32, alpha=0.5,
+        return make_inputs(B or 1, 2, 128, 64, nclust=16, iters=3, W=32, alpha=0.5,
                            dtype=F32, seed=1 if seed is None else seed,
                            blobs=None, name=name)
     if name == "distilbert":
-        return make_inputs(32, 12, 128, 64, nclust=16, iters=3, W=32, alpha=0.5,
+        return make_inputs(B or 32, 12, 128, 64, nclust=16, iters=3, W=32, alpha=0.5,
                            dtype=F32, seed=2 if seed is None else seed,
                            blobs=16, name=name)
     if name == "bf16_l512":
-        return make_inputs(8, 12, 512, 64, nclust=16, iters=3, W=32, alpha=0.5,
+        return make_inputs(B or 8, 12, 512, 64, nclust=16, iters=3, W=32, alpha=0.5,
                            dtype=BF16, seed=3 if seed is None else seed,
                            blobs=16, name=name)
     if name == "long_l8192":
-        return make_inputs(1, 12, 8192, 64, nclust=64, iters=5, W=32, alpha=0.5,
+        return make_inputs(B or 1, 12, 8192, 64, nclust=64, iters=5, W=32, alpha=0.5,
                            dtype=F32, seed=4 if seed is None else seed,
                            blobs=64, name=name)
     if name == "layer_bf16":
