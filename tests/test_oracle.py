@@ -368,6 +368,56 @@ def test_matmul_and_heads():
     assert np.array_equal(oracle.merge_heads(q).reshape(2, 5, 24)[:, :, 8:16], q[:, 1])
 
 
+def test_output_projection_permutation_and_rectangular():
+    """Y = O_merged W_O (model card pipeline figure, the last step; ClusterFormer
+    section 3, last row of the tensor trace), with W_O stored [H*d, Dm].
+
+    A permutation W_O moves column p of the merged heads to column perm[p];
+    a rectangular W_O (Dm != H*d) checks orientation against numpy. Every
+    entry of O is a distinct small integer (exact in bf16), so a transposed
+    W_O or a wrong head order changes the result."""
+    B, H, L, d = 2, 3, 4, 4
+    O = np.arange(B * H * L * d, dtype=np.float64).reshape(B, H, L, d) - 40.0
+    perm = np.random.default_rng(7).permutation(H * d)
+    P = np.zeros((H * d, H * d))
+    P[np.arange(H * d), perm] = 1.0
+    Y = oracle.output_projection(O, P)
+    assert Y.shape == (B, L, H * d)
+    for b in range(B):
+        for i in range(L):
+            for h in range(H):
+                for t in range(d):
+                    assert Y[b, i, perm[h * d + t]] == O[b, h, i, t]
+    Wr = np.round(np.random.default_rng(8).standard_normal((H * d, 5)) * 8) / 8   # Dm = 5
+    Yr = oracle.output_projection(O, Wr)
+    merged = np.concatenate([O[:, h] for h in range(H)], axis=-1)   # [B, L, H*d]
+    assert Yr.shape == (B, L, 5)
+    assert np.allclose(Yr, merged @ Wr, rtol=0, atol=1e-12)
+
+
+def test_layer_forward_closed_form_uniform_attention():
+    """Layer composition on a case with a closed form: W_Q = W_K = 0 makes every
+    score zero, so both softmaxes are uniform and, for any alpha, every token's
+    output is the mean of its batch row's V = X W_V rows (the window of radius
+    L covers the whole sequence); with W_V = I and W_O a permutation, row i of
+    Y is that mean of X permuted. X holds small integers and L = 4, so every
+    value stays exact in bf16."""
+    B, L, H, d = 2, 4, 2, 4
+    Dm = H * d
+    rng = np.random.default_rng(9)
+    X = rng.integers(-3, 4, size=(B, L, Dm)).astype(np.float64)
+    Z = np.zeros((Dm, Dm))
+    perm = rng.permutation(Dm)
+    P = np.zeros((Dm, Dm))
+    P[np.arange(Dm), perm] = 1.0
+    for alpha in (0.0, 0.5, 1.0):
+        res = oracle.layer_forward(X, Z, Z, np.eye(Dm), P, H, 2, 2, 2 * L, alpha)
+        mean = X.mean(axis=1)   # [B, Dm]
+        for b in range(B):
+            for i in range(L):
+                assert np.array_equal(res["Y"][b, i, perm], mean[b])
+
+
 # ------------------------------------------------ P10: key-padding mask
 # Semantics (ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-
 # cluster" page, forward, bidirectional branch): a padded key's logit is -10000
