@@ -26,9 +26,12 @@ if ROOT not in sys.path:
 
 METRIC = "cluster-attention fwd tokens/s (B·L per s, all heads) + % HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (vector and matrix)
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix (v_mfma_f32_*_f16)
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 MALL_BYTES = 256 << 20         # Infinity Cache
+SPLIT_PRODUCTS = 3             # fp32-accurate contraction = 3 fp16 products of an h/m split
+REPEATS = 5                    # timed groups inside the K steps (their median is reported)
+PARITY_REPORT = os.path.join(ROOT, "profiles", "parity_report.md")
 
 
 # HBM traffic of the fused kernel on the distilbert workload, measured with
@@ -70,6 +73,88 @@ def algorithmic_flops(B, H, L, d, K, iters, W) -> int:
     P = sum(min(L - 1, i + r) - max(0, i - r) + 1 for i in range(L))
     per = 2 * iters * L * K * d + iters * L * d + 4 * K * L * d + 4 * P * d + 3 * L * d
     return B * H * per
+
+
+def contraction_flops(B, H, L, d, K, iters, W) -> int:
+    """The algorithmic FLOPs of the contractions alone (distances 2ILKd,
+    centroid attention 4KLd, local window 4Pd, per slice): the work the fp16
+    matrix cores carry, SPLIT_PRODUCTS times over."""
+    r = W // 2
+    P = sum(min(L - 1, i + r) - max(0, i - r) + 1 for i in range(L))
+    return B * H * (2 * iters * L * K * d + 4 * K * L * d + 4 * P * d)
+
+
+def compute_record(x, ms) -> dict:
+    """Rates of one step: all algorithmic FLOPs, and the fp16 matrix-core work
+    (every fp32-accurate contraction runs as SPLIT_PRODUCTS fp16 products of an
+    h/m split) against the dense fp16 peak. The path is not bound by it."""
+    kc = min(x.nclust, x.L)
+    flops = algorithmic_flops(x.B, x.H, x.L, x.d, kc, x.iters, x.W)
+    cf = contraction_flops(x.B, x.H, x.L, x.d, kc, x.iters, x.W)
+    mfma = SPLIT_PRODUCTS * cf / (ms / 1e3) / 1e12
+    return {"flops_per_launch": flops, "achieved_TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
+            "contraction_flops": cf, "fp16_products_per_contraction": SPLIT_PRODUCTS,
+            "achieved_fp16_mfma_TFLOPs": round(mfma, 2), "peak_fp16_mfma_TFLOPs": FP16_PEAK_TFLOPS,
+            "frac": round(mfma / FP16_PEAK_TFLOPS, 4)}
+
+
+def parity_summary(workload: str):
+    """The parity record of this workload from profiles/parity_report.md (made
+    by tests/test_gpu_parity_report.py on the GPU); None if absent."""
+    try:
+        text = open(PARITY_REPORT).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, flags=re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1)).get(workload)
+    if rec is None:
+        return None
+    keys = ("plan", "near_ties", "excused", "bad", "zero_centroid_tokens_last",
+            "free_running_mismatches", "max_dist_err_rel", "near_tie_window", "max_out_err", "tol")
+    out = {k: rec.get(k) for k in keys}
+    out["near_ties_by_iter"] = [i["near_ties"] for i in rec.get("iterations", [])]
+    out["source"] = ("profiles/parity_report.md (python -m pytest tests/test_gpu_parity_report.py "
+                     "-m gpu; P0 protocol of tests/parity.py)")
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def timed_steps(torch, stream, step, steps: int, warmup: int):
+    """W untimed steps, then exactly K timed steps between two synchronisations,
+    with HIP events on the launch stream at the ends and at REPEATS - 1 group
+    boundaries inside. Returns (ms per step over all K, the groups' ms per step)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    groups = max(1, min(REPEATS, steps))
+    bounds = [round(steps * g / groups) for g in range(groups + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    ev[0].record(stream)
+    for g in range(groups):
+        for i in range(bounds[g], bounds[g + 1]):
+            step(i)
+        ev[g + 1].record(stream)
+    torch.cuda.synchronize()
+    total = ev[0].elapsed_time(ev[-1]) / steps
+    per = [ev[g].elapsed_time(ev[g + 1]) / max(1, bounds[g + 1] - bounds[g]) for g in range(groups)]
+    return total, per
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 def parse():
@@ -143,23 +228,51 @@ def hbm_probe(torch, set_bytes: int) -> dict:
 
 
 def cpu_baseline(x, seconds: float, mask=None, flags: int = 0):
+    """The oracle on the same batch: three runs on all host threads (value: their
+    median) and three on one thread, each run repeating the whole batch until its
+    share of the time budget has passed."""
     import oracle
     q, k, v = x.values("q"), x.values("k"), x.values("v")
-    oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask,
-                   flags=flags)   # warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def once():
         oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask,
                        flags=flags)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    tokens = x.B * x.L * reps
-    return {"value": tokens / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}) run {reps} times "
-                      f"back to back, {el:.1f} s, fp64 C oracle with OpenMP over slices"}
+
+    return _cpu_legs(once, x.B * x.L, seconds,
+                     f"the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}), fp64 C oracle with "
+                     f"OpenMP over slices")
+
+
+def _cpu_legs(once, tokens: int, seconds: float, what: str):
+    import oracle
+    cores = oracle.num_threads()
+
+    def leg(budget):
+        rates, reps_all = [], []
+        once()   # warm
+        for _ in range(3):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                once()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget / 3:
+                    break
+            rates.append(tokens * reps / el)
+            reps_all.append(reps)
+        return median(rates), reps_all
+
+    value, reps = leg(0.75 * seconds)
+    oracle.set_num_threads(1)
+    try:
+        one, reps1 = leg(0.25 * seconds)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}; median of 3 runs of {reps} batch repeats on {cores} threads",
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": one, "cores": 1,
+                              "sample": f"median of 3 runs of {reps1} batch repeats"}}
 
 
 def cpu_baseline_backward(x, seconds: float, mask=None):
@@ -169,19 +282,10 @@ def cpu_baseline_backward(x, seconds: float, mask=None):
     dO = np.random.default_rng(x.seed + 600).standard_normal(q.shape)
     c = oracle.forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, trace=False, valid=mask)["assign"]
     K = oracle.num_clusters(x.nclust, x.L)
-    oracle.backward(q, k, v, dO, c, K, x.W, x.alpha, valid=mask)   # warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.backward(q, k, v, dO, c, K, x.W, x.alpha, valid=mask)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": x.B * x.L * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"the backward pass of the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}) "
-                      f"on the oracle's own assignment, {reps} times back to back, {el:.1f} s, "
-                      f"fp64 C oracle with OpenMP over slices"}
+    return _cpu_legs(lambda: oracle.backward(q, k, v, dO, c, K, x.W, x.alpha, valid=mask),
+                     x.B * x.L, seconds,
+                     f"the backward pass of the whole {x.name} batch (B={x.B}, H={x.H}, L={x.L}) "
+                     f"on the oracle's own assignment, fp64 C oracle with OpenMP over slices")
 
 
 def bench_backward(args, x, mask, b, gen, torch, np):
@@ -226,17 +330,7 @@ def bench_backward(args, x, mask, b, gen, torch, np):
         if st != b.CA_OK:
             raise b.CaError(st, "cluster_attn_backward")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, groups = timed_steps(torch, stream, step, args.steps, args.warmup)
     achieved = set_bytes / (ms / 1e3) / 1e9
     rec = {"metric": "cluster-attention bwd tokens/s (B·L per s, all heads) + % HBM roofline",
            "value": round(x.B * x.L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -246,6 +340,7 @@ def bench_backward(args, x, mask, b, gen, torch, np):
            "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d, "K": x.nclust,
                       "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
                       "pass": "backward", "input_sets": nsets},
+           "timing": {"groups": len(groups), "median_ms_per_step": round(median(groups), 6)},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                         "traffic": None, "kernel": "backward launch sequence",
@@ -293,19 +388,9 @@ def bench_layer(args, x, b, gen, torch, np):
             raise b.CaError(st, "cluster_attn_layer_forward")
 
     def timed(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(steps):
-            fn(i)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        return timed_steps(torch, stream, fn, steps, warmup)[0]
 
-    ms = timed(step, args.steps, args.warmup)
+    ms, groups = timed_steps(torch, stream, step, args.steps, args.warmup)
     # the projection GEMM alone: C [B*L, 3*768] = X [B*L, 768] . Wqkv, with
     # Bt = Wqkv^T [3*768, 768] as the layer's own transpose launch prepares it
     Bt = torch.cat([Wq.t(), Wk.t(), Wv.t()], dim=0).contiguous()
@@ -332,6 +417,7 @@ def bench_layer(args, x, b, gen, torch, np):
            "config": {"workload": x.name, "B": B, "L": L, "Dm": Dm, "H": H, "d": d,
                       "K": x.nclust, "iters": x.iters, "W": x.W, "alpha": x.alpha,
                       "input_sets": nsets},
+           "timing": {"groups": len(groups), "median_ms_per_step": round(median(groups), 6)},
            "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
@@ -351,18 +437,11 @@ def cpu_baseline_layer(x, seconds: float):
     import oracle
     X1 = x.values("x")[:1]
     args = (x.values("wq"), x.values("wk"), x.values("wv"), x.values("wo"))
-    oracle.layer_forward(X1, *args, x.H, x.nclust, x.iters, x.W, x.alpha)   # warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.layer_forward(X1, *args, x.H, x.nclust, x.iters, x.W, x.alpha)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": x.L * reps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"batch row 0 of {x.name} (1 x {x.L} tokens, all 12 heads) run {reps} "
-                      f"times, {el:.1f} s, fp64 projections (numpy) and the C oracle"}
+    return _cpu_legs(lambda: oracle.layer_forward(X1, *args, x.H, x.nclust, x.iters, x.W,
+                                                  x.alpha),
+                     x.L, seconds,
+                     f"batch row 0 of {x.name} (1 x {x.L} tokens, all {x.H} heads), fp64 "
+                     f"projections and the C oracle")
 
 
 def bench_decoder(args, x, mask, b, gen, torch, np):
@@ -394,17 +473,7 @@ def bench_decoder(args, x, mask, b, gen, torch, np):
         if st != b.CA_OK:
             raise b.CaError(st, "cluster_attn_exact_forward")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, groups = timed_steps(torch, stream, step, args.steps, args.warmup)
     achieved = set_bytes / (ms / 1e3) / 1e9
     rec = {"metric": "causal exact attention (decoder branch) tokens/s + % HBM roofline",
            "value": round(x.B * x.L / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -413,6 +482,7 @@ def bench_decoder(args, x, mask, b, gen, torch, np):
            "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
            "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d,
                       "storage": x.dtype, "pass": "decoder", "input_sets": nsets},
+           "timing": {"groups": len(groups), "median_ms_per_step": round(median(groups), 6)},
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                         "traffic": None,
@@ -421,18 +491,9 @@ def bench_decoder(args, x, mask, b, gen, torch, np):
     if args.cpu_seconds > 0:
         import oracle
         q, k, v = x.values("q"), x.values("k"), x.values("v")
-        oracle.exact_attention(q, k, v, True, qvalid=mask, kvalid=mask)
-        reps, c0 = 0, time.perf_counter()
-        while True:
-            oracle.exact_attention(q, k, v, True, qvalid=mask, kvalid=mask)
-            reps += 1
-            el = time.perf_counter() - c0
-            if el >= args.cpu_seconds:
-                break
-        rec["cpu_baseline"] = {"value": x.B * x.L * reps / el, "unit": "tokens/s",
-                               "cores": oracle.num_threads(), "kind": "oracle",
-                               "sample": f"causal exact attention of the whole {x.name} batch, "
-                                         f"{reps} times back to back, {el:.1f} s, fp64 C oracle"}
+        rec["cpu_baseline"] = _cpu_legs(
+            lambda: oracle.exact_attention(q, k, v, True, qvalid=mask, kvalid=mask), x.B * x.L,
+            args.cpu_seconds, f"causal exact attention of the whole {x.name} batch, fp64 C oracle")
     print(json.dumps(rec), flush=True)
 
 
@@ -507,33 +568,14 @@ def main():
         if st != b.CA_OK:
             raise b.CaError(st, "cluster_attn_forward")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    ms, groups = timed_steps(torch, stream, step, args.steps, args.warmup)
     tokens = x.B * x.L
     value = tokens / (ms / 1e3)
 
-    # the hot path is one kernel launch per step on the fused path; on the
-    # staged path the roofline record covers the whole launch sequence
-    fused = ws_bytes == 0
-    # the library's dispatch rule: one launch per slice for L <= 128 and
-    # K <= 16 (cluster_attn_fused_kernel), or for 128 < L <= 512, K <= 16,
-    # radius <= 16 without mask or listing flags (the 16-wave kernel) when
-    # forced or when the slices fill half to all of the CUs
-    kc = min(x.nclust, x.L)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    S = x.B * x.H
-    fused512 = (128 < x.L <= 512 and kc <= 16 and x.W // 2 <= 16 and mask is None
-                and not args.flags
-                and (args.path == "fused" or (args.path == "auto" and cus < 2 * S <= 2 * cus)))
+    # the launch sequence the library takes (its own dispatch decision)
+    plan = b.cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, flags=args.flags,
+                               masked=mask is not None, path=path)
+    fused = plan == "fused"
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
     if (fused and mask is None and not args.flags and not args.batch
@@ -543,8 +585,8 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ("cluster_attn_fused_kernel" if fused else
-                       "cluster_attn_fused512_kernel" if fused512 else
-                       "staged sequence (one launch per step)"),
+                       "cluster_attn_fused512_kernel" if plan == "fused512" else
+                       "launch sequence " + plan),
             "bytes_per_launch": set_bytes}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
@@ -552,22 +594,31 @@ def main():
            "dtype": "bf16" if elem == 2 else "f32", "data": "synthetic",
            "config": {"workload": x.name, "B": x.B, "H": x.H, "L": x.L, "d": x.d, "K": x.nclust,
                       "iters": x.iters, "W": x.W, "alpha": x.alpha, "storage": x.dtype,
-                      "path": ("fused" if fused else "fused512" if fused512 else "staged"),
-                      "input_sets": nsets},
-           "roofline": roof}
+                      "path": plan, "input_sets": nsets},
+           "roofline": roof,
+           "timing": {"groups": len(groups), "ms_per_step_by_group": [round(g, 6) for g in groups],
+                      "median_ms_per_step": round(median(groups), 6),
+                      "note": "the K timed steps split into equal groups between HIP events "
+                              "on the launch stream; value uses all K steps"}}
     if mask is not None:
         rec["config"]["mask"] = (f"right padding, row lengths ~ U{{{max(1, x.L // 4)}..{x.L}}}, "
                                  f"{int(mask.sum())} of {mask.size} tokens real")
     if args.flags:
         rec["config"]["flags"] = args.flags
-    flops = algorithmic_flops(x.B, x.H, x.L, x.d, min(x.nclust, x.L), x.iters, x.W)
-    tflops = flops / (ms / 1e3) / 1e12
-    rec["compute"] = {"flops_per_launch": flops, "achieved_TFLOPs": round(tflops, 2),
-                      "peak_fp32_TFLOPs": FP32_PEAK_TFLOPS,
-                      "frac": round(tflops / FP32_PEAK_TFLOPS, 4)}
+    rec["compute"] = compute_record(x, ms)
+    # the same launches on one input set (reads served partly from the
+    # Infinity Cache): labelled, never the value
+    one = sets[0]
+    cms, _ = timed_steps(torch, stream, lambda i: step(0), max(1, args.steps // 2), 3)
+    rec["cache_resident"] = {"ms_per_step": round(cms, 6), "input_sets": 1,
+                             "note": "one input set reused, so reads may hit the 256 MB "
+                                     "Infinity Cache; not the headline value"}
+    del one
     if not args.no_probe:
         rec["hbm_probe"] = hbm_probe(torch, set_bytes)
         roof["frac_of_copy"] = round(achieved / rec["hbm_probe"]["copy_same_bytes_GBps"], 4)
+    if mask is None and not args.flags and not args.batch:
+        rec["parity"] = parity_summary(x.name)
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, mask, args.flags)
     print(json.dumps(rec), flush=True)

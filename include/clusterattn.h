@@ -20,9 +20,12 @@
  * Conventions shared by every entry point:
  *   - Tensors are device pointers to contiguous row-major arrays. "[B,H,L,d]"
  *     means slice s = b*H + h holds rows s*L .. s*L+L-1 of d elements each.
- *   - Storage dtype CA_F32 (float) or CA_BF16 (uint16 bf16 bits). All
- *     arithmetic is fp32; a bf16 output is rounded to nearest-even once, at
- *     the store. Centroids, centroid context and partials are always fp32.
+ *   - Storage dtype CA_F32 (float) or CA_BF16 (uint16 bf16 bits). Results
+ *     are fp32-accurate: contractions run on the fp16 matrix cores as three
+ *     products of an fp16 split (high and remainder parts) of each fp32
+ *     operand with fp32 accumulation; everything else is fp32. A bf16 output
+ *     is rounded to nearest-even once, at the store. Centroids, centroid
+ *     context and partials are always fp32.
  *   - d must be 64 (CA_ERR_UNSUPPORTED otherwise); K = min(nclust, L) must
  *     be <= 256 (CA_ERR_UNSUPPORTED otherwise).
  *   - Ownership: the caller owns every buffer, including the workspace; the
@@ -118,6 +121,18 @@ size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust,
                                       ca_dtype_t dt, ca_path_t path);
 
 /*
+ * Name of the launch sequence that cluster_attn_forward_opts (with the same
+ * B, H, L, nclust, W, flags, a mask when masked != 0, and path) takes on the
+ * current device, as a static string: "fused" (one launch per slice,
+ * L <= 128), "fused512" (one 16-wave launch per slice, 128 < L <= 512), or
+ * "staged: ..." naming its clustering, centroid-attention and window
+ * launches. NULL when such a call would be rejected. For labelling and
+ * tests; the forward decides the same way on its own.
+ */
+const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags, int masked,
+                              ca_path_t path);
+
+/*
  * Cluster attention with a key-padding mask (padded batches): the
  * ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page,
  * forward, bidirectional branch (its attention_mask path).
@@ -151,11 +166,20 @@ ca_status_t cluster_attn_forward_masked(const void *Q, const void *K, const void
  *             listing on the "Hooshaai/svd-sst2-roberta-cluster" page where it
  *             departs from the model card's equations (0 = the equations);
  *             another bit is CA_ERR_INVALID_ARG.
+ *   assign_hist  NULL, or device int32 [iters, B, H, L] (4-byte aligned)
+ *             receiving the assignment of every Lloyd iteration: slot t-1
+ *             holds c^(t), the assignment against mu^(t-1) (model card,
+ *             Mathematical Formulation 1; ClusterFormer 2.1, t = 1..iters), so
+ *             slot iters-1 equals assign_out. It must not overlap any other
+ *             argument buffer. Every path writes it; it changes no other
+ *             output. Slot t-1 equals assign_out of the same call with
+ *             iters = t (prefix determinism).
  */
 typedef struct {
     const uint8_t *valid;
     int kv_heads;
     int flags;
+    int32_t *assign_hist;
 } ca_options_t;
 
 /* Initial centroids mu_k = Q[k * max(1, floor(L / K))] (the listing's k-means
@@ -267,6 +291,20 @@ ca_status_t cluster_attn_exact_forward(const void *Q, const void *K, const void 
 ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L,
                              int d, int Kc, ca_dtype_t dt, int32_t *assign,
                              hipStream_t stream);
+
+/*
+ * Assignment scores as the matrix-core assignment step evaluates them, for
+ * measuring its distance error: scores[s, i, k] = mu_k . q_i - ||mu_k||^2 / 2
+ * (fp32, unscaled units), so that ||q_i - mu_k||^2 = ||q_i||^2 - 2 scores[s, i,
+ * k]; the step assigns token i to the k with the largest score (lowest k on
+ * ties). Same passages as ca_kmeans_assign; the arithmetic is the one every
+ * matrix-core clustering kernel uses (power-of-two scaling, fp16 h/m split,
+ * three partial products, the -||mu||^2/2 parts in the same chain).
+ *   Q in [S,L,d] dtype dt; mu in fp32 [S,Kc,d]; scores out fp32 [S,L,Kc].
+ *   Kc <= 64 (CA_ERR_UNSUPPORTED otherwise).
+ */
+ca_status_t ca_kmeans_scores(const void *Q, const float *mu, int S, int L, int d, int Kc,
+                             ca_dtype_t dt, float *scores, hipStream_t stream);
 
 /*
  * One update step (same passages): mu[s,k] = sum_{assign = k} q_i /

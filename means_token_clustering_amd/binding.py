@@ -36,6 +36,7 @@ SIGNATURES = {
     "ca_status_string": (ctypes.c_char_p, [_i]),
     "ca_version": (_i, []),
     "cluster_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "cluster_attn_plan": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "cluster_attn_workspace_size_ex": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "cluster_attn_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
                                   _vp, _sz, _vp]),
@@ -46,6 +47,7 @@ SIGNATURES = {
     "cluster_attn_forward_opts": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                        _vp, _i, _vp, _sz, _i, _vp]),
     "ca_kmeans_assign": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
+    "ca_kmeans_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "ca_centroid_update": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "ca_centroid_update_workspace_size": (_sz, [_i, _i, _i, _i]),
     "ca_centroid_xattn": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -66,7 +68,7 @@ SIGNATURES = {
 
 class CaOptions(ctypes.Structure):
     """ca_options_t of the C ABI."""
-    _fields_ = [("valid", _vp), ("kv_heads", _i), ("flags", _i)]
+    _fields_ = [("valid", _vp), ("kv_heads", _i), ("flags", _i), ("assign_hist", _vp)]
 
 
 class CaError(RuntimeError):
@@ -157,13 +159,21 @@ def _ws_bytes(ws) -> int:
     return ws.numel() * ws.element_size() - ((p + 255) // 256 * 256 - p)
 
 
+def cluster_attn_plan(B, H, L, nclust, W, flags=0, masked=False, path=CA_PATH_AUTO):
+    """Name of the launch sequence the forward takes for these arguments (None
+    when the call would be rejected)."""
+    r = lib().cluster_attn_plan(B, H, L, nclust, W, int(flags), int(bool(masked)), int(path))
+    return r.decode() if r is not None else None
+
+
 def cluster_attn_workspace_size(B, H, L, d, nclust, dtype=CA_F32, path=CA_PATH_AUTO) -> int:
     return lib().cluster_attn_workspace_size_ex(B, H, L, d, nclust, dtype, path)
 
 
 def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float, out=None,
                          assign_out=None, path: int = CA_PATH_AUTO, workspace=None,
-                         stream=None, want_assign: bool = True, valid=None, flags: int = 0):
+                         stream=None, want_assign: bool = True, valid=None, flags: int = 0,
+                         assign_hist=None):
     """Q: contiguous [B, H, L, d] float32 or bfloat16 GPU tensor; K, V:
     [B, Hkv, L, d] of the same dtype, Hkv dividing H (Hkv < H: grouped K/V
     heads, cluster_attn_forward_opts).
@@ -171,6 +181,8 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
     valid: optional key-padding mask, a contiguous [B, L] uint8 (or bool) GPU
     tensor, nonzero = real token (cluster_attn_forward_masked). flags: OR of
     CA_FLAG_* (listing-compatible variants, cluster_attn_forward_opts).
+    assign_hist: optional int32 GPU tensor [iters, B, H, L] receiving every
+    iteration's assignment (ca_options_t.assign_hist).
     Returns (out, assign_out); allocates out/assign_out/workspace with torch
     when not given.
     """
@@ -188,8 +200,11 @@ def cluster_attn_forward(Q, K, V, nclust: int, iters: int, W: int, alpha: float,
         raise ValueError("K and V must be [B, Hkv, L, d] with Q's B, L and d")
     if valid is not None and (tuple(valid.shape) != (B, L) or valid.element_size() != 1):
         raise ValueError("valid must be a [B, L] tensor of one-byte elements")
-    if hkv != H or flags:
-        opts = CaOptions(_ptr(valid), hkv, int(flags))
+    if assign_hist is not None and (tuple(assign_hist.shape) != (iters, B, H, L)
+                                    or assign_hist.dtype != torch.int32):
+        raise ValueError("assign_hist must be an int32 [iters, B, H, L] tensor")
+    if hkv != H or flags or assign_hist is not None:
+        opts = CaOptions(_ptr(valid), hkv, int(flags), _ptr(assign_hist))
         st = lib().cluster_attn_forward_opts(
             _ptr(Q), _ptr(K), _ptr(V), B, H, L, d, nclust, iters, W, float(alpha),
             ctypes.byref(opts), _ptr(out), _ptr(assign_out), dt, _aligned_ptr(ws), _ws_bytes(ws),
@@ -264,6 +279,20 @@ def ca_kmeans_assign(Q, mu, Kc: int, assign=None, stream=None):
                                 _stream(stream))
     _check(st, "ca_kmeans_assign")
     return assign
+
+
+def ca_kmeans_scores(Q, mu, scores=None, stream=None):
+    """Scores mu_k . q_i - ||mu_k||^2 / 2 of the matrix-core assignment step:
+    Q [B, H, L, d], mu fp32 [B, H, Kc, d]; returns fp32 [B, H, L, Kc]."""
+    torch = _torch()
+    B, H, L, d = Q.shape
+    Kc = mu.shape[2]
+    if scores is None:
+        scores = torch.empty((B, H, L, Kc), dtype=torch.float32, device=Q.device)
+    st = lib().ca_kmeans_scores(_ptr(Q), _ptr(mu), B * H, L, d, Kc, _dtype_code(Q), _ptr(scores),
+                                _stream(stream))
+    _check(st, "ca_kmeans_scores")
+    return scores
 
 
 def ca_centroid_update(Q, assign, Kc: int, stream=None):

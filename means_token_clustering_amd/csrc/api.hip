@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "launch.h"
 
 namespace {
@@ -25,6 +27,18 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 int clusters(int nclust, int L) { return nclust < L ? nclust : L; }
+
+struct Span {
+    const void *p;
+    size_t n;
+};
+
+bool any_overlap(const Span *s, int count) {
+    for (int i = 0; i < count; ++i)
+        for (int j = i + 1; j < count; ++j)
+            if (s[i].p && s[j].p && overlap(s[i].p, s[i].n, s[j].p, s[j].n)) return true;
+    return false;
+}
 
 // Shape checks shared by the whole-forward entry points. Returns CA_OK,
 // CA_ERR_INVALID_ARG or CA_ERR_UNSUPPORTED.
@@ -74,19 +88,30 @@ StagedLayout staged_layout(long S, int L, int Kc) {
     return w;
 }
 
+// Compute units of the current device, looked up once per device (the
+// count never changes while the process runs).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int known = g_cus[dev].load(std::memory_order_relaxed);
+        if (known > 0) return known;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev >= 0 && dev < kMaxDevices && cus > 0) g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 // The 16-wave single launch for 128 < L <= 512 holds one slice per CU; it
 // beats the staged launches when the slices fill between half and all of the
 // CUs in one round (measured on MI355X, bf16 L = 512: 43.5 against 50.0 us at
 // 144 slices, 47.1 against 60.1 us at 252, but 41.4 against 38.8 us at 96 and
 // 83.5 against 79.0 us at 264).
-int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return 0;
-    return cus;
-}
-
 bool fused512_pays(long S) {
     const int cus = device_cus();
     return cus > 0 && 2 * S > cus && S <= cus;
@@ -107,6 +132,88 @@ bool use_fused(ca_path_t path, int L, int Kc) {
     return fused_supported(L, Kc);
 }
 
+// The launch sequence of one forward call, decided on the host from the shape,
+// the variants and the device's CU count.
+enum PlanKind {
+    kPlanFused,      // cluster_attn_fused_kernel: one launch, L <= 128
+    kPlanFused512,   // cluster_attn_fused512_kernel: one launch, 128 < L <= 512
+    kPlanBeside,     // kmeans_window_kernel (clustering + window), centroid attention, gather
+    kPlanSlice,      // kmeans_slice_kernel, centroid attention, window branch
+    kPlanSteps       // one launch per Lloyd step, centroid attention, window branch
+};
+
+struct Plan {
+    PlanKind kind;
+    bool km_mfma;          // steps on the matrix cores (else the scalar step)
+    bool chain;            // steps pass their block sums on (no reduce in between)
+    bool mfma_local;       // window branch on the matrix cores (else scalar)
+    bool merge_in_local;   // the window kernel merges the key-range partials
+};
+
+// Returns CA_OK and the plan, or CA_ERR_UNSUPPORTED when CA_PATH_FUSED was
+// asked for a shape without a single launch.
+ca_status_t make_plan(long S, int L, int Kc, int radius, const Variant &var, bool masked,
+                      ca_path_t path, Plan &p) {
+    p = Plan{};
+    if (use_fused(path, L, Kc)) {
+        p.kind = kPlanFused;
+        return CA_OK;
+    }
+    // 128 < L <= 512: the 16-wave single launch (forced by CA_PATH_FUSED, by
+    // the auto path when it pays)
+    const bool f512 = !masked && !var.soft && !var.keep_empty && fused512_supported(L, Kc, radius);
+    if (path == CA_PATH_FUSED && !f512) return CA_ERR_UNSUPPORTED;
+    if (f512 && (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && fused512_pays(S)))) {
+        p.kind = kPlanFused512;
+        return CA_OK;
+    }
+    const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
+    if (one_launch && !var.soft && kmeans_window_supported(S, L, Kc, radius) &&
+        window_beside_pays(S, L)) {
+        p.kind = kPlanBeside;
+        p.merge_in_local = xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+        return CA_OK;
+    }
+    p.kind = one_launch ? kPlanSlice : kPlanSteps;
+    p.km_mfma = kmeans_mfma_supported(Kc);
+    // kept empty clusters need every step's centroids in place: no chaining
+    p.chain = chain_steps(L, Kc) && !var.keep_empty;
+    p.mfma_local = !var.soft && local_mfma_supported(radius);
+    // a few key ranges: the window kernel merges them, no combine launch
+    p.merge_in_local = p.mfma_local && xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+    return CA_OK;
+}
+
+const char *plan_name(const Plan &p) {
+    switch (p.kind) {
+        case kPlanFused: return "fused";
+        case kPlanFused512: return "fused512";
+        case kPlanBeside:
+            return p.merge_in_local ? "staged: kmeans_window, xattn ranges, gather_oloc (merge)"
+                                    : "staged: kmeans_window, xattn, gather_oloc";
+        case kPlanSlice:
+        case kPlanSteps: break;
+    }
+    // [window: scalar, matrix cores, matrix cores merging the key ranges]
+    static const char *const slice_names[3] = {
+        "staged: kmeans_slice, xattn, local_scalar", "staged: kmeans_slice, xattn, local_mfma",
+        "staged: kmeans_slice, xattn ranges, local_mfma (merge)"};
+    // [steps: chained, with reduce launches, scalar][window as above]
+    static const char *const step_names[3][3] = {
+        {"staged: kmeans_mfma steps (chained), xattn, local_scalar",
+         "staged: kmeans_mfma steps (chained), xattn, local_mfma",
+         "staged: kmeans_mfma steps (chained), xattn ranges, local_mfma (merge)"},
+        {"staged: kmeans_mfma steps + reduce, xattn, local_scalar",
+         "staged: kmeans_mfma steps + reduce, xattn, local_mfma",
+         "staged: kmeans_mfma steps + reduce, xattn ranges, local_mfma (merge)"},
+        {"staged: scalar kmeans steps + reduce, xattn, local_scalar",
+         "staged: scalar kmeans steps + reduce, xattn, local_mfma",
+         "staged: scalar kmeans steps + reduce, xattn ranges, local_mfma (merge)"}};
+    const int loc = !p.mfma_local ? 0 : p.merge_in_local ? 2 : 1;
+    if (p.kind == kPlanSlice) return slice_names[loc];
+    return step_names[!p.km_mfma ? 2 : p.chain ? 0 : 1][loc];
+}
+
 ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_HIP; }
 
 #define CA_TRY(expr)                                  \
@@ -116,12 +223,13 @@ ca_status_t hip_status(hipError_t e) { return e == hipSuccess ? CA_OK : CA_ERR_H
     } while (0)
 
 // valid: key-padding mask [B, L] or nullptr (the unmasked operation); G:
-// query heads per K/V head (K and V are [B, H / G, L, d]); flags: CA_FLAG_*.
+// query heads per K/V head (K and V are [B, H / G, L, d]); flags: CA_FLAG_*;
+// hist: nullable [iters, B, H, L] trace of every iteration's assignment.
 ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint8_t *valid, int G,
                          int flags, int B, int H, int L, int d, int nclust, int iters, int W,
                          float alpha, void *out, int32_t *assign_out, ca_dtype_t dt,
                          void *workspace, size_t workspace_bytes, ca_path_t path,
-                         hipStream_t stream) {
+                         hipStream_t stream, int32_t *hist = nullptr) {
     if (flags & ~CA_FLAG_LISTING) return CA_ERR_INVALID_ARG;
     if (flags & CA_FLAG_ALPHA_LOGIT) {   // the listing's sigmoid of its parameter
         if (alpha != alpha) return CA_ERR_INVALID_ARG;
@@ -152,6 +260,14 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (valid && (overlap(valid, vbytes, out, tbytes) ||
                   (assign_out && overlap(valid, vbytes, assign_out, abytes))))
         return CA_ERR_INVALID_ARG;
+    const size_t hbytes = abytes * (size_t)iters;
+    if (hist) {
+        const Span others[] = {{Q, tbytes}, {K, kvbytes}, {V, kvbytes}, {out, tbytes},
+                               {assign_out, abytes}, {valid, vbytes}};
+        if (!aligned(hist, 4)) return CA_ERR_INVALID_ARG;
+        for (const Span &o : others)
+            if (o.p && overlap(hist, hbytes, o.p, o.n)) return CA_ERR_INVALID_ARG;
+    }
     const int Kc = clusters(nclust, L);
     Variant var{};
     if (flags & CA_FLAG_INIT_STEP) var.init_step = L / Kc > 1 ? L / Kc : 1;
@@ -168,17 +284,16 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         }
     }
 
-    if (use_fused(path, L, Kc)) {
+    Plan plan;
+    st = make_plan(S, L, Kc, radius, var, valid != nullptr, path, plan);
+    if (st != CA_OK) return st;
+    if (plan.kind == kPlanFused)
         return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var,
-                                               dt, valid, H, G, out, assign_out, stream));
-    }
-    // 128 < L <= 512: the 16-wave single launch (forced by CA_PATH_FUSED, by
-    // the auto path when it pays)
-    const bool f512 = !valid && !var.soft && !var.keep_empty && fused512_supported(L, Kc, radius);
-    if (path == CA_PATH_FUSED && !f512) return CA_ERR_UNSUPPORTED;
-    if (f512 && (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && fused512_pays(S))))
+                                               dt, valid, H, G, out, assign_out, stream, hist));
+    if (plan.kind == kPlanFused512)
         return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
-                                          var.init_step, dt, H, G, out, assign_out, stream));
+                                          var.init_step, dt, H, G, out, assign_out, stream,
+                                          hist));
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;
@@ -186,7 +301,8 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (overlap(ws, lay.total, out, tbytes) || overlap(ws, lay.total, Q, tbytes) ||
         overlap(ws, lay.total, K, kvbytes) || overlap(ws, lay.total, V, kvbytes) ||
         (assign_out && overlap(ws, lay.total, assign_out, abytes)) ||
-        (valid && overlap(ws, lay.total, valid, vbytes)))
+        (valid && overlap(ws, lay.total, valid, vbytes)) ||
+        (hist && overlap(ws, lay.total, hist, hbytes)))
         return CA_ERR_INVALID_ARG;
     float *mu = reinterpret_cast<float *>(ws + lay.mu);
     int32_t *c = assign_out ? assign_out : reinterpret_cast<int32_t *>(ws + lay.assign);
@@ -194,49 +310,52 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     int32_t *pcnt = reinterpret_cast<int32_t *>(ws + lay.part_cnt);
     float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
-    const bool km_mfma = kmeans_mfma_supported(Kc);
+    const bool km_mfma = plan.km_mfma;
     const int nblk = km_mfma ? kmeans_mfma_blocks(L) : kmeans_tiles(L);
-    // kept empty clusters need every step's centroids in place: no chaining
-    const bool chain = chain_steps(L, Kc) && !var.keep_empty;
+    const bool chain = plan.chain;
     float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
     int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
-    const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
-    if (one_launch && !var.soft && kmeans_window_supported(S, L, Kc, radius) &&
-        window_beside_pays(S, L)) {
+    const bool one_launch = plan.kind == kPlanSlice;
+    if (plan.kind == kPlanBeside) {
         // clustering and window blocks in one launch, then the centroid
         // attention (its key ranges left unmerged up to kXMergeInLocal) and
         // the gather of (1 - alpha) V^cent_{c_i} onto alpha O^loc
         float *oloc = reinterpret_cast<float *>(ws + lay.oloc);
-        const bool merge = xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+        const bool merge = plan.merge_in_local;
         CA_TRY(launch_kmeans_window(Q, K, V, (int)S, L, Kc, iters, dt, c, mu, var.init_step,
-                                    radius, alpha, valid, H, G, oloc, stream));
+                                    radius, alpha, valid, H, G, oloc, stream, hist));
         CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                      stream, nullptr, !merge));
         return hip_status(launch_gather_oloc(oloc, c, vcent, merge ? xpart : nullptr, (int)S, L,
                                              Kc, alpha, valid, H, dt, out, stream));
     }
     if (one_launch)
-        CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream));
+        CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream,
+                                   hist));
     for (int t = 1; !one_launch && t <= iters; ++t) {
         const int cur = chain ? (t - 1) & 1 : 0;
         // a kept empty cluster of the first update needs mu^(0) in place
         const float *mu_in = t == 1 ? nullptr : mu;
         float *mu0 = t == 1 && var.keep_empty ? mu : nullptr;
+        // each step's assignment is read by no later step, so the steps
+        // before the last write theirs straight into the trace
+        int32_t *ct = hist && t < iters ? hist + (size_t)(t - 1) * S * L : c;
         if (km_mfma)
-            CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, c, ps[cur], pc[cur], stream,
+            CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, ct, ps[cur], pc[cur], stream,
                                       var.init_step, mu0, chain && t > 1 ? ps[cur ^ 1] : nullptr,
                                       chain && t > 1 ? pc[cur ^ 1] : nullptr));
         else
-            CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, c, psum, pcnt, stream,
+            CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, ct, psum, pcnt, stream,
                                         var.init_step, mu0));
         if (!chain || t == iters)
             CA_TRY(launch_centroid_reduce(ps[cur], pc[cur], nblk, (int)S, Kc, mu, nullptr, stream,
                                           var.keep_empty));
     }
-    const bool mfma_local = !var.soft && local_mfma_supported(radius);
-    // a few key ranges: the window kernel merges them, no combine launch
-    const bool merge_in_local =
-        mfma_local && xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+    if (hist && !one_launch)
+        CA_TRY(hipMemcpyAsync(hist + (size_t)(iters - 1) * S * L, c, abytes,
+                              hipMemcpyDeviceToDevice, stream));
+    const bool mfma_local = plan.mfma_local;
+    const bool merge_in_local = plan.merge_in_local;
     CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
                                  stream, nullptr, !merge_in_local));
     if (mfma_local)
@@ -317,17 +436,6 @@ ca_status_t check_layer(int B, int L, int Dm, int H, int d, int nclust, int iter
     return CA_OK;
 }
 
-struct Span {
-    const void *p;
-    size_t n;
-};
-
-bool any_overlap(const Span *s, int count) {
-    for (int i = 0; i < count; ++i)
-        for (int j = i + 1; j < count; ++j)
-            if (s[i].p && s[j].p && overlap(s[i].p, s[i].n, s[j].p, s[j].n)) return true;
-    return false;
-}
 
 }  // namespace
 
@@ -343,7 +451,7 @@ const char *ca_status_string(ca_status_t s) {
     return "unknown status";
 }
 
-int ca_version(void) { return 100; }
+int ca_version(void) { return 200; }
 
 size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust, ca_dtype_t dt,
                                       ca_path_t path) {
@@ -351,6 +459,24 @@ size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust, ca
     const int Kc = clusters(nclust, L);
     if (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && use_fused(path, L, Kc))) return 0;
     return staged_layout((long)B * H, L, Kc).total;
+}
+
+const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags, int masked,
+                              ca_path_t path) {
+    if (check_shape(B, H, L, kD, nclust, 1, W, 0.f, CA_F32) != CA_OK) return nullptr;
+    if ((flags & ~CA_FLAG_LISTING) ||
+        (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED))
+        return nullptr;
+    const int Kc = clusters(nclust, L);
+    Variant var{};
+    if (flags & CA_FLAG_INIT_STEP) var.init_step = L / Kc > 1 ? L / Kc : 1;
+    var.keep_empty = (flags & CA_FLAG_KEEP_EMPTY) != 0;
+    var.soft = (flags & CA_FLAG_SOFT_GATHER) != 0;
+    int radius = W / 2;
+    if (flags & CA_FLAG_BAND) radius = (W == 0 || W >= L) ? 0 : W;
+    Plan p;
+    if (make_plan((long)B * H, L, Kc, radius, var, masked != 0, path, p) != CA_OK) return nullptr;
+    return plan_name(p);
 }
 
 size_t cluster_attn_workspace_size(int B, int H, int L, int d, int nclust, ca_dtype_t dt) {
@@ -392,6 +518,7 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
                                       ca_path_t path, hipStream_t stream) {
     const uint8_t *valid = opts ? opts->valid : nullptr;
     const int flags = opts ? opts->flags : 0;
+    int32_t *hist = opts ? opts->assign_hist : nullptr;
     int G = 1;
     if (opts) {
         if (opts->kv_heads < 0) return CA_ERR_INVALID_ARG;
@@ -401,7 +528,7 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
         }
     }
     return forward_impl(Q, K, V, valid, G, flags, B, H, L, d, nclust, iters, W, alpha, out,
-                        assign_out, dt, workspace, workspace_bytes, path, stream);
+                        assign_out, dt, workspace, workspace_bytes, path, stream, hist);
 }
 
 size_t cluster_attn_backward_workspace_size(int B, int H, int kv_heads, int L, int d,
@@ -516,6 +643,21 @@ ca_status_t ca_kmeans_assign(const void *Q, const float *mu, int S, int L, int d
     if (!aligned(Q, 16) || (mu && !aligned(mu, 16)) || !aligned(assign, 4))
         return CA_ERR_INVALID_ARG;
     return hip_status(launch_kmeans_assign(Q, mu, S, L, Kc, dt, assign, nullptr, nullptr, stream));
+}
+
+ca_status_t ca_kmeans_scores(const void *Q, const float *mu, int S, int L, int d, int Kc,
+                             ca_dtype_t dt, float *scores, hipStream_t stream) {
+    ca_status_t st = check_step(S, L, d, Kc, dt);
+    if (st != CA_OK) return st;
+    if (!kmeans_mfma_supported(Kc)) return CA_ERR_UNSUPPORTED;
+    if (!Q || !mu || !scores) return CA_ERR_INVALID_ARG;
+    if ((long long)S * L * Kc > (1LL << 40)) return CA_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(mu, 16) || !aligned(scores, 4)) return CA_ERR_INVALID_ARG;
+    const size_t sb = sizeof(float) * (size_t)S * L * Kc;
+    if (overlap(scores, sb, Q, (size_t)S * L * d * elem_bytes(dt)) ||
+        overlap(scores, sb, mu, sizeof(float) * (size_t)S * Kc * d))
+        return CA_ERR_INVALID_ARG;
+    return hip_status(launch_kmeans_scores(Q, mu, S, L, Kc, dt, scores, stream));
 }
 
 size_t ca_centroid_update_workspace_size(int S, int L, int d, int Kc) {

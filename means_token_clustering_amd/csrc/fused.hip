@@ -87,7 +87,8 @@ struct InitMask {
 // padded keys take the logit -10000 in both softmaxes, and the output rows of
 // padded queries are zero.
 // EXT: the listing's variants below are switched by the runtime flags
-// (without EXT both are off and compiled out). soft: the gathered context
+// (without EXT both are off and compiled out), and hist (nullable) receives
+// the assignment of every Lloyd iteration, [iters, S, L]. soft: the gathered context
 // of token i is sum_k softmax_k(q_i . mu_k / sqrt(d)) V^cent_k over the
 // final centroids instead of V^cent_{c_i}. keep_empty: an empty cluster
 // keeps its previous centroid instead of becoming the zero vector. (Both are
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     int Kc, int iters, int radius, float alpha, const uint8_t *__restrict__ valid, int H, int G,
     T *__restrict__ out, int32_t *__restrict__ assign_out, InitMask init, int keep_empty,
-    int soft) {
+    int soft, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kLdsTotal];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem + kOffK);
     uint16_t *sQV = reinterpret_cast<uint16_t *>(smem + kOffQV);
@@ -281,6 +282,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                     cprev = bk;
                 }
                 if (t == iters) sC[tok] = bk;
+                // c^(t) of every iteration, slot t - 1 (EXT only)
+                if (EXT && hist) hist[((long)(t - 1) * S + slice) * L + tok] = bk;
             }
         }
         __syncthreads();
@@ -771,6 +774,7 @@ struct FusedArgs {
     int32_t *assign;
     InitMask init;
     int keep_empty, soft;
+    int32_t *hist;
 };
 
 template <typename T, bool FULL, bool NARROW, bool MASKED, bool EXT>
@@ -780,7 +784,7 @@ static hipError_t fused_launch_t(const FusedArgs &a, hipStream_t st) {
                        static_cast<const T *>(a.Q), static_cast<const T *>(a.K),
                        static_cast<const T *>(a.V), a.S, a.L, a.Kc, a.iters, a.radius, a.alpha,
                        a.valid, a.H, a.G, static_cast<T *>(a.out), a.assign, a.init,
-                       a.keep_empty, a.soft);
+                       a.keep_empty, a.soft, a.hist);
     return hipGetLastError();
 }
 
@@ -796,7 +800,7 @@ static hipError_t fused_launch_m(const FusedArgs &a, hipStream_t st) {
 
 template <typename T>
 static hipError_t fused_launch(const FusedArgs &a, hipStream_t st) {
-    const bool ext = a.keep_empty || a.soft;
+    const bool ext = a.keep_empty || a.soft || a.hist;
     if (a.valid)
         return ext ? fused_launch_m<T, true, true>(a, st) : fused_launch_m<T, true, false>(a, st);
     return ext ? fused_launch_m<T, false, true>(a, st) : fused_launch_m<T, false, false>(a, st);
@@ -805,9 +809,9 @@ static hipError_t fused_launch(const FusedArgs &a, hipStream_t st) {
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int radius, float alpha, const Variant &var,
                                 ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
-                                int32_t *assign, hipStream_t st) {
+                                int32_t *assign, hipStream_t st, int32_t *hist) {
     FusedArgs a{Q, K, V, S, L, Kc, iters, radius, alpha, valid, H, G, out, assign, InitMask{},
-                var.keep_empty ? 1 : 0, var.soft ? 1 : 0};
+                var.keep_empty ? 1 : 0, var.soft ? 1 : 0, hist};
     for (int k = 0; k < Kc; ++k) {
         const int t = init_row(k, L, Kc, var.init_step);
         a.init.w[t >> 5] |= 1u << (t & 31);

@@ -56,11 +56,13 @@ static_assert(kGLds <= 163840, "one workgroup per CU");
 
 }  // namespace
 
-template <typename T>
+// HIST: hist receives the assignment of every Lloyd iteration, [iters, S, L]
+// (S = the grid size).
+template <typename T, bool HIST>
 __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
     int iters, int rad, float alpha, int init_step, int H, int G, T *__restrict__ out,
-    int32_t *__restrict__ assign) {
+    int32_t *__restrict__ assign, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kGLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);
     float *sPart = reinterpret_cast<float *>(smem + kGOffPart);
@@ -178,6 +180,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                         if (g == 0 && tok < L) {
                             sC[tok] = bk;
                             if (t == iters && assign) assign[s * L + tok] = bk;
+                            if (HIST) hist[((long)(t - 1) * gridDim.x + s) * L + tok] = bk;
                         }
                     }
                 }
@@ -528,18 +531,19 @@ bool fused512_supported(int L, int Kc, int r) {
 
 hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                            int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
-                           int G, void *out, int32_t *assign, hipStream_t st) {
+                           int G, void *out, int32_t *assign, hipStream_t st, int32_t *hist) {
     const dim3 grid((unsigned)S), block(kGThreads);
-    if (dt == CA_BF16)
-        hipLaunchKernelGGL(cluster_attn_fused512_kernel<bf16_t>, grid, block, 0, st,
-                           static_cast<const bf16_t *>(Q), static_cast<const bf16_t *>(K),
-                           static_cast<const bf16_t *>(V), L, Kc, iters, r, alpha, init_step, H,
-                           G, static_cast<bf16_t *>(out), assign);
-    else
-        hipLaunchKernelGGL(cluster_attn_fused512_kernel<float>, grid, block, 0, st,
-                           static_cast<const float *>(Q), static_cast<const float *>(K),
-                           static_cast<const float *>(V), L, Kc, iters, r, alpha, init_step, H,
-                           G, static_cast<float *>(out), assign);
+#define CA_F512_LAUNCH(TT, HH)                                                                   \
+    hipLaunchKernelGGL((cluster_attn_fused512_kernel<TT, HH>), grid, block, 0, st,               \
+                       static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
+                       static_cast<const TT *>(V), L, Kc, iters, r, alpha, init_step, H, G,      \
+                       static_cast<TT *>(out), assign, hist)
+    if (dt == CA_BF16) {
+        if (hist) CA_F512_LAUNCH(bf16_t, true); else CA_F512_LAUNCH(bf16_t, false);
+    } else {
+        if (hist) CA_F512_LAUNCH(float, true); else CA_F512_LAUNCH(float, false);
+    }
+#undef CA_F512_LAUNCH
     return hipGetLastError();
 }
 

@@ -40,12 +40,14 @@ static_assert(kKLds <= 81920, "two workgroups per CU");
 
 }  // namespace
 
-template <typename T, bool INIT>
+// SCORES: instead of the assignment, write every score mu_k . q_i -
+// ||mu_k||^2 / 2 in unscaled units to scores [S, L, Kc] (no partials).
+template <typename T, bool INIT, bool SCORES>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
     int init_step, float *__restrict__ mu_init, const float *__restrict__ prev_sum,
-    const int32_t *__restrict__ prev_cnt) {
+    const int32_t *__restrict__ prev_cnt, float *__restrict__ scores) {
     __shared__ __align__(16) unsigned char smem[kKLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kKOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kKOffMu);
@@ -180,6 +182,15 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
             f32x4_t a = mma(mx, ones_g0, kZero4);
             a = mma3(mu0, qf[0], a);
             a = mma3(mu1, qf[1], a);
+            if (SCORES) {   // both operands carry 2^-sq: the score carries 2^-2sq
+                const float up2 = __builtin_ldexpf(1.f, 2 * sq);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int k = 16 * kg + 4 * g + rr;
+                    if (tok_in && k < Kc) scores[(s * L + i0 + tok) * (long)Kc + k] = a[rr] * up2;
+                }
+                continue;
+            }
             float best = a[0];
             int bk = 16 * kg + 4 * g;
 #pragma unroll
@@ -205,12 +216,12 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
                 rk = bk;
             }
         }
-        if (g == 0 && tok_in) {
+        if (!SCORES && g == 0 && tok_in) {
             assign[s * L + i0 + tok] = rk;
             sOH[off128(rk, tok)] = 0x3c00;   // fp16 1.0
         }
     }
-    if (part_sum == nullptr) return;
+    if (SCORES || part_sum == nullptr) return;
     __syncthreads();
 
     // ------------------------------------------------------------ cluster sums
@@ -252,13 +263,34 @@ static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, in
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
     const T *q = static_cast<const T *>(Q);
+    float *const no_scores = nullptr;
     if (mu == nullptr)
-        hipLaunchKernelGGL((kmeans_mfma_kernel<T, true>), grid, block, 0, st, q, mu, L, Kc, nblk,
-                           assign, part_sum, part_cnt, init_step, mu_init, prev_sum, prev_cnt);
+        hipLaunchKernelGGL((kmeans_mfma_kernel<T, true, false>), grid, block, 0, st, q, mu, L, Kc,
+                           nblk, assign, part_sum, part_cnt, init_step, mu_init, prev_sum,
+                           prev_cnt, no_scores);
     else
-        hipLaunchKernelGGL((kmeans_mfma_kernel<T, false>), grid, block, 0, st, q, mu, L, Kc, nblk,
-                           assign, part_sum, part_cnt, init_step, mu_init, prev_sum, prev_cnt);
+        hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, false>), grid, block, 0, st, q, mu, L,
+                           Kc, nblk, assign, part_sum, part_cnt, init_step, mu_init, prev_sum,
+                           prev_cnt, no_scores);
     return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t kmeans_scores_dispatch(const void *Q, const float *mu, int S, int L, int Kc,
+                                         float *scores, hipStream_t st) {
+    const int nblk = kmeans_mfma_blocks(L);
+    const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
+    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true>), grid, block, 0, st,
+                       static_cast<const T *>(Q), mu, L, Kc, nblk, (int32_t *)nullptr,
+                       (float *)nullptr, (int32_t *)nullptr, 0, (float *)nullptr,
+                       (const float *)nullptr, (const int32_t *)nullptr, scores);
+    return hipGetLastError();
+}
+
+hipError_t launch_kmeans_scores(const void *Q, const float *mu, int S, int L, int Kc,
+                                ca_dtype_t dt, float *scores, hipStream_t st) {
+    if (dt == CA_BF16) return kmeans_scores_dispatch<bf16_t>(Q, mu, S, L, Kc, scores, st);
+    return kmeans_scores_dispatch<float>(Q, mu, S, L, Kc, scores, st);
 }
 
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,

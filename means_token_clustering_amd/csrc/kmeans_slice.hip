@@ -40,12 +40,15 @@ static_assert(kSLds <= 163840, "one workgroup per CU");
 
 }  // namespace
 
-template <typename T>
+// HIST: hist receives c^(t) of every iteration t at hist[(t - 1) * S + s][L]
+// (S slices in all).
+template <typename T, bool HIST>
 __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L, int Kc,
                                                   int iters, int init_step,
                                                   int32_t *__restrict__ assign,
                                                   float *__restrict__ mu_out, long s, int tid,
-                                                  unsigned char *smem) {
+                                                  unsigned char *smem,
+                                                  int32_t *__restrict__ hist, long S) {
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kSOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kSOffMu);
     uint16_t *sMuX = reinterpret_cast<uint16_t *>(smem + kSOffMuX);
@@ -156,6 +159,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                     if (g == 0 && tok < L) {
                         sC[tok] = bk;
                         if (t == iters) assign[s * L + tok] = bk;
+                        if (HIST) hist[((long)(t - 1) * S + s) * L + tok] = bk;
                     }
                 }
             }
@@ -237,13 +241,13 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
     }
 }
 
-template <typename T>
+template <typename T, bool HIST>
 __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
     const T *__restrict__ Q, int L, int Kc, int iters, int init_step,
-    int32_t *__restrict__ assign, float *__restrict__ mu_out) {
+    int32_t *__restrict__ assign, float *__restrict__ mu_out, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kSLds];
-    kmeans_slice_body<T>(Q, L, Kc, iters, init_step, assign, mu_out, blockIdx.x, threadIdx.x,
-                         smem);
+    kmeans_slice_body<T, HIST>(Q, L, Kc, iters, init_step, assign, mu_out, blockIdx.x,
+                               threadIdx.x, smem, hist, gridDim.x);
 }
 
 // The clustering of S slices (workgroups 0 .. S-1) and, beside it, the window
@@ -253,16 +257,16 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
 constexpr int kKWLds = kSLds > 2 * kMLds ? kSLds : 2 * kMLds;
 static_assert(kKWLds <= 163840, "one workgroup per CU");
 
-template <typename T, bool MASKED_IN>
+template <typename T, bool MASKED_IN, bool HIST>
 __global__ __launch_bounds__(kSThreads, 1) void kmeans_window_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
     int iters, int init_step, int32_t *__restrict__ assign_out, float *__restrict__ mu_out, int S,
     int rad, int nblk, float alpha, const uint8_t *__restrict__ valid_in, int H, int G,
-    float *__restrict__ oloc) {
+    float *__restrict__ oloc, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kKWLds];
     if ((int)blockIdx.x < S) {
-        kmeans_slice_body<T>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
-                             threadIdx.x, smem);
+        kmeans_slice_body<T, HIST>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
+                                   threadIdx.x, smem, hist, S);
         return;
     }
     // window blocks: alpha O^loc only (no gather; padded query rows zero)
@@ -290,20 +294,25 @@ bool kmeans_window_supported(long S, int L, int Kc, int r) {
 hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int S, int L,
                                 int Kc, int iters, ca_dtype_t dt, int32_t *assign, float *mu,
                                 int init_step, int r, float alpha, const uint8_t *valid, int H,
-                                int G, float *oloc, hipStream_t st) {
+                                int G, float *oloc, hipStream_t st, int32_t *hist) {
     const int nblk = (L + 127) / 128;
     if (!kmeans_window_supported(S, L, Kc, r)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(S + (long)S * nblk / 2)), block(kSThreads);
-#define CA_KW_LAUNCH(TT, M)                                                                      \
-    hipLaunchKernelGGL((kmeans_window_kernel<TT, M>), grid, block, 0, st,                        \
+#define CA_KW_LAUNCH(TT, M, HH)                                                                  \
+    hipLaunchKernelGGL((kmeans_window_kernel<TT, M, HH>), grid, block, 0, st,                    \
                        static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
                        static_cast<const TT *>(V), L, Kc, iters, init_step, assign, mu, S, r,    \
-                       nblk, alpha, valid, H, G, oloc)
+                       nblk, alpha, valid, H, G, oloc, hist)
+#define CA_KW_LAUNCH_H(TT, M)                                                                    \
+    do {                                                                                         \
+        if (hist) CA_KW_LAUNCH(TT, M, true); else CA_KW_LAUNCH(TT, M, false);                    \
+    } while (0)
     if (dt == CA_BF16) {
-        if (valid) CA_KW_LAUNCH(bf16_t, true); else CA_KW_LAUNCH(bf16_t, false);
+        if (valid) CA_KW_LAUNCH_H(bf16_t, true); else CA_KW_LAUNCH_H(bf16_t, false);
     } else {
-        if (valid) CA_KW_LAUNCH(float, true); else CA_KW_LAUNCH(float, false);
+        if (valid) CA_KW_LAUNCH_H(float, true); else CA_KW_LAUNCH_H(float, false);
     }
+#undef CA_KW_LAUNCH_H
 #undef CA_KW_LAUNCH
     return hipGetLastError();
 }
@@ -311,14 +320,18 @@ hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int
 bool kmeans_slice_supported(int L, int Kc) { return L >= 1 && L <= kSL && Kc >= 1 && Kc <= kFK; }
 
 hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, ca_dtype_t dt,
-                               int32_t *assign, float *mu, int init_step, hipStream_t st) {
+                               int32_t *assign, float *mu, int init_step, hipStream_t st,
+                               int32_t *hist) {
     const dim3 grid((unsigned)S), block(kSThreads);
-    if (dt == CA_BF16)
-        hipLaunchKernelGGL(kmeans_slice_kernel<bf16_t>, grid, block, 0, st,
-                           static_cast<const bf16_t *>(Q), L, Kc, iters, init_step, assign, mu);
-    else
-        hipLaunchKernelGGL(kmeans_slice_kernel<float>, grid, block, 0, st,
-                           static_cast<const float *>(Q), L, Kc, iters, init_step, assign, mu);
+#define CA_KS_LAUNCH(TT, HH)                                                                     \
+    hipLaunchKernelGGL((kmeans_slice_kernel<TT, HH>), grid, block, 0, st,                        \
+                       static_cast<const TT *>(Q), L, Kc, iters, init_step, assign, mu, hist)
+    if (dt == CA_BF16) {
+        if (hist) CA_KS_LAUNCH(bf16_t, true); else CA_KS_LAUNCH(bf16_t, false);
+    } else {
+        if (hist) CA_KS_LAUNCH(float, true); else CA_KS_LAUNCH(float, false);
+    }
+#undef CA_KS_LAUNCH
     return hipGetLastError();
 }
 

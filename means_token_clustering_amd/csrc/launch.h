@@ -51,18 +51,25 @@ hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int 
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr,
                               const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr);
 
+// Scores mu_k . q_i - ||mu_k||^2 / 2 of the matrix-core step (Kc <= 64) in
+// unscaled units, [S, L, Kc]: the distances the step compares.
+hipError_t launch_kmeans_scores(const void *Q, const float *mu, int S, int L, int Kc,
+                                ca_dtype_t dt, float *scores, hipStream_t st);
+
 // The whole forward in one launch per slice for 128 < L <= 512, K <= 16,
 // radius <= 16, without a key-padding mask (fused512.hip); assign nullable.
 bool fused512_supported(int L, int Kc, int r);
 hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                            int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
-                           int G, void *out, int32_t *assign, hipStream_t st);
+                           int G, void *out, int32_t *assign, hipStream_t st,
+                           int32_t *hist = nullptr);
 
 // All Lloyd iterations of each slice in one launch (kmeans_slice.hip) for
 // L <= 512, K <= 16: the last assignment and the final centroids mu [S, K, 64].
 bool kmeans_slice_supported(int L, int Kc);
 hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, ca_dtype_t dt,
-                               int32_t *assign, float *mu, int init_step, hipStream_t st);
+                               int32_t *assign, float *mu, int init_step, hipStream_t st,
+                               int32_t *hist = nullptr);
 
 // key ranges per slice of the centroid cross-attention (partials when > 1)
 int xattn_splits(int L);
@@ -106,7 +113,7 @@ bool kmeans_window_supported(long S, int L, int Kc, int r);
 hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int S, int L,
                                 int Kc, int iters, ca_dtype_t dt, int32_t *assign, float *mu,
                                 int init_step, int r, float alpha, const uint8_t *valid, int H,
-                                int G, float *oloc, hipStream_t st);
+                                int G, float *oloc, hipStream_t st, int32_t *hist = nullptr);
 hipError_t launch_gather_oloc(const float *oloc, const int32_t *assign, const float *vcent,
                               const float *xpart, int S, int L, int Kc, float alpha,
                               const uint8_t *valid, int H, ca_dtype_t dt, void *out,
@@ -170,7 +177,7 @@ bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int radius, float alpha, const Variant &var,
                                 ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
-                                int32_t *assign, hipStream_t st);
+                                int32_t *assign, hipStream_t st, int32_t *hist = nullptr);
 
 // C[z] = A . Bt[z]^T for z < count (bf16 bits, fp32 accumulation). a_heads:
 // A is [B, H, L, 64] read as [B*L, 64 H]; c_heads: C[z] is written as

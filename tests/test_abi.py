@@ -112,6 +112,32 @@ def test_step_entry_points_reject():
     assert lib.ca_gather_fuse(Q, ASG, V, 1, 8, 64, 2, 0.5, 5, OUT, None) == INV
 
 
+def test_scores_entry_point_rejects():
+    lib = b.lib()
+    assert lib.ca_kmeans_scores(None, K, 1, 8, 64, 2, 0, OUT, None) == INV
+    assert lib.ca_kmeans_scores(Q, None, 1, 8, 64, 2, 0, OUT, None) == INV
+    assert lib.ca_kmeans_scores(Q, K, 1, 8, 64, 65, 0, OUT, None) == UNS   # matrix-core step only
+    assert lib.ca_kmeans_scores(Q, K, 1, 8, 48, 2, 0, OUT, None) == UNS
+    assert lib.ca_kmeans_scores(Q, K, 1, 8, 64, 2, 0, Q + 64, None) == INV  # scores over Q
+    assert lib.ca_kmeans_scores(Q, K, 1, 8, 64, 2, 0, OUT + 2, None) == INV
+
+
+def test_plan_names():
+    """The launch-sequence query follows the forward's own decision; without a
+    GPU the CU count is unknown, so only the shape-decided plans are checked."""
+    assert b.cluster_attn_plan(32, 12, 128, 16, 32) == "fused"
+    assert b.cluster_attn_plan(1, 2, 300, 16, 32, path=b.CA_PATH_FUSED) == "fused512"
+    assert b.cluster_attn_plan(1, 2, 300, 16, 32, masked=True, path=b.CA_PATH_FUSED) is None
+    assert b.cluster_attn_plan(1, 2, 300, 16, 32, flags=b.CA_FLAG_KEEP_EMPTY).startswith(
+        "staged: kmeans_mfma steps + reduce")
+    assert b.cluster_attn_plan(1, 1, 600, 32, 32).startswith("staged: kmeans_mfma steps (chained)")
+    assert b.cluster_attn_plan(1, 1, 300, 80, 32).startswith("staged: scalar kmeans steps")
+    assert b.cluster_attn_plan(1, 1, 300, 16, 64).endswith("local_scalar")   # radius 32
+    assert b.cluster_attn_plan(0, 1, 300, 16, 32) is None
+    assert b.cluster_attn_plan(1, 1, 300, 16, -1) is None
+    assert b.cluster_attn_plan(1, 1, 300, 16, 32, flags=64) is None
+
+
 def test_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 1, 8, 64)
@@ -191,8 +217,17 @@ def test_masked_forward_rejects(kw, code):
     assert fwd_masked(**kw) == code
 
 
-class _Opts(ctypes.Structure):
-    _fields_ = [("valid", ctypes.c_void_p), ("kv_heads", ctypes.c_int), ("flags", ctypes.c_int)]
+def _Opts(valid, kv_heads, flags, hist=None):
+    return b.CaOptions(valid, kv_heads, flags, hist)
+
+
+def test_options_layout_matches_header():
+    """ca_options_t: valid, kv_heads, flags, assign_hist (the binding's mirror)."""
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} ca_options_t;", text, flags=re.S).group(1)
+    fields = re.findall(r"(\w+);", body)
+    assert fields == [f for f, _ in b.CaOptions._fields_]
+    assert ctypes.sizeof(b.CaOptions) == 24
 
 
 def fwd_opts(opts, **kw):
@@ -218,6 +253,11 @@ def fwd_opts(opts, **kw):
     (_Opts(None, 4, 0), dict(out=K + 4096), INV),   # out overlaps the smaller K
     (_Opts(MASK, 3, 0), dict(alpha=-1.0), INV),
     (None, dict(ws=None), INV),
+    (_Opts(None, 0, 0, WS + (1 << 29) + 2), {}, INV),      # trace not 4-byte aligned
+    (_Opts(None, 0, 0, OUT + 64), {}, INV),                # trace over the output
+    (_Opts(None, 0, 0, ASG - 4096), {}, INV),              # trace runs into assign_out
+    (_Opts(None, 0, 0, WS + 4096), {}, INV),               # trace over the workspace
+    (_Opts(MASK - 256, 0, 0, MASK - 512), {}, INV),        # trace over the mask
 ])
 def test_opts_forward_rejects(opts, kw, code):
     assert fwd_opts(opts, **kw) == code

@@ -37,27 +37,34 @@ def _say(msg: str) -> None:
 
 
 def run_iters(x: gen.AttnInputs, path: int):
-    """GPU assignments for iters = 1..I and the output of the full run."""
+    """GPU assignment of every iteration (the run's trace, slot t - 1 = c^(t))
+    and the output of the run."""
     b = _b()
     q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
-    assigns = []
-    out = None
-    for t in range(1, x.iters + 1):
-        o, c = b.cluster_attn_forward(q, k, v, x.nclust, t, x.W, x.alpha, path=path)
-        assigns.append(c.cpu().numpy())
-        out = o
+    hist = torch.empty((x.iters, x.B, x.H, x.L), dtype=torch.int32, device="cuda")
+    out, c = b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, path=path,
+                                    assign_hist=hist)
     torch.cuda.synchronize()
-    return assigns, _host(out), (q, k, v)
+    h = hist.cpu().numpy()
+    assert np.array_equal(h[-1], c.cpu().numpy())
+    return [h[t] for t in range(x.iters)], _host(out), (q, k, v)
 
 
-def check(x: gen.AttnInputs, path: int, tol=None):
+def check(x: gen.AttnInputs, path: int, tol=None, record: str = None):
+    plan = _b().cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, path=path)
     _say(f"[parity] {x.name or 'case'} B={x.B} H={x.H} L={x.L} K={x.nclust} I={x.iters} "
-         f"W={x.W} a={x.alpha} {x.dtype} seed={x.seed} path={path}")
+         f"W={x.W} a={x.alpha} {x.dtype} seed={x.seed} path={path} plan={plan}")
     assigns, out, _ = run_iters(x, path)
+    q64, k64, v64 = x.values("q"), x.values("k"), x.values("v")
     reports, err, tol, ref = parity.check_forward(
-        x.values("q"), x.values("k"), x.values("v"), x.nclust, x.iters, x.W, x.alpha, x.dtype,
-        assigns, out, tol)
-    _say(f"  {parity.summarize(reports)}; max|out-ref|={err:.3e} (tol {tol})")
+        q64, k64, v64, x.nclust, x.iters, x.W, x.alpha, x.dtype, assigns, out, tol)
+    free = parity.free_running_mismatches(q64, k64, v64, x.nclust, x.iters, x.W, x.alpha,
+                                          assigns[-1])
+    _say(f"  {parity.summarize(reports)}; free-running mismatches={free}; "
+         f"max|out-ref|={err:.3e} (tol {tol})")
+    name = record or (f"{x.name or 'case'}_B{x.B}_H{x.H}_L{x.L}_K{x.nclust}_I{x.iters}_W{x.W}"
+                      f"_a{x.alpha}_{x.dtype}_s{x.seed}_p{path}")
+    parity.write_record(name, parity.report_dict(name, plan, reports, err, tol, free, None))
     for r in reports:
         assert r.bad == 0, parity.summarize(reports)
     assert err <= tol
