@@ -57,7 +57,8 @@ typedef enum {
     CA_OK = 0,
     CA_ERR_INVALID_ARG = 1,
     CA_ERR_UNSUPPORTED = 2,
-    CA_ERR_HIP = 3
+    CA_ERR_HIP = 3,
+    CA_ERR_SCRATCH_TOO_SMALL = 4   /* cluster_attn_forward_noalloc only */
 } ca_status_t;
 
 typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype_t;
@@ -216,6 +217,30 @@ ca_status_t cluster_attn_forward_opts(const void *Q, const void *K, const void *
                                       int32_t *assign_out, ca_dtype_t dt, void *workspace,
                                       size_t workspace_bytes, ca_path_t path,
                                       hipStream_t stream);
+
+/*
+ * Allocation-free variant of cluster_attn_forward_opts, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, results and paths
+ * as cluster_attn_forward_opts, without the workspace: a staged call takes
+ * its workspace from a device array of CA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends (the single-
+ * launch paths need none). The call allocates and frees nothing.
+ *   Errors: CA_ERR_SCRATCH_TOO_SMALL, before any launch and with the outputs
+ *   untouched, when cluster_attn_workspace_size_ex(B, H, L, d, nclust, dt,
+ *   path) exceeds CA_NOALLOC_SCRATCH_BYTES; CA_ERR_HIP if the array's address
+ *   cannot be looked up; otherwise the statuses of cluster_attn_forward_opts.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time
+ *   on one GPU (different streams, or different host threads) race and must
+ *   be serialised by the caller. The array keeps the last call's contents;
+ *   no call relies on them.
+ */
+#define CA_NOALLOC_SCRATCH_BYTES (64u << 20)
+ca_status_t cluster_attn_forward_noalloc(const void *Q, const void *K, const void *V, int B,
+                                         int H, int L, int d, int nclust, int iters, int W,
+                                         float alpha, const ca_options_t *opts, void *out,
+                                         int32_t *assign_out, ca_dtype_t dt, ca_path_t path,
+                                         hipStream_t stream);
 
 /*
  * Backward pass of the forward above (equations' rules, no listing flags):

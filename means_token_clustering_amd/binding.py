@@ -16,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libclusterattn.so")
 
 CA_OK, CA_ERR_INVALID_ARG, CA_ERR_UNSUPPORTED, CA_ERR_HIP = 0, 1, 2, 3
+CA_ERR_SCRATCH_TOO_SMALL = 4
+CA_NOALLOC_SCRATCH_BYTES = 64 << 20
 CA_F32, CA_BF16 = 0, 1
 CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED = 0, 1, 2
 # listing-compatible variants (ca_options_t.flags)
@@ -46,6 +48,8 @@ SIGNATURES = {
                                          _vp, _i, _vp, _sz, _i, _vp]),
     "cluster_attn_forward_opts": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp,
                                        _vp, _i, _vp, _sz, _i, _vp]),
+    "cluster_attn_forward_noalloc": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp,
+                                          _vp, _vp, _i, _i, _vp]),
     "ca_kmeans_assign": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "ca_kmeans_scores": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp]),
     "ca_centroid_update": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),

@@ -447,6 +447,8 @@ const char *ca_status_string(ca_status_t s) {
         case CA_ERR_INVALID_ARG: return "invalid argument";
         case CA_ERR_UNSUPPORTED: return "unsupported shape or type";
         case CA_ERR_HIP: return "HIP launch error";
+        case CA_ERR_SCRATCH_TOO_SMALL:
+            return "the call needs more workspace than the allocation-free entry point holds";
     }
     return "unknown status";
 }

@@ -122,6 +122,22 @@ def test_scores_entry_point_rejects():
     assert lib.ca_kmeans_scores(Q, K, 1, 8, 64, 2, 0, OUT + 2, None) == INV
 
 
+def test_noalloc_rejects_before_any_launch():
+    """The allocation-free forward checks its workspace need against the
+    device array before touching the GPU (fake pointers here)."""
+    lib = b.lib()
+    need = b.cluster_attn_workspace_size(1, 12, 16384, 64, 64, b.CA_F32, b.CA_PATH_STAGED)
+    assert need > b.CA_NOALLOC_SCRATCH_BYTES
+    assert lib.cluster_attn_forward_noalloc(Q, K, V, 1, 12, 16384, 64, 64, 1, 32, 0.5, None, OUT,
+                                            ASG, b.CA_F32, b.CA_PATH_STAGED, None) == 4
+    assert b.status_string(4).startswith("the call needs more workspace")
+    # single-launch shapes need no workspace: argument errors come first
+    assert lib.cluster_attn_forward_noalloc(None, K, V, 2, 12, 128, 64, 16, 3, 32, 0.5, None, OUT,
+                                            ASG, b.CA_F32, b.CA_PATH_AUTO, None) == INV
+    assert lib.cluster_attn_forward_noalloc(Q, K, V, 2, 12, 128, 64, 16, 3, 32, 1.5, None, OUT,
+                                            ASG, b.CA_F32, b.CA_PATH_AUTO, None) == INV
+
+
 def test_plan_names():
     """The launch-sequence query follows the forward's own decision; without a
     GPU the CU count is unknown, so only the shape-decided plans are checked."""
