@@ -524,8 +524,8 @@ static hipError_t bwd_dispatch(const BwdArgs &a, hipStream_t st) {
     const dim3 block(256);
     // 1. dVc
     const size_t lds = sizeof(float) * ((size_t)kBT * kBPad + (size_t)a.Kc * kD) + sizeof(int) * kBT;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_cluster_sum_kernel<T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e =
+        ensure_dynamic_lds(reinterpret_cast<const void *>(bwd_cluster_sum_kernel<T>), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_cluster_sum_kernel<T>, dim3((unsigned)(S * ntile)), block, lds, st, dO,
                        a.assign, a.valid, a.L, a.Kc, a.H, ntile, a.part);

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
-        qf[c] = split8(x);
+        qf[c] = split8<true>(x);
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = graw[c][i] * fg;
-        gf[c] = split8(y);
+        gf[c] = split8<true>(y);
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {

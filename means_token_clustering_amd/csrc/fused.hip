@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 x[i] = scaled ? qraw[c][i] * fq : qraw[c][i];
                 n2 = fmaf(x[i], x[i], n2);
             }
-            qf[c] = split8(x);
+            qf[c] = split8<true>(x);
             const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
             st16(sQV + o, qf[c].h);
             st16(sQV + kPlaneE + o, qf[c].m);
@@ -663,7 +663,7 @@ __global__ __launch_bounds__(kThreads, 4) void exact_fused_kernel(
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;   // exact power-of-two scaling
-        qf[c] = split8(x);
+        qf[c] = split8<true>(x);
     }
 #pragma unroll
     for (int n = 0; n < 2; ++n) {

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = qraw[u][c][i] * fq;
-            qf[u][c] = split8(x);
+            qf[u][c] = split8<true>(x);
             const int o = (2048 * (w + 16 * u) + (lo.rl64 ^ (64 * c))) / 2;
             st16(sQ + o, qf[u][c].h);
             st16(sQ + kGPlaneQ / 2 + o, qf[u][c].m);
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, x);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) x[i] *= fq;
-                    qp[c] = split8(x);
+                    qp[c] = split8<true>(x);
                 }
                 f32x4_t o[4];
                 float lsum;

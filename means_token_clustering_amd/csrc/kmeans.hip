@@ -13,6 +13,10 @@
 // The same workgroup emits its tile's per-cluster partial sums in token
 // order; a second kernel adds the tiles' partials in tile order. No float
 // atomics anywhere, so the result is bitwise reproducible.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "launch.h"
 
 namespace ca {
@@ -184,8 +188,7 @@ static hipError_t assign_launch(const void *Q, const float *mu, int S, int L, in
                                 hipStream_t st, int init_step = 0, float *mu_init = nullptr) {
     auto kern = kmeans_assign_kernel<T, INIT, MODE>;
     const size_t lds = assign_lds_bytes(Kc, MODE != 0);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void *>(kern), (int)lds);
     if (e != hipSuccess) return e;
     const int ntile = kmeans_tiles(L);
     hipLaunchKernelGGL(kern, dim3((unsigned)((long)S * ntile)), dim3(256), lds, st,
@@ -234,6 +237,20 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
     hipLaunchKernelGGL(centroid_reduce_kernel, dim3((unsigned)((long)S * Kc)), dim3(256), 0, st,
                        part_sum, part_cnt, nblk, Kc, mu, counts, keep_empty ? 1 : 0);
     return hipGetLastError();
+}
+
+hipError_t ensure_dynamic_lds(const void *fn, int bytes) {
+    static std::mutex lock;
+    static std::map<std::pair<const void *, int>, int> limits;   // (kernel, device) -> bytes
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> guard(lock);
+    int &have = limits[{fn, dev}];
+    if (have >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
 }
 
 }  // namespace ca

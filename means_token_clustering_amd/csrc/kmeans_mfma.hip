@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
-        qf[c] = split8(x);
+        qf[c] = split8<true>(x);
         const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
         st16(sQ + o, qf[c].h);
         st16(sQ + kPlaneE + o, qf[c].m);

@@ -93,7 +93,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = qraw[u][c][i] * fq;
-            qf[u][c] = split8(x);
+            qf[u][c] = split8<true>(x);
             const int o = (2048 * (w + 16 * u) + (lo.rl64 ^ (64 * c))) / 2;
             st16(sQ + o, qf[u][c].h);
             st16(sQ + kSPlane / 2 + o, qf[u][c].m);
@@ -271,19 +271,10 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_window_kernel(
     }
     // window blocks: alpha O^loc only (no gather; padded query rows zero)
     const int half = threadIdx.x >> 9;   // uniform per wave
-    unsigned char *const smem_all = smem;
-    {
-        unsigned char *const smem = smem_all + half * kMLds;
-        constexpr bool OLOC = true, MASKED = MASKED_IN;
-        const int tid = threadIdx.x & (kThreads - 1);
-        const unsigned bid = 2 * (blockIdx.x - S) + half;
-        const float *const vcent = nullptr, *const xpart = nullptr;
-        const int32_t *const assign = nullptr;
-        const uint8_t *const valid = valid_in;
-        T *const out = nullptr;
-        const int nsplit = 0;
-#include "local_mfma_body.inc"
-    }
+    local_window_block<T, MASKED_IN, true, false>(Q, Kx, Vx, L, rad, nblk, nullptr, nullptr, Kc,
+                                                  alpha, valid_in, H, G, nullptr, nullptr, 0, oloc,
+                                           smem + half * kMLds, threadIdx.x & (kThreads - 1),
+                                           2 * (blockIdx.x - S) + half);
 }
 
 bool kmeans_window_supported(long S, int L, int Kc, int r) {

@@ -23,6 +23,11 @@ __host__ __device__ inline int init_row(int k, int L, int Kc, int init_step) {
     return init_step > 0 ? k * init_step : (int)(((long)k * L) / Kc);
 }
 
+// Lets kernel fn launch with `bytes` of dynamic LDS on the current device:
+// hipFuncSetAttribute runs only when the device has not yet been given a limit
+// at least that large for fn (once per kernel and device in practice).
+hipError_t ensure_dynamic_lds(const void *fn, int bytes);
+
 // mu == nullptr: the centroids are the initial rows of Q (init_row with
 // init_step); mu_init, if not null, then receives them.
 hipError_t launch_kmeans_assign(const void *Q, const float *mu, int S, int L, int Kc,

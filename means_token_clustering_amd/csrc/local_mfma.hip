@@ -24,18 +24,16 @@
 
 namespace ca {
 
-template <typename T, bool MASKED>
+template <typename T, bool MASKED, bool XPART>
 __global__ __launch_bounds__(kThreads, 4) void local_mfma_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int rad,
     int nblk, const float *__restrict__ vcent, const int32_t *__restrict__ assign, int Kc,
     float alpha, const uint8_t *__restrict__ valid, int H, int G, T *__restrict__ out,
     const float *__restrict__ xpart, int nsplit) {
     __shared__ __align__(16) unsigned char smem[kMLds];
-    constexpr bool OLOC = false;
-    float *const oloc = nullptr;
-    const int tid = threadIdx.x;
-    const unsigned bid = blockIdx.x;
-#include "local_mfma_body.inc"
+    local_window_block<T, MASKED, false, XPART>(Q, Kx, Vx, L, rad, nblk, vcent, assign, Kc, alpha,
+                                                valid, H, G, out, xpart, nsplit, nullptr, smem,
+                                                threadIdx.x, blockIdx.x);
 }
 
 bool local_mfma_supported(int r) { return r >= 0 && r <= 16; }
@@ -142,14 +140,15 @@ static hipError_t local_mfma_dispatch(const void *Q, const void *K, const void *
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
     const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K);
     const T *v = static_cast<const T *>(V);
-    if (valid)
-        hipLaunchKernelGGL((local_mfma_kernel<T, true>), grid, block, 0, st, q, k, v, L, r, nblk,
-                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), xpart,
-                           nsplit);
-    else
-        hipLaunchKernelGGL((local_mfma_kernel<T, false>), grid, block, 0, st, q, k, v, L, r, nblk,
-                           vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), xpart,
-                           nsplit);
+#define CA_LM_LAUNCH(M, X)                                                                       \
+    hipLaunchKernelGGL((local_mfma_kernel<T, M, X>), grid, block, 0, st, q, k, v, L, r, nblk,    \
+                       vcent, assign, Kc, alpha, valid, H, G, static_cast<T *>(out), xpart, nsplit)
+    if (valid) {
+        if (xpart) CA_LM_LAUNCH(true, true); else CA_LM_LAUNCH(true, false);
+    } else {
+        if (xpart) CA_LM_LAUNCH(false, true); else CA_LM_LAUNCH(false, false);
+    }
+#undef CA_LM_LAUNCH
     return hipGetLastError();
 }
 

@@ -47,38 +47,49 @@ struct Sp4 {  // 4 values as two fp16 planes
 // x0, x1 -> packed fp16 pairs h and m with x = h + m + e: h rounded toward
 // zero, m = x - h (exact inside the mixed-precision fma) rounded to nearest
 // into the low / high half of m.
-// MFMA = true: m feeds a matrix instruction at once. The compiler inserts
-// the wait states that a matrix read of a vector-ALU result needs only after
-// instructions it can see, not after asm, so the asm supplies them with a
-// trailing s_nop. split8 / split4 put it after their last pair, which covers
-// every part of the group.
-template <bool MFMA = false>
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t &h, uint32_t &m) {
     h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(x0, x1));
     uint32_t r;
     asm("v_fma_mixlo_f16 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x0));
-    if (MFMA)
-        asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\ts_nop 3"
-            : "+v"(r) : "v"(h), "v"(x1));
-    else
-        asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-            : "+v"(r) : "v"(h), "v"(x1));
+    asm("v_fma_mixhi_f16 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "+v"(r) : "v"(h), "v"(x1));
     m = r;
 }
+
+// A matrix instruction that reads a vector-ALU result from registers needs
+// wait states after the write; the compiler inserts them only after writes it
+// can see, not after asm. mfma_ready passes a whole split group through one
+// asm that names every register of the group as an in-out operand and holds
+// s_nop 4 (five wait states): data dependence places it after the last write
+// of any part of the group and every matrix read after it, and any copy the
+// compiler makes afterwards is a visible vector-ALU write that it guards
+// itself. Only groups that reach a matrix instruction from registers need it;
+// groups stored to LDS are read back by LDS loads.
+__device__ __forceinline__ void mfma_ready(u32x4_t &h, u32x4_t &m) {
+    asm("s_nop 4" : "+v"(h), "+v"(m));
+}
+__device__ __forceinline__ void mfma_ready(u32x2_t &h, u32x2_t &m) {
+    asm("s_nop 4" : "+v"(h), "+v"(m));
+}
+
+// MFMA = true: the group feeds matrix instructions from registers (mfma_ready).
 template <bool MFMA = false>
 __device__ __forceinline__ Sp8 split8(const float *x) {
     uint32_t h[4], m[4];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
-    split2<MFMA>(x[6], x[7], h[3], m[3]);
-    return Sp8{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{m[0], m[1], m[2], m[3]}};
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], m[i]);
+    Sp8 r{u32x4_t{h[0], h[1], h[2], h[3]}, u32x4_t{m[0], m[1], m[2], m[3]}};
+    if (MFMA) mfma_ready(r.h, r.m);
+    return r;
 }
 template <bool MFMA = false>
 __device__ __forceinline__ Sp4 split4(float x0, float x1, float x2, float x3) {
     uint32_t h0, m0, h1, m1;
     split2(x0, x1, h0, m0);
-    split2<MFMA>(x2, x3, h1, m1);
-    return Sp4{u32x2_t{h0, h1}, u32x2_t{m0, m1}};
+    split2(x2, x3, h1, m1);
+    Sp4 r{u32x2_t{h0, h1}, u32x2_t{m0, m1}};
+    if (MFMA) mfma_ready(r.h, r.m);
+    return r;
 }
 
 // fp16 value i (0..3) of a packed pair of pairs, widened
