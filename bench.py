@@ -164,7 +164,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="distilbert",
                    choices=["tiny", "distilbert", "bf16_l512", "long_l8192", "layer_bf16"])
-    p.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
+    p.add_argument("--path", default="auto", choices=["auto", "fused", "staged", "segmented"])
     p.add_argument("--batch", type=int, default=0,
                    help="batch size B of the attention workload (0 = the workload's own)")
     p.add_argument("--sets", type=int, default=0, help="input sets to rotate (0 = auto)")
@@ -517,7 +517,8 @@ def main():
         (bench_backward if args.backward else bench_decoder)(args, x, mask, b, gen, torch, np)
         return
     elem = 2 if x.dtype == gen.BF16 else 4
-    path = {"auto": b.CA_PATH_AUTO, "fused": b.CA_PATH_FUSED, "staged": b.CA_PATH_STAGED}[args.path]
+    path = {"auto": b.CA_PATH_AUTO, "fused": b.CA_PATH_FUSED, "staged": b.CA_PATH_STAGED,
+            "segmented": b.CA_PATH_SEGMENTED}[args.path]
     dev = torch.device("cuda:0")
 
     def to_dev(a):

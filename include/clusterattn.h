@@ -67,7 +67,12 @@ typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype_t;
  * shape allows it (L <= 128 and min(nclust, L) <= 16), else STAGED. FUSED:
  * one launch, one workgroup per slice, the whole slice on chip. STAGED: one
  * kernel per step, any supported shape. */
-typedef enum { CA_PATH_AUTO = 0, CA_PATH_FUSED = 1, CA_PATH_STAGED = 2 } ca_path_t;
+typedef enum {
+    CA_PATH_AUTO = 0,
+    CA_PATH_FUSED = 1,
+    CA_PATH_STAGED = 2,
+    CA_PATH_SEGMENTED = 3   /* one launch, each slice over several co-resident workgroups */
+} ca_path_t;
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char *ca_status_string(ca_status_t s);
@@ -107,10 +112,19 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V,
  * one launch per slice: any supported call with L <= 128 and nclust <= 16, or
  * 128 < L <= 512 with min(nclust, L) <= 16, a window radius <= 16 and neither
  * a key-padding mask nor the kept-centroid or soft-gather variants; on other
- * shapes it returns CA_ERR_UNSUPPORTED. CA_PATH_AUTO picks the single launch
- * for L <= 128, and for the longer shapes when the slice count fills between
- * half and all of the device's compute units. STAGED needs
- * cluster_attn_workspace_size_ex(..., CA_PATH_STAGED) bytes. */
+ * shapes it returns CA_ERR_UNSUPPORTED. CA_PATH_SEGMENTED runs one launch in
+ * which each slice is split into segments of at most 480 tokens, one
+ * workgroup each, all resident at once (B * H * segments <= the device's
+ * compute units, at least two segments per slice), for min(nclust, L) <= 64,
+ * a window radius <= 16 and neither a mask nor a listing variant; otherwise
+ * CA_ERR_UNSUPPORTED. Its workgroups wait for one another between steps; a
+ * wait longer than about 7 ms (possible only while other work holds the CUs
+ * it needs) turns the affected output rows into NaN and their assignments
+ * into -1. CA_PATH_AUTO picks the single launch for L <= 128; for
+ * longer slices the 512-token single launch when the slice count fills
+ * between half and all of the compute units, else the staged launches (the
+ * segmented launch only when asked for). AUTO, STAGED and SEGMENTED need
+ * cluster_attn_workspace_size_ex(..., path) bytes. */
 ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     int B, int H, int L, int d, int nclust,
                                     int iters, int W, float alpha, void *out,

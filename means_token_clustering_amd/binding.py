@@ -19,7 +19,7 @@ CA_OK, CA_ERR_INVALID_ARG, CA_ERR_UNSUPPORTED, CA_ERR_HIP = 0, 1, 2, 3
 CA_ERR_SCRATCH_TOO_SMALL = 4
 CA_NOALLOC_SCRATCH_BYTES = 64 << 20
 CA_F32, CA_BF16 = 0, 1
-CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED = 0, 1, 2
+CA_PATH_AUTO, CA_PATH_FUSED, CA_PATH_STAGED, CA_PATH_SEGMENTED = 0, 1, 2, 3
 # listing-compatible variants (ca_options_t.flags)
 CA_FLAG_INIT_STEP, CA_FLAG_KEEP_EMPTY, CA_FLAG_SOFT_GATHER, CA_FLAG_BAND = 1, 2, 4, 8
 CA_FLAG_ALPHA_LOGIT = 16

@@ -137,6 +137,7 @@ bool use_fused(ca_path_t path, int L, int Kc) {
 enum PlanKind {
     kPlanFused,      // cluster_attn_fused_kernel: one launch, L <= 128
     kPlanFused512,   // cluster_attn_fused512_kernel: one launch, 128 < L <= 512
+    kPlanSeg,        // cluster_attn_seg_kernel: one launch, each slice over ns workgroups
     kPlanBeside,     // kmeans_window_kernel (clustering + window), centroid attention, gather
     kPlanSlice,      // kmeans_slice_kernel, centroid attention, window branch
     kPlanSteps       // one launch per Lloyd step, centroid attention, window branch
@@ -144,6 +145,7 @@ enum PlanKind {
 
 struct Plan {
     PlanKind kind;
+    int ns;                // segments per slice (kPlanSeg)
     bool km_mfma;          // steps on the matrix cores (else the scalar step)
     bool chain;            // steps pass their block sums on (no reduce in between)
     bool mfma_local;       // window branch on the matrix cores (else scalar)
@@ -155,16 +157,26 @@ struct Plan {
 ca_status_t make_plan(long S, int L, int Kc, int radius, const Variant &var, bool masked,
                       ca_path_t path, Plan &p) {
     p = Plan{};
-    if (use_fused(path, L, Kc)) {
+    if (path != CA_PATH_SEGMENTED && use_fused(path, L, Kc)) {
         p.kind = kPlanFused;
         return CA_OK;
     }
+    const bool plain = !masked && !var.soft && !var.keep_empty;
     // 128 < L <= 512: the 16-wave single launch (forced by CA_PATH_FUSED, by
     // the auto path when it pays)
-    const bool f512 = !masked && !var.soft && !var.keep_empty && fused512_supported(L, Kc, radius);
+    const bool f512 = plain && fused512_supported(L, Kc, radius);
     if (path == CA_PATH_FUSED && !f512) return CA_ERR_UNSUPPORTED;
     if (f512 && (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && fused512_pays(S)))) {
         p.kind = kPlanFused512;
+        return CA_OK;
+    }
+    // the segmented single launch: only when CA_PATH_SEGMENTED asks for it
+    // (on the shapes measured so far the staged launches are faster)
+    if (path == CA_PATH_SEGMENTED) {
+        const int ns = plain ? seg_count(S, L, Kc, radius, device_cus()) : 0;
+        if (ns == 0) return CA_ERR_UNSUPPORTED;
+        p.kind = kPlanSeg;
+        p.ns = ns;
         return CA_OK;
     }
     const bool one_launch = kmeans_slice_supported(L, Kc) && !var.keep_empty;
@@ -188,6 +200,7 @@ const char *plan_name(const Plan &p) {
     switch (p.kind) {
         case kPlanFused: return "fused";
         case kPlanFused512: return "fused512";
+        case kPlanSeg: return "segmented";
         case kPlanBeside:
             return p.merge_in_local ? "staged: kmeans_window, xattn ranges, gather_oloc (merge)"
                                     : "staged: kmeans_window, xattn, gather_oloc";
@@ -237,7 +250,8 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     }
     ca_status_t st = check_shape(B, H, L, d, nclust, iters, W, alpha, dt);
     if (st != CA_OK) return st;
-    if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED)
+    if (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED &&
+        path != CA_PATH_SEGMENTED)
         return CA_ERR_INVALID_ARG;
     if (!Q || !K || !V || !out) return CA_ERR_INVALID_ARG;
     if (G < 1 || H % G != 0) return CA_ERR_INVALID_ARG;
@@ -294,6 +308,18 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
                                           var.init_step, dt, H, G, out, assign_out, stream,
                                           hist));
+    if (plan.kind == kPlanSeg) {
+        const size_t need = seg_workspace_bytes(S, L, Kc, plan.ns);
+        if (workspace_bytes < need || !workspace || !aligned(workspace, kAlign))
+            return CA_ERR_INVALID_ARG;
+        const Span others[] = {{Q, tbytes}, {K, kvbytes}, {V, kvbytes}, {out, tbytes},
+                               {assign_out, abytes}, {hist, hbytes}};
+        for (const Span &o : others)
+            if (o.p && overlap(workspace, need, o.p, o.n)) return CA_ERR_INVALID_ARG;
+        return hip_status(launch_seg(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var.init_step,
+                                     dt, H, G, out, assign_out, plan.ns, workspace, stream,
+                                     hist));
+    }
     const StagedLayout lay = staged_layout(S, L, Kc);
     if (workspace_bytes < lay.total || !workspace) return CA_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign)) return CA_ERR_INVALID_ARG;
@@ -459,15 +485,21 @@ size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust, ca
                                       ca_path_t path) {
     if (check_shape(B, H, L, d, nclust, 1, 0, 0.f, dt) != CA_OK) return 0;
     const int Kc = clusters(nclust, L);
+    const long S = (long)B * H;
     if (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && use_fused(path, L, Kc))) return 0;
-    return staged_layout((long)B * H, L, Kc).total;
+    if (path == CA_PATH_SEGMENTED) {
+        const int ns = seg_count(S, L, Kc, 0, device_cus());
+        return ns > 0 ? seg_workspace_bytes(S, L, Kc, ns) : 0;
+    }
+    return staged_layout(S, L, Kc).total;
 }
 
 const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags, int masked,
                               ca_path_t path) {
     if (check_shape(B, H, L, kD, nclust, 1, W, 0.f, CA_F32) != CA_OK) return nullptr;
     if ((flags & ~CA_FLAG_LISTING) ||
-        (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED))
+        (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED &&
+         path != CA_PATH_SEGMENTED))
         return nullptr;
     const int Kc = clusters(nclust, L);
     Variant var{};

@@ -69,6 +69,18 @@ hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, i
                            int G, void *out, int32_t *assign, hipStream_t st,
                            int32_t *hist = nullptr);
 
+// The whole forward in one launch with each slice split over ns co-resident
+// workgroups of at most 480 tokens (seg.hip): K <= 64, radius <= 16, no mask
+// or listing variants. seg_count: ns for this shape on a device with `cus`
+// compute units (0: not supported); the launch needs seg_workspace_bytes of
+// workspace (256-byte aligned).
+int seg_count(long S, int L, int Kc, int r, int cus);
+size_t seg_workspace_bytes(long S, int L, int Kc, int ns);
+hipError_t launch_seg(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                      int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H, int G,
+                      void *out, int32_t *assign, int ns, void *workspace, hipStream_t st,
+                      int32_t *hist = nullptr);
+
 // All Lloyd iterations of each slice in one launch (kmeans_slice.hip) for
 // L <= 512, K <= 16: the last assignment and the final centroids mu [S, K, 64].
 bool kmeans_slice_supported(int L, int Kc);

@@ -152,6 +152,35 @@ def test_single_launch_long_full_batch():
     check(gen.workload("bf16_l512"), 1)
 
 
+# the segmented single launch (each slice over several co-resident
+# workgroups), forced with CA_PATH_SEGMENTED; with few slices the launch
+# takes many short segments (exchange through owner workgroups), with more
+# slices a few long ones (every workgroup adds the segment sums itself)
+SEGMENTED = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
+    (1, 2, 300, 16, 3, 32, 0.5, "f32", 12),        # many 16-token segments, one group
+    (8, 12, 512, 16, 3, 32, 0.5, "bf16", 16),      # two 256-token segments per slice
+    (2, 12, 1100, 32, 3, 32, 0.5, "f32", 24),      # ten segments, two groups, ragged
+    (1, 12, 2000, 48, 4, 24, 0.4, "f32", 40),      # three groups, owners of 3-4 rows
+    (2, 12, 1500, 64, 2, 33, 0.6, "bf16", 48),     # four groups, radius 16
+    (4, 16, 1000, 20, 3, 0, 0.5, "f32", 16),       # W = 0, one-level, 3 segments of 336
+    (2, 8, 960, 16, 1, 32, 1.0, "f32", 16),        # one iteration, pure local branch
+    (1, 12, 777, 64, 3, 32, 0.0, "f32", 30),       # pure centroid branch, ragged
+    (3, 12, 481, 16, 3, 32, 0.5, "bf16", 16),      # 7 segments of 80 on 256 CUs: the last holds one token
+]
+
+
+@pytest.mark.parametrize("case", SEGMENTED)
+def test_segmented_launch(case):
+    B, H, L, nclust, iters, W, alpha, dtype, blobs = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
+                        dtype=dtype, seed=5000 + L + W, blobs=blobs, name="segmented")
+    check(x, 3)
+
+
+def test_segmented_long_workload():
+    check(gen.workload("long_l8192"), 3)
+
+
 def test_empty_cluster_and_exact_ties():
     """L=8, K=2, Q[4] = Q[0]: identical initial centroids tie exactly, so all
     tokens take cluster 0; cluster 1 becomes the zero vector; at iteration 2
@@ -176,7 +205,7 @@ def test_empty_cluster_and_exact_ties():
         assert np.abs(_host(out) - ref["out"]).max() <= 1e-4
 
 
-@pytest.mark.parametrize("path", PATHS + [1])   # 1: the 16-wave single launch (L = 160)
+@pytest.mark.parametrize("path", PATHS + [1, 3])   # 1: the 16-wave single launch, 3: segmented
 def test_determinism_and_slice_independence(path):
     x = gen.make_inputs(2, 3, 160, 64, nclust=16, iters=3, W=32, alpha=0.5, seed=21, blobs=8)
     b = _b()

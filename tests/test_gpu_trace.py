@@ -46,6 +46,8 @@ PATHS = [
     ("scalar steps (K > 64)", 2, 1, 1, 300, 80, 3, 32, "f32", 40, 0, False),
     ("staged kept centroids", 2, 1, 2, 200, 16, 3, 32, "f32", 6, 2, False),
     ("staged masked", 2, 2, 2, 257, 24, 3, 20, "bf16", 10, 0, True),
+    ("segmented, owner exchange", 3, 1, 2, 1100, 40, 4, 32, "f32", 20, 0, False),
+    ("segmented, every workgroup adds", 3, 8, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
 ]
 
 
