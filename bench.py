@@ -391,17 +391,19 @@ def bench_layer(args, x, b, gen, torch, np):
         return timed_steps(torch, stream, fn, steps, warmup)[0]
 
     ms, groups = timed_steps(torch, stream, step, args.steps, args.warmup)
-    # the projection GEMM alone: C [B*L, 3*768] = X [B*L, 768] . Wqkv, with
-    # Bt = Wqkv^T [3*768, 768] as the layer's own transpose launch prepares it
-    Bt = torch.cat([Wq.t(), Wk.t(), Wv.t()], dim=0).contiguous()
+    # the projection GEMM alone: C [B*L, 3*768] = X [B*L, 768] . Wqkv with
+    # Wqkv = [Wq | Wk | Wv] in the [in, out] layout the layer reads (the same
+    # 128 x 192 tiles as the layer's Q/K/V launch)
+    Wqkv = torch.cat([Wq, Wk, Wv], dim=1).contiguous()
     C = torch.empty((B * L, 3 * Dm), dtype=torch.bfloat16, device=dev)
     gsets = [X.view(B * L, Dm) for X, _, _ in sets]
 
     def gstep(i):
         A = gsets[i % nsets]
-        st = lib.ca_gemm_bf16(A.data_ptr(), Bt.data_ptr(), B * L, 3 * Dm, Dm, C.data_ptr(), sptr)
+        st = lib.ca_gemm_bf16_kn(A.data_ptr(), Wqkv.data_ptr(), B * L, 3 * Dm, Dm, C.data_ptr(),
+                                 sptr)
         if st != b.CA_OK:
-            raise b.CaError(st, "ca_gemm_bf16")
+            raise b.CaError(st, "ca_gemm_bf16_kn")
 
     gms = timed(gstep, 100, 10)
     gflops = 2.0 * B * L * Dm * 3 * Dm
@@ -421,7 +423,7 @@ def bench_layer(args, x, b, gen, torch, np):
            "roofline": {"bound": "mfma", "achieved": round(g_tflops, 1),
                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                        "kernel": "gemm_nt_kernel, [%d x %d] x [%d x %d]" % (B * L, Dm, Dm, 3 * Dm),
+                        "kernel": "gemm_bf16_kernel, [%d x %d] x [%d x %d]" % (B * L, Dm, Dm, 3 * Dm),
                         "kernel_us": round(gms * 1e3, 3), "flops_per_launch": int(gflops)},
            "compute": {"flops_per_step": int(proj + att),
                        "achieved_TFLOPs": round((proj + att) / (ms / 1e3) / 1e12, 2),

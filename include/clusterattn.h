@@ -416,12 +416,11 @@ ca_status_t ca_gather_fuse(const float *vcent, const int32_t *assign,
  *   assign_out  out  device int32 [B, H, L] or NULL.
  *   qkv_out     out  device bf16 [3, B, H, L, d] receiving Q, K, V, or NULL.
  *   workspace        device, cluster_attn_layer_workspace_size(...) bytes,
- *                    256-byte aligned; it holds the transposed weights, Q,
- *                    K, V (when qkv_out is NULL), O and the attention
- *                    workspace.
+ *                    256-byte aligned; it holds Q, K, V (when qkv_out is
+ *                    NULL), O and the attention workspace.
  *   Outputs and workspace must not overlap each other or the inputs.
- *   Launches: one weight transpose, one GEMM for Q, K and V together, the
- *   cluster attention launches, one GEMM for Y.
+ *   Launches: one GEMM for Q, K and V together (weights read in their
+ *   [in, out] layout), the cluster attention launches, one GEMM for Y.
  * --------------------------------------------------------------------- */
 size_t cluster_attn_layer_workspace_size(int B, int L, int Dm, int H, int d,
                                          int nclust);
@@ -441,10 +440,21 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq,
  * layer's weight), fp32 accumulation, one round-to-nearest-even to bf16.
  *   A, Bt in, C out: device bf16 bits, row-major, 16-byte aligned; C must
  *   not overlap A or Bt. M, N, Kd >= 1 (CA_ERR_INVALID_ARG otherwise); N and
- *   Kd multiples of 64 (CA_ERR_UNSUPPORTED otherwise); any M.
+ *   Kd multiples of 64 and N * Kd < 2^31 (CA_ERR_UNSUPPORTED otherwise);
+ *   any M.
  */
 ca_status_t ca_gemm_bf16(const void *A, const void *Bt, int M, int N, int Kd,
                          void *C, hipStream_t stream);
+
+/*
+ * The same GEMM with the weight in the [in, out] layout the layer's
+ * projections take (Architecture Overview of the model card: Q = X W_Q, ...):
+ * C[M, N] = A[M, Kd] . W[Kd, N], C[m][n] = sum_k A[m][k] W[k][n]. Arguments,
+ * alignment, precision and errors as for ca_gemm_bf16, with W [Kd, N]
+ * row-major in place of Bt.
+ */
+ca_status_t ca_gemm_bf16_kn(const void *A, const void *W, int M, int N, int Kd,
+                            void *C, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -62,6 +62,7 @@ SIGNATURES = {
     "cluster_attn_layer_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i,
                                         _f, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ca_gemm_bf16": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
+    "ca_gemm_bf16_kn": (_i, [_vp, _vp, _i, _i, _i, _vp, _vp]),
     "cluster_attn_exact_forward": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp,
                                         _i, _vp]),
     "cluster_attn_backward_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -376,4 +377,17 @@ def ca_gemm_bf16(A, Bt, stream=None):
     C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     st = lib().ca_gemm_bf16(_ptr(A), _ptr(Bt), M, N, Kd, _ptr(C), _stream(stream))
     _check(st, "ca_gemm_bf16")
+    return C
+
+
+def ca_gemm_bf16_kn(A, W, stream=None):
+    """C = A W for bfloat16 GPU tensors A [M, Kd] and W [Kd, N] ([in, out]); returns C [M, N]."""
+    torch = _torch()
+    M, Kd = A.shape
+    Kw, N = W.shape
+    if Kw != Kd:
+        raise ValueError("A and W disagree on the contraction length")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    st = lib().ca_gemm_bf16_kn(_ptr(A), _ptr(W), M, N, Kd, _ptr(C), _stream(stream))
+    _check(st, "ca_gemm_bf16_kn")
     return C

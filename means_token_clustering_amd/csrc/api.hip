@@ -430,18 +430,17 @@ ca_status_t check_step(int S, int L, int d, int Kc, ca_dtype_t dt) {
 }
 
 // Workspace of the full layer, carved in this order (each 256-B aligned):
-// the four transposed weights, Q/K/V ([3, B, H, L, 64]; unused when the
-// caller passes qkv_out), the attention output O ([B, H, L, 64]) and the
-// cluster attention workspace of the bf16 [B, H, L, 64] problem.
+// Q/K/V ([3, B, H, L, 64]; unused when the caller passes qkv_out), the
+// attention output O ([B, H, L, 64]) and the cluster attention workspace of
+// the bf16 [B, H, L, 64] problem.
 struct LayerLayout {
-    size_t wt, qkv, o, attn, attn_bytes, total;
+    size_t qkv, o, attn, attn_bytes, total;
 };
 
 LayerLayout layer_layout(int B, int L, int Dm, int H, int nclust) {
     LayerLayout w{};
     const size_t tok = (size_t)B * L;
     size_t off = 0;
-    w.wt = off;   off += align_up(sizeof(uint16_t) * 4 * (size_t)Dm * Dm);
     w.qkv = off;  off += align_up(sizeof(uint16_t) * 3 * tok * Dm);
     w.o = off;    off += align_up(sizeof(uint16_t) * tok * Dm);
     w.attn = off;
@@ -796,44 +795,52 @@ ca_status_t cluster_attn_layer_forward(const void *X, const void *Wq, const void
             if (o.p && overlap(o.p, o.n, i.p, i.n)) return CA_ERR_INVALID_ARG;
 
     char *ws = static_cast<char *>(workspace);
-    uint16_t *wt[4];
-    for (int i = 0; i < 4; ++i)
-        wt[i] = reinterpret_cast<uint16_t *>(ws + lay.wt) + (size_t)i * Dm * Dm;
-    const uint16_t *wsrc[4] = {static_cast<const uint16_t *>(Wq), static_cast<const uint16_t *>(Wk),
-                               static_cast<const uint16_t *>(Wv), static_cast<const uint16_t *>(Wo)};
     uint16_t *qkv = qkv_out ? static_cast<uint16_t *>(qkv_out)
                             : reinterpret_cast<uint16_t *>(ws + lay.qkv);
     uint16_t *heads[3] = {qkv, qkv + tok * Dm, qkv + 2 * tok * Dm};
     uint16_t *O = reinterpret_cast<uint16_t *>(ws + lay.o);
-    // W is [in, out]; the matrix cores read both operands along the contraction
-    CA_TRY(launch_transpose_bf16(wsrc, wt, 4, Dm, Dm, stream));
-    const uint16_t *wqkv[3] = {wt[0], wt[1], wt[2]};
-    CA_TRY(launch_gemm_nt(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
-                          false, true, L, H, stream));
+    // the weights are read in their [in, out] layout
+    const uint16_t *wqkv[3] = {static_cast<const uint16_t *>(Wq), static_cast<const uint16_t *>(Wk),
+                               static_cast<const uint16_t *>(Wv)};
+    CA_TRY(launch_gemm_bf16(static_cast<const uint16_t *>(X), wqkv, heads, 3, (int)tok, Dm, Dm,
+                            true, false, true, L, H, device_cus(), stream));
     st = forward_impl(heads[0], heads[1], heads[2], nullptr, 1, 0, B, H, L, d, nclust, iters, W,
                       alpha, O, assign_out, CA_BF16, ws + lay.attn, lay.attn_bytes, CA_PATH_AUTO,
                       stream);
     if (st != CA_OK) return st;
-    const uint16_t *wo[1] = {wt[3]};
+    const uint16_t *wo[1] = {static_cast<const uint16_t *>(Wo)};
     uint16_t *yv[1] = {static_cast<uint16_t *>(Y)};
-    return hip_status(launch_gemm_nt(O, wo, yv, 1, (int)tok, Dm, Dm, true, false, L, H, stream));
+    return hip_status(
+        launch_gemm_bf16(O, wo, yv, 1, (int)tok, Dm, Dm, true, true, false, L, H, device_cus(),
+                         stream));
+}
+
+static ca_status_t gemm_entry(const void *A, const void *B, int M, int N, int Kd, void *C,
+                              bool w_kn, hipStream_t stream) {
+    if (!A || !B || !C || M < 1 || N < 1 || Kd < 1) return CA_ERR_INVALID_ARG;
+    if ((long long)M * Kd > (1LL << 40) || (long long)N * Kd > (1LL << 40) ||
+        (long long)M * N > (1LL << 40))
+        return CA_ERR_INVALID_ARG;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16)) return CA_ERR_INVALID_ARG;
+    const size_t ca = sizeof(uint16_t) * (size_t)M * Kd, cb = sizeof(uint16_t) * (size_t)N * Kd,
+                 cc = sizeof(uint16_t) * (size_t)M * N;
+    if (overlap(C, cc, A, ca) || overlap(C, cc, B, cb)) return CA_ERR_INVALID_ARG;
+    if (N % 64 != 0 || Kd % 64 != 0 || M > (1 << 30) || (long long)N * Kd >= (1LL << 31))
+        return CA_ERR_UNSUPPORTED;
+    const uint16_t *b[1] = {static_cast<const uint16_t *>(B)};
+    uint16_t *c[1] = {static_cast<uint16_t *>(C)};
+    return hip_status(launch_gemm_bf16(static_cast<const uint16_t *>(A), b, c, 1, M, N, Kd, w_kn,
+                                       false, false, 1, 1, device_cus(), stream));
 }
 
 ca_status_t ca_gemm_bf16(const void *A, const void *Bt, int M, int N, int Kd, void *C,
                          hipStream_t stream) {
-    if (!A || !Bt || !C || M < 1 || N < 1 || Kd < 1) return CA_ERR_INVALID_ARG;
-    if ((long long)M * Kd > (1LL << 40) || (long long)N * Kd > (1LL << 40) ||
-        (long long)M * N > (1LL << 40))
-        return CA_ERR_INVALID_ARG;
-    if (!aligned(A, 16) || !aligned(Bt, 16) || !aligned(C, 16)) return CA_ERR_INVALID_ARG;
-    const size_t ca = sizeof(uint16_t) * (size_t)M * Kd, cb = sizeof(uint16_t) * (size_t)N * Kd,
-                 cc = sizeof(uint16_t) * (size_t)M * N;
-    if (overlap(C, cc, A, ca) || overlap(C, cc, Bt, cb)) return CA_ERR_INVALID_ARG;
-    if (N % 64 != 0 || Kd % 64 != 0 || M > (1 << 30) || N > (1 << 30)) return CA_ERR_UNSUPPORTED;
-    const uint16_t *b[1] = {static_cast<const uint16_t *>(Bt)};
-    uint16_t *c[1] = {static_cast<uint16_t *>(C)};
-    return hip_status(launch_gemm_nt(static_cast<const uint16_t *>(A), b, c, 1, M, N, Kd, false,
-                                     false, 1, 1, stream));
+    return gemm_entry(A, Bt, M, N, Kd, C, false, stream);
+}
+
+ca_status_t ca_gemm_bf16_kn(const void *A, const void *W, int M, int N, int Kd, void *C,
+                            hipStream_t stream) {
+    return gemm_entry(A, W, M, N, Kd, C, true, stream);
 }
 
 }  // extern "C"

@@ -189,8 +189,9 @@ def test_layer_rejects(kw, code):
 def test_layer_workspace_size():
     lib = b.lib()
     n = lib.cluster_attn_layer_workspace_size(16, 512, 768, 12, 64, 16)
-    # transposed weights + Q/K/V + O + staged attention workspace
-    assert n >= 4 * 768 * 768 * 2 + 4 * 16 * 512 * 768 * 2 and n % 256 == 0
+    # Q/K/V + O + staged attention workspace (no copy of the weights)
+    assert n >= 4 * 16 * 512 * 768 * 2 and n % 256 == 0
+    assert n < 4 * 768 * 768 * 2 + 4 * 16 * 512 * 768 * 2 + (64 << 20)
     assert lib.cluster_attn_layer_workspace_size(16, 512, 768, 12, 32, 16) == 0
     assert lib.cluster_attn_layer_workspace_size(16, 512, 700, 12, 64, 16) == 0
 
@@ -204,6 +205,14 @@ def test_gemm_rejects():
     assert lib.ca_gemm_bf16(A_ + 8, B_, 64, 64, 64, C_, None) == INV
     assert lib.ca_gemm_bf16(A_, B_, 64, 100, 64, C_, None) == UNS
     assert lib.ca_gemm_bf16(A_, B_, 64, 64, 96, C_, None) == UNS
+    for fn in (lib.ca_gemm_bf16, lib.ca_gemm_bf16_kn):
+        assert fn(A_, None, 64, 64, 64, C_, None) == INV
+        assert fn(A_, B_, 64, 64, 64, B_ + 2048, None) == INV   # C overlaps the weight
+        assert fn(A_, B_, 64, 64, 64, C_ + 4, None) == INV
+        assert fn(A_, B_, 64, 64, 0, C_, None) == INV
+        assert fn(A_, B_, 64, 192, 32, C_, None) == UNS
+        far = [1 << 44, 2 << 44, 3 << 44]   # distinct, 16-byte aligned, never touched
+        assert fn(far[0], far[1], 64, 1 << 16, 1 << 15, far[2], None) == UNS   # N * Kd >= 2^31
 
 
 MASK = 0x10000000 * 8

@@ -69,6 +69,22 @@ def test_gemm_bf16(M, N, Kd):
     check_rounded_product(_host(C), A64, np.ascontiguousarray(B64.T), "C")
 
 
+@pytest.mark.parametrize("M,N,Kd", [(300, 192, 256), (64, 64, 64), (1, 128, 768), (513, 768, 768),
+                                    (257, 320, 128), (129, 2304, 768)])
+def test_gemm_bf16_kn(M, N, Kd):
+    """Weights in the [in, out] layout: partial 192-column tiles (N = 64, 128,
+    320), ragged M, one k step, the stand-alone projection shape's width."""
+    _say(f"[gemm kn] M={M} N={N} Kd={Kd}")
+    rng = np.random.default_rng(M * 11 + N)
+    A = gen.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
+    W = gen.f32_to_bf16_bits((0.05 * rng.standard_normal((Kd, N))).astype(np.float32))
+    C = _b().ca_gemm_bf16_kn(_dev_bf16(A), _dev_bf16(W))
+    torch.cuda.synchronize()
+    A64 = gen.bf16_bits_to_f32(A).astype(np.float64)
+    W64 = gen.bf16_bits_to_f32(W).astype(np.float64)
+    check_rounded_product(_host(C), A64, W64, "C")
+
+
 # ------------------------------------------------------------------ layer
 def run_layer(x: gen.LayerInputs):
     """Layer runs with iters = 1..I; returns per-iteration assignments, the
