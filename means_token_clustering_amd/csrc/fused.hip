@@ -246,11 +246,43 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         load_row8<T, FULL>(Kx + kvbase, it >> 3, L, (it & 7) * 8, kraw[n]);
     }
     const int tv = iters >= 3 ? 3 : iters;   // iteration that requests V
+    // iteration at whose start the K planes are written (into the K region,
+    // which the clustering does not use), from the maximum published at the
+    // end of the iteration before; 0: after the clustering (one iteration)
+    const int tk = iters >= 2 ? 2 : 0;
+    int sk = 0;
+    // K planes: the items of this thread (rows it/8, dims 8 (it%8) ..,
+    // it = tid, tid + 512), range-scaled by 2^-sk
+    auto k_planes = [&]() {
+        uint32_t mk = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) mk = max(mk, sMax[4 * ww + 1]);
+        sk = scale_shift(mk, kKVLimit);
+        if (__builtin_expect(sk != 0, 0)) {   // uniform; rare
+            const float fk = __builtin_ldexpf(1.f, -sk);
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kraw[n][i] *= fk;
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int it = tid + kThreads * n;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
+            const Sp8 kp = split8(x);
+            const int o = off64(it >> 3, (it & 7) * 8);
+            st16(sK + o, kp.h);
+            st16(sK + kPlaneE + o, kp.m);
+        }
+    };
 
     // ------------------------------------------------------------ Lloyd
     const u32x4_t ones_g0 = g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
     int cprev = -1;
     for (int t = 1; t <= iters; ++t) {
+        if (t == tk) k_planes();
         if (t == tv) {
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
@@ -336,23 +368,19 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 }
             }
         }
-        if (t == iters) {   // largest |k| of the slice, published by the barrier below
+        if (t == (tk > 0 ? tk - 1 : iters)) {   // largest |k| of the slice, published by the barrier below
             const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
             if (lane == 0) sMax[w * 4 + 1] = bk;
         }
         __syncthreads();
     }
-
-    // ------------------------------------------------------------ K planes
-    // (V, requested last, gets its maximum here and its planes in the next
-    // phase)
-    int sk;
-    {
-        uint32_t mk = 0;
-#pragma unroll
-        for (int ww = 0; ww < 8; ++ww) mk = max(mk, sMax[4 * ww + 1]);
-        sk = scale_shift(mk, kKVLimit);
+    if (tk == 0) {   // one iteration: the K planes now, published with the V maximum
+        k_planes();
     }
+
+    // ------------------------------------------------------------ after the clustering
+    // (V, requested last, gets its maximum after the scores and its planes
+    // after the barrier that follows, in the place of the Q planes)
     const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;   // log2(e)/sqrt(64)
     // soft gather: softmax over the final centroids of token tok, clusters
     // 4g .. 4g+3 (the B operand of the gather product below, normalised)
@@ -380,29 +408,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         psoft = split4<true>(x[0] * iz, x[1] * iz, x[2] * iz, x[3] * iz);
     }
     uint16_t *sV = sQV;   // Q planes are dead
-    {
-        if (__builtin_expect(sk != 0, 0)) {   // uniform; rare
-            const float fk = __builtin_ldexpf(1.f, -sk);
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) kraw[n][i] *= fk;
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int it = tid + kThreads * n;
-            float x[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = kraw[n][i];
-            const Sp8 kp = split8(x);
-            const int o = off64(it >> 3, (it & 7) * 8);
-            st16(sK + o, kp.h);
-            st16(sK + kPlaneE + o, kp.m);
-        }
-        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
-        if (lane == 0) sMax[w * 4 + 2] = bv;
-    }
-    __syncthreads();
+    if (tk == 0) __syncthreads();   // the K planes written after the clustering
 
     // ------------------------------------------------------------ centroid-key scores
     float sx[4];
@@ -429,7 +435,12 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         }
         if (g == 0) sXm[l16 * 8 + w] = mloc;
     }
-    // V planes (first read after the next two barriers)
+    {   // largest |v| of the slice (V arrives last: after the scores)
+        const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+        if (lane == 0) sMax[w * 4 + 2] = bv;
+    }
+    __syncthreads();   // V maxima and the score maxima published
+    // V planes (first read after the next barrier)
     int sv;
     {
         uint32_t mv = 0;
@@ -456,7 +467,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         st16(sV + o, vp.h);
         st16(sV + kPlaneE + o, vp.m);
     }
-    __syncthreads();   // mu and the one-hot matrix are dead from here on (P reuses them)
+    // mu and the one-hot matrix are dead from here on (P reuses them): every
+    // wave read mu for its scores before the barrier above
     {
         const float4 m0 = *reinterpret_cast<const float4 *>(sXm + l16 * 8);
         const float4 m1 = *reinterpret_cast<const float4 *>(sXm + l16 * 8 + 4);
