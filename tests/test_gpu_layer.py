@@ -70,10 +70,13 @@ def test_gemm_bf16(M, N, Kd):
 
 
 @pytest.mark.parametrize("M,N,Kd", [(300, 192, 256), (64, 64, 64), (1, 128, 768), (513, 768, 768),
-                                    (257, 320, 128), (129, 2304, 768)])
+                                    (257, 320, 128), (129, 2304, 768), (8192, 2304, 64),
+                                    (8100, 2304, 128)])
 def test_gemm_bf16_kn(M, N, Kd):
     """Weights in the [in, out] layout: partial 192-column tiles (N = 64, 128,
-    320), ragged M, one k step, the stand-alone projection shape's width."""
+    320), ragged M, one k step, the stand-alone projection shape's width; with
+    at least as many 256 x 288 tiles as CUs (the last two) the large-tile
+    launch runs, here with two and four k steps and a ragged last row tile."""
     _say(f"[gemm kn] M={M} N={N} Kd={Kd}")
     rng = np.random.default_rng(M * 11 + N)
     A = gen.f32_to_bf16_bits(rng.standard_normal((M, Kd)).astype(np.float32))
