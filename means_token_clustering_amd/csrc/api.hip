@@ -337,8 +337,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     float *vcent = reinterpret_cast<float *>(ws + lay.vcent);
     float *xpart = reinterpret_cast<float *>(ws + lay.xpart);
     const bool km_mfma = plan.km_mfma;
-    const int nblk = km_mfma ? kmeans_mfma_blocks(L) : kmeans_tiles(L);
     const bool chain = plan.chain;
+    const int nsub = km_mfma && !chain ? kmeans_mfma_run(S, L, device_cus()) : 1;
+    const int nblk = km_mfma ? kmeans_mfma_parts(L, nsub) : kmeans_tiles(L);
     float *ps[2] = {psum, chain ? reinterpret_cast<float *>(ws + lay.part_sum2) : psum};
     int32_t *pc[2] = {pcnt, chain ? reinterpret_cast<int32_t *>(ws + lay.part_cnt2) : pcnt};
     const bool one_launch = plan.kind == kPlanSlice;
@@ -369,7 +370,7 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         if (km_mfma)
             CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, ct, ps[cur], pc[cur], stream,
                                       var.init_step, mu0, chain && t > 1 ? ps[cur ^ 1] : nullptr,
-                                      chain && t > 1 ? pc[cur ^ 1] : nullptr));
+                                      chain && t > 1 ? pc[cur ^ 1] : nullptr, nsub));
         else
             CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, ct, psum, pcnt, stream,
                                         var.init_step, mu0));

@@ -8,14 +8,19 @@
 // token i is mu_k . q_i - ||mu_k||^2 / 2 (the largest is the nearest); ties
 // go to the lowest index.
 //
-// Work split: one workgroup (8 waves) per 128-token block of a slice; wave w
-// owns token tile w, as in the single-launch forward. The centroids sit in
+// Work split: one workgroup (8 waves) per run of up to nsub consecutive
+// 128-token blocks of a slice (nsub = 1 when the blocks fill the chip at most
+// two deep); wave w owns token tile w of each block, as in the single-launch
+// forward. The workgroup takes its blocks in order, requesting the next
+// block's Q rows while it scores the current one, and keeps the run's cluster
+// sums in fp32 registers (block sums added in block order), so a run of nsub
+// blocks writes one partial instead of nsub. The centroids sit in
 // LDS as fp16 h/m planes of up to 64 rows with their -||mu||^2/2 parts; each
 // group of 16 clusters costs one chain of seven products per wave, and the
 // running best over the groups keeps the earlier group on equal scores. The
 // block's cluster sums and sizes are one-hot products of the same planes
 // (Q^T times the [cluster][token] one-hot matrix, exact 0/1 weights), stored
-// per block; centroid_reduce_kernel adds the blocks in a fixed order, or, for
+// per run; centroid_reduce_kernel adds the runs in a fixed order, or, for
 // few blocks, the next step's workgroups add them themselves.
 // Q and the centroids are scaled by one power of two per block (the largest
 // |q| or |mu|), which leaves every comparison unchanged; the sums are scaled
@@ -42,9 +47,10 @@ static_assert(kKLds <= 81920, "two workgroups per CU");
 
 // SCORES: instead of the assignment, write every score mu_k . q_i -
 // ||mu_k||^2 / 2 in unscaled units to scores [S, L, Kc] (no partials).
-template <typename T, bool INIT, bool SCORES>
+// RUN: runs of nsub blocks per workgroup; else one block (nsub is 1).
+template <typename T, bool INIT, bool SCORES, bool RUN>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
-    const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk,
+    const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk, int nsub,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
     int init_step, float *__restrict__ mu_init, const float *__restrict__ prev_sum,
     const int32_t *__restrict__ prev_cnt, float *__restrict__ scores) {
@@ -59,19 +65,37 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const int blk = blockIdx.x % nblk;
-    const long s = blockIdx.x / nblk;
+    // runs of nsub blocks; the slices' shorter last runs come after all the
+    // full runs, so that they are the workgroups of a second round
+    const unsigned nfull = (unsigned)(nblk / nsub), npart = (unsigned)((nblk + nsub - 1) / nsub);
+    const unsigned nfw = gridDim.x / npart * nfull;   // workgroups of full runs
+    unsigned s32, part;
+    if (!RUN) {
+        s32 = blockIdx.x / (unsigned)nblk;
+        part = blockIdx.x - s32 * (unsigned)nblk;
+    } else if (blockIdx.x < nfw) {
+        s32 = blockIdx.x / nfull;
+        part = blockIdx.x - s32 * nfull;
+    } else {
+        s32 = blockIdx.x - nfw;
+        part = nfull;
+    }
+    const long s = s32;
+    const int b0 = RUN ? (int)part * nsub : (int)part;
+    const int b1 = RUN ? min(nblk, b0 + nsub) : b0 + 1;
     const T *Qs = Q + s * (long)L * kD;
-    const int i0 = 128 * blk;
-    const int Lb = min(128, L - i0);               // tokens of the block
-    const int tok = 16 * w + l16;                  // the lane's token in the block
+    const int tok = 16 * w + l16;                  // the lane's token in a block
     const int NG = (Kc + 15) >> 4;                 // groups of 16 clusters
     const LaneOffs lo = lane_offsets(l16, g);
 
-    // the wave's Q rows (dims 32c + 8g ..), zeros past the block
+    // the wave's Q rows of the first block (dims 32c + 8g ..), zeros past it
     float qraw[2][8];
+    {
+        const int Lb0 = min(128, L - 128 * b0);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) load_row8<T, false>(Qs + (long)i0 * kD, tok, Lb, 32 * c + 8 * g, qraw[c]);
+        for (int c = 0; c < 2; ++c)
+            load_row8<T, false>(Qs + (long)(128 * b0) * kD, tok, Lb0, 32 * c + 8 * g, qraw[c]);
+    }
     // centroid row tid / 8, dims 8 (tid % 8) .. (zeros for rows >= Kc)
     const int mrow = tid >> 3, mcol = (tid & 7) * 8;
     float mraw[8];
@@ -79,21 +103,21 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         if (INIT) {
             const long row = init_row(mrow, L, Kc, init_step);
             load8<T>(Qs + row * kD + mcol, mraw);
-            if (mu_init && blk == 0) {
+            if (mu_init && part == 0) {
                 *reinterpret_cast<float4 *>(mu_init + (s * Kc + mrow) * kD + mcol) =
                     make_float4(mraw[0], mraw[1], mraw[2], mraw[3]);
                 *reinterpret_cast<float4 *>(mu_init + (s * Kc + mrow) * kD + mcol + 4) =
                     make_float4(mraw[4], mraw[5], mraw[6], mraw[7]);
             }
         } else if (prev_sum) {
-            // the previous step's block sums of this slice, added in block
-            // order, over max(1, n) (the update of centroid_reduce_kernel)
+            // the previous step's run sums of this slice, added in run order,
+            // over max(1, n) (the update of centroid_reduce_kernel)
             float x[8];
             int n = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) mraw[i] = 0.f;
-            for (int b2 = 0; b2 < nblk; ++b2) {
-                const long pr = (s * nblk + b2) * (long)Kc + mrow;
+            for (int b2 = 0; b2 < (int)npart; ++b2) {
+                const long pr = (s * (long)npart + b2) * (long)Kc + mrow;
                 load8<float>(prev_sum + pr * kD + mcol, x);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) mraw[i] += x[i];
@@ -109,8 +133,18 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) mraw[i] = 0.f;
     }
+    const float mmax = absmax8(mraw, 0.f);
+
+    // the run's cluster sums: tile u = w + 8 j (dimension tile u % 4, cluster
+    // group u / 4), four dims per lane, and the tile's cluster sizes
+    float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float accn[2] = {0.f, 0.f};
+
+    for (int blk = b0; blk < b1; ++blk) {
+    const int i0 = 128 * blk;
+    const int Lb = min(128, L - i0);               // tokens of the block
     {
-        const float mq = absmax8(qraw[1], absmax8(qraw[0], absmax8(mraw, 0.f)));
+        const float mq = absmax8(qraw[1], absmax8(qraw[0], mmax));
         const uint32_t b = wave_max_u(__float_as_uint(mq));
         if (lane == 0) sMax[w] = b;
     }
@@ -166,6 +200,13 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         *reinterpret_cast<u32x2_t *>(sMuX + mrow * kKMuXCols + c0) = u32x2_t{v0, v1};
     }
     __syncthreads();
+    // the next block's Q rows, in flight while this block is scored
+    if (blk + 1 < b1) {
+        const int Ln = min(128, L - i0 - 128);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+            load_row8<T, false>(Qs + (long)(i0 + 128) * kD, tok, Ln, 32 * c + 8 * g, qraw[c]);
+    }
 
     // ------------------------------------------------------------ assignment
     const bool tok_in = tok < Lb;
@@ -221,33 +262,58 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
             sOH[off128(rk, tok)] = 0x3c00;   // fp16 1.0
         }
     }
-    if (SCORES || part_sum == nullptr) return;
+    if (!SCORES && part_sum != nullptr) {
     __syncthreads();
 
     // ------------------------------------------------------------ cluster sums
     // tile u = (dimension tile dt = u % 4, cluster group kg = u / 4): sums of
     // dims 16 dt + 4g + rr for cluster 16 kg + l16, and its size
-    const long pb = (s * nblk + blk) * (long)Kc;
     const float back = __builtin_ldexpf(1.f, sq);
     const u32x4_t ones = {kOneH2, kOneH2, kOneH2, kOneH2};
-    const int nch = (Lb + 31) >> 5;
-    for (int u = w; u < 4 * NG; u += 8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = w + 8 * j;
+        if (u >= 4 * NG) break;
         const int dt = u & 3, kg = u >> 2;
         const int trq0 = 1024 * g + (lo.tr0 ^ (32 * dt)), trq1 = 1024 * g + (lo.tr4 ^ (32 * dt));
+        // the chunks of 32 tokens: in a run all four (past the block's tokens
+        // the Q planes and the one-hot rows are zero, so those products add
+        // exact zeros), unrolled; a single block stops at its last chunk
         f32x4_t sh = kZero4, sm = kZero4, cnt = kZero4;
-        for (int c = 0; c < nch; ++c) {
+        auto chunk = [&](int c) {
             const u32x4_t oh = ldb16(pOH, 4096 * kg + (lo.rl128 ^ (64 * c)));
             const Sp8 qt = colfrag8_at(pQ, 4096 * c + trq0, 4096 * c + trq1);
             sm = mma(qt.m, oh, sm);
             sh = mma(qt.h, oh, sh);
             if (dt == 0) cnt = mma(ones, oh, cnt);
+        };
+        if constexpr (RUN) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) chunk(c);
+        } else {
+            const int nch = (Lb + 31) >> 5;
+            for (int c = 0; c < nch; ++c) chunk(c);
         }
-        const int k = 16 * kg + l16;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[j][rr] += (sm[rr] + sh[rr]) * back;
+        accn[j] += cnt[0];
+    }
+    }
+    if (blk + 1 < b1) __syncthreads();   // the planes and the one-hot matrix are rewritten
+    }   // blocks of the run
+    if (SCORES || part_sum == nullptr) return;
+
+    // the run's sums and sizes
+    const long pb = (s * (long)npart + part) * (long)Kc;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = w + 8 * j;
+        if (u >= 4 * NG) break;
+        const int dt = u & 3, k = 16 * (u >> 2) + l16;
         if (k < Kc) {
             *reinterpret_cast<float4 *>(part_sum + (pb + k) * kD + 16 * dt + 4 * g) =
-                make_float4((sm[0] + sh[0]) * back, (sm[1] + sh[1]) * back,
-                            (sm[2] + sh[2]) * back, (sm[3] + sh[3]) * back);
-            if (dt == 0 && g == 0) part_cnt[pb + k] = (int32_t)cnt[0];
+                make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            if (dt == 0 && g == 0) part_cnt[pb + k] = (int32_t)accn[j];
         }
     }
 }
@@ -255,23 +321,38 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
 bool kmeans_mfma_supported(int Kc) { return Kc >= 1 && Kc <= kKM; }
 int kmeans_mfma_blocks(int L) { return (L + 127) / 128; }
 
+// Blocks per workgroup: one while the blocks fill the compute units at most
+// two deep (every workgroup resident in the first round), else runs of
+// kRunBlocks, which leaves about one run per compute unit for long slices.
+constexpr int kRunBlocks = 3;
+int kmeans_mfma_run(long S, int L, int cus) {
+    const int nblk = kmeans_mfma_blocks(L);
+    if (S * nblk <= 2L * cus) return 1;
+    return nblk < kRunBlocks ? nblk : kRunBlocks;
+}
+int kmeans_mfma_parts(int L, int nsub) { return (kmeans_mfma_blocks(L) + nsub - 1) / nsub; }
+
 template <typename T>
 static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, int L, int Kc,
                                        int32_t *assign, float *part_sum, int32_t *part_cnt,
                                        hipStream_t st, int init_step, float *mu_init,
-                                       const float *prev_sum, const int32_t *prev_cnt) {
+                                       const float *prev_sum, const int32_t *prev_cnt,
+                                       int nsub) {
     const int nblk = kmeans_mfma_blocks(L);
-    const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
+    const dim3 grid((unsigned)((long)S * kmeans_mfma_parts(L, nsub))), block(kThreads);
     const T *q = static_cast<const T *>(Q);
     float *const no_scores = nullptr;
-    if (mu == nullptr)
-        hipLaunchKernelGGL((kmeans_mfma_kernel<T, true, false>), grid, block, 0, st, q, mu, L, Kc,
-                           nblk, assign, part_sum, part_cnt, init_step, mu_init, prev_sum,
-                           prev_cnt, no_scores);
-    else
-        hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, false>), grid, block, 0, st, q, mu, L,
-                           Kc, nblk, assign, part_sum, part_cnt, init_step, mu_init, prev_sum,
-                           prev_cnt, no_scores);
+    auto launch = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, block, 0, st, q, mu, L, Kc, nblk, nsub, assign, part_sum,
+                           part_cnt, init_step, mu_init, prev_sum, prev_cnt, no_scores);
+    };
+    if (mu == nullptr) {
+        if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true>);
+        else launch(kmeans_mfma_kernel<T, true, false, false>);
+    } else {
+        if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true>);
+        else launch(kmeans_mfma_kernel<T, false, false, false>);
+    }
     return hipGetLastError();
 }
 
@@ -280,8 +361,8 @@ static hipError_t kmeans_scores_dispatch(const void *Q, const float *mu, int S, 
                                          float *scores, hipStream_t st) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
-    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true>), grid, block, 0, st,
-                       static_cast<const T *>(Q), mu, L, Kc, nblk, (int32_t *)nullptr,
+    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false>), grid, block, 0, st,
+                       static_cast<const T *>(Q), mu, L, Kc, nblk, 1, (int32_t *)nullptr,
                        (float *)nullptr, (int32_t *)nullptr, 0, (float *)nullptr,
                        (const float *)nullptr, (const int32_t *)nullptr, scores);
     return hipGetLastError();
@@ -296,12 +377,13 @@ hipError_t launch_kmeans_scores(const void *Q, const float *mu, int S, int L, in
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
                               hipStream_t st, int init_step, float *mu_init,
-                              const float *prev_sum, const int32_t *prev_cnt) {
+                              const float *prev_sum, const int32_t *prev_cnt, int nsub) {
+    if (nsub < 1) return hipErrorInvalidValue;
     if (dt == CA_BF16)
         return kmeans_mfma_dispatch<bf16_t>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                            init_step, mu_init, prev_sum, prev_cnt);
+                                            init_step, mu_init, prev_sum, prev_cnt, nsub);
     return kmeans_mfma_dispatch<float>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                       init_step, mu_init, prev_sum, prev_cnt);
+                                       init_step, mu_init, prev_sum, prev_cnt, nsub);
 }
 
 }  // namespace ca

@@ -44,17 +44,21 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
                                   bool keep_empty = false);
 
 // One Lloyd step on the matrix cores (kmeans_mfma.hip) for K <= 64: the
-// assignment and per-block (128 tokens) cluster sums / sizes laid out as
-// launch_kmeans_assign's partials with kmeans_mfma_blocks(L) blocks per
-// slice; part_sum == nullptr: assignment only. With prev_sum / prev_cnt (the
-// previous step's partials) the centroids are formed from them in block
-// order instead of being read from mu.
+// assignment and the cluster sums / sizes of each run of nsub 128-token
+// blocks, laid out as launch_kmeans_assign's partials with
+// kmeans_mfma_parts(L, nsub) runs per slice; part_sum == nullptr: assignment
+// only. With prev_sum / prev_cnt (the previous step's partials, same nsub)
+// the centroids are formed from them in run order instead of being read
+// from mu. kmeans_mfma_run picks nsub for S slices on cus compute units.
 bool kmeans_mfma_supported(int Kc);
 int kmeans_mfma_blocks(int L);
+int kmeans_mfma_run(long S, int L, int cus);
+int kmeans_mfma_parts(int L, int nsub);
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr,
-                              const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr);
+                              const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr,
+                              int nsub = 1);
 
 // Scores mu_k . q_i - ||mu_k||^2 / 2 of the matrix-core step (Kc <= 64) in
 // unscaled units, [S, L, Kc]: the distances the step compares.

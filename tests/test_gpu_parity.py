@@ -181,6 +181,23 @@ def test_segmented_long_workload():
     check(gen.workload("long_l8192"), 3)
 
 
+# staged Lloyd steps whose workgroups take runs of three 128-token blocks
+# (more blocks than two per compute unit); the slices' last runs are shorter
+# and launch after the full ones
+LLOYD_RUNS = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
+    (1, 8, 8498, 64, 2, 32, 0.5, "f32", 64),       # 67 blocks: a last run of one 50-token block
+    (1, 6, 11000, 48, 3, 24, 0.5, "bf16", 48),     # 86 blocks: a last run of two, ragged
+]
+
+
+@pytest.mark.parametrize("case", LLOYD_RUNS)
+def test_lloyd_block_runs(case):
+    B, H, L, nclust, iters, W, alpha, dtype, blobs = case
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
+                        dtype=dtype, seed=7000 + L, blobs=blobs, name="lloyd_runs")
+    check(x, 0)
+
+
 def test_empty_cluster_and_exact_ties():
     """L=8, K=2, Q[4] = Q[0]: identical initial centroids tie exactly, so all
     tokens take cluster 0; cluster 1 becomes the zero vector; at iteration 2

@@ -43,6 +43,7 @@ PATHS = [
     ("kmeans_window (window beside)", 2, 1, 4, 300, 16, 3, 32, "f32", 10, 0, False),
     ("chained matrix-core steps", 2, 1, 2, 600, 32, 4, 32, "f32", 20, 0, False),
     ("steps with reduce launches", 2, 1, 2, 1100, 20, 3, 32, "f32", 20, 0, False),
+    ("steps over runs of blocks", 2, 1, 8, 8269, 64, 3, 32, "f32", 64, 0, False),
     ("scalar steps (K > 64)", 2, 1, 1, 300, 80, 3, 32, "f32", 40, 0, False),
     ("staged kept centroids", 2, 1, 2, 200, 16, 3, 32, "f32", 6, 2, False),
     ("staged masked", 2, 2, 2, 257, 24, 3, 20, "bf16", 10, 0, True),
