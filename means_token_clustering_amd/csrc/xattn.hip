@@ -73,8 +73,21 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
         load_row8<T, false>(Kx + kvrow * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
         load_row8<T, false>(Vx + kvrow * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
     }
-    float mm = 0.f;   // largest |mu| of the slice
-    for (int e = tid; e < Kc * (kD / 4); e += kThreads) {
+    // the slice's first 64 centroid rows: row tid / 8, dims 8 (tid % 8) ..
+    // (zeros past Kc), requested with K and V so that every group of 16
+    // takes its planes from registers
+    float mraw[8];
+    {
+        const int r = tid >> 3, c = (tid & 7) * 8;
+        if (r < Kc) {
+            load8<float>(mu + (s * Kc + r) * kD + c, mraw);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mraw[i] = 0.f;
+        }
+    }
+    float mm = absmax8(mraw, 0.f);   // largest |mu| of the slice
+    for (int e = kThreads * 2 + tid; e < Kc * (kD / 4); e += kThreads) {
         const float4 v = load4<float>(mu + s * (long)Kc * kD + 4 * e);
         mm = fmaxf(mm, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
@@ -135,7 +148,16 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
 
     // ------------------------------------------------------------ groups of 16 centroids
     for (int k0 = 0; k0 < Kc; k0 += kFK) {
-        if (tid < 128) {   // centroid row k0 + tid / 8, dims 8 (tid % 8) ..
+        if (k0 < 64 && (tid >> 7) == (k0 >> 4)) {   // rows k0 .. k0 + 15 from registers
+            const int r = (tid >> 3) - k0, c = (tid & 7) * 8;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = mraw[i] * fmu;
+            const Sp8 mp = split8(x);
+            const int o = off64(r, c);
+            st16(sMu + o, mp.h);
+            st16(sMu + kPlaneMuE + o, mp.m);
+        } else if (k0 >= 64 && tid < 128) {   // centroid row k0 + tid / 8, dims 8 (tid % 8) ..
             const int r = tid >> 3, c = (tid & 7) * 8;
             float x[8];
             if (k0 + r < Kc) {
