@@ -365,6 +365,7 @@ MASK_EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, mask kind
     (1, 2, 300, 16, 3, 32, 0.5, gen.F32, "prefix"),   # staged only (L > 128)
     (2, 2, 260, 40, 3, 20, 0.5, gen.F32, "holes"),    # staged, ragged last block
     (2, 2, 128, 16, 3, 32, 0.5, gen.F32, "zeros"),    # everything padded
+    (2, 4, 8300, 64, 2, 32, 0.5, gen.F32, "prefix"),  # Lloyd steps over runs of blocks
 ]
 
 
