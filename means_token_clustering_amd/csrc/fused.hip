@@ -114,6 +114,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     uint32_t *sMax = reinterpret_cast<uint32_t *>(smem + kOffMax);
 
     const int tid = threadIdx.x;
+    constexpr bool kZ = bf16_storage<T>();   // Q, K, V planes with zero m parts
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const bool keep_old = EXT && keep_empty != 0, soft_g = EXT && soft != 0;   // uniform
     const long slice = blockIdx.x;
@@ -296,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             const Sp8 mu0 = frag_at(pMu, kPlaneMu, lo.rl64), mu1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
             __builtin_amdgcn_sched_barrier(0);
             f32x4_t a = mma(mx, ones_g0, kZero4);
-            a = mma3(mu0, qf[0], a);
-            a = mma3(mu1, qf[1], a);
+            a = mma3z<false, kZ>(mu0, qf[0], a);
+            a = mma3z<false, kZ>(mu1, qf[1], a);
             float best = a[0];
             int bk = 4 * g;
 #pragma unroll
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
                 if (c < nch) {
                     const u32x4_t oh = ldb16(pOH, lo.rl128 ^ (64 * c));
                     const Sp8 qt = colfrag8_at(pQV, 4096 * c + trq0, 4096 * c + trq1);
-                    sm = mma(qt.m, oh, sm);
+                    if (!kZ) sm = mma(qt.m, oh, sm);
                     sh = mma(qt.h, oh, sh);
                     cnt = mma(ones, oh, cnt);
                 }
@@ -388,8 +389,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     if (soft_g && (FULL || w < NT)) {
         const Sp8 mu0 = frag_at(pMu, kPlaneMu, lo.rl64), mu1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
         __builtin_amdgcn_sched_barrier(0);
-        f32x4_t a = mma3(mu0, qf[0], kZero4);   // a[rr] = mu_{4g+rr} . q_tok (scaled units)
-        a = mma3(mu1, qf[1], a);
+        f32x4_t a = mma3z<false, kZ>(mu0, qf[0], kZero4);   // a[rr] = mu_{4g+rr} . q_tok (scaled units)
+        a = mma3z<false, kZ>(mu1, qf[1], a);
         const float s2 = __builtin_ldexpf(0.125f, 2 * sq) * 1.4426950408889634f;
         float x[4], mx = -__builtin_inff();
 #pragma unroll
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             const Sp8 k0 = frag_at(pK, kPlane, 2048 * w + lo.rl64), m0 = frag_at(pMu, kPlaneMu, lo.rl64);
             const Sp8 k1 = frag_at(pK, kPlane, 2048 * w + (lo.rl64 ^ 64)), m1 = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
             __builtin_amdgcn_sched_barrier(0);
-            f32x4_t a = mma3(k0, m0, kZero4);
-            a = mma3(k1, m1, a);
+            f32x4_t a = mma3z<kZ, false>(k0, m0, kZero4);
+            a = mma3z<kZ, false>(k1, m1, a);
             const uint32_t nib = MASKED ? kb.tile(w) >> (4 * g) : 0xfu;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         f32x4_t a2[2] = {kZero4, kZero4};   // even and odd key chunks
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            if (FULL || c < nch) a2[c & 1] = mma3(vf[c], pf[c], a2[c & 1]);
+            if (FULL || c < nch) a2[c & 1] = mma3z<kZ, false>(vf[c], pf[c], a2[c & 1]);
         const f32x4_t a = a2[0] + a2[1];
         const float4 l0 = *reinterpret_cast<const float4 *>(sXl + l16 * 8);
         const float4 l1 = *reinterpret_cast<const float4 *>(sXl + l16 * 8 + 4);
@@ -524,8 +525,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
     if (FULL || w < NT) {
         const int rad = radius < L ? radius : L;
         if (NARROW)
-            local_narrow<FULL, MASKED>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv,
-                                       kb, o, lsum);
+            local_narrow<FULL, MASKED, KeyBits, kPlane, kZ>(pK, pQV, qf, w, NT, L, rad, sscale2,
+                                                            l16, g, lo.rl64, trv, kb, o, lsum);
         else
             local_wide<FULL, MASKED>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, kb,
                                      o, lsum);

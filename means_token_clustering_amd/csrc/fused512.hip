@@ -76,6 +76,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const u8 *pQ = smem, *pMu = smem + kGOffMu, *pMuX = smem + kGOffMuX;
 
     const int tid = threadIdx.x;
+    constexpr bool kZ = bf16_storage<T>();   // Q (K, V) planes with zero m parts
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const long s = blockIdx.x;
     const long base = s * (long)L * kD;
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     const int tile = w + 16 * u;
                     if (tile < NT) {
                         f32x4_t a = mma(mx, ones_g0, kZero4);
-                        a = mma3(mu0, qf[u][0], a);
-                        a = mma3(mu1, qf[u][1], a);
+                        a = mma3z<false, kZ>(mu0, qf[u][0], a);
+                        a = mma3z<false, kZ>(mu1, qf[u][1], a);
                         float best = a[0];
                         int bk = 4 * g;
 #pragma unroll
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     }
                     const u32x4_t oh = {pk[0], pk[1], pk[2], pk[3]};
                     const Sp8 qt = colfrag8_at<kGPlaneQ>(pQ, 4096 * cc + trq0, 4096 * cc + trq1);
-                    sm = mma(qt.m, oh, sm);
+                    if (!kZ) sm = mma(qt.m, oh, sm);
                     sh = mma(qt.h, oh, sh);
                     cnt = mma(ones, oh, cnt);
                 }
@@ -329,8 +330,8 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 const Sp8 ka = frag_at(pK, kPlane, 2048 * wl + lo.rl64), ma = frag_at(pMu, kPlaneMu, lo.rl64);
                 const Sp8 kc = frag_at(pK, kPlane, 2048 * wl + (lo.rl64 ^ 64)), mc = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
                 __builtin_amdgcn_sched_barrier(0);
-                f32x4_t a = mma3(ka, ma, kZero4);
-                a = mma3(kc, mc, a);
+                f32x4_t a = mma3z<kZ, false>(ka, ma, kZero4);
+                a = mma3z<kZ, false>(kc, mc, a);
                 float mloc = -__builtin_inff();
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     if (c < nch) {
                         const Sp8 vf = colfrag8_at(pV, 4096 * c + trc0, 4096 * c + trc1);
                         const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
-                        a2[c & 1] = mma3(vf, pf, a2[c & 1]);
+                        a2[c & 1] = mma3z<kZ, false>(vf, pf, a2[c & 1]);
                     }
                 }
                 const float4 l0 = *reinterpret_cast<const float4 *>(xl + l16 * 8);
@@ -464,6 +465,12 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 mv = max(mv, sMax[4 * ww + 2]);
             }
             const int sk = scale_shift(mk, kKVLimit), sv = scale_shift(mv, kKVLimit);
+            // the wave's query rows of this pass, requested before the planes
+            // are built so that their latency passes during that work
+            const int tile = 16 * p + w;   // the wave's query tile of this pass
+            float qx[2][8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, qx[c]);
             {
                 const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
 #pragma unroll
@@ -486,7 +493,6 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 }
             }
             __syncthreads();
-            const int tile = 16 * p + w;   // the wave's query tile of this pass
             if (tile < NT) {
                 const int qt = (16 * tile - r0) >> 4;
                 const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
@@ -495,15 +501,13 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 Sp8 qp[2];
 #pragma unroll
                 for (int c = 0; c < 2; ++c) {
-                    float x[8];
-                    load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, x);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] *= fq;
-                    qp[c] = split8<true>(x);
+                    for (int i = 0; i < 8; ++i) qx[c][i] *= fq;
+                    qp[c] = split8<true>(qx[c]);
                 }
                 f32x4_t o[4];
                 float lsum;
-                local_narrow<false, false, KeyBits, kGPlane3>(pK3, pV3, qp, qt, NTp, Lp, rad,
+                local_narrow<false, false, KeyBits, kGPlane3, kZ>(pK3, pV3, qp, qt, NTp, Lp, rad,
                                                             sscale2, l16, g, lo.rl64, trv, kb, o,
                                                             lsum);
                 const int tok = 16 * tile + l16;

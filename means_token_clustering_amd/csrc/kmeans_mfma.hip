@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
              *pMuX = smem + kKOffMuX;
 
     const int tid = threadIdx.x;
+    constexpr bool kZ = bf16_storage<T>();   // Q (K, V) planes with zero m parts
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     // runs of nsub blocks; the slices' shorter last runs come after all the
     // full runs, so that they are the workgroups of a second round
@@ -221,8 +222,8 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
             const Sp8 mu1 = frag_at(pMu, kKMuPlane, 2048 * kg + (lo.rl64 ^ 64));
             __builtin_amdgcn_sched_barrier(0);
             f32x4_t a = mma(mx, ones_g0, kZero4);
-            a = mma3(mu0, qf[0], a);
-            a = mma3(mu1, qf[1], a);
+            a = mma3z<false, kZ>(mu0, qf[0], a);
+            a = mma3z<false, kZ>(mu1, qf[1], a);
             if (SCORES) {   // both operands carry 2^-sq: the score carries 2^-2sq
                 const float up2 = __builtin_ldexpf(1.f, 2 * sq);
 #pragma unroll
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         auto chunk = [&](int c) {
             const u32x4_t oh = ldb16(pOH, 4096 * kg + (lo.rl128 ^ (64 * c)));
             const Sp8 qt = colfrag8_at(pQ, 4096 * c + trq0, 4096 * c + trq1);
-            sm = mma(qt.m, oh, sm);
+            if (!kZ) sm = mma(qt.m, oh, sm);
             sh = mma(qt.h, oh, sh);
             if (dt == 0) cnt = mma(ones, oh, cnt);
         };

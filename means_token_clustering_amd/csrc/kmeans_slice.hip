@@ -58,6 +58,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
     const u8 *pQ = smem + kSOffQ, *pMu = smem + kSOffMu, *pMuX = smem + kSOffMuX;
 
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
+    constexpr bool kZ = bf16_storage<T>();   // Q (K, V) planes with zero m parts
     const T *Qs = Q + s * (long)L * kD;
     const int NT = (L + 15) >> 4;
     const LaneOffs lo = lane_offsets(l16, g);
@@ -144,8 +145,8 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                 const int tile = w + 16 * u;
                 if (tile < NT) {
                     f32x4_t a = mma(mx, ones_g0, kZero4);
-                    a = mma3(mu0, qf[u][0], a);
-                    a = mma3(mu1, qf[u][1], a);
+                    a = mma3z<false, kZ>(mu0, qf[u][0], a);
+                    a = mma3z<false, kZ>(mu1, qf[u][1], a);
                     float best = a[0];
                     int bk = 4 * g;
 #pragma unroll
@@ -186,7 +187,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                 }
                 const u32x4_t oh = {pk[0], pk[1], pk[2], pk[3]};
                 const Sp8 qt = colfrag8_at<kSPlane>(pQ, 4096 * cc + trq0, 4096 * cc + trq1);
-                sm = mma(qt.m, oh, sm);
+                if (!kZ) sm = mma(qt.m, oh, sm);
                 sh = mma(qt.h, oh, sh);
                 cnt = mma(ones, oh, cnt);
             }

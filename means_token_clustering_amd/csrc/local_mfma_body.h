@@ -197,8 +197,8 @@ __device__ __forceinline__ void local_window_block(
     float lsum = 1.f;
     if (wave_on) {
         const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
-        local_narrow<false, MASKED, KeyBits160, kMPlane>(pK, pV, qf, qt, NTp, Lp, rad, sscale2,
-                                                         l16, g, lo.rl64, trv, kb, o, lsum);
+        local_narrow<false, MASKED, KeyBits160, kMPlane, bf16_storage<T>()>(
+            pK, pV, qf, qt, NTp, Lp, rad, sscale2, l16, g, lo.rl64, trv, kb, o, lsum);
     }
     __syncthreads();   // the K planes become the output staging area, the V
                        // planes the V^cent table

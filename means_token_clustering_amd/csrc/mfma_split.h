@@ -107,6 +107,22 @@ __device__ __forceinline__ f32x4_t mma3(const Sp8 &a, const Sp8 &b, f32x4_t c) {
     c = mma(a.h, b.m, c);
     return mma(a.h, b.h, c);
 }
+// The same with the products of a's (ZA) or b's (ZB) m plane left out, for
+// operands split from bf16 storage. A bf16 value carries 8 significant bits,
+// so once scaled by a power of two into fp16's normal range it is an fp16
+// value: its h part is exact and its m part zero, and the left-out products
+// would add exact zeros (same result, same order of the remaining ones). Only
+// values that scale below fp16's smallest normal (2^-14; the scaled maxima
+// lie in [2^4, 2^15)) lose m parts below the subnormal step 2^-24.
+template <bool ZA, bool ZB>
+__device__ __forceinline__ f32x4_t mma3z(const Sp8 &a, const Sp8 &b, f32x4_t c) {
+    if (!ZA) c = mma(a.m, b.h, c);
+    if (!ZB) c = mma(a.h, b.m, c);
+    return mma(a.h, b.h, c);
+}
+// whether a storage type is bf16 (its split planes have zero m parts)
+template <typename T>
+constexpr bool bf16_storage() { return sizeof(T) == 2; }
 // the same on 16-deep operands (v_mfma_f32_16x16x16_f16: lane l holds
 // A[l%16][4(l/16)+i] and B[4(l/16)+i][l%16], i = 0..3; D as for 16x16x32)
 __device__ __forceinline__ f32x4_t mma16(u32x2_t a, u32x2_t b, f32x4_t c) {
@@ -314,8 +330,8 @@ struct KeyBits160 {
 // independent tiles alternate, so that neither the LDS latency nor the
 // matrix-core latency is exposed per product. PLANE: byte distance of the
 // h and m planes (rows of the planes: NT tiles of 16, L valid; KB: the key
-// mask of those rows).
-template <bool FULL, bool MASKED, typename KB = KeyBits, int PLANE = kPlane>
+// mask of those rows). Z: Q, K and V come from bf16 storage (mma3z).
+template <bool FULL, bool MASKED, typename KB = KeyBits, int PLANE = kPlane, bool Z = false>
 __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                              int qt, int NT, int L, int rad, float sscale2,
                                              int l16, int g, int rl64, int trv, const KB &kb,
@@ -334,10 +350,12 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
     f32x4_t sc[3] = {kZero4, kZero4, kZero4};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {   // the three mma3 chains, interleaved
+        if (!Z) {
 #pragma unroll
-        for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].m, qf[c].h, sc[d]);
+            for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].m, qf[c].h, sc[d]);
 #pragma unroll
-        for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].h, qf[c].m, sc[d]);
+            for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].h, qf[c].m, sc[d]);
+        }
 #pragma unroll
         for (int d = 0; d < 3; ++d) sc[d] = mma(kfr[d][c].h, qf[c].h, sc[d]);
     }
@@ -397,14 +415,18 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4_t acc[2] = {kZero4, kZero4};
+        if (!Z) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].m, pA.h, acc[u]);
+            for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].m, pA.h, acc[u]);
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].h, pA.m, acc[u]);
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[u] = mma(va[u].h, pA.h, acc[u]);
+        if (!Z) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) acc[u] = mma(vb[u].m, pB.h, acc[u]);
+            for (int u = 0; u < 2; ++u) acc[u] = mma(vb[u].m, pB.h, acc[u]);
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) acc[u] = mma(vb[u].h, pB.m, acc[u]);
 #pragma unroll

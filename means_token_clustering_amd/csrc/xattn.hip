@@ -55,6 +55,7 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
     const u8 *pK = smem + kXOffK, *pV = smem + kXOffV, *pMu = smem + kXOffMu, *pP = smem + kXOffP;
 
     const int tid = threadIdx.x;
+    constexpr bool kZ = bf16_storage<T>();   // Q (K, V) planes with zero m parts
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const int split = blockIdx.x % nsplit;
     const long s = blockIdx.x / nsplit;
@@ -180,8 +181,8 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
             const Sp8 ka = frag_at(pK, kPlane, 2048 * w + lo.rl64), ma = frag_at(pMu, kPlaneMu, lo.rl64);
             const Sp8 kc = frag_at(pK, kPlane, 2048 * w + (lo.rl64 ^ 64)), mc = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
             __builtin_amdgcn_sched_barrier(0);
-            f32x4_t a = mma3(ka, ma, kZero4);
-            a = mma3(kc, mc, a);
+            f32x4_t a = mma3z<kZ, false>(ka, ma, kZero4);
+            a = mma3z<kZ, false>(kc, mc, a);
             const uint32_t nib = MASKED ? kb.tile(w) >> (4 * g) : 0xfu;
             float mloc = -__builtin_inff();
 #pragma unroll
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
                 if (c < nch) {
                     const Sp8 vf = colfrag8_at(pV, 4096 * c + trq0, 4096 * c + trq1);
                     const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
-                    a2[c & 1] = mma3(vf, pf, a2[c & 1]);
+                    a2[c & 1] = mma3z<kZ, false>(vf, pf, a2[c & 1]);
                 }
             }
             const f32x4_t a = a2[0] + a2[1];
