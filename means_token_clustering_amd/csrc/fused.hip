@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             qf[c] = split8<true>(x);
             const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
             st16(sQV + o, qf[c].h);
-            st16(sQV + kPlaneE + o, qf[c].m);
+            if (!kZ) st16(sQV + kPlaneE + o, qf[c].m);   // zero for bf16 storage, never read
             if (owner) {
                 const int om = off64(kinit, 32 * c + 8 * g);
                 st16(sMu + om, qf[c].h);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             const Sp8 kp = split8(x);
             const int o = off64(it >> 3, (it & 7) * 8);
             st16(sK + o, kp.h);
-            st16(sK + kPlaneE + o, kp.m);
+            if (!kZ) st16(sK + kPlaneE + o, kp.m);   // zero for bf16 storage, never read
         }
     };
 
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
         const Sp8 vp = split8(x);
         const int o = off64(it >> 3, (it & 7) * 8);
         st16(sV + o, vp.h);
-        st16(sV + kPlaneE + o, vp.m);
+        if (!kZ) st16(sV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
     }
     // mu and the one-hot matrix are dead from here on (P reuses them): every
     // wave read mu for its scores before the barrier above
@@ -528,8 +528,8 @@ __global__ __launch_bounds__(kThreads, 4) void cluster_attn_fused_kernel(
             local_narrow<FULL, MASKED, KeyBits, kPlane, kZ>(pK, pQV, qf, w, NT, L, rad, sscale2,
                                                             l16, g, lo.rl64, trv, kb, o, lsum);
         else
-            local_wide<FULL, MASKED>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g, lo.rl64, trv, kb,
-                                     o, lsum);
+            local_wide<FULL, MASKED, false, kZ>(pK, pQV, qf, w, NT, L, rad, sscale2, l16, g,
+                                                lo.rl64, trv, kb, o, lsum);
     }
     __syncthreads();
 

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
             qf[u][c] = split8<true>(x);
             const int o = (2048 * (w + 16 * u) + (lo.rl64 ^ (64 * c))) / 2;
             st16(sQ + o, qf[u][c].h);
-            st16(sQ + kGPlaneQ / 2 + o, qf[u][c].m);
+            if (!kZ) st16(sQ + kGPlaneQ / 2 + o, qf[u][c].m);   // zero for bf16 storage, never read
         }
     if (tid < 128) {   // mu_k = Q[init_row(k)]; rows >= Kc: zero with a -inf part
         const int r = tid >> 3, c8 = (tid & 7) * 8;
@@ -317,9 +317,9 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     const Sp8 kp = split8(x), vp = split8(y);
                     const int o = off64(it >> 3, (it & 7) * 8);
                     st16(cK + o, kp.h);
-                    st16(cK + kPlaneE + o, kp.m);
+                    if (!kZ) st16(cK + kPlaneE + o, kp.m);   // zero for bf16 storage, never read
                     st16(cV + o, vp.h);
-                    st16(cV + kPlaneE + o, vp.m);
+                    if (!kZ) st16(cV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
                 }
                 if (r == 0 && 128 * (ch + 2) < L) load_chunk(ch + 2);   // the next round's chunk
             }
@@ -486,9 +486,9 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                         const Sp8 kp = split8(x), vp = split8(y);
                         const int o = off64(it >> 3, (it & 7) * 8);
                         st16(tK + o, kp.h);
-                        st16(tK + kGPlane3 / 2 + o, kp.m);
+                        if (!kZ) st16(tK + kGPlane3 / 2 + o, kp.m);   // zero for bf16 storage, never read
                         st16(tV + o, vp.h);
-                        st16(tV + kGPlane3 / 2 + o, vp.m);
+                        if (!kZ) st16(tV + kGPlane3 / 2 + o, vp.m);   // zero for bf16 storage, never read
                     }
                 }
             }

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         qf[c] = split8<true>(x);
         const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
         st16(sQ + o, qf[c].h);
-        st16(sQ + kPlaneE + o, qf[c].m);
+        if (!kZ) st16(sQ + kPlaneE + o, qf[c].m);   // zero for bf16 storage, never read
     }
     {
         float x[8], n2 = 0.f;

@@ -97,7 +97,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
             qf[u][c] = split8<true>(x);
             const int o = (2048 * (w + 16 * u) + (lo.rl64 ^ (64 * c))) / 2;
             st16(sQ + o, qf[u][c].h);
-            st16(sQ + kSPlane / 2 + o, qf[u][c].m);
+            if (!kZ) st16(sQ + kSPlane / 2 + o, qf[u][c].m);   // zero for bf16 storage, never read
         }
     // initial centroids mu_k = Q[init_row(k)] (rows >= Kc: zero, -inf part)
     if (tid < 128) {

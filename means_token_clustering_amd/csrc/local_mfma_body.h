@@ -162,9 +162,9 @@ __device__ __forceinline__ void local_window_block(
                 const Sp8 kp = split8(x), vp = split8(y);
                 const int o = off64(it >> 3, (it & 7) * 8);
                 st16(sK + o, kp.h);
-                st16(sK + kMPlaneE + o, kp.m);
+                if (!bf16_storage<T>()) st16(sK + kMPlaneE + o, kp.m);   // zero for bf16 storage, never read
                 st16(sV + o, vp.h);
-                st16(sV + kMPlaneE + o, vp.m);
+                if (!bf16_storage<T>()) st16(sV + kMPlaneE + o, vp.m);   // zero for bf16 storage, never read
             }
         }
     }

@@ -439,7 +439,8 @@ __device__ __forceinline__ void local_narrow(const u8 *pK, const u8 *pV, const S
 // products; a missing second tile gets zero weights on repeated V rows.
 // CAUSAL: the window is keys 0 .. qi instead (rad unused). mfinal (if not
 // null) receives the final running maximum of the column's base-2 logits.
-template <bool FULL, bool MASKED, bool CAUSAL = false>
+// Z: Q, K and V come from bf16 storage (mma3z).
+template <bool FULL, bool MASKED, bool CAUSAL = false, bool Z = false>
 __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8 *qf,
                                            int qt, int NT, int L, int rad, float sscale2,
                                            int l16, int g, int rl64, int trv, const KeyBits &kb,
@@ -458,8 +459,8 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ktt = two ? kt + h : kt;
-            f32x4_t a = mma3(frag_at(pK, kPlane, 2048 * ktt + rl64), qf[0], kZero4);
-            a = mma3(frag_at(pK, kPlane, 2048 * ktt + (rl64 ^ 64)), qf[1], a);
+            f32x4_t a = mma3z<Z, Z>(frag_at(pK, kPlane, 2048 * ktt + rl64), qf[0], kZero4);
+            a = mma3z<Z, Z>(frag_at(pK, kPlane, 2048 * ktt + (rl64 ^ 64)), qf[1], a);
             const uint32_t nib = MASKED ? kb.tile(ktt) >> (4 * g) : 0xfu;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
@@ -487,7 +488,7 @@ __device__ __forceinline__ void local_wide(const u8 *pK, const u8 *pV, const Sp8
         const int b0 = 2048 * kt + trv, b1 = two ? b0 + 2048 : b0;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            o[j] = mma3(colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j)), p, o[j] * f);
+            o[j] = mma3z<Z, false>(colfrag8_at(pV, b0 ^ (32 * j), b1 ^ (32 * j)), p, o[j] * f);
     }
     lsum = col_sum(ls);
     if (mfinal) *mfinal = M;

@@ -138,9 +138,9 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
             const Sp8 kp = split8(x), vp = split8(y);
             const int o = off64(it >> 3, (it & 7) * 8);
             st16(sK + o, kp.h);
-            st16(sK + kPlaneE + o, kp.m);
+            if (!kZ) st16(sK + kPlaneE + o, kp.m);   // zero for bf16 storage, never read
             st16(sV + o, vp.h);
-            st16(sV + kPlaneE + o, vp.m);
+            if (!kZ) st16(sV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
         }
     }
     const float sscale2 = __builtin_ldexpf(0.125f, smu + sk) * 1.4426950408889634f;
