@@ -320,6 +320,25 @@ def test_extreme_magnitudes(scales, path):
     assert err <= 1e-4 * sv
 
 
+@pytest.mark.parametrize("case", [(128, 0), (512, 1), (512, 2), (300, 2)])
+def test_bf16_tiny_elements(case):
+    """bf16 Q, K, V where a tenth of the elements are 2^-20 times smaller
+    than the rest: after the power-of-two scaling into fp16's range those fall
+    below fp16's smallest normal, the one place where the bf16 kernels'
+    omission of the m planes (zero for every other bf16 value) drops anything
+    (m parts under 2^-24 in scaled units). Same protocol and tolerances."""
+    L, path = case
+    x = gen.make_inputs(1, 3, L, 64, nclust=16, iters=3, W=32, alpha=0.5, dtype=gen.BF16,
+                        seed=91 + L, blobs=8, name="bf16_tiny")
+    rng = np.random.default_rng(5 + L)
+    for name in ("q", "k", "v"):
+        vals = gen.bf16_bits_to_f32(getattr(x, name)).astype(np.float64)
+        tiny = rng.random(vals.shape) < 0.1
+        vals = np.where(tiny, vals * 2.0 ** -20, vals).astype(np.float32)
+        setattr(x, name, gen.f32_to_bf16_bits(vals))
+    check(x, path)
+
+
 # ---------------------------------------------------------------- key-padding mask
 def check_masked(x: gen.AttnInputs, mask: np.ndarray, path: int, tol=None):
     """Masked forward: per-iteration assignments equal the unmasked run's (the
