@@ -57,7 +57,7 @@ ca_status_t check_shape(int B, int H, int L, int d, int nclust, int iters, int W
 
 // Workspace of the staged path, carved in this order (each 256-B aligned).
 struct StagedLayout {
-    size_t mu, assign, part_sum, part_cnt, part_sum2, part_cnt2, vcent, xpart, oloc, total;
+    size_t mu, assign, part_sum, part_cnt, part_sum2, part_cnt2, vcent, xpart, oloc, qmax, total;
 };
 
 // Lloyd steps on the matrix cores pass their block sums straight to the next
@@ -84,6 +84,9 @@ StagedLayout staged_layout(long S, int L, int Kc) {
     w.xpart = off;    off += nsplit > 1 ? align_up(sizeof(float) * S * nsplit * Kc * (kD + 2)) : 0;
     // alpha O^loc rows when the window runs beside the clustering
     w.oloc = off;     off += kmeans_slice_supported(L, Kc) ? align_up(sizeof(float) * S * L * kD) : 0;
+    // the largest |q| of each run of blocks of the matrix-core Lloyd steps
+    const long nrun = kmeans_mfma_supported(Kc) && !nchain ? kmeans_mfma_blocks(L) : 0;
+    w.qmax = off;     off += nrun ? align_up(sizeof(uint32_t) * S * nrun) : 0;
     w.total = off;
     return w;
 }
@@ -370,7 +373,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         if (km_mfma)
             CA_TRY(launch_kmeans_mfma(Q, mu_in, (int)S, L, Kc, dt, ct, ps[cur], pc[cur], stream,
                                       var.init_step, mu0, chain && t > 1 ? ps[cur ^ 1] : nullptr,
-                                      chain && t > 1 ? pc[cur ^ 1] : nullptr, nsub));
+                                      chain && t > 1 ? pc[cur ^ 1] : nullptr, nsub,
+                                      nsub > 1 ? reinterpret_cast<uint32_t *>(ws + lay.qmax)
+                                               : nullptr));
         else
             CA_TRY(launch_kmeans_assign(Q, mu_in, (int)S, L, Kc, dt, ct, psum, pcnt, stream,
                                         var.init_step, mu0));

@@ -48,12 +48,19 @@ static_assert(kKLds <= 81920, "two workgroups per CU");
 // SCORES: instead of the assignment, write every score mu_k . q_i -
 // ||mu_k||^2 / 2 in unscaled units to scores [S, L, Kc] (no partials).
 // RUN: runs of nsub blocks per workgroup; else one block (nsub is 1).
-template <typename T, bool INIT, bool SCORES, bool RUN>
+// qmax (RUN, nullable): the run's largest |q| (float bits), [S, runs]; the
+// first step (INIT) writes it, and with FIXED a later step takes it: one
+// scale for the whole run (with the centroids' maximum), the centroid planes
+// built once, no per-block maximum. Each block's own scale gives the same
+// products (power-of-two scaling is exact), so only fp16 subnormals differ.
+template <typename T, bool INIT, bool SCORES, bool RUN, bool FIXED>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk, int nsub,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
     int init_step, float *__restrict__ mu_init, const float *__restrict__ prev_sum,
-    const int32_t *__restrict__ prev_cnt, float *__restrict__ scores) {
+    const int32_t *__restrict__ prev_cnt, float *__restrict__ scores,
+    uint32_t *__restrict__ qmax) {
+    static_assert(!FIXED || (RUN && !INIT && !SCORES), "a fixed run scale is for later steps");
     __shared__ __align__(16) unsigned char smem[kKLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kKOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kKOffMu);
@@ -135,46 +142,12 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         for (int i = 0; i < 8; ++i) mraw[i] = 0.f;
     }
     const float mmax = absmax8(mraw, 0.f);
-
-    // the run's cluster sums: tile u = w + 8 j (dimension tile u % 4, cluster
-    // group u / 4), four dims per lane, and the tile's cluster sizes
-    float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    float accn[2] = {0.f, 0.f};
-
-    for (int blk = b0; blk < b1; ++blk) {
-    const int i0 = 128 * blk;
-    const int Lb = min(128, L - i0);               // tokens of the block
-    {
-        const float mq = absmax8(qraw[1], absmax8(qraw[0], mmax));
-        const uint32_t b = wave_max_u(__float_as_uint(mq));
-        if (lane == 0) sMax[w] = b;
+    {   // the centroids' largest magnitude, published by the first barrier below
+        const uint32_t b = wave_max_u(__float_as_uint(mmax));
+        if (lane == 0) sMax[8 + w] = b;
     }
-    // one-hot matrix cleared (16 KB: 32 bytes per thread)
-    reinterpret_cast<u32x4_t *>(sOH)[2 * tid] = u32x4_t{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4_t *>(sOH)[2 * tid + 1] = u32x4_t{0u, 0u, 0u, 0u};
-    __syncthreads();
-    int sq;
-    {
-        uint32_t m = 0;
-#pragma unroll
-        for (int ww = 0; ww < 8; ++ww) m = max(m, sMax[ww]);
-        sq = scale_shift(m, kQLimit);
-    }
-    const float fq = __builtin_ldexpf(1.f, -sq);
-
-    // Q planes + the wave's fragments; centroid planes and norm parts
-    Sp8 qf[2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
-        qf[c] = split8<true>(x);
-        const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
-        st16(sQ + o, qf[c].h);
-        if (!kZ) st16(sQ + kPlaneE + o, qf[c].m);   // zero for bf16 storage, never read
-    }
-    {
+    // centroid planes and -||mu||^2/2 parts at scale 2^-sq
+    auto mu_planes = [&](float fq) {
         float x[8], n2 = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -199,7 +172,62 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
             v0 = mrow < Kc ? ((h & 0xffffu) | ((m & 0xffffu) << 16)) : (uint32_t)kNegInfH;
         }
         *reinterpret_cast<u32x2_t *>(sMuX + mrow * kKMuXCols + c0) = u32x2_t{v0, v1};
+    };
+    int sq = 0;
+    float fq = 1.f;
+    if constexpr (FIXED) {
+        __syncthreads();
+        uint32_t m = qmax[s * (long)npart + part];
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) m = max(m, sMax[8 + ww]);
+        sq = scale_shift(m, kQLimit);
+        fq = __builtin_ldexpf(1.f, -sq);
+        mu_planes(fq);   // published by the first block's planes barrier
     }
+    uint32_t runq = 0;   // the run's largest |q| so far (INIT with qmax)
+
+    // the run's cluster sums: tile u = w + 8 j (dimension tile u % 4, cluster
+    // group u / 4), four dims per lane, and the tile's cluster sizes
+    float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float accn[2] = {0.f, 0.f};
+
+    for (int blk = b0; blk < b1; ++blk) {
+    const int i0 = 128 * blk;
+    const int Lb = min(128, L - i0);               // tokens of the block
+    if constexpr (!FIXED) {
+        const float mq = absmax8(qraw[1], absmax8(qraw[0], 0.f));
+        const uint32_t b = wave_max_u(__float_as_uint(mq));
+        if (lane == 0) sMax[w] = b;
+    }
+    // one-hot matrix cleared (16 KB: 32 bytes per thread)
+    reinterpret_cast<u32x4_t *>(sOH)[2 * tid] = u32x4_t{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4_t *>(sOH)[2 * tid + 1] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (!FIXED) {
+        __syncthreads();
+        uint32_t mq = 0, m = 0;
+#pragma unroll
+        for (int ww = 0; ww < 8; ++ww) {
+            mq = max(mq, sMax[ww]);
+            m = max(m, sMax[8 + ww]);
+        }
+        runq = max(runq, mq);
+        sq = scale_shift(max(m, mq), kQLimit);
+        fq = __builtin_ldexpf(1.f, -sq);
+    }
+
+    // Q planes + the wave's fragments; centroid planes and norm parts
+    Sp8 qf[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = qraw[c][i] * fq;
+        qf[c] = split8<true>(x);
+        const int o = (2048 * w + (lo.rl64 ^ (64 * c))) / 2;   // row tok, cols 32c + 8g
+        st16(sQ + o, qf[c].h);
+        if (!kZ) st16(sQ + kPlaneE + o, qf[c].m);   // zero for bf16 storage, never read
+    }
+    if constexpr (!FIXED) mu_planes(fq);
     __syncthreads();
     // the next block's Q rows, in flight while this block is scored
     if (blk + 1 < b1) {
@@ -302,6 +330,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     }
     if (blk + 1 < b1) __syncthreads();   // the planes and the one-hot matrix are rewritten
     }   // blocks of the run
+    if (INIT && RUN && qmax != nullptr && tid == 0) qmax[s * (long)npart + part] = runq;
     if (SCORES || part_sum == nullptr) return;
 
     // the run's sums and sizes
@@ -338,21 +367,23 @@ static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, in
                                        int32_t *assign, float *part_sum, int32_t *part_cnt,
                                        hipStream_t st, int init_step, float *mu_init,
                                        const float *prev_sum, const int32_t *prev_cnt,
-                                       int nsub) {
+                                       int nsub, uint32_t *qmax) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * kmeans_mfma_parts(L, nsub))), block(kThreads);
     const T *q = static_cast<const T *>(Q);
     float *const no_scores = nullptr;
+    uint32_t *const qm = nsub > 1 ? qmax : nullptr;
     auto launch = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, block, 0, st, q, mu, L, Kc, nblk, nsub, assign, part_sum,
-                           part_cnt, init_step, mu_init, prev_sum, prev_cnt, no_scores);
+                           part_cnt, init_step, mu_init, prev_sum, prev_cnt, no_scores, qm);
     };
     if (mu == nullptr) {
-        if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true>);
-        else launch(kmeans_mfma_kernel<T, true, false, false>);
+        if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true, false>);
+        else launch(kmeans_mfma_kernel<T, true, false, false, false>);
     } else {
-        if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true>);
-        else launch(kmeans_mfma_kernel<T, false, false, false>);
+        if (nsub > 1 && qm && !prev_sum) launch(kmeans_mfma_kernel<T, false, false, true, true>);
+        else if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true, false>);
+        else launch(kmeans_mfma_kernel<T, false, false, false, false>);
     }
     return hipGetLastError();
 }
@@ -362,10 +393,11 @@ static hipError_t kmeans_scores_dispatch(const void *Q, const float *mu, int S, 
                                          float *scores, hipStream_t st) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
-    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false>), grid, block, 0, st,
+    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false, false>), grid, block, 0, st,
                        static_cast<const T *>(Q), mu, L, Kc, nblk, 1, (int32_t *)nullptr,
                        (float *)nullptr, (int32_t *)nullptr, 0, (float *)nullptr,
-                       (const float *)nullptr, (const int32_t *)nullptr, scores);
+                       (const float *)nullptr, (const int32_t *)nullptr, scores,
+                       (uint32_t *)nullptr);
     return hipGetLastError();
 }
 
@@ -378,13 +410,14 @@ hipError_t launch_kmeans_scores(const void *Q, const float *mu, int S, int L, in
 hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int Kc,
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
                               hipStream_t st, int init_step, float *mu_init,
-                              const float *prev_sum, const int32_t *prev_cnt, int nsub) {
+                              const float *prev_sum, const int32_t *prev_cnt, int nsub,
+                              uint32_t *qmax) {
     if (nsub < 1) return hipErrorInvalidValue;
     if (dt == CA_BF16)
         return kmeans_mfma_dispatch<bf16_t>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                            init_step, mu_init, prev_sum, prev_cnt, nsub);
+                                            init_step, mu_init, prev_sum, prev_cnt, nsub, qmax);
     return kmeans_mfma_dispatch<float>(Q, mu, S, L, Kc, assign, part_sum, part_cnt, st,
-                                       init_step, mu_init, prev_sum, prev_cnt, nsub);
+                                       init_step, mu_init, prev_sum, prev_cnt, nsub, qmax);
 }
 
 }  // namespace ca

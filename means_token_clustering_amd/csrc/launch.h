@@ -50,6 +50,9 @@ hipError_t launch_centroid_reduce(const float *part_sum, const int32_t *part_cnt
 // only. With prev_sum / prev_cnt (the previous step's partials, same nsub)
 // the centroids are formed from them in run order instead of being read
 // from mu. kmeans_mfma_run picks nsub for S slices on cus compute units.
+// qmax (nsub > 1, nullable; [S, runs] words): the first step (mu == nullptr)
+// writes each run's largest |q|, and a later step given it scales the whole
+// run at once.
 bool kmeans_mfma_supported(int Kc);
 int kmeans_mfma_blocks(int L);
 int kmeans_mfma_run(long S, int L, int cus);
@@ -58,7 +61,7 @@ hipError_t launch_kmeans_mfma(const void *Q, const float *mu, int S, int L, int 
                               ca_dtype_t dt, int32_t *assign, float *part_sum, int32_t *part_cnt,
                               hipStream_t st, int init_step = 0, float *mu_init = nullptr,
                               const float *prev_sum = nullptr, const int32_t *prev_cnt = nullptr,
-                              int nsub = 1);
+                              int nsub = 1, uint32_t *qmax = nullptr);
 
 // Scores mu_k . q_i - ||mu_k||^2 / 2 of the matrix-core step (Kc <= 64) in
 // unscaled units, [S, L, Kc]: the distances the step compares.
