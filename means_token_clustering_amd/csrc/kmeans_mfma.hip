@@ -182,9 +182,15 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         for (int ww = 0; ww < 8; ++ww) m = max(m, sMax[8 + ww]);
         sq = scale_shift(m, kQLimit);
         fq = __builtin_ldexpf(1.f, -sq);
-        mu_planes(fq);   // published by the first block's planes barrier
+        mu_planes(fq);
+        // one-hot matrix cleared once: afterwards each token's lane resets
+        // the one entry it set (its own column) before setting the next
+        reinterpret_cast<u32x4_t *>(sOH)[2 * tid] = u32x4_t{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4_t *>(sOH)[2 * tid + 1] = u32x4_t{0u, 0u, 0u, 0u};
+        __syncthreads();
     }
     uint32_t runq = 0;   // the run's largest |q| so far (INIT with qmax)
+    int set_k = -1;      // FIXED: the cluster of this lane's one-hot entry (-1: none)
 
     // the run's cluster sums: tile u = w + 8 j (dimension tile u % 4, cluster
     // group u / 4), four dims per lane, and the tile's cluster sizes
@@ -199,10 +205,15 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         const uint32_t b = wave_max_u(__float_as_uint(mq));
         if (lane == 0) sMax[w] = b;
     }
-    // one-hot matrix cleared (16 KB: 32 bytes per thread)
-    reinterpret_cast<u32x4_t *>(sOH)[2 * tid] = u32x4_t{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4_t *>(sOH)[2 * tid + 1] = u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (!FIXED) {
+    if constexpr (FIXED) {
+        // the previous block's entry of this lane's column (every wave has
+        // read the matrix: the last barrier followed the sums)
+        if (set_k >= 0) sOH[off128(set_k, tok)] = 0;
+        set_k = -1;
+    } else {
+        // one-hot matrix cleared (16 KB: 32 bytes per thread)
+        reinterpret_cast<u32x4_t *>(sOH)[2 * tid] = u32x4_t{0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4_t *>(sOH)[2 * tid + 1] = u32x4_t{0u, 0u, 0u, 0u};
         __syncthreads();
         uint32_t mq = 0, m = 0;
 #pragma unroll
@@ -227,8 +238,13 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         st16(sQ + o, qf[c].h);
         if (!kZ) st16(sQ + kPlaneE + o, qf[c].m);   // zero for bf16 storage, never read
     }
-    if constexpr (!FIXED) mu_planes(fq);
-    __syncthreads();
+    // FIXED: the centroid planes are already published and the assignment
+    // reads only registers and them, so the Q planes go out with the one-hot
+    // matrix at the next barrier
+    if constexpr (!FIXED) {
+        mu_planes(fq);
+        __syncthreads();
+    }
     // the next block's Q rows, in flight while this block is scored
     if (blk + 1 < b1) {
         const int Ln = min(128, L - i0 - 128);
@@ -289,6 +305,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
         if (!SCORES && g == 0 && tok_in) {
             assign[s * L + i0 + tok] = rk;
             sOH[off128(rk, tok)] = 0x3c00;   // fp16 1.0
+            if (FIXED) set_k = rk;
         }
     }
     if (!SCORES && part_sum != nullptr) {
