@@ -16,15 +16,17 @@
 // sums in fp32 registers (block sums added in block order), so a run of nsub
 // blocks writes one partial instead of nsub. The centroids sit in
 // LDS as fp16 h/m planes of up to 64 rows with their -||mu||^2/2 parts; each
-// group of 16 clusters costs one chain of seven products per wave, and the
-// running best over the groups keeps the earlier group on equal scores. The
+// group of 16 clusters costs one chain of seven products per wave (five for
+// bf16 storage), and the running best over the groups keeps the earlier
+// group on equal scores. The
 // block's cluster sums and sizes are one-hot products of the same planes
 // (Q^T times the [cluster][token] one-hot matrix, exact 0/1 weights), stored
 // per run; centroid_reduce_kernel adds the runs in a fixed order, or, for
 // few blocks, the next step's workgroups add them themselves.
 // Q and the centroids are scaled by one power of two per block (the largest
-// |q| or |mu|), which leaves every comparison unchanged; the sums are scaled
-// back exactly.
+// |q| or |mu|), or, in the steps after the first of a run launch, per run
+// (the run's largest |q| recorded by the first step), which leaves every
+// comparison unchanged; the sums are scaled back exactly.
 #include "launch.h"
 #include "mfma_split.h"
 
