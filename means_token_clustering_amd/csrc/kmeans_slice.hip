@@ -70,6 +70,18 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
 #pragma unroll
         for (int c = 0; c < 2; ++c)
             load_row8<T, false>(Qs, 16 * (w + 16 * u) + l16, L, 32 * c + 8 * g, qraw[u][c]);
+    // the initial centroids' rows mu_k = Q[init_row(k)] (threads tid < 128:
+    // row tid / 8, dims 8 (tid % 8) ..), requested with the Q rows
+    float m0[8];
+    {
+        const int r = tid >> 3, c8 = (tid & 7) * 8;
+        if (tid < 128 && r < Kc) {
+            load8<T>(Qs + (long)init_row(r, L, Kc, init_step) * kD + c8, m0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m0[i] = 0.f;
+        }
+    }
     {
         float m = 0.f;
 #pragma unroll
@@ -103,15 +115,9 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
     if (tid < 128) {
         const int r = tid >> 3, c8 = (tid & 7) * 8;
         float x[8], n2 = 0.f;
-        if (r < Kc) {
-            load8<T>(Qs + (long)init_row(r, L, Kc, init_step) * kD + c8, x);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.f;
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            x[i] *= fq;
+            x[i] = m0[i] * fq;
             n2 = fmaf(x[i], x[i], n2);
         }
         const Sp8 mp = split8(x);
