@@ -26,7 +26,10 @@
 //     in 544 rows of operands per k instead of the 960 of three 128 x 192
 //     tiles (operand delivery into a CU runs at 64 B per clock).
 //   2 x 2 waves, 128 x 192 tiles, 2 stages, three workgroups per CU (other
-//     shapes, e.g. the output projection [8192 x 768] x [768 x 768]).
+//     shapes); with at most one tile per CU (the output projection
+//     [8192 x 768] x [768 x 768]) two k groups of 2 x 2 waves, each taking
+//     every other 32-deep k step, their sums added in LDS at the end: 17.4
+//     against 18.6 us with one group (three groups 17.8, three stages 19.3).
 // Measured on [8192 x 768] x [768 x 2304] (same box, A rotating past the
 // caches): 34.9 us for the 256 x 288 tiles, 35.9 us for 128 x 192 tiles with
 // three workgroups per CU, 38-46 us with 2 workgroups per CU or 128 x 288
@@ -75,20 +78,29 @@ struct GemmArgs {
     int tiles_m, tiles_n;   // tiles_n over all count * N columns
 };
 
-// Shape of one launch: WM x WN waves, S stages.
-template <int WM, int WN, int S>
+// Shape of one launch: WM x WN waves per k group, KS k groups, S stages. With
+// KS > 1 a stage holds KS consecutive 32-deep k tiles and wave group g
+// multiplies tile g of each stage; the groups' sums meet in LDS at the end,
+// folded from the last group down (group 0 ends with g0 + (g1 + (g2 ..))).
+template <int WM, int WN, int S, int KS>
 struct Cfg {
-    static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+    static constexpr int kWavesT = WM * WN;                  // waves per k group
+    static constexpr int kWaves = kWavesT * KS, kThreads = 64 * kWaves;
     static constexpr int kTM = kWaveM * WM, kTN = kWaveN * WN;
     static constexpr int kATile = kTM * kBK, kBTile = kTN * kBK;   // elements
-    static constexpr int kStage = kATile + kBTile;
-    static constexpr int kAInst = kATile * 2 / 1024;   // 1 KB direct loads per stage
-    static constexpr int kInst = kStage * 2 / 1024;
+    static constexpr int kTile1 = kATile + kBTile;           // one k tile
+    static constexpr int kStage = KS * kTile1;
+    static constexpr int kAInst = kATile * 2 / 1024;   // 1 KB direct loads per k tile
+    static constexpr int kInst1 = kTile1 * 2 / 1024;
+    static constexpr int kInst = KS * kInst1;
     static constexpr int kMaxPerWave = (kInst + kWaves - 1) / kWaves;
     static constexpr int kCpr = kTN / 8;                // 16-byte chunks of a W tile row
-    static constexpr int kLdsElems = S * kStage > kWaves * 64 * kWRow / 2 ? S * kStage
-                                                                          : kWaves * 64 * kWRow / 2;
-    static_assert(kATile * 2 % 1024 == 0 && kStage * 2 % 1024 == 0, "whole 1 KB loads");
+    static constexpr int kStgElems = kWavesT * 64 * kWRow / 2;
+    static constexpr int kRedElems = KS > 1 ? kWavesT * 64 * 96 * 2 : 0;   // fp32 sums of a group
+    static constexpr int kLdsElems =
+        S * kStage > kStgElems ? (S * kStage > kRedElems ? S * kStage : kRedElems)
+                               : (kStgElems > kRedElems ? kStgElems : kRedElems);
+    static_assert(kATile * 2 % 1024 == 0 && kTile1 * 2 % 1024 == 0, "whole 1 KB loads");
     static_assert(kLdsElems * 2 <= 160 * 1024, "LDS");
     static_assert((S - 2) * kMaxPerWave <= 12, "wait counts");
 };
@@ -146,12 +158,12 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
 // waves per SIMD the register budget has to allow
-template <int WM, int WN, int S>
-constexpr int occupancy() { return WM * WN >= 12 ? 3 : (S == 2 ? 3 : 2); }
+template <int WM, int WN, int S, int KS>
+constexpr int occupancy() { return KS > 1 ? 2 : (WM * WN >= 12 ? 3 : (S == 2 ? 3 : 2)); }
 
-template <int WM, int WN, int S, bool AHEADS, bool CHEADS, bool KN>
-__global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm_bf16_kernel(GemmArgs p) {
-    using G = Cfg<WM, WN, S>;
+template <int WM, int WN, int S, int KS, bool AHEADS, bool CHEADS, bool KN>
+__global__ __launch_bounds__((64 * WM * WN * KS), (occupancy<WM, WN, S, KS>())) void gemm_bf16_kernel(GemmArgs p) {
+    using G = Cfg<WM, WN, S, KS>;
     __shared__ __align__(16) uint16_t smem[G::kLdsElems];
     // tile numbering: consecutive numbers share the A rows; workgroup ids
     // that differ by a multiple of 8 (one XCD) get consecutive numbers
@@ -162,7 +174,8 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
     const int m0 = mt * G::kTM, n0 = nt * G::kTN;   // n0 over all count * N columns
     const int ncols = p.count * p.N;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const int wm = w / WN, wn = w - wm * WN;
+    const int ks = w / G::kWavesT, wt = w - ks * G::kWavesT;   // k group, wave in the group
+    const int wm = wt / WN, wn = wt - wm * WN;
     const int wu = __builtin_amdgcn_readfirstlane(w);
 
     // Direct loads of one stage: load i (1 KB: the A rows, then the weight
@@ -173,6 +186,7 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
     const uint16_t *src[G::kMaxPerWave];
     long step[G::kMaxPerWave];   // source advance per k step (weight loads)
     bool is_a[G::kMaxPerWave];
+    int kj[G::kMaxPerWave];      // k tile of the stage the load fills
     int nl = 0;                  // loads of this wave per stage (wave-uniform)
 #pragma unroll
     for (int t = 0; t < G::kMaxPerWave; ++t) {
@@ -180,10 +194,13 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
         src[t] = p.A;
         step[t] = 0;
         is_a[t] = false;
+        kj[t] = 0;
         if (i >= G::kInst) continue;
         ++nl;
-        if (i < G::kAInst) {
-            const int pos = i * 64 + lane;   // 16-byte chunk of the A tile
+        kj[t] = i / G::kInst1;
+        const int i1 = i - kj[t] * G::kInst1;   // load within the k tile
+        if (i1 < G::kAInst) {
+            const int pos = i1 * 64 + lane;   // 16-byte chunk of the A tile
             const int row = pos >> 2, lc = (pos & 3) ^ ((row >> 1) & 3);
             const int m = min(m0 + row, p.M - 1);
             if (AHEADS) {
@@ -194,7 +211,7 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
             }
             is_a[t] = true;
         } else {
-            const int pos = (i - G::kAInst) * 64 + lane;   // chunk of the weight tile
+            const int pos = (i1 - G::kAInst) * 64 + lane;   // chunk of the weight tile
             if (KN) {   // [32 k][kCpr chunks of n]
                 const int row = pos / G::kCpr, pc = pos - row * G::kCpr;
                 const int lc = pc ^ (wx<WN>(row) >> 1);
@@ -210,17 +227,19 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
             }
         }
     }
-    const int nk = p.K / kBK;
+    const int nk = p.K / kBK / KS;   // stages of KS k tiles
     const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)smem;
     auto issue = [&](int kt) {
         const uint32_t s = lds0 + 2 * G::kStage * (kt % S);   // byte address of the stage
-        // A advance: 32 columns per step; in head layout 2 steps per head
-        const long aoff = AHEADS ? (long)(kt >> 1) * p.L * kD + 32 * (kt & 1) : (long)kt * kBK;
 #pragma unroll
         for (int t = 0; t < G::kMaxPerWave; ++t) {
             const int i = wu + G::kWaves * t;
+            const int kk = KS * kt + kj[t];   // 32-deep k step of this load
+            // A advance: 32 columns per step; in head layout 2 steps per head
+            const long aoff =
+                AHEADS ? (long)(kk >> 1) * p.L * kD + 32 * (kk & 1) : (long)kk * kBK;
             if (i < G::kInst)
-                load_lds16(src[t] + (is_a[t] ? aoff : (long)kt * step[t]), s + 1024 * i);
+                load_lds16(src[t] + (is_a[t] ? aoff : (long)kk * step[t]), s + 1024 * i);
         }
     };
 
@@ -275,15 +294,38 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
         wait_vm(later * nl);
         bar();
         if (kt + S - 1 < nk) issue(kt + S - 1);
-        products(smem + G::kStage * (kt % S));
+        products(smem + G::kStage * (kt % S) + G::kTile1 * ks);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this tile's LDS reads are done
     }
     bar();   // every wave is done reading the stages
+    if constexpr (KS > 1) {
+        // from the last k group down: group k2 leaves its sums in LDS, group
+        // k2 - 1 adds them; group 0 then writes the block
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(smem);
+#pragma unroll
+        for (int k2 = KS - 1; k2 > 0; --k2) {
+            if (ks == k2) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 6; ++j) red[(wt * 24 + 6 * i + j) * 64 + lane] = acc[i][j];
+            }
+            __syncthreads();
+            if (ks == k2 - 1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 6; ++j) acc[i][j] += red[(wt * 24 + 6 * i + j) * 64 + lane];
+            }
+            __syncthreads();   // the next fold or the staging reuses the region
+        }
+        if (ks > 0) return;
+    }
 
     // acc[i][j][r] = C[m0 + 64 wm + 16 i + l16][n0 + 96 wn + 16 j + 4 g + r]:
     // wave w stages its 64 x 96 block as bf16 rows, then writes 16-byte
     // chunks of whole row segments
-    unsigned char *cs = reinterpret_cast<unsigned char *>(smem) + 64 * kWRow * w;
+    unsigned char *cs = reinterpret_cast<unsigned char *>(smem) + 64 * kWRow * wt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * i + l16;
@@ -317,18 +359,20 @@ __global__ __launch_bounds__((64 * WM * WN), (occupancy<WM, WN, S>())) void gemm
     }
 }
 
-template <int WM, int WN, int S, bool AHEADS, bool CHEADS, bool KN>
+template <int WM, int WN, int S, bool AHEADS, bool CHEADS, bool KN, int KS = 1>
 hipError_t launch_cfg(const GemmArgs &a0, hipStream_t st) {
-    using G = Cfg<WM, WN, S>;
+    using G = Cfg<WM, WN, S, KS>;
     GemmArgs a = a0;
     a.tiles_m = (a.M + G::kTM - 1) / G::kTM;
     a.tiles_n = (a.count * a.N + G::kTN - 1) / G::kTN;
     const long T = (long)a.tiles_m * a.tiles_n;
     if (T >= (1L << 31)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, S, AHEADS, CHEADS, KN>), dim3((unsigned)T),
+    hipLaunchKernelGGL((gemm_bf16_kernel<WM, WN, S, KS, AHEADS, CHEADS, KN>), dim3((unsigned)T),
                        dim3(G::kThreads), 0, st, a);
     return hipGetLastError();
 }
+
+constexpr int kSmallKS = 2, kSmallS = 2;   // k groups and stages of the one-tile-per-CU 128 x 192 shape
 
 }  // namespace
 
@@ -360,6 +404,15 @@ hipError_t launch_gemm_bf16(const uint16_t *A, const uint16_t *const *B, uint16_
         if (a_heads) return launch_cfg<4, 3, 3, true, false, true>(a, st);
         if (c_heads) return launch_cfg<4, 3, 3, false, true, true>(a, st);
         return launch_cfg<4, 3, 3, false, false, true>(a, st);
+    }
+    // 128 x 192 tiles; at most one per CU (and an even number of k steps):
+    // two k groups of four waves
+    const long small = (long)((M + 127) / 128) * ((total_n + 191) / 192);
+    if (small <= cus && (K / kBK) % kSmallKS == 0) {
+        if (!w_kn) return launch_cfg<2, 2, kSmallS, false, false, false, kSmallKS>(a, st);
+        if (a_heads) return launch_cfg<2, 2, kSmallS, true, false, true, kSmallKS>(a, st);
+        if (c_heads) return launch_cfg<2, 2, kSmallS, false, true, true, kSmallKS>(a, st);
+        return launch_cfg<2, 2, kSmallS, false, false, true, kSmallKS>(a, st);
     }
     if (!w_kn) return launch_cfg<2, 2, 2, false, false, false>(a, st);
     if (a_heads) return launch_cfg<2, 2, 2, true, false, true>(a, st);
