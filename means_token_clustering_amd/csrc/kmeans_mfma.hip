@@ -27,6 +27,8 @@
 // |q| or |mu|), or, in the steps after the first of a run launch, per run
 // (the run's largest |q| recorded by the first step), which leaves every
 // comparison unchanged; the sums are scaled back exactly.
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma_split.h"
 
@@ -55,7 +57,12 @@ static_assert(kKLds <= 81920, "two workgroups per CU");
 // scale for the whole run (with the centroids' maximum), the centroid planes
 // built once, no per-block maximum. Each block's own scale gives the same
 // products (power-of-two scaling is exact), so only fp16 subnormals differ.
-template <typename T, bool INIT, bool SCORES, bool RUN, bool FIXED>
+// K64: all four groups of 16 clusters are present (Kc > 48). The groups'
+// score chains are then independent products and one (score, index) maximum
+// runs over the lane's 16 clusters before the column, and the two sum tiles
+// of a wave (same dimension tile, cluster groups kg and kg + 2) share their Q
+// fragments; every result is the one of the group-by-group form.
+template <typename T, bool INIT, bool SCORES, bool RUN, bool FIXED, bool K64>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk, int nsub,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
@@ -63,6 +70,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const int32_t *__restrict__ prev_cnt, float *__restrict__ scores,
     uint32_t *__restrict__ qmax) {
     static_assert(!FIXED || (RUN && !INIT && !SCORES), "a fixed run scale is for later steps");
+    static_assert(!K64 || !SCORES, "the score dump takes the group-by-group form");
     __shared__ __align__(16) unsigned char smem[kKLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kKOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kKOffMu);
@@ -95,7 +103,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const int b1 = RUN ? min(nblk, b0 + nsub) : b0 + 1;
     const T *Qs = Q + s * (long)L * kD;
     const int tok = 16 * w + l16;                  // the lane's token in a block
-    const int NG = (Kc + 15) >> 4;                 // groups of 16 clusters
+    const int NG = K64 ? 4 : (Kc + 15) >> 4;       // groups of 16 clusters
     const LaneOffs lo = lane_offsets(l16, g);
 
     // the wave's Q rows of the first block (dims 32c + 8g ..), zeros past it
@@ -262,7 +270,45 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
             g == 0 ? u32x4_t{kOneH2, kOneH2, kOneH2, kOneH2} : u32x4_t{0u, 0u, 0u, 0u};
         float run = -__builtin_inff();
         int rk = 0;
-        for (int kg = 0; kg < NG; ++kg) {
+        if constexpr (K64) {
+            // four independent chains, then the lane's best of its clusters
+            // 16 kg + 4 g + rr in index order (strictly larger replaces)
+            f32x4_t a[4];
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg) {
+                const u32x4_t mx = ldb16(pMuX, 64 * (16 * kg + l16) + 16 * g);
+                const Sp8 mu0 = frag_at(pMu, kKMuPlane, 2048 * kg + lo.rl64);
+                const Sp8 mu1 = frag_at(pMu, kKMuPlane, 2048 * kg + (lo.rl64 ^ 64));
+                a[kg] = mma(mx, ones_g0, kZero4);
+                a[kg] = mma3z<false, kZ>(mu0, qf[0], a[kg]);
+                a[kg] = mma3z<false, kZ>(mu1, qf[1], a[kg]);
+            }
+            float best = a[0][0];
+            int bk = 4 * g;
+#pragma unroll
+            for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+                for (int rr = kg == 0 ? 1 : 0; rr < 4; ++rr) {
+                    const bool up = a[kg][rr] > best;
+                    best = up ? a[kg][rr] : best;
+                    bk = up ? 16 * kg + 4 * g + rr : bk;
+                }
+            // over the column's four lane groups: the larger score, the lower
+            // index on equal scores
+            uint32_t x0, x1, i0a, i1a;
+            pair16(__float_as_uint(best), x0, x1);
+            pair16((uint32_t)bk, i0a, i1a);
+            bool up = __uint_as_float(x1) > __uint_as_float(x0) ||
+                      (__uint_as_float(x1) == __uint_as_float(x0) && i1a < i0a);
+            best = up ? __uint_as_float(x1) : __uint_as_float(x0);
+            bk = up ? (int)i1a : (int)i0a;
+            pair32(__float_as_uint(best), x0, x1);
+            pair32((uint32_t)bk, i0a, i1a);
+            up = __uint_as_float(x1) > __uint_as_float(x0) ||
+                 (__uint_as_float(x1) == __uint_as_float(x0) && i1a < i0a);
+            rk = up ? (int)i1a : (int)i0a;
+        }
+        for (int kg = 0; !K64 && kg < NG; ++kg) {
             const u32x4_t mx = ldb16(pMuX, 64 * (16 * kg + l16) + 16 * g);
             const Sp8 mu0 = frag_at(pMu, kKMuPlane, 2048 * kg + lo.rl64);
             const Sp8 mu1 = frag_at(pMu, kKMuPlane, 2048 * kg + (lo.rl64 ^ 64));
@@ -318,8 +364,44 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     // dims 16 dt + 4g + rr for cluster 16 kg + l16, and its size
     const float back = __builtin_ldexpf(1.f, sq);
     const u32x4_t ones = {kOneH2, kOneH2, kOneH2, kOneH2};
+    if constexpr (K64) {
+        // tiles u = w and w + 8 together: dimension tile w % 4, cluster
+        // groups w / 4 and w / 4 + 2, one Q fragment per chunk for both
+        const int dt = w & 3, kg = w >> 2;
+        const int trq0 = 1024 * g + (lo.tr0 ^ (32 * dt)), trq1 = 1024 * g + (lo.tr4 ^ (32 * dt));
+        f32x4_t sh0 = kZero4, sm0 = kZero4, cn0 = kZero4, sh1 = kZero4, sm1 = kZero4, cn1 = kZero4;
+        auto chunk2 = [&](int c) {
+            const Sp8 qt = colfrag8_at(pQ, 4096 * c + trq0, 4096 * c + trq1);
+            const u32x4_t oh0 = ldb16(pOH, 4096 * kg + (lo.rl128 ^ (64 * c)));
+            const u32x4_t oh1 = ldb16(pOH, 4096 * (kg + 2) + (lo.rl128 ^ (64 * c)));
+            if (!kZ) {
+                sm0 = mma(qt.m, oh0, sm0);
+                sm1 = mma(qt.m, oh1, sm1);
+            }
+            sh0 = mma(qt.h, oh0, sh0);
+            sh1 = mma(qt.h, oh1, sh1);
+            if (dt == 0) {
+                cn0 = mma(ones, oh0, cn0);
+                cn1 = mma(ones, oh1, cn1);
+            }
+        };
+        if constexpr (RUN) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+            for (int c = 0; c < 4; ++c) chunk2(c);
+        } else {
+            const int nch = (Lb + 31) >> 5;
+            for (int c = 0; c < nch; ++c) chunk2(c);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            acc[0][rr] += (sm0[rr] + sh0[rr]) * back;
+            acc[1][rr] += (sm1[rr] + sh1[rr]) * back;
+        }
+        accn[0] += cn0[0];
+        accn[1] += cn1[0];
+    }
+#pragma unroll
+    for (int j = 0; !K64 && j < 2; ++j) {
         const int u = w + 8 * j;
         if (u >= 4 * NG) break;
         const int dt = u & 3, kg = u >> 2;
@@ -396,14 +478,19 @@ static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, in
         hipLaunchKernelGGL(kern, grid, block, 0, st, q, mu, L, Kc, nblk, nsub, assign, part_sum,
                            part_cnt, init_step, mu_init, prev_sum, prev_cnt, no_scores, qm);
     };
-    if (mu == nullptr) {
-        if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true, false>);
-        else launch(kmeans_mfma_kernel<T, true, false, false, false>);
-    } else {
-        if (nsub > 1 && qm && !prev_sum) launch(kmeans_mfma_kernel<T, false, false, true, true>);
-        else if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true, false>);
-        else launch(kmeans_mfma_kernel<T, false, false, false, false>);
-    }
+    auto pick = [&](auto k64) {
+        constexpr bool K = decltype(k64)::value;
+        if (mu == nullptr) {
+            if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true, false, K>);
+            else launch(kmeans_mfma_kernel<T, true, false, false, false, K>);
+        } else {
+            if (nsub > 1 && qm && !prev_sum) launch(kmeans_mfma_kernel<T, false, false, true, true, K>);
+            else if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true, false, K>);
+            else launch(kmeans_mfma_kernel<T, false, false, false, false, K>);
+        }
+    };
+    if (Kc > 48) pick(std::true_type{});
+    else pick(std::false_type{});
     return hipGetLastError();
 }
 
@@ -412,7 +499,7 @@ static hipError_t kmeans_scores_dispatch(const void *Q, const float *mu, int S, 
                                          float *scores, hipStream_t st) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
-    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false, false>), grid, block, 0, st,
+    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false, false, false>), grid, block, 0, st,
                        static_cast<const T *>(Q), mu, L, Kc, nblk, 1, (int32_t *)nullptr,
                        (float *)nullptr, (int32_t *)nullptr, 0, (float *)nullptr,
                        (const float *)nullptr, (const int32_t *)nullptr, scores,

@@ -187,6 +187,8 @@ def test_segmented_long_workload():
 LLOYD_RUNS = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 8, 8498, 64, 2, 32, 0.5, "f32", 64),       # 67 blocks: a last run of one 50-token block
     (1, 6, 11000, 48, 3, 24, 0.5, "bf16", 48),     # 86 blocks: a last run of two, ragged
+    (1, 6, 11000, 56, 3, 24, 0.5, "bf16", 56),     # four cluster groups, the last one half empty
+    (1, 2, 1300, 50, 3, 32, 0.5, "f32", 50),       # four groups, single blocks with the reduce
 ]
 
 
