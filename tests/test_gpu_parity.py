@@ -107,6 +107,8 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 2, 257, 48, 3, 32, 0.5, "f32", 12),        # one-token last block, three full groups
     (2, 2, 129, 17, 2, 32, 0.5, "f32", 9),         # 17 clusters: a one-row last group
     (1, 1, 640, 64, 2, 24, 0.5, "bf16", 20),       # most clusters of the matrix-core step
+    (1, 2, 120, 64, 2, 32, 0.5, "f32", 20),        # all four groups, one key range
+    (2, 3, 300, 60, 3, 20, 0.5, "bf16", 24),       # 60 clusters, three ragged key ranges
     (1, 2, 200, 65, 2, 32, 0.5, "f32", 20),        # first count above it (scalar step)
     (2, 2, 512, 16, 3, 33, 0.5, "f32", 16),        # longest single-launch slice, radius 16
     (1, 3, 385, 9, 2, 12, 0.7, "bf16", 9),         # three key chunks and a one-token fourth
@@ -289,6 +291,20 @@ def test_step_xattn_local_fuse(L):
                            torch.float32)
     want = oracle.fuse(vc.astype(np.float64), c, ol.cpu().numpy().astype(np.float64), 0.25)
     assert np.abs(_host(out) - want).max() <= 1e-6
+
+
+# the centroid attention with all four 16-centroid groups in one pass (49 to
+# 64 centroids): one key range, several, and a ragged last range
+@pytest.mark.parametrize("L,K", [(128, 64), (1100, 56), (300, 49)])
+def test_step_xattn_all_groups(L, K):
+    x = gen.make_inputs(1, 3, L, 64, nclust=K, seed=52 + L, blobs=8)
+    b = _b()
+    k, v = (_dev(getattr(x, n), x.dtype) for n in ("k", "v"))
+    Qd, Kd, Vd = x.values("q"), x.values("k"), x.values("v")
+    mu = oracle.init_centroids(Qd, K).astype(np.float32)
+    vc = b.ca_centroid_xattn(torch.from_numpy(mu).cuda(), k, v).cpu().numpy()
+    vc_o, _ = oracle.centroid_xattn(mu.astype(np.float64), Kd, Vd)
+    assert np.abs(vc - vc_o).max() <= 1e-5
 
 
 @pytest.mark.parametrize("path", PATHS)
