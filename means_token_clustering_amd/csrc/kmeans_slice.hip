@@ -41,8 +41,8 @@ static_assert(kSLds <= 163840, "one workgroup per CU");
 }  // namespace
 
 // HIST: hist receives c^(t) of every iteration t at hist[(t - 1) * S + s][L]
-// (S slices in all).
-template <typename T, bool HIST>
+// (S slices in all). FULL: L is 512 (no bounds tests).
+template <typename T, bool HIST, bool FULL>
 __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L, int Kc,
                                                   int iters, int init_step,
                                                   int32_t *__restrict__ assign,
@@ -69,7 +69,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            load_row8<T, false>(Qs, 16 * (w + 16 * u) + l16, L, 32 * c + 8 * g, qraw[u][c]);
+            load_row8<T, FULL>(Qs, 16 * (w + 16 * u) + l16, L, 32 * c + 8 * g, qraw[u][c]);
     // the initial centroids' rows mu_k = Q[init_row(k)] (threads tid < 128:
     // row tid / 8, dims 8 (tid % 8) ..), requested with the Q rows
     float m0[8];
@@ -149,7 +149,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int tile = w + 16 * u;
-                if (tile < NT) {
+                if (FULL || tile < NT) {
                     f32x4_t a = mma(mx, ones_g0, kZero4);
                     a = mma3z<false, kZ>(mu0, qf[u][0], a);
                     a = mma3z<false, kZ>(mu1, qf[u][1], a);
@@ -163,7 +163,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                     }
                     bk = col_argmax(best, bk);
                     const int tok = 16 * tile + l16;
-                    if (g == 0 && tok < L) {
+                    if (g == 0 && (FULL || tok < L)) {
                         sC[tok] = bk;
                         if (t == iters) assign[s * L + tok] = bk;
                         if (HIST) hist[((long)(t - 1) * S + s) * L + tok] = bk;
@@ -178,7 +178,7 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int cc = 4 * qd + c;   // 32-token chunk
-            if (32 * cc < L) {
+            if (FULL || 32 * cc < L) {
                 // one-hot B fragment: tokens 32cc + 8g .. +7 for cluster l16
                 const int t0 = 32 * cc + 8 * g;
                 const int4 ca = *reinterpret_cast<const int4 *>(sC + t0);
@@ -187,8 +187,9 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                 uint32_t pk[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t lo16 = (t0 + 2 * e < L && cv[2 * e] == l16) ? 0x3c00u : 0u;
-                    const uint32_t hi16 = (t0 + 2 * e + 1 < L && cv[2 * e + 1] == l16) ? 0x3c00u : 0u;
+                    const uint32_t lo16 = ((FULL || t0 + 2 * e < L) && cv[2 * e] == l16) ? 0x3c00u : 0u;
+                    const uint32_t hi16 =
+                        ((FULL || t0 + 2 * e + 1 < L) && cv[2 * e + 1] == l16) ? 0x3c00u : 0u;
                     pk[e] = lo16 | (hi16 << 16);
                 }
                 const u32x4_t oh = {pk[0], pk[1], pk[2], pk[3]};
@@ -248,12 +249,12 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
     }
 }
 
-template <typename T, bool HIST>
+template <typename T, bool HIST, bool FULL>
 __global__ __launch_bounds__(kSThreads, 1) void kmeans_slice_kernel(
     const T *__restrict__ Q, int L, int Kc, int iters, int init_step,
     int32_t *__restrict__ assign, float *__restrict__ mu_out, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kSLds];
-    kmeans_slice_body<T, HIST>(Q, L, Kc, iters, init_step, assign, mu_out, blockIdx.x,
+    kmeans_slice_body<T, HIST, FULL>(Q, L, Kc, iters, init_step, assign, mu_out, blockIdx.x,
                                threadIdx.x, smem, hist, gridDim.x);
 }
 
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kSThreads, 1) void kmeans_window_kernel(
     float *__restrict__ oloc, int32_t *__restrict__ hist) {
     __shared__ __align__(16) unsigned char smem[kKWLds];
     if ((int)blockIdx.x < S) {
-        kmeans_slice_body<T, HIST>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
+        kmeans_slice_body<T, HIST, false>(Q, L, Kc, iters, init_step, assign_out, mu_out, blockIdx.x,
                                    threadIdx.x, smem, hist, S);
         return;
     }
@@ -321,14 +322,19 @@ hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, c
                                int32_t *assign, float *mu, int init_step, hipStream_t st,
                                int32_t *hist) {
     const dim3 grid((unsigned)S), block(kSThreads);
-#define CA_KS_LAUNCH(TT, HH)                                                                     \
-    hipLaunchKernelGGL((kmeans_slice_kernel<TT, HH>), grid, block, 0, st,                        \
+#define CA_KS_LAUNCH(TT, HH, F)                                                                  \
+    hipLaunchKernelGGL((kmeans_slice_kernel<TT, HH, F>), grid, block, 0, st,                     \
                        static_cast<const TT *>(Q), L, Kc, iters, init_step, assign, mu, hist)
+#define CA_KS_LAUNCH_F(TT, HH)                                                                   \
+    do {                                                                                         \
+        if (L == kSL) CA_KS_LAUNCH(TT, HH, true); else CA_KS_LAUNCH(TT, HH, false);              \
+    } while (0)
     if (dt == CA_BF16) {
-        if (hist) CA_KS_LAUNCH(bf16_t, true); else CA_KS_LAUNCH(bf16_t, false);
+        if (hist) CA_KS_LAUNCH_F(bf16_t, true); else CA_KS_LAUNCH_F(bf16_t, false);
     } else {
-        if (hist) CA_KS_LAUNCH(float, true); else CA_KS_LAUNCH(float, false);
+        if (hist) CA_KS_LAUNCH_F(float, true); else CA_KS_LAUNCH_F(float, false);
     }
+#undef CA_KS_LAUNCH_F
 #undef CA_KS_LAUNCH
     return hipGetLastError();
 }
