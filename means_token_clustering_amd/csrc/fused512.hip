@@ -58,7 +58,9 @@ static_assert(kGLds <= 163840, "one workgroup per CU");
 
 // HIST: hist receives the assignment of every Lloyd iteration, [iters, S, L]
 // (S = the grid size).
-template <typename T, bool HIST>
+// FULL: L is 512 (no bounds tests in the clustering and the centroid attention;
+// the window passes keep theirs, which the register budget needs).
+template <typename T, bool HIST, bool FULL>
 __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
     int iters, int rad, float alpha, int init_step, int H, int G, T *__restrict__ out,
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            load_row8<T, false>(Qs, 16 * (w + 16 * u) + l16, L, 32 * c + 8 * g, qraw[u][c]);
+            load_row8<T, FULL>(Qs, 16 * (w + 16 * u) + l16, L, 32 * c + 8 * g, qraw[u][c]);
     // the initial centroids' rows mu_k = Q[init_row(k)] (threads tid < 128:
     // row tid / 8, dims 8 (tid % 8) ..), requested with the Q rows
     float m0[8];
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
                     const int tile = w + 16 * u;
-                    if (tile < NT) {
+                    if (FULL || tile < NT) {
                         f32x4_t a = mma(mx, ones_g0, kZero4);
                         a = mma3z<false, kZ>(mu0, qf[u][0], a);
                         a = mma3z<false, kZ>(mu1, qf[u][1], a);
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                         }
                         bk = col_argmax(best, bk);
                         const int tok = 16 * tile + l16;
-                        if (g == 0 && tok < L) {
+                        if (g == 0 && (FULL || tok < L)) {
                             sC[tok] = bk;
                             if (t == iters && assign) assign[s * L + tok] = bk;
                             if (HIST) hist[((long)(t - 1) * gridDim.x + s) * L + tok] = bk;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int cc = 4 * qd + c;
-                if (32 * cc < L) {
+                if (FULL || 32 * cc < L) {
                     const int t0 = 32 * cc + 8 * g;
                     const int4 ca = *reinterpret_cast<const int4 *>(sC + t0);
                     const int4 cb = *reinterpret_cast<const int4 *>(sC + t0 + 4);
@@ -205,8 +207,10 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     uint32_t pk[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t lo16 = (t0 + 2 * e < L && cv[2 * e] == l16) ? 0x3c00u : 0u;
-                        const uint32_t hi16 = (t0 + 2 * e + 1 < L && cv[2 * e + 1] == l16) ? 0x3c00u : 0u;
+                        const uint32_t lo16 =
+                            ((FULL || t0 + 2 * e < L) && cv[2 * e] == l16) ? 0x3c00u : 0u;
+                        const uint32_t hi16 =
+                            ((FULL || t0 + 2 * e + 1 < L) && cv[2 * e + 1] == l16) ? 0x3c00u : 0u;
                         pk[e] = lo16 | (hi16 << 16);
                     }
                     const u32x4_t oh = {pk[0], pk[1], pk[2], pk[3]};
@@ -268,12 +272,12 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         const int hf = w >> 3, tl = tid & 511, wl = w & 7;
         float kraw[2][8], vraw[2][8];
         auto load_chunk = [&](int ch) {
-            const int j0 = 128 * ch, nk = min(128, L - j0);
+            const int j0 = 128 * ch, nk = FULL ? 128 : min(128, L - j0);
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int it = tl + 512 * n;
-                load_row8<T, false>(Kx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
-                load_row8<T, false>(Vx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
+                load_row8<T, FULL>(Kx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
+                load_row8<T, FULL>(Vx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
             }
         };
         load_chunk(hf);   // L > 128: both halves have a first chunk
@@ -289,8 +293,8 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         for (int r = 0; r < 2; ++r) {
             const int ch = 2 * r + hf;
             const int j0 = 128 * ch;
-            const bool on = j0 < L;                 // uniform over the half
-            const int nk = on ? min(128, L - j0) : 0;
+            const bool on = FULL || j0 < L;         // uniform over the half
+            const int nk = FULL ? 128 : on ? min(128, L - j0) : 0;
             if (on) {   // kraw, vraw hold chunk ch (requested earlier)
                 const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
                 const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                     st16(cV + o, vp.h);
                     if (!kZ) st16(cV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
                 }
-                if (r == 0 && 128 * (ch + 2) < L) load_chunk(ch + 2);   // the next round's chunk
+                if (r == 0 && (FULL || 128 * (ch + 2) < L)) load_chunk(ch + 2);   // the next round's chunk
             }
             __syncthreads();
             const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
                     const int key = 16 * wl + 4 * g + rr;
-                    sx[rr] = key < nk ? a[rr] * sscale2 : -__builtin_inff();
+                    sx[rr] = FULL || key < nk ? a[rr] * sscale2 : -__builtin_inff();
                     mloc = fmaxf(mloc, sx[rr]);
                 }
                 mloc = col_max(mloc);
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 f32x4_t a2[2] = {kZero4, kZero4};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    if (c < nch) {
+                    if (FULL || c < nch) {
                         const Sp8 vf = colfrag8_at(pV, 4096 * c + trc0, 4096 * c + trc1);
                         const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
                         a2[c & 1] = mma3z<kZ, false>(vf, pf, a2[c & 1]);
@@ -543,16 +547,21 @@ hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, i
                            int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
                            int G, void *out, int32_t *assign, hipStream_t st, int32_t *hist) {
     const dim3 grid((unsigned)S), block(kGThreads);
-#define CA_F512_LAUNCH(TT, HH)                                                                   \
-    hipLaunchKernelGGL((cluster_attn_fused512_kernel<TT, HH>), grid, block, 0, st,               \
+#define CA_F512_LAUNCH(TT, HH, F)                                                                \
+    hipLaunchKernelGGL((cluster_attn_fused512_kernel<TT, HH, F>), grid, block, 0, st,            \
                        static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
                        static_cast<const TT *>(V), L, Kc, iters, r, alpha, init_step, H, G,      \
                        static_cast<TT *>(out), assign, hist)
+#define CA_F512_LAUNCH_F(TT, HH)                                                                 \
+    do {                                                                                         \
+        if (L == kGL) CA_F512_LAUNCH(TT, HH, true); else CA_F512_LAUNCH(TT, HH, false);          \
+    } while (0)
     if (dt == CA_BF16) {
-        if (hist) CA_F512_LAUNCH(bf16_t, true); else CA_F512_LAUNCH(bf16_t, false);
+        if (hist) CA_F512_LAUNCH_F(bf16_t, true); else CA_F512_LAUNCH_F(bf16_t, false);
     } else {
-        if (hist) CA_F512_LAUNCH(float, true); else CA_F512_LAUNCH(float, false);
+        if (hist) CA_F512_LAUNCH_F(float, true); else CA_F512_LAUNCH_F(float, false);
     }
+#undef CA_F512_LAUNCH_F
 #undef CA_F512_LAUNCH
     return hipGetLastError();
 }
