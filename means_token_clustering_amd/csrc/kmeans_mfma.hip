@@ -61,8 +61,9 @@ static_assert(kKLds <= 81920, "two workgroups per CU");
 // score chains are then independent products and one (score, index) maximum
 // runs over the lane's 16 clusters before the column, and the two sum tiles
 // of a wave (same dimension tile, cluster groups kg and kg + 2) share their Q
-// fragments; every result is the one of the group-by-group form.
-template <typename T, bool INIT, bool SCORES, bool RUN, bool FIXED, bool K64>
+// fragments; every result is the one of the group-by-group form. FB: L is
+// a multiple of 128, so every block holds 128 tokens (no bounds tests).
+template <typename T, bool INIT, bool SCORES, bool RUN, bool FIXED, bool K64, bool FB>
 __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     const T *__restrict__ Q, const float *__restrict__ mu, int L, int Kc, int nblk, int nsub,
     int32_t *__restrict__ assign, float *__restrict__ part_sum, int32_t *__restrict__ part_cnt,
@@ -109,10 +110,10 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     // the wave's Q rows of the first block (dims 32c + 8g ..), zeros past it
     float qraw[2][8];
     {
-        const int Lb0 = min(128, L - 128 * b0);
+        const int Lb0 = FB ? 128 : min(128, L - 128 * b0);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            load_row8<T, false>(Qs + (long)(128 * b0) * kD, tok, Lb0, 32 * c + 8 * g, qraw[c]);
+            load_row8<T, FB>(Qs + (long)(128 * b0) * kD, tok, Lb0, 32 * c + 8 * g, qraw[c]);
     }
     // centroid row tid / 8, dims 8 (tid % 8) .. (zeros for rows >= Kc)
     const int mrow = tid >> 3, mcol = (tid & 7) * 8;
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
 
     for (int blk = b0; blk < b1; ++blk) {
     const int i0 = 128 * blk;
-    const int Lb = min(128, L - i0);               // tokens of the block
+    const int Lb = FB ? 128 : min(128, L - i0);    // tokens of the block
     if constexpr (!FIXED) {
         const float mq = absmax8(qraw[1], absmax8(qraw[0], 0.f));
         const uint32_t b = wave_max_u(__float_as_uint(mq));
@@ -257,10 +258,10 @@ __global__ __launch_bounds__(kThreads, 4) void kmeans_mfma_kernel(
     }
     // the next block's Q rows, in flight while this block is scored
     if (blk + 1 < b1) {
-        const int Ln = min(128, L - i0 - 128);
+        const int Ln = FB ? 128 : min(128, L - i0 - 128);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-            load_row8<T, false>(Qs + (long)(i0 + 128) * kD, tok, Ln, 32 * c + 8 * g, qraw[c]);
+            load_row8<T, FB>(Qs + (long)(i0 + 128) * kD, tok, Ln, 32 * c + 8 * g, qraw[c]);
     }
 
     // ------------------------------------------------------------ assignment
@@ -478,15 +479,23 @@ static hipError_t kmeans_mfma_dispatch(const void *Q, const float *mu, int S, in
         hipLaunchKernelGGL(kern, grid, block, 0, st, q, mu, L, Kc, nblk, nsub, assign, part_sum,
                            part_cnt, init_step, mu_init, prev_sum, prev_cnt, no_scores, qm);
     };
+    // runs of blocks over slices of whole blocks drop the bounds tests
+    const bool fb = nsub > 1 && L % 128 == 0;
     auto pick = [&](auto k64) {
         constexpr bool K = decltype(k64)::value;
         if (mu == nullptr) {
-            if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true, false, K>);
-            else launch(kmeans_mfma_kernel<T, true, false, false, false, K>);
+            if (fb) launch(kmeans_mfma_kernel<T, true, false, true, false, K, true>);
+            else if (nsub > 1) launch(kmeans_mfma_kernel<T, true, false, true, false, K, false>);
+            else launch(kmeans_mfma_kernel<T, true, false, false, false, K, false>);
         } else {
-            if (nsub > 1 && qm && !prev_sum) launch(kmeans_mfma_kernel<T, false, false, true, true, K>);
-            else if (nsub > 1) launch(kmeans_mfma_kernel<T, false, false, true, false, K>);
-            else launch(kmeans_mfma_kernel<T, false, false, false, false, K>);
+            if (nsub > 1 && qm && !prev_sum) {
+                if (fb) launch(kmeans_mfma_kernel<T, false, false, true, true, K, true>);
+                else launch(kmeans_mfma_kernel<T, false, false, true, true, K, false>);
+            } else if (nsub > 1) {
+                launch(kmeans_mfma_kernel<T, false, false, true, false, K, false>);
+            } else {
+                launch(kmeans_mfma_kernel<T, false, false, false, false, K, false>);
+            }
         }
     };
     if (Kc > 48) pick(std::true_type{});
@@ -499,7 +508,7 @@ static hipError_t kmeans_scores_dispatch(const void *Q, const float *mu, int S, 
                                          float *scores, hipStream_t st) {
     const int nblk = kmeans_mfma_blocks(L);
     const dim3 grid((unsigned)((long)S * nblk)), block(kThreads);
-    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false, false, false>), grid, block, 0, st,
+    hipLaunchKernelGGL((kmeans_mfma_kernel<T, false, true, false, false, false, false>), grid, block, 0, st,
                        static_cast<const T *>(Q), mu, L, Kc, nblk, 1, (int32_t *)nullptr,
                        (float *)nullptr, (int32_t *)nullptr, 0, (float *)nullptr,
                        (const float *)nullptr, (const int32_t *)nullptr, scores,

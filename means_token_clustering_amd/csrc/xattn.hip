@@ -49,8 +49,9 @@ static_assert(2 * kX64PPlane <= kXOffV && kX64Lds <= 81920, "two workgroups per 
 
 // K64: Kc in 49 .. 64, every centroid in one pass (fewer barriers, the four
 // groups' score chains independent, V^T P^T on all eight waves); the same
-// arithmetic in the same order as the group-by-group pass.
-template <typename T, bool MASKED, bool K64>
+// arithmetic in the same order as the group-by-group pass. FULLR: L is a
+// multiple of 128, so every range holds 128 keys (no bounds tests).
+template <typename T, bool MASKED, bool K64, bool FULLR>
 __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
     const float *__restrict__ mu, const T *__restrict__ Kx, const T *__restrict__ Vx, int L,
     int Kc, int nsplit, const uint8_t *__restrict__ valid, int H, int G,
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
     const int split = blockIdx.x % nsplit;
     const long s = blockIdx.x / nsplit;
     const int j0 = 128 * split;                    // first key of the range
-    const int nk = min(128, L - j0);
+    const int nk = FULLR ? 128 : min(128, L - j0);
     const long kvrow = kv_slice(s, H, G) * (long)L + j0;
     const LaneOffs lo = lane_offsets(l16, g);
     const int trq0 = 1024 * g + (lo.tr0 ^ (32 * (w & 3)));
@@ -82,8 +83,8 @@ __global__ __launch_bounds__(kThreads, 4) void xattn_mfma_kernel(
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         const int it = tid + kThreads * n;   // row it / 8, dims 8 (it % 8) ..
-        load_row8<T, false>(Kx + kvrow * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
-        load_row8<T, false>(Vx + kvrow * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
+        load_row8<T, FULLR>(Kx + kvrow * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
+        load_row8<T, FULLR>(Vx + kvrow * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
     }
     // the slice's first 64 centroid rows: row tid / 8, dims 8 (tid % 8) ..
     // (zeros past Kc), requested with K and V so that every group of 16
@@ -461,15 +462,20 @@ static hipError_t xattn_mfma_dispatch(const float *mu, const void *K, const void
     const int nsplit = xattn_splits(L);
     const dim3 grid((unsigned)((long)S * nsplit)), block(kThreads);
     const T *k = static_cast<const T *>(K), *v = static_cast<const T *>(V);
-#define CA_XA_LAUNCH(M, K64)                                                                  \
-    hipLaunchKernelGGL((xattn_mfma_kernel<T, M, K64>), grid, block, 0, st, mu, k, v, L, Kc,   \
+#define CA_XA_LAUNCH(M, K64, F)                                                               \
+    hipLaunchKernelGGL((xattn_mfma_kernel<T, M, K64, F>), grid, block, 0, st, mu, k, v, L, Kc, \
                        nsplit, valid, H, G, vcent, partials, stats)
+#define CA_XA_LAUNCH_F(M, K64)                                                                \
+    do {                                                                                      \
+        if (L % 128 == 0) CA_XA_LAUNCH(M, K64, true); else CA_XA_LAUNCH(M, K64, false);       \
+    } while (0)
     const bool k64 = Kc > 48 && Kc <= 64;
     if (valid) {
-        if (k64) CA_XA_LAUNCH(true, true); else CA_XA_LAUNCH(true, false);
+        if (k64) CA_XA_LAUNCH_F(true, true); else CA_XA_LAUNCH_F(true, false);
     } else {
-        if (k64) CA_XA_LAUNCH(false, true); else CA_XA_LAUNCH(false, false);
+        if (k64) CA_XA_LAUNCH_F(false, true); else CA_XA_LAUNCH_F(false, false);
     }
+#undef CA_XA_LAUNCH_F
 #undef CA_XA_LAUNCH
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || nsplit == 1 || !combine) return err;

@@ -191,6 +191,8 @@ LLOYD_RUNS = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 6, 11000, 48, 3, 24, 0.5, "bf16", 48),     # 86 blocks: a last run of two, ragged
     (1, 6, 11000, 56, 3, 24, 0.5, "bf16", 56),     # four cluster groups, the last one half empty
     (1, 2, 1300, 50, 3, 32, 0.5, "f32", 50),       # four groups, single blocks with the reduce
+    (1, 6, 11008, 48, 3, 24, 0.5, "bf16", 48),     # whole blocks only (86 of them)
+    (1, 5, 13312, 32, 2, 32, 0.5, "f32", 32),      # whole blocks only (104), two groups
 ]
 
 
