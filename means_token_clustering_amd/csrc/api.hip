@@ -153,6 +153,7 @@ struct Plan {
     bool chain;            // steps pass their block sums on (no reduce in between)
     bool mfma_local;       // window branch on the matrix cores (else scalar)
     bool merge_in_local;   // the window kernel merges the key-range partials
+    bool slice_xattn;      // kPlanSlice: the clustering launch forms the key ranges too
 };
 
 // Returns CA_OK and the plan, or CA_ERR_UNSUPPORTED when CA_PATH_FUSED was
@@ -196,6 +197,11 @@ ca_status_t make_plan(long S, int L, int Kc, int radius, const Variant &var, boo
     p.mfma_local = !var.soft && local_mfma_supported(radius);
     // a few key ranges: the window kernel merges them, no combine launch
     p.merge_in_local = p.mfma_local && xattn_splits(L) > 1 && xattn_splits(L) <= kXMergeInLocal;
+    // four ranges and the clustering's workgroups doubled within one round:
+    // the clustering launch forms the ranges itself (measured, bf16 L = 512,
+    // 96 slices: see kmeans_xattn_kernel)
+    p.slice_xattn = p.kind == kPlanSlice && !masked && p.merge_in_local &&
+                    kmeans_xattn_supported(S, L, Kc, device_cus());
     return CA_OK;
 }
 
@@ -226,6 +232,8 @@ const char *plan_name(const Plan &p) {
          "staged: scalar kmeans steps + reduce, xattn, local_mfma",
          "staged: scalar kmeans steps + reduce, xattn ranges, local_mfma (merge)"}};
     const int loc = !p.mfma_local ? 0 : p.merge_in_local ? 2 : 1;
+    if (p.kind == kPlanSlice && p.slice_xattn)
+        return "staged: kmeans_slice + xattn ranges, local_mfma (merge)";
     if (p.kind == kPlanSlice) return slice_names[loc];
     return step_names[!p.km_mfma ? 2 : p.chain ? 0 : 1][loc];
 }
@@ -359,7 +367,10 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         return hip_status(launch_gather_oloc(oloc, c, vcent, merge ? xpart : nullptr, (int)S, L,
                                              Kc, alpha, valid, H, dt, out, stream));
     }
-    if (one_launch)
+    if (one_launch && plan.slice_xattn)
+        CA_TRY(launch_kmeans_xattn(Q, K, V, (int)S, L, Kc, iters, dt, c, mu, var.init_step, H, G,
+                                   xpart, stream, hist));
+    else if (one_launch)
         CA_TRY(launch_kmeans_slice(Q, (int)S, L, Kc, iters, dt, c, mu, var.init_step, stream,
                                    hist));
     for (int t = 1; !one_launch && t <= iters; ++t) {
@@ -388,8 +399,9 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
                               hipMemcpyDeviceToDevice, stream));
     const bool mfma_local = plan.mfma_local;
     const bool merge_in_local = plan.merge_in_local;
-    CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
-                                 stream, nullptr, !merge_in_local));
+    if (!plan.slice_xattn)
+        CA_TRY(launch_centroid_xattn(mu, K, V, (int)S, L, Kc, dt, valid, H, G, vcent, xpart,
+                                     stream, nullptr, !merge_in_local));
     if (mfma_local)
         return hip_status(launch_local_mfma(Q, K, V, (int)S, L, radius, dt, vcent, c, Kc, alpha,
                                             valid, H, G, out, stream,

@@ -21,6 +21,7 @@
 // slice (the centroids, means of its rows, follow); the centroids are scaled
 // back exactly when stored.
 #include "local_mfma_body.h"
+#include "xattn_body.h"
 
 namespace ca {
 namespace {
@@ -48,7 +49,8 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
                                                   int32_t *__restrict__ assign,
                                                   float *__restrict__ mu_out, long s, int tid,
                                                   unsigned char *smem,
-                                                  int32_t *__restrict__ hist, long S) {
+                                                  int32_t *__restrict__ hist, long S,
+                                                  float *mu_tab = nullptr) {
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem + kSOffQ);
     uint16_t *sMu = reinterpret_cast<uint16_t *>(smem + kSOffMu);
     uint16_t *sMuX = reinterpret_cast<uint16_t *>(smem + kSOffMuX);
@@ -223,8 +225,10 @@ __device__ __forceinline__ void kmeans_slice_body(const T *__restrict__ Q, int L
             if (t == iters) {
                 if (l16 < Kc) {
                     const float back = __builtin_ldexpf(1.f, sq);
-                    *reinterpret_cast<float4 *>(mu_out + (s * Kc + l16) * kD + 16 * dt + 4 * g) =
-                        make_float4(v[0] * back, v[1] * back, v[2] * back, v[3] * back);
+                    const float4 f4 = make_float4(v[0] * back, v[1] * back, v[2] * back, v[3] * back);
+                    *reinterpret_cast<float4 *>(mu_out + (s * Kc + l16) * kD + 16 * dt + 4 * g) = f4;
+                    // the same rows for a centroid attention in this workgroup
+                    if (mu_tab) *reinterpret_cast<float4 *>(mu_tab + l16 * kD + 16 * dt + 4 * g) = f4;
                 }
             } else {
                 const Sp4 mu4 = split4(v[0], v[1], v[2], v[3]);
@@ -313,6 +317,65 @@ hipError_t launch_kmeans_window(const void *Q, const void *K, const void *V, int
     }
 #undef CA_KW_LAUNCH_H
 #undef CA_KW_LAUNCH
+    return hipGetLastError();
+}
+
+// The clustering of S slices followed, in the same launch, by their centroid
+// attention over four 128-key ranges: two workgroups per slice both run the
+// clustering (the same arithmetic, so the same assignments and centroids,
+// which both store), keep the final centroids in LDS, and then each half of
+// a workgroup's waves forms one key range's partial (workgroup s: ranges 0
+// and 1, workgroup S + s: ranges 2 and 3), merged later in range order by
+// the window kernel. The clustering's LDS is dead by then; the table of
+// centroids lies past both halves' attention LDS.
+constexpr int kKXTab = 2 * kXLdsM;                          // [16][64] fp32 centroids
+constexpr int kKXLds = kKXTab + kFK * kD * 4;
+static_assert(kSLds <= kKXTab && kKXLds <= 163840, "one workgroup per CU");
+
+template <typename T, bool HIST, bool FULL>
+__global__ __launch_bounds__(kSThreads, 1) void kmeans_xattn_kernel(
+    const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
+    int iters, int init_step, int H, int G, int32_t *__restrict__ assign,
+    float *__restrict__ mu_out, float *__restrict__ xpart, int32_t *__restrict__ hist, int S) {
+    __shared__ __align__(16) unsigned char smem[kKXLds];
+    const int part = (int)blockIdx.x >= S ? 1 : 0;
+    const long s = (long)blockIdx.x - (long)part * S;
+    float *tab = reinterpret_cast<float *>(smem + kKXTab);
+    kmeans_slice_body<T, HIST, FULL>(Q, L, Kc, iters, init_step, assign, mu_out, s, threadIdx.x,
+                                     smem, hist, S, tab);
+    __syncthreads();   // the centroids are in the table; the clustering's LDS is free
+    const int half = threadIdx.x >> 9;   // uniform per wave
+    xattn_range<T, false, false, FULL>(tab, Kx, Vx, L, Kc, 4, nullptr, H, G, nullptr, xpart,
+                                       nullptr, smem + half * kXLdsM, threadIdx.x & (kThreads - 1),
+                                       s, 2 * part + half);
+}
+
+bool kmeans_xattn_supported(long S, int L, int Kc, int cus) {
+    return kmeans_slice_supported(L, Kc) && xattn_splits(L) == 4 && 2 * S <= cus;
+}
+
+hipError_t launch_kmeans_xattn(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                               int iters, ca_dtype_t dt, int32_t *assign, float *mu,
+                               int init_step, int H, int G, float *xpart, hipStream_t st,
+                               int32_t *hist) {
+    if (!kmeans_slice_supported(L, Kc) || xattn_splits(L) != 4) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(2 * S)), block(kSThreads);
+#define CA_KX_LAUNCH(TT, HH, F)                                                                  \
+    hipLaunchKernelGGL((kmeans_xattn_kernel<TT, HH, F>), grid, block, 0, st,                     \
+                       static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
+                       static_cast<const TT *>(V), L, Kc, iters, init_step, H, G, assign, mu,    \
+                       xpart, hist, S)
+#define CA_KX_LAUNCH_F(TT, HH)                                                                   \
+    do {                                                                                         \
+        if (L == kSL) CA_KX_LAUNCH(TT, HH, true); else CA_KX_LAUNCH(TT, HH, false);              \
+    } while (0)
+    if (dt == CA_BF16) {
+        if (hist) CA_KX_LAUNCH_F(bf16_t, true); else CA_KX_LAUNCH_F(bf16_t, false);
+    } else {
+        if (hist) CA_KX_LAUNCH_F(float, true); else CA_KX_LAUNCH_F(float, false);
+    }
+#undef CA_KX_LAUNCH_F
+#undef CA_KX_LAUNCH
     return hipGetLastError();
 }
 

@@ -94,6 +94,14 @@ bool kmeans_slice_supported(int L, int Kc);
 hipError_t launch_kmeans_slice(const void *Q, int S, int L, int Kc, int iters, ca_dtype_t dt,
                                int32_t *assign, float *mu, int init_step, hipStream_t st,
                                int32_t *hist = nullptr);
+// The same clustering followed by the centroid attention's four key-range
+// partials (xpart, unmasked) in one launch of 2 S workgroups, for 384 < L <=
+// 512 and 2 S <= cus (every workgroup resident at once).
+bool kmeans_xattn_supported(long S, int L, int Kc, int cus);
+hipError_t launch_kmeans_xattn(const void *Q, const void *K, const void *V, int S, int L, int Kc,
+                               int iters, ca_dtype_t dt, int32_t *assign, float *mu,
+                               int init_step, int H, int G, float *xpart, hipStream_t st,
+                               int32_t *hist = nullptr);
 
 // key ranges per slice of the centroid cross-attention (partials when > 1)
 int xattn_splits(int L);

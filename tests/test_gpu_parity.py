@@ -117,6 +117,9 @@ EDGE = [  # B, H, L, nclust, iters, W, alpha, dtype, blobs
     (1, 2, 384, 12, 3, 20, 0.6, "bf16", 10),       # three ranges, ragged clusters
     # staged: S x blocks odd, the launches in sequence
     (1, 1, 300, 16, 3, 32, 0.5, "bf16", 10),       # three blocks
+    # staged: the clustering launch forms the four key ranges (86-128 slices)
+    (8, 12, 400, 16, 3, 32, 0.5, "f32", 16),       # ragged last range
+    (9, 12, 512, 12, 2, 20, 0.5, "bf16", 12),      # 108 slices, 12 clusters
 ]
 
 

@@ -39,7 +39,9 @@ PATHS = [
     ("fused kept centroids", 0, 1, 3, 128, 16, 3, 32, "f32", 6, 2, False),
     ("fused512", 1, 2, 3, 300, 16, 3, 32, "f32", 12, 0, False),
     ("fused512 bf16", 1, 1, 2, 512, 16, 4, 33, "bf16", 16, 0, False),
-    ("kmeans_slice (96 slices)", 2, 8, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
+    ("kmeans_slice + key ranges (96 slices)", 2, 8, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
+    ("kmeans_slice + key ranges, ragged", 2, 8, 12, 400, 12, 3, 32, "f32", 12, 0, False),
+    ("kmeans_slice (132 slices)", 2, 11, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
     ("kmeans_window (window beside)", 2, 1, 4, 300, 16, 3, 32, "f32", 10, 0, False),
     ("chained matrix-core steps", 2, 1, 2, 600, 32, 4, 32, "f32", 20, 0, False),
     ("steps with reduce launches", 2, 1, 2, 1100, 20, 3, 32, "f32", 20, 0, False),
