@@ -314,7 +314,8 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     if (st != CA_OK) return st;
     if (plan.kind == kPlanFused)
         return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var,
-                                               dt, valid, H, G, out, assign_out, stream, hist));
+                                               dt, valid, H, G, out, assign_out, stream, hist,
+                                               device_cus()));
     if (plan.kind == kPlanFused512)
         return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
                                           var.init_step, dt, H, G, out, assign_out, stream,

@@ -209,7 +209,8 @@ bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                                 int iters, int radius, float alpha, const Variant &var,
                                 ca_dtype_t dt, const uint8_t *valid, int H, int G, void *out,
-                                int32_t *assign, hipStream_t st, int32_t *hist = nullptr);
+                                int32_t *assign, hipStream_t st, int32_t *hist = nullptr,
+                                int cus = 0);   // cus: the device's CU count (0: unknown)
 
 // C[z] = A . W[z] for z < count (bf16 bits, fp32 accumulation): w_kn, W[z]
 // is [K, N] row-major; otherwise B[z] is Bt [N, K] and C = A . Bt^T.
