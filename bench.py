@@ -577,7 +577,7 @@ def main():
 
     # the launch sequence the library takes (its own dispatch decision)
     plan = b.cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, flags=args.flags,
-                               masked=mask is not None, path=path)
+                               masked=mask is not None, path=path, dtype=dt)
     fused = plan == "fused"
     achieved = set_bytes / (ms / 1e3) / 1e9
     traffic = None
@@ -589,6 +589,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "kernel": ("cluster_attn_fused_kernel" if fused else
                        "cluster_attn_fused512_kernel" if plan == "fused512" else
+                       "cluster_attn_fused512_kernel, split form"
+                       if plan.startswith("fused512 split") else
                        "launch sequence " + plan),
             "bytes_per_launch": set_bytes}
     rec = {"metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,

@@ -148,6 +148,18 @@ const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags,
                               ca_path_t path);
 
 /*
+ * cluster_attn_plan for the storage type dt (cluster_attn_plan itself answers
+ * for CA_F32). With CA_BF16, 128 < L <= 512, nclust <= 16, W / 2 <= 16, no
+ * mask or listing variant and B * H slices filling at most half of the CUs,
+ * the auto path takes "fused512 split (clustering and window workgroups)":
+ * a second workgroup per slice forms the window branch beside the clustering
+ * and writes the fused rows once the clustering workgroup has published its
+ * centroid context (the rows come out as NaN if that wait ever gave up).
+ */
+const char *cluster_attn_plan_dt(int B, int H, int L, int nclust, int W, int flags, int masked,
+                                 ca_path_t path, ca_dtype_t dt);
+
+/*
  * Cluster attention with a key-padding mask (padded batches): the
  * ClusterAttention listing on the "Hooshaai/svd-sst2-roberta-cluster" page,
  * forward, bidirectional branch (its attention_mask path).

@@ -39,6 +39,7 @@ SIGNATURES = {
     "ca_version": (_i, []),
     "cluster_attn_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "cluster_attn_plan": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "cluster_attn_plan_dt": (ctypes.c_char_p, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
     "cluster_attn_workspace_size_ex": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "cluster_attn_forward": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _vp, _i,
                                   _vp, _sz, _vp]),
@@ -164,10 +165,12 @@ def _ws_bytes(ws) -> int:
     return ws.numel() * ws.element_size() - ((p + 255) // 256 * 256 - p)
 
 
-def cluster_attn_plan(B, H, L, nclust, W, flags=0, masked=False, path=CA_PATH_AUTO):
-    """Name of the launch sequence the forward takes for these arguments (None
-    when the call would be rejected)."""
-    r = lib().cluster_attn_plan(B, H, L, nclust, W, int(flags), int(bool(masked)), int(path))
+def cluster_attn_plan(B, H, L, nclust, W, flags=0, masked=False, path=CA_PATH_AUTO,
+                      dtype=CA_F32):
+    """Name of the launch sequence the forward takes for these arguments and
+    storage type (None when the call would be rejected)."""
+    r = lib().cluster_attn_plan_dt(B, H, L, nclust, W, int(flags), int(bool(masked)), int(path),
+                                   int(dtype))
     return r.decode() if r is not None else None
 
 

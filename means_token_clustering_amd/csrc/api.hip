@@ -120,6 +120,15 @@ bool fused512_pays(long S) {
     return cus > 0 && 2 * S > cus && S <= cus;
 }
 
+// With at most half the CUs' worth of slices, the split form of that launch
+// (bf16 storage) runs each slice's window branch on a second workgroup beside
+// its clustering, on CUs the single launch would leave idle (measured, bf16
+// L = 512, 96 slices: see fused512.hip).
+bool fused512_split_pays(long S) {
+    const int cus = device_cus();
+    return cus > 0 && 2 * S <= cus && S <= fused512_split_max_slices();
+}
+
 // The window blocks beside the clustering fill CUs that the clustering
 // (one workgroup per slice) leaves idle: taken when the clustering and the
 // window workgroups (two 128-query blocks each) fit the CUs in one round
@@ -140,6 +149,7 @@ bool use_fused(ca_path_t path, int L, int Kc) {
 enum PlanKind {
     kPlanFused,      // cluster_attn_fused_kernel: one launch, L <= 128
     kPlanFused512,   // cluster_attn_fused512_kernel: one launch, 128 < L <= 512
+    kPlanF512Split,  // its split form: 2 S workgroups (clustering, window), bf16 storage
     kPlanSeg,        // cluster_attn_seg_kernel: one launch, each slice over ns workgroups
     kPlanBeside,     // kmeans_window_kernel (clustering + window), centroid attention, gather
     kPlanSlice,      // kmeans_slice_kernel, centroid attention, window branch
@@ -159,7 +169,7 @@ struct Plan {
 // Returns CA_OK and the plan, or CA_ERR_UNSUPPORTED when CA_PATH_FUSED was
 // asked for a shape without a single launch.
 ca_status_t make_plan(long S, int L, int Kc, int radius, const Variant &var, bool masked,
-                      ca_path_t path, Plan &p) {
+                      ca_path_t path, bool bf16, Plan &p) {
     p = Plan{};
     if (path != CA_PATH_SEGMENTED && use_fused(path, L, Kc)) {
         p.kind = kPlanFused;
@@ -170,6 +180,10 @@ ca_status_t make_plan(long S, int L, int Kc, int radius, const Variant &var, boo
     // the auto path when it pays)
     const bool f512 = plain && fused512_supported(L, Kc, radius);
     if (path == CA_PATH_FUSED && !f512) return CA_ERR_UNSUPPORTED;
+    if (f512 && bf16 && path == CA_PATH_AUTO && fused512_split_pays(S)) {
+        p.kind = kPlanF512Split;
+        return CA_OK;
+    }
     if (f512 && (path == CA_PATH_FUSED || (path == CA_PATH_AUTO && fused512_pays(S)))) {
         p.kind = kPlanFused512;
         return CA_OK;
@@ -209,6 +223,7 @@ const char *plan_name(const Plan &p) {
     switch (p.kind) {
         case kPlanFused: return "fused";
         case kPlanFused512: return "fused512";
+        case kPlanF512Split: return "fused512 split (clustering and window workgroups)";
         case kPlanSeg: return "segmented";
         case kPlanBeside:
             return p.merge_in_local ? "staged: kmeans_window, xattn ranges, gather_oloc (merge)"
@@ -310,7 +325,7 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
     }
 
     Plan plan;
-    st = make_plan(S, L, Kc, radius, var, valid != nullptr, path, plan);
+    st = make_plan(S, L, Kc, radius, var, valid != nullptr, path, dt == CA_BF16, plan);
     if (st != CA_OK) return st;
     if (plan.kind == kPlanFused)
         return hip_status(launch_fused_forward(Q, K, V, (int)S, L, Kc, iters, radius, alpha, var,
@@ -320,6 +335,18 @@ ca_status_t forward_impl(const void *Q, const void *K, const void *V, const uint
         return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
                                           var.init_step, dt, H, G, out, assign_out, stream,
                                           hist));
+    if (plan.kind == kPlanF512Split) {
+        const size_t need = fused512_split_workspace_bytes(S);
+        if (workspace_bytes < need || !workspace || !aligned(workspace, kAlign))
+            return CA_ERR_INVALID_ARG;
+        const Span others[] = {{Q, tbytes}, {K, kvbytes}, {V, kvbytes}, {out, tbytes},
+                               {assign_out, abytes}, {hist, hbytes}};
+        for (const Span &o : others)
+            if (o.p && overlap(workspace, need, o.p, o.n)) return CA_ERR_INVALID_ARG;
+        return hip_status(launch_fused512(Q, K, V, (int)S, L, Kc, iters, radius, alpha,
+                                          var.init_step, dt, H, G, out, assign_out, stream, hist,
+                                          workspace));
+    }
     if (plan.kind == kPlanSeg) {
         const size_t need = seg_workspace_bytes(S, L, Kc, plan.ns);
         if (workspace_bytes < need || !workspace || !aligned(workspace, kAlign))
@@ -509,12 +536,21 @@ size_t cluster_attn_workspace_size_ex(int B, int H, int L, int d, int nclust, ca
         const int ns = seg_count(S, L, Kc, 0, device_cus());
         return ns > 0 ? seg_workspace_bytes(S, L, Kc, ns) : 0;
     }
-    return staged_layout(S, L, Kc).total;
+    // the auto path's split form needs less than the staged launches, but
+    // take the larger of the two so the size never depends on the CU count
+    const size_t staged = staged_layout(S, L, Kc).total;
+    const size_t split = fused512_split_workspace_bytes(S);
+    return staged > split ? staged : split;
 }
 
 const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags, int masked,
                               ca_path_t path) {
-    if (check_shape(B, H, L, kD, nclust, 1, W, 0.f, CA_F32) != CA_OK) return nullptr;
+    return cluster_attn_plan_dt(B, H, L, nclust, W, flags, masked, path, CA_F32);
+}
+
+const char *cluster_attn_plan_dt(int B, int H, int L, int nclust, int W, int flags, int masked,
+                                 ca_path_t path, ca_dtype_t dt) {
+    if (check_shape(B, H, L, kD, nclust, 1, W, 0.f, dt) != CA_OK) return nullptr;
     if ((flags & ~CA_FLAG_LISTING) ||
         (path != CA_PATH_AUTO && path != CA_PATH_FUSED && path != CA_PATH_STAGED &&
          path != CA_PATH_SEGMENTED))
@@ -527,7 +563,8 @@ const char *cluster_attn_plan(int B, int H, int L, int nclust, int W, int flags,
     int radius = W / 2;
     if (flags & CA_FLAG_BAND) radius = (W == 0 || W >= L) ? 0 : W;
     Plan p;
-    if (make_plan((long)B * H, L, Kc, radius, var, masked != 0, path, p) != CA_OK) return nullptr;
+    if (make_plan((long)B * H, L, Kc, radius, var, masked != 0, path, dt == CA_BF16, p) != CA_OK)
+        return nullptr;
     return plan_name(p);
 }
 

@@ -25,6 +25,8 @@
 //      16-row halo (at most 288) as K, V planes, the forward's narrow window
 //      routine per query tile, then the gather of (1 - alpha) V^cent_{c_i}
 //      and the fused row stores.
+#include <atomic>
+
 #include "launch.h"
 #include "mfma_split.h"
 
@@ -56,15 +58,127 @@ static_assert(kGLds <= 163840, "one workgroup per CU");
 
 }  // namespace
 
-// HIST: hist receives the assignment of every Lloyd iteration, [iters, S, L]
-// (S = the grid size).
+// Split form (SPLIT, bf16 storage): a grid of 2 S workgroups, S at most half
+// the CUs, so that all of them are resident at once (one per CU).
+//   Workgroup s < S (clustering) runs phase 1 for slice s, publishes the
+//   final centroid planes and its Q scale and raises the slice's flag to
+//   2e + 1 (e: the launch number), runs round 0 of phase 2 (key chunks 0 and
+//   1), publishes that round's record (maximum, sum, row of each context lane)
+//   and the assignment, and raises the flag to 2e + 2.
+//   Workgroup S + s (window) runs phase 3 for slice s on a CU the single launch
+//   would leave idle, each pass with its own Q scale, and keeps the window
+//   rows in LDS as fp16; after the first flag it runs round 1 of phase 2 (key
+//   chunks 2 and 3) with the published centroids, after the second it merges
+//   the two records in chunk order into (1 - alpha) V^cent and writes the
+//   fused rows. Measured, bf16 L = 512, 96 slices: 25.9 us per forward
+//   against 27.9 us for the staged launches (same box); per workgroup, the
+//   clustering publishes its centroids at 10.4 us and its record at 15.5 us,
+//   the window workgroup ends its passes at 13.3 us and its round at 17.3 us
+//   and writes the last rows at 20.3 us.
+// Each value that crosses workgroups is written with a device-scope atomic
+// store and read with a device-scope atomic load (coherent across the XCDs'
+// L2 caches); a writer waits for its stores to complete before the barrier
+// that precedes its flag store, a reader loads only after it saw the flag, so
+// no cache write-back or invalidate is needed. A wait is bounded: past
+// kSpinLimit polls it records the launch in the ring's error word and the
+// window workgroup writes NaN rows, so that the failure cannot pass unnoticed.
+// words of one slice's published values: the final centroid planes (h, m), the
+// record of key chunks 0 and 1 ([4 dim tiles][64 lanes][M, l, row 0..3]), c
+constexpr int kPubMu = 0;
+constexpr int kPubPart = kPubMu + 2 * kPlaneMu / 4;
+constexpr int kPubC = kPubPart + 4 * 64 * 6;
+constexpr int kPubSq = kPubC + kGL;          // the clustering's Q scale shift
+constexpr int kPubStride = kPubSq + 64;      // (rounded up to 256 bytes)
+constexpr int kSpinLimit = 1 << 18;          // polls of a flag before giving up (about 0.3 s)
+
+// Flags of the split form, owned by the library (zero when the code object is
+// loaded, one copy per device): launch number e (per device, from 1, never
+// reused) uses ring e % kRings; the clustering workgroup of slice s sets word
+// s of that ring to 2e + 1 once its centroids are published and to 2e + 2 once
+// its record and the assignment are, and a wait that gives up stores e in the
+// ring's error word. Values left by earlier launches of the ring are at most
+// 2 (e - kRings) + 2, so no reset is needed between launches, and launches in
+// flight at the same time use different rings unless kRings of them overlap.
+constexpr int kRings = 64;
+constexpr int kMaxSplitSlices = 512;
+__device__ unsigned long long g_split_flags[kRings * kMaxSplitSlices];
+__device__ unsigned long long g_split_err[kRings];
+__device__ __forceinline__ unsigned long long *split_flag(unsigned long long e, long s) {
+    return g_split_flags + (e % kRings) * kMaxSplitSlices + s;
+}
+__device__ __forceinline__ unsigned long long *split_err(unsigned long long e) {
+    return g_split_err + e % kRings;
+}
+static_assert(2 * kPlaneMu / 4 == kGThreads, "one centroid-plane word per thread");
+
+// device-scope atomic load of a published word (coherent across the XCDs)
+__device__ __forceinline__ uint32_t ld_pub(const uint32_t *p) {
+    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 polls *flag until it holds at least v (bounded: past kSpinLimit
+// polls it stores the launch number e in the ring's error word and stops
+// waiting); the workgroup then passes a barrier.
+__device__ __forceinline__ void wait_flag(unsigned long long *flag, unsigned long long v,
+                                          unsigned long long e) {
+    if (threadIdx.x == 0) {
+        int polls = 0;
+        while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++polls > kSpinLimit) {
+                __hip_atomic_store(split_err(e), e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// LDS block (2 KB, lane-major 16-byte chunks) holding wave w's window rows of
+// pass p as fp16 while the split form's window workgroup runs the rest: bytes
+// [48K, 64K) and [112K, 128K) for pass 0 (unwritten by the second pass and by
+// the centroid attention), [16K, 32K) and [80K, 96K) for pass 1 (unwritten by
+// the centroid attention), waves 0-7 in the first range, 8-15 in the second.
+__device__ __forceinline__ u32x4_t *stash_at(unsigned char *smem, int p, int w) {
+    const int base = (p == 0 ? 48 : 16) * 1024 + (w < 8 ? 0 : 64 * 1024) + 2048 * (w & 7);
+    return reinterpret_cast<u32x4_t *>(smem + base);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+// o[j][rr] * il (rounded to nearest fp16) of this lane
+__device__ __forceinline__ void stash_put(u32x4_t *blk, const f32x4_t *o, float il) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const f32x4_t a = o[2 * c] * il, b = o[2 * c + 1] * il;
+        blk[64 * c + lane] = u32x4_t{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]),
+                                     pack_f16x2(b[0], b[1]), pack_f16x2(b[2], b[3])};
+    }
+}
+__device__ __forceinline__ void stash_get(const u32x4_t *blk, float *y) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const u32x4_t v = blk[64 * c + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[8 * c + 2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] & 0xffffu));
+            y[8 * c + 2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[i] >> 16));
+        }
+    }
+}
+
+// HIST: hist receives the assignment of every Lloyd iteration, [iters, S, L].
 // FULL: L is 512 (no bounds tests in the clustering and the centroid attention;
 // the window passes keep theirs, which the register budget needs).
-template <typename T, bool HIST, bool FULL>
+template <typename T, bool HIST, bool FULL, bool SPLIT>
 __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int L, int Kc,
     int iters, int rad, float alpha, int init_step, int H, int G, T *__restrict__ out,
-    int32_t *__restrict__ assign, int32_t *__restrict__ hist) {
+    int32_t *__restrict__ assign, int32_t *__restrict__ hist, int S, uint32_t *__restrict__ pub,
+    unsigned long long epoch) {
     __shared__ __align__(16) unsigned char smem[kGLds];
     uint16_t *sQ = reinterpret_cast<uint16_t *>(smem);
     float *sPart = reinterpret_cast<float *>(smem + kGOffPart);
@@ -80,7 +194,8 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const int tid = threadIdx.x;
     constexpr bool kZ = bf16_storage<T>();   // Q (K, V) planes with zero m parts
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
-    const long s = blockIdx.x;
+    const bool win = SPLIT && (int)blockIdx.x >= S;   // window workgroup of the split form
+    const long s = win ? (long)blockIdx.x - S : (long)blockIdx.x;
     const long base = s * (long)L * kD;
     const long kvbase = kv_slice(s, H, G) * (long)L * kD;
     const T *Qs = Q + base;
@@ -88,6 +203,403 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     const LaneOffs lo = lane_offsets(l16, g);
     const int trv = 1024 * (g >> 1) + ((g & 1) ? lo.tr4 : lo.tr0);
 
+    // Phase 3 (below) as a routine of the slice's Q scale shift: the single
+    // launch runs it after phase 2, a window workgroup of the split form alone.
+    float wfac0 = 0.f, wfac1 = 0.f;   // split form: alpha 2^sv of each window pass
+    auto phase3 = [&](const int sq, const float fq) {
+    {
+        uint16_t *tK = reinterpret_cast<uint16_t *>(smem), *tV = tK + kGPlane3;   // h, m pairs
+        const u8 *pK3 = smem, *pV3 = smem + 2 * kGPlane3;
+        constexpr int kItems = (kGRows3 * kD / 8 + kGThreads - 1) / kGThreads;   // 3
+        KeyBits kb;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kb.w[k] = ~0u;
+        // split form: each pass's window rows O^loc / l (scaled units of V)
+        // wait for the gather as fp16 in LDS that neither the second pass nor
+        // the centroid attention writes (bf16 storage leaves their m planes
+        // unused; stash_at), their factor alpha 2^sv in wfac0 / wfac1; the second
+        // pass's rows are stored once its planes are dead
+        static_assert(!SPLIT || bf16_storage<T>(), "the split form keeps results in the m planes");
+        f32x4_t o1[4] = {kZero4, kZero4, kZero4, kZero4};
+        float il1 = 0.f;
+        // one window pass (p = 0: queries 0 .. 255, 1: 256 ..); false when L has no such queries
+        auto pass = [&](const int p) -> bool {
+            const int q0 = 256 * p;                 // first query of the pass
+            if (q0 >= L) return false;              // uniform
+            const int r0 = p == 0 ? 0 : q0 - 16;    // first staged row
+            const int Lp = min(L, q0 + 272) - r0;   // staged rows holding keys
+            const int NTp = (Lp + 15) >> 4;
+            float kraw[kItems][8], vraw[kItems][8];
+#pragma unroll
+            for (int n = 0; n < kItems; ++n) {
+                const int it = tid + kGThreads * n;
+                if (it < kGRows3 * kD / 8) {
+                    load_row8<T, false>(Kx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, kraw[n]);
+                    load_row8<T, false>(Vx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, vraw[n]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) kraw[n][i] = vraw[n][i] = 0.f;
+                }
+            }
+            const int tile = 16 * p + w;   // the wave's query tile of this pass
+            // split form: the pass's own Q scale (its 256 query rows), so that
+            // the window workgroup needs nothing of phase 1; a power of two
+            // either way, which leaves the products unchanged. The rows are
+            // requested again below (from the cache) rather than kept.
+            uint32_t bq = 0u;
+            if (SPLIT) {
+                float qm[2][8];
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, qm[c]);
+                bq = __float_as_uint(absmax8(qm[1], absmax8(qm[0], 0.f)));
+            }
+            {
+                float mk = 0.f, mv = 0.f;
+#pragma unroll
+                for (int n = 0; n < kItems; ++n) {
+                    mk = absmax8(kraw[n], mk);
+                    mv = absmax8(vraw[n], mv);
+                }
+                const uint32_t bk = wave_max_u(__float_as_uint(mk));
+                const uint32_t bv = wave_max_u(__float_as_uint(mv));
+                if (SPLIT) bq = wave_max_u(bq);
+                if (lane == 0) {
+                    if (SPLIT) sMax[4 * w] = bq;
+                    sMax[4 * w + 1] = bk;
+                    sMax[4 * w + 2] = bv;
+                }
+            }
+            __syncthreads();
+            uint32_t mk = 0, mv = 0, mq = 0;
+#pragma unroll
+            for (int ww = 0; ww < 16; ++ww) {
+                mk = max(mk, sMax[4 * ww + 1]);
+                mv = max(mv, sMax[4 * ww + 2]);
+                if (SPLIT) mq = max(mq, sMax[4 * ww]);
+            }
+            const int sk = scale_shift(mk, kKVLimit), sv = scale_shift(mv, kKVLimit);
+            const int sqp = SPLIT ? scale_shift(mq, kQLimit) : sq;
+            const float fqp = SPLIT ? __builtin_ldexpf(1.f, -sqp) : fq;
+            (p == 0 ? wfac0 : wfac1) = alpha * __builtin_ldexpf(1.f, sv);   // uniform
+            // the wave's query rows of this pass, requested before the planes
+            // are built so that their latency passes during that work
+            float qx[2][8];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, qx[c]);
+            {
+                const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
+#pragma unroll
+                for (int n = 0; n < kItems; ++n) {
+                    const int it = tid + kGThreads * n;
+                    if (it < kGRows3 * kD / 8) {
+                        float x[8], y[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            x[i] = kraw[n][i] * fk;
+                            y[i] = vraw[n][i] * fv;
+                        }
+                        const Sp8 kp = split8(x), vp = split8(y);
+                        const int o = off64(it >> 3, (it & 7) * 8);
+                        st16(tK + o, kp.h);
+                        if (!kZ) st16(tK + kGPlane3 / 2 + o, kp.m);   // zero for bf16 storage, never read
+                        st16(tV + o, vp.h);
+                        if (!kZ) st16(tV + kGPlane3 / 2 + o, vp.m);   // zero for bf16 storage, never read
+                    }
+                }
+            }
+            __syncthreads();
+            if (tile < NT) {
+                const int qt = (16 * tile - r0) >> 4;
+                const float sscale2 = __builtin_ldexpf(0.125f, sqp + sk) * 1.4426950408889634f;
+                // the tile's Q fragments again (cheaper than keeping them live
+                // through the centroid attention): the same values as in phase 1
+                Sp8 qp[2];
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) qx[c][i] *= fqp;
+                    qp[c] = split8<true>(qx[c]);
+                }
+                f32x4_t o[4];
+                float lsum;
+                local_narrow<false, false, KeyBits, kGPlane3, kZ>(pK3, pV3, qp, qt, NTp, Lp, rad,
+                                                            sscale2, l16, g, lo.rl64, trv, kb, o,
+                                                            lsum);
+                const int tok = 16 * tile + l16;
+                if (SPLIT) {
+                    if (p == 0) {
+                        stash_put(stash_at(smem, 0, w), o, __builtin_amdgcn_rcpf(lsum));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) o1[j] = o[j];
+                        il1 = __builtin_amdgcn_rcpf(lsum);
+                    }
+                } else if (tok < L) {
+                    const float f = alpha * __builtin_ldexpf(1.f, sv) * __builtin_amdgcn_rcpf(lsum);
+                    const float *vc = sVc + sC[tok] * kD;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
+                        const int d0 = 16 * j + 4 * g;
+                        const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
+                        store4<T>(out + base + (long)tok * kD + d0,
+                                  make_float4(fmaf(o[j][0], f, c4.x), fmaf(o[j][1], f, c4.y),
+                                              fmaf(o[j][2], f, c4.z), fmaf(o[j][3], f, c4.w)));
+                    }
+                }
+            }
+            __syncthreads();   // the planes are rewritten by the next pass
+            return true;
+        };
+        // the split form runs the passes as separate copies (p known to the
+        // compiler), so that the first pass's registers hold nothing of the second's
+        if (SPLIT) {
+            if (pass(0)) pass(1);
+        } else {
+            for (int p = 0; p < 2; ++p)
+                if (!pass(p)) break;
+        }
+        if (SPLIT && 16 * (16 + w) < L) stash_put(stash_at(smem, 1, w), o1, il1);
+    }
+    };
+    // ============================================================ 2. centroid attention
+    // Rounds r0 .. r1 - 1 of it: in round r, half hf = w / 8 takes key chunk
+    // 2 r + hf (keys 128 ch ..; the single launch runs rounds 0 and 1); wave
+    // w % 8 scores key tile w % 8 of its chunk; waves with w % 8 < 4 form the
+    // context for dimension tile w % 8 and keep the running (max, sum, row).
+    // The halves meet in a fixed order (half 0, then half 1), leaving in the
+    // context waves of half 0 the record of every chunk taken: maximum Mo,
+    // sum lo2 and unnormalised row ao in real base-2 units (-inf, 0, 0 when
+    // there was none).
+    auto phase2 = [&](const int sq, const int r0, const int r1, float &Mo, float &lo2,
+                      f32x4_t &ao) {
+        // key chunk loads of this wave's half (keys 128 ch ..); each round's
+        // successor is requested as soon as the round's planes are written
+        const int hf = w >> 3, tl = tid & 511, wl = w & 7;
+        float kraw[2][8], vraw[2][8];
+        auto load_chunk = [&](int ch) {
+            const int j0 = 128 * ch, nk = FULL ? 128 : min(128, L - j0);
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int it = tl + 512 * n;
+                load_row8<T, FULL>(Kx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
+                load_row8<T, FULL>(Vx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
+            }
+        };
+        if (FULL || 128 * (2 * r0 + hf) < L) load_chunk(2 * r0 + hf);
+        u8 *pK = smem + 4 * kPlane * hf, *pV = pK + 2 * kPlane;
+        uint16_t *cK = reinterpret_cast<uint16_t *>(pK), *cV = reinterpret_cast<uint16_t *>(pV);
+        uint16_t *cP = reinterpret_cast<uint16_t *>(smem + kGOffP + 2 * kPlaneRow * hf);
+        const u8 *pP = reinterpret_cast<const u8 *>(cP);
+        float *xm = sXm + hf * kFK * 8, *xl = sXl + hf * kFK * 8;
+        const int trc0 = 1024 * g + (lo.tr0 ^ (32 * (wl & 3)));
+        const int trc1 = 1024 * g + (lo.tr4 ^ (32 * (wl & 3)));
+        float Mr = -__builtin_inff(), lr = 0.f;
+        f32x4_t ar = kZero4;
+        for (int r = r0; r < r1; ++r) {
+            const int ch = 2 * r + hf;
+            const int j0 = 128 * ch;
+            const bool on = FULL || j0 < L;         // uniform over the half
+            const int nk = FULL ? 128 : on ? min(128, L - j0) : 0;
+            if (on) {   // kraw, vraw hold chunk ch (requested earlier)
+                const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
+                const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
+                if (lane == 0) {
+                    sMax[4 * w + 1] = bk;
+                    sMax[4 * w + 2] = bv;
+                }
+            }
+            __syncthreads();
+            int sk = 0, sv = 0;
+            if (on) {
+                uint32_t mk = 0, mv = 0;
+#pragma unroll
+                for (int ww = 0; ww < 8; ++ww) {
+                    mk = max(mk, sMax[4 * (8 * hf + ww) + 1]);
+                    mv = max(mv, sMax[4 * (8 * hf + ww) + 2]);
+                }
+                sk = scale_shift(mk, kKVLimit);
+                sv = scale_shift(mv, kKVLimit);
+                const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int it = tl + 512 * n;
+                    float x[8], y[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        x[i] = kraw[n][i] * fk;
+                        y[i] = vraw[n][i] * fv;
+                    }
+                    const Sp8 kp = split8(x), vp = split8(y);
+                    const int o = off64(it >> 3, (it & 7) * 8);
+                    st16(cK + o, kp.h);
+                    if (!kZ) st16(cK + kPlaneE + o, kp.m);   // zero for bf16 storage, never read
+                    st16(cV + o, vp.h);
+                    if (!kZ) st16(cV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
+                }
+                if (r + 1 < r1 && (FULL || 128 * (ch + 2) < L)) load_chunk(ch + 2);   // the next round's chunk
+            }
+            __syncthreads();
+            const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
+            float sx[4];
+            if (on) {
+                const Sp8 ka = frag_at(pK, kPlane, 2048 * wl + lo.rl64), ma = frag_at(pMu, kPlaneMu, lo.rl64);
+                const Sp8 kc = frag_at(pK, kPlane, 2048 * wl + (lo.rl64 ^ 64)), mc = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
+                __builtin_amdgcn_sched_barrier(0);
+                f32x4_t a = mma3z<kZ, false>(ka, ma, kZero4);
+                a = mma3z<kZ, false>(kc, mc, a);
+                float mloc = -__builtin_inff();
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int key = 16 * wl + 4 * g + rr;
+                    sx[rr] = FULL || key < nk ? a[rr] * sscale2 : -__builtin_inff();
+                    mloc = fmaxf(mloc, sx[rr]);
+                }
+                mloc = col_max(mloc);
+                if (g == 0) xm[l16 * 8 + wl] = mloc;
+            }
+            __syncthreads();
+            float M = -__builtin_inff();
+            if (on) {
+                const float4 m0 = *reinterpret_cast<const float4 *>(xm + l16 * 8);
+                const float4 m1 = *reinterpret_cast<const float4 *>(xm + l16 * 8 + 4);
+                M = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
+                          fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
+                float p[4], ls = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    p[rr] = __builtin_amdgcn_exp2f(sx[rr] - M);
+                    ls += p[rr];
+                }
+                ls = col_sum(ls);
+                const Sp4 ps = split4(p[0], p[1], p[2], p[3]);
+                const int o = off128(l16, 16 * wl + 4 * g);
+                st8(cP + o, ps.h);
+                st8(cP + kPlaneRowE + o, ps.m);
+                if (g == 0) xl[l16 * 8 + wl] = ls;
+            }
+            __syncthreads();
+            if (on && wl < 4) {
+                const int nch = (nk + 31) >> 5;
+                f32x4_t a2[2] = {kZero4, kZero4};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (FULL || c < nch) {
+                        const Sp8 vf = colfrag8_at(pV, 4096 * c + trc0, 4096 * c + trc1);
+                        const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
+                        a2[c & 1] = mma3z<kZ, false>(vf, pf, a2[c & 1]);
+                    }
+                }
+                const float4 l0 = *reinterpret_cast<const float4 *>(xl + l16 * 8);
+                const float4 l1 = *reinterpret_cast<const float4 *>(xl + l16 * 8 + 4);
+                const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
+                const float vu = __builtin_ldexpf(1.f, sv);
+                const f32x4_t ac = (a2[0] + a2[1]) * vu;   // real units, max M
+                if (r == r0) {
+                    Mr = M;
+                    lr = den;
+                    ar = ac;
+                } else {   // fold chunk 2 + hf into the running record of chunk hf
+                    const float Mn = fmaxf(Mr, M);
+                    const float fa = __builtin_amdgcn_exp2f(Mr - Mn), fb = __builtin_amdgcn_exp2f(M - Mn);
+                    lr = lr * fa + den * fb;
+                    ar = ar * fa + ac * fb;
+                    Mr = Mn;
+                }
+            }
+            __syncthreads();   // the chunk planes are rewritten next round
+        }
+        // the two halves meet in a fixed order: half 0, then half 1
+        float *xch = reinterpret_cast<float *>(smem + kGOffP);   // [4 dim tiles][64 lanes][6]
+        if (hf == 1 && wl < 4) {
+            float *e = xch + (wl * 64 + lane) * 6;
+            e[0] = Mr; e[1] = lr; e[2] = ar[0]; e[3] = ar[1]; e[4] = ar[2]; e[5] = ar[3];
+        }
+        __syncthreads();
+        Mo = -__builtin_inff();
+        lo2 = 0.f;
+        ao = kZero4;
+        if (hf == 0 && wl < 4) {
+            const float *e = xch + (wl * 64 + lane) * 6;
+            const float M1 = e[0];
+            const float Mn = fmaxf(Mr, M1);
+            if (Mn != -__builtin_inff()) {
+                const float fa = Mr == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(Mr - Mn);
+                const float fb = M1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M1 - Mn);
+                Mo = Mn;
+                lo2 = lr * fa + e[1] * fb;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) ao[rr] = ar[rr] * fa + e[2 + rr] * fb;
+            }
+        }
+        __syncthreads();   // xch is rewritten next
+    };
+
+    if (win) {
+        // window workgroup: both window passes (each with its own Q scale) ...
+        phase3(0, 1.f);
+        // ... then the clustering workgroup's final centroids and Q scale
+        // (flag value 2 epoch + 1) and key chunks 2 and 3 of the centroid
+        // attention with them
+        const uint32_t *pv = pub + s * kPubStride;
+        unsigned long long *flag = split_flag(epoch, s);
+        wait_flag(flag, 2 * epoch + 1, epoch);
+        reinterpret_cast<uint32_t *>(sMu)[tid] = ld_pub(pv + kPubMu + tid);   // 2 kPlaneMu bytes
+        const int sqc = (int)ld_pub(pv + kPubSq);
+        __syncthreads();
+        const int hf = w >> 3, wl = w & 7;
+        float Mh, lh;
+        f32x4_t ah;
+        phase2(sqc, 1, 2, Mh, lh, ah);
+        // its record of chunks 0 and 1 and the assignment (flag value
+        // 2 epoch + 2); the records meet in chunk order, then (1 - alpha) V^cent
+        wait_flag(flag, 2 * epoch + 2, epoch);
+        if (hf == 0 && wl < 4) {
+            const uint32_t *e = pv + kPubPart + (wl * 64 + lane) * 6;
+            float rec[6];
+#pragma unroll
+            for (int i = 0; i < 6; ++i) rec[i] = __uint_as_float(ld_pub(e + i));
+            const float Mn = fmaxf(rec[0], Mh);   // chunk 0 makes it finite
+            const float fa = rec[0] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(rec[0] - Mn);
+            const float fb = Mh == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(Mh - Mn);
+            const float f = (1.0f - alpha) / (rec[1] * fa + lh * fb);
+            float v[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) v[rr] = (rec[2 + rr] * fa + ah[rr] * fb) * f;
+            *reinterpret_cast<float4 *>(sVc + l16 * kD + 16 * wl + 4 * g) =
+                make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (tid < L) sC[tid] = (int)ld_pub(pv + kPubC + tid);
+        __syncthreads();
+        // the gather and the fused rows of both passes; a wait that gave up
+        // leaves no valid V^cent: NaN rows, so that it cannot pass unnoticed
+        const bool bad = __hip_atomic_load(split_err(epoch), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == epoch;
+        const float qnan = __builtin_nanf("");
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int tok = 16 * (16 * p + w) + l16;
+            if (tok < L) {
+                float y[16];
+                stash_get(stash_at(smem, p, w), y);
+                const float f = p == 0 ? wfac0 : wfac1;
+                const float *vc = sVc + sC[tok] * kD;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {   // y[4j + rr] = Oloc^T[dim 16j + 4g + rr][query tok] / l
+                    const int d0 = 16 * j + 4 * g;
+                    const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
+                    float4 r = make_float4(fmaf(y[4 * j], f, c4.x), fmaf(y[4 * j + 1], f, c4.y),
+                                           fmaf(y[4 * j + 2], f, c4.z), fmaf(y[4 * j + 3], f, c4.w));
+                    if (bad) r = make_float4(qnan, qnan, qnan, qnan);
+                    store4<T>(out + base + (long)tok * kD + d0, r);
+                }
+            }
+        }
+        return;
+    }
+
+    int sq;     // the slice's Q scale shift
+    float fq;   // 2^-sq
     // ============================================================ 1. clustering
     float qraw[2][2][8];   // [tile u: w + 16u][c][i]
 #pragma unroll
@@ -115,14 +627,13 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         if (lane == 0) sMax[4 * w] = b;
     }
     __syncthreads();
-    int sq;
     {
         uint32_t m = 0;
 #pragma unroll
         for (int ww = 0; ww < 16; ++ww) m = max(m, sMax[4 * ww]);
         sq = scale_shift(m, kQLimit);
     }
-    const float fq = __builtin_ldexpf(1.f, -sq);
+    fq = __builtin_ldexpf(1.f, -sq);
     Sp8 qf[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -189,7 +700,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                         if (g == 0 && (FULL || tok < L)) {
                             sC[tok] = bk;
                             if (t == iters && assign) assign[s * L + tok] = bk;
-                            if (HIST) hist[((long)(t - 1) * gridDim.x + s) * L + tok] = bk;
+                            if (HIST) hist[((long)(t - 1) * (SPLIT ? S : gridDim.x) + s) * L + tok] = bk;
                         }
                     }
                 }
@@ -262,306 +773,128 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         }
     }
 
-    // ============================================================ 2. centroid attention
-    // half hf = w / 8 takes chunks hf and hf + 2 (keys 128 ch ..); wave w % 8
-    // scores key tile w % 8 of its chunk; waves with w % 8 < 4 form the
-    // context for dimension tile w % 8 and keep the running (max, sum, row)
-    {
-        // key chunk loads of this wave's half (keys 128 ch ..); each round's
-        // successor is requested as soon as the round's planes are written
-        const int hf = w >> 3, tl = tid & 511, wl = w & 7;
-        float kraw[2][8], vraw[2][8];
-        auto load_chunk = [&](int ch) {
-            const int j0 = 128 * ch, nk = FULL ? 128 : min(128, L - j0);
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                const int it = tl + 512 * n;
-                load_row8<T, FULL>(Kx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, kraw[n]);
-                load_row8<T, FULL>(Vx + kvbase + (long)j0 * kD, it >> 3, nk, (it & 7) * 8, vraw[n]);
-            }
-        };
-        load_chunk(hf);   // L > 128: both halves have a first chunk
-        u8 *pK = smem + 4 * kPlane * hf, *pV = pK + 2 * kPlane;
-        uint16_t *cK = reinterpret_cast<uint16_t *>(pK), *cV = reinterpret_cast<uint16_t *>(pV);
-        uint16_t *cP = reinterpret_cast<uint16_t *>(smem + kGOffP + 2 * kPlaneRow * hf);
-        const u8 *pP = reinterpret_cast<const u8 *>(cP);
-        float *xm = sXm + hf * kFK * 8, *xl = sXl + hf * kFK * 8;
-        const int trc0 = 1024 * g + (lo.tr0 ^ (32 * (wl & 3)));
-        const int trc1 = 1024 * g + (lo.tr4 ^ (32 * (wl & 3)));
-        float Mr = -__builtin_inff(), lr = 0.f;
-        f32x4_t ar = kZero4;
-        for (int r = 0; r < 2; ++r) {
-            const int ch = 2 * r + hf;
-            const int j0 = 128 * ch;
-            const bool on = FULL || j0 < L;         // uniform over the half
-            const int nk = FULL ? 128 : on ? min(128, L - j0) : 0;
-            if (on) {   // kraw, vraw hold chunk ch (requested earlier)
-                const uint32_t bk = wave_max_u(__float_as_uint(absmax8(kraw[1], absmax8(kraw[0], 0.f))));
-                const uint32_t bv = wave_max_u(__float_as_uint(absmax8(vraw[1], absmax8(vraw[0], 0.f))));
-                if (lane == 0) {
-                    sMax[4 * w + 1] = bk;
-                    sMax[4 * w + 2] = bv;
-                }
-            }
-            __syncthreads();
-            int sk = 0, sv = 0;
-            if (on) {
-                uint32_t mk = 0, mv = 0;
-#pragma unroll
-                for (int ww = 0; ww < 8; ++ww) {
-                    mk = max(mk, sMax[4 * (8 * hf + ww) + 1]);
-                    mv = max(mv, sMax[4 * (8 * hf + ww) + 2]);
-                }
-                sk = scale_shift(mk, kKVLimit);
-                sv = scale_shift(mv, kKVLimit);
-                const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const int it = tl + 512 * n;
-                    float x[8], y[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        x[i] = kraw[n][i] * fk;
-                        y[i] = vraw[n][i] * fv;
-                    }
-                    const Sp8 kp = split8(x), vp = split8(y);
-                    const int o = off64(it >> 3, (it & 7) * 8);
-                    st16(cK + o, kp.h);
-                    if (!kZ) st16(cK + kPlaneE + o, kp.m);   // zero for bf16 storage, never read
-                    st16(cV + o, vp.h);
-                    if (!kZ) st16(cV + kPlaneE + o, vp.m);   // zero for bf16 storage, never read
-                }
-                if (r == 0 && (FULL || 128 * (ch + 2) < L)) load_chunk(ch + 2);   // the next round's chunk
-            }
-            __syncthreads();
-            const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
-            float sx[4];
-            if (on) {
-                const Sp8 ka = frag_at(pK, kPlane, 2048 * wl + lo.rl64), ma = frag_at(pMu, kPlaneMu, lo.rl64);
-                const Sp8 kc = frag_at(pK, kPlane, 2048 * wl + (lo.rl64 ^ 64)), mc = frag_at(pMu, kPlaneMu, lo.rl64 ^ 64);
-                __builtin_amdgcn_sched_barrier(0);
-                f32x4_t a = mma3z<kZ, false>(ka, ma, kZero4);
-                a = mma3z<kZ, false>(kc, mc, a);
-                float mloc = -__builtin_inff();
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int key = 16 * wl + 4 * g + rr;
-                    sx[rr] = FULL || key < nk ? a[rr] * sscale2 : -__builtin_inff();
-                    mloc = fmaxf(mloc, sx[rr]);
-                }
-                mloc = col_max(mloc);
-                if (g == 0) xm[l16 * 8 + wl] = mloc;
-            }
-            __syncthreads();
-            float M = -__builtin_inff();
-            if (on) {
-                const float4 m0 = *reinterpret_cast<const float4 *>(xm + l16 * 8);
-                const float4 m1 = *reinterpret_cast<const float4 *>(xm + l16 * 8 + 4);
-                M = fmaxf(fmaxf(fmaxf(m0.x, m0.y), fmaxf(m0.z, m0.w)),
-                          fmaxf(fmaxf(m1.x, m1.y), fmaxf(m1.z, m1.w)));
-                float p[4], ls = 0.f;
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    p[rr] = __builtin_amdgcn_exp2f(sx[rr] - M);
-                    ls += p[rr];
-                }
-                ls = col_sum(ls);
-                const Sp4 ps = split4(p[0], p[1], p[2], p[3]);
-                const int o = off128(l16, 16 * wl + 4 * g);
-                st8(cP + o, ps.h);
-                st8(cP + kPlaneRowE + o, ps.m);
-                if (g == 0) xl[l16 * 8 + wl] = ls;
-            }
-            __syncthreads();
-            if (on && wl < 4) {
-                const int nch = (nk + 31) >> 5;
-                f32x4_t a2[2] = {kZero4, kZero4};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (FULL || c < nch) {
-                        const Sp8 vf = colfrag8_at(pV, 4096 * c + trc0, 4096 * c + trc1);
-                        const Sp8 pf = frag_at(pP, kPlaneRow, lo.rl128 ^ (64 * c));
-                        a2[c & 1] = mma3z<kZ, false>(vf, pf, a2[c & 1]);
-                    }
-                }
-                const float4 l0 = *reinterpret_cast<const float4 *>(xl + l16 * 8);
-                const float4 l1 = *reinterpret_cast<const float4 *>(xl + l16 * 8 + 4);
-                const float den = ((((((l0.x + l0.y) + l0.z) + l0.w) + l1.x) + l1.y) + l1.z) + l1.w;
-                const float vu = __builtin_ldexpf(1.f, sv);
-                const f32x4_t ac = (a2[0] + a2[1]) * vu;   // real units, max M
-                if (r == 0) {
-                    Mr = M;
-                    lr = den;
-                    ar = ac;
-                } else {   // fold chunk 2 + hf into the running record of chunk hf
-                    const float Mn = fmaxf(Mr, M);
-                    const float fa = __builtin_amdgcn_exp2f(Mr - Mn), fb = __builtin_amdgcn_exp2f(M - Mn);
-                    lr = lr * fa + den * fb;
-                    ar = ar * fa + ac * fb;
-                    Mr = Mn;
-                }
-            }
-            __syncthreads();   // the chunk planes are rewritten next round
-        }
-        // the two halves meet in a fixed order: half 0, then half 1
-        float *xch = reinterpret_cast<float *>(smem + kGOffP);   // [4 dim tiles][64 lanes][6]
-        if (hf == 1 && wl < 4) {
-            float *e = xch + (wl * 64 + lane) * 6;
-            e[0] = Mr; e[1] = lr; e[2] = ar[0]; e[3] = ar[1]; e[4] = ar[2]; e[5] = ar[3];
-        }
-        __syncthreads();
-        if (hf == 0 && wl < 4) {
-            const float *e = xch + (wl * 64 + lane) * 6;
-            const float M1 = e[0];
-            const float Mn = fmaxf(Mr, M1);
-            const float fa = __builtin_amdgcn_exp2f(Mr - Mn);
-            const float fb = M1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(M1 - Mn);
-            const float den = lr * fa + e[1] * fb;
-            const float f = (1.0f - alpha) / den;
+    const int hf = w >> 3, wl = w & 7;   // the halves and context waves of phase 2
+    if (!SPLIT) {
+        float Mh, lh;
+        f32x4_t ah;
+        phase2(sq, 0, 2, Mh, lh, ah);
+        if (hf == 0 && wl < 4) {   // (1 - alpha) V^cent
+            const float f = (1.0f - alpha) / lh;
             float v[4];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) v[rr] = (ar[rr] * fa + e[2 + rr] * fb) * f;
+            for (int rr = 0; rr < 4; ++rr) v[rr] = ah[rr] * f;
             *reinterpret_cast<float4 *>(sVc + l16 * kD + 16 * wl + 4 * g) =
                 make_float4(v[0], v[1], v[2], v[3]);
         }
         __syncthreads();
+        phase3(sq, fq);
+        return;
     }
-
-    // ============================================================ 3. local window + output
-    {
-        uint16_t *tK = reinterpret_cast<uint16_t *>(smem), *tV = tK + kGPlane3;   // h, m pairs
-        const u8 *pK3 = smem, *pV3 = smem + 2 * kGPlane3;
-        constexpr int kItems = (kGRows3 * kD / 8 + kGThreads - 1) / kGThreads;   // 3
-        KeyBits kb;
+    // split form, clustering workgroup: the final centroid planes for the
+    // window workgroup's half of the centroid attention (flag word 0) ...
+    uint32_t *pv = pub + s * kPubStride;
+    unsigned long long *flag = split_flag(epoch, s);
+    __hip_atomic_store(pv + kPubMu + tid, reinterpret_cast<const uint32_t *>(sMu)[tid],
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // 2 kPlaneMu bytes
+    if (tid == 0)
+        __hip_atomic_store(pv + kPubSq, (uint32_t)sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store complete ...
+    __syncthreads();
+    if (tid == 0)   // ... before the flag goes up
+        __hip_atomic_store(flag, 2 * epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ... then its own half (key chunks 0 and 1), whose record goes out with
+    // the assignment (flag word 1)
+    float Mh, lh;
+    f32x4_t ah;
+    phase2(sq, 0, 1, Mh, lh, ah);
+    if (hf == 0 && wl < 4) {
+        uint32_t *e = pv + kPubPart + (wl * 64 + lane) * 6;
+        const float rec[6] = {Mh, lh, ah[0], ah[1], ah[2], ah[3]};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) kb.w[k] = ~0u;
-        for (int p = 0; p < 2; ++p) {
-            const int q0 = 256 * p;                 // first query of the pass
-            if (q0 >= L) break;                     // uniform
-            const int r0 = p == 0 ? 0 : q0 - 16;    // first staged row
-            const int Lp = min(L, q0 + 272) - r0;   // staged rows holding keys
-            const int NTp = (Lp + 15) >> 4;
-            float kraw[kItems][8], vraw[kItems][8];
-#pragma unroll
-            for (int n = 0; n < kItems; ++n) {
-                const int it = tid + kGThreads * n;
-                if (it < kGRows3 * kD / 8) {
-                    load_row8<T, false>(Kx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, kraw[n]);
-                    load_row8<T, false>(Vx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, vraw[n]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) kraw[n][i] = vraw[n][i] = 0.f;
-                }
-            }
-            {
-                float mk = 0.f, mv = 0.f;
-#pragma unroll
-                for (int n = 0; n < kItems; ++n) {
-                    mk = absmax8(kraw[n], mk);
-                    mv = absmax8(vraw[n], mv);
-                }
-                const uint32_t bk = wave_max_u(__float_as_uint(mk));
-                const uint32_t bv = wave_max_u(__float_as_uint(mv));
-                if (lane == 0) {
-                    sMax[4 * w + 1] = bk;
-                    sMax[4 * w + 2] = bv;
-                }
-            }
-            __syncthreads();
-            uint32_t mk = 0, mv = 0;
-#pragma unroll
-            for (int ww = 0; ww < 16; ++ww) {
-                mk = max(mk, sMax[4 * ww + 1]);
-                mv = max(mv, sMax[4 * ww + 2]);
-            }
-            const int sk = scale_shift(mk, kKVLimit), sv = scale_shift(mv, kKVLimit);
-            // the wave's query rows of this pass, requested before the planes
-            // are built so that their latency passes during that work
-            const int tile = 16 * p + w;   // the wave's query tile of this pass
-            float qx[2][8];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) load_row8<T, false>(Qs, 16 * tile + l16, L, 32 * c + 8 * g, qx[c]);
-            {
-                const float fk = __builtin_ldexpf(1.f, -sk), fv = __builtin_ldexpf(1.f, -sv);
-#pragma unroll
-                for (int n = 0; n < kItems; ++n) {
-                    const int it = tid + kGThreads * n;
-                    if (it < kGRows3 * kD / 8) {
-                        float x[8], y[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            x[i] = kraw[n][i] * fk;
-                            y[i] = vraw[n][i] * fv;
-                        }
-                        const Sp8 kp = split8(x), vp = split8(y);
-                        const int o = off64(it >> 3, (it & 7) * 8);
-                        st16(tK + o, kp.h);
-                        if (!kZ) st16(tK + kGPlane3 / 2 + o, kp.m);   // zero for bf16 storage, never read
-                        st16(tV + o, vp.h);
-                        if (!kZ) st16(tV + kGPlane3 / 2 + o, vp.m);   // zero for bf16 storage, never read
-                    }
-                }
-            }
-            __syncthreads();
-            if (tile < NT) {
-                const int qt = (16 * tile - r0) >> 4;
-                const float sscale2 = __builtin_ldexpf(0.125f, sq + sk) * 1.4426950408889634f;
-                // the tile's Q fragments again (cheaper than keeping them live
-                // through the centroid attention): the same values as in phase 1
-                Sp8 qp[2];
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) qx[c][i] *= fq;
-                    qp[c] = split8<true>(qx[c]);
-                }
-                f32x4_t o[4];
-                float lsum;
-                local_narrow<false, false, KeyBits, kGPlane3, kZ>(pK3, pV3, qp, qt, NTp, Lp, rad,
-                                                            sscale2, l16, g, lo.rl64, trv, kb, o,
-                                                            lsum);
-                const int tok = 16 * tile + l16;
-                if (tok < L) {
-                    const float f = alpha * __builtin_ldexpf(1.f, sv) * __builtin_amdgcn_rcpf(lsum);
-                    const float *vc = sVc + sC[tok] * kD;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {   // o[j][rr] = Oloc^T[dim 16j + 4g + rr][query tok]
-                        const int d0 = 16 * j + 4 * g;
-                        const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
-                        store4<T>(out + base + (long)tok * kD + d0,
-                                  make_float4(fmaf(o[j][0], f, c4.x), fmaf(o[j][1], f, c4.y),
-                                              fmaf(o[j][2], f, c4.z), fmaf(o[j][3], f, c4.w)));
-                    }
-                }
-            }
-            __syncthreads();   // the planes are rewritten by the next pass
-        }
+        for (int i = 0; i < 6; ++i)
+            __hip_atomic_store(e + i, __float_as_uint(rec[i]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid < L)
+        __hip_atomic_store(pv + kPubC + tid, (uint32_t)sC[tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_store(flag, 2 * epoch + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Clears the flags of launch e's ring for S slices (before a launch that a
+// graph records, whose replays repeat the same launch number).
+__global__ void fused512_clear_flags_kernel(unsigned long long e, int S) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < S) *split_flag(e, i) = 0ull;
+    if (i == 0) *split_err(e) = 0ull;
+}
+
+// launch numbers of the split form, per device
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned long long> g_split_launches[kMaxDevices];
 
 bool fused512_supported(int L, int Kc, int r) {
     return L > 128 && L <= kGL && Kc >= 1 && Kc <= kFK && r >= 0 && r <= 16;
 }
 
+size_t fused512_split_workspace_bytes(long S) {
+    return ((sizeof(uint32_t) * (size_t)S * kPubStride + 255) / 256) * 256;
+}
+
+int fused512_split_max_slices() { return kMaxSplitSlices; }
+
 hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                            int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
-                           int G, void *out, int32_t *assign, hipStream_t st, int32_t *hist) {
-    const dim3 grid((unsigned)S), block(kGThreads);
-#define CA_F512_LAUNCH(TT, HH, F)                                                                \
-    hipLaunchKernelGGL((cluster_attn_fused512_kernel<TT, HH, F>), grid, block, 0, st,            \
+                           int G, void *out, int32_t *assign, hipStream_t st, int32_t *hist,
+                           void *split_ws) {
+    uint32_t *pub = nullptr;
+    unsigned long long epoch = 0;
+    const bool split = split_ws != nullptr;
+    if (split) {
+        if (S > kMaxSplitSlices || dt != CA_BF16) return hipErrorInvalidValue;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+        pub = static_cast<uint32_t *>(split_ws);
+        epoch = g_split_launches[dev].fetch_add(1, std::memory_order_relaxed) + 1;
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(st, &cap);
+        if (e != hipSuccess) return e;
+        if (cap != hipStreamCaptureStatusNone)
+            hipLaunchKernelGGL(fused512_clear_flags_kernel, dim3((unsigned)((S + 255) / 256)),
+                               dim3(256), 0, st, epoch, S);
+    }
+    const dim3 grid((unsigned)(split ? 2 * S : S)), block(kGThreads);
+#define CA_F512_LAUNCH(TT, HH, F, SP)                                                            \
+    hipLaunchKernelGGL((cluster_attn_fused512_kernel<TT, HH, F, SP>), grid, block, 0, st,        \
                        static_cast<const TT *>(Q), static_cast<const TT *>(K),                   \
                        static_cast<const TT *>(V), L, Kc, iters, r, alpha, init_step, H, G,      \
-                       static_cast<TT *>(out), assign, hist)
+                       static_cast<TT *>(out), assign, hist, S, pub, epoch)
+#define CA_F512_LAUNCH_S(TT, HH, F)                                                              \
+    do {                                                                                         \
+        if (split) CA_F512_LAUNCH(TT, HH, F, true); else CA_F512_LAUNCH(TT, HH, F, false);       \
+    } while (0)
 #define CA_F512_LAUNCH_F(TT, HH)                                                                 \
     do {                                                                                         \
-        if (L == kGL) CA_F512_LAUNCH(TT, HH, true); else CA_F512_LAUNCH(TT, HH, false);          \
+        if (L == kGL) CA_F512_LAUNCH_S(TT, HH, true); else CA_F512_LAUNCH_S(TT, HH, false);      \
+    } while (0)
+#define CA_F512_LAUNCH_F2(TT, HH)                                                                \
+    do {                                                                                         \
+        if (L == kGL) CA_F512_LAUNCH(TT, HH, true, false); else CA_F512_LAUNCH(TT, HH, false, false); \
     } while (0)
     if (dt == CA_BF16) {
         if (hist) CA_F512_LAUNCH_F(bf16_t, true); else CA_F512_LAUNCH_F(bf16_t, false);
-    } else {
-        if (hist) CA_F512_LAUNCH_F(float, true); else CA_F512_LAUNCH_F(float, false);
+    } else {   // the split form is for bf16 storage only
+        if (split) return hipErrorInvalidValue;
+        if (hist) CA_F512_LAUNCH_F2(float, true); else CA_F512_LAUNCH_F2(float, false);
     }
+#undef CA_F512_LAUNCH_F2
 #undef CA_F512_LAUNCH_F
+#undef CA_F512_LAUNCH_S
 #undef CA_F512_LAUNCH
     return hipGetLastError();
 }

@@ -70,11 +70,17 @@ hipError_t launch_kmeans_scores(const void *Q, const float *mu, int S, int L, in
 
 // The whole forward in one launch per slice for 128 < L <= 512, K <= 16,
 // radius <= 16, without a key-padding mask (fused512.hip); assign nullable.
+// split_ws (256-byte aligned, fused512_split_workspace_bytes(S) bytes): the
+// split form, a second workgroup per slice running the window branch beside
+// the clustering (2 S workgroups, one per CU: only for 2 S <= the CU count),
+// preceded by a small launch that clears its flags.
 bool fused512_supported(int L, int Kc, int r);
+size_t fused512_split_workspace_bytes(long S);
+int fused512_split_max_slices();   // largest S of the split form
 hipError_t launch_fused512(const void *Q, const void *K, const void *V, int S, int L, int Kc,
                            int iters, int r, float alpha, int init_step, ca_dtype_t dt, int H,
                            int G, void *out, int32_t *assign, hipStream_t st,
-                           int32_t *hist = nullptr);
+                           int32_t *hist = nullptr, void *split_ws = nullptr);
 
 // The whole forward in one launch with each slice split over ns co-resident
 // workgroups of at most 480 tokens (seg.hip): K <= 64, radius <= 16, no mask

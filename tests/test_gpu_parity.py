@@ -51,7 +51,9 @@ def run_iters(x: gen.AttnInputs, path: int):
 
 
 def check(x: gen.AttnInputs, path: int, tol=None, record: str = None):
-    plan = _b().cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, path=path)
+    b = _b()
+    plan = b.cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, path=path,
+                               dtype=b.CA_BF16 if x.dtype == gen.BF16 else b.CA_F32)
     _say(f"[parity] {x.name or 'case'} B={x.B} H={x.H} L={x.L} K={x.nclust} I={x.iters} "
          f"W={x.W} a={x.alpha} {x.dtype} seed={x.seed} path={path} plan={plan}")
     assigns, out, _ = run_iters(x, path)
@@ -155,6 +157,53 @@ def test_single_launch_long(case):
 
 def test_single_launch_long_full_batch():
     check(gen.workload("bf16_l512"), 1)
+
+
+# the split form of that launch (bf16 storage, at most half the CUs' worth of
+# slices): a window workgroup per slice beside its clustering workgroup, taken
+# by the auto path
+SPLIT512 = [  # B, H, L, nclust, iters, W, alpha, blobs
+    (1, 1, 129, 16, 3, 32, 0.5, 8),               # one slice, one pass, a one-key second chunk
+    (1, 2, 256, 16, 3, 32, 0.5, 8),               # exactly one pass
+    (1, 3, 257, 16, 3, 32, 0.5, 8),               # a second pass of one query
+    (2, 3, 300, 7, 4, 17, 0.3, 6),                # odd W, K not dividing L, ragged pass
+    (1, 2, 512, 16, 3, 33, 0.5, 16),              # radius 16, two full passes
+    (1, 2, 272, 4, 4, 0, 0.3, 4),                 # W = 0
+    (2, 2, 200, 16, 1, 20, 1.0, 6),               # one iteration, pure local branch
+    (1, 2, 450, 16, 3, 32, 0.0, 16),              # pure centroid branch
+    (8, 16, 512, 16, 3, 32, 0.5, 16),             # 128 slices: every CU of the grid busy
+]
+
+
+@pytest.mark.parametrize("case", SPLIT512)
+def test_single_launch_split(case):
+    B, H, L, nclust, iters, W, alpha, blobs = case
+    b = _b()
+    plan = b.cluster_attn_plan(B, H, L, nclust, W, dtype=b.CA_BF16)
+    if not plan.startswith("fused512 split"):
+        pytest.skip(f"this device's CU count gives the plan {plan!r}")
+    x = gen.make_inputs(B, H, L, 64, nclust=nclust, iters=iters, W=W, alpha=alpha,
+                        dtype=gen.BF16, seed=3500 + L + W, blobs=blobs, name="split512")
+    check(x, 0)
+
+
+def test_single_launch_split_full_batch_and_repeats():
+    """The bf16 L = 512 workload through the split form, three calls in a row
+    on the same workspace: identical outputs (the flags are cleared per call)."""
+    x = gen.workload("bf16_l512")
+    b = _b()
+    plan = b.cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, dtype=b.CA_BF16)
+    if not plan.startswith("fused512 split"):
+        pytest.skip(f"this device's CU count gives the plan {plan!r}")
+    check(x, 0)
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    ws = torch.empty(b.cluster_attn_workspace_size(x.B, x.H, x.L, 64, x.nclust, b.CA_BF16) + 256,
+                     dtype=torch.uint8, device="cuda")
+    runs = [b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, workspace=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, c in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(c, runs[0][1])
 
 
 # the segmented single launch (each slice over several co-resident

@@ -68,7 +68,8 @@ def distance_errors(q_dev, Q64, hist: np.ndarray, K: int):
 def p0_record(name, q_dev, k_dev, v_dev, Q64, K64, V64, nclust, iters, W, alpha, dtype, extra):
     b = _b()
     B, H, L, _ = Q64.shape
-    plan = b.cluster_attn_plan(B, H, L, nclust, W)
+    plan = b.cluster_attn_plan(B, H, L, nclust, W,
+                               dtype=b.CA_BF16 if dtype == gen.BF16 else b.CA_F32)
     print(f"[report] {name}: B={B} H={H} L={L} K={nclust} I={iters} W={W} {dtype} plan={plan}",
           flush=True)
     hist = torch.empty((iters, B, H, L), dtype=torch.int32, device="cuda")

@@ -39,6 +39,8 @@ PATHS = [
     ("fused kept centroids", 0, 1, 3, 128, 16, 3, 32, "f32", 6, 2, False),
     ("fused512", 1, 2, 3, 300, 16, 3, 32, "f32", 12, 0, False),
     ("fused512 bf16", 1, 1, 2, 512, 16, 4, 33, "bf16", 16, 0, False),
+    ("fused512 split (auto, 96 slices)", 0, 8, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
+    ("fused512 split, ragged (auto)", 0, 1, 3, 300, 12, 4, 20, "bf16", 10, 0, False),
     ("kmeans_slice + key ranges (96 slices)", 2, 8, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
     ("kmeans_slice + key ranges, ragged", 2, 8, 12, 400, 12, 3, 32, "f32", 12, 0, False),
     ("kmeans_slice (132 slices)", 2, 11, 12, 512, 16, 3, 32, "bf16", 16, 0, False),
