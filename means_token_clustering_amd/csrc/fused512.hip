@@ -223,6 +223,20 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         f32x4_t o1[4] = {kZero4, kZero4, kZero4, kZero4};
         float il1 = 0.f;
         // one window pass (p = 0: queries 0 .. 255, 1: 256 ..); false when L has no such queries
+        // split form: the second pass's K and V rows, requested during the
+        // first pass's window products and kept as raw bf16 (16 bytes per item)
+        u32x4_t kpre[kItems], vpre[kItems];
+        auto prefetch1 = [&]() {
+            const int r0 = 240, Lp = min(L, 528) - r0;
+#pragma unroll
+            for (int n = 0; n < kItems; ++n) {
+                const int it = tid + kGThreads * n;
+                const int row = it >> 3, rc = row < Lp ? row : Lp - 1;
+                const long off = kvbase + (long)(r0 + rc) * kD + (it & 7) * 8;
+                kpre[n] = *reinterpret_cast<const u32x4_t *>(Kx + off);
+                vpre[n] = *reinterpret_cast<const u32x4_t *>(Vx + off);
+            }
+        };
         auto pass = [&](const int p) -> bool {
             const int q0 = 256 * p;                 // first query of the pass
             if (q0 >= L) return false;              // uniform
@@ -234,8 +248,20 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
             for (int n = 0; n < kItems; ++n) {
                 const int it = tid + kGThreads * n;
                 if (it < kGRows3 * kD / 8) {
-                    load_row8<T, false>(Kx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, kraw[n]);
-                    load_row8<T, false>(Vx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, vraw[n]);
+                    if (SPLIT && p == 1) {   // prefetched: rows past the slice become zeros
+                        const bool in = (it >> 3) < Lp;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t ku = in ? kpre[n][i] : 0u, vu = in ? vpre[n][i] : 0u;
+                            kraw[n][2 * i] = __uint_as_float(ku << 16);
+                            kraw[n][2 * i + 1] = __uint_as_float(ku & 0xffff0000u);
+                            vraw[n][2 * i] = __uint_as_float(vu << 16);
+                            vraw[n][2 * i + 1] = __uint_as_float(vu & 0xffff0000u);
+                        }
+                    } else {
+                        load_row8<T, false>(Kx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, kraw[n]);
+                        load_row8<T, false>(Vx + kvbase + (long)r0 * kD, it >> 3, Lp, (it & 7) * 8, vraw[n]);
+                    }
                 } else {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) kraw[n][i] = vraw[n][i] = 0.f;
@@ -309,6 +335,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 }
             }
             __syncthreads();
+            if (SPLIT && p == 0 && L > 256) prefetch1();
             if (tile < NT) {
                 const int qt = (16 * tile - r0) >> 4;
                 const float sscale2 = __builtin_ldexpf(0.125f, sqp + sk) * 1.4426950408889634f;
@@ -538,21 +565,22 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
     if (win) {
         // window workgroup: both window passes (each with its own Q scale) ...
         phase3(0, 1.f);
-        // ... then the clustering workgroup's final centroids and Q scale
-        // (flag value 2 epoch + 1) and key chunks 2 and 3 of the centroid
-        // attention with them
+        // ... then the clustering workgroup's final centroids, Q scale and
+        // assignment (flag value 2 epoch + 1) and key chunks 2 and 3 of the
+        // centroid attention with them
         const uint32_t *pv = pub + s * kPubStride;
         unsigned long long *flag = split_flag(epoch, s);
         wait_flag(flag, 2 * epoch + 1, epoch);
         reinterpret_cast<uint32_t *>(sMu)[tid] = ld_pub(pv + kPubMu + tid);   // 2 kPlaneMu bytes
+        if (tid < L) sC[tid] = (int)ld_pub(pv + kPubC + tid);
         const int sqc = (int)ld_pub(pv + kPubSq);
         __syncthreads();
         const int hf = w >> 3, wl = w & 7;
         float Mh, lh;
         f32x4_t ah;
         phase2(sqc, 1, 2, Mh, lh, ah);
-        // its record of chunks 0 and 1 and the assignment (flag value
-        // 2 epoch + 2); the records meet in chunk order, then (1 - alpha) V^cent
+        // its record of chunks 0 and 1 (flag value 2 epoch + 2); the records
+        // meet in chunk order, then (1 - alpha) V^cent
         wait_flag(flag, 2 * epoch + 2, epoch);
         if (hf == 0 && wl < 4) {
             const uint32_t *e = pv + kPubPart + (wl * 64 + lane) * 6;
@@ -569,16 +597,21 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
             *reinterpret_cast<float4 *>(sVc + l16 * kD + 16 * wl + 4 * g) =
                 make_float4(v[0], v[1], v[2], v[3]);
         }
-        if (tid < L) sC[tid] = (int)ld_pub(pv + kPubC + tid);
         __syncthreads();
         // the gather and the fused rows of both passes; a wait that gave up
         // leaves no valid V^cent: NaN rows, so that it cannot pass unnoticed
         const bool bad = __hip_atomic_load(split_err(epoch), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT) == epoch;
         const float qnan = __builtin_nanf("");
+        // each wave's 16 rows go through a 2 KB LDS tile (16-byte chunks
+        // XOR-swizzled by the row; bytes [0, 16K) and [64K, 80K), which phase 2
+        // no longer needs) so that every store writes 64 x 16 bytes of whole rows
+        u8 *stg = smem + (w < 8 ? 0 : 64 * 1024) + 2048 * (w & 7);
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int tok = 16 * (16 * p + w) + l16;
+            const int tile = 16 * p + w;
+            if (16 * tile >= L) continue;   // uniform over the wave
+            const int tok = 16 * tile + l16;
             if (tok < L) {
                 float y[16];
                 stash_get(stash_at(smem, p, w), y);
@@ -588,12 +621,26 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
                 for (int j = 0; j < 4; ++j) {   // y[4j + rr] = Oloc^T[dim 16j + 4g + rr][query tok] / l
                     const int d0 = 16 * j + 4 * g;
                     const float4 c4 = *reinterpret_cast<const float4 *>(vc + d0);
-                    float4 r = make_float4(fmaf(y[4 * j], f, c4.x), fmaf(y[4 * j + 1], f, c4.y),
-                                           fmaf(y[4 * j + 2], f, c4.z), fmaf(y[4 * j + 3], f, c4.w));
-                    if (bad) r = make_float4(qnan, qnan, qnan, qnan);
-                    store4<T>(out + base + (long)tok * kD + d0, r);
+                    float v0 = fmaf(y[4 * j], f, c4.x), v1 = fmaf(y[4 * j + 1], f, c4.y);
+                    float v2 = fmaf(y[4 * j + 2], f, c4.z), v3 = fmaf(y[4 * j + 3], f, c4.w);
+                    if (bad) v0 = v1 = v2 = v3 = qnan;
+                    const int byte = 2 * d0;   // within the 128-byte row
+                    *reinterpret_cast<u32x2_t *>(stg + 128 * l16 + (((byte >> 4) ^ (l16 & 7)) << 4) +
+                                                 (byte & 15)) =
+                        u32x2_t{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                                (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            u8 *dst = reinterpret_cast<u8 *>(out + base + (long)16 * tile * kD);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {   // 128 chunks of 16 bytes, 8 per row
+                const int flat = 64 * i + lane, row = flat >> 3, c = flat & 7;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(stg + 128 * row + ((c ^ (row & 7)) << 4));
+                if (16 * tile + row < L)
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(dst + 16 * flat));
+            }
+            __builtin_amdgcn_wave_barrier();   // the tile is rewritten by the next pass
         }
         return;
     }
@@ -790,20 +837,23 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
         phase3(sq, fq);
         return;
     }
-    // split form, clustering workgroup: the final centroid planes for the
-    // window workgroup's half of the centroid attention (flag word 0) ...
+    // split form, clustering workgroup: the final centroid planes, Q scale and
+    // assignment for the window workgroup (flag value 2 epoch + 1) ...
     uint32_t *pv = pub + s * kPubStride;
     unsigned long long *flag = split_flag(epoch, s);
     __hip_atomic_store(pv + kPubMu + tid, reinterpret_cast<const uint32_t *>(sMu)[tid],
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // 2 kPlaneMu bytes
     if (tid == 0)
         __hip_atomic_store(pv + kPubSq, (uint32_t)sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < L)
+        __hip_atomic_store(pv + kPubC + tid, (uint32_t)sC[tid], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store complete ...
     __syncthreads();
     if (tid == 0)   // ... before the flag goes up
         __hip_atomic_store(flag, 2 * epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // ... then its own half (key chunks 0 and 1), whose record goes out with
-    // the assignment (flag word 1)
+    // ... then its own half (key chunks 0 and 1), whose record goes out next
+    // (flag value 2 epoch + 2)
     float Mh, lh;
     f32x4_t ah;
     phase2(sq, 0, 1, Mh, lh, ah);
@@ -815,9 +865,6 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_kernel(
             __hip_atomic_store(e + i, __float_as_uint(rec[i]), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid < L)
-        __hip_atomic_store(pv + kPubC + tid, (uint32_t)sC[tid], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0)
