@@ -1278,6 +1278,9 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_split_kern
                     }
                 }
             }
+            // the rows of key chunk w / 8 (phase 2's round 0), in flight
+            // during the last update
+            if (t == iters) load_chunk(w >> 3);
             __syncthreads();
             f32x4_t sh = kZero4, sm = kZero4, cnt = kZero4;
 #pragma unroll
@@ -1366,7 +1369,7 @@ __global__ __launch_bounds__(kGThreads, 1) void cluster_attn_fused512_split_kern
     // (flag value 2 epoch + 2)
     float Mh, lh;
     f32x4_t ah;
-    phase2(sq, 0, 1, false, Mh, lh, ah);
+    phase2(sq, 0, 1, true, Mh, lh, ah);
     if (hf == 0 && wl < 4) {
         uint32_t *e = pv + kPubPart + (wl * 64 + lane) * 6;
         const float rec[6] = {Mh, lh, ah[0], ah[1], ah[2], ah[3]};
