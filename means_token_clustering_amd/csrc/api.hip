@@ -679,6 +679,13 @@ ca_status_t cluster_attn_backward(const void *Q, const void *K, const void *V, c
     a.dkc = reinterpret_cast<float *>(ws + lay.dkc);
     a.dvl = reinterpret_cast<float *>(ws + lay.dvl);
     if (bwd_fused_supported(L, Kc, H / Hkv)) {   // two launches per slice, then dalpha
+        // measured, 384 slices on 256 CUs: 56.6 -> 54.3 us with the solo
+        // workgroups delayed (same-box A/B)
+        const int cus = device_cus();
+        if (cus > 0 && S > cus && S < 2 * cus) {
+            a.solo_lo = (int)(S - cus);
+            a.solo_hi = cus;
+        }
         CA_TRY(launch_backward_fused(a, dt, stream));
         return hip_status(launch_bwd_sum(a.dal, S, dalpha, stream));
     }
@@ -718,7 +725,7 @@ ca_status_t cluster_attn_exact_forward(const void *Q, const void *K, const void 
     // single launch when the future-key exclusion equals the listing's fill
     if (exact_fused_supported(L, Nk) && (!causal || !k_valid || k_valid == q_valid))
         return hip_status(launch_exact_fused(Q, K, V, B * H, L, causal != 0, dt, q_valid, k_valid,
-                                             H, H / Hkv, out, stream));
+                                             H, H / Hkv, out, stream, device_cus()));
     return hip_status(launch_exact_attention(Q, K, V, B * H, L, Nk, causal != 0, dt, q_valid,
                                              k_valid, H, H / Hkv, out, stream));
 }

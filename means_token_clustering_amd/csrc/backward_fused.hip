@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
     const float *__restrict__ dmu, const int32_t *__restrict__ counts,
     const float *__restrict__ dKc, const float *__restrict__ dVc, int S, int L, int Kc,
     int radius, float alpha, int H, T *__restrict__ dQ, T *__restrict__ dK, T *__restrict__ dV,
-    float *__restrict__ dal) {
+    float *__restrict__ dal, int solo_lo, int solo_hi) {
     __shared__ __align__(16) unsigned char smem[kBLds];
     uint16_t *sA = reinterpret_cast<uint16_t *>(smem);            // K, then Q planes
     uint16_t *sB = reinterpret_cast<uint16_t *>(smem + kBOffB);   // V, then g planes
@@ -60,6 +60,10 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_local_fused_kernel(
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const long slice = blockIdx.x;
     if (slice >= S) return;
+    // a workgroup alone on its CU starts about 2 us late, so that the loads of
+    // the CUs holding two slices are served first (the launcher names these
+    // workgroups)
+    if ((int)blockIdx.x >= solo_lo && (int)blockIdx.x < solo_hi) __builtin_amdgcn_s_sleep(64);
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const bool tile_on = FULL || w < NT;
     const int tok = 16 * w + l16;                // query (first pass) and key (second) of the lane
@@ -406,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
     const T *__restrict__ dO, const int32_t *__restrict__ assign,
     const uint8_t *__restrict__ valid, int S, int L, int Kc, float alpha, int H,
     float *__restrict__ dKc, float *__restrict__ dVc, float *__restrict__ dmu,
-    int32_t *__restrict__ counts, float *__restrict__ dalc) {
+    int32_t *__restrict__ counts, float *__restrict__ dalc, int solo_lo, int solo_hi) {
     __shared__ __align__(16) unsigned char smem[kCLds];
     uint16_t *sA = reinterpret_cast<uint16_t *>(smem);               // Q, then K planes
     uint16_t *sB = reinterpret_cast<uint16_t *>(smem + kBOffB);      // g, then V planes
@@ -424,6 +428,10 @@ __global__ __launch_bounds__(kThreads, 4) void bwd_centroid_fused_kernel(
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const long slice = blockIdx.x;
     if (slice >= S) return;
+    // a workgroup alone on its CU starts about 2 us late, so that the loads of
+    // the CUs holding two slices are served first (the launcher names these
+    // workgroups)
+    if ((int)blockIdx.x >= solo_lo && (int)blockIdx.x < solo_hi) __builtin_amdgcn_s_sleep(64);
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;   // the lane's key in the centroid phase
     const bool tok_in = FULL || tok < L;
@@ -744,12 +752,12 @@ static hipError_t bwd_fused_launch_t(const BwdArgs &a, hipStream_t st) {
     int32_t *counts = const_cast<int32_t *>(a.counts);
     hipLaunchKernelGGL((bwd_centroid_fused_kernel<T, FULL, MASKED>), dim3((unsigned)S),
                        dim3(kThreads), 0, st, q, k, v, go, a.assign, a.valid, S, a.L, a.Kc, a.alpha,
-                       a.H, a.dkc, a.dvl, a.dmu, counts, dalc);
+                       a.H, a.dkc, a.dvl, a.dmu, counts, dalc, a.solo_lo, a.solo_hi);
     hipLaunchKernelGGL((bwd_local_fused_kernel<T, FULL, MASKED>), dim3((unsigned)S),
                        dim3(kThreads), 0, st, q, k, v, go, a.assign, a.valid, dalc, a.dmu,
                        a.counts, a.dkc, a.dvl, S, a.L, a.Kc, a.r, a.alpha, a.H,
                        static_cast<T *>(a.dQ), static_cast<T *>(a.dK), static_cast<T *>(a.dV),
-                       a.dal);
+                       a.dal, a.solo_lo, a.solo_hi);
     return hipGetLastError();
 }
 

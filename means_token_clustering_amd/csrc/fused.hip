@@ -611,7 +611,7 @@ template <typename T, bool FULL, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(kThreads, 4) void exact_fused_kernel(
     const T *__restrict__ Q, const T *__restrict__ Kx, const T *__restrict__ Vx, int S, int L,
     const uint8_t *__restrict__ qvalid, const uint8_t *__restrict__ kvalid, int H, int G,
-    T *__restrict__ out) {
+    T *__restrict__ out, int solo_lo, int solo_hi) {
     __shared__ __align__(16) unsigned char smem[kXLds];
     uint16_t *sK = reinterpret_cast<uint16_t *>(smem);
     uint16_t *sV = reinterpret_cast<uint16_t *>(smem + kXOffV);
@@ -620,6 +620,8 @@ __global__ __launch_bounds__(kThreads, 4) void exact_fused_kernel(
     const int w = tid >> 6, lane = tid & 63, l16 = lane & 15, g = lane >> 4;
     const long slice = blockIdx.x;
     if (slice >= S) return;
+    // a workgroup alone on its CU starts about 2 us late (as in the forward)
+    if ((int)blockIdx.x >= solo_lo && (int)blockIdx.x < solo_hi) __builtin_amdgcn_s_sleep(64);
     const int NT = FULL ? 8 : (L + 15) >> 4;
     const int tok = 16 * w + l16;
     const long base = slice * (long)L * kD;
@@ -745,38 +747,44 @@ bool exact_fused_supported(int L, int Nk) { return L == Nk && L >= 1 && L <= kFL
 template <typename T, bool CAUSAL, bool MASKED>
 static hipError_t exact_fused_launch_t(const void *Q, const void *K, const void *V, int S, int L,
                                        const uint8_t *qvalid, const uint8_t *kvalid, int H, int G,
-                                       void *out, hipStream_t st) {
+                                       void *out, hipStream_t st, int cus) {
     const T *q = static_cast<const T *>(Q), *k = static_cast<const T *>(K);
+    // two workgroups fit a CU: with cus < S < 2 cus, workgroups S - cus ..
+    // cus - 1 run alone
+    const int solo_lo = cus > 0 && S > cus && S < 2 * cus ? S - cus : 0;
+    const int solo_hi = solo_lo > 0 ? cus : 0;
     const T *v = static_cast<const T *>(V);
     if (L == kFL)
         hipLaunchKernelGGL((exact_fused_kernel<T, true, CAUSAL, MASKED>), dim3((unsigned)S),
                            dim3(kThreads), 0, st, q, k, v, S, L, qvalid, kvalid, H, G,
-                           static_cast<T *>(out));
+                           static_cast<T *>(out), solo_lo, solo_hi);
     else
         hipLaunchKernelGGL((exact_fused_kernel<T, false, CAUSAL, MASKED>), dim3((unsigned)S),
                            dim3(kThreads), 0, st, q, k, v, S, L, qvalid, kvalid, H, G,
-                           static_cast<T *>(out));
+                           static_cast<T *>(out), solo_lo, solo_hi);
     return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t exact_fused_dispatch(const void *Q, const void *K, const void *V, int S, int L,
                                        bool causal, const uint8_t *qvalid, const uint8_t *kvalid,
-                                       int H, int G, void *out, hipStream_t st) {
+                                       int H, int G, void *out, hipStream_t st, int cus) {
     const bool masked = qvalid != nullptr || kvalid != nullptr;
     if (causal)
-        return masked ? exact_fused_launch_t<T, true, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st)
-                      : exact_fused_launch_t<T, true, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st);
-    return masked ? exact_fused_launch_t<T, false, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st)
-                  : exact_fused_launch_t<T, false, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st);
+        return masked ? exact_fused_launch_t<T, true, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st, cus)
+                      : exact_fused_launch_t<T, true, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st, cus);
+    return masked ? exact_fused_launch_t<T, false, true>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st, cus)
+                  : exact_fused_launch_t<T, false, false>(Q, K, V, S, L, qvalid, kvalid, H, G, out, st, cus);
 }
 
 hipError_t launch_exact_fused(const void *Q, const void *K, const void *V, int S, int L,
                               bool causal, ca_dtype_t dt, const uint8_t *qvalid,
-                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st) {
+                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st,
+                              int cus) {
     if (dt == CA_BF16)
-        return exact_fused_dispatch<bf16_t>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st);
-    return exact_fused_dispatch<float>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st);
+        return exact_fused_dispatch<bf16_t>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st,
+                                            cus);
+    return exact_fused_dispatch<float>(Q, K, V, S, L, causal, qvalid, kvalid, H, G, out, st, cus);
 }
 
 bool fused_supported(int L, int Kc) { return L >= 1 && L <= kFL && Kc >= 1 && Kc <= kFK; }

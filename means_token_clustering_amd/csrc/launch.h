@@ -183,6 +183,9 @@ struct BwdArgs {
     // fp32 [S, L, 64] shares of the centroid branch in dK and dV; nullable
     // (then the staged sequence runs for every shape)
     float *dkc, *dvl;
+    // two-launch form: workgroups alone on their CU, [solo_lo, solo_hi) (two
+    // workgroups fit a CU; with CUs < S < 2 CUs these are S - CUs .. CUs - 1)
+    int solo_lo, solo_hi;
 };
 int bwd_tiles(int L);
 hipError_t launch_backward(const BwdArgs &a, ca_dtype_t dt, hipStream_t st);
@@ -209,7 +212,8 @@ hipError_t launch_exact_attention(const void *Q, const void *K, const void *V, i
 bool exact_fused_supported(int L, int Nk);
 hipError_t launch_exact_fused(const void *Q, const void *K, const void *V, int S, int L,
                               bool causal, ca_dtype_t dt, const uint8_t *qvalid,
-                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st);
+                              const uint8_t *kvalid, int H, int G, void *out, hipStream_t st,
+                              int cus = 0);   // cus: the device's CU count (0: unknown)
 
 bool fused_supported(int L, int Kc);
 hipError_t launch_fused_forward(const void *Q, const void *K, const void *V, int S, int L, int Kc,
