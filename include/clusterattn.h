@@ -63,10 +63,11 @@ typedef enum {
 
 typedef enum { CA_F32 = 0, CA_BF16 = 1 } ca_dtype_t;
 
-/* Execution strategy of cluster_attn_forward_ex. AUTO picks FUSED when the
- * shape allows it (L <= 128 and min(nclust, L) <= 16), else STAGED. FUSED:
- * one launch, one workgroup per slice, the whole slice on chip. STAGED: one
- * kernel per step, any supported shape. */
+/* Execution strategy of cluster_attn_forward_ex. AUTO picks the fastest
+ * launch sequence for the shape, storage type and CU count (see
+ * cluster_attn_forward_ex and cluster_attn_plan_dt). FUSED: one launch, one
+ * workgroup per slice, the whole slice on chip. STAGED: one kernel per step,
+ * any supported shape. */
 typedef enum {
     CA_PATH_AUTO = 0,
     CA_PATH_FUSED = 1,
@@ -121,10 +122,15 @@ ca_status_t cluster_attn_forward(const void *Q, const void *K, const void *V,
  * wait longer than about 7 ms (possible only while other work holds the CUs
  * it needs) turns the affected output rows into NaN and their assignments
  * into -1. CA_PATH_AUTO picks the single launch for L <= 128; for
- * longer slices the 512-token single launch when the slice count fills
- * between half and all of the compute units, else the staged launches (the
- * segmented launch only when asked for). AUTO, STAGED and SEGMENTED need
- * cluster_attn_workspace_size_ex(..., path) bytes. */
+ * longer slices (L <= 512, nclust <= 16, W / 2 <= 16, no mask or listing
+ * variant) with bf16 storage and at most half of the compute units' worth
+ * of slices, the split form of the 512-token single launch (a second
+ * workgroup per slice for the window branch; its bounded waits turn the
+ * affected output rows into NaN if they ever give up); the 512-token single
+ * launch when the slice count fills between half and all of the compute
+ * units; else the staged launches (the segmented launch only when asked
+ * for). AUTO, STAGED and SEGMENTED need cluster_attn_workspace_size_ex(...,
+ * path) bytes. */
 ca_status_t cluster_attn_forward_ex(const void *Q, const void *K, const void *V,
                                     int B, int H, int L, int d, int nclust,
                                     int iters, int W, float alpha, void *out,
