@@ -661,3 +661,43 @@ def test_listing_flags_zero_is_default():
     o1, c1 = b.cluster_attn_forward(q, kk, vv, 16, 3, 32, 0.5, flags=0)
     torch.cuda.synchronize()
     assert torch.equal(c0, c1) and torch.equal(o0, o1)
+
+
+def test_single_launch_split_graph_replays():
+    """The split form captured in a HIP graph (its flag-clearing launch is
+    recorded ahead of it, as replays repeat the launch number): three replays,
+    with eager forwards on other inputs between them, each bitwise equal to
+    the eager result."""
+    x = gen.workload("bf16_l512")
+    b = _b()
+    plan = b.cluster_attn_plan(x.B, x.H, x.L, x.nclust, x.W, dtype=b.CA_BF16)
+    if not plan.startswith("fused512 split"):
+        pytest.skip(f"this device's CU count gives the plan {plan!r}")
+    q, k, v = (_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v"))
+    ws = torch.empty(b.cluster_attn_workspace_size(x.B, x.H, x.L, 64, x.nclust, b.CA_BF16) + 256,
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    c = torch.empty((x.B, x.H, x.L), dtype=torch.int32, device="cuda")
+    o_ref, c_ref = b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the side stream before capture
+        b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, out=out, assign_out=c,
+                               workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha, out=out, assign_out=c,
+                               workspace=ws)
+    ws2 = torch.empty_like(ws)
+    for r in range(3):
+        out.zero_()
+        c.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_ref) and torch.equal(c, c_ref), f"replay {r}"
+        # eager work between replays: other inputs, another workspace
+        b.cluster_attn_forward(k, v, q, x.nclust, x.iters, x.W, x.alpha, workspace=ws2)
+        torch.cuda.synchronize()
