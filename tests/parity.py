@@ -32,7 +32,8 @@ import numpy as np
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-RECORD_DIR = os.path.join(ROOT, "gpurun_out", "parity")
+# where the parity records go (CA_PARITY_RECORDS overrides the default)
+RECORD_DIR = os.environ.get("CA_PARITY_RECORDS", os.path.join(ROOT, "gpurun_out", "parity"))
 
 NEAR_TIE = 1e-5
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -159,8 +160,8 @@ def report_dict(case: str, plan: Optional[str], reports: List[AssignReport], out
 
 
 def write_record(name: str, rec: Dict) -> None:
-    """Keep one JSON record per case under gpurun_out/parity/ (the folder a GPU
-    run brings back), so the counts outlive pytest's captured output."""
+    """Keep one JSON record per case under RECORD_DIR, so that the counts
+    outlive pytest's captured output."""
     os.makedirs(RECORD_DIR, exist_ok=True)
     safe = "".join(ch if ch.isalnum() or ch in "-_." else "_" for ch in name)
     with open(os.path.join(RECORD_DIR, safe + ".json"), "w") as f:

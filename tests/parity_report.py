@@ -2,8 +2,9 @@
 
 Usage: python -m tests.parity_report [RECORD_DIR] [OUT.md]
 
-Reads gpurun_out/parity/report_<workload>.json (written by
-tests/test_gpu_parity_report.py on the GPU) and prints, or writes, a table
+Reads RECORD_DIR/report_<workload>.json (written by
+tests/test_gpu_parity_report.py on the GPU; RECORD_DIR defaults to the
+records folder of tests/parity.py) and prints, or writes, a table
 per configuration plus the records themselves as one JSON block at the end.
 CPU only; it reads the JSON records and calls nothing else.
 """
@@ -13,6 +14,11 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORDER = ["tiny", "distilbert", "bf16_l512", "long_l8192", "layer_bf16"]
+
+
+def parity_records_dir():
+    from tests import parity
+    return parity.RECORD_DIR
 
 
 def load(record_dir):
@@ -47,7 +53,7 @@ def render(recs) -> str:
 
 
 def main():
-    record_dir = sys.argv[1] if len(sys.argv) > 1 else os.path.join(ROOT, "gpurun_out", "parity")
+    record_dir = sys.argv[1] if len(sys.argv) > 1 else parity_records_dir()
     recs = load(record_dir)
     text = render(recs) + "\n\n```json\n" + json.dumps(recs, indent=1, sort_keys=True) + "\n```\n"
     if len(sys.argv) > 2:

@@ -1,8 +1,9 @@
 """Parity report of the five benchmark configurations (P0 protocol at full size).
 
 For each configuration the forward runs once on the path the benchmark takes
-(CA_PATH_AUTO) with the assignment trace, and the record kept under
-gpurun_out/parity/report_<workload>.json holds, per Lloyd iteration:
+(CA_PATH_AUTO) with the assignment trace, and the record kept as
+report_<workload>.json in the records folder of tests/parity.py holds, per
+Lloyd iteration:
 
 - near-ties (the oracle's best-to-second gap below 1e-5 ||q_i||^2),
 - GPU != oracle at a near-tie (excused) and elsewhere (must be 0),
