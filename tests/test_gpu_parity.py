@@ -701,3 +701,30 @@ def test_single_launch_split_graph_replays():
         # eager work between replays: other inputs, another workspace
         b.cluster_attn_forward(k, v, q, x.nclust, x.iters, x.W, x.alpha, workspace=ws2)
         torch.cuda.synchronize()
+
+
+def test_single_launch_split_concurrent_streams():
+    """Split-form forwards in flight on two streams at once (each launch takes
+    its own ring of flags): every output equals the same call made alone."""
+    b = _b()
+    xs = [gen.make_inputs(4, 12, 512, 64, nclust=16, iters=3, W=32, alpha=0.5, dtype=gen.BF16,
+                          seed=3900 + i, blobs=16, name="split512") for i in range(2)]
+    plan = b.cluster_attn_plan(4, 12, 512, 16, 32, dtype=b.CA_BF16)
+    if not plan.startswith("fused512 split"):
+        pytest.skip(f"this device's CU count gives the plan {plan!r}")
+    ins = [tuple(_dev(getattr(x, n), x.dtype) for n in ("q", "k", "v")) for x in xs]
+    refs = []
+    for (q, k, v), x in zip(ins, xs):
+        refs.append(b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    torch.cuda.synchronize()
+    for r in range(4):
+        for i, ((q, k, v), x) in enumerate(zip(ins, xs)):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(b.cluster_attn_forward(q, k, v, x.nclust, x.iters, x.W, x.alpha))
+    torch.cuda.synchronize()
+    for i in range(2):
+        for o, c in outs[i]:
+            assert torch.equal(o, refs[i][0]) and torch.equal(c, refs[i][1])
